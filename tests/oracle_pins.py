@@ -1,0 +1,436 @@
+"""Pins for the fp64 oracle: checks that do not trust the oracle's own formula.
+
+Each ``pin_*`` function takes a forward callable with the signature of
+``oracle.gdr_fwd`` and raises ``AssertionError`` when it disagrees with what
+the mathematics fixes.  ``test_oracle_pins.py`` runs them on the oracle;
+``test_oracle_mutants.py`` runs them on deliberately broken copies of the
+oracle's C source to show that each plausible mistake trips at least one pin.
+
+The recurrence being pinned is the gated delta rule (Gated DeltaNet), the op
+the FlashQLA pages call ``chunk_gated_delta_rule`` ("FlashQLA GDN backend
+produces different tokens from FLA Triton", Setup; "Findings from integrating
+FlashQLA's Blackwell GDN kernels into a JAX trainer", items 1-2):
+``S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T``,
+``o_t = scale S_t q_t``; the returned state is ``H = S^T`` ``[dk, dv]``.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------------------
+# Independent references used by the pins (none of them is the oracle's form)
+# ----------------------------------------------------------------------------
+
+def literal_fraction(q, k, v, decay, beta, cu, h0, scale, Hk, Hv):
+    """The matrix recurrence written literally, in exact rational arithmetic.
+
+    ``decay`` holds exp(g) as exact rationals.  S is dv x dk; returns (o, H=S^T)
+    as nested lists of Fractions.  Inputs are lists of Fractions indexed
+    [t][head][i].
+    """
+    r = Hv // Hk
+    dk = len(k[0][0])
+    dv = len(v[0][0])
+    n_seq = len(cu) - 1
+    o = [[[Fraction(0)] * dv for _ in range(Hv)] for _ in range(len(v))]
+    ht = [[None] * Hv for _ in range(n_seq)]
+    for n in range(n_seq):
+        for h in range(Hv):
+            hk = h // r
+            if cu[n + 1] == cu[n]:
+                continue
+            if h0 is None:
+                S = [[Fraction(0)] * dk for _ in range(dv)]
+            else:
+                S = [[h0[n][h][i][j] for i in range(dk)] for j in range(dv)]   # S = H^T
+            for t in range(cu[n], cu[n + 1]):
+                kt, qt, vt = k[t][hk], q[t][hk], v[t][h]
+                a, b = decay[t][h], beta[t][h]
+                # M = I - b k k^T ;  S <- a S M + b v k^T
+                M = [[(Fraction(1) if i == j else Fraction(0)) - b * kt[i] * kt[j]
+                      for j in range(dk)] for i in range(dk)]
+                S = [[a * sum(S[row][m] * M[m][col] for m in range(dk)) + b * vt[row] * kt[col]
+                      for col in range(dk)] for row in range(dv)]
+                o[t][h] = [scale * sum(S[row][m] * qt[m] for m in range(dk)) for row in range(dv)]
+            ht[n][h] = [[S[j][i] for j in range(dv)] for i in range(dk)]
+    return o, ht
+
+
+def literal_numpy(q, k, v, g, beta, cu, h0, scale):
+    """Literal matrix form in fp64 with explicit (I - beta k k^T) products.
+    Arrays are [T, H, d] (packed, B=1)."""
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    r = Hv // Hk
+    n_seq = len(cu) - 1
+    o = np.zeros((T, Hv, dv))
+    ht = np.zeros((n_seq, Hv, dk, dv))
+    I = np.eye(dk)
+    for n in range(n_seq):
+        for h in range(Hv):
+            S = np.zeros((dv, dk)) if h0 is None else h0[n, h].T.copy()
+            for t in range(cu[n], cu[n + 1]):
+                kt = k[t, h // r]
+                S = math.exp(g[t, h]) * S @ (I - beta[t, h] * np.outer(kt, kt)) \
+                    + beta[t, h] * np.outer(v[t, h], kt)
+                o[t, h] = scale * S @ q[t, h // r]
+            ht[n, h] = S.T
+    return o, ht
+
+
+def chunked_numpy(q, k, v, g, beta, cu, h0, scale, C):
+    """Chunked (WY) evaluation, derived independently from the recurrence.
+
+    Within a chunk with incoming state H0, gate prefix sums G_i = sum_{j<=i} g_j:
+      A_ij = beta_i exp(G_i - G_j) k_i.k_j (j < i),  T = (I + A)^-1,
+      W = T diag(beta e^G) K,  U = T diag(beta) V,  V_new = U - W H0,
+      O = scale (diag(e^G) Q H0 + (M o Q K^T) V_new),  M_ij = exp(G_i - G_j) (j <= i),
+      H_end = e^{G_L} H0 + (diag(e^{G_L - G}) K)^T V_new.
+    Arrays are [T, H, d] (packed, B=1).
+    """
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    r = Hv // Hk
+    n_seq = len(cu) - 1
+    o = np.zeros((T, Hv, dv))
+    ht = np.zeros((n_seq, Hv, dk, dv))
+    for n in range(n_seq):
+        for h in range(Hv):
+            H = np.zeros((dk, dv)) if h0 is None else h0[n, h].copy()
+            for s in range(cu[n], cu[n + 1], C):
+                e = min(s + C, cu[n + 1])
+                L = e - s
+                K, Q, V = k[s:e, h // r], q[s:e, h // r], v[s:e, h]
+                b = beta[s:e, h]
+                G = np.cumsum(g[s:e, h])
+                low = np.tril(np.ones((L, L), dtype=bool))
+                strict = np.tril(np.ones((L, L), dtype=bool), -1)
+                Mx = np.where(low, np.exp(np.where(low, G[:, None] - G[None, :], 0.0)), 0.0)
+                A = b[:, None] * np.where(strict, Mx, 0.0) * (K @ K.T)
+                Tm = np.linalg.inv(np.eye(L) + A)
+                W = Tm @ ((b * np.exp(G))[:, None] * K)
+                U = Tm @ (b[:, None] * V)
+                Vn = U - W @ H
+                o[s:e, h] = scale * (np.exp(G)[:, None] * (Q @ H) + (Mx * (Q @ K.T)) @ Vn)
+                H = np.exp(G[-1]) * H + (np.exp(G[-1] - G)[:, None] * K).T @ Vn
+            ht[n, h] = H
+    return o, ht
+
+
+# ----------------------------------------------------------------------------
+# Small inputs
+# ----------------------------------------------------------------------------
+
+def small_case(seed, lengths, Hk=2, Hv=2, dk=5, dv=3, with_h0=True, g_scale=1.0):
+    """Random packed inputs [1, T, H, d] with L2-normalised q, k."""
+    rng = np.random.default_rng(seed)
+    T = int(sum(lengths))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    q = rng.standard_normal((1, T, Hk, dk))
+    k = rng.standard_normal((1, T, Hk, dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((1, T, Hv, dv))
+    x = rng.standard_normal((1, T, Hv))
+    g = g_scale * -np.log1p(np.exp(-x))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((1, T, Hv))))
+    n = len(lengths)
+    h0 = 0.3 * rng.standard_normal((n, Hv, dk, dv)) if with_h0 else None
+    return dict(q=q, k=k, v=v, g=g, beta=beta, cu=cu, h0=h0)
+
+
+def _close(a, b, rtol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    ref = max(1.0, float(np.abs(b).max()) if b.size else 1.0)
+    err = float(np.abs(a - b).max()) if a.size else 0.0
+    assert np.all(np.isfinite(a)), "%s: non-finite" % what
+    assert err <= rtol * ref, "%s: max|diff| %.3e > %.1e * %.3e" % (what, err, rtol, ref)
+
+
+def _run(fwd, c, cu=None, h0="same", **kw):
+    return fwd(c["q"], c["k"], c["v"], c["g"], c["beta"],
+               c["cu"] if cu is None else cu, c["h0"] if h0 == "same" else h0, **kw)
+
+
+# ----------------------------------------------------------------------------
+# Pins
+# ----------------------------------------------------------------------------
+
+def pin_exact_rational(fwd):
+    """Tiny case (T=5 in two segments, GQA 1:2, dk=3, dv=2) against the literal
+    recurrence in exact rational arithmetic.  Dyadic inputs are exact in fp64;
+    the decays are the fp64 values exp(g) taken as exact rationals."""
+    F = Fraction
+    kk = [[(1, 0, 0)], [(F(3, 4), F(1, 2), F(-1, 4))], [(0, F(5, 8), F(3, 4))],
+          [(F(1, 2), F(1, 2), F(1, 2))], [(F(-3, 8), F(1, 4), F(7, 8))]]
+    qq = [[(F(1, 2), F(-1, 4), F(3, 4))], [(0, 1, 0)], [(F(1, 4), F(1, 4), F(-1, 2))],
+          [(F(-1, 2), F(3, 8), F(1, 8))], [(1, F(1, 2), F(-1, 4))]]
+    vv = [[(F(1), F(-2)), (F(1, 2), F(3, 4))], [(F(3, 2), F(1, 4)), (F(-1), F(5, 8))],
+          [(F(-3, 4), F(1)), (F(1, 4), F(-1, 2))], [(F(2), F(-1, 8)), (F(3, 8), F(7, 4))],
+          [(F(1, 8), F(-5, 4)), (F(-7, 8), F(1, 2))]]
+    bb = [[F(1, 2), F(1, 4)], [F(3, 4), F(1)], [F(1, 4), F(1, 2)], [F(1), F(3, 8)],
+          [F(5, 8), F(3, 4)]]
+    gg = [[0.0, -0.5], [-0.25, 0.0], [-1.0, -0.125], [0.0, -2.0], [-0.75, -0.3]]
+    cu = [0, 3, 5]
+    h0f = [[[[F((i + 1) * (j + 2) * (-1) ** (n + h + i), 8 * (1 + h)) for j in range(2)]
+             for i in range(3)] for h in range(2)] for n in range(2)]
+    scale = F(1, 2)
+    kf = [[[F(x) for x in hd] for hd in t] for t in kk]
+    qf = [[[F(x) for x in hd] for hd in t] for t in qq]
+    vf = [[[F(x) for x in hd] for hd in t] for t in vv]
+    decay = [[F(math.exp(x)) for x in t] for t in gg]
+    o_ex, ht_ex = literal_fraction(qf, kf, vf, decay, bb, cu, h0f, scale, Hk=1, Hv=2)
+
+    as_np = lambda x: np.array([[[float(e) for e in hd] for hd in t] for t in x])[None]
+    o, ht = fwd(as_np(qf), as_np(kf), as_np(vf), np.array(gg)[None],
+                np.array([[float(b) for b in t] for t in bb])[None], np.array(cu),
+                np.array([[[[float(e) for e in r] for r in hd] for hd in n] for n in h0f]),
+                scale=0.5)
+    o_exf = np.array([[[float(e) for e in hd] for hd in t] for t in o_ex])
+    ht_exf = np.array([[[[float(e) for e in r] for r in hd] for hd in n] for n in ht_ex])
+    _close(o[0], o_exf, 1e-13, "exact rational: o")
+    _close(ht, ht_exf, 1e-13, "exact rational: ht")
+
+
+def pin_literal_matrix_form(fwd):
+    """Random small case against the literal S-form in fp64 (explicit
+    I - beta k k^T products), with dk != dv, GQA and several segments."""
+    c = small_case(11, [7, 1, 12], Hk=2, Hv=4, dk=6, dv=4)
+    o, ht = _run(fwd, c, scale=0.7)
+    o_r, ht_r = literal_numpy(c["q"][0], c["k"][0], c["v"][0], c["g"][0], c["beta"][0],
+                              c["cu"], c["h0"], 0.7)
+    _close(o[0], o_r, 1e-12, "literal form: o")
+    _close(ht, ht_r, 1e-12, "literal form: ht")
+
+
+def pin_chunked_form(fwd):
+    """Chunked (WY) evaluation for chunk sizes 1, 2, 7, 16, 64 and one chunk
+    spanning each whole segment, segments not multiples of the chunk size."""
+    c = small_case(12, [70, 33, 5, 129], Hk=1, Hv=2, dk=8, dv=6)
+    o, ht = _run(fwd, c, scale=0.3)
+    for C in (1, 2, 7, 16, 64, 1000):
+        o_c, ht_c = chunked_numpy(c["q"][0], c["k"][0], c["v"][0], c["g"][0], c["beta"][0],
+                                  c["cu"], c["h0"], 0.3, C)
+        _close(o[0], o_c, 1e-11, "chunked C=%d: o" % C)
+        _close(ht, ht_c, 1e-11, "chunked C=%d: ht" % C)
+
+
+def pin_identity_when_beta_and_g_zero(fwd):
+    """beta = 0 and g = 0: the state never moves (ht == h0 bit for bit) and
+    o_t = scale * h0^T q_t."""
+    c = small_case(13, [9, 4], dk=5, dv=3)
+    c["beta"][:] = 0.0
+    c["g"][:] = 0.0
+    o, ht = _run(fwd, c, scale=0.5)
+    assert np.array_equal(ht, c["h0"]), "beta=g=0: ht must equal h0 exactly"
+    exp_o = np.zeros_like(o)
+    for n in range(2):
+        for t in range(c["cu"][n], c["cu"][n + 1]):
+            for h in range(2):
+                exp_o[0, t, h] = 0.5 * c["h0"][n, h].T @ c["q"][0, t, h]
+    _close(o, exp_o, 1e-14, "beta=g=0: o")
+
+
+def pin_pure_decay(fwd):
+    """beta = 0: ht = exp(sum g) h0 and o_t = scale exp(G_t) h0^T q_t."""
+    c = small_case(14, [11], dk=4, dv=3)
+    c["beta"][:] = 0.0
+    o, ht = _run(fwd, c, scale=1.0)
+    G = np.cumsum(c["g"][0], axis=0)            # [T, H]
+    for h in range(2):
+        _close(ht[0, h], np.exp(G[-1, h]) * c["h0"][0, h], 1e-13, "pure decay: ht")
+        for t in range(11):
+            _close(o[0, t, h], np.exp(G[t, h]) * c["h0"][0, h].T @ c["q"][0, t, h], 1e-13,
+                   "pure decay: o")
+
+
+def pin_single_token(fwd):
+    """One token from a zero state: ht = beta k v^T, o = scale beta (q.k) v."""
+    c = small_case(15, [1], Hk=1, Hv=1, dk=4, dv=3, with_h0=False)
+    o, ht = _run(fwd, c, scale=0.25)
+    q, k, v = c["q"][0, 0, 0], c["k"][0, 0, 0], c["v"][0, 0, 0]
+    b = c["beta"][0, 0, 0]
+    _close(ht[0, 0], b * np.outer(k, v), 1e-15, "single token: ht")
+    _close(o[0, 0, 0], 0.25 * b * (q @ k) * v, 1e-15, "single token: o")
+
+
+def pin_orthonormal_overwrite(fwd):
+    """Keys drawn from the standard basis, beta = 1, g = 0: each write replaces
+    the row of H for its key, so H^T k_t = v_t after every token and at the end
+    row i of H holds the value last written under key i (h0's row otherwise)."""
+    rng = np.random.default_rng(16)
+    T, dk, dv = 25, 7, 3
+    idx = rng.integers(0, dk, size=T)
+    idx[:3] = [2, 2, 5]
+    k = np.zeros((1, T, 1, dk))
+    k[0, np.arange(T), 0, idx] = 1.0
+    q = k.copy()                                     # read back the key just written
+    v = rng.standard_normal((1, T, 1, dv))
+    g = np.zeros((1, T, 1))
+    beta = np.ones((1, T, 1))
+    h0 = rng.standard_normal((1, 1, dk, dv))
+    o, ht = fwd(q, k, v, g, beta, None, h0, scale=1.0)
+    _close(o[0, :, 0], v[0, :, 0], 1e-15, "overwrite: o_t = v_t")
+    expect = h0[0, 0].copy()
+    for t in range(T):
+        expect[idx[t]] = v[0, t, 0]
+    _close(ht[0, 0], expect, 1e-15, "overwrite: final rows")
+
+
+def pin_scalar_iir(fwd):
+    """dk = dv = 1 with constant g, beta, k, q: the state is the first-order IIR
+    filter h_t = a h_{t-1} + b v_t, a = e^g (1 - beta k^2), b = beta k,
+    evaluated with scipy.signal.lfilter."""
+    from scipy.signal import lfilter
+    rng = np.random.default_rng(17)
+    T = 40
+    kk, qq, gg, bb, h0 = 0.8, -0.6, -0.2, 0.7, 0.35
+    v = rng.standard_normal(T)
+    a = math.exp(gg) * (1.0 - bb * kk * kk)
+    y, _ = lfilter([bb * kk], [1.0, -a], v, zi=[a * h0])
+    o, ht = fwd(np.full((1, T, 1, 1), qq), np.full((1, T, 1, 1), kk), v.reshape(1, T, 1, 1),
+                np.full((1, T, 1), gg), np.full((1, T, 1), bb), None,
+                np.full((1, 1, 1, 1), h0), scale=2.0)
+    _close(o[0, :, 0, 0], 2.0 * qq * y, 1e-13, "scalar IIR: o")
+    _close(ht[0, 0, 0, 0], y[-1], 1e-13, "scalar IIR: ht")
+
+
+def pin_segment_independence(fwd):
+    """A packed call equals separate calls per segment, bit for bit."""
+    c = small_case(18, [6, 13, 1, 9], Hk=1, Hv=2)
+    o, ht = _run(fwd, c, scale=0.5)
+    cu = c["cu"]
+    for n in range(4):
+        s, e = cu[n], cu[n + 1]
+        sub = {key: c[key][:, s:e] for key in ("q", "k", "v", "g", "beta")}
+        o_n, ht_n = fwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], None,
+                        c["h0"][n:n + 1], scale=0.5)
+        assert np.array_equal(o[:, s:e], o_n), "segment %d: o differs from a separate call" % n
+        assert np.array_equal(ht[n], ht_n[0]), "segment %d: ht differs" % n
+
+
+def pin_ghost_segments(fwd):
+    """Length-0 segments (leading, interior, trailing, 120 trailing) change
+    nothing: o and the real ht rows are bit-identical, ghost ht rows keep the
+    caller's bytes."""
+    c = small_case(19, [5, 8, 3], Hk=1, Hv=2)
+    o_ref, ht_ref = _run(fwd, c, scale=0.5)
+    base = [0, 5, 13, 16]
+    for layout in ([0, 0, 5, 13, 16], [0, 5, 5, 5, 13, 16], [0, 5, 13, 16, 16], base + [16] * 120):
+        cu = np.array(layout)
+        real = [i for i in range(len(cu) - 1) if cu[i + 1] > cu[i]]
+        h0 = np.full((len(cu) - 1, 2, 5, 3), np.nan)
+        h0[real] = c["h0"]
+        sentinel = np.full((len(cu) - 1, 2, 5, 3), -7.25)
+        o, ht = fwd(c["q"], c["k"], c["v"], c["g"], c["beta"], cu, h0, scale=0.5,
+                    ht_init=sentinel)
+        assert np.array_equal(o, o_ref), "ghosts %s: o changed" % layout[:8]
+        assert np.array_equal(ht[real], ht_ref), "ghosts: real ht changed"
+        ghosts = [i for i in range(len(cu) - 1) if i not in real]
+        assert np.all(ht[ghosts] == -7.25), "ghosts: a ghost ht row was written"
+
+
+def pin_split_resume(fwd):
+    """Running [0, m) then [m, T) with h0 := ht equals one run, bit for bit."""
+    c = small_case(20, [37], Hk=1, Hv=1, dk=4, dv=5)
+    o, ht = _run(fwd, c, scale=0.5)
+    for m in (1, 16, 20, 36):
+        a = {key: c[key][:, :m] for key in ("q", "k", "v", "g", "beta")}
+        b = {key: c[key][:, m:] for key in ("q", "k", "v", "g", "beta")}
+        o1, h1 = fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], None, c["h0"], scale=0.5)
+        o2, h2 = fwd(b["q"], b["k"], b["v"], b["g"], b["beta"], None, h1, scale=0.5)
+        assert np.array_equal(np.concatenate([o1, o2], axis=1), o), "split at %d: o" % m
+        assert np.array_equal(h2, ht), "split at %d: ht" % m
+
+
+def pin_linearity(fwd):
+    """For fixed q, k, g, beta the outputs are jointly linear in (v, h0):
+    scaling both by 4 scales o and ht by 4 exactly (a power of two)."""
+    c = small_case(21, [10, 7])
+    o, ht = _run(fwd, c, scale=0.5)
+    o4, ht4 = fwd(c["q"], c["k"], 4 * c["v"], c["g"], c["beta"], c["cu"], 4 * c["h0"], scale=0.5)
+    assert np.array_equal(o4, 4 * o) and np.array_equal(ht4, 4 * ht), "linearity"
+    # superposition: (v, 0) + (0, h0)
+    ov, htv = fwd(c["q"], c["k"], c["v"], c["g"], c["beta"], c["cu"], None, scale=0.5)
+    oh, hth = fwd(c["q"], c["k"], 0 * c["v"], c["g"], c["beta"], c["cu"], c["h0"], scale=0.5)
+    _close(ov + oh, o, 1e-13, "superposition: o")
+    _close(htv + hth, ht, 1e-13, "superposition: ht")
+
+
+def pin_causality(fwd):
+    """Changing tokens after t leaves o at positions <= t unchanged."""
+    c = small_case(22, [30], Hk=1, Hv=1)
+    o, _ = _run(fwd, c, scale=0.5)
+    c2 = {key: (val.copy() if isinstance(val, np.ndarray) else val) for key, val in c.items()}
+    t0 = 17
+    for key in ("q", "k", "v", "g", "beta"):
+        c2[key][:, t0 + 1:] = c2[key][:, t0 + 1:] * 0.5 + 0.1
+    o2, _ = _run(fwd, c2, scale=0.5)
+    assert np.array_equal(o[:, :t0 + 1], o2[:, :t0 + 1]), "causality"
+    assert not np.array_equal(o[:, t0 + 1:], o2[:, t0 + 1:])
+
+
+def pin_contraction_bound(fwd):
+    """With ||k|| = 1, 0 < beta < 1 and g <= 0 each transition
+    e^g (I - beta k k^T) has spectral norm <= 1, so with v = 0 the state's
+    spectral norm never grows; checked token by token via split runs."""
+    c = small_case(23, [24], Hk=1, Hv=1, dk=5, dv=4)
+    c["v"][:] = 0.0
+    H = c["h0"]
+    prev = np.linalg.norm(H[0, 0], 2)
+    for t in range(24):
+        sl = {key: c[key][:, t:t + 1] for key in ("q", "k", "v", "g", "beta")}
+        _, H = fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], None, H, scale=1.0)
+        nrm = np.linalg.norm(H[0, 0], 2)
+        assert nrm <= prev * (1 + 1e-12), "state norm grew at token %d" % t
+        prev = nrm
+    assert prev < np.linalg.norm(c["h0"][0, 0], 2)
+
+
+def read_page_max_ref():
+    rows = {}
+    with open(os.path.join(GOLDEN, "page_max_ref.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            what, T, val = line.split()
+            rows[(what, int(T))] = float(val)
+    return rows
+
+
+def pin_page_magnitudes(fwd, T=512):
+    """Magnitude check against the max_ref values the maintainers printed
+    (soft: the page omits the gate and beta distributions).  With no decay
+    (g = 0), beta = sigmoid(N(0,1)), L2-normalised q, k and Gaussian v, d = 128,
+    the largest |o| and |ht| over 4 heads must land within a factor 1.5 of the
+    printed max_ref."""
+    rows = read_page_max_ref()
+    rng = np.random.default_rng(24)
+    H, d = 4, 128
+    q = rng.standard_normal((1, T, H, d))
+    k = rng.standard_normal((1, T, H, d))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((1, T, H, d))
+    g = np.zeros((1, T, H))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((1, T, H))))
+    o, ht = fwd(q, k, v, g, beta, None, None, scale=d ** -0.5)
+    for what, val in (("output", float(np.abs(o).max())), ("final_state", float(np.abs(ht).max()))):
+        ref = rows[(what, T)]
+        assert ref / 1.5 <= val <= ref * 1.5, "%s max %.4f vs page max_ref %.4f" % (what, val, ref)
+
+
+ALL_PINS = [pin_exact_rational, pin_literal_matrix_form, pin_chunked_form,
+            pin_identity_when_beta_and_g_zero, pin_pure_decay, pin_single_token,
+            pin_orthonormal_overwrite, pin_scalar_iir, pin_segment_independence,
+            pin_ghost_segments, pin_split_resume, pin_linearity, pin_causality,
+            pin_contraction_bound, pin_page_magnitudes]

@@ -1,0 +1,76 @@
+"""Plant plausible mistakes in copies of the oracle's C source (on the CPU
+only) and check that the pins catch every one of them."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS, pin_page_magnitudes
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "gdr_oracle.c")
+
+# (name, text in the source, replacement)
+MUTANTS = [
+    ("no_decay", "for (int64_t i = 0; i < dk * dv; ++i) H[i] *= a;", ""),
+    ("delta_sign", "p[j] = b * (vt[j] - p[j]);", "p[j] = b * (vt[j] + p[j]);"),
+    ("no_beta", "p[j] = b * (vt[j] - p[j]);", "p[j] = (vt[j] - p[j]);"),
+    ("read_with_key", "ot[j] += H[i * dv + j] * qt[i];", "ot[j] += H[i * dv + j] * kt[i];"),
+    ("no_scale", "ot[j] *= J->scale;", "ot[j] *= 1.0;"),
+    ("gqa_modulo", "const int64_t hk = h / (Hv / Hk);", "const int64_t hk = h % Hk;"),
+    ("ghost_writes", "if (eos <= bos) return;", "if (eos < bos) return;"),
+    ("transposed_update", "H[i * dv + j] += kt[i] * p[j];",
+     "H[(i * dv + j) % (dk * dv)] += kt[j % dk] * p[i % dv];"),
+    ("beta_on_decay", "const double a = exp(J->g[t * Hv + h]);",
+     "const double a = exp(J->g[t * Hv + h]) * J->beta[t * Hv + h];"),
+    ("output_before_update",  # read the state before the rank-1 write
+     "for (int64_t j = 0; j < dv; ++j) p[j] = b * (vt[j] - p[j]);   /* p now holds d */",
+     "for (int64_t j = 0; j < dv; ++j) p[j] = b * (vt[j] - p[j]);"
+     " { double *o2 = J->o + (t * Hv + h) * dv; for (int64_t j = 0; j < dv; ++j) { o2[j] = 0.0;"
+     " for (int64_t i = 0; i < dk; ++i) o2[j] += H[i * dv + j] * qt[i]; o2[j] *= J->scale; } }"
+     " if (0)"),
+    ("decay_after_update", "for (int64_t i = 0; i < dk * dv; ++i) H[i] *= a;\n",
+     "H[0] *= 1.0;\n"),
+]
+
+
+def _build(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert old in src, "mutant %s: pattern not found" % name
+    src = src.replace(old, new, 1)
+    if name == "decay_after_update":
+        src = src.replace("double *ot = J->o + (t * Hv + h) * dv;",
+                          "for (int64_t i = 0; i < dk * dv; ++i) H[i] *= a;\n"
+                          "        double *ot = J->o + (t * Hv + h) * dv;", 1)
+    if name == "output_before_update":
+        # the original output block must not overwrite the planted early read
+        src = src.replace("double *ot = J->o + (t * Hv + h) * dv;\n",
+                          "double *ot = J->o + (t * Hv + h) * dv; if (0)\n", 1)
+        src = src.replace("for (int64_t j = 0; j < dv; ++j) ot[j] = 0.0;",
+                          "{ for (int64_t j = 0; j < dv; ++j) ot[j] = 0.0; } if (0)", 1)
+        src = src.replace("for (int64_t j = 0; j < dv; ++j) ot[j] *= J->scale;",
+                          "if (0) for (int64_t j = 0; j < dv; ++j) ot[j] *= J->scale;", 1)
+    c = tmp_path / ("m_%s.c" % name)
+    c.write_text(src)
+    so = tmp_path / ("m_%s.so" % name)
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", str(c),
+                           "-o", str(so), "-lm"])
+    return str(so)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    so = _build(tmp_path, name, old, new)
+
+    def fwd(*a, **kw):
+        return oracle.gdr_fwd(*a, _lib_path=so, **kw)
+
+    caught = []
+    for pin in ALL_PINS:
+        if pin is pin_page_magnitudes:
+            continue  # soft magnitude check; the exact pins must suffice
+        try:
+            pin(fwd)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, "mutant %s passed every pin" % name
