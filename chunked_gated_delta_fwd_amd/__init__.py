@@ -1,0 +1,212 @@
+"""Chunked gated delta rule forward for AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libgdr.so`` (HIP kernels behind the C ABI of
+``include/gdr.h``).  Every step of the computation runs in the library's
+kernels; this module only marshals torch tensors into descriptors and passes
+torch's current HIP stream.  There is no fallback: if the library is missing
+or the device is not gfx950, calls raise.
+
+The op is ``chunk_gated_delta_rule`` (chunk size 64, varlen ``cu_seqlens``,
+initial/final state) as named on the FlashQLA pages; per sequence and v-head
+``S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T`` and
+``o_t = scale S_t q_t``, the state returned as ``H = S^T`` ``[N, Hv, dk, dv]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdr.so")
+
+GDR_F32, GDR_BF16, GDR_I32 = 0, 1, 2
+STATUS = {0: "GDR_OK", -1: "GDR_EINVAL", -2: "GDR_ESHAPE", -3: "GDR_EDTYPE", -4: "GDR_ESTRIDE",
+          -5: "GDR_EALIAS", -6: "GDR_EDEVICE", -7: "GDR_ELAUNCH", -8: "GDR_ENOMEM"}
+
+# every symbol include/gdr.h declares
+EXPORTS = ("gdr_chunk_fwd", "gdr_plan", "gdr_prepare_chunks", "gdr_chunk_local_cumsum",
+           "gdr_last_error", "gdr_version", "gdr_selftest_mfma")
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (%d): %s" % (STATUS.get(status, "?"), status, message))
+        self.status = status
+        self.message = message
+
+
+class GdrTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.POINTER(ctypes.c_int64)), ("strides", ctypes.POINTER(ctypes.c_int64))]
+
+
+class GdrLaunchPlan(ctypes.Structure):
+    _fields_ = [("n_seq", ctypes.c_int64), ("total_tokens", ctypes.c_int64), ("nt_max", ctypes.c_int64),
+                ("hk", ctypes.c_int32), ("hv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32), ("varlen", ctypes.c_int32),
+                ("has_h0", ctypes.c_int32), ("has_ht", ctypes.c_int32), ("grid_fwd", ctypes.c_int64),
+                ("block_fwd", ctypes.c_int32), ("lds_fwd", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library(path: Optional[str] = None):
+    """Load ``libgdr.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("libgdr.so is not built (%s); run __graft_entry__.build()" % p)
+    lib = ctypes.CDLL(p)
+    TP = ctypes.POINTER(GdrTensor)
+    lib.gdr_chunk_fwd.argtypes = [TP] * 9 + [ctypes.c_float, ctypes.c_void_p]
+    lib.gdr_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_plan.argtypes = [TP] * 9 + [ctypes.c_float, ctypes.POINTER(GdrLaunchPlan)]
+    lib.gdr_plan.restype = ctypes.c_int
+    lib.gdr_prepare_chunks.argtypes = [TP] * 4 + [ctypes.c_void_p]
+    lib.gdr_prepare_chunks.restype = ctypes.c_int
+    lib.gdr_chunk_local_cumsum.argtypes = [TP] * 3 + [ctypes.c_void_p]
+    lib.gdr_chunk_local_cumsum.restype = ctypes.c_int
+    lib.gdr_last_error.argtypes = []
+    lib.gdr_last_error.restype = ctypes.c_char_p
+    lib.gdr_version.argtypes = []
+    lib.gdr_version.restype = ctypes.c_int
+    lib.gdr_selftest_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.gdr_selftest_mfma.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(lib, status: int):
+    if status != 0:
+        raise GdrError(status, lib.gdr_last_error().decode("utf-8", "replace"))
+
+
+class _Desc:
+    """A gdr_tensor plus the shape/stride arrays it points to."""
+
+    def __init__(self, data: int, dtype: int, shape: Sequence[int], strides: Optional[Sequence[int]]):
+        n = len(shape)
+        self._shape = (ctypes.c_int64 * max(n, 1))(*shape)
+        self._strides = None if strides is None else (ctypes.c_int64 * max(n, 1))(*strides)
+        self.t = GdrTensor(ctypes.c_void_p(data), dtype, n,
+                           ctypes.cast(self._shape, ctypes.POINTER(ctypes.c_int64)),
+                           None if self._strides is None else
+                           ctypes.cast(self._strides, ctypes.POINTER(ctypes.c_int64)))
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.t)
+
+
+def describe(data: int, dtype: int, shape: Sequence[int], strides: Optional[Sequence[int]] = None) -> _Desc:
+    """Descriptor from a raw address (used by host-only planning tests)."""
+    return _Desc(int(data), int(dtype), [int(s) for s in shape],
+                 None if strides is None else [int(s) for s in strides])
+
+
+def _torch_dtype_code(t) -> int:
+    import torch
+    m = {torch.float32: GDR_F32, torch.bfloat16: GDR_BF16, torch.int32: GDR_I32}
+    if t.dtype not in m:
+        raise GdrError(-3, "unsupported dtype %s" % t.dtype)
+    return m[t.dtype]
+
+
+def _desc(t) -> Optional[_Desc]:
+    if t is None:
+        return None
+    return _Desc(t.data_ptr(), _torch_dtype_code(t), list(t.shape), list(t.stride()))
+
+
+def _ref(d: Optional[_Desc]):
+    return None if d is None else d.ref
+
+
+def _stream_handle(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Optional[float] = None,
+              output_final_state: bool = True, o=None, ht=None) -> Tuple[object, Optional[object]]:
+    """Forward of chunk_gated_delta_rule on torch tensors (device memory).
+
+    q, k ``[B,T,Hk,d]``; v ``[B,T,Hv,d]``; g, beta ``[B,T,Hv]``; ``cu_seqlens``
+    int32 ``[N+1]`` (B == 1) or None; h0 f32 ``[N,Hv,d,d]`` or None.  Returns
+    ``(o, ht)``; ``ht`` is None unless ``output_final_state``.  ``o``/``ht`` may be
+    given preallocated (ghost rows of ``ht`` keep their contents).
+    """
+    import torch
+    lib = library()
+    B, T, Hk, d = q.shape
+    Hv = v.shape[2]
+    N = (cu_seqlens.shape[0] - 1) if cu_seqlens is not None else B
+    if scale is None:
+        scale = float(d) ** -0.5
+    if o is None:
+        o = torch.empty((B, T, Hv, v.shape[3]), dtype=q.dtype, device=q.device)
+    if ht is None and output_final_state:
+        ht = torch.zeros((N, Hv, d, v.shape[3]), dtype=torch.float32, device=q.device)
+    ds = [_desc(x) for x in (q, k, v, g, beta, cu_seqlens, h0, o, ht)]
+    _check(lib, lib.gdr_chunk_fwd(*[_ref(x) for x in ds], ctypes.c_float(scale),
+                                  ctypes.c_void_p(_stream_handle(q))))
+    return o, ht
+
+
+def plan(q, k, v, g, beta, cu_seqlens=None, h0=None, o=None, ht=None, scale: float = 1.0) -> dict:
+    """The launch plan for these descriptors (no device access)."""
+    lib = library()
+    p = GdrLaunchPlan()
+    ds = [x if (x is None or isinstance(x, _Desc)) else _desc(x)
+          for x in (q, k, v, g, beta, cu_seqlens, h0, o, ht)]
+    _check(lib, lib.gdr_plan(*[_ref(x) for x in ds], ctypes.c_float(scale), ctypes.byref(p)))
+    return {name: getattr(p, name) for name, _ in GdrLaunchPlan._fields_}
+
+
+def prepare_chunks(cu_seqlens, nt_max: Optional[int] = None, with_map: bool = True,
+                   with_order: bool = True):
+    """Chunk offsets [N+1], chunk map [nt_max, 2] and longest-first order [N]
+    derived on the device from the content of ``cu_seqlens``."""
+    import torch
+    lib = library()
+    N = cu_seqlens.shape[0] - 1
+    dev = cu_seqlens.device
+    offs = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    if nt_max is None:
+        nt_max = 0
+    cmap = torch.empty((nt_max, 2), dtype=torch.int32, device=dev) if with_map else None
+    order = torch.empty(N, dtype=torch.int32, device=dev) if with_order else None
+    ds = [_desc(x) for x in (cu_seqlens, offs, cmap, order)]
+    _check(lib, lib.gdr_prepare_chunks(*[_ref(x) for x in ds], ctypes.c_void_p(_stream_handle(cu_seqlens))))
+    return offs, cmap, order
+
+
+def chunk_local_cumsum(g, cu_seqlens=None, out=None):
+    """Chunk-local (64-token) inclusive prefix sum of the log-gate, fp32."""
+    import torch
+    lib = library()
+    if out is None:
+        out = torch.zeros(g.shape, dtype=torch.float32, device=g.device)
+    ds = [_desc(x) for x in (g, cu_seqlens, out)]
+    _check(lib, lib.gdr_chunk_local_cumsum(*[_ref(x) for x in ds], ctypes.c_void_p(_stream_handle(g))))
+    return out
+
+
+def selftest_mfma(a_bits, b_bits):
+    """Run the MFMA layout self-test on int16 device tensors of 64x8 bf16 bits."""
+    import torch
+    lib = library()
+    c = torch.zeros(512, dtype=torch.float32, device=a_bits.device)
+    _check(lib, lib.gdr_selftest_mfma(ctypes.c_void_p(a_bits.data_ptr()), ctypes.c_void_p(b_bits.data_ptr()),
+                                      ctypes.c_void_p(c.data_ptr()), ctypes.c_void_p(_stream_handle(a_bits))))
+    return c
+
+
+def version() -> int:
+    return library().gdr_version()

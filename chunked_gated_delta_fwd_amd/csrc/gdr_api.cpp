@@ -1,0 +1,375 @@
+// Host side of the C ABI declared in include/gdr.h: descriptor validation,
+// launch planning from shapes only, stream-ordered workspace, error text.
+//
+// Validation rules follow the pages' integration lessons: NULL strides mean
+// compact row-major ("Findings from integrating FlashQLA's Blackwell GDN
+// kernels into a JAX trainer", item 3), length-0 segments are legal anywhere
+// (item 2), chunk indices come from the cu_seqlens content on the device every
+// call and nothing is cached by tensor identity (item 1).
+#include "gdr.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "gdr_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return GDR_OK;
+}
+
+size_t dtype_size(int32_t dt) { return dt == GDR_F32 ? 4 : dt == GDR_BF16 ? 2 : dt == GDR_I32 ? 4 : 0; }
+
+const char *dtype_name(int32_t dt) {
+    return dt == GDR_F32 ? "f32" : dt == GDR_BF16 ? "bf16" : dt == GDR_I32 ? "i32" : "?";
+}
+
+struct Span {
+    uintptr_t lo = 0, hi = 0;   // [lo, hi) bytes; empty when lo == hi
+};
+
+// Checks rank, non-negative extents, compact strides and the data pointer.
+int check_tensor(const gdr_tensor *t, const char *name, int ndim, int64_t *numel, size_t align) {
+    if (!t) return fail(GDR_EINVAL, "%s: descriptor is NULL", name);
+    if (t->ndim != ndim) return fail(GDR_ESHAPE, "%s: expected %d dimensions, got %d", name, ndim, t->ndim);
+    if (ndim > 0 && !t->shape) return fail(GDR_EINVAL, "%s: shape pointer is NULL", name);
+    if (dtype_size(t->dtype) == 0) return fail(GDR_EDTYPE, "%s: unknown dtype %d", name, t->dtype);
+    int64_t n = 1;
+    for (int i = 0; i < ndim; ++i) {
+        if (t->shape[i] < 0) return fail(GDR_ESHAPE, "%s: negative extent in dimension %d", name, i);
+        if (t->shape[i] > 0 && n > (INT64_MAX / 16) / t->shape[i])
+            return fail(GDR_ESHAPE, "%s: too many elements", name);
+        n *= t->shape[i];
+    }
+    if (t->strides) {
+        int64_t expect = 1;
+        for (int i = ndim - 1; i >= 0; --i) {
+            if (t->shape[i] != 1 && t->strides[i] != expect)
+                return fail(GDR_ESTRIDE,
+                            "%s: strides must be compact row-major (dimension %d has stride %lld, expected %lld)",
+                            name, i, (long long)t->strides[i], (long long)expect);
+            expect *= t->shape[i];
+        }
+    }
+    if (n > 0 && !t->data) return fail(GDR_EINVAL, "%s: data pointer is NULL", name);
+    if (n > 0 && (reinterpret_cast<uintptr_t>(t->data) % align) != 0)
+        return fail(GDR_EINVAL, "%s: data pointer must be %zu-byte aligned", name, align);
+    *numel = n;
+    return GDR_OK;
+}
+
+Span span_of(const gdr_tensor *t, int64_t numel) {
+    Span s;
+    if (t && t->data && numel > 0) {
+        s.lo = reinterpret_cast<uintptr_t>(t->data);
+        s.hi = s.lo + static_cast<uintptr_t>(numel) * dtype_size(t->dtype);
+    }
+    return s;
+}
+
+bool overlap(const Span &a, const Span &b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool shape_is(const gdr_tensor *t, std::initializer_list<int64_t> s) {
+    int i = 0;
+    for (int64_t e : s)
+        if (t->shape[i++] != e) return false;
+    return true;
+}
+
+std::string shape_str(const gdr_tensor *t) {
+    std::string s = "[";
+    for (int i = 0; i < t->ndim; ++i) {
+        if (i) s += ", ";
+        s += std::to_string(static_cast<long long>(t->shape[i]));
+    }
+    return s + "]";
+}
+
+// Validates a forward call and fills the plan (shapes only, no device access).
+int plan_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
+             const gdr_tensor *beta, const gdr_tensor *cu, const gdr_tensor *h0, const gdr_tensor *o,
+             const gdr_tensor *ht, float scale, gdr_launch_plan *p) {
+    int64_t nq, nk, nv, ng, nb, no, ncu = 0, nh0 = 0, nht = 0;
+    int rc;
+    if ((rc = check_tensor(q, "q", 4, &nq, 16))) return rc;
+    if ((rc = check_tensor(k, "k", 4, &nk, 16))) return rc;
+    if ((rc = check_tensor(v, "v", 4, &nv, 16))) return rc;
+    if ((rc = check_tensor(g, "g", 3, &ng, 4))) return rc;
+    if ((rc = check_tensor(beta, "beta", 3, &nb, 4))) return rc;
+    if ((rc = check_tensor(o, "o", 4, &no, 16))) return rc;
+    if (cu && (rc = check_tensor(cu, "cu_seqlens", 1, &ncu, 4))) return rc;
+    if (h0 && (rc = check_tensor(h0, "h0", 4, &nh0, 4))) return rc;
+    if (ht && (rc = check_tensor(ht, "ht", 4, &nht, 4))) return rc;
+
+    if (q->dtype != GDR_BF16 && q->dtype != GDR_F32)
+        return fail(GDR_EDTYPE, "q: dtype must be bf16 or f32, got %s", dtype_name(q->dtype));
+    if (k->dtype != q->dtype || v->dtype != q->dtype || o->dtype != q->dtype)
+        return fail(GDR_EDTYPE, "q, k, v and o must share one dtype (q is %s)", dtype_name(q->dtype));
+    if (g->dtype != GDR_BF16 && g->dtype != GDR_F32)
+        return fail(GDR_EDTYPE, "g: dtype must be bf16 or f32, got %s", dtype_name(g->dtype));
+    if (beta->dtype != g->dtype) return fail(GDR_EDTYPE, "beta must have the dtype of g");
+    if (cu && cu->dtype != GDR_I32) return fail(GDR_EDTYPE, "cu_seqlens: dtype must be i32");
+    if (h0 && h0->dtype != GDR_F32) return fail(GDR_EDTYPE, "h0: dtype must be f32");
+    if (ht && ht->dtype != GDR_F32) return fail(GDR_EDTYPE, "ht: dtype must be f32");
+
+    const int64_t B = q->shape[0], T = q->shape[1], Hk = q->shape[2], dk = q->shape[3];
+    const int64_t Hv = v->shape[2], dv = v->shape[3];
+    if (!shape_is(k, {B, T, Hk, dk}))
+        return fail(GDR_ESHAPE, "k: shape %s must equal q's %s", shape_str(k).c_str(), shape_str(q).c_str());
+    if (v->shape[0] != B || v->shape[1] != T)
+        return fail(GDR_ESHAPE, "v: shape %s must be [B, T, Hv, dv] with q's B, T", shape_str(v).c_str());
+    if (!shape_is(o, {B, T, Hv, dv}))
+        return fail(GDR_ESHAPE, "o: shape %s must equal v's %s", shape_str(o).c_str(), shape_str(v).c_str());
+    if (!shape_is(g, {B, T, Hv}) || !shape_is(beta, {B, T, Hv}))
+        return fail(GDR_ESHAPE, "g and beta must be [B, T, Hv] = [%lld, %lld, %lld]", (long long)B,
+                    (long long)T, (long long)Hv);
+    if (dk != dv) return fail(GDR_ESHAPE, "dk (%lld) must equal dv (%lld)", (long long)dk, (long long)dv);
+    if (dk != 64 && dk != 128) return fail(GDR_ESHAPE, "head dim must be 64 or 128, got %lld", (long long)dk);
+    if (Hk < 1 || Hv < 1) return fail(GDR_ESHAPE, "head counts must be positive");
+    if (Hv % Hk != 0)
+        return fail(GDR_ESHAPE, "Hv (%lld) must be a multiple of Hk (%lld)", (long long)Hv, (long long)Hk);
+    if (Hv > 65536) return fail(GDR_ESHAPE, "too many v-heads");
+
+    int64_t N;
+    if (cu) {
+        if (B != 1) return fail(GDR_ESHAPE, "cu_seqlens requires B == 1 (got B = %lld)", (long long)B);
+        if (cu->shape[0] < 1) return fail(GDR_ESHAPE, "cu_seqlens must hold at least one offset");
+        N = cu->shape[0] - 1;
+    } else {
+        N = B;
+    }
+    if (h0 && !shape_is(h0, {N, Hv, dk, dv}))
+        return fail(GDR_ESHAPE, "h0: shape %s must be [N, Hv, dk, dv] = [%lld, %lld, %lld, %lld]",
+                    shape_str(h0).c_str(), (long long)N, (long long)Hv, (long long)dk, (long long)dv);
+    if (ht && !shape_is(ht, {N, Hv, dk, dv}))
+        return fail(GDR_ESHAPE, "ht: shape %s must be [N, Hv, dk, dv] = [%lld, %lld, %lld, %lld]",
+                    shape_str(ht).c_str(), (long long)N, (long long)Hv, (long long)dk, (long long)dv);
+    if (!std::isfinite(scale)) return fail(GDR_EINVAL, "scale must be finite");
+    if (N * Hv > 0x7FFFFFFFLL) return fail(GDR_ESHAPE, "N * Hv exceeds the launch grid limit");
+    if (B * T > 0x7FFFFFFFLL) return fail(GDR_ESHAPE, "B * T exceeds 2^31 - 1 tokens");
+
+    const Span so = span_of(o, no), sht = span_of(ht, nht);
+    const Span ins[] = {span_of(q, nq), span_of(k, nk), span_of(v, nv), span_of(g, ng),
+                        span_of(beta, nb), span_of(cu, ncu), span_of(h0, nh0)};
+    for (const Span &s : ins) {
+        if (overlap(so, s)) return fail(GDR_EALIAS, "o overlaps an input");
+        if (overlap(sht, s)) return fail(GDR_EALIAS, "ht overlaps an input");
+    }
+    if (overlap(so, sht)) return fail(GDR_EALIAS, "o and ht overlap");
+
+    std::memset(p, 0, sizeof(*p));
+    p->n_seq = N;
+    p->total_tokens = B * T;
+    p->nt_max = (B * T + gdr::kChunk - 1) / gdr::kChunk + N;
+    p->hk = static_cast<int32_t>(Hk);
+    p->hv = static_cast<int32_t>(Hv);
+    p->d = static_cast<int32_t>(dk);
+    p->in_dtype = q->dtype;
+    p->gate_dtype = g->dtype;
+    p->varlen = cu ? 1 : 0;
+    p->has_h0 = h0 ? 1 : 0;
+    p->has_ht = ht ? 1 : 0;
+    p->grid_fwd = N * Hv;
+    p->block_fwd = gdr::kFwdThreads;
+    p->lds_fwd = gdr::fwd_lds_bytes(static_cast<int>(dk));
+    p->workspace_bytes = cu ? 4 * N : 0;
+    return GDR_OK;
+}
+
+// gfx950 check for the current device, remembered per device ordinal.
+int check_device() {
+    static int state[64];   // 0 unknown, 1 gfx950, -1 other
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(GDR_EDEVICE, "hipGetDevice failed");
+    if (dev >= 0 && dev < 64 && state[dev] == 1) return GDR_OK;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return fail(GDR_EDEVICE, "hipGetDeviceProperties failed for device %d", dev);
+    const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev >= 0 && dev < 64) state[dev] = good ? 1 : -1;
+    if (!good) return fail(GDR_EDEVICE, "device %d is %s; this library is built for gfx950", dev, prop.gcnArchName);
+    return GDR_OK;
+}
+
+int launch_error(hipError_t e, const char *what) {
+    return fail(GDR_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_plan(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
+             const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
+             const gdr_tensor *o, const gdr_tensor *ht, float scale, gdr_launch_plan *plan) {
+    if (!plan) return fail(GDR_EINVAL, "plan is NULL");
+    const int rc = plan_fwd(q, k, v, g, beta, cu_seqlens, h0, o, ht, scale, plan);
+    return rc ? rc : ok();
+}
+
+int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
+                  const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
+                  const gdr_tensor *o, const gdr_tensor *ht, float scale, hipStream_t stream) {
+    gdr_launch_plan p;
+    int rc = plan_fwd(q, k, v, g, beta, cu_seqlens, h0, o, ht, scale, &p);
+    if (rc) return rc;
+    if ((rc = check_device())) return rc;
+    if (p.n_seq == 0 || p.total_tokens == 0) return ok();
+
+    gdr::FwdArgs a;
+    a.q = q->data;
+    a.k = k->data;
+    a.v = v->data;
+    a.g = g->data;
+    a.beta = beta->data;
+    a.cu = cu_seqlens ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
+    a.order = nullptr;
+    a.h0 = h0 ? static_cast<const float *>(h0->data) : nullptr;
+    a.o = o->data;
+    a.ht = ht ? static_cast<float *>(ht->data) : nullptr;
+    a.n_seq = p.n_seq;
+    a.seq_len = cu_seqlens ? p.total_tokens : q->shape[1];
+    a.total_tokens = p.total_tokens;
+    a.hk = p.hk;
+    a.hv = p.hv;
+    a.d = p.d;
+    a.in_bf16 = p.in_dtype == GDR_BF16;
+    a.gate_bf16 = p.gate_dtype == GDR_BF16;
+    a.scale = scale;
+
+    void *ws = nullptr;
+    if (cu_seqlens) {
+        hipError_t e = hipMallocAsync(&ws, static_cast<size_t>(p.workspace_bytes), stream);
+        if (e != hipSuccess) return fail(GDR_ENOMEM, "workspace of %lld bytes: %s",
+                                         (long long)p.workspace_bytes, hipGetErrorString(e));
+        int32_t *order = static_cast<int32_t *>(ws);
+        e = gdr::launch_prepare(a.cu, p.n_seq, nullptr, nullptr, 0, order, stream);
+        if (e != hipSuccess) {
+            (void)hipFreeAsync(ws, stream);
+            return launch_error(e, "chunk preparation kernel");
+        }
+        a.order = order;
+    }
+    hipError_t e = gdr::launch_fwd(a, stream);
+    if (ws) {
+        const hipError_t fe = hipFreeAsync(ws, stream);
+        if (e == hipSuccess && fe != hipSuccess) return launch_error(fe, "workspace release");
+    }
+    if (e != hipSuccess) return launch_error(e, "forward kernel");
+    return ok();
+}
+
+int gdr_prepare_chunks(const gdr_tensor *cu_seqlens, const gdr_tensor *chunk_offsets,
+                       const gdr_tensor *chunk_map, const gdr_tensor *seq_order, hipStream_t stream) {
+    int64_t ncu, noff, nmap = 0, nord = 0;
+    int rc;
+    if ((rc = check_tensor(cu_seqlens, "cu_seqlens", 1, &ncu, 4))) return rc;
+    if ((rc = check_tensor(chunk_offsets, "chunk_offsets", 1, &noff, 4))) return rc;
+    if (chunk_map && (rc = check_tensor(chunk_map, "chunk_map", 2, &nmap, 4))) return rc;
+    if (seq_order && (rc = check_tensor(seq_order, "seq_order", 1, &nord, 4))) return rc;
+    if (cu_seqlens->dtype != GDR_I32 || chunk_offsets->dtype != GDR_I32 ||
+        (chunk_map && chunk_map->dtype != GDR_I32) || (seq_order && seq_order->dtype != GDR_I32))
+        return fail(GDR_EDTYPE, "chunk preparation tensors must be i32");
+    if (ncu < 1) return fail(GDR_ESHAPE, "cu_seqlens must hold at least one offset");
+    const int64_t N = ncu - 1;
+    if (noff != N + 1) return fail(GDR_ESHAPE, "chunk_offsets must have N + 1 = %lld entries", (long long)(N + 1));
+    if (chunk_map && chunk_map->shape[1] != 2) return fail(GDR_ESHAPE, "chunk_map must be [nt_max, 2]");
+    if (seq_order && nord != N) return fail(GDR_ESHAPE, "seq_order must have N = %lld entries", (long long)N);
+    const Span in = span_of(cu_seqlens, ncu);
+    const Span outs[] = {span_of(chunk_offsets, noff), span_of(chunk_map, nmap), span_of(seq_order, nord)};
+    for (int i = 0; i < 3; ++i) {
+        if (overlap(in, outs[i])) return fail(GDR_EALIAS, "an output overlaps cu_seqlens");
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return fail(GDR_EALIAS, "outputs overlap");
+    }
+    if ((rc = check_device())) return rc;
+    const hipError_t e = gdr::launch_prepare(
+        static_cast<const int32_t *>(cu_seqlens->data), N, static_cast<int32_t *>(chunk_offsets->data),
+        chunk_map ? static_cast<int32_t *>(chunk_map->data) : nullptr, chunk_map ? chunk_map->shape[0] : 0,
+        seq_order ? static_cast<int32_t *>(seq_order->data) : nullptr, stream);
+    if (e != hipSuccess) return launch_error(e, "chunk preparation kernel");
+    return ok();
+}
+
+int gdr_chunk_local_cumsum(const gdr_tensor *g, const gdr_tensor *cu_seqlens, const gdr_tensor *G,
+                           hipStream_t stream) {
+    int64_t ng, ncu = 0, nG;
+    int rc;
+    if ((rc = check_tensor(g, "g", 3, &ng, 4))) return rc;
+    if (cu_seqlens && (rc = check_tensor(cu_seqlens, "cu_seqlens", 1, &ncu, 4))) return rc;
+    if ((rc = check_tensor(G, "G", 3, &nG, 4))) return rc;
+    if (g->dtype != GDR_BF16 && g->dtype != GDR_F32) return fail(GDR_EDTYPE, "g: dtype must be bf16 or f32");
+    if (G->dtype != GDR_F32) return fail(GDR_EDTYPE, "G: dtype must be f32");
+    if (cu_seqlens && cu_seqlens->dtype != GDR_I32) return fail(GDR_EDTYPE, "cu_seqlens: dtype must be i32");
+    const int64_t B = g->shape[0], T = g->shape[1], H = g->shape[2];
+    if (!shape_is(G, {B, T, H})) return fail(GDR_ESHAPE, "G must have the shape of g");
+    if (H > 0x7FFFFFFF) return fail(GDR_ESHAPE, "too many heads");
+    if (cu_seqlens && B != 1) return fail(GDR_ESHAPE, "cu_seqlens requires B == 1");
+    if (cu_seqlens && ncu < 1) return fail(GDR_ESHAPE, "cu_seqlens must hold at least one offset");
+    if (overlap(span_of(G, nG), span_of(g, ng)) || overlap(span_of(G, nG), span_of(cu_seqlens, ncu)))
+        return fail(GDR_EALIAS, "G overlaps an input");
+    if (B * T > 0x7FFFFFFFLL) return fail(GDR_ESHAPE, "B * T exceeds 2^31 - 1 tokens");
+    if ((rc = check_device())) return rc;
+    if (B * T == 0 || H == 0) return ok();
+    const int gate_bf16 = g->dtype == GDR_BF16;
+    if (!cu_seqlens) {
+        const hipError_t e = gdr::launch_cumsum(g->data, gate_bf16, nullptr, nullptr, 0, B, T, B * T,
+                                                static_cast<int32_t>(H), static_cast<float *>(G->data), stream);
+        if (e != hipSuccess) return launch_error(e, "cumsum kernel");
+        return ok();
+    }
+    const int64_t N = ncu - 1;
+    if (N == 0) return ok();
+    const int64_t nt_max = (T + gdr::kChunk - 1) / gdr::kChunk + N;
+    if (nt_max > 0x7FFFFFFFLL) return fail(GDR_ESHAPE, "too many chunks");
+    void *ws = nullptr;
+    const size_t bytes = static_cast<size_t>(nt_max) * 8;
+    hipError_t e = hipMallocAsync(&ws, bytes, stream);
+    if (e != hipSuccess) return fail(GDR_ENOMEM, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
+    int32_t *map = static_cast<int32_t *>(ws);
+    const int32_t *cu = static_cast<const int32_t *>(cu_seqlens->data);
+    e = gdr::launch_prepare(cu, N, nullptr, map, nt_max, nullptr, stream);
+    if (e == hipSuccess)
+        e = gdr::launch_cumsum(g->data, gate_bf16, cu, map, nt_max, 1, T, T, static_cast<int32_t>(H),
+                               static_cast<float *>(G->data), stream);
+    const hipError_t fe = hipFreeAsync(ws, stream);
+    if (e != hipSuccess) return launch_error(e, "chunk preparation / cumsum kernels");
+    if (fe != hipSuccess) return launch_error(fe, "workspace release");
+    return ok();
+}
+
+const char *gdr_last_error(void) { return g_last_error.c_str(); }
+
+int gdr_version(void) { return 10000; }
+
+int gdr_selftest_mfma(const uint16_t *a, const uint16_t *b, float *c, hipStream_t stream) {
+    if (!a || !b || !c) return fail(GDR_EINVAL, "selftest: NULL pointer");
+    int rc;
+    if ((rc = check_device())) return rc;
+    const hipError_t e = gdr::launch_selftest_mfma(a, b, c, stream);
+    if (e != hipSuccess) return launch_error(e, "selftest kernel");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal interface between the host API (gdr_api.cpp) and the kernels
+// (gdr_kernels.hip).  Not installed; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+// Everything a fused-forward launch needs, already validated on the host.
+struct FwdArgs {
+    const void *q, *k, *v, *g, *beta;
+    const int32_t *cu;      // NULL: fixed-length rows
+    const int32_t *order;   // NULL: natural order
+    const float *h0;        // NULL: zero state
+    void *o;
+    float *ht;              // NULL: not written
+    int64_t n_seq;          // N
+    int64_t seq_len;        // T per row when cu == NULL
+    int64_t total_tokens;   // rows of q/k/v/o (B * T); bounds every token index
+    int32_t hk, hv, d;
+    int32_t in_bf16;        // q/k/v/o dtype: 1 bf16, 0 f32
+    int32_t gate_bf16;      // g/beta dtype
+    float scale;
+};
+
+// Dynamic LDS bytes and threads per work-group of the fused forward kernel.
+int fwd_lds_bytes(int d);
+constexpr int kFwdThreads = 256;
+constexpr int kChunk = 64;
+
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
+
+hipError_t launch_prepare(const int32_t *cu, int64_t n_seq, int32_t *chunk_offsets,
+                          int32_t *chunk_map, int64_t nt_max, int32_t *order,
+                          hipStream_t stream);
+
+// chunk_map != NULL: varlen (grid nt_max); else n_rows fixed rows of seq_len tokens.
+hipError_t launch_cumsum(const void *g, int gate_bf16, const int32_t *cu,
+                         const int32_t *chunk_map, int64_t nt_max, int64_t n_rows,
+                         int64_t seq_len, int64_t total_tokens, int32_t heads, float *G,
+                         hipStream_t stream);
+
+hipError_t launch_selftest_mfma(const uint16_t *a, const uint16_t *b, float *c,
+                                hipStream_t stream);
+
+}  // namespace gdr

@@ -1,0 +1,193 @@
+/*
+ * gdr.h - C ABI of the chunked gated delta rule forward pass for AMD MI355X
+ * (gfx950, CDNA4).
+ *
+ * The operation is `chunk_gated_delta_rule`, named on the FlashQLA pages
+ * ("FlashQLA GDN backend produces different tokens from FLA Triton", Setup:
+ * chunk size 64, varlen API, initial and final state; "Findings from
+ * integrating FlashQLA's Blackwell GDN kernels into a JAX trainer", items 1-3).
+ * The pages name the op but not its formula; it is the gated delta rule of
+ * Gated DeltaNet.  Per sequence and v-head, with the state kept as H = S^T
+ * (dk x dv):
+ *
+ *     S_t = exp(g_t) * S_{t-1} * (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = scale * S_t q_t
+ *
+ * evaluated in chunks of 64 tokens (within a chunk: a 64x64 unit lower
+ * triangular solve into the WY form, then one state hand-off per chunk).
+ *
+ * Tensors are passed as plain descriptors (device pointer, dtype, shape and
+ * optional strides).  No torch or other framework type appears here.
+ *
+ * Ownership: the caller owns every buffer.  The library keeps no pointer after
+ * a call returns, never frees caller memory, and caches nothing keyed by a
+ * tensor's address or by a stream.  Work is enqueued on `stream` and the call
+ * returns without synchronising.  cu_seqlens is read only on the device, on
+ * every call (no host copy, no cache of derived chunk indices).
+ *
+ * Errors: every descriptor is validated on the host before anything is
+ * enqueued.  On a non-zero status nothing has been enqueued and no output has
+ * been touched; gdr_last_error() returns a message for the calling thread.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t; NULL means the default (null) stream. */
+struct ihipStream_t;
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum {
+    GDR_OK = 0,
+    GDR_EINVAL = -1,  /* NULL descriptor / data pointer, non-finite scale, bad argument */
+    GDR_ESHAPE = -2,  /* ranks or extents inconsistent with one another or unsupported */
+    GDR_EDTYPE = -3,  /* dtype not accepted for that argument */
+    GDR_ESTRIDE = -4, /* strides are not compact row-major */
+    GDR_EALIAS = -5,  /* an output overlaps an input or another output */
+    GDR_EDEVICE = -6, /* current device is not gfx950 or cannot be queried */
+    GDR_ELAUNCH = -7, /* a kernel launch or a stream-ordered allocation failed */
+    GDR_ENOMEM = -8   /* device memory for the call's workspace could not be obtained */
+} gdr_status;
+
+typedef enum { GDR_F32 = 0, GDR_BF16 = 1, GDR_I32 = 2 } gdr_dtype;
+
+/*
+ * A tensor descriptor.  `data` is a device pointer (may be NULL only when the
+ * tensor has no elements).  `shape` has `ndim` extents.  `strides` (in
+ * elements) may be NULL, meaning compact row-major, as DLPack defines it
+ * (the integration report, item 3, notes a generated stub that rejected NULL
+ * strides); non-NULL strides must equal the compact row-major ones.
+ */
+typedef struct {
+    void *data;
+    int32_t dtype;          /* a gdr_dtype value */
+    int32_t ndim;
+    const int64_t *shape;
+    const int64_t *strides; /* NULL = compact row-major */
+} gdr_tensor;
+
+/*
+ * gdr_chunk_fwd - forward pass of chunk_gated_delta_rule, chunk size 64.
+ *
+ *   q, k        [B, T, Hk, dk]   bf16 or f32 (q, k, v, o share one dtype)
+ *   v           [B, T, Hv, dv]
+ *   g           [B, T, Hv]       log-gate (natural log; decay is exp(g)), bf16 or f32
+ *   beta        [B, T, Hv]       same dtype as g
+ *   cu_seqlens  [N+1] int32, or NULL.  With cu_seqlens, B must be 1 and
+ *               sequence n owns tokens [cu[n], cu[n+1]).  Preconditions (not
+ *               checked on the host, since the content stays on the device):
+ *               cu[0] == 0, non-decreasing, cu[N] == T.  Repeated offsets are
+ *               length-0 ("ghost") segments, allowed anywhere: they read
+ *               nothing and write nothing (the integration report, item 2).
+ *               NULL means B fixed-length sequences of T tokens (N = B).
+ *   h0          [N, Hv, dk, dv] f32 initial state, or NULL for zero.
+ *   o           [B, T, Hv, dv]   output, dtype of q.  Rows of tokens outside
+ *               every segment are not written.
+ *   ht          [N, Hv, dk, dv] f32 final state, or NULL (not written).
+ *               Rows of ghost segments keep their previous bytes.
+ *   scale       output scale (callers usually pass dk^-0.5).
+ *   stream      HIP stream the work is enqueued on.
+ *
+ * Constraints: dk == dv, dk in {64, 128}; Hv % Hk == 0 and v-head h reads
+ * q/k head h / (Hv / Hk); all tensors compact row-major.  o and ht must not
+ * overlap any input or each other.  The current device must be gfx950.
+ *
+ * Numerics: bf16 MFMA operands (f32 inputs are rounded to bf16 when staged),
+ * fp32 accumulation, fp32 state; o is rounded once to its dtype (nearest-even).
+ * Results do not depend on scheduling: ghost padding and repeated calls are
+ * bitwise reproducible.
+ *
+ * Uses a small stream-ordered device workspace (hipMallocAsync / hipFreeAsync
+ * on `stream`, 4*N bytes) when cu_seqlens is given.
+ */
+int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
+                  const gdr_tensor *g, const gdr_tensor *beta, const gdr_tensor *cu_seqlens,
+                  const gdr_tensor *h0, const gdr_tensor *o, const gdr_tensor *ht,
+                  float scale, hipStream_t stream);
+
+/*
+ * Launch plan of a gdr_chunk_fwd call, computed from shapes only (no device
+ * access).  gdr_plan validates exactly like gdr_chunk_fwd and fills `plan`;
+ * it is what gdr_chunk_fwd launches.
+ */
+typedef struct {
+    int64_t n_seq;          /* N */
+    int64_t total_tokens;   /* B * T */
+    int64_t nt_max;         /* upper bound on the number of 64-token chunks: ceil(B*T/64) + N */
+    int32_t hk, hv, d;      /* heads and head dim (dk == dv == d) */
+    int32_t in_dtype;       /* gdr_dtype of q/k/v/o */
+    int32_t gate_dtype;     /* gdr_dtype of g/beta */
+    int32_t varlen;         /* 1 when cu_seqlens is given */
+    int32_t has_h0, has_ht;
+    int64_t grid_fwd;       /* work-groups of the fused kernel: N * Hv */
+    int32_t block_fwd;      /* threads per work-group */
+    int32_t lds_fwd;        /* bytes of LDS per work-group */
+    int64_t workspace_bytes;/* device workspace per call */
+} gdr_launch_plan;
+
+int gdr_plan(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
+             const gdr_tensor *g, const gdr_tensor *beta, const gdr_tensor *cu_seqlens,
+             const gdr_tensor *h0, const gdr_tensor *o, const gdr_tensor *ht, float scale,
+             gdr_launch_plan *plan);
+
+/*
+ * gdr_prepare_chunks - chunk indices derived from the content of cu_seqlens on
+ * the device (the integration report, item 1: the indices must follow the
+ * content of every call, never a cache keyed by tensor identity).
+ *
+ *   cu_seqlens     [N+1] int32 (device)
+ *   chunk_offsets  [N+1] int32 out: exclusive prefix sum of ceil(L_n / 64)
+ *   chunk_map      [nt_max, 2] int32 out, or NULL: entry i < NT holds
+ *                  (sequence n, chunk c within n); entries NT..nt_max-1 hold
+ *                  (-1, -1).  nt_max = shape[0] must be >= the true NT
+ *                  (ceil(T/64) + N always is); extra entries are marked.
+ *   seq_order      [N] int32 out, or NULL: sequence indices by length,
+ *                  longest first, ties by index (N > 8192: identity order).
+ *
+ * Work-list only: the forward pass uses seq_order to start long sequences
+ * first; results never depend on it.
+ */
+int gdr_prepare_chunks(const gdr_tensor *cu_seqlens, const gdr_tensor *chunk_offsets,
+                       const gdr_tensor *chunk_map, const gdr_tensor *seq_order,
+                       hipStream_t stream);
+
+/*
+ * gdr_chunk_local_cumsum - chunk-local inclusive prefix sum of the log-gate:
+ * G[t, h] = sum of g[s, h] for s from the start of t's 64-token chunk to t.
+ * Chunks restart at every sequence start.  Computed in fp32.
+ *
+ *   g           [B, T, H] bf16 or f32
+ *   cu_seqlens  [N+1] int32 or NULL (B fixed-length rows)
+ *   G           [B, T, H] f32 out (rows outside every segment not written)
+ *
+ * Uses a stream-ordered workspace for the chunk map (8 * nt_max + 4 * (N+1) bytes).
+ */
+int gdr_chunk_local_cumsum(const gdr_tensor *g, const gdr_tensor *cu_seqlens,
+                           const gdr_tensor *G, hipStream_t stream);
+
+/* Text of the last non-OK status returned on the calling thread ("" if none). */
+const char *gdr_last_error(void);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int gdr_version(void);
+
+/*
+ * gdr_selftest_mfma - diagnostic: runs one wave of each bf16 MFMA shape the
+ * kernels use on the given operands, so a test can check the lane layout the
+ * kernels assume.  a, b: 64 lanes x 8 bf16 (device); c: out, 2 x 64 lanes x 4
+ * f32 (first block: 16x16x32, second: 16x16x16 using the first 4 values of
+ * each lane).  Returns GDR_ELAUNCH on a launch failure.
+ */
+int gdr_selftest_mfma(const uint16_t *a, const uint16_t *b, float *c, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

@@ -1,0 +1,170 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and validates descriptors / plans launches without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_gated_delta_fwd_amd as gdr
+from chunked_gated_delta_fwd_amd import GDR_BF16, GDR_F32, GDR_I32, describe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdr.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return gdr.library()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(gdr_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert set(declared) == set(gdr.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.gdr_version() == 10000
+
+
+def test_exports_match_nm():
+    out = os.popen("nm -D --defined-only %s" % gdr.LIB_PATH).read()
+    syms = set(re.findall(r"\b(gdr_\w+)\b", out))
+    assert set(header_functions()) <= syms
+
+
+# --- planning / validation with fake addresses (never dereferenced) -------------
+
+BASE = 1 << 40
+
+
+class Alloc:
+    """Hands out disjoint, aligned fake device addresses."""
+
+    def __init__(self):
+        self.next = BASE
+
+    def __call__(self, dtype, shape, strides=None, misalign=0):
+        n = 1
+        for s in shape:
+            n *= s
+        addr = self.next + misalign
+        self.next += ((n * 4 + 4096) // 4096 + 1) * 4096
+        return describe(addr, dtype, shape, strides)
+
+
+def fwd_descs(B=1, T=256, Hk=2, Hv=4, d=128, dt=GDR_BF16, gdt=GDR_BF16, N=None, varlen=True,
+              h0=True, ht=True):
+    A = Alloc()
+    N = N if N is not None else (3 if varlen else B)
+    return dict(q=A(dt, [B, T, Hk, d]), k=A(dt, [B, T, Hk, d]), v=A(dt, [B, T, Hv, d]),
+                g=A(gdt, [B, T, Hv]), beta=A(gdt, [B, T, Hv]),
+                cu_seqlens=A(GDR_I32, [N + 1]) if varlen else None,
+                h0=A(GDR_F32, [N, Hv, d, d]) if h0 else None, o=A(dt, [B, T, Hv, d]),
+                ht=A(GDR_F32, [N, Hv, d, d]) if ht else None)
+
+
+def test_plan_varlen(lib):
+    p = gdr.plan(**fwd_descs(T=1000, N=5), scale=0.1)
+    assert p["n_seq"] == 5 and p["hv"] == 4 and p["hk"] == 2 and p["d"] == 128
+    assert p["nt_max"] == (1000 + 63) // 64 + 5
+    assert p["grid_fwd"] == 5 * 4 and p["block_fwd"] == 256
+    assert 0 < p["lds_fwd"] <= 160 * 1024
+    assert p["workspace_bytes"] == 4 * 5 and p["varlen"] == 1
+
+
+def test_plan_fixed_and_d64(lib):
+    p = gdr.plan(**fwd_descs(B=4, T=512, Hk=16, Hv=16, d=64, dt=GDR_F32, gdt=GDR_F32, varlen=False))
+    assert p["n_seq"] == 4 and p["workspace_bytes"] == 0 and p["varlen"] == 0 and p["d"] == 64
+    assert p["lds_fwd"] < gdr.plan(**fwd_descs())["lds_fwd"]
+
+
+def test_null_strides_equal_compact_strides(lib):
+    d = fwd_descs(B=1, T=64, Hk=1, Hv=1)
+    A = Alloc()
+    d["q"] = A(GDR_BF16, [1, 64, 1, 128], strides=[64 * 128, 128, 128, 1])
+    gdr.plan(**d)   # explicit compact strides accepted
+    d["q"] = A(GDR_BF16, [1, 64, 1, 128], strides=[64 * 128, 256, 128, 1])
+    with pytest.raises(gdr.GdrError) as e:
+        gdr.plan(**d)
+    assert e.value.status == -4 and "q" in e.value.message
+
+
+@pytest.mark.parametrize("mutate,status,text", [
+    (lambda d, A: d.update(q=None), -1, "q: descriptor is NULL"),
+    (lambda d, A: d.update(k=A(GDR_BF16, [1, 256, 3, 128])), -2, "k: shape"),
+    (lambda d, A: d.update(v=A(GDR_F32, [1, 256, 4, 128])), -3, "share one dtype"),
+    (lambda d, A: d.update(g=A(GDR_I32, [1, 256, 4])), -3, "g: dtype"),
+    (lambda d, A: d.update(beta=A(GDR_F32, [1, 256, 4])), -3, "beta"),
+    (lambda d, A: d.update(o=A(GDR_BF16, [1, 256, 4, 64])), -2, "o: shape"),
+    (lambda d, A: d.update(g=A(GDR_BF16, [1, 255, 4])), -2, "g and beta"),
+    (lambda d, A: d.update(h0=A(GDR_F32, [2, 4, 128, 128])), -2, "h0: shape"),
+    (lambda d, A: d.update(ht=A(GDR_BF16, [3, 4, 128, 128])), -3, "ht: dtype"),
+    (lambda d, A: d.update(cu_seqlens=A(GDR_F32, [4])), -3, "cu_seqlens"),
+    (lambda d, A: d.update(cu_seqlens=A(GDR_I32, [0])), -2, "at least one offset"),
+    (lambda d, A: d.update(q=A(GDR_BF16, [1, 256, 2, 128], misalign=2)), -1, "aligned"),
+    (lambda d, A: d.update(o=describe(d["q"].t.data + 256, GDR_BF16, [1, 256, 4, 128])), -5,
+     "o overlaps"),
+    (lambda d, A: d.update(ht=d["h0"]), -5, "ht overlaps"),
+])
+def test_rejections(lib, mutate, status, text):
+    d = fwd_descs()
+    mutate(d, Alloc())
+    with pytest.raises(gdr.GdrError) as e:
+        gdr.plan(**d)
+    assert e.value.status == status, e.value
+    assert text in e.value.message, e.value.message
+
+
+def test_rejects_unsupported_heads(lib):
+    with pytest.raises(gdr.GdrError) as e:
+        gdr.plan(**fwd_descs(Hk=3, Hv=4))
+    assert "multiple of Hk" in e.value.message
+    with pytest.raises(gdr.GdrError) as e:
+        gdr.plan(**fwd_descs(d=96))
+    assert "64 or 128" in e.value.message
+    d = fwd_descs(B=2, varlen=True)
+    with pytest.raises(gdr.GdrError) as e:
+        gdr.plan(**d)
+    assert "B == 1" in e.value.message
+
+
+def test_rejects_nonfinite_scale(lib):
+    with pytest.raises(gdr.GdrError) as e:
+        gdr.plan(**fwd_descs(), scale=float("nan"))
+    assert e.value.status == -1
+
+
+def test_empty_inputs_plan(lib):
+    p = gdr.plan(**fwd_descs(T=0, N=2))
+    assert p["total_tokens"] == 0 and p["nt_max"] == 2
+
+
+def test_error_text_is_per_call(lib):
+    with pytest.raises(gdr.GdrError):
+        gdr.plan(**fwd_descs(d=96))
+    gdr.plan(**fwd_descs())
+    assert lib.gdr_last_error() == b""
+
+
+def test_chunk_fwd_without_gpu_reports_device(lib):
+    """On a machine without a usable gfx950 device the call fails cleanly
+    before enqueuing anything."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except Exception:
+        pass
+    d = fwd_descs()
+    rc = lib.gdr_chunk_fwd(*[None if d[n] is None else d[n].ref for n in
+                             ("q", "k", "v", "g", "beta", "cu_seqlens", "h0", "o", "ht")],
+                           ctypes.c_float(1.0), None)
+    assert rc == -6, (rc, lib.gdr_last_error())
