@@ -31,10 +31,13 @@
 //   B fragment (k x cols):  col l16, k = 4*lq + r
 //   C/D tile:               col l16, row = 4*lq + r
 // so an MFMA result tile is directly the B fragment of the next product over
-// its rows.  A 16x16x32 instruction is used as two 16x16x16 products fused:
-// lane slots 0-3 carry one K16 block and slots 4-7 the next one, the same
-// pairing on both operands (the instruction's own k numbering of the slots
-// does not matter because it is shared by A and B).
+// its rows.  Every product runs on the 16x16x32 instruction used as two
+// 16x16x16 products fused: lane slots 0-3 carry one K16 block and slots 4-7
+// the next one, the same pairing on both operands (the instruction's own k
+// numbering of the slots does not matter because it is shared by A and B).
+// A lone K16 block is zero-padded rather than issued as a 16x16x16
+// instruction: chaining a 16x16x16 accumulation on the result of a 16x16x32
+// one was observed to read a partly written accumulator on gfx950.
 #include "gdr_internal.h"
 
 #include <stdint.h>
@@ -53,6 +56,14 @@ constexpr float kLog2e = 1.44269504088896340736f;
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// one K16 block on the 16x16x32 instruction, upper slots zero
+__device__ __forceinline__ f32x4 mfma16z(bf16x4 a, bf16x4 b, f32x4 c) {
+    const bf16x4 z = {};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(a, z, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                   __builtin_shufflevector(b, z, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                   c, 0, 0, 0);
+}
+// the 16x16x16 instruction, for the lane-layout self test only
 __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
                                                      __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
@@ -376,12 +387,12 @@ __global__ void __launch_bounds__(kFwdThreads, 1) gdr_fwd_kernel(FwdArgs a) {
                 const int c = blk - 1;
                 const bf16x4 af = cvt4(-*reinterpret_cast<const f32x4 *>(arow + 16 * c));
 #pragma unroll
-                for (int tt = 0; tt < 2 * NTW; ++tt) R[tt] = mfma16(af, Xb[c][tt], R[tt]);
+                for (int tt = 0; tt < 2 * NTW; ++tt) R[tt] = mfma16z(af, Xb[c][tt], R[tt]);
             }
             const bf16x4 df = cvt4(*reinterpret_cast<const f32x4 *>(sDi + (16 * blk + l16) * PD + 4 * lq));
 #pragma unroll
             for (int tt = 0; tt < 2 * NTW; ++tt) {
-                const f32x4 X = mfma16(df, cvt4(R[tt]), zero4());
+                const f32x4 X = mfma16z(df, cvt4(R[tt]), zero4());
                 Xb[blk][tt] = cvt4(X);
                 if (tt < NTW) {
                     const int col = colw + 16 * tt + l16;
@@ -449,7 +460,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) gdr_fwd_kernel(FwdArgs a) {
             if ((blk & 1) == 0) {
                 const bf16x4 pf = ld4(pp + 16 * blk);
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) oacc[nt] = mfma16(pf, Vb[blk][nt], oacc[nt]);
+                for (int nt = 0; nt < NTW; ++nt) oacc[nt] = mfma16z(pf, Vb[blk][nt], oacc[nt]);
             }
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
