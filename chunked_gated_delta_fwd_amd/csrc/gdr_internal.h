@@ -24,9 +24,10 @@ struct FwdArgs {
     float scale;
 };
 
-// Dynamic LDS bytes and threads per work-group of the fused forward kernel.
+// Dynamic LDS bytes and threads per work-group of the fused forward kernel
+// (d / 16 waves: one per 16 dv columns of the state).
 int fwd_lds_bytes(int d);
-constexpr int kFwdThreads = 256;
+constexpr int fwd_threads(int d) { return 4 * d; }
 constexpr int kChunk = 64;
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);

@@ -137,55 +137,72 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 }
 
 // --------------------------------------------------------------------------
-// Fused forward: LDS layout of one work-group (bf16 buffers hold raw bits).
+// Fused forward.  One work-group of D/16 waves (8 at D = 128: two per SIMD)
+// walks one (sequence, v-head) through its chunks in order; wave w owns the
+// 16 dv columns 16w..16w+15 of the state.  The chunk loop is software-pipelined:
+// iteration c runs the state-dependent chain of chunk c (Vnew, output, state
+// update) next to the state-independent preparation of chunk c+1 (staging,
+// K K^T and Q K^T, diagonal-block inverses, WY solve) and prefetches chunk c+2
+// from HBM into registers.  LDS buffers both streams touch are doubled.
+//
+// Per iteration (4 barriers):
+//   P1  stage c+1 from registers, prefetch c+2    | Vnew_c = U_c - W_c H
+//   P2  K K^T -> A, Q K^T -> P  (c+1)             | O_c^T = e^G (H^T Q^T) + Vnew^T P^T, store
+//   P3  16x16 diagonal inverses (c+1, waves 0-3) | H <- e^{G_L} H + K^T diag(e^{G_L-G}) Vnew_c
+//   P4  WY solve -> -W (LDS), U (registers) (c+1) | H^T Q^T for chunk c+1
 // --------------------------------------------------------------------------
 template <int D>
 struct FwdLds {
-    static constexpr int PK = D + 8;   // pitch of [64][D] row-major buffers (q, k, -W)
-    static constexpr int PT = C + 8;   // pitch of [D][64] transposed buffers (k^T, v^T)
-    static constexpr int PP = C + 8;   // pitch of P [64][64]
-    static constexpr int PA = C + 4;   // pitch of A [64][64] (f32)
-    static constexpr int PD = 20;      // pitch of the four 16x16 diagonal inverses (f32)
+    static constexpr int PK = D + 8;    // [64][D] row-major bf16: q, k, -W
+    static constexpr int PT = C + 8;    // [D][64] transposed bf16: k^T (two buffers), v^T
+    static constexpr int PP = C + 8;    // [64][64] bf16: P (two buffers), -A off the diagonal
+    static constexpr int PAT = 20;      // [4][16][16] f32: diagonal blocks of A, transposed
+    static constexpr int PDI = 24;      // [4][16][16] bf16: inverses of the diagonal blocks
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + C * PK * 2;
     static constexpr int oW = oK + C * PK * 2;
     static constexpr int oKT = oW + C * PK * 2;
-    static constexpr int oVT = oKT + D * PT * 2;
+    static constexpr int oVT = oKT + 2 * D * PT * 2;
     static constexpr int oP = oVT + D * PT * 2;
-    static constexpr int oA = oP + C * PP * 2;
-    static constexpr int oDi = oA + C * PA * 4;
-    static constexpr int oS = oDi + 4 * 16 * PD * 4;   // six [64] f32 vectors
-    static constexpr int bytes = oS + 6 * C * 4;
+    static constexpr int oAo = oP + 2 * C * PP * 2;
+    static constexpr int oAT = oAo + C * PP * 2;
+    static constexpr int oDi = oAT + 4 * 16 * PAT * 4;
+    static constexpr int oS = oDi + 4 * 16 * PDI * 2;
+    // f32 vectors of 64: G*log2(e), beta, beta*e^G, e^G (x2), e^{G_L-G} (x2); then e^{G_L} (x2)
+    static constexpr int bytes = oS + 7 * C * 4 + 16;
 };
 
-// Lower-triangular 16x16 tile pairs (ib >= jb) of a 64x64 chunk matrix.
-__constant__ int8_t kTileI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int8_t kTileJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int D, bool IN_BF16, bool GATE_BF16>
-__global__ void __launch_bounds__(kFwdThreads, 1) gdr_fwd_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(4 * D) gdr_fwd_kernel(FwdArgs a) {
     using Ly = FwdLds<D>;
-    constexpr int PK = Ly::PK, PT = Ly::PT, PP = Ly::PP, PA = Ly::PA, PD = Ly::PD;
-    constexpr int DW = D / 4;      // dv columns owned by each of the 4 waves
+    constexpr int PK = Ly::PK, PT = Ly::PT, PP = Ly::PP, PAT = Ly::PAT, PDI = Ly::PDI;
+    constexpr int NW = D / 16;     // waves per work-group
+    constexpr int DW = 16;         // dv columns owned by each wave
     constexpr int NTW = DW / 16;   // 16-wide column tiles per wave
     constexpr int KB = D / 16;     // K16 blocks over the head dim
-    static_assert(KB % 2 == 0, "head dim must be a multiple of 32");
+    constexpr int FG = D / 8;      // 8-element feature groups per row (staging)
+    constexpr int TG = 64 * NW / FG;
+    constexpr int TPT = C / TG;    // tokens staged per thread
+    static_assert(KB % 2 == 0 && (TPT == 2 || TPT == 4), "unsupported head dim");
 
     extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + Ly::oQ);
-    uint16_t *sK = reinterpret_cast<uint16_t *>(smem + Ly::oK);
-    uint16_t *sW = reinterpret_cast<uint16_t *>(smem + Ly::oW);
-    uint16_t *sKT = reinterpret_cast<uint16_t *>(smem + Ly::oKT);
-    uint16_t *sVT = reinterpret_cast<uint16_t *>(smem + Ly::oVT);
-    uint16_t *sP = reinterpret_cast<uint16_t *>(smem + Ly::oP);
-    float *sA = reinterpret_cast<float *>(smem + Ly::oA);
-    float *sDi = reinterpret_cast<float *>(smem + Ly::oDi);
-    float *sG2 = reinterpret_cast<float *>(smem + Ly::oS);   // G * log2(e)
-    float *sB = sG2 + C;                                     // beta
-    float *sBG = sB + C;                                     // beta * e^G
-    float *sGam = sBG + C;                                   // e^G
-    float *sDec = sGam + C;                                  // e^{G_last - G}
-    float *sMisc = sDec + C;                                 // [0] = e^{G_last}
+    uint16_t *const sQ = reinterpret_cast<uint16_t *>(smem + Ly::oQ);
+    uint16_t *const sK = reinterpret_cast<uint16_t *>(smem + Ly::oK);
+    uint16_t *const sW = reinterpret_cast<uint16_t *>(smem + Ly::oW);
+    uint16_t *const sKT0 = reinterpret_cast<uint16_t *>(smem + Ly::oKT);
+    uint16_t *const sVT = reinterpret_cast<uint16_t *>(smem + Ly::oVT);
+    uint16_t *const sP0 = reinterpret_cast<uint16_t *>(smem + Ly::oP);
+    uint16_t *const sAo = reinterpret_cast<uint16_t *>(smem + Ly::oAo);
+    float *const sAT = reinterpret_cast<float *>(smem + Ly::oAT);
+    uint16_t *const sDi = reinterpret_cast<uint16_t *>(smem + Ly::oDi);
+    float *const sG2 = reinterpret_cast<float *>(smem + Ly::oS);   // chunk being prepared
+    float *const sB = sG2 + C;
+    float *const sBG = sG2 + 2 * C;
+    float *const sGam0 = sG2 + 3 * C;                               // [2][64]
+    float *const sDec0 = sG2 + 5 * C;                               // [2][64]
+    float *const sGL = sG2 + 7 * C;                                 // [2]
 
     // ---- work item: (sequence n, v-head h), longest sequences first
     const int64_t item = blockIdx.x;
@@ -211,10 +228,25 @@ __global__ void __launch_bounds__(kFwdThreads, 1) gdr_fwd_kernel(FwdArgs a) {
     const int wave = tid >> 6;
     const int l16 = lane & 15;
     const int lq = lane >> 4;
-    const int colw = wave * DW;   // first dv column of this wave
+    const int colw = wave * DW;         // first dv (and dk, in the solve) column of this wave
+    const int fg = tid % FG, tg = tid / FG;
+    const int f0 = fg * 8;
+    const int64_t nch = (eos - bos + C - 1) / C;
 
-    // ---- fp32 state in C layout: tile (kb, nt) holds rows dk 16kb+4lq+r, column dv colw+16nt+l16
-    f32x4 hs[KB][NTW];
+    auto chunk_len = [&](int64_t c) -> int {
+        const int64_t r = eos - (bos + c * C);
+        return r < C ? static_cast<int>(r) : C;
+    };
+
+    // ---- registers carried across phases
+    f32x4 hs[KB][NTW];        // state tile (kb, nt): rows dk 16kb+4lq+r, column dv colw+16nt+l16
+    bf16x4 hb[KB][NTW];       // its bf16 copy (B operand of W H, A operand of H^T Q^T)
+    f32x4 U[4][NTW];          // U of the chunk the chain works on, C layout (rows tokens)
+    f32x4 Ot[4][NTW];         // O^T accumulators: rows dv colw+16nt+4lq+r, column token 16blk+l16
+    f32x4 Vn[4][NTW];         // Vnew of the chunk the chain works on
+    uint4 pq[TPT], pk[TPT], pv[TPT];   // prefetched rows of the next chunk to stage
+    float pg = 0.f, pb = 0.f;          // prefetched gate and beta (wave 0, lane = token)
+
     const int64_t sbase = (n * a.hv + h) * static_cast<int64_t>(D) * D;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -224,143 +256,154 @@ __global__ void __launch_bounds__(kFwdThreads, 1) gdr_fwd_kernel(FwdArgs a) {
             for (int r = 0; r < 4; ++r)
                 hs[kb][nt][r] = a.h0 ? a.h0[sbase + (16 * kb + 4 * lq + r) * D + colw + 16 * nt + l16] : 0.f;
 
-    const int64_t nchunks = (eos - bos + C - 1) / C;
-    for (int64_t ci = 0; ci < nchunks; ++ci) {
-        const int64_t t0 = bos + ci * C;
-        const int L = static_cast<int>((eos - t0) < C ? (eos - t0) : C);
-
-        // ---- stage q, k (row-major) and k, v (transposed) of this chunk in LDS
-        {
-            constexpr int FG = D / 8;        // 8-element feature groups per row
-            constexpr int TG = 256 / FG;     // token groups
-            constexpr int TPT = C / TG;      // tokens per thread (4 at D=128, 2 at D=64)
-            const int fg = tid % FG, tg = tid / FG;
-            const int f0 = fg * 8;
-            uint4 qv[TPT], kv[TPT], vv[TPT];
+    // HBM -> registers (rows past the segment end are zero; padding is exactly neutral)
+    auto load_chunk = [&](int64_t c) {
+        const int64_t t0 = bos + c * C;
+        const int L = chunk_len(c);
 #pragma unroll
-            for (int j = 0; j < TPT; ++j) {
-                const int t = tg * TPT + j;
-                if (t < L) {
-                    const int64_t tok = t0 + t;
-                    qv[j] = load8<IN_BF16>(a.q, (tok * a.hk + hk) * D + f0);
-                    kv[j] = load8<IN_BF16>(a.k, (tok * a.hk + hk) * D + f0);
-                    vv[j] = load8<IN_BF16>(a.v, (tok * a.hv + h) * D + f0);
-                } else {
-                    qv[j] = kv[j] = vv[j] = make_uint4(0, 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < TPT; ++j) {
-                const int t = tg * TPT + j;
-                *reinterpret_cast<uint4 *>(sQ + t * PK + f0) = qv[j];
-                *reinterpret_cast<uint4 *>(sK + t * PK + f0) = kv[j];
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if constexpr (TPT == 4) {
-                    uint2 kt, vt;
-                    kt.x = elem8(kv[0], e) | (static_cast<uint32_t>(elem8(kv[1], e)) << 16);
-                    kt.y = elem8(kv[2], e) | (static_cast<uint32_t>(elem8(kv[3], e)) << 16);
-                    vt.x = elem8(vv[0], e) | (static_cast<uint32_t>(elem8(vv[1], e)) << 16);
-                    vt.y = elem8(vv[2], e) | (static_cast<uint32_t>(elem8(vv[3], e)) << 16);
-                    *reinterpret_cast<uint2 *>(sKT + (f0 + e) * PT + tg * TPT) = kt;
-                    *reinterpret_cast<uint2 *>(sVT + (f0 + e) * PT + tg * TPT) = vt;
-                } else {
-                    static_assert(TPT == 2, "unsupported head dim");
-                    *reinterpret_cast<uint32_t *>(sKT + (f0 + e) * PT + tg * TPT) =
-                        elem8(kv[0], e) | (static_cast<uint32_t>(elem8(kv[1], e)) << 16);
-                    *reinterpret_cast<uint32_t *>(sVT + (f0 + e) * PT + tg * TPT) =
-                        elem8(vv[0], e) | (static_cast<uint32_t>(elem8(vv[1], e)) << 16);
-                }
+        for (int j = 0; j < TPT; ++j) {
+            const int t = tg * TPT + j;
+            if (t < L) {
+                const int64_t tok = t0 + t;
+                pq[j] = load8<IN_BF16>(a.q, (tok * a.hk + hk) * D + f0);
+                pk[j] = load8<IN_BF16>(a.k, (tok * a.hk + hk) * D + f0);
+                pv[j] = load8<IN_BF16>(a.v, (tok * a.hv + h) * D + f0);
+            } else {
+                pq[j] = pk[j] = pv[j] = make_uint4(0, 0, 0, 0);
             }
         }
-        // ---- gates: chunk-local prefix sum of g, one token per lane of wave 0
         if (wave == 0) {
-            float gv = 0.f, bv = 0.f;
+            pg = pb = 0.f;
             if (lane < L) {
                 const int64_t gi = (t0 + lane) * a.hv + h;
-                gv = load_scalar<GATE_BF16>(a.g, gi);
-                bv = load_scalar<GATE_BF16>(a.beta, gi);
+                pg = load_scalar<GATE_BF16>(a.g, gi);
+                pb = load_scalar<GATE_BF16>(a.beta, gi);
             }
-            const float G2 = wave_inclusive_scan(gv, lane) * kLog2e;
-            const float Glast2 = __shfl(G2, 63, 64);   // padding has g = 0: equals G at L-1
-            const float gam = exp2f(G2);
-            sG2[lane] = G2;
-            sB[lane] = bv;
-            sBG[lane] = bv * gam;
-            sGam[lane] = gam;
-            sDec[lane] = exp2f(Glast2 - G2);
-            if (lane == 0) sMisc[0] = exp2f(Glast2);
         }
-        __syncthreads();
+    };
 
-        // ---- A = strictly lower part of diag(b) (e^{G_i - G_j}) o K K^T   (f32, LDS)
-        for (int ti = wave; ti < 10; ti += 4) {
-            const int ib = kTileI[ti], jb = kTileJ[ti];
-            f32x4 acc = zero4();
+    // registers -> LDS (q, k row-major; k, v transposed) and the gate vectors
+    auto stage_chunk = [&](int par) {
+        uint16_t *kt = sKT0 + par * D * PT;
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) {
+            const int t = tg * TPT + j;
+            *reinterpret_cast<uint4 *>(sQ + t * PK + f0) = pq[j];
+            *reinterpret_cast<uint4 *>(sK + t * PK + f0) = pk[j];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if constexpr (TPT == 4) {
+                uint2 k2, v2;
+                k2.x = elem8(pk[0], e) | (static_cast<uint32_t>(elem8(pk[1], e)) << 16);
+                k2.y = elem8(pk[2], e) | (static_cast<uint32_t>(elem8(pk[3], e)) << 16);
+                v2.x = elem8(pv[0], e) | (static_cast<uint32_t>(elem8(pv[1], e)) << 16);
+                v2.y = elem8(pv[2], e) | (static_cast<uint32_t>(elem8(pv[3], e)) << 16);
+                *reinterpret_cast<uint2 *>(kt + (f0 + e) * PT + tg * TPT) = k2;
+                *reinterpret_cast<uint2 *>(sVT + (f0 + e) * PT + tg * TPT) = v2;
+            } else {
+                *reinterpret_cast<uint32_t *>(kt + (f0 + e) * PT + tg * TPT) =
+                    elem8(pk[0], e) | (static_cast<uint32_t>(elem8(pk[1], e)) << 16);
+                *reinterpret_cast<uint32_t *>(sVT + (f0 + e) * PT + tg * TPT) =
+                    elem8(pv[0], e) | (static_cast<uint32_t>(elem8(pv[1], e)) << 16);
+            }
+        }
+        if (wave == 0) {
+            const float G2 = wave_inclusive_scan(pg, lane) * kLog2e;
+            const float GL2 = __shfl(G2, 63, 64);   // padding has g = 0: equals G at the last token
+            const float gam = fast_exp2(G2);
+            sG2[lane] = G2;
+            sB[lane] = pb;
+            sBG[lane] = pb * gam;
+            sGam0[par * C + lane] = gam;
+            sDec0[par * C + lane] = fast_exp2(GL2 - G2);
+            if (lane == 0) sGL[par] = fast_exp2(GL2);
+        }
+    };
+
+    // K K^T -> A (diagonal blocks f32 transposed; other blocks -A in bf16),
+    // Q K^T -> P; 20 lower-triangular 16x16 tiles spread over the waves
+    auto prep_kq = [&](int par) {
+        uint16_t *sPp = sP0 + par * C * PP;
+#pragma unroll
+        for (int s = 0; s < (20 + NW - 1) / NW; ++s) {
+            const int ti = wave + NW * s;
+            if (ti >= 20) break;
+            const bool qk = ti >= 10;
+            const int t = qk ? ti - 10 : ti;
+            const int ib = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+            const int jb = t - ib * (ib + 1) / 2;
             const uint16_t *pa = sK + (16 * jb + l16) * PK + 4 * lq;
-            const uint16_t *pb = sK + (16 * ib + l16) * PK + 4 * lq;
+            const uint16_t *pbp = (qk ? sQ : sK) + (16 * ib + l16) * PK + 4 * lq;
+            f32x4 acc = zero4();
 #pragma unroll
             for (int p = 0; p < KB / 2; ++p)
                 acc = mfma32(cat(ld4(pa + 32 * p), ld4(pa + 32 * p + 16)),
-                             cat(ld4(pb + 32 * p), ld4(pb + 32 * p + 16)), acc);
-            // tile element (row j, col i) = k_j . k_i
-            const int i = 16 * ib + l16;
-            const float gi = sG2[i], bi = sB[i];
-            f32x4 out;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 16 * jb + 4 * lq + r;
-                out[r] = (i > j) ? bi * exp2f(gi - sG2[j]) * acc[r] : 0.f;
-            }
-            *reinterpret_cast<f32x4 *>(sA + i * PA + 16 * jb + 4 * lq) = out;
-        }
-        __syncthreads();
-
-        if (wave == 0) {
-            // ---- inverses of the four 16x16 unit lower diagonal blocks of I + A
-            // lane = (block, column): forward substitution down the column
-            const int blk = lane >> 4, c = l16;
-            const float *Ab = sA + (16 * blk) * PA + 16 * blk;
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = (i == c) ? 1.f : 0.f;
-#pragma unroll
-                for (int j = 0; j < i; ++j) s -= Ab[i * PA + j] * x[j];
-                x[i] = s;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sDi[(16 * blk + i) * PD + c] = x[i];
-        } else {
-            // ---- P = lower part of (e^{G_i - G_j}) o Q K^T   (bf16, LDS)
-            for (int ti = wave - 1; ti < 10; ti += 3) {
-                const int ib = kTileI[ti], jb = kTileJ[ti];
-                f32x4 acc = zero4();
-                const uint16_t *pa = sK + (16 * jb + l16) * PK + 4 * lq;   // keys
-                const uint16_t *pb = sQ + (16 * ib + l16) * PK + 4 * lq;   // queries
-#pragma unroll
-                for (int p = 0; p < KB / 2; ++p)
-                    acc = mfma32(cat(ld4(pa + 32 * p), ld4(pa + 32 * p + 16)),
-                                 cat(ld4(pb + 32 * p), ld4(pb + 32 * p + 16)), acc);
-                // tile element (row j = key, col i = query) = k_j . q_i
+                             cat(ld4(pbp + 32 * p), ld4(pbp + 32 * p + 16)), acc);
+            if (qk) {
+                // element (row key j = 16jb+4lq+r, column query i = 16ib+l16) = k_j . q_i
                 const int i = 16 * ib + l16;
                 const float gi = sG2[i];
+                const f32x4 gj = *reinterpret_cast<const f32x4 *>(sG2 + 16 * jb + 4 * lq);
                 f32x4 out;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * jb + 4 * lq + r;
-                    out[r] = (i >= j) ? exp2f(gi - sG2[j]) * acc[r] : 0.f;
+                    const bool keep = i >= 16 * jb + 4 * lq + r;
+                    out[r] = keep ? fast_exp2(gi - gj[r]) * acc[r] : 0.f;
                 }
-                *reinterpret_cast<bf16x4 *>(sP + i * PP + 16 * jb + 4 * lq) = cvt4(out);
+                *reinterpret_cast<bf16x4 *>(sPp + i * PP + 16 * jb + 4 * lq) = cvt4(out);
+            } else if (ib == jb) {
+                // symmetric tile: element (row i = 16ib+4lq+r, column j = 16ib+l16) = k_i . k_j
+                const int j = 16 * jb + l16;
+                const float gj = sG2[j];
+                const f32x4 gi = *reinterpret_cast<const f32x4 *>(sG2 + 16 * ib + 4 * lq);
+                const f32x4 bi = *reinterpret_cast<const f32x4 *>(sB + 16 * ib + 4 * lq);
+                f32x4 out;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool keep = 16 * ib + 4 * lq + r > j;
+                    out[r] = keep ? bi[r] * fast_exp2(gi[r] - gj) * acc[r] : 0.f;
+                }
+                *reinterpret_cast<f32x4 *>(sAT + (16 * ib + l16) * PAT + 4 * lq) = out;
+            } else {
+                // element (row j = 16jb+4lq+r, column i = 16ib+l16) = k_j . k_i, i > j
+                const int i = 16 * ib + l16;
+                const float gi = sG2[i], bi = sB[i];
+                const f32x4 gj = *reinterpret_cast<const f32x4 *>(sG2 + 16 * jb + 4 * lq);
+                f32x4 out;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[r] = -bi * fast_exp2(gi - gj[r]) * acc[r];
+                *reinterpret_cast<bf16x4 *>(sAo + i * PP + 16 * jb + 4 * lq) = cvt4(out);
             }
         }
-        __syncthreads();
+    };
 
-        // ---- WY solve by 16-row blocks: X_a = D_a (B_a - sum_{c<a} A_ac X_c)
-        // tiles tt < NTW: W columns (dk) colw+16tt..; tt >= NTW: U columns (dv)
+    // inverses of the four 16x16 unit lower diagonal blocks of I + A: wave
+    // blk < 4 takes block blk, lane = column; right-looking substitution in f32
+    auto prep_inv = [&]() {
+        const int blk = wave, c = l16;
+        const float *at = sAT + blk * 16 * PAT;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < 15; ++j) {
+            const float xj = x[j];
+#pragma unroll
+            for (int i = j + 1; i < 16; ++i) x[i] -= at[j * PAT + i] * xj;
+        }
+        if (lane < 16) {
+            uint16_t *di = sDi + blk * 16 * PDI + c;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) di[i * PDI] = bf16_bits(x[i]);
+        }
+    };
+
+    // WY solve by 16-row blocks X_a = D_a (B_a - sum_{c<a} A_ac X_c):
+    // this wave's W columns (dk) go to LDS as -W, its U columns (dv) stay in U
+    auto prep_solve = [&](int par) {
+        const uint16_t *kt = sKT0 + par * D * PT;
         bf16x4 Xb[4][2 * NTW];
-        f32x4 U[4][NTW];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
             const int trow = 16 * blk + 4 * lq;
@@ -371,25 +414,21 @@ __global__ void __launch_bounds__(kFwdThreads, 1) gdr_fwd_kernel(FwdArgs a) {
             for (int tt = 0; tt < 2 * NTW; ++tt) {
                 const bool isW = tt < NTW;
                 const int col = colw + 16 * (isW ? tt : tt - NTW) + l16;
-                const f32x4 raw = up4(ld4((isW ? sKT : sVT) + col * PT + trow));
-                R[tt] = raw * (isW ? bg : bb);
+                R[tt] = up4(ld4((isW ? kt : sVT) + col * PT + trow)) * (isW ? bg : bb);
             }
-            const float *arow = sA + (16 * blk + l16) * PA + 4 * lq;
+            const uint16_t *ar = sAo + (16 * blk + l16) * PP + 4 * lq;
 #pragma unroll
             for (int c = 0; c + 1 < blk; c += 2) {
-                const bf16x8 af = cat(cvt4(-*reinterpret_cast<const f32x4 *>(arow + 16 * c)),
-                                      cvt4(-*reinterpret_cast<const f32x4 *>(arow + 16 * c + 16)));
+                const bf16x8 af = cat(ld4(ar + 16 * c), ld4(ar + 16 * c + 16));
 #pragma unroll
-                for (int tt = 0; tt < 2 * NTW; ++tt)
-                    R[tt] = mfma32(af, cat(Xb[c][tt], Xb[c + 1][tt]), R[tt]);
+                for (int tt = 0; tt < 2 * NTW; ++tt) R[tt] = mfma32(af, cat(Xb[c][tt], Xb[c + 1][tt]), R[tt]);
             }
             if (blk & 1) {
-                const int c = blk - 1;
-                const bf16x4 af = cvt4(-*reinterpret_cast<const f32x4 *>(arow + 16 * c));
+                const bf16x4 af = ld4(ar + 16 * (blk - 1));
 #pragma unroll
-                for (int tt = 0; tt < 2 * NTW; ++tt) R[tt] = mfma16z(af, Xb[c][tt], R[tt]);
+                for (int tt = 0; tt < 2 * NTW; ++tt) R[tt] = mfma16z(af, Xb[blk - 1][tt], R[tt]);
             }
-            const bf16x4 df = cvt4(*reinterpret_cast<const f32x4 *>(sDi + (16 * blk + l16) * PD + 4 * lq));
+            const bf16x4 df = ld4(sDi + (16 * blk + l16) * PDI + 4 * lq);
 #pragma unroll
             for (int tt = 0; tt < 2 * NTW; ++tt) {
                 const f32x4 X = mfma16z(df, cvt4(R[tt]), zero4());
@@ -403,15 +442,10 @@ __global__ void __launch_bounds__(kFwdThreads, 1) gdr_fwd_kernel(FwdArgs a) {
                 }
             }
         }
-        __syncthreads();
+    };
 
-        // ---- Vnew = U - W H0   (sW holds -W)
-        bf16x4 hb[KB][NTW];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) hb[kb][nt] = cvt4(hs[kb][nt]);
-        f32x4 Vn[4][NTW];
+    // Vnew = U - W H   (sW holds -W)
+    auto chain_vnew = [&]() {
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
 #pragma unroll
@@ -425,8 +459,12 @@ __global__ void __launch_bounds__(kFwdThreads, 1) gdr_fwd_kernel(FwdArgs a) {
                     Vn[blk][nt] = mfma32(af, cat(hb[2 * p][nt], hb[2 * p + 1][nt]), Vn[blk][nt]);
             }
         }
+    };
 
-        // ---- O = scale (diag(e^G) Q H0 + P Vnew)
+    // O^T = diag(e^G) (H^T Q^T) + Vnew^T P^T, scaled and stored 4 dv per lane
+    auto chain_out = [&](int par, int64_t t0, int L) {
+        const uint16_t *sPp = sP0 + par * C * PP;
+        const float *gam = sGam0 + par * C;
         bf16x4 Vb[4][NTW];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk)
@@ -434,77 +472,123 @@ __global__ void __launch_bounds__(kFwdThreads, 1) gdr_fwd_kernel(FwdArgs a) {
             for (int nt = 0; nt < NTW; ++nt) Vb[blk][nt] = cvt4(Vn[blk][nt]);
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
-            f32x4 oacc[NTW];
+            const float gt = gam[16 * blk + l16];
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) oacc[nt] = zero4();
-            const uint16_t *pq = sQ + (16 * blk + l16) * PK + 4 * lq;
-#pragma unroll
-            for (int p = 0; p < KB / 2; ++p) {
-                const bf16x8 af = cat(ld4(pq + 32 * p), ld4(pq + 32 * p + 16));
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt)
-                    oacc[nt] = mfma32(af, cat(hb[2 * p][nt], hb[2 * p + 1][nt]), oacc[nt]);
-            }
-            const int trow = 16 * blk + 4 * lq;
-            const f32x4 gam = *reinterpret_cast<const f32x4 *>(sGam + trow);
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) oacc[nt] = oacc[nt] * gam;
-            const uint16_t *pp = sP + (16 * blk + l16) * PP + 4 * lq;
+            for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = Ot[blk][nt] * gt;
+            const uint16_t *pp = sPp + (16 * blk + l16) * PP + 4 * lq;
 #pragma unroll
             for (int c = 0; c + 1 <= blk; c += 2) {
-                const bf16x8 pf = cat(ld4(pp + 16 * c), ld4(pp + 16 * c + 16));
+                const bf16x8 bf = cat(ld4(pp + 16 * c), ld4(pp + 16 * c + 16));
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt)
-                    oacc[nt] = mfma32(pf, cat(Vb[c][nt], Vb[c + 1][nt]), oacc[nt]);
+                for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = mfma32(cat(Vb[c][nt], Vb[c + 1][nt]), bf, Ot[blk][nt]);
             }
             if ((blk & 1) == 0) {
-                const bf16x4 pf = ld4(pp + 16 * blk);
+                const bf16x4 bf = ld4(pp + 16 * blk);
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) oacc[nt] = mfma16z(pf, Vb[blk][nt], oacc[nt]);
+                for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = mfma16z(Vb[blk][nt], bf, Ot[blk][nt]);
             }
+            const int t = 16 * blk + l16;
+            if (t < L) {
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const int col = colw + 16 * nt + l16;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = trow + r;
-                    if (t < L) {
-                        const int64_t oi = ((t0 + t) * a.hv + h) * D + col;
-                        const float val = a.scale * oacc[nt][r];
-                        if constexpr (IN_BF16)
-                            reinterpret_cast<uint16_t *>(a.o)[oi] = bf16_bits(val);
-                        else
-                            reinterpret_cast<float *>(a.o)[oi] = val;
+                for (int nt = 0; nt < NTW; ++nt) {
+                    const int64_t oi = ((t0 + t) * a.hv + h) * D + colw + 16 * nt + 4 * lq;
+                    const f32x4 val = Ot[blk][nt] * a.scale;
+                    if constexpr (IN_BF16) {
+                        uint2 st;
+                        st.x = bf16_bits(val[0]) | (static_cast<uint32_t>(bf16_bits(val[1])) << 16);
+                        st.y = bf16_bits(val[2]) | (static_cast<uint32_t>(bf16_bits(val[3])) << 16);
+                        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.o) + oi) = st;
+                    } else {
+                        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.o) + oi) =
+                            make_float4(val[0], val[1], val[2], val[3]);
                     }
                 }
             }
         }
+    };
 
-        // ---- H = e^{G_L} H0 + K^T diag(e^{G_L - G}) Vnew
-        {
-            const float gl = sMisc[0];
-            bf16x4 Vt[4][NTW];
+    // H <- e^{G_L} H + K^T diag(e^{G_L - G}) Vnew
+    auto chain_h = [&](int par) {
+        const uint16_t *kt = sKT0 + par * D * PT;
+        const float gl = sGL[par];
+        const float *dec = sDec0 + par * C;
+        bf16x4 Vt[4][NTW];
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                const f32x4 dec = *reinterpret_cast<const f32x4 *>(sDec + 16 * blk + 4 * lq);
+        for (int blk = 0; blk < 4; ++blk) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4 *>(dec + 16 * blk + 4 * lq);
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) Vt[blk][nt] = cvt4(Vn[blk][nt] * dec);
-            }
+            for (int nt = 0; nt < NTW; ++nt) Vt[blk][nt] = cvt4(Vn[blk][nt] * d4);
+        }
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const uint16_t *pk = sKT + (16 * kb + l16) * PT + 4 * lq;
-                const bf16x8 a01 = cat(ld4(pk), ld4(pk + 16));
-                const bf16x8 a23 = cat(ld4(pk + 32), ld4(pk + 48));
+        for (int kb = 0; kb < KB; ++kb) {
+            const uint16_t *pkt = kt + (16 * kb + l16) * PT + 4 * lq;
+            const bf16x8 a01 = cat(ld4(pkt), ld4(pkt + 16));
+            const bf16x8 a23 = cat(ld4(pkt + 32), ld4(pkt + 48));
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) {
-                    f32x4 s = hs[kb][nt] * gl;
-                    s = mfma32(a01, cat(Vt[0][nt], Vt[1][nt]), s);
-                    s = mfma32(a23, cat(Vt[2][nt], Vt[3][nt]), s);
-                    hs[kb][nt] = s;
-                }
+            for (int nt = 0; nt < NTW; ++nt) {
+                f32x4 s = hs[kb][nt] * gl;
+                s = mfma32(a01, cat(Vt[0][nt], Vt[1][nt]), s);
+                s = mfma32(a23, cat(Vt[2][nt], Vt[3][nt]), s);
+                hs[kb][nt] = s;
             }
         }
-        __syncthreads();   // LDS is restaged by the next chunk
+    };
+
+    // H^T Q^T for the chunk staged in sQ (before the e^G row scaling)
+    auto chain_qh = [&]() {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) hb[kb][nt] = cvt4(hs[kb][nt]);
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = zero4();
+            const uint16_t *pq_ = sQ + (16 * blk + l16) * PK + 4 * lq;
+#pragma unroll
+            for (int p = 0; p < KB / 2; ++p) {
+                const bf16x8 bq = cat(ld4(pq_ + 32 * p), ld4(pq_ + 32 * p + 16));
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+                    Ot[blk][nt] = mfma32(cat(hb[2 * p][nt], hb[2 * p + 1][nt]), bq, Ot[blk][nt]);
+            }
+        }
+    };
+
+    // ---- prologue: prepare chunk 0
+    load_chunk(0);
+    stage_chunk(0);
+    load_chunk(1);   // all zero when there is no chunk 1
+    __syncthreads();
+    prep_kq(0);
+    __syncthreads();
+    if (wave < 4) prep_inv();
+    __syncthreads();
+    prep_solve(0);
+    chain_qh();
+    __syncthreads();
+
+    // The preparation stream runs unconditionally: past the last chunk it
+    // works on zero rows and its results are never read.
+    for (int64_t c = 0; c < nch; ++c) {
+        const int par = static_cast<int>(c & 1), npar = par ^ 1;
+        // P1
+        stage_chunk(npar);
+        load_chunk(c + 2);
+        chain_vnew();
+        __syncthreads();
+        // P2
+        prep_kq(npar);
+        chain_out(par, bos + c * C, chunk_len(c));
+        __syncthreads();
+        // P3
+        if (wave < 4) prep_inv();
+        chain_h(par);
+        __syncthreads();
+        // P4
+        prep_solve(npar);
+        chain_qh();
+        __syncthreads();
     }
 
     if (a.ht) {
@@ -650,7 +734,7 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(a.n_seq * a.hv)), dim3(kFwdThreads), lds,
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(a.n_seq * a.hv)), dim3(fwd_threads(D)), lds,
                        stream, a);
     return hipGetLastError();
 }
