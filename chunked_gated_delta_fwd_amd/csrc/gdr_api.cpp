@@ -191,7 +191,7 @@ int plan_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, cons
     p->has_h0 = h0 ? 1 : 0;
     p->has_ht = ht ? 1 : 0;
     p->grid_fwd = N * Hv;
-    p->block_fwd = gdr::fwd_threads(static_cast<int>(dk));
+    p->block_fwd = gdr::kFwdThreads;
     p->lds_fwd = gdr::fwd_lds_bytes(static_cast<int>(dk));
     p->workspace_bytes = cu ? 4 * N : 0;
     return GDR_OK;

@@ -25,9 +25,9 @@ struct FwdArgs {
 };
 
 // Dynamic LDS bytes and threads per work-group of the fused forward kernel
-// (d / 16 waves: one per 16 dv columns of the state).
+// (4 state-chain waves + 4 preparation waves).
 int fwd_lds_bytes(int d);
-constexpr int fwd_threads(int d) { return 4 * d; }
+constexpr int kFwdThreads = 512;
 constexpr int kChunk = 64;
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);

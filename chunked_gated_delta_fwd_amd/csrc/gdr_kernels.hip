@@ -137,72 +137,83 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 }
 
 // --------------------------------------------------------------------------
-// Fused forward.  One work-group of D/16 waves (8 at D = 128: two per SIMD)
-// walks one (sequence, v-head) through its chunks in order; wave w owns the
-// 16 dv columns 16w..16w+15 of the state.  The chunk loop is software-pipelined:
-// iteration c runs the state-dependent chain of chunk c (Vnew, output, state
-// update) next to the state-independent preparation of chunk c+1 (staging,
-// K K^T and Q K^T, diagonal-block inverses, WY solve) and prefetches chunk c+2
-// from HBM into registers.  LDS buffers both streams touch are doubled.
+// Fused forward, warp-specialised.  One work-group of 8 waves walks one
+// (sequence, v-head) through its chunks in order:
+//   waves 0-3  the state chain: wave c owns dv columns [c*D/4, (c+1)*D/4) of
+//              the fp32 state and computes the U half of the WY solve, Vnew,
+//              the output and the state update of chunk c;
+//   waves 4-7  prepare chunk c+1 meanwhile: staging of q and k, K K^T and
+//              Q K^T, K^T, the 16x16 diagonal inverses and the W half of the
+//              WY solve; they prefetch chunk c+2 from HBM into registers.
+// Each SIMD hosts one wave of each kind, so the hardware interleaves the
+// chain's dependent MFMAs with the preparation's loads, LDS traffic and VALU.
 //
-// Per iteration (4 barriers):
-//   P1  stage c+1 from registers, prefetch c+2    | Vnew_c = U_c - W_c H
-//   P2  K K^T -> A, Q K^T -> P  (c+1)             | O_c^T = e^G (H^T Q^T) + Vnew^T P^T, store
-//   P3  16x16 diagonal inverses (c+1, waves 0-3) | H <- e^{G_L} H + K^T diag(e^{G_L-G}) Vnew_c
-//   P4  WY solve -> -W (LDS), U (registers) (c+1) | H^T Q^T for chunk c+1
+// Per iteration c (4 barriers):
+//   P1  stage c+1 (q, k), gates c+1, prefetch c+2  | U solve c; Vnew_c = U_c - W_c H
+//   P2  A, P = gated K K^T, Q K^T (c+1); K^T (c+1)  | O_c^T = e^G H^T Q^T + Vnew^T P^T, store
+//   P3  diagonal inverses (c+1)                     | H <- e^{G_L} H + K^T diag(e^{G_L-G}) Vnew_c
+//   P4  W solve (c+1) -> -W                         | prefetch v of c+1
+//
+// Shared matrices keep each 32-wide k range with its 4-element groups in the
+// order 0,4,1,5,2,6,3,7 (pc below), so the 8 k values a lane feeds to one
+// 16x16x32 MFMA (groups lq and lq+4) are 16 contiguous bytes.
 // --------------------------------------------------------------------------
+__device__ __forceinline__ int pc(int x) { return (x & ~31) | ((x & 12) << 1) | ((x >> 2) & 4) | (x & 3); }
+
+__device__ __forceinline__ bf16x8 ld8(const uint16_t *p) {   // 16-byte LDS read
+    return *reinterpret_cast<const bf16x8 *>(p);
+}
+__device__ __forceinline__ void st4(uint16_t *p, bf16x4 v) { *reinterpret_cast<bf16x4 *>(p) = v; }
+
 template <int D>
 struct FwdLds {
-    static constexpr int PK = D + 8;    // [64][D] row-major bf16: q, k, -W
-    static constexpr int PT = C + 8;    // [D][64] transposed bf16: k^T (two buffers), v^T
-    static constexpr int PP = C + 8;    // [64][64] bf16: P (two buffers), -A off the diagonal
+    static constexpr int PK = D + 8;    // [64][D] bf16, k permuted: q (two buffers), k, -W
+    static constexpr int PT = C + 8;    // [D][64] bf16, tokens permuted: k^T (two buffers)
+    static constexpr int PP = C + 8;    // [64][64] bf16, keys permuted: P (two buffers), -A off the diagonal
     static constexpr int PAT = 20;      // [4][16][16] f32: diagonal blocks of A, transposed
     static constexpr int PDI = 24;      // [4][16][16] bf16: inverses of the diagonal blocks
     static constexpr int oQ = 0;
-    static constexpr int oK = oQ + C * PK * 2;
+    static constexpr int oK = oQ + 2 * C * PK * 2;
     static constexpr int oW = oK + C * PK * 2;
     static constexpr int oKT = oW + C * PK * 2;
-    static constexpr int oVT = oKT + 2 * D * PT * 2;
-    static constexpr int oP = oVT + D * PT * 2;
+    static constexpr int oP = oKT + 2 * D * PT * 2;
     static constexpr int oAo = oP + 2 * C * PP * 2;
     static constexpr int oAT = oAo + C * PP * 2;
     static constexpr int oDi = oAT + 4 * 16 * PAT * 4;
     static constexpr int oS = oDi + 4 * 16 * PDI * 2;
-    // f32 vectors of 64: G*log2(e), beta, beta*e^G, e^G (x2), e^{G_L-G} (x2); then e^{G_L} (x2)
-    static constexpr int bytes = oS + 7 * C * 4 + 16;
+    // f32 vectors of 64: G*log2(e), beta*e^G, beta (x2), scale*e^G (x2), e^{G_L-G} (x2); then e^{G_L} (x2)
+    static constexpr int bytes = oS + 8 * C * 4 + 16;
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int D, bool IN_BF16, bool GATE_BF16>
-__global__ void __launch_bounds__(4 * D) gdr_fwd_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     using Ly = FwdLds<D>;
     constexpr int PK = Ly::PK, PT = Ly::PT, PP = Ly::PP, PAT = Ly::PAT, PDI = Ly::PDI;
-    constexpr int NW = D / 16;     // waves per work-group
-    constexpr int DW = 16;         // dv columns owned by each wave
-    constexpr int NTW = DW / 16;   // 16-wide column tiles per wave
+    constexpr int DW = D / 4;      // state columns per chain wave (and W columns per prep wave)
+    constexpr int NTW = DW / 16;   // 16-wide tiles of those
     constexpr int KB = D / 16;     // K16 blocks over the head dim
-    constexpr int FG = D / 8;      // 8-element feature groups per row (staging)
-    constexpr int TG = 64 * NW / FG;
-    constexpr int TPT = C / TG;    // tokens staged per thread
-    static_assert(KB % 2 == 0 && (TPT == 2 || TPT == 4), "unsupported head dim");
+    constexpr int FG = D / 8;      // staging: 8-element feature groups per row
+    constexpr int TG = 256 / FG;   // staging: token groups over the 4 prep waves
+    constexpr int TPT = C / TG;    // staging: tokens per prep thread
+    static_assert(KB % 2 == 0 && NTW >= 1 && (TPT == 2 || TPT == 4), "unsupported head dim");
 
     extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t *const sQ = reinterpret_cast<uint16_t *>(smem + Ly::oQ);
+    uint16_t *const sQ0 = reinterpret_cast<uint16_t *>(smem + Ly::oQ);
     uint16_t *const sK = reinterpret_cast<uint16_t *>(smem + Ly::oK);
     uint16_t *const sW = reinterpret_cast<uint16_t *>(smem + Ly::oW);
     uint16_t *const sKT0 = reinterpret_cast<uint16_t *>(smem + Ly::oKT);
-    uint16_t *const sVT = reinterpret_cast<uint16_t *>(smem + Ly::oVT);
     uint16_t *const sP0 = reinterpret_cast<uint16_t *>(smem + Ly::oP);
     uint16_t *const sAo = reinterpret_cast<uint16_t *>(smem + Ly::oAo);
     float *const sAT = reinterpret_cast<float *>(smem + Ly::oAT);
     uint16_t *const sDi = reinterpret_cast<uint16_t *>(smem + Ly::oDi);
     float *const sG2 = reinterpret_cast<float *>(smem + Ly::oS);   // chunk being prepared
-    float *const sB = sG2 + C;
-    float *const sBG = sG2 + 2 * C;
-    float *const sGam0 = sG2 + 3 * C;                               // [2][64]
-    float *const sDec0 = sG2 + 5 * C;                               // [2][64]
-    float *const sGL = sG2 + 7 * C;                                 // [2]
+    float *const sBG = sG2 + C;
+    float *const sB0 = sG2 + 2 * C;                                 // [2][64]
+    float *const sGam0 = sG2 + 4 * C;                               // [2][64], scale folded in
+    float *const sDec0 = sG2 + 6 * C;                               // [2][64]
+    float *const sGL = sG2 + 8 * C;                                 // [2]
 
     // ---- work item: (sequence n, v-head h), longest sequences first
     const int64_t item = blockIdx.x;
@@ -226,53 +237,74 @@ __global__ void __launch_bounds__(4 * D) gdr_fwd_kernel(FwdArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const bool chain = wave < 4;
+    const int role = wave & 3;          // chain wave c / prep wave p
     const int l16 = lane & 15;
     const int lq = lane >> 4;
-    const int colw = wave * DW;         // first dv (and dk, in the solve) column of this wave
-    const int fg = tid % FG, tg = tid / FG;
-    const int f0 = fg * 8;
+    const int colw = role * DW;         // this wave's 16*NTW columns (dv for chain, dk for the W solve)
     const int64_t nch = (eos - bos + C - 1) / C;
 
     auto chunk_len = [&](int64_t c) -> int {
         const int64_t r = eos - (bos + c * C);
-        return r < C ? static_cast<int>(r) : C;
+        return r < C ? (r < 0 ? 0 : static_cast<int>(r)) : C;
     };
 
-    // ---- registers carried across phases
+    // 16x16 identity as a zero-padded B fragment: slot r of lane l is I[4lq+r][l16]
+    bf16x8 ident;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) ident[r] = (__bf16)((r < 4 && 4 * lq + r == l16) ? 1.f : 0.f);
+
+    // ---- chain registers
     f32x4 hs[KB][NTW];        // state tile (kb, nt): rows dk 16kb+4lq+r, column dv colw+16nt+l16
-    bf16x4 hb[KB][NTW];       // its bf16 copy (B operand of W H, A operand of H^T Q^T)
-    f32x4 U[4][NTW];          // U of the chunk the chain works on, C layout (rows tokens)
-    f32x4 Ot[4][NTW];         // O^T accumulators: rows dv colw+16nt+4lq+r, column token 16blk+l16
-    f32x4 Vn[4][NTW];         // Vnew of the chunk the chain works on
-    uint4 pq[TPT], pk[TPT], pv[TPT];   // prefetched rows of the next chunk to stage
-    float pg = 0.f, pb = 0.f;          // prefetched gate and beta (wave 0, lane = token)
+    f32x4 Vn[4][NTW];         // Vnew of the chunk the chain works on (rows tokens)
+    bf16x4 vp[4][NTW];        // v of the chunk the chain solves next: token 16blk+l16, dv colw+16nt+4lq..+3
+    // ---- preparation registers
+    uint4 pq[TPT], pk[TPT];   // q, k rows of the next chunk to stage
+    float pg = 0.f, pb = 0.f; // its gate and beta (prep wave 0, lane = token)
 
     const int64_t sbase = (n * a.hv + h) * static_cast<int64_t>(D) * D;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                hs[kb][nt][r] = a.h0 ? a.h0[sbase + (16 * kb + 4 * lq + r) * D + colw + 16 * nt + l16] : 0.f;
 
-    // HBM -> registers (rows past the segment end are zero; padding is exactly neutral)
-    auto load_chunk = [&](int64_t c) {
+    // chain: v of chunk c as A fragments (rows past the segment end are zero)
+    auto load_v = [&](int64_t c) {
         const int64_t t0 = bos + c * C;
         const int L = chunk_len(c);
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const int t = 16 * blk + l16;
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                bf16x4 x = {};
+                if (t < L) {
+                    const int64_t vi = ((t0 + t) * a.hv + h) * D + colw + 16 * nt + 4 * lq;
+                    if constexpr (IN_BF16) {
+                        x = *reinterpret_cast<const bf16x4 *>(reinterpret_cast<const uint16_t *>(a.v) + vi);
+                    } else {
+                        const float4 f = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.v) + vi);
+                        x = cvt4(f32x4{f.x, f.y, f.z, f.w});
+                    }
+                }
+                vp[blk][nt] = x;
+            }
+        }
+    };
+
+    // prep: q, k rows and gates of chunk c into registers (zero past the end)
+    auto load_qk = [&](int64_t c) {
+        const int64_t t0 = bos + c * C;
+        const int L = chunk_len(c);
+        const int pt = tid - 256, fg = pt % FG, tg = pt / FG;
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
             const int t = tg * TPT + j;
             if (t < L) {
-                const int64_t tok = t0 + t;
-                pq[j] = load8<IN_BF16>(a.q, (tok * a.hk + hk) * D + f0);
-                pk[j] = load8<IN_BF16>(a.k, (tok * a.hk + hk) * D + f0);
-                pv[j] = load8<IN_BF16>(a.v, (tok * a.hv + h) * D + f0);
+                const int64_t row = ((t0 + t) * a.hk + hk) * D + fg * 8;
+                pq[j] = load8<IN_BF16>(a.q, row);
+                pk[j] = load8<IN_BF16>(a.k, row);
             } else {
-                pq[j] = pk[j] = pv[j] = make_uint4(0, 0, 0, 0);
+                pq[j] = pk[j] = make_uint4(0, 0, 0, 0);
             }
         }
-        if (wave == 0) {
+        if (role == 0) {
             pg = pb = 0.f;
             if (lane < L) {
                 const int64_t gi = (t0 + lane) * a.hv + h;
@@ -282,66 +314,53 @@ __global__ void __launch_bounds__(4 * D) gdr_fwd_kernel(FwdArgs a) {
         }
     };
 
-    // registers -> LDS (q, k row-major; k, v transposed) and the gate vectors
-    auto stage_chunk = [&](int par) {
-        uint16_t *kt = sKT0 + par * D * PT;
+    // prep: registers -> LDS (permuted rows of q and k) and the gate vectors
+    auto stage = [&](int par) {
+        const int pt = tid - 256, fg = pt % FG, tg = pt / FG;
+        const int c0 = pc(fg * 8), c1 = pc(fg * 8 + 4);
+        uint16_t *sQ = sQ0 + par * C * PK;
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
             const int t = tg * TPT + j;
-            *reinterpret_cast<uint4 *>(sQ + t * PK + f0) = pq[j];
-            *reinterpret_cast<uint4 *>(sK + t * PK + f0) = pk[j];
+            *reinterpret_cast<uint2 *>(sQ + t * PK + c0) = make_uint2(pq[j].x, pq[j].y);
+            *reinterpret_cast<uint2 *>(sQ + t * PK + c1) = make_uint2(pq[j].z, pq[j].w);
+            *reinterpret_cast<uint2 *>(sK + t * PK + c0) = make_uint2(pk[j].x, pk[j].y);
+            *reinterpret_cast<uint2 *>(sK + t * PK + c1) = make_uint2(pk[j].z, pk[j].w);
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if constexpr (TPT == 4) {
-                uint2 k2, v2;
-                k2.x = elem8(pk[0], e) | (static_cast<uint32_t>(elem8(pk[1], e)) << 16);
-                k2.y = elem8(pk[2], e) | (static_cast<uint32_t>(elem8(pk[3], e)) << 16);
-                v2.x = elem8(pv[0], e) | (static_cast<uint32_t>(elem8(pv[1], e)) << 16);
-                v2.y = elem8(pv[2], e) | (static_cast<uint32_t>(elem8(pv[3], e)) << 16);
-                *reinterpret_cast<uint2 *>(kt + (f0 + e) * PT + tg * TPT) = k2;
-                *reinterpret_cast<uint2 *>(sVT + (f0 + e) * PT + tg * TPT) = v2;
-            } else {
-                *reinterpret_cast<uint32_t *>(kt + (f0 + e) * PT + tg * TPT) =
-                    elem8(pk[0], e) | (static_cast<uint32_t>(elem8(pk[1], e)) << 16);
-                *reinterpret_cast<uint32_t *>(sVT + (f0 + e) * PT + tg * TPT) =
-                    elem8(pv[0], e) | (static_cast<uint32_t>(elem8(pv[1], e)) << 16);
-            }
-        }
-        if (wave == 0) {
+        if (role == 0) {
             const float G2 = wave_inclusive_scan(pg, lane) * kLog2e;
             const float GL2 = __shfl(G2, 63, 64);   // padding has g = 0: equals G at the last token
             const float gam = fast_exp2(G2);
             sG2[lane] = G2;
-            sB[lane] = pb;
+            sB0[par * C + lane] = pb;
             sBG[lane] = pb * gam;
-            sGam0[par * C + lane] = gam;
+            sGam0[par * C + lane] = gam * a.scale;
             sDec0[par * C + lane] = fast_exp2(GL2 - G2);
             if (lane == 0) sGL[par] = fast_exp2(GL2);
         }
     };
 
-    // K K^T -> A (diagonal blocks f32 transposed; other blocks -A in bf16),
-    // Q K^T -> P; 20 lower-triangular 16x16 tiles spread over the waves
+    // prep: gated K K^T -> A (diagonal blocks f32 transposed, others -A bf16),
+    // gated Q K^T -> P (scale folded in); K^T of the chunk
     auto prep_kq = [&](int par) {
         uint16_t *sPp = sP0 + par * C * PP;
+        uint16_t *kt = sKT0 + par * D * PT;
+        const uint16_t *sQ = sQ0 + par * C * PK;
+        const float *sB = sB0 + par * C;
 #pragma unroll
-        for (int s = 0; s < (20 + NW - 1) / NW; ++s) {
-            const int ti = wave + NW * s;
-            if (ti >= 20) break;
+        for (int s = 0; s < 5; ++s) {
+            const int ti = role + 4 * s;            // 20 lower-triangular tiles, 5 per prep wave
             const bool qk = ti >= 10;
             const int t = qk ? ti - 10 : ti;
             const int ib = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
             const int jb = t - ib * (ib + 1) / 2;
-            const uint16_t *pa = sK + (16 * jb + l16) * PK + 4 * lq;
-            const uint16_t *pbp = (qk ? sQ : sK) + (16 * ib + l16) * PK + 4 * lq;
+            const uint16_t *pa = sK + (16 * jb + l16) * PK + 8 * lq;
+            const uint16_t *pbp = (qk ? sQ : sK) + (16 * ib + l16) * PK + 8 * lq;
             f32x4 acc = zero4();
 #pragma unroll
-            for (int p = 0; p < KB / 2; ++p)
-                acc = mfma32(cat(ld4(pa + 32 * p), ld4(pa + 32 * p + 16)),
-                             cat(ld4(pbp + 32 * p), ld4(pbp + 32 * p + 16)), acc);
+            for (int p = 0; p < KB / 2; ++p) acc = mfma32(ld8(pa + 32 * p), ld8(pbp + 32 * p), acc);
             if (qk) {
-                // element (row key j = 16jb+4lq+r, column query i = 16ib+l16) = k_j . q_i
+                // (row key j = 16jb+4lq+r, column query i = 16ib+l16) = k_j . q_i
                 const int i = 16 * ib + l16;
                 const float gi = sG2[i];
                 const f32x4 gj = *reinterpret_cast<const f32x4 *>(sG2 + 16 * jb + 4 * lq);
@@ -349,11 +368,11 @@ __global__ void __launch_bounds__(4 * D) gdr_fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const bool keep = i >= 16 * jb + 4 * lq + r;
-                    out[r] = keep ? fast_exp2(gi - gj[r]) * acc[r] : 0.f;
+                    out[r] = keep ? a.scale * fast_exp2(gi - gj[r]) * acc[r] : 0.f;
                 }
-                *reinterpret_cast<bf16x4 *>(sPp + i * PP + 16 * jb + 4 * lq) = cvt4(out);
+                st4(sPp + i * PP + pc(16 * jb + 4 * lq), cvt4(out));
             } else if (ib == jb) {
-                // symmetric tile: element (row i = 16ib+4lq+r, column j = 16ib+l16) = k_i . k_j
+                // symmetric: (row i = 16ib+4lq+r, column j = 16ib+l16) = k_i . k_j
                 const int j = 16 * jb + l16;
                 const float gj = sG2[j];
                 const f32x4 gi = *reinterpret_cast<const f32x4 *>(sG2 + 16 * ib + 4 * lq);
@@ -366,22 +385,31 @@ __global__ void __launch_bounds__(4 * D) gdr_fwd_kernel(FwdArgs a) {
                 }
                 *reinterpret_cast<f32x4 *>(sAT + (16 * ib + l16) * PAT + 4 * lq) = out;
             } else {
-                // element (row j = 16jb+4lq+r, column i = 16ib+l16) = k_j . k_i, i > j
+                // (row j = 16jb+4lq+r, column i = 16ib+l16) = k_j . k_i with i > j
                 const int i = 16 * ib + l16;
                 const float gi = sG2[i], bi = sB[i];
                 const f32x4 gj = *reinterpret_cast<const f32x4 *>(sG2 + 16 * jb + 4 * lq);
                 f32x4 out;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) out[r] = -bi * fast_exp2(gi - gj[r]) * acc[r];
-                *reinterpret_cast<bf16x4 *>(sAo + i * PP + 16 * jb + 4 * lq) = cvt4(out);
+                st4(sAo + i * PP + pc(16 * jb + 4 * lq), cvt4(out));
             }
+        }
+        // K^T tiles (token block blk, dk block kb) through an identity product
+#pragma unroll
+        for (int s = 0; s < KB; ++s) {
+            const int tt = role + 4 * s;            // 4*KB tiles, KB per prep wave
+            const int blk = tt & 3, kb = tt >> 2;
+            const bf16x4 af = ld4(sK + (16 * blk + l16) * PK + pc(16 * kb + 4 * lq));
+            const bf16x8 a8 = __builtin_shufflevector(af, bf16x4{}, 0, 1, 2, 3, 4, 5, 6, 7);
+            const f32x4 x = mfma32(a8, ident, zero4());   // (row token 16blk+4lq+r, column dk 16kb+l16)
+            st4(kt + (16 * kb + l16) * PT + pc(16 * blk + 4 * lq), cvt4(x));
         }
     };
 
-    // inverses of the four 16x16 unit lower diagonal blocks of I + A: wave
-    // blk < 4 takes block blk, lane = column; right-looking substitution in f32
+    // prep: inverse of diagonal block p of I + A (lane = column), right-looking, f32
     auto prep_inv = [&]() {
-        const int blk = wave, c = l16;
+        const int blk = role, c = l16;
         const float *at = sAT + blk * 16 * PAT;
         float x[16];
 #pragma unroll
@@ -399,61 +427,87 @@ __global__ void __launch_bounds__(4 * D) gdr_fwd_kernel(FwdArgs a) {
         }
     };
 
-    // WY solve by 16-row blocks X_a = D_a (B_a - sum_{c<a} A_ac X_c):
-    // this wave's W columns (dk) go to LDS as -W, its U columns (dv) stay in U
-    auto prep_solve = [&](int par) {
-        const uint16_t *kt = sKT0 + par * D * PT;
-        bf16x4 Xb[4][2 * NTW];
+    // block forward substitution X_a = D_a (R_a - sum_{c<a} A_ac X_c) on NTW tiles;
+    // rhs(blk, nt) gives R_a in C layout; out(blk, nt, X) consumes X_a
+    auto solve = [&](auto rhs, auto out) {
+        bf16x4 Xb[4][NTW];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
-            const int trow = 16 * blk + 4 * lq;
-            const f32x4 bg = *reinterpret_cast<const f32x4 *>(sBG + trow);
-            const f32x4 bb = *reinterpret_cast<const f32x4 *>(sB + trow);
-            f32x4 R[2 * NTW];
+            f32x4 R[NTW];
 #pragma unroll
-            for (int tt = 0; tt < 2 * NTW; ++tt) {
-                const bool isW = tt < NTW;
-                const int col = colw + 16 * (isW ? tt : tt - NTW) + l16;
-                R[tt] = up4(ld4((isW ? kt : sVT) + col * PT + trow)) * (isW ? bg : bb);
-            }
-            const uint16_t *ar = sAo + (16 * blk + l16) * PP + 4 * lq;
+            for (int nt = 0; nt < NTW; ++nt) R[nt] = rhs(blk, nt);
+            const uint16_t *ar = sAo + (16 * blk + l16) * PP;
+            if (blk >= 2) {
+                const bf16x8 af = ld8(ar + 8 * lq);   // blocks 0 and 1
 #pragma unroll
-            for (int c = 0; c + 1 < blk; c += 2) {
-                const bf16x8 af = cat(ld4(ar + 16 * c), ld4(ar + 16 * c + 16));
-#pragma unroll
-                for (int tt = 0; tt < 2 * NTW; ++tt) R[tt] = mfma32(af, cat(Xb[c][tt], Xb[c + 1][tt]), R[tt]);
+                for (int nt = 0; nt < NTW; ++nt) R[nt] = mfma32(af, cat(Xb[0][nt], Xb[1][nt]), R[nt]);
             }
             if (blk & 1) {
-                const bf16x4 af = ld4(ar + 16 * (blk - 1));
+                const bf16x4 af = ld4(ar + pc(16 * (blk - 1) + 4 * lq));
 #pragma unroll
-                for (int tt = 0; tt < 2 * NTW; ++tt) R[tt] = mfma16z(af, Xb[blk - 1][tt], R[tt]);
+                for (int nt = 0; nt < NTW; ++nt) R[nt] = mfma16z(af, Xb[blk - 1][nt], R[nt]);
             }
             const bf16x4 df = ld4(sDi + (16 * blk + l16) * PDI + 4 * lq);
 #pragma unroll
-            for (int tt = 0; tt < 2 * NTW; ++tt) {
-                const f32x4 X = mfma16z(df, cvt4(R[tt]), zero4());
-                Xb[blk][tt] = cvt4(X);
-                if (tt < NTW) {
-                    const int col = colw + 16 * tt + l16;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sW[(trow + r) * PK + col] = bf16_bits(-X[r]);
-                } else {
-                    U[blk][tt - NTW] = X;
-                }
+            for (int nt = 0; nt < NTW; ++nt) {
+                const f32x4 X = mfma16z(df, cvt4(R[nt]), zero4());
+                Xb[blk][nt] = cvt4(X);
+                out(blk, nt, X, Xb[blk][nt]);
             }
         }
     };
 
-    // Vnew = U - W H   (sW holds -W)
-    auto chain_vnew = [&]() {
+    // prep: W columns colw.. of the chunk -> sW as -W (row token, k = dk permuted)
+    auto prep_wsolve = [&](int par) {
+        const uint16_t *kt = sKT0 + par * D * PT;
+        solve([&](int blk, int nt) {
+                  const f32x4 bg = *reinterpret_cast<const f32x4 *>(sBG + 16 * blk + 4 * lq);
+                  return up4(ld4(kt + (colw + 16 * nt + l16) * PT + pc(16 * blk + 4 * lq))) * bg;
+              },
+              [&](int blk, int nt, f32x4 X, bf16x4 Xb) {
+                  // transpose -W through an identity product: (row dk, column token)
+                  const bf16x4 nx = cvt4(-X);
+                  const f32x4 y = mfma32(__builtin_shufflevector(nx, bf16x4{}, 0, 1, 2, 3, 4, 5, 6, 7), ident, zero4());
+                  st4(sW + (16 * blk + l16) * PK + pc(colw + 16 * nt + 4 * lq), cvt4(y));
+                  (void)Xb;
+              });
+    };
+
+    // chain: U columns colw.. of the chunk in vp (solved with that chunk's A, D and beta)
+    auto chain_usolve = [&](int par, f32x4 (&U)[4][NTW]) {
+        const float *sB = sB0 + par * C;
+        solve([&](int blk, int nt) {
+                  const f32x4 bb = *reinterpret_cast<const f32x4 *>(sB + 16 * blk + 4 * lq);
+                  // v (row token, k dv) times identity: (row token 16blk+4lq+r, column dv)
+                  const f32x4 x = mfma32(__builtin_shufflevector(vp[blk][nt], bf16x4{}, 0, 1, 2, 3, 4, 5, 6, 7),
+                                         ident, zero4());
+                  return x * bb;
+              },
+              [&](int blk, int nt, f32x4 X, bf16x4 Xb) {
+                  U[blk][nt] = X;
+                  (void)Xb;
+              });
+    };
+
+    auto to_bf16_state = [&](bf16x4 (&hb)[KB][NTW]) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) hb[kb][nt] = cvt4(hs[kb][nt]);
+    };
+
+    // chain: Vnew = U - W H   (sW holds -W)
+    auto chain_vnew = [&](const f32x4 (&U)[4][NTW]) {
+        bf16x4 hb[KB][NTW];
+        to_bf16_state(hb);
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) Vn[blk][nt] = U[blk][nt];
-            const uint16_t *pw = sW + (16 * blk + l16) * PK + 4 * lq;
+            const uint16_t *pw = sW + (16 * blk + l16) * PK + 8 * lq;
 #pragma unroll
             for (int p = 0; p < KB / 2; ++p) {
-                const bf16x8 af = cat(ld4(pw + 32 * p), ld4(pw + 32 * p + 16));
+                const bf16x8 af = ld8(pw + 32 * p);
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt)
                     Vn[blk][nt] = mfma32(af, cat(hb[2 * p][nt], hb[2 * p + 1][nt]), Vn[blk][nt]);
@@ -461,10 +515,32 @@ __global__ void __launch_bounds__(4 * D) gdr_fwd_kernel(FwdArgs a) {
         }
     };
 
-    // O^T = diag(e^G) (H^T Q^T) + Vnew^T P^T, scaled and stored 4 dv per lane
+    // chain: H^T Q^T for the chunk staged in sQ[par] (before the scale e^G row scaling)
+    auto chain_qh = [&](int par, f32x4 (&Ot)[4][NTW]) {
+        bf16x4 hb[KB][NTW];
+        to_bf16_state(hb);
+        const uint16_t *sQ = sQ0 + par * C * PK;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = zero4();
+            const uint16_t *pq_ = sQ + (16 * blk + l16) * PK + 8 * lq;
+#pragma unroll
+            for (int p = 0; p < KB / 2; ++p) {
+                const bf16x8 bq = ld8(pq_ + 32 * p);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+                    Ot[blk][nt] = mfma32(cat(hb[2 * p][nt], hb[2 * p + 1][nt]), bq, Ot[blk][nt]);
+            }
+        }
+    };
+
+    // chain: O^T = diag(scale e^G) (H^T Q^T) + Vnew^T P^T (P carries the scale), stored 4 dv per lane
     auto chain_out = [&](int par, int64_t t0, int L) {
         const uint16_t *sPp = sP0 + par * C * PP;
         const float *gam = sGam0 + par * C;
+        f32x4 Ot[4][NTW];
+        chain_qh(par, Ot);
         bf16x4 Vb[4][NTW];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk)
@@ -475,15 +551,19 @@ __global__ void __launch_bounds__(4 * D) gdr_fwd_kernel(FwdArgs a) {
             const float gt = gam[16 * blk + l16];
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = Ot[blk][nt] * gt;
-            const uint16_t *pp = sPp + (16 * blk + l16) * PP + 4 * lq;
+            const uint16_t *pp = sPp + (16 * blk + l16) * PP;
+            if (blk >= 1) {
+                const bf16x8 bf = ld8(pp + 8 * lq);   // keys of blocks 0, 1
 #pragma unroll
-            for (int c = 0; c + 1 <= blk; c += 2) {
-                const bf16x8 bf = cat(ld4(pp + 16 * c), ld4(pp + 16 * c + 16));
+                for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = mfma32(cat(Vb[0][nt], Vb[1][nt]), bf, Ot[blk][nt]);
+            }
+            if (blk == 3) {
+                const bf16x8 bf = ld8(pp + 32 + 8 * lq);   // keys of blocks 2, 3
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = mfma32(cat(Vb[c][nt], Vb[c + 1][nt]), bf, Ot[blk][nt]);
+                for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = mfma32(cat(Vb[2][nt], Vb[3][nt]), bf, Ot[blk][nt]);
             }
             if ((blk & 1) == 0) {
-                const bf16x4 bf = ld4(pp + 16 * blk);
+                const bf16x4 bf = ld4(pp + pc(16 * blk + 4 * lq));
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = mfma16z(Vb[blk][nt], bf, Ot[blk][nt]);
             }
@@ -492,12 +572,9 @@ __global__ void __launch_bounds__(4 * D) gdr_fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     const int64_t oi = ((t0 + t) * a.hv + h) * D + colw + 16 * nt + 4 * lq;
-                    const f32x4 val = Ot[blk][nt] * a.scale;
+                    const f32x4 val = Ot[blk][nt];
                     if constexpr (IN_BF16) {
-                        uint2 st;
-                        st.x = bf16_bits(val[0]) | (static_cast<uint32_t>(bf16_bits(val[1])) << 16);
-                        st.y = bf16_bits(val[2]) | (static_cast<uint32_t>(bf16_bits(val[3])) << 16);
-                        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.o) + oi) = st;
+                        *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(a.o) + oi) = cvt4(val);
                     } else {
                         *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.o) + oi) =
                             make_float4(val[0], val[1], val[2], val[3]);
@@ -507,7 +584,7 @@ __global__ void __launch_bounds__(4 * D) gdr_fwd_kernel(FwdArgs a) {
         }
     };
 
-    // H <- e^{G_L} H + K^T diag(e^{G_L - G}) Vnew
+    // chain: H <- e^{G_L} H + K^T diag(e^{G_L - G}) Vnew
     auto chain_h = [&](int par) {
         const uint16_t *kt = sKT0 + par * D * PT;
         const float gl = sGL[par];
@@ -521,9 +598,9 @@ __global__ void __launch_bounds__(4 * D) gdr_fwd_kernel(FwdArgs a) {
         }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const uint16_t *pkt = kt + (16 * kb + l16) * PT + 4 * lq;
-            const bf16x8 a01 = cat(ld4(pkt), ld4(pkt + 16));
-            const bf16x8 a23 = cat(ld4(pkt + 32), ld4(pkt + 48));
+            const uint16_t *pkt = kt + (16 * kb + l16) * PT + 8 * lq;
+            const bf16x8 a01 = ld8(pkt);
+            const bf16x8 a23 = ld8(pkt + 32);
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
                 f32x4 s = hs[kb][nt] * gl;
@@ -534,71 +611,72 @@ __global__ void __launch_bounds__(4 * D) gdr_fwd_kernel(FwdArgs a) {
         }
     };
 
-    // H^T Q^T for the chunk staged in sQ (before the e^G row scaling)
-    auto chain_qh = [&]() {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) hb[kb][nt] = cvt4(hs[kb][nt]);
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = zero4();
-            const uint16_t *pq_ = sQ + (16 * blk + l16) * PK + 4 * lq;
-#pragma unroll
-            for (int p = 0; p < KB / 2; ++p) {
-                const bf16x8 bq = cat(ld4(pq_ + 32 * p), ld4(pq_ + 32 * p + 16));
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt)
-                    Ot[blk][nt] = mfma32(cat(hb[2 * p][nt], hb[2 * p + 1][nt]), bq, Ot[blk][nt]);
-            }
-        }
-    };
-
-    // ---- prologue: prepare chunk 0
-    load_chunk(0);
-    stage_chunk(0);
-    load_chunk(1);   // all zero when there is no chunk 1
-    __syncthreads();
-    prep_kq(0);
-    __syncthreads();
-    if (wave < 4) prep_inv();
-    __syncthreads();
-    prep_solve(0);
-    chain_qh();
-    __syncthreads();
-
-    // The preparation stream runs unconditionally: past the last chunk it
-    // works on zero rows and its results are never read.
-    for (int64_t c = 0; c < nch; ++c) {
-        const int par = static_cast<int>(c & 1), npar = par ^ 1;
-        // P1
-        stage_chunk(npar);
-        load_chunk(c + 2);
-        chain_vnew();
-        __syncthreads();
-        // P2
-        prep_kq(npar);
-        chain_out(par, bos + c * C, chunk_len(c));
-        __syncthreads();
-        // P3
-        if (wave < 4) prep_inv();
-        chain_h(par);
-        __syncthreads();
-        // P4
-        prep_solve(npar);
-        chain_qh();
-        __syncthreads();
-    }
-
-    if (a.ht) {
+    // The two roles run separate loops with the same barrier sequence: 4
+    // barriers for the prologue (preparation of chunk 0), then 4 per chunk.
+    // (s_barrier counts arriving waves; the roles are uniform per wave.)
+    if (chain) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    a.ht[sbase + (16 * kb + 4 * lq + r) * D + colw + 16 * nt + l16] = hs[kb][nt][r];
+                    hs[kb][nt][r] = a.h0 ? a.h0[sbase + (16 * kb + 4 * lq + r) * D + colw + 16 * nt + l16] : 0.f;
+        load_v(0);
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
+        for (int64_t c = 0; c < nch; ++c) {
+            const int par = static_cast<int>(c & 1);
+            {   // P1: U solve and Vnew of chunk c
+                f32x4 U[4][NTW];
+                chain_usolve(par, U);
+                chain_vnew(U);
+            }
+            __syncthreads();
+            chain_out(par, bos + c * C, chunk_len(c));   // P2
+            __syncthreads();
+            chain_h(par);                                 // P3
+            __syncthreads();
+            load_v(c + 1);                                // P4 (zero past the end)
+            __syncthreads();
+        }
+        if (a.ht) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        a.ht[sbase + (16 * kb + 4 * lq + r) * D + colw + 16 * nt + l16] = hs[kb][nt][r];
+        }
+    } else {
+        // prologue: chunk 0
+        load_qk(0);
+        stage(0);
+        load_qk(1);   // zero when there is no chunk 1
+        __syncthreads();
+        prep_kq(0);
+        __syncthreads();
+        prep_inv();
+        __syncthreads();
+        prep_wsolve(0);
+        __syncthreads();
+        // chunk c+1 while the chain works on chunk c; past the last chunk the
+        // preparation runs on zero rows and its results are never read
+        for (int64_t c = 0; c < nch; ++c) {
+            const int npar = static_cast<int>((c + 1) & 1);
+            stage(npar);          // P1
+            load_qk(c + 2);
+            __syncthreads();
+            prep_kq(npar);        // P2
+            __syncthreads();
+            prep_inv();           // P3
+            __syncthreads();
+            prep_wsolve(npar);    // P4
+            __syncthreads();
+        }
     }
 }
 
@@ -734,7 +812,7 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(a.n_seq * a.hv)), dim3(fwd_threads(D)), lds,
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(a.n_seq * a.hv)), dim3(kFwdThreads), lds,
                        stream, a);
     return hipGetLastError();
 }
