@@ -49,6 +49,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 
 constexpr int C = kChunk;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -122,6 +124,25 @@ __device__ __forceinline__ uint4 load8(const void *p, int64_t i) {
     }
 }
 
+// two 4-element pieces of a row as 8 bf16 (16 bytes); f32 inputs are rounded
+template <bool BF16>
+__device__ __forceinline__ uint4 load4x2(const void *p, int64_t i0, int64_t i1) {
+    if constexpr (BF16) {
+        const uint2 x = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i0);
+        const uint2 y = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i1);
+        return make_uint4(x.x, x.y, y.x, y.y);
+    } else {
+        const float4 x = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + i0);
+        const float4 y = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + i1);
+        uint4 r;
+        r.x = bf16_bits(x.x) | (static_cast<uint32_t>(bf16_bits(x.y)) << 16);
+        r.y = bf16_bits(x.z) | (static_cast<uint32_t>(bf16_bits(x.w)) << 16);
+        r.z = bf16_bits(y.x) | (static_cast<uint32_t>(bf16_bits(y.y)) << 16);
+        r.w = bf16_bits(y.z) | (static_cast<uint32_t>(bf16_bits(y.w)) << 16);
+        return r;
+    }
+}
+
 __device__ __forceinline__ uint16_t elem8(const uint4 &v, int e) {
     const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
     return static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xFFFFu));
@@ -143,16 +164,18 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 //              the fp32 state and computes the U half of the WY solve, Vnew,
 //              the output and the state update of chunk c;
 //   waves 4-7  prepare chunk c+1 meanwhile: staging of q and k, K K^T and
-//              Q K^T, K^T, the 16x16 diagonal inverses and the W half of the
-//              WY solve; they prefetch chunk c+2 from HBM into registers.
+//              Q K^T, K^T and the four 16x16 diagonal inverses; they prefetch
+//              chunk c+2 from HBM into registers.
+//   all 8      share the W half of the WY solve of chunk c+1.
 // Each SIMD hosts one wave of each kind, so the hardware interleaves the
 // chain's dependent MFMAs with the preparation's loads, LDS traffic and VALU.
 //
 // Per iteration c (4 barriers):
 //   P1  stage c+1 (q, k), gates c+1, prefetch c+2  | U solve c; Vnew_c = U_c - W_c H
-//   P2  A, P = gated K K^T, Q K^T (c+1); K^T (c+1)  | O_c^T = e^G H^T Q^T + Vnew^T P^T, store
+//   P2  A, P = gated K K^T, Q K^T (c+1); K^T (c+1)  | prefetch v of c+1;
+//                                                   |   O_c^T = e^G H^T Q^T + Vnew^T P^T, store
 //   P3  diagonal inverses (c+1)                     | H <- e^{G_L} H + K^T diag(e^{G_L-G}) Vnew_c
-//   P4  W solve (c+1) -> -W                         | prefetch v of c+1
+//   P4  W solve (c+1) -> -W, half the columns       | the other half
 //
 // Shared matrices keep each 32-wide k range with its 4-element groups in the
 // order 0,4,1,5,2,6,3,7 (pc below), so the 8 k values a lane feeds to one
@@ -187,6 +210,34 @@ struct FwdLds {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer resource over [base, base + bytes): loads past the end return 0
+// and stores past it are dropped, so one resource per chunk covers exactly the
+// chunk's rows and the padding needs no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+template <int BYTES>
+__device__ __forceinline__ auto buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (BYTES == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    else if constexpr (BYTES == 4) return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    else if constexpr (BYTES == 8) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+// 4 consecutive elements at byte offset off as bf16 (f32 inputs are rounded).
+// The loaded value is always bit-cast whole: indexing the builtin's result
+// directly lets the compiler narrow the load to its first dword.
+template <bool BF16>
+__device__ __forceinline__ bf16x4 buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (BF16) return __builtin_bit_cast(bf16x4, buf_load<8>(r, off));
+    else return cvt4(__builtin_bit_cast(f32x4, buf_load<16>(r, off)));
+}
+template <bool BF16>
+__device__ __forceinline__ float buf_load_scalar(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (BF16) return __uint_as_float(static_cast<uint32_t>(buf_load<2>(r, off)) << 16);
+    else return __builtin_bit_cast(float, buf_load<4>(r, off));
+}
+
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     using Ly = FwdLds<D>;
@@ -198,6 +249,8 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     constexpr int TG = 256 / FG;   // staging: token groups over the 4 prep waves
     constexpr int TPT = C / TG;    // staging: tokens per prep thread
     static_assert(KB % 2 == 0 && NTW >= 1 && (TPT == 2 || TPT == 4), "unsupported head dim");
+    constexpr uint32_t ES = IN_BF16 ? 2 : 4;      // bytes per q/k/v/o element
+    constexpr uint32_t GES = GATE_BF16 ? 2 : 4;   // bytes per g/beta element
 
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t *const sQ0 = reinterpret_cast<uint16_t *>(smem + Ly::oQ);
@@ -264,68 +317,56 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 
     const int64_t sbase = (n * a.hv + h) * static_cast<int64_t>(D) * D;
 
-    // chain: v of chunk c as A fragments (rows past the segment end are zero)
+    // chain: v of chunk c as A fragments (rows past the segment end read as zero)
     auto load_v = [&](int64_t c) {
         const int64_t t0 = bos + c * C;
-        const int L = chunk_len(c);
+        const uint32_t rowb = static_cast<uint32_t>(a.hv) * D * ES;
+        const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(
+            reinterpret_cast<const unsigned char *>(a.v) + ((t0 * a.hv + h) * D) * ES, chunk_len(c) * rowb);
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const int t = 16 * blk + l16;
+        for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                bf16x4 x = {};
-                if (t < L) {
-                    const int64_t vi = ((t0 + t) * a.hv + h) * D + colw + 16 * nt + 4 * lq;
-                    if constexpr (IN_BF16) {
-                        x = *reinterpret_cast<const bf16x4 *>(reinterpret_cast<const uint16_t *>(a.v) + vi);
-                    } else {
-                        const float4 f = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.v) + vi);
-                        x = cvt4(f32x4{f.x, f.y, f.z, f.w});
-                    }
-                }
-                vp[blk][nt] = x;
-            }
-        }
+            for (int nt = 0; nt < NTW; ++nt)
+                vp[blk][nt] = buf_load4<IN_BF16>(rv, (16 * blk + l16) * rowb + (colw + 16 * nt + 4 * lq) * ES);
     };
 
-    // prep: q, k rows and gates of chunk c into registers (zero past the end)
+    // prep: q, k rows and gates of chunk c into registers (zero past the end).
+    // Thread (tg, fg) holds, for each of its tokens, the 16 bytes that land at
+    // physical columns 8fg..8fg+7: logical groups m and m+4 of 32-range fg/4.
     auto load_qk = [&](int64_t c) {
         const int64_t t0 = bos + c * C;
         const int L = chunk_len(c);
         const int pt = tid - 256, fg = pt % FG, tg = pt / FG;
+        const uint32_t e0 = 32 * (fg >> 2) + 4 * (fg & 3);   // logical columns e0.. and e0+16..
+        const uint32_t rowb = static_cast<uint32_t>(a.hk) * D * ES;
+        const int64_t base = (t0 * a.hk + hk) * D * ES;
+        const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(reinterpret_cast<const unsigned char *>(a.q) + base, L * rowb);
+        const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(reinterpret_cast<const unsigned char *>(a.k) + base, L * rowb);
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
-            const int t = tg * TPT + j;
-            if (t < L) {
-                const int64_t row = ((t0 + t) * a.hk + hk) * D + fg * 8;
-                pq[j] = load8<IN_BF16>(a.q, row);
-                pk[j] = load8<IN_BF16>(a.k, row);
-            } else {
-                pq[j] = pk[j] = make_uint4(0, 0, 0, 0);
-            }
+            const uint32_t off = (tg * TPT + j) * rowb + e0 * ES;
+            pq[j] = __builtin_bit_cast(uint4, cat(buf_load4<IN_BF16>(rq, off), buf_load4<IN_BF16>(rq, off + 16 * ES)));
+            pk[j] = __builtin_bit_cast(uint4, cat(buf_load4<IN_BF16>(rk, off), buf_load4<IN_BF16>(rk, off + 16 * ES)));
         }
         if (role == 0) {
-            pg = pb = 0.f;
-            if (lane < L) {
-                const int64_t gi = (t0 + lane) * a.hv + h;
-                pg = load_scalar<GATE_BF16>(a.g, gi);
-                pb = load_scalar<GATE_BF16>(a.beta, gi);
-            }
+            const uint32_t growb = static_cast<uint32_t>(a.hv) * GES;
+            const int64_t gbase = (t0 * a.hv + h) * GES;
+            const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(reinterpret_cast<const unsigned char *>(a.g) + gbase, L * growb);
+            const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(reinterpret_cast<const unsigned char *>(a.beta) + gbase, L * growb);
+            pg = buf_load_scalar<GATE_BF16>(rg, lane * growb);
+            pb = buf_load_scalar<GATE_BF16>(rb, lane * growb);
         }
     };
 
     // prep: registers -> LDS (permuted rows of q and k) and the gate vectors
     auto stage = [&](int par) {
         const int pt = tid - 256, fg = pt % FG, tg = pt / FG;
-        const int c0 = pc(fg * 8), c1 = pc(fg * 8 + 4);
         uint16_t *sQ = sQ0 + par * C * PK;
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
             const int t = tg * TPT + j;
-            *reinterpret_cast<uint2 *>(sQ + t * PK + c0) = make_uint2(pq[j].x, pq[j].y);
-            *reinterpret_cast<uint2 *>(sQ + t * PK + c1) = make_uint2(pq[j].z, pq[j].w);
-            *reinterpret_cast<uint2 *>(sK + t * PK + c0) = make_uint2(pk[j].x, pk[j].y);
-            *reinterpret_cast<uint2 *>(sK + t * PK + c1) = make_uint2(pk[j].z, pk[j].w);
+            *reinterpret_cast<uint4 *>(sQ + t * PK + 8 * fg) = pq[j];
+            *reinterpret_cast<uint4 *>(sK + t * PK + 8 * fg) = pk[j];
         }
         if (role == 0) {
             const float G2 = wave_inclusive_scan(pg, lane) * kLog2e;
@@ -340,62 +381,80 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         }
     };
 
-    // prep: gated K K^T -> A (diagonal blocks f32 transposed, others -A bf16),
-    // gated Q K^T -> P (scale folded in); K^T of the chunk
+    // prep: gated K K^T -> A (diagonal blocks f32 transposed, others -A bf16)
+    // and gated Q K^T -> P (scale folded in), by row strips: strip i holds
+    // the tiles (i, j <= i) of both products, which share k_j as the A
+    // operand; the B operands (k_i, q_i) stay in registers across the strip.
     auto prep_kq = [&](int par) {
         uint16_t *sPp = sP0 + par * C * PP;
-        uint16_t *kt = sKT0 + par * D * PT;
         const uint16_t *sQ = sQ0 + par * C * PK;
         const float *sB = sB0 + par * C;
+        // strips per prep wave: p0 = K K^T of strip 3, p1 = strip 2, p2 = strip 1,
+        // p3 = Q K^T of strip 3 and strip 0
+        auto strip = [&](int i, bool do_kk, bool do_qk) {
+            bf16x8 bk[KB / 2], bq[KB / 2];
+            const uint16_t *pki = sK + (16 * i + l16) * PK + 8 * lq;
+            const uint16_t *pqi = sQ + (16 * i + l16) * PK + 8 * lq;
 #pragma unroll
-        for (int s = 0; s < 5; ++s) {
-            const int ti = role + 4 * s;            // 20 lower-triangular tiles, 5 per prep wave
-            const bool qk = ti >= 10;
-            const int t = qk ? ti - 10 : ti;
-            const int ib = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
-            const int jb = t - ib * (ib + 1) / 2;
-            const uint16_t *pa = sK + (16 * jb + l16) * PK + 8 * lq;
-            const uint16_t *pbp = (qk ? sQ : sK) + (16 * ib + l16) * PK + 8 * lq;
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int p = 0; p < KB / 2; ++p) acc = mfma32(ld8(pa + 32 * p), ld8(pbp + 32 * p), acc);
-            if (qk) {
-                // (row key j = 16jb+4lq+r, column query i = 16ib+l16) = k_j . q_i
-                const int i = 16 * ib + l16;
-                const float gi = sG2[i];
-                const f32x4 gj = *reinterpret_cast<const f32x4 *>(sG2 + 16 * jb + 4 * lq);
-                f32x4 out;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool keep = i >= 16 * jb + 4 * lq + r;
-                    out[r] = keep ? a.scale * fast_exp2(gi - gj[r]) * acc[r] : 0.f;
-                }
-                st4(sPp + i * PP + pc(16 * jb + 4 * lq), cvt4(out));
-            } else if (ib == jb) {
-                // symmetric: (row i = 16ib+4lq+r, column j = 16ib+l16) = k_i . k_j
-                const int j = 16 * jb + l16;
-                const float gj = sG2[j];
-                const f32x4 gi = *reinterpret_cast<const f32x4 *>(sG2 + 16 * ib + 4 * lq);
-                const f32x4 bi = *reinterpret_cast<const f32x4 *>(sB + 16 * ib + 4 * lq);
-                f32x4 out;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool keep = 16 * ib + 4 * lq + r > j;
-                    out[r] = keep ? bi[r] * fast_exp2(gi[r] - gj) * acc[r] : 0.f;
-                }
-                *reinterpret_cast<f32x4 *>(sAT + (16 * ib + l16) * PAT + 4 * lq) = out;
-            } else {
-                // (row j = 16jb+4lq+r, column i = 16ib+l16) = k_j . k_i with i > j
-                const int i = 16 * ib + l16;
-                const float gi = sG2[i], bi = sB[i];
-                const f32x4 gj = *reinterpret_cast<const f32x4 *>(sG2 + 16 * jb + 4 * lq);
-                f32x4 out;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) out[r] = -bi * fast_exp2(gi - gj[r]) * acc[r];
-                st4(sAo + i * PP + pc(16 * jb + 4 * lq), cvt4(out));
+            for (int p = 0; p < KB / 2; ++p) {
+                if (do_kk) bk[p] = ld8(pki + 32 * p);
+                if (do_qk) bq[p] = ld8(pqi + 32 * p);
             }
+            const float gi_col = sG2[16 * i + l16];
+            const float bi_col = sB[16 * i + l16];
+            for (int j = 0; j <= i; ++j) {
+                f32x4 akk = zero4(), aqk = zero4();
+                const uint16_t *pkj = sK + (16 * j + l16) * PK + 8 * lq;
+#pragma unroll
+                for (int p = 0; p < KB / 2; ++p) {
+                    const bf16x8 af = (j == i && do_kk) ? bk[p] : ld8(pkj + 32 * p);
+                    if (do_kk) akk = mfma32(af, bk[p], akk);
+                    if (do_qk) aqk = mfma32(af, bq[p], aqk);
+                }
+                // tile element (row j' = 16j+4lq+r, column i' = 16i+l16) = k_j' . k_i' (resp. . q_i')
+                const int ic = 16 * i + l16;
+                const f32x4 gj = *reinterpret_cast<const f32x4 *>(sG2 + 16 * j + 4 * lq);
+                if (do_qk) {
+                    f32x4 out;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const bool keep = ic >= 16 * j + 4 * lq + r;
+                        out[r] = keep ? a.scale * fast_exp2(gi_col - gj[r]) * aqk[r] : 0.f;
+                    }
+                    st4(sPp + ic * PP + pc(16 * j + 4 * lq), cvt4(out));
+                }
+                if (do_kk) {
+                    if (j < i) {
+                        f32x4 out;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) out[r] = -bi_col * fast_exp2(gi_col - gj[r]) * akk[r];
+                        st4(sAo + ic * PP + pc(16 * j + 4 * lq), cvt4(out));
+                    } else {
+                        // diagonal, symmetric: read it as (row i' = 16i+4lq+r, column j' = 16i+l16)
+                        const f32x4 bi = *reinterpret_cast<const f32x4 *>(sB + 16 * i + 4 * lq);
+                        f32x4 out;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const bool keep = 4 * lq + r > l16;
+                            out[r] = keep ? bi[r] * fast_exp2(gj[r] - gi_col) * akk[r] : 0.f;
+                        }
+                        *reinterpret_cast<f32x4 *>(sAT + (16 * i + l16) * PAT + 4 * lq) = out;
+                    }
+                }
+            }
+        };
+        if (role == 0) strip(3, true, false);
+        else if (role == 1) strip(2, true, true);
+        else if (role == 2) strip(1, true, true);
+        else {
+            strip(3, false, true);
+            strip(0, true, true);
         }
-        // K^T tiles (token block blk, dk block kb) through an identity product
+    };
+
+    // prep: K^T tiles (token block blk, dk block kb) through identity products
+    auto prep_kt = [&](int par) {
+        uint16_t *kt = sKT0 + par * D * PT;
 #pragma unroll
         for (int s = 0; s < KB; ++s) {
             const int tt = role + 4 * s;            // 4*KB tiles, KB per prep wave
@@ -407,24 +466,30 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         }
     };
 
-    // prep: inverse of diagonal block p of I + A (lane = column), right-looking, f32
-    auto prep_inv = [&]() {
-        const int blk = role, c = l16;
-        const float *at = sAT + blk * 16 * PAT;
-        float x[16];
+    // inverse of diagonal block `role` of I + A.  With L the strictly lower
+    // block, L^16 = 0 and (I + L)^-1 = sum_{k<16} (-L)^k: 14 chained one-block
+    // MFMAs L^k = L L^(k-1) (each power's C layout is the next B operand),
+    // accumulated in f32; an identity product then transposes the C layout of
+    // D into rows so it is stored row-major.
+    auto block_inv = [&]() {
+        const float *at = sAT + role * 16 * PAT;
+        const f32x4 cl = *reinterpret_cast<const f32x4 *>(at + l16 * PAT + 4 * lq);   // L[4lq+r][l16]
+        f32x4 al;                                                                      // L[l16][4lq+r]
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+        for (int r = 0; r < 4; ++r) al[r] = at[(4 * lq + r) * PAT + l16];
+        const bf16x4 alb = cvt4(al);
+        f32x4 sum = -cl, pw = cl;
 #pragma unroll
-        for (int j = 0; j < 15; ++j) {
-            const float xj = x[j];
-#pragma unroll
-            for (int i = j + 1; i < 16; ++i) x[i] -= at[j * PAT + i] * xj;
+        for (int k = 2; k < 16; ++k) {
+            pw = mfma16z(alb, cvt4(pw), zero4());
+            sum = (k & 1) ? sum - pw : sum + pw;
         }
-        if (lane < 16) {
-            uint16_t *di = sDi + blk * 16 * PDI + c;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) di[i * PDI] = bf16_bits(x[i]);
-        }
+        for (int r = 0; r < 4; ++r)
+            if (4 * lq + r == l16) sum[r] += 1.f;
+        const bf16x4 db = cvt4(sum);
+        const f32x4 dt = mfma32(__builtin_shufflevector(db, bf16x4{}, 0, 1, 2, 3, 4, 5, 6, 7), ident, zero4());
+        st4(sDi + (16 * role + l16) * PDI + 4 * lq, cvt4(dt));   // D[l16][4lq..4lq+3]
     };
 
     // block forward substitution X_a = D_a (R_a - sum_{c<a} A_ac X_c) on NTW tiles;
@@ -457,20 +522,34 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         }
     };
 
-    // prep: W columns colw.. of the chunk -> sW as -W (row token, k = dk permuted)
-    auto prep_wsolve = [&](int par) {
+    // the same substitution for a single 16-column tile
+    auto solve1 = [&](auto rhs, auto out) {
+        bf16x4 Xb[4];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            f32x4 R = rhs(blk);
+            const uint16_t *ar = sAo + (16 * blk + l16) * PP;
+            if (blk >= 2) R = mfma32(ld8(ar + 8 * lq), cat(Xb[0], Xb[1]), R);
+            if (blk & 1) R = mfma16z(ld4(ar + pc(16 * (blk - 1) + 4 * lq)), Xb[blk - 1], R);
+            const f32x4 X = mfma16z(ld4(sDi + (16 * blk + l16) * PDI + 4 * lq), cvt4(R), zero4());
+            Xb[blk] = cvt4(X);
+            out(blk, X);
+        }
+    };
+
+    // W columns 16*wt..16*wt+15 of the chunk -> sW as -W (row token, k = dk permuted)
+    auto wsolve_tile = [&](int par, int wt) {
         const uint16_t *kt = sKT0 + par * D * PT;
-        solve([&](int blk, int nt) {
-                  const f32x4 bg = *reinterpret_cast<const f32x4 *>(sBG + 16 * blk + 4 * lq);
-                  return up4(ld4(kt + (colw + 16 * nt + l16) * PT + pc(16 * blk + 4 * lq))) * bg;
-              },
-              [&](int blk, int nt, f32x4 X, bf16x4 Xb) {
-                  // transpose -W through an identity product: (row dk, column token)
-                  const bf16x4 nx = cvt4(-X);
-                  const f32x4 y = mfma32(__builtin_shufflevector(nx, bf16x4{}, 0, 1, 2, 3, 4, 5, 6, 7), ident, zero4());
-                  st4(sW + (16 * blk + l16) * PK + pc(colw + 16 * nt + 4 * lq), cvt4(y));
-                  (void)Xb;
-              });
+        solve1([&](int blk) {
+                   const f32x4 bg = *reinterpret_cast<const f32x4 *>(sBG + 16 * blk + 4 * lq);
+                   return up4(ld4(kt + (16 * wt + l16) * PT + pc(16 * blk + 4 * lq))) * bg;
+               },
+               [&](int blk, f32x4 X) {
+                   // transpose -W through an identity product: (row dk, column token)
+                   const bf16x4 nx = cvt4(-X);
+                   const f32x4 y = mfma32(__builtin_shufflevector(nx, bf16x4{}, 0, 1, 2, 3, 4, 5, 6, 7), ident, zero4());
+                   st4(sW + (16 * blk + l16) * PK + pc(16 * wt + 4 * lq), cvt4(y));
+               });
     };
 
     // chain: U columns colw.. of the chunk in vp (solved with that chunk's A, D and beta)
@@ -537,6 +616,8 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 
     // chain: O^T = diag(scale e^G) (H^T Q^T) + Vnew^T P^T (P carries the scale), stored 4 dv per lane
     auto chain_out = [&](int par, int64_t t0, int L) {
+        const uint32_t rowb = static_cast<uint32_t>(a.hv) * D * ES;
+        const __amdgpu_buffer_rsrc_t ro = chunk_rsrc(reinterpret_cast<unsigned char *>(a.o) + ((t0 * a.hv + h) * D) * ES, L * rowb);
         const uint16_t *sPp = sP0 + par * C * PP;
         const float *gam = sGam0 + par * C;
         f32x4 Ot[4][NTW];
@@ -567,19 +648,14 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = mfma16z(Vb[blk][nt], bf, Ot[blk][nt]);
             }
-            const int t = 16 * blk + l16;
-            if (t < L) {
+            const uint32_t orow = (16 * blk + l16) * rowb;
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) {
-                    const int64_t oi = ((t0 + t) * a.hv + h) * D + colw + 16 * nt + 4 * lq;
-                    const f32x4 val = Ot[blk][nt];
-                    if constexpr (IN_BF16) {
-                        *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(a.o) + oi) = cvt4(val);
-                    } else {
-                        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.o) + oi) =
-                            make_float4(val[0], val[1], val[2], val[3]);
-                    }
-                }
+            for (int nt = 0; nt < NTW; ++nt) {
+                const uint32_t off = orow + (colw + 16 * nt + 4 * lq) * ES;
+                if constexpr (IN_BF16)
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, cvt4(Ot[blk][nt])), ro, off, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, Ot[blk][nt]), ro, off, 0, 0);
             }
         }
     };
@@ -611,6 +687,11 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         }
     };
 
+    // W tiles of the solve: D/16 of them, wave w takes tile w (at D = 64 only
+    // the preparation waves have one)
+    constexpr int WT = KB;
+    const int my_wt = WT == 8 ? wave : (chain ? -1 : role);
+
     // The two roles run separate loops with the same barrier sequence: 4
     // barriers for the prologue (preparation of chunk 0), then 4 per chunk.
     // (s_barrier counts arriving waves; the roles are uniform per wave.)
@@ -626,20 +707,22 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         __syncthreads();
         __syncthreads();
         __syncthreads();
+        if (my_wt >= 0) wsolve_tile(0, my_wt);
         __syncthreads();
         for (int64_t c = 0; c < nch; ++c) {
-            const int par = static_cast<int>(c & 1);
+            const int par = static_cast<int>(c & 1), npar = par ^ 1;
             {   // P1: U solve and Vnew of chunk c
                 f32x4 U[4][NTW];
                 chain_usolve(par, U);
                 chain_vnew(U);
             }
             __syncthreads();
-            chain_out(par, bos + c * C, chunk_len(c));   // P2
+            load_v(c + 1);                                // P2 (zero past the end)
+            chain_out(par, bos + c * C, chunk_len(c));
             __syncthreads();
             chain_h(par);                                 // P3
             __syncthreads();
-            load_v(c + 1);                                // P4 (zero past the end)
+            if (my_wt >= 0) wsolve_tile(npar, my_wt);     // P4 (chunk c+1)
             __syncthreads();
         }
         if (a.ht) {
@@ -658,10 +741,11 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         load_qk(1);   // zero when there is no chunk 1
         __syncthreads();
         prep_kq(0);
+        prep_kt(0);
         __syncthreads();
-        prep_inv();
+        block_inv();
         __syncthreads();
-        prep_wsolve(0);
+        if (my_wt >= 0) wsolve_tile(0, my_wt);
         __syncthreads();
         // chunk c+1 while the chain works on chunk c; past the last chunk the
         // preparation runs on zero rows and its results are never read
@@ -671,10 +755,11 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             load_qk(c + 2);
             __syncthreads();
             prep_kq(npar);        // P2
+            prep_kt(npar);
             __syncthreads();
-            prep_inv();           // P3
+            block_inv();          // P3
             __syncthreads();
-            prep_wsolve(npar);    // P4
+            if (my_wt >= 0) wsolve_tile(npar, my_wt);   // P4
             __syncthreads();
         }
     }
