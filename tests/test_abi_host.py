@@ -75,7 +75,7 @@ def test_plan_varlen(lib):
     p = gdr.plan(**fwd_descs(T=1000, N=5), scale=0.1)
     assert p["n_seq"] == 5 and p["hv"] == 4 and p["hk"] == 2 and p["d"] == 128
     assert p["nt_max"] == (1000 + 63) // 64 + 5
-    assert p["grid_fwd"] == 5 * 4 and p["block_fwd"] == 256
+    assert p["grid_fwd"] == 5 * 4 and p["block_fwd"] == 512
     assert 0 < p["lds_fwd"] <= 160 * 1024
     assert p["workspace_bytes"] == 4 * 5 and p["varlen"] == 1
 
