@@ -7,6 +7,17 @@ fp32 state, per-segment initial state.  Inputs are resident in HBM before the
 timed region.  Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Two helper modes feed the HBM traffic figure of the roofline object:
+  python bench.py --copy-probe-mib M     a plain device copy of M MiB (one
+                                         elementwise kernel that reads M MiB
+                                         and writes M MiB), run under
+                                         rocprofv3 --pmc to calibrate the
+                                         FETCH_SIZE / WRITE_SIZE counters;
+  python bench.py --traffic-summary FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR --copy-probe-mib M
+                                         reads the counter CSVs of those four
+                                         rocprofv3 runs and writes the traffic
+                                         summary that later bench runs report.
 """
 from __future__ import annotations
 
@@ -59,12 +70,17 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="v-heads of every segment the CPU baseline runs (a bounded sample)")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_fwd_packed64k.json"))
+    ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "fwd_packed64k_traffic.txt"))
+    ap.add_argument("--copy-probe-mib", type=int, default=0)
+    ap.add_argument("--traffic-summary", nargs=4, metavar="DIR", default=None)
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(args)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -79,6 +95,9 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
     gdr.library()
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     w = gi.WORKLOADS[args.workload]
     d = gi.generate(w)
     dev = torch.device("cuda:0")
@@ -125,15 +144,7 @@ def main():
     f_min = flops_min(w.dk, w.dv, w.hv // w.hk) * tokens * w.hv
     nbytes = bytes_alg(tokens, N, w.hk, w.hv, w.dk, w.dv, in_bytes, in_bytes)
     achieved_tflops = f_chunk / (launch_ms * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            with open(args.traffic_json) as f:
-                tj = json.load(f)
-            if tj.get("workload") == w.name and tj.get("kernel_source_sha") == kernel_source_sha():
-                traffic = tj.get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = read_traffic(args.traffic_file, w.name)
 
     out = {
         "metric": METRIC,
@@ -169,6 +180,104 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, w, args.cpu_heads)
     print(json.dumps(out), flush=True)
+
+
+FWD_KERNEL = "gdr_fwd_kernel"
+COPY_KERNEL = "neg_kernel"
+
+
+def copy_probe(mib: int):
+    """A plain copy of known size: torch's elementwise negation of an fp32
+    buffer into another reads and writes mib MiB once each."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4}), flush=True)
+
+
+def _counter_rows(d: str, counter: str, kernel_substr: str):
+    """Per-dispatch values of one counter for the kernels whose name contains
+    kernel_substr, from a rocprofv3 --pmc run written with -f csv under d."""
+    import csv
+    import glob
+    vals = {}
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no *counter_collection.csv under %s" % d)
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter or kernel_substr not in row.get("Kernel_Name", ""):
+                    continue
+                key = (fn, row.get("Dispatch_Id"))
+                vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+    if not vals:
+        raise SystemExit("no %s rows for kernels matching %r under %s" % (counter, kernel_substr, d))
+    return list(vals.values())
+
+
+def traffic_summary(args):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the fused kernel,
+    each divided by the factor the same counter reads on the copy probe
+    (counter bytes / true bytes), written as key: value lines."""
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_summary
+    if not args.copy_probe_mib:
+        raise SystemExit("--traffic-summary needs --copy-probe-mib (the size the copy probe ran with)")
+    true_bytes = args.copy_probe_mib * (1 << 20)
+    avg = lambda xs: sum(xs) / len(xs)
+    fetch = _counter_rows(fetch_dir, "FETCH_SIZE", FWD_KERNEL)
+    write = _counter_rows(write_dir, "WRITE_SIZE", FWD_KERNEL)
+    cfetch = _counter_rows(cfetch_dir, "FETCH_SIZE", COPY_KERNEL)
+    cwrite = _counter_rows(cwrite_dir, "WRITE_SIZE", COPY_KERNEL)
+    f_fetch = avg(cfetch) * 1024.0 / true_bytes
+    f_write = avg(cwrite) * 1024.0 / true_bytes
+    fetch_b = avg(fetch) * 1024.0 / f_fetch
+    write_b = avg(write) * 1024.0 / f_write
+    import gdr_inputs as gi
+    w = gi.WORKLOADS[args.workload]
+    lines = [
+        "# HBM traffic of %s on %s (rocprofv3 --pmc, KiB per dispatch)" % (FWD_KERNEL, w.name),
+        "workload: %s" % w.name,
+        "kernel_source_sha: %s" % kernel_source_sha(),
+        "fwd_dispatches: %d" % len(fetch),
+        "fwd_fetch_kib_avg: %.1f" % avg(fetch),
+        "fwd_write_kib_avg: %.1f" % avg(write),
+        "copy_probe_bytes: %d" % true_bytes,
+        "copy_dispatches: %d" % len(cfetch),
+        "copy_fetch_kib_avg: %.1f" % avg(cfetch),
+        "copy_write_kib_avg: %.1f" % avg(cwrite),
+        "fetch_factor: %.4f" % f_fetch,
+        "write_factor: %.4f" % f_write,
+        "fwd_fetch_bytes: %.0f" % fetch_b,
+        "fwd_write_bytes: %.0f" % write_b,
+        "bytes_per_launch: %.0f" % (fetch_b + write_b),
+    ]
+    with open(args.traffic_file, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_traffic(path: str, workload: str):
+    """bytes_per_launch of the traffic summary, or None when it is missing or
+    was taken on another workload or another version of the kernel sources."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("workload") != workload or kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def kernel_source_sha() -> str:
