@@ -9,8 +9,8 @@
 // chunk-local gate prefix sums G (all exponents below are <= 0):
 //
 //   A_ij  = b_i exp(G_i - G_j) (k_i . k_j)    for j < i
-//   [W|U] = (I + A)^-1 [diag(b e^G) K | diag(b) V]        (the WY form)
-//   Vnew  = U - W H0
+//   Vnew  = (I + A)^-1 (diag(b) V - diag(b e^G) K H0)
+//           (= U - W H0 of the WY form, without forming W or U)
 //   O     = scale (diag(e^G) Q H0 + P Vnew),  P_ij = exp(G_i - G_j) (q_i . k_j), j <= i
 //   H     = e^{G_L} H0 + K^T diag(e^{G_L - G}) Vnew
 //
@@ -161,21 +161,26 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 // Fused forward, warp-specialised.  One work-group of 8 waves walks one
 // (sequence, v-head) through its chunks in order:
 //   waves 0-3  the state chain: wave c owns dv columns [c*D/4, (c+1)*D/4) of
-//              the fp32 state and computes the U half of the WY solve, Vnew,
-//              the output and the state update of chunk c;
-//   waves 4-7  prepare chunk c+1 meanwhile: staging of q and k, K K^T and
-//              Q K^T, K^T and the four 16x16 diagonal inverses; they prefetch
-//              chunk c+2 from HBM into registers.
-//   all 8      share the W half of the WY solve of chunk c+1.
-// Each SIMD hosts one wave of each kind, so the hardware interleaves the
-// chain's dependent MFMAs with the preparation's loads, LDS traffic and VALU.
+//              the fp32 state and, for chunk c, computes
+//                R    = diag(b) V - diag(b e^G) K H
+//                Vnew = (I + A)^-1 R          (block forward substitution)
+//                O    = diag(scale e^G) Q H + P Vnew
+//                H   <- e^{G_L} H + K^T diag(e^{G_L - G}) Vnew;
+//   waves 4-7  prepare chunk c+1 meanwhile: staging of q and k and the gate
+//              vectors, gated K K^T and Q K^T (A and P), K^T and the four
+//              16x16 diagonal inverses of (I + A); they prefetch chunk c+2 of
+//              q and k from HBM into registers.
+// Substituting the within-chunk unrolled state into the delta correction
+// gives (I + A) Vnew = diag(b) V - diag(b e^G) K H directly, so the W half
+// of the WY form is never built.
 //
-// Per iteration c (4 barriers):
-//   P1  stage c+1 (q, k), gates c+1, prefetch c+2  | U solve c; Vnew_c = U_c - W_c H
-//   P2  A, P = gated K K^T, Q K^T (c+1); K^T (c+1)  | prefetch v of c+1;
-//                                                   |   O_c^T = e^G H^T Q^T + Vnew^T P^T, store
-//   P3  diagonal inverses (c+1)                     | H <- e^{G_L} H + K^T diag(e^{G_L-G}) Vnew_c
-//   P4  W solve (c+1) -> -W, half the columns       | the other half
+// Every buffer the chain reads for chunk c is double-buffered by chunk
+// parity, so one barrier per chunk separates the roles.  Inside a chunk the
+// preparation waves wait for each other once (staging -> products) on an
+// LDS counter; each of them inverts the diagonal block its own strip of
+// K K^T produced, so no other cross-wave wait is needed.  Each SIMD hosts one
+// wave of each kind, so the hardware interleaves the chain's dependent MFMAs
+// with the preparation's loads, LDS traffic and VALU.
 //
 // Shared matrices keep each 32-wide k range with its 4-element groups in the
 // order 0,4,1,5,2,6,3,7 (pc below), so the 8 k values a lane feeds to one
@@ -187,25 +192,30 @@ __device__ __forceinline__ bf16x8 ld8(const uint16_t *p) {   // 16-byte LDS read
     return *reinterpret_cast<const bf16x8 *>(p);
 }
 __device__ __forceinline__ void st4(uint16_t *p, bf16x4 v) { *reinterpret_cast<bf16x4 *>(p) = v; }
+__device__ __forceinline__ bf16x8 ext8(bf16x4 a) { return __builtin_shufflevector(a, bf16x4{}, 0, 1, 2, 3, 4, 5, 6, 7); }
+
+// wait until this wave's LDS accesses are complete (also a compiler barrier)
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int D>
 struct FwdLds {
-    static constexpr int PK = D + 8;    // [64][D] bf16, k permuted: q (two buffers), k, -W
-    static constexpr int PT = C + 8;    // [D][64] bf16, tokens permuted: k^T (two buffers)
-    static constexpr int PP = C + 8;    // [64][64] bf16, keys permuted: P (two buffers), -A off the diagonal
-    static constexpr int PAT = 20;      // [4][16][16] f32: diagonal blocks of A, transposed
-    static constexpr int PDI = 24;      // [4][16][16] bf16: inverses of the diagonal blocks
+    static constexpr int PK = D + 8;    // [64][D] bf16 rows, k permuted: q and k, two buffers each
+    static constexpr int PT = C + 8;    // [D][64] bf16, tokens permuted: k^T, two buffers
+    static constexpr int PP = C + 8;    // [64][64] bf16, keys permuted: P and -A off the diagonal, two buffers each
+    static constexpr int PAT = 20;      // [4][16][16] f32: diagonal blocks of A, transposed (preparation only)
+    static constexpr int PDI = 24;      // [4][16][16] bf16: inverses of the diagonal blocks, two buffers
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + 2 * C * PK * 2;
-    static constexpr int oW = oK + C * PK * 2;
-    static constexpr int oKT = oW + C * PK * 2;
+    static constexpr int oKT = oK + 2 * C * PK * 2;
     static constexpr int oP = oKT + 2 * D * PT * 2;
     static constexpr int oAo = oP + 2 * C * PP * 2;
-    static constexpr int oAT = oAo + C * PP * 2;
+    static constexpr int oAT = oAo + 2 * C * PP * 2;
     static constexpr int oDi = oAT + 4 * 16 * PAT * 4;
-    static constexpr int oS = oDi + 4 * 16 * PDI * 2;
-    // f32 vectors of 64: G*log2(e), beta*e^G, beta (x2), scale*e^G (x2), e^{G_L-G} (x2); then e^{G_L} (x2)
-    static constexpr int bytes = oS + 8 * C * 4 + 16;
+    static constexpr int oS = oDi + 2 * 4 * 16 * PDI * 2;
+    // f32 vectors of 64: G*log2(e) (preparation only); per buffer beta,
+    // beta*e^G, scale*e^G, e^{G_L-G}; then e^{G_L} per buffer and the
+    // preparation waves' arrival counter
+    static constexpr int bytes = oS + 9 * C * 4 + 16;
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -238,35 +248,50 @@ __device__ __forceinline__ float buf_load_scalar(__amdgpu_buffer_rsrc_t r, uint3
     else return __builtin_bit_cast(float, buf_load<4>(r, off));
 }
 
+// upper bound on the polls of the preparation waves' arrival counter: the
+// wait always ends (the four waves arrive within one chunk's work); the bound
+// only guarantees that the kernel terminates whatever happens
+constexpr int kSpinMax = 1 << 16;
+
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     using Ly = FwdLds<D>;
     constexpr int PK = Ly::PK, PT = Ly::PT, PP = Ly::PP, PAT = Ly::PAT, PDI = Ly::PDI;
-    constexpr int DW = D / 4;      // state columns per chain wave (and W columns per prep wave)
+    constexpr int DW = D / 4;      // state columns per chain wave
     constexpr int NTW = DW / 16;   // 16-wide tiles of those
     constexpr int KB = D / 16;     // K16 blocks over the head dim
     constexpr int FG = D / 8;      // staging: 8-element feature groups per row
     constexpr int TG = 256 / FG;   // staging: token groups over the 4 prep waves
     constexpr int TPT = C / TG;    // staging: tokens per prep thread
     static_assert(KB % 2 == 0 && NTW >= 1 && (TPT == 2 || TPT == 4), "unsupported head dim");
+    static_assert(Ly::bytes <= 160 * 1024, "LDS budget");
     constexpr uint32_t ES = IN_BF16 ? 2 : 4;      // bytes per q/k/v/o element
     constexpr uint32_t GES = GATE_BF16 ? 2 : 4;   // bytes per g/beta element
 
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t *const sQ0 = reinterpret_cast<uint16_t *>(smem + Ly::oQ);
-    uint16_t *const sK = reinterpret_cast<uint16_t *>(smem + Ly::oK);
-    uint16_t *const sW = reinterpret_cast<uint16_t *>(smem + Ly::oW);
+    uint16_t *const sK0 = reinterpret_cast<uint16_t *>(smem + Ly::oK);
     uint16_t *const sKT0 = reinterpret_cast<uint16_t *>(smem + Ly::oKT);
     uint16_t *const sP0 = reinterpret_cast<uint16_t *>(smem + Ly::oP);
-    uint16_t *const sAo = reinterpret_cast<uint16_t *>(smem + Ly::oAo);
+    uint16_t *const sAo0 = reinterpret_cast<uint16_t *>(smem + Ly::oAo);
     float *const sAT = reinterpret_cast<float *>(smem + Ly::oAT);
-    uint16_t *const sDi = reinterpret_cast<uint16_t *>(smem + Ly::oDi);
+    uint16_t *const sDi0 = reinterpret_cast<uint16_t *>(smem + Ly::oDi);
     float *const sG2 = reinterpret_cast<float *>(smem + Ly::oS);   // chunk being prepared
-    float *const sBG = sG2 + C;
-    float *const sB0 = sG2 + 2 * C;                                 // [2][64]
-    float *const sGam0 = sG2 + 4 * C;                               // [2][64], scale folded in
-    float *const sDec0 = sG2 + 6 * C;                               // [2][64]
-    float *const sGL = sG2 + 8 * C;                                 // [2]
+    float *const sVec0 = sG2 + C;                                   // [2][4][64]
+    float *const sGL = sG2 + 9 * C;                                 // [2]
+    uint32_t *const sArrive = reinterpret_cast<uint32_t *>(sGL + 2);
+
+    // per-buffer views
+    auto Qb = [&](int par) { return sQ0 + par * C * PK; };
+    auto Kb = [&](int par) { return sK0 + par * C * PK; };
+    auto KTb = [&](int par) { return sKT0 + par * D * PT; };
+    auto Pb = [&](int par) { return sP0 + par * C * PP; };
+    auto Aob = [&](int par) { return sAo0 + par * C * PP; };
+    auto Dib = [&](int par) { return sDi0 + par * 4 * 16 * PDI; };
+    auto vB = [&](int par) { return sVec0 + par * 4 * C; };            // beta
+    auto vBG = [&](int par) { return sVec0 + par * 4 * C + C; };       // beta e^G
+    auto vGam = [&](int par) { return sVec0 + par * 4 * C + 2 * C; };  // scale e^G
+    auto vDec = [&](int par) { return sVec0 + par * 4 * C + 3 * C; };  // e^{G_L - G}
 
     // ---- work item: (sequence n, v-head h), longest sequences first
     const int64_t item = blockIdx.x;
@@ -294,7 +319,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     const int role = wave & 3;          // chain wave c / prep wave p
     const int l16 = lane & 15;
     const int lq = lane >> 4;
-    const int colw = role * DW;         // this wave's 16*NTW columns (dv for chain, dk for the W solve)
+    const int colw = role * DW;         // the chain wave's 16*NTW state columns
     const int64_t nch = (eos - bos + C - 1) / C;
 
     auto chunk_len = [&](int64_t c) -> int {
@@ -309,8 +334,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 
     // ---- chain registers
     f32x4 hs[KB][NTW];        // state tile (kb, nt): rows dk 16kb+4lq+r, column dv colw+16nt+l16
-    f32x4 Vn[4][NTW];         // Vnew of the chunk the chain works on (rows tokens)
-    bf16x4 vp[4][NTW];        // v of the chunk the chain solves next: token 16blk+l16, dv colw+16nt+4lq..+3
+    bf16x4 vp[4][NTW];        // v of the chunk the chain works on next: token 16blk+l16, dv colw+16nt+4lq..+3
     // ---- preparation registers
     uint4 pq[TPT], pk[TPT];   // q, k rows of the next chunk to stage
     float pg = 0.f, pb = 0.f; // its gate and beta (prep wave 0, lane = token)
@@ -361,7 +385,8 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     // prep: registers -> LDS (permuted rows of q and k) and the gate vectors
     auto stage = [&](int par) {
         const int pt = tid - 256, fg = pt % FG, tg = pt / FG;
-        uint16_t *sQ = sQ0 + par * C * PK;
+        uint16_t *sQ = Qb(par);
+        uint16_t *sK = Kb(par);
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
             const int t = tg * TPT + j;
@@ -373,12 +398,26 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             const float GL2 = __shfl(G2, 63, 64);   // padding has g = 0: equals G at the last token
             const float gam = fast_exp2(G2);
             sG2[lane] = G2;
-            sB0[par * C + lane] = pb;
-            sBG[lane] = pb * gam;
-            sGam0[par * C + lane] = gam * a.scale;
-            sDec0[par * C + lane] = fast_exp2(GL2 - G2);
+            vB(par)[lane] = pb;
+            vBG(par)[lane] = pb * gam;
+            vGam(par)[lane] = gam * a.scale;
+            vDec(par)[lane] = fast_exp2(GL2 - G2);
             if (lane == 0) sGL[par] = fast_exp2(GL2);
         }
+    };
+
+    // prep: the four preparation waves wait for each other (after staging).
+    // `target` = 4 x the number of waits so far including this one.
+    auto prep_arrive_wait = [&](uint32_t target) {
+        lds_wait();   // this wave's staging writes have landed
+        if (lane == 0) __hip_atomic_fetch_add(sArrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        for (int it = 0; it < kSpinMax; ++it) {
+            const uint32_t seen = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(sArrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+            if (seen >= target) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        lds_wait();
     };
 
     // prep: gated K K^T -> A (diagonal blocks f32 transposed, others -A bf16)
@@ -386,11 +425,13 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     // the tiles (i, j <= i) of both products, which share k_j as the A
     // operand; the B operands (k_i, q_i) stay in registers across the strip.
     auto prep_kq = [&](int par) {
-        uint16_t *sPp = sP0 + par * C * PP;
-        const uint16_t *sQ = sQ0 + par * C * PK;
-        const float *sB = sB0 + par * C;
+        uint16_t *sPp = Pb(par);
+        uint16_t *sAo = Aob(par);
+        const uint16_t *sQ = Qb(par);
+        const uint16_t *sK = Kb(par);
+        const float *sB = vB(par);
         // strips per prep wave: p0 = K K^T of strip 3, p1 = strip 2, p2 = strip 1,
-        // p3 = Q K^T of strip 3 and strip 0
+        // p3 = Q K^T of strip 3 and strip 0; wave p holds diagonal block 3-p
         auto strip = [&](int i, bool do_kk, bool do_qk) {
             bf16x8 bk[KB / 2], bq[KB / 2];
             const uint16_t *pki = sK + (16 * i + l16) * PK + 8 * lq;
@@ -454,25 +495,28 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 
     // prep: K^T tiles (token block blk, dk block kb) through identity products
     auto prep_kt = [&](int par) {
-        uint16_t *kt = sKT0 + par * D * PT;
+        uint16_t *kt = KTb(par);
+        const uint16_t *sK = Kb(par);
 #pragma unroll
         for (int s = 0; s < KB; ++s) {
             const int tt = role + 4 * s;            // 4*KB tiles, KB per prep wave
             const int blk = tt & 3, kb = tt >> 2;
             const bf16x4 af = ld4(sK + (16 * blk + l16) * PK + pc(16 * kb + 4 * lq));
-            const bf16x8 a8 = __builtin_shufflevector(af, bf16x4{}, 0, 1, 2, 3, 4, 5, 6, 7);
-            const f32x4 x = mfma32(a8, ident, zero4());   // (row token 16blk+4lq+r, column dk 16kb+l16)
+            const f32x4 x = mfma32(ext8(af), ident, zero4());   // (row token 16blk+4lq+r, column dk 16kb+l16)
             st4(kt + (16 * kb + l16) * PT + pc(16 * blk + 4 * lq), cvt4(x));
         }
     };
 
-    // inverse of diagonal block `role` of I + A.  With L the strictly lower
-    // block, L^16 = 0 and (I + L)^-1 = sum_{k<16} (-L)^k: 14 chained one-block
-    // MFMAs L^k = L L^(k-1) (each power's C layout is the next B operand),
+    // prep: inverse of diagonal block b = 3 - role of I + A (the block this
+    // wave's strip wrote).  With L the strictly lower block, L^16 = 0 and
+    // (I + L)^-1 = sum_{k<16} (-L)^k: 14 chained one-block MFMAs
+    // L^k = L L^(k-1) (each power's C layout is the next B operand),
     // accumulated in f32; an identity product then transposes the C layout of
     // D into rows so it is stored row-major.
-    auto block_inv = [&]() {
-        const float *at = sAT + role * 16 * PAT;
+    auto block_inv = [&](int par) {
+        const int b = 3 - role;
+        const float *at = sAT + b * 16 * PAT;
+        lds_wait();   // this wave's own writes of the block
         const f32x4 cl = *reinterpret_cast<const f32x4 *>(at + l16 * PAT + 4 * lq);   // L[4lq+r][l16]
         f32x4 al;                                                                      // L[l16][4lq+r]
 #pragma unroll
@@ -487,85 +531,8 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             if (4 * lq + r == l16) sum[r] += 1.f;
-        const bf16x4 db = cvt4(sum);
-        const f32x4 dt = mfma32(__builtin_shufflevector(db, bf16x4{}, 0, 1, 2, 3, 4, 5, 6, 7), ident, zero4());
-        st4(sDi + (16 * role + l16) * PDI + 4 * lq, cvt4(dt));   // D[l16][4lq..4lq+3]
-    };
-
-    // block forward substitution X_a = D_a (R_a - sum_{c<a} A_ac X_c) on NTW tiles;
-    // rhs(blk, nt) gives R_a in C layout; out(blk, nt, X) consumes X_a
-    auto solve = [&](auto rhs, auto out) {
-        bf16x4 Xb[4][NTW];
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            f32x4 R[NTW];
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) R[nt] = rhs(blk, nt);
-            const uint16_t *ar = sAo + (16 * blk + l16) * PP;
-            if (blk >= 2) {
-                const bf16x8 af = ld8(ar + 8 * lq);   // blocks 0 and 1
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) R[nt] = mfma32(af, cat(Xb[0][nt], Xb[1][nt]), R[nt]);
-            }
-            if (blk & 1) {
-                const bf16x4 af = ld4(ar + pc(16 * (blk - 1) + 4 * lq));
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) R[nt] = mfma16z(af, Xb[blk - 1][nt], R[nt]);
-            }
-            const bf16x4 df = ld4(sDi + (16 * blk + l16) * PDI + 4 * lq);
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const f32x4 X = mfma16z(df, cvt4(R[nt]), zero4());
-                Xb[blk][nt] = cvt4(X);
-                out(blk, nt, X, Xb[blk][nt]);
-            }
-        }
-    };
-
-    // the same substitution for a single 16-column tile
-    auto solve1 = [&](auto rhs, auto out) {
-        bf16x4 Xb[4];
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            f32x4 R = rhs(blk);
-            const uint16_t *ar = sAo + (16 * blk + l16) * PP;
-            if (blk >= 2) R = mfma32(ld8(ar + 8 * lq), cat(Xb[0], Xb[1]), R);
-            if (blk & 1) R = mfma16z(ld4(ar + pc(16 * (blk - 1) + 4 * lq)), Xb[blk - 1], R);
-            const f32x4 X = mfma16z(ld4(sDi + (16 * blk + l16) * PDI + 4 * lq), cvt4(R), zero4());
-            Xb[blk] = cvt4(X);
-            out(blk, X);
-        }
-    };
-
-    // W columns 16*wt..16*wt+15 of the chunk -> sW as -W (row token, k = dk permuted)
-    auto wsolve_tile = [&](int par, int wt) {
-        const uint16_t *kt = sKT0 + par * D * PT;
-        solve1([&](int blk) {
-                   const f32x4 bg = *reinterpret_cast<const f32x4 *>(sBG + 16 * blk + 4 * lq);
-                   return up4(ld4(kt + (16 * wt + l16) * PT + pc(16 * blk + 4 * lq))) * bg;
-               },
-               [&](int blk, f32x4 X) {
-                   // transpose -W through an identity product: (row dk, column token)
-                   const bf16x4 nx = cvt4(-X);
-                   const f32x4 y = mfma32(__builtin_shufflevector(nx, bf16x4{}, 0, 1, 2, 3, 4, 5, 6, 7), ident, zero4());
-                   st4(sW + (16 * blk + l16) * PK + pc(16 * wt + 4 * lq), cvt4(y));
-               });
-    };
-
-    // chain: U columns colw.. of the chunk in vp (solved with that chunk's A, D and beta)
-    auto chain_usolve = [&](int par, f32x4 (&U)[4][NTW]) {
-        const float *sB = sB0 + par * C;
-        solve([&](int blk, int nt) {
-                  const f32x4 bb = *reinterpret_cast<const f32x4 *>(sB + 16 * blk + 4 * lq);
-                  // v (row token, k dv) times identity: (row token 16blk+4lq+r, column dv)
-                  const f32x4 x = mfma32(__builtin_shufflevector(vp[blk][nt], bf16x4{}, 0, 1, 2, 3, 4, 5, 6, 7),
-                                         ident, zero4());
-                  return x * bb;
-              },
-              [&](int blk, int nt, f32x4 X, bf16x4 Xb) {
-                  U[blk][nt] = X;
-                  (void)Xb;
-              });
+        const f32x4 dt = mfma32(ext8(cvt4(sum)), ident, zero4());
+        st4(Dib(par) + (16 * b + l16) * PDI + 4 * lq, cvt4(dt));   // D[l16][4lq..4lq+3]
     };
 
     auto to_bf16_state = [&](bf16x4 (&hb)[KB][NTW]) {
@@ -575,30 +542,48 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             for (int nt = 0; nt < NTW; ++nt) hb[kb][nt] = cvt4(hs[kb][nt]);
     };
 
-    // chain: Vnew = U - W H   (sW holds -W)
-    auto chain_vnew = [&](const f32x4 (&U)[4][NTW]) {
+    // chain: one chunk.  t0, L: its first token and length.
+    auto chain_chunk = [&](int par, int64_t c) {
+        const uint16_t *sK = Kb(par);
+        const uint16_t *sQ = Qb(par);
+        const uint16_t *sAo = Aob(par);
+        const uint16_t *sDi = Dib(par);
+        const uint16_t *sPp = Pb(par);
+        const uint16_t *kt = KTb(par);
+        const float *vb = vB(par), *vbg = vBG(par), *vgam = vGam(par), *vdec = vDec(par);
+
         bf16x4 hb[KB][NTW];
         to_bf16_state(hb);
+
+        // R = diag(b) V - diag(b e^G) (K H): rows token 16blk+4lq+r, column dv
+        f32x4 R[4][NTW];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) Vn[blk][nt] = U[blk][nt];
-            const uint16_t *pw = sW + (16 * blk + l16) * PK + 8 * lq;
+            for (int nt = 0; nt < NTW; ++nt) R[blk][nt] = zero4();
+            const uint16_t *pk = sK + (16 * blk + l16) * PK + 8 * lq;
 #pragma unroll
             for (int p = 0; p < KB / 2; ++p) {
-                const bf16x8 af = ld8(pw + 32 * p);
+                const bf16x8 af = ld8(pk + 32 * p);
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt)
-                    Vn[blk][nt] = mfma32(af, cat(hb[2 * p][nt], hb[2 * p + 1][nt]), Vn[blk][nt]);
+                for (int nt = 0; nt < NTW; ++nt) R[blk][nt] = mfma32(af, cat(hb[2 * p][nt], hb[2 * p + 1][nt]), R[blk][nt]);
             }
         }
-    };
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const f32x4 bb = *reinterpret_cast<const f32x4 *>(vb + 16 * blk + 4 * lq);
+            const f32x4 bg = *reinterpret_cast<const f32x4 *>(vbg + 16 * blk + 4 * lq);
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                // v (row token, k dv) times identity: (row token 16blk+4lq+r, column dv)
+                const f32x4 x = mfma32(ext8(vp[blk][nt]), ident, zero4());
+                R[blk][nt] = x * bb - bg * R[blk][nt];
+            }
+        }
+        load_v(c + 1);   // zero past the end
 
-    // chain: H^T Q^T for the chunk staged in sQ[par] (before the scale e^G row scaling)
-    auto chain_qh = [&](int par, f32x4 (&Ot)[4][NTW]) {
-        bf16x4 hb[KB][NTW];
-        to_bf16_state(hb);
-        const uint16_t *sQ = sQ0 + par * C * PK;
+        // H^T Q^T (row dv, column token), before the scale e^G column scaling
+        f32x4 Ot[4][NTW];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
 #pragma unroll
@@ -612,88 +597,102 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                     Ot[blk][nt] = mfma32(cat(hb[2 * p][nt], hb[2 * p + 1][nt]), bq, Ot[blk][nt]);
             }
         }
-    };
 
-    // chain: O^T = diag(scale e^G) (H^T Q^T) + Vnew^T P^T (P carries the scale), stored 4 dv per lane
-    auto chain_out = [&](int par, int64_t t0, int L) {
-        const uint32_t rowb = static_cast<uint32_t>(a.hv) * D * ES;
-        const __amdgpu_buffer_rsrc_t ro = chunk_rsrc(reinterpret_cast<unsigned char *>(a.o) + ((t0 * a.hv + h) * D) * ES, L * rowb);
-        const uint16_t *sPp = sP0 + par * C * PP;
-        const float *gam = sGam0 + par * C;
-        f32x4 Ot[4][NTW];
-        chain_qh(par, Ot);
-        bf16x4 Vb[4][NTW];
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) Vb[blk][nt] = cvt4(Vn[blk][nt]);
+        // Vnew: block forward substitution X_a = D_a (R_a - sum_{c<a} A_ac X_c)
+        // (sAo holds -A); R becomes Vnew in f32, Xb its bf16 copy
+        bf16x4 Xb[4][NTW];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
-            const float gt = gam[16 * blk + l16];
+            const uint16_t *ar = sAo + (16 * blk + l16) * PP;
+            if (blk >= 2) {
+                const bf16x8 af = ld8(ar + 8 * lq);   // blocks 0 and 1
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = Ot[blk][nt] * gt;
-            const uint16_t *pp = sPp + (16 * blk + l16) * PP;
-            if (blk >= 1) {
-                const bf16x8 bf = ld8(pp + 8 * lq);   // keys of blocks 0, 1
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = mfma32(cat(Vb[0][nt], Vb[1][nt]), bf, Ot[blk][nt]);
+                for (int nt = 0; nt < NTW; ++nt) R[blk][nt] = mfma32(af, cat(Xb[0][nt], Xb[1][nt]), R[blk][nt]);
             }
-            if (blk == 3) {
-                const bf16x8 bf = ld8(pp + 32 + 8 * lq);   // keys of blocks 2, 3
+            if (blk & 1) {
+                const bf16x4 af = ld4(ar + pc(16 * (blk - 1) + 4 * lq));
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = mfma32(cat(Vb[2][nt], Vb[3][nt]), bf, Ot[blk][nt]);
+                for (int nt = 0; nt < NTW; ++nt) R[blk][nt] = mfma16z(af, Xb[blk - 1][nt], R[blk][nt]);
             }
-            if ((blk & 1) == 0) {
-                const bf16x4 bf = ld4(pp + pc(16 * blk + 4 * lq));
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = mfma16z(Vb[blk][nt], bf, Ot[blk][nt]);
-            }
-            const uint32_t orow = (16 * blk + l16) * rowb;
+            const bf16x4 df = ld4(sDi + (16 * blk + l16) * PDI + 4 * lq);
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
-                const uint32_t off = orow + (colw + 16 * nt + 4 * lq) * ES;
-                if constexpr (IN_BF16)
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, cvt4(Ot[blk][nt])), ro, off, 0, 0);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, Ot[blk][nt]), ro, off, 0, 0);
+                R[blk][nt] = mfma16z(df, cvt4(R[blk][nt]), zero4());
+                Xb[blk][nt] = cvt4(R[blk][nt]);
+            }
+        }
+
+        // O^T = diag(scale e^G) (H^T Q^T) + Vnew^T P^T (P carries the scale), stored 4 dv per lane
+        {
+            const int L = chunk_len(c);
+            const uint32_t rowb = static_cast<uint32_t>(a.hv) * D * ES;
+            const __amdgpu_buffer_rsrc_t ro = chunk_rsrc(
+                reinterpret_cast<unsigned char *>(a.o) + (((bos + c * C) * a.hv + h) * D) * ES, L * rowb);
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                const float gt = vgam[16 * blk + l16];
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = Ot[blk][nt] * gt;
+                const uint16_t *pp = sPp + (16 * blk + l16) * PP;
+                if (blk >= 1) {
+                    const bf16x8 bf = ld8(pp + 8 * lq);   // keys of blocks 0, 1
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = mfma32(cat(Xb[0][nt], Xb[1][nt]), bf, Ot[blk][nt]);
+                }
+                if (blk == 3) {
+                    const bf16x8 bf = ld8(pp + 32 + 8 * lq);   // keys of blocks 2, 3
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = mfma32(cat(Xb[2][nt], Xb[3][nt]), bf, Ot[blk][nt]);
+                }
+                if ((blk & 1) == 0) {
+                    const bf16x4 bf = ld4(pp + pc(16 * blk + 4 * lq));
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = mfma16z(Xb[blk][nt], bf, Ot[blk][nt]);
+                }
+                const uint32_t orow = (16 * blk + l16) * rowb;
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    const uint32_t off = orow + (colw + 16 * nt + 4 * lq) * ES;
+                    if constexpr (IN_BF16)
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, cvt4(Ot[blk][nt])), ro, off, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, Ot[blk][nt]), ro, off, 0, 0);
+                }
+            }
+        }
+
+        // H <- e^{G_L} H + K^T diag(e^{G_L - G}) Vnew
+        {
+            const float gl = sGL[par];
+            bf16x4 Vt[4][NTW];
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(vdec + 16 * blk + 4 * lq);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) Vt[blk][nt] = cvt4(R[blk][nt] * d4);
+            }
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const uint16_t *pkt = kt + (16 * kb + l16) * PT + 8 * lq;
+                const bf16x8 a01 = ld8(pkt);
+                const bf16x8 a23 = ld8(pkt + 32);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    f32x4 s = hs[kb][nt] * gl;
+                    s = mfma32(a01, cat(Vt[0][nt], Vt[1][nt]), s);
+                    s = mfma32(a23, cat(Vt[2][nt], Vt[3][nt]), s);
+                    hs[kb][nt] = s;
+                }
             }
         }
     };
 
-    // chain: H <- e^{G_L} H + K^T diag(e^{G_L - G}) Vnew
-    auto chain_h = [&](int par) {
-        const uint16_t *kt = sKT0 + par * D * PT;
-        const float gl = sGL[par];
-        const float *dec = sDec0 + par * C;
-        bf16x4 Vt[4][NTW];
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const f32x4 d4 = *reinterpret_cast<const f32x4 *>(dec + 16 * blk + 4 * lq);
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) Vt[blk][nt] = cvt4(Vn[blk][nt] * d4);
-        }
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const uint16_t *pkt = kt + (16 * kb + l16) * PT + 8 * lq;
-            const bf16x8 a01 = ld8(pkt);
-            const bf16x8 a23 = ld8(pkt + 32);
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                f32x4 s = hs[kb][nt] * gl;
-                s = mfma32(a01, cat(Vt[0][nt], Vt[1][nt]), s);
-                s = mfma32(a23, cat(Vt[2][nt], Vt[3][nt]), s);
-                hs[kb][nt] = s;
-            }
-        }
-    };
+    // The arrival counter starts at zero before any preparation wave uses it.
+    if (tid == 0) *sArrive = 0u;
+    __syncthreads();
 
-    // W tiles of the solve: D/16 of them, wave w takes tile w (at D = 64 only
-    // the preparation waves have one)
-    constexpr int WT = KB;
-    const int my_wt = WT == 8 ? wave : (chain ? -1 : role);
-
-    // The two roles run separate loops with the same barrier sequence: 4
-    // barriers for the prologue (preparation of chunk 0), then 4 per chunk.
+    // The two roles run separate loops with the same barrier sequence: one
+    // barrier after the preparation of chunk 0, then one per chunk.
     // (s_barrier counts arriving waves; the roles are uniform per wave.)
     if (chain) {
 #pragma unroll
@@ -705,24 +704,8 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                     hs[kb][nt][r] = a.h0 ? a.h0[sbase + (16 * kb + 4 * lq + r) * D + colw + 16 * nt + l16] : 0.f;
         load_v(0);
         __syncthreads();
-        __syncthreads();
-        __syncthreads();
-        if (my_wt >= 0) wsolve_tile(0, my_wt);
-        __syncthreads();
         for (int64_t c = 0; c < nch; ++c) {
-            const int par = static_cast<int>(c & 1), npar = par ^ 1;
-            {   // P1: U solve and Vnew of chunk c
-                f32x4 U[4][NTW];
-                chain_usolve(par, U);
-                chain_vnew(U);
-            }
-            __syncthreads();
-            load_v(c + 1);                                // P2 (zero past the end)
-            chain_out(par, bos + c * C, chunk_len(c));
-            __syncthreads();
-            chain_h(par);                                 // P3
-            __syncthreads();
-            if (my_wt >= 0) wsolve_tile(npar, my_wt);     // P4 (chunk c+1)
+            chain_chunk(static_cast<int>(c & 1), c);
             __syncthreads();
         }
         if (a.ht) {
@@ -738,28 +721,22 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         // prologue: chunk 0
         load_qk(0);
         stage(0);
+        prep_arrive_wait(4u);
         load_qk(1);   // zero when there is no chunk 1
-        __syncthreads();
         prep_kq(0);
         prep_kt(0);
-        __syncthreads();
-        block_inv();
-        __syncthreads();
-        if (my_wt >= 0) wsolve_tile(0, my_wt);
+        block_inv(0);
         __syncthreads();
         // chunk c+1 while the chain works on chunk c; past the last chunk the
         // preparation runs on zero rows and its results are never read
         for (int64_t c = 0; c < nch; ++c) {
             const int npar = static_cast<int>((c + 1) & 1);
-            stage(npar);          // P1
+            stage(npar);
+            prep_arrive_wait(static_cast<uint32_t>(4 * (c + 2)));
             load_qk(c + 2);
-            __syncthreads();
-            prep_kq(npar);        // P2
+            prep_kq(npar);
             prep_kt(npar);
-            __syncthreads();
-            block_inv();          // P3
-            __syncthreads();
-            if (my_wt >= 0) wsolve_tile(npar, my_wt);   // P4
+            block_inv(npar);
             __syncthreads();
         }
     }
