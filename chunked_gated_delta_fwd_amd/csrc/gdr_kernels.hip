@@ -182,9 +182,17 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 // wave of each kind, so the hardware interleaves the chain's dependent MFMAs
 // with the preparation's loads, LDS traffic and VALU.
 //
-// Shared matrices keep each 32-wide k range with its 4-element groups in the
-// order 0,4,1,5,2,6,3,7 (pc below), so the 8 k values a lane feeds to one
-// 16x16x32 MFMA (groups lq and lq+4) are 16 contiguous bytes.
+// Register layout of the state.  Tile pair (2p, 2p+1) of a chain wave holds
+// dk rows 32p + 8lq + r (tile 2p) and 32p + 8lq + 4 + r (tile 2p+1) in its
+// C-layout row 4lq + r, so the 8 k values a lane feeds to one 16x16x32 MFMA
+// from that pair are dk 32p + 8lq .. +7: the matching operand from q or k is
+// 16 contiguous bytes of a plain row-major row.  Likewise tile nt column c
+// holds dv colw + 4*NTW*(c/4) + 4nt + c%4, so the NTW tiles' values of one
+// output row in a lane are 4*NTW contiguous dv (one 8- or 16-byte store).
+// Shared matrices indexed by token on the k side (K^T, P, A) keep each 32-wide
+// token range with its 4-element groups in the order 0,4,1,5,2,6,3,7 (pc
+// below), because their other operand comes from a C layout (token rows
+// 4lq + r of two 16-token blocks).
 // --------------------------------------------------------------------------
 __device__ __forceinline__ int pc(int x) { return (x & ~31) | ((x & 12) << 1) | ((x >> 2) & 4) | (x & 3); }
 
@@ -199,7 +207,7 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 
 template <int D>
 struct FwdLds {
-    static constexpr int PK = D + 8;    // [64][D] bf16 rows, k permuted: q and k, two buffers each
+    static constexpr int PK = D + 8;    // [64][D] bf16 rows: q and k, two buffers each
     static constexpr int PT = C + 8;    // [D][64] bf16, tokens permuted: k^T, two buffers
     static constexpr int PP = C + 8;    // [64][64] bf16, keys permuted: P and -A off the diagonal, two buffers each
     static constexpr int PAT = 20;      // [4][16][16] f32: diagonal blocks of A, transposed (preparation only)
@@ -241,6 +249,12 @@ template <bool BF16>
 __device__ __forceinline__ bf16x4 buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     if constexpr (BF16) return __builtin_bit_cast(bf16x4, buf_load<8>(r, off));
     else return cvt4(__builtin_bit_cast(f32x4, buf_load<16>(r, off)));
+}
+// 8 consecutive elements at byte offset off as bf16 (16 or 32 bytes)
+template <bool BF16>
+__device__ __forceinline__ bf16x8 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (BF16) return __builtin_bit_cast(bf16x8, buf_load<16>(r, off));
+    else return cat(buf_load4<false>(r, off), buf_load4<false>(r, off + 16));
 }
 template <bool BF16>
 __device__ __forceinline__ float buf_load_scalar(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -326,15 +340,28 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         const int64_t r = eos - (bos + c * C);
         return r < C ? (r < 0 ? 0 : static_cast<int>(r)) : C;
     };
+    // dk row of state tile kb at C-layout row i; dv column of tile nt at column c
+    auto dk_of = [&](int kb, int i) { return 32 * (kb >> 1) + 8 * (i >> 2) + 4 * (kb & 1) + (i & 3); };
+    auto dv_of = [&](int nt, int c) { return colw + 4 * NTW * (c >> 2) + 4 * nt + (c & 3); };
 
     // 16x16 identity as a zero-padded B fragment: slot r of lane l is I[4lq+r][l16]
     bf16x8 ident;
 #pragma unroll
     for (int r = 0; r < 8; ++r) ident[r] = (__bf16)((r < 4 && 4 * lq + r == l16) ? 1.f : 0.f);
 
+    // selection of tile nt's columns out of the 16*NTW dv a lane-row of v
+    // holds (lane lq: dv colw + 4*NTW*lq ..): slot s of lane (l16, lq) picks
+    // k = 4*NTW*lq + s for column l16 when that is dv_of(nt, l16)
+    bf16x8 sel[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            sel[nt][s] = (__bf16)((s < 4 * NTW && 4 * NTW * lq + s == dv_of(nt, l16) - colw) ? 1.f : 0.f);
+
     // ---- chain registers
-    f32x4 hs[KB][NTW];        // state tile (kb, nt): rows dk 16kb+4lq+r, column dv colw+16nt+l16
-    bf16x4 vp[4][NTW];        // v of the chunk the chain works on next: token 16blk+l16, dv colw+16nt+4lq..+3
+    f32x4 hs[KB][NTW];        // state tile (kb, nt): row dk_of(kb, 4lq+r), column dv_of(nt, l16)
+    bf16x4 vp[4][NTW];        // v of the chunk the chain works on next: token 16blk+l16, dv colw+4*NTW*lq+4nt..+3
     // ---- preparation registers
     uint4 pq[TPT], pk[TPT];   // q, k rows of the next chunk to stage
     float pg = 0.f, pb = 0.f; // its gate and beta (prep wave 0, lane = token)
@@ -348,20 +375,26 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(
             reinterpret_cast<const unsigned char *>(a.v) + ((t0 * a.hv + h) * D) * ES, chunk_len(c) * rowb);
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
-                vp[blk][nt] = buf_load4<IN_BF16>(rv, (16 * blk + l16) * rowb + (colw + 16 * nt + 4 * lq) * ES);
+        for (int blk = 0; blk < 4; ++blk) {
+            const uint32_t off = (16 * blk + l16) * rowb + (colw + 4 * NTW * lq) * ES;
+            if constexpr (NTW == 2) {
+                const bf16x8 x = buf_load8<IN_BF16>(rv, off);
+                vp[blk][0] = __builtin_shufflevector(x, x, 0, 1, 2, 3);
+                vp[blk][1] = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+            } else {
+                vp[blk][0] = buf_load4<IN_BF16>(rv, off);
+            }
+        }
     };
 
     // prep: q, k rows and gates of chunk c into registers (zero past the end).
-    // Thread (tg, fg) holds, for each of its tokens, the 16 bytes that land at
-    // physical columns 8fg..8fg+7: logical groups m and m+4 of 32-range fg/4.
+    // Thread (tg, fg) holds, for each of its tokens, columns 8fg..8fg+7: 16
+    // lanes cover a row, one instruction 4 rows.
     auto load_qk = [&](int64_t c) {
         const int64_t t0 = bos + c * C;
         const int L = chunk_len(c);
         const int pt = tid - 256, fg = pt % FG, tg = pt / FG;
-        const uint32_t e0 = 32 * (fg >> 2) + 4 * (fg & 3);   // logical columns e0.. and e0+16..
+        const uint32_t e0 = 8 * fg;
         const uint32_t rowb = static_cast<uint32_t>(a.hk) * D * ES;
         const int64_t base = (t0 * a.hk + hk) * D * ES;
         const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(reinterpret_cast<const unsigned char *>(a.q) + base, L * rowb);
@@ -369,8 +402,8 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
             const uint32_t off = (tg * TPT + j) * rowb + e0 * ES;
-            pq[j] = __builtin_bit_cast(uint4, cat(buf_load4<IN_BF16>(rq, off), buf_load4<IN_BF16>(rq, off + 16 * ES)));
-            pk[j] = __builtin_bit_cast(uint4, cat(buf_load4<IN_BF16>(rk, off), buf_load4<IN_BF16>(rk, off + 16 * ES)));
+            pq[j] = __builtin_bit_cast(uint4, buf_load8<IN_BF16>(rq, off));
+            pk[j] = __builtin_bit_cast(uint4, buf_load8<IN_BF16>(rk, off));
         }
         if (role == 0) {
             const uint32_t growb = static_cast<uint32_t>(a.hv) * GES;
@@ -382,7 +415,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         }
     };
 
-    // prep: registers -> LDS (permuted rows of q and k) and the gate vectors
+    // prep: registers -> LDS (rows of q and k) and the gate vectors
     auto stage = [&](int par) {
         const int pt = tid - 256, fg = pt % FG, tg = pt / FG;
         uint16_t *sQ = Qb(par);
@@ -501,7 +534,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         for (int s = 0; s < KB; ++s) {
             const int tt = role + 4 * s;            // 4*KB tiles, KB per prep wave
             const int blk = tt & 3, kb = tt >> 2;
-            const bf16x4 af = ld4(sK + (16 * blk + l16) * PK + pc(16 * kb + 4 * lq));
+            const bf16x4 af = ld4(sK + (16 * blk + l16) * PK + 16 * kb + 4 * lq);
             const f32x4 x = mfma32(ext8(af), ident, zero4());   // (row token 16blk+4lq+r, column dk 16kb+l16)
             st4(kt + (16 * kb + l16) * PT + pc(16 * blk + 4 * lq), cvt4(x));
         }
@@ -573,10 +606,11 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         for (int blk = 0; blk < 4; ++blk) {
             const f32x4 bb = *reinterpret_cast<const f32x4 *>(vb + 16 * blk + 4 * lq);
             const f32x4 bg = *reinterpret_cast<const f32x4 *>(vbg + 16 * blk + 4 * lq);
+            const bf16x8 va = NTW == 2 ? cat(vp[blk][0], vp[blk][NTW - 1]) : ext8(vp[blk][0]);
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
-                // v (row token, k dv) times identity: (row token 16blk+4lq+r, column dv)
-                const f32x4 x = mfma32(ext8(vp[blk][nt]), ident, zero4());
+                // v (row token, k dv) times a selection: (row token 16blk+4lq+r, column dv_of(nt, l16))
+                const f32x4 x = mfma32(va, sel[nt], zero4());
                 R[blk][nt] = x * bb - bg * R[blk][nt];
             }
         }
@@ -649,14 +683,18 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt) Ot[blk][nt] = mfma16z(Xb[blk][nt], bf, Ot[blk][nt]);
                 }
-                const uint32_t orow = (16 * blk + l16) * rowb;
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) {
-                    const uint32_t off = orow + (colw + 16 * nt + 4 * lq) * ES;
-                    if constexpr (IN_BF16)
-                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, cvt4(Ot[blk][nt])), ro, off, 0, 0);
+                // lane (l16, lq) holds o[token 16blk+l16][dv colw + 4*NTW*lq .. + 4*NTW-1]
+                const uint32_t off = (16 * blk + l16) * rowb + (colw + 4 * NTW * lq) * ES;
+                if constexpr (IN_BF16) {
+                    if constexpr (NTW == 2)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(v4u32, cat(cvt4(Ot[blk][0]), cvt4(Ot[blk][NTW - 1]))), ro, off, 0, 0);
                     else
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, Ot[blk][nt]), ro, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, cvt4(Ot[blk][0])), ro, off, 0, 0);
+                } else {
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt)
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, Ot[blk][nt]), ro, off + 16 * nt, 0, 0);
                 }
             }
         }
@@ -673,7 +711,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             }
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const uint16_t *pkt = kt + (16 * kb + l16) * PT + 8 * lq;
+                const uint16_t *pkt = kt + dk_of(kb, l16) * PT + 8 * lq;
                 const bf16x8 a01 = ld8(pkt);
                 const bf16x8 a23 = ld8(pkt + 32);
 #pragma unroll
@@ -701,7 +739,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    hs[kb][nt][r] = a.h0 ? a.h0[sbase + (16 * kb + 4 * lq + r) * D + colw + 16 * nt + l16] : 0.f;
+                    hs[kb][nt][r] = a.h0 ? a.h0[sbase + dk_of(kb, 4 * lq + r) * D + dv_of(nt, l16)] : 0.f;
         load_v(0);
         __syncthreads();
         for (int64_t c = 0; c < nch; ++c) {
@@ -715,7 +753,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        a.ht[sbase + (16 * kb + 4 * lq + r) * D + colw + 16 * nt + l16] = hs[kb][nt][r];
+                        a.ht[sbase + dk_of(kb, 4 * lq + r) * D + dv_of(nt, l16)] = hs[kb][nt][r];
         }
     } else {
         // prologue: chunk 0
