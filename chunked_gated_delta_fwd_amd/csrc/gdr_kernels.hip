@@ -189,7 +189,7 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 // 16 contiguous bytes of a plain row-major row.  Likewise tile nt column c
 // holds dv colw + 4*NTW*(c/4) + 4nt + c%4, so the NTW tiles' values of one
 // output row in a lane are 4*NTW contiguous dv (one 8- or 16-byte store).
-// Shared matrices indexed by token on the k side (K^T, P, A) keep each 32-wide
+// Shared matrices indexed by token on the k side (P, A) keep each 32-wide
 // token range with its 4-element groups in the order 0,4,1,5,2,6,3,7 (pc
 // below), because their other operand comes from a C layout (token rows
 // 4lq + r of two 16-token blocks).
@@ -200,6 +200,13 @@ __device__ __forceinline__ bf16x8 ld8(const uint16_t *p) {   // 16-byte LDS read
     return *reinterpret_cast<const bf16x8 *>(p);
 }
 __device__ __forceinline__ void st4(uint16_t *p, bf16x4 v) { *reinterpret_cast<bf16x4 *>(p) = v; }
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16): each lane names 8 bytes
+// (4 elements); within every group of 16 lanes, slot r of lane i receives
+// element i%4 of the piece named by lane 4r + i/4.
+__device__ __forceinline__ bf16x4 ld4_tr(const uint16_t *p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p)));
+}
 __device__ __forceinline__ bf16x8 ext8(bf16x4 a) { return __builtin_shufflevector(a, bf16x4{}, 0, 1, 2, 3, 4, 5, 6, 7); }
 
 // wait until this wave's LDS accesses are complete (also a compiler barrier)
@@ -207,15 +214,16 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 
 template <int D>
 struct FwdLds {
-    static constexpr int PK = D + 8;    // [64][D] bf16 rows: q and k, two buffers each
-    static constexpr int PT = C + 8;    // [D][64] bf16, tokens permuted: k^T, two buffers
+    // [64][D] bf16 rows: q and k, two buffers each.  The pitch (D + 16
+    // elements) keeps both the 16-byte row-fragment reads and the transposing
+    // reads of k (4 rows x 32 bytes per 16 lanes) free of bank conflicts.
+    static constexpr int PK = D + 16;
     static constexpr int PP = C + 8;    // [64][64] bf16, keys permuted: P and -A off the diagonal, two buffers each
     static constexpr int PAT = 20;      // [4][16][16] f32: diagonal blocks of A, transposed (preparation only)
     static constexpr int PDI = 24;      // [4][16][16] bf16: inverses of the diagonal blocks, two buffers
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + 2 * C * PK * 2;
-    static constexpr int oKT = oK + 2 * C * PK * 2;
-    static constexpr int oP = oKT + 2 * D * PT * 2;
+    static constexpr int oP = oK + 2 * C * PK * 2;
     static constexpr int oAo = oP + 2 * C * PP * 2;
     static constexpr int oAT = oAo + 2 * C * PP * 2;
     static constexpr int oDi = oAT + 4 * 16 * PAT * 4;
@@ -270,7 +278,7 @@ constexpr int kSpinMax = 1 << 16;
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     using Ly = FwdLds<D>;
-    constexpr int PK = Ly::PK, PT = Ly::PT, PP = Ly::PP, PAT = Ly::PAT, PDI = Ly::PDI;
+    constexpr int PK = Ly::PK, PP = Ly::PP, PAT = Ly::PAT, PDI = Ly::PDI;
     constexpr int DW = D / 4;      // state columns per chain wave
     constexpr int NTW = DW / 16;   // 16-wide tiles of those
     constexpr int KB = D / 16;     // K16 blocks over the head dim
@@ -285,7 +293,6 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t *const sQ0 = reinterpret_cast<uint16_t *>(smem + Ly::oQ);
     uint16_t *const sK0 = reinterpret_cast<uint16_t *>(smem + Ly::oK);
-    uint16_t *const sKT0 = reinterpret_cast<uint16_t *>(smem + Ly::oKT);
     uint16_t *const sP0 = reinterpret_cast<uint16_t *>(smem + Ly::oP);
     uint16_t *const sAo0 = reinterpret_cast<uint16_t *>(smem + Ly::oAo);
     float *const sAT = reinterpret_cast<float *>(smem + Ly::oAT);
@@ -298,7 +305,6 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     // per-buffer views
     auto Qb = [&](int par) { return sQ0 + par * C * PK; };
     auto Kb = [&](int par) { return sK0 + par * C * PK; };
-    auto KTb = [&](int par) { return sKT0 + par * D * PT; };
     auto Pb = [&](int par) { return sP0 + par * C * PP; };
     auto Aob = [&](int par) { return sAo0 + par * C * PP; };
     auto Dib = [&](int par) { return sDi0 + par * 4 * 16 * PDI; };
@@ -307,8 +313,21 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     auto vGam = [&](int par) { return sVec0 + par * 4 * C + 2 * C; };  // scale e^G
     auto vDec = [&](int par) { return sVec0 + par * 4 * C + 3 * C; };  // e^{G_L - G}
 
-    // ---- work item: (sequence n, v-head h), longest sequences first
-    const int64_t item = blockIdx.x;
+    // ---- work item: (sequence n, v-head h), longest sequences first.
+    // Work-groups are dispatched round-robin over the 8 XCDs (each with its
+    // own L2), so block b and b+8 start together on one XCD: blocks are
+    // renumbered so those get the r = Hv/Hk v-heads that share a q/k head,
+    // and the second reads q and k from L2.
+    int64_t item = blockIdx.x;
+    {
+        const int64_t r = a.hv / a.hk;
+        const int64_t span = 8 * r;
+        const int64_t full = (static_cast<int64_t>(gridDim.x) / span) * span;
+        if (r > 1 && item < full) {
+            const int64_t w = item % span;
+            item = (item - w) + (w % 8) * r + w / 8;
+        }
+    }
     const int64_t rank = item / a.hv;
     const int h = static_cast<int>(item % a.hv);
     const int64_t n = a.order ? static_cast<int64_t>(a.order[rank]) : rank;
@@ -526,20 +545,6 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         }
     };
 
-    // prep: K^T tiles (token block blk, dk block kb) through identity products
-    auto prep_kt = [&](int par) {
-        uint16_t *kt = KTb(par);
-        const uint16_t *sK = Kb(par);
-#pragma unroll
-        for (int s = 0; s < KB; ++s) {
-            const int tt = role + 4 * s;            // 4*KB tiles, KB per prep wave
-            const int blk = tt & 3, kb = tt >> 2;
-            const bf16x4 af = ld4(sK + (16 * blk + l16) * PK + 16 * kb + 4 * lq);
-            const f32x4 x = mfma32(ext8(af), ident, zero4());   // (row token 16blk+4lq+r, column dk 16kb+l16)
-            st4(kt + (16 * kb + l16) * PT + pc(16 * blk + 4 * lq), cvt4(x));
-        }
-    };
-
     // prep: inverse of diagonal block b = 3 - role of I + A (the block this
     // wave's strip wrote).  With L the strictly lower block, L^16 = 0 and
     // (I + L)^-1 = sum_{k<16} (-L)^k: 14 chained one-block MFMAs
@@ -582,7 +587,6 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         const uint16_t *sAo = Aob(par);
         const uint16_t *sDi = Dib(par);
         const uint16_t *sPp = Pb(par);
-        const uint16_t *kt = KTb(par);
         const float *vb = vB(par), *vbg = vBG(par), *vgam = vGam(par), *vdec = vDec(par);
 
         bf16x4 hb[KB][NTW];
@@ -699,7 +703,9 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             }
         }
 
-        // H <- e^{G_L} H + K^T diag(e^{G_L - G}) Vnew
+        // H <- e^{G_L} H + K^T diag(e^{G_L - G}) Vnew; the K^T fragments are
+        // transposing reads of the k rows: lane (l16, lq) of tile kb gets
+        // k[32p' + 4lq + r][dk_of(kb, l16)] (and tokens +16 for slots 4-7)
         {
             const float gl = sGL[par];
             bf16x4 Vt[4][NTW];
@@ -711,9 +717,9 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             }
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const uint16_t *pkt = kt + dk_of(kb, l16) * PT + 8 * lq;
-                const bf16x8 a01 = ld8(pkt);
-                const bf16x8 a23 = ld8(pkt + 32);
+                const uint16_t *pkt = sK + (4 * lq + (l16 >> 2)) * PK + 32 * (kb >> 1) + 4 * (kb & 1) + 8 * (l16 & 3);
+                const bf16x8 a01 = cat(ld4_tr(pkt), ld4_tr(pkt + 16 * PK));
+                const bf16x8 a23 = cat(ld4_tr(pkt + 32 * PK), ld4_tr(pkt + 48 * PK));
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     f32x4 s = hs[kb][nt] * gl;
@@ -762,7 +768,6 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         prep_arrive_wait(4u);
         load_qk(1);   // zero when there is no chunk 1
         prep_kq(0);
-        prep_kt(0);
         block_inv(0);
         __syncthreads();
         // chunk c+1 while the chain works on chunk c; past the last chunk the
@@ -773,7 +778,6 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             prep_arrive_wait(static_cast<uint32_t>(4 * (c + 2)));
             load_qk(c + 2);
             prep_kq(npar);
-            prep_kt(npar);
             block_inv(npar);
             __syncthreads();
         }
