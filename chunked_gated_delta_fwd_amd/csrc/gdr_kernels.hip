@@ -363,10 +363,6 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     auto dk_of = [&](int kb, int i) { return 32 * (kb >> 1) + 8 * (i >> 2) + 4 * (kb & 1) + (i & 3); };
     auto dv_of = [&](int nt, int c) { return colw + 4 * NTW * (c >> 2) + 4 * nt + (c & 3); };
 
-    // 16x16 identity as a zero-padded B fragment: slot r of lane l is I[4lq+r][l16]
-    bf16x8 ident;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) ident[r] = (__bf16)((r < 4 && 4 * lq + r == l16) ? 1.f : 0.f);
 
     // selection of tile nt's columns out of the 16*NTW dv a lane-row of v
     // holds (lane lq: dv colw + 4*NTW*lq ..): slot s of lane (l16, lq) picks
@@ -546,12 +542,13 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     };
 
     // prep: inverse of diagonal block b = 3 - role of I + A (the block this
-    // wave's strip wrote).  With L the strictly lower block, L^16 = 0 and
-    // (I + L)^-1 = sum_{k<16} (-L)^k: 14 chained one-block MFMAs
-    // L^k = L L^(k-1) (each power's C layout is the next B operand),
-    // accumulated in f32; an identity product then transposes the C layout of
-    // D into rows so it is stored row-major.
-    auto block_inv = [&](int par) {
+    // wave's strip wrote).  With X = -L (L the strictly lower block, so
+    // X^16 = 0), (I + L)^-1 = (I + X)(I + X^2)(I + X^4)(I + X^8).  A C-layout
+    // tile of M is the A fragment of M^T and the B fragment of M, so each
+    // factor is carried with its transpose: 8 one-block MFMAs, 4 dependent
+    // levels, and the last product comes out as D^T in C layout, i.e. the
+    // rows of D, ready to store.
+    auto block_inv = [&](int par) __attribute__((always_inline)) {
         const int b = 3 - role;
         const float *at = sAT + b * 16 * PAT;
         lds_wait();   // this wave's own writes of the block
@@ -559,18 +556,22 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         f32x4 al;                                                                      // L[l16][4lq+r]
 #pragma unroll
         for (int r = 0; r < 4; ++r) al[r] = at[(4 * lq + r) * PAT + l16];
-        const bf16x4 alb = cvt4(al);
-        f32x4 sum = -cl, pw = cl;
+        f32x4 eye;
 #pragma unroll
-        for (int k = 2; k < 16; ++k) {
-            pw = mfma16z(alb, cvt4(pw), zero4());
-            sum = (k & 1) ? sum - pw : sum + pw;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (4 * lq + r == l16) sum[r] += 1.f;
-        const f32x4 dt = mfma32(ext8(cvt4(sum)), ident, zero4());
-        st4(Dib(par) + (16 * b + l16) * PDI + 4 * lq, cvt4(dt));   // D[l16][4lq..4lq+3]
+        for (int r = 0; r < 4; ++r) eye[r] = (4 * lq + r == l16) ? 1.f : 0.f;
+        const bf16x4 x = cvt4(-cl), xt = cvt4(-al);             // C(X), C(X^T)
+        const f32x4 x2 = mfma16z(xt, x, zero4());                // C(X^2)
+        const f32x4 x2t = mfma16z(x, xt, zero4());               // C((X^2)^T)
+        const bf16x4 x2b = cvt4(x2), x2tb = cvt4(x2t);
+        const f32x4 p1t = eye - al;                              // C((I + X)^T)
+        const f32x4 p2t = mfma16z(x2b, cvt4(p1t), p1t);          // C(P2^T), P2 = (I + X)(I + X^2)
+        const f32x4 x4 = mfma16z(x2tb, x2b, zero4());            // C(X^4)
+        const f32x4 x4t = mfma16z(x2b, x2tb, zero4());           // C((X^4)^T)
+        const bf16x4 x4b = cvt4(x4);
+        const f32x4 p3t = mfma16z(x4b, cvt4(p2t), p2t);          // C(P3^T), P3 = P2 (I + X^4)
+        const f32x4 x8 = mfma16z(cvt4(x4t), x4b, zero4());       // C(X^8)
+        const f32x4 dt = mfma16z(cvt4(x8), cvt4(p3t), p3t);      // C(D^T): lane holds D[l16][4lq+r]
+        st4(Dib(par) + (16 * b + l16) * PDI + 4 * lq, cvt4(dt));
     };
 
     auto to_bf16_state = [&](bf16x4 (&hb)[KB][NTW]) {
