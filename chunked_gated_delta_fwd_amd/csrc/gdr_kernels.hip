@@ -214,24 +214,25 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 
 template <int D>
 struct FwdLds {
-    // [64][D] bf16 rows: q and k, two buffers each.  The pitch (D + 16
-    // elements) keeps both the 16-byte row-fragment reads and the transposing
-    // reads of k (4 rows x 32 bytes per 16 lanes) free of bank conflicts.
+    // [64][D] bf16 rows: q and k, three buffers each (chunks c, c+1, c+2).
+    // The pitch (D + 16 elements) keeps both the 16-byte row-fragment reads
+    // and the transposing reads of k (4 rows x 32 bytes per 16 lanes) free of
+    // bank conflicts.
     static constexpr int PK = D + 16;
     static constexpr int PP = C + 8;    // [64][64] bf16, keys permuted: P and -A off the diagonal, two buffers each
     static constexpr int PAT = 20;      // [4][16][16] f32: diagonal blocks of A, transposed (preparation only)
     static constexpr int PDI = 24;      // [4][16][16] bf16: inverses of the diagonal blocks, two buffers
     static constexpr int oQ = 0;
-    static constexpr int oK = oQ + 2 * C * PK * 2;
-    static constexpr int oP = oK + 2 * C * PK * 2;
+    static constexpr int oK = oQ + 3 * C * PK * 2;
+    static constexpr int oP = oK + 3 * C * PK * 2;
     static constexpr int oAo = oP + 2 * C * PP * 2;
     static constexpr int oAT = oAo + 2 * C * PP * 2;
     static constexpr int oDi = oAT + 4 * 16 * PAT * 4;
     static constexpr int oS = oDi + 2 * 4 * 16 * PDI * 2;
-    // f32 vectors of 64: G*log2(e) (preparation only); per buffer beta,
-    // beta*e^G, scale*e^G, e^{G_L-G}; then e^{G_L} per buffer and the
-    // preparation waves' arrival counter
-    static constexpr int bytes = oS + 9 * C * 4 + 16;
+    // f32 vectors of 64: per preparation wave its own G*log2(e) and beta of
+    // the chunk it prepares; per buffer beta, beta*e^G, scale*e^G,
+    // e^{G_L-G}; then e^{G_L} per buffer
+    static constexpr int bytes = oS + 16 * C * 4 + 16;
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -270,11 +271,6 @@ __device__ __forceinline__ float buf_load_scalar(__amdgpu_buffer_rsrc_t r, uint3
     else return __builtin_bit_cast(float, buf_load<4>(r, off));
 }
 
-// upper bound on the polls of the preparation waves' arrival counter: the
-// wait always ends (the four waves arrive within one chunk's work); the bound
-// only guarantees that the kernel terminates whatever happens
-constexpr int kSpinMax = 1 << 16;
-
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     using Ly = FwdLds<D>;
@@ -297,14 +293,13 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     uint16_t *const sAo0 = reinterpret_cast<uint16_t *>(smem + Ly::oAo);
     float *const sAT = reinterpret_cast<float *>(smem + Ly::oAT);
     uint16_t *const sDi0 = reinterpret_cast<uint16_t *>(smem + Ly::oDi);
-    float *const sG2 = reinterpret_cast<float *>(smem + Ly::oS);   // chunk being prepared
-    float *const sVec0 = sG2 + C;                                   // [2][4][64]
-    float *const sGL = sG2 + 9 * C;                                 // [2]
-    uint32_t *const sArrive = reinterpret_cast<uint32_t *>(sGL + 2);
+    float *const sGw0 = reinterpret_cast<float *>(smem + Ly::oS);  // [4 prep waves][G*log2e, beta][64]
+    float *const sVec0 = sGw0 + 8 * C;                              // [2][4][64]
+    float *const sGL = sGw0 + 16 * C;                               // [2]
 
     // per-buffer views
-    auto Qb = [&](int par) { return sQ0 + par * C * PK; };
-    auto Kb = [&](int par) { return sK0 + par * C * PK; };
+    auto Qb = [&](int b3) { return sQ0 + b3 * C * PK; };   // buffer b3 = chunk % 3
+    auto Kb = [&](int b3) { return sK0 + b3 * C * PK; };
     auto Pb = [&](int par) { return sP0 + par * C * PP; };
     auto Aob = [&](int par) { return sAo0 + par * C * PP; };
     auto Dib = [&](int par) { return sDi0 + par * 4 * 16 * PDI; };
@@ -378,8 +373,8 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     f32x4 hs[KB][NTW];        // state tile (kb, nt): row dk_of(kb, 4lq+r), column dv_of(nt, l16)
     bf16x4 vp[4][NTW];        // v of the chunk the chain works on next: token 16blk+l16, dv colw+4*NTW*lq+4nt..+3
     // ---- preparation registers
-    uint4 pq[TPT], pk[TPT];   // q, k rows of the next chunk to stage
-    float pg = 0.f, pb = 0.f; // its gate and beta (prep wave 0, lane = token)
+    uint4 pq[TPT], pk[TPT];   // q, k rows of the chunk to store next
+    float pg = 0.f, pb = 0.f; // gate and beta of the next chunk to prepare (lane = token)
 
     const int64_t sbase = (n * a.hv + h) * static_cast<int64_t>(D) * D;
 
@@ -402,82 +397,80 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         }
     };
 
-    // prep: q, k rows and gates of chunk c into registers (zero past the end).
-    // Thread (tg, fg) holds, for each of its tokens, columns 8fg..8fg+7: 16
-    // lanes cover a row, one instruction 4 rows.
+    // prep: q, k rows of chunk c into registers (zero past the end).  Thread
+    // (tg, fg) holds, for each of its tokens, columns 8fg..8fg+7: 16 lanes
+    // cover a row, one instruction 4 rows.
     auto load_qk = [&](int64_t c) {
         const int64_t t0 = bos + c * C;
         const int L = chunk_len(c);
         const int pt = tid - 256, fg = pt % FG, tg = pt / FG;
-        const uint32_t e0 = 8 * fg;
         const uint32_t rowb = static_cast<uint32_t>(a.hk) * D * ES;
         const int64_t base = (t0 * a.hk + hk) * D * ES;
         const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(reinterpret_cast<const unsigned char *>(a.q) + base, L * rowb);
         const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(reinterpret_cast<const unsigned char *>(a.k) + base, L * rowb);
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
-            const uint32_t off = (tg * TPT + j) * rowb + e0 * ES;
+            const uint32_t off = (tg * TPT + j) * rowb + 8 * fg * ES;
             pq[j] = __builtin_bit_cast(uint4, buf_load8<IN_BF16>(rq, off));
             pk[j] = __builtin_bit_cast(uint4, buf_load8<IN_BF16>(rk, off));
         }
-        if (role == 0) {
-            const uint32_t growb = static_cast<uint32_t>(a.hv) * GES;
-            const int64_t gbase = (t0 * a.hv + h) * GES;
-            const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(reinterpret_cast<const unsigned char *>(a.g) + gbase, L * growb);
-            const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(reinterpret_cast<const unsigned char *>(a.beta) + gbase, L * growb);
-            pg = buf_load_scalar<GATE_BF16>(rg, lane * growb);
-            pb = buf_load_scalar<GATE_BF16>(rb, lane * growb);
-        }
     };
-
-    // prep: registers -> LDS (rows of q and k) and the gate vectors
-    auto stage = [&](int par) {
+    // prep: those registers -> rows of LDS buffer b3
+    auto store_qk = [&](int b3) {
         const int pt = tid - 256, fg = pt % FG, tg = pt / FG;
-        uint16_t *sQ = Qb(par);
-        uint16_t *sK = Kb(par);
+        uint16_t *sQ = Qb(b3);
+        uint16_t *sK = Kb(b3);
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
             const int t = tg * TPT + j;
             *reinterpret_cast<uint4 *>(sQ + t * PK + 8 * fg) = pq[j];
             *reinterpret_cast<uint4 *>(sK + t * PK + 8 * fg) = pk[j];
         }
+    };
+
+    // prep: gate and beta of chunk c into registers (lane = token, zero past the end)
+    auto load_gates = [&](int64_t c) {
+        const int64_t t0 = bos + c * C;
+        const int L = chunk_len(c);
+        const uint32_t growb = static_cast<uint32_t>(a.hv) * GES;
+        const int64_t gbase = (t0 * a.hv + h) * GES;
+        const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(reinterpret_cast<const unsigned char *>(a.g) + gbase, L * growb);
+        const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(reinterpret_cast<const unsigned char *>(a.beta) + gbase, L * growb);
+        pg = buf_load_scalar<GATE_BF16>(rg, lane * growb);
+        pb = buf_load_scalar<GATE_BF16>(rb, lane * growb);
+    };
+
+    // prep: gate prefix sums of the chunk whose gates are in registers.  Every
+    // preparation wave scans them itself into its own copy (no cross-wave
+    // wait); wave 0 also writes the chain's vectors for buffer par.
+    float *const sG2 = sGw0 + (chain ? 0 : role) * 2 * C;   // this wave's G*log2(e)
+    float *const sBw = sG2 + C;                              // and beta
+    auto gates = [&](int par) {
+        const float G2 = wave_inclusive_scan(pg, lane) * kLog2e;
+        const float GL2 = __shfl(G2, 63, 64);   // padding has g = 0: equals G at the last token
+        sG2[lane] = G2;
+        sBw[lane] = pb;
         if (role == 0) {
-            const float G2 = wave_inclusive_scan(pg, lane) * kLog2e;
-            const float GL2 = __shfl(G2, 63, 64);   // padding has g = 0: equals G at the last token
             const float gam = fast_exp2(G2);
-            sG2[lane] = G2;
             vB(par)[lane] = pb;
             vBG(par)[lane] = pb * gam;
             vGam(par)[lane] = gam * a.scale;
             vDec(par)[lane] = fast_exp2(GL2 - G2);
             if (lane == 0) sGL[par] = fast_exp2(GL2);
         }
-    };
-
-    // prep: the four preparation waves wait for each other (after staging).
-    // `target` = 4 x the number of waits so far including this one.
-    auto prep_arrive_wait = [&](uint32_t target) {
-        lds_wait();   // this wave's staging writes have landed
-        if (lane == 0) __hip_atomic_fetch_add(sArrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        for (int it = 0; it < kSpinMax; ++it) {
-            const uint32_t seen = __builtin_amdgcn_readfirstlane(
-                __hip_atomic_load(sArrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-            if (seen >= target) break;
-            __builtin_amdgcn_s_sleep(1);
-        }
-        lds_wait();
+        lds_wait();   // this wave's copies are written before its strips read them
     };
 
     // prep: gated K K^T -> A (diagonal blocks f32 transposed, others -A bf16)
     // and gated Q K^T -> P (scale folded in), by row strips: strip i holds
     // the tiles (i, j <= i) of both products, which share k_j as the A
     // operand; the B operands (k_i, q_i) stay in registers across the strip.
-    auto prep_kq = [&](int par) {
+    auto prep_kq = [&](int par, int b3) {
         uint16_t *sPp = Pb(par);
         uint16_t *sAo = Aob(par);
-        const uint16_t *sQ = Qb(par);
-        const uint16_t *sK = Kb(par);
-        const float *sB = vB(par);
+        const uint16_t *sQ = Qb(b3);
+        const uint16_t *sK = Kb(b3);
+        const float *sB = sBw;
         // strips per prep wave: p0 = K K^T of strip 3, p1 = strip 2, p2 = strip 1,
         // p3 = Q K^T of strip 3 and strip 0; wave p holds diagonal block 3-p
         auto strip = [&](int i, bool do_kk, bool do_qk) {
@@ -582,9 +575,9 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     };
 
     // chain: one chunk.  t0, L: its first token and length.
-    auto chain_chunk = [&](int par, int64_t c) {
-        const uint16_t *sK = Kb(par);
-        const uint16_t *sQ = Qb(par);
+    auto chain_chunk = [&](int par, int b3, int64_t c) {
+        const uint16_t *sK = Kb(b3);
+        const uint16_t *sQ = Qb(b3);
         const uint16_t *sAo = Aob(par);
         const uint16_t *sDi = Dib(par);
         const uint16_t *sPp = Pb(par);
@@ -727,13 +720,11 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         }
     };
 
-    // The arrival counter starts at zero before any preparation wave uses it.
-    if (tid == 0) *sArrive = 0u;
-    __syncthreads();
-
-    // The two roles run separate loops with the same barrier sequence: one
-    // barrier after the preparation of chunk 0, then one per chunk.
-    // (s_barrier counts arriving waves; the roles are uniform per wave.)
+    // The two roles run separate loops with the same barrier sequence: two
+    // barriers for the prologue, then one per chunk.  (s_barrier counts
+    // arriving waves; the roles are uniform per wave.)  q and k of chunk c sit
+    // in buffer c % 3: the chain reads chunk c, the preparation waves read
+    // chunk c+1 and store chunk c+2, loaded at the start of the same step.
     if (chain) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -744,9 +735,12 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                     hs[kb][nt][r] = a.h0 ? a.h0[sbase + dk_of(kb, 4 * lq + r) * D + dv_of(nt, l16)] : 0.f;
         load_v(0);
         __syncthreads();
+        __syncthreads();
+        int b3 = 0;
         for (int64_t c = 0; c < nch; ++c) {
-            chain_chunk(static_cast<int>(c & 1), c);
+            chain_chunk(static_cast<int>(c & 1), b3, c);
             __syncthreads();
+            b3 = b3 == 2 ? 0 : b3 + 1;
         }
         if (a.ht) {
 #pragma unroll
@@ -758,24 +752,33 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                         a.ht[sbase + dk_of(kb, 4 * lq + r) * D + dv_of(nt, l16)] = hs[kb][nt][r];
         }
     } else {
-        // prologue: chunk 0
+        // prologue: q, k of chunks 0 and 1 into buffers 0 and 1, gates of
+        // chunk 0, then chunk 0 prepared
         load_qk(0);
-        stage(0);
-        prep_arrive_wait(4u);
+        store_qk(0);
         load_qk(1);   // zero when there is no chunk 1
-        prep_kq(0);
+        store_qk(1);
+        load_gates(0);
+        gates(0);
+        load_gates(1);
+        __syncthreads();
+        prep_kq(0, 0);
         block_inv(0);
         __syncthreads();
         // chunk c+1 while the chain works on chunk c; past the last chunk the
         // preparation runs on zero rows and its results are never read
+        int b3 = 0;
         for (int64_t c = 0; c < nch; ++c) {
             const int npar = static_cast<int>((c + 1) & 1);
-            stage(npar);
-            prep_arrive_wait(static_cast<uint32_t>(4 * (c + 2)));
+            const int b3n = b3 == 2 ? 0 : b3 + 1, b3nn = b3n == 2 ? 0 : b3n + 1;
             load_qk(c + 2);
-            prep_kq(npar);
+            gates(npar);
+            load_gates(c + 2);
+            prep_kq(npar, b3n);
             block_inv(npar);
+            store_qk(b3nn);
             __syncthreads();
+            b3 = b3n;
         }
     }
 }
