@@ -8,6 +8,9 @@ timed region.  Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
+The defaults (100 warm-up calls, 200 timed) let the clock settle: the first
+few milliseconds of back-to-back calls run through a clock transient.
+
 Two helper modes feed the HBM traffic figure of the roofline object:
   python bench.py --copy-probe-mib M     a plain device copy of M MiB (one
                                          elementwise kernel that reads M MiB
@@ -64,8 +67,8 @@ def bytes_alg(T: int, N: int, hk: int, hv: int, dk: int, dv: int, in_bytes: int,
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="packed64k_gqa_Hk16_Hv32_d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8,
@@ -119,13 +122,13 @@ def main():
     def step():
         gdr.chunk_fwd(q, k, v, g, beta, cu, h0, scale=d["scale"], o=o, ht=ht)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
+    # events are created before the warm-up: creating them after it would
+    # leave the GPU idle long enough to restart its clock transient
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s, e in ev:

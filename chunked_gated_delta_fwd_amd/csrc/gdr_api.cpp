@@ -13,7 +13,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "gdr_internal.h"
@@ -212,6 +214,40 @@ int check_device() {
     return GDR_OK;
 }
 
+// Library-owned stream-ordered memory pool of a device for the small
+// per-call workspace.  Its release threshold keeps freed blocks reserved, so
+// an allocation never has to map memory again; the default pool hands its
+// memory back at synchronisation points, and re-mapping it now and then
+// stalled a call for tens of milliseconds.  Created on first use, kept until
+// the process ends (it holds at most the largest workspace asked for).
+hipError_t workspace_pool(hipMemPool_t *out) {
+    static std::mutex mu;
+    static hipMemPool_t pools[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!pools[dev]) {
+        hipMemPoolProps props;
+        std::memset(&props, 0, sizeof(props));
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        if ((e = hipMemPoolCreate(&pool, &props)) != hipSuccess) return e;
+        uint64_t keep = UINT64_MAX;
+        if ((e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) {
+            (void)hipMemPoolDestroy(pool);
+            return e;
+        }
+        pools[dev] = pool;
+    }
+    *out = pools[dev];
+    return hipSuccess;
+}
+
 int launch_error(hipError_t e, const char *what) {
     return fail(GDR_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
 }
@@ -260,7 +296,9 @@ int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
 
     void *ws = nullptr;
     if (cu_seqlens) {
-        hipError_t e = hipMallocAsync(&ws, static_cast<size_t>(p.workspace_bytes), stream);
+        hipMemPool_t pool = nullptr;
+        hipError_t e = workspace_pool(&pool);
+        if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, static_cast<size_t>(p.workspace_bytes), pool, stream);
         if (e != hipSuccess) return fail(GDR_ENOMEM, "workspace of %lld bytes: %s",
                                          (long long)p.workspace_bytes, hipGetErrorString(e));
         int32_t *order = static_cast<int32_t *>(ws);
@@ -345,7 +383,9 @@ int gdr_chunk_local_cumsum(const gdr_tensor *g, const gdr_tensor *cu_seqlens, co
     if (nt_max > 0x7FFFFFFFLL) return fail(GDR_ESHAPE, "too many chunks");
     void *ws = nullptr;
     const size_t bytes = static_cast<size_t>(nt_max) * 8;
-    hipError_t e = hipMallocAsync(&ws, bytes, stream);
+    hipMemPool_t pool = nullptr;
+    hipError_t e = workspace_pool(&pool);
+    if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, bytes, pool, stream);
     if (e != hipSuccess) return fail(GDR_ENOMEM, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
     int32_t *map = static_cast<int32_t *>(ws);
     const int32_t *cu = static_cast<const int32_t *>(cu_seqlens->data);

@@ -103,8 +103,11 @@ typedef struct {
  * Results do not depend on scheduling: ghost padding and repeated calls are
  * bitwise reproducible.
  *
- * Uses a small stream-ordered device workspace (hipMallocAsync / hipFreeAsync
- * on `stream`, 4*N bytes) when cu_seqlens is given.
+ * Uses a small stream-ordered device workspace (4*N bytes, allocated and
+ * freed on `stream`) when cu_seqlens is given.  It comes from a memory pool
+ * the library creates per device on first use and keeps until the process
+ * ends, with its release threshold raised so freed blocks stay reserved
+ * (the pool holds at most the largest workspace requested).
  */
 int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
                   const gdr_tensor *g, const gdr_tensor *beta, const gdr_tensor *cu_seqlens,
@@ -166,7 +169,8 @@ int gdr_prepare_chunks(const gdr_tensor *cu_seqlens, const gdr_tensor *chunk_off
  *   cu_seqlens  [N+1] int32 or NULL (B fixed-length rows)
  *   G           [B, T, H] f32 out (rows outside every segment not written)
  *
- * Uses a stream-ordered workspace for the chunk map (8 * nt_max + 4 * (N+1) bytes).
+ * Uses a stream-ordered workspace for the chunk map (8 * nt_max bytes) from the
+ * same per-device pool as gdr_chunk_fwd.
  */
 int gdr_chunk_local_cumsum(const gdr_tensor *g, const gdr_tensor *cu_seqlens,
                            const gdr_tensor *G, hipStream_t stream);
