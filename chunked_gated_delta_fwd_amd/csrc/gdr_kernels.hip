@@ -612,10 +612,19 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 R[blk][nt] = x * bb - bg * R[blk][nt];
             }
         }
+
         load_v(c + 1);   // zero past the end
 
         // Vnew: block forward substitution X_a = D_a (R_a - sum_{c<a} A_ac X_c)
-        // (sAo holds -A); R becomes Vnew in f32, Xb its bf16 copy
+        // (sAo holds -A); R becomes Vnew in f32, Xb its bf16 copy.  Right after
+        // block a is solved, the output of token block a is formed and stored:
+        // O^T = diag(scale e^G) (H^T Q^T) + Vnew^T P^T (P carries the scale)
+        // needs Vnew of blocks <= a only, and its H^T Q^T products do not
+        // depend on the substitution, so they fill its dependency gaps.
+        const int L = chunk_len(c);
+        const uint32_t rowb = static_cast<uint32_t>(a.hv) * D * ES;
+        const __amdgpu_buffer_rsrc_t ro = chunk_rsrc(
+            reinterpret_cast<unsigned char *>(a.o) + (((bos + c * C) * a.hv + h) * D) * ES, L * rowb);
         bf16x4 Xb[4][NTW];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
@@ -636,59 +645,49 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 R[blk][nt] = mfma16z(df, cvt4(R[blk][nt]), zero4());
                 Xb[blk][nt] = cvt4(R[blk][nt]);
             }
-        }
 
-        // O^T = diag(scale e^G) (H^T Q^T) + Vnew^T P^T (P carries the scale), one
-        // 16-token block at a time (H^T Q^T of the block first), stored 4 dv per lane
-        {
-            const int L = chunk_len(c);
-            const uint32_t rowb = static_cast<uint32_t>(a.hv) * D * ES;
-            const __amdgpu_buffer_rsrc_t ro = chunk_rsrc(
-                reinterpret_cast<unsigned char *>(a.o) + (((bos + c * C) * a.hv + h) * D) * ES, L * rowb);
+            // output of token block blk, stored 4*NTW dv per lane
+            f32x4 Ot[NTW];
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                f32x4 Ot[NTW];
+            for (int nt = 0; nt < NTW; ++nt) Ot[nt] = zero4();
+            const uint16_t *pq_ = sQ + (16 * blk + l16) * PK + 8 * lq;
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) Ot[nt] = zero4();
-                const uint16_t *pq_ = sQ + (16 * blk + l16) * PK + 8 * lq;
+            for (int p = 0; p < KB / 2; ++p) {
+                const bf16x8 bq = ld8(pq_ + 32 * p);
 #pragma unroll
-                for (int p = 0; p < KB / 2; ++p) {
-                    const bf16x8 bq = ld8(pq_ + 32 * p);
+                for (int nt = 0; nt < NTW; ++nt) Ot[nt] = mfma32(cat(hb[2 * p][nt], hb[2 * p + 1][nt]), bq, Ot[nt]);
+            }
+            const float gt = vgam[16 * blk + l16];
 #pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt) Ot[nt] = mfma32(cat(hb[2 * p][nt], hb[2 * p + 1][nt]), bq, Ot[nt]);
-                }
-                const float gt = vgam[16 * blk + l16];
+            for (int nt = 0; nt < NTW; ++nt) Ot[nt] = Ot[nt] * gt;
+            const uint16_t *pp = sPp + (16 * blk + l16) * PP;
+            if (blk >= 1) {
+                const bf16x8 bf = ld8(pp + 8 * lq);   // keys of blocks 0, 1
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) Ot[nt] = Ot[nt] * gt;
-                const uint16_t *pp = sPp + (16 * blk + l16) * PP;
-                if (blk >= 1) {
-                    const bf16x8 bf = ld8(pp + 8 * lq);   // keys of blocks 0, 1
+                for (int nt = 0; nt < NTW; ++nt) Ot[nt] = mfma32(cat(Xb[0][nt], Xb[1][nt]), bf, Ot[nt]);
+            }
+            if (blk == 3) {
+                const bf16x8 bf = ld8(pp + 32 + 8 * lq);   // keys of blocks 2, 3
 #pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt) Ot[nt] = mfma32(cat(Xb[0][nt], Xb[1][nt]), bf, Ot[nt]);
-                }
-                if (blk == 3) {
-                    const bf16x8 bf = ld8(pp + 32 + 8 * lq);   // keys of blocks 2, 3
+                for (int nt = 0; nt < NTW; ++nt) Ot[nt] = mfma32(cat(Xb[2][nt], Xb[3][nt]), bf, Ot[nt]);
+            }
+            if ((blk & 1) == 0) {
+                const bf16x4 bf = ld4(pp + pc(16 * blk + 4 * lq));
 #pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt) Ot[nt] = mfma32(cat(Xb[2][nt], Xb[3][nt]), bf, Ot[nt]);
-                }
-                if ((blk & 1) == 0) {
-                    const bf16x4 bf = ld4(pp + pc(16 * blk + 4 * lq));
+                for (int nt = 0; nt < NTW; ++nt) Ot[nt] = mfma16z(Xb[blk][nt], bf, Ot[nt]);
+            }
+            // lane (l16, lq) holds o[token 16blk+l16][dv colw + 4*NTW*lq .. + 4*NTW-1]
+            const uint32_t off = (16 * blk + l16) * rowb + (colw + 4 * NTW * lq) * ES;
+            if constexpr (IN_BF16) {
+                if constexpr (NTW == 2)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(v4u32, cat(cvt4(Ot[0]), cvt4(Ot[NTW - 1]))), ro, off, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, cvt4(Ot[0])), ro, off, 0, 0);
+            } else {
 #pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt) Ot[nt] = mfma16z(Xb[blk][nt], bf, Ot[nt]);
-                }
-                // lane (l16, lq) holds o[token 16blk+l16][dv colw + 4*NTW*lq .. + 4*NTW-1]
-                const uint32_t off = (16 * blk + l16) * rowb + (colw + 4 * NTW * lq) * ES;
-                if constexpr (IN_BF16) {
-                    if constexpr (NTW == 2)
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            __builtin_bit_cast(v4u32, cat(cvt4(Ot[0]), cvt4(Ot[NTW - 1]))), ro, off, 0, 0);
-                    else
-                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, cvt4(Ot[0])), ro, off, 0, 0);
-                } else {
-#pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt)
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, Ot[nt]), ro, off + 16 * nt, 0, 0);
-                }
+                for (int nt = 0; nt < NTW; ++nt)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, Ot[nt]), ro, off + 16 * nt, 0, 0);
             }
         }
 
