@@ -96,6 +96,9 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ bf16x4 neg4(bf16x4 x) {   // exact: flips the sign bits
+    return __builtin_bit_cast(bf16x4, __builtin_bit_cast(v2u32, x) ^ 0x80008000u);
+}
 
 template <bool BF16>
 __device__ __forceinline__ float load_scalar(const void *p, int64_t i) {
@@ -219,20 +222,20 @@ struct FwdLds {
     // and the transposing reads of k (4 rows x 32 bytes per 16 lanes) free of
     // bank conflicts.
     static constexpr int PK = D + 16;
-    static constexpr int PP = C + 8;    // [64][64] bf16, keys permuted: P and -A off the diagonal, two buffers each
-    static constexpr int PAT = 20;      // [4][16][16] f32: diagonal blocks of A, transposed (preparation only)
-    static constexpr int PDI = 24;      // [4][16][16] bf16: inverses of the diagonal blocks, two buffers
+    static constexpr int PP = C + 8;    // [64][64] bf16, keys permuted: P and -A~ off the diagonal, two buffers each
+    static constexpr int PAT = 16;      // [4][16][16] bf16: diagonal blocks of A, transposed (preparation only)
+    static constexpr int PDI = 16;      // [4][16][16] bf16: scaled inverses of the diagonal blocks, two kinds x two buffers
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + 3 * C * PK * 2;
     static constexpr int oP = oK + 3 * C * PK * 2;
     static constexpr int oAo = oP + 2 * C * PP * 2;
     static constexpr int oAT = oAo + 2 * C * PP * 2;
-    static constexpr int oDi = oAT + 4 * 16 * PAT * 4;
-    static constexpr int oS = oDi + 2 * 4 * 16 * PDI * 2;
+    static constexpr int oDi = oAT + 4 * 16 * PAT * 2;
+    static constexpr int oDd = oDi + 2 * 4 * 16 * PDI * 2;
+    static constexpr int oS = oDd + 2 * 4 * 16 * PDI * 2;
     // f32 vectors of 64: per preparation wave its own G*log2(e) and beta of
-    // the chunk it prepares; per buffer beta, beta*e^G, scale*e^G,
-    // e^{G_L-G}; then e^{G_L} per buffer
-    static constexpr int bytes = oS + 16 * C * 4 + 16;
+    // the chunk it prepares; per buffer e^G and scale*e^G; then e^{G_L} per buffer
+    static constexpr int bytes = oS + 12 * C * 4 + 16;
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -291,22 +294,22 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     uint16_t *const sK0 = reinterpret_cast<uint16_t *>(smem + Ly::oK);
     uint16_t *const sP0 = reinterpret_cast<uint16_t *>(smem + Ly::oP);
     uint16_t *const sAo0 = reinterpret_cast<uint16_t *>(smem + Ly::oAo);
-    float *const sAT = reinterpret_cast<float *>(smem + Ly::oAT);
+    uint16_t *const sAT = reinterpret_cast<uint16_t *>(smem + Ly::oAT);
     uint16_t *const sDi0 = reinterpret_cast<uint16_t *>(smem + Ly::oDi);
+    uint16_t *const sDd0 = reinterpret_cast<uint16_t *>(smem + Ly::oDd);
     float *const sGw0 = reinterpret_cast<float *>(smem + Ly::oS);  // [4 prep waves][G*log2e, beta][64]
-    float *const sVec0 = sGw0 + 8 * C;                              // [2][4][64]
-    float *const sGL = sGw0 + 16 * C;                               // [2]
+    float *const sVec0 = sGw0 + 8 * C;                              // [2][2][64]
+    float *const sGL = sGw0 + 12 * C;                               // [2]
 
     // per-buffer views
     auto Qb = [&](int b3) { return sQ0 + b3 * C * PK; };   // buffer b3 = chunk % 3
     auto Kb = [&](int b3) { return sK0 + b3 * C * PK; };
     auto Pb = [&](int par) { return sP0 + par * C * PP; };
     auto Aob = [&](int par) { return sAo0 + par * C * PP; };
-    auto Dib = [&](int par) { return sDi0 + par * 4 * 16 * PDI; };
-    auto vB = [&](int par) { return sVec0 + par * 4 * C; };            // beta
-    auto vBG = [&](int par) { return sVec0 + par * 4 * C + C; };       // beta e^G
-    auto vGam = [&](int par) { return sVec0 + par * 4 * C + 2 * C; };  // scale e^G
-    auto vDec = [&](int par) { return sVec0 + par * 4 * C + 3 * C; };  // e^{G_L - G}
+    auto Dib = [&](int par) { return sDi0 + par * 4 * 16 * PDI; };   // D_a diag(b_a)
+    auto Ddb = [&](int par) { return sDd0 + par * 4 * 16 * PDI; };   // diag(e^{G_L - G_a}) D_a diag(b_a)
+    auto vEG = [&](int par) { return sVec0 + par * 2 * C; };         // e^G
+    auto vGam = [&](int par) { return sVec0 + par * 2 * C + C; };    // scale e^G
 
     // ---- work item: (sequence n, v-head h), longest sequences first.
     // Work-groups are dispatched round-robin over the 8 XCDs (each with its
@@ -452,17 +455,16 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         sBw[lane] = pb;
         if (role == 0) {
             const float gam = fast_exp2(G2);
-            vB(par)[lane] = pb;
-            vBG(par)[lane] = pb * gam;
+            vEG(par)[lane] = gam;
             vGam(par)[lane] = gam * a.scale;
-            vDec(par)[lane] = fast_exp2(GL2 - G2);
             if (lane == 0) sGL[par] = fast_exp2(GL2);
         }
         lds_wait();   // this wave's copies are written before its strips read them
     };
 
-    // prep: gated K K^T -> A (diagonal blocks f32 transposed, others -A bf16)
-    // and gated Q K^T -> P (scale folded in), by row strips: strip i holds
+    // prep: gated K K^T -> A (diagonal blocks transposed, with beta; the
+    // others as -A~ = -diag(1/b) A, i.e. without beta) and gated Q K^T -> P
+    // (scale folded in), by row strips: strip i holds
     // the tiles (i, j <= i) of both products, which share k_j as the A
     // operand; the B operands (k_i, q_i) stay in registers across the strip.
     auto prep_kq = [&](int par, int b3) {
@@ -483,7 +485,6 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 if (do_qk) bq[p] = ld8(pqi + 32 * p);
             }
             const float gi_col = sG2[16 * i + l16];
-            const float bi_col = sB[16 * i + l16];
             for (int j = 0; j <= i; ++j) {
                 f32x4 akk = zero4(), aqk = zero4();
                 const uint16_t *pkj = sK + (16 * j + l16) * PK + 8 * lq;
@@ -509,7 +510,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                     if (j < i) {
                         f32x4 out;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) out[r] = -bi_col * fast_exp2(gi_col - gj[r]) * akk[r];
+                        for (int r = 0; r < 4; ++r) out[r] = -fast_exp2(gi_col - gj[r]) * akk[r];
                         st4(sAo + ic * PP + pc(16 * j + 4 * lq), cvt4(out));
                     } else {
                         // diagonal, symmetric: read it as (row i' = 16i+4lq+r, column j' = 16i+l16)
@@ -520,7 +521,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                             const bool keep = 4 * lq + r > l16;
                             out[r] = keep ? bi[r] * fast_exp2(gj[r] - gi_col) * akk[r] : 0.f;
                         }
-                        *reinterpret_cast<f32x4 *>(sAT + (16 * i + l16) * PAT + 4 * lq) = out;
+                        st4(sAT + (16 * i + l16) * PAT + 4 * lq, cvt4(out));
                     }
                 }
             }
@@ -540,19 +541,20 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     // tile of M is the A fragment of M^T and the B fragment of M, so each
     // factor is carried with its transpose: 8 one-block MFMAs, 4 dependent
     // levels, and the last product comes out as D^T in C layout, i.e. the
-    // rows of D, ready to store.
+    // rows of D.  Stored are D diag(b) (the substitution works on A~, which
+    // lacks the row factor b) and diag(e^{G_L - G}) D diag(b), which gives the
+    // decayed rows of Vnew for the state update directly.
     auto block_inv = [&](int par) __attribute__((always_inline)) {
         const int b = 3 - role;
-        const float *at = sAT + b * 16 * PAT;
+        const uint16_t *at = sAT + b * 16 * PAT;
         lds_wait();   // this wave's own writes of the block
-        const f32x4 cl = *reinterpret_cast<const f32x4 *>(at + l16 * PAT + 4 * lq);   // L[4lq+r][l16]
-        f32x4 al;                                                                      // L[l16][4lq+r]
-#pragma unroll
-        for (int r = 0; r < 4; ++r) al[r] = at[(4 * lq + r) * PAT + l16];
+        const bf16x4 cl = ld4(at + l16 * PAT + 4 * lq);                               // L[4lq+r][l16]
+        const bf16x4 alb = ld4_tr(at + (4 * lq + (l16 >> 2)) * PAT + 4 * (l16 & 3));  // L[l16][4lq+r]
+        const f32x4 al = up4(alb);
         f32x4 eye;
 #pragma unroll
         for (int r = 0; r < 4; ++r) eye[r] = (4 * lq + r == l16) ? 1.f : 0.f;
-        const bf16x4 x = cvt4(-cl), xt = cvt4(-al);             // C(X), C(X^T)
+        const bf16x4 x = neg4(cl), xt = neg4(alb);               // C(X), C(X^T)
         const f32x4 x2 = mfma16z(xt, x, zero4());                // C(X^2)
         const f32x4 x2t = mfma16z(x, xt, zero4());               // C((X^2)^T)
         const bf16x4 x2b = cvt4(x2), x2tb = cvt4(x2t);
@@ -564,7 +566,11 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         const f32x4 p3t = mfma16z(x4b, cvt4(p2t), p2t);          // C(P3^T), P3 = P2 (I + X^4)
         const f32x4 x8 = mfma16z(cvt4(x4t), x4b, zero4());       // C(X^8)
         const f32x4 dt = mfma16z(cvt4(x8), cvt4(p3t), p3t);      // C(D^T): lane holds D[l16][4lq+r]
-        st4(Dib(par) + (16 * b + l16) * PDI + 4 * lq, cvt4(dt));
+        const f32x4 bc = *reinterpret_cast<const f32x4 *>(sBw + 16 * b + 4 * lq);
+        const float dec = fast_exp2(sG2[C - 1] - sG2[16 * b + l16]);   // padding has g = 0: G_L at the last row
+        const f32x4 d1 = dt * bc;
+        st4(Dib(par) + (16 * b + l16) * PDI + 4 * lq, cvt4(d1));
+        st4(Ddb(par) + (16 * b + l16) * PDI + 4 * lq, cvt4(d1 * dec));
     };
 
     auto to_bf16_state = [&](bf16x4 (&hb)[KB][NTW]) {
@@ -580,13 +586,15 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         const uint16_t *sQ = Qb(b3);
         const uint16_t *sAo = Aob(par);
         const uint16_t *sDi = Dib(par);
+        const uint16_t *sDd = Ddb(par);
         const uint16_t *sPp = Pb(par);
-        const float *vb = vB(par), *vbg = vBG(par), *vgam = vGam(par), *vdec = vDec(par);
+        const float *veg = vEG(par), *vgam = vGam(par);
 
         bf16x4 hb[KB][NTW];
         to_bf16_state(hb);
 
-        // R = diag(b) V - diag(b e^G) (K H): rows token 16blk+4lq+r, column dv
+        // R~ = V - diag(e^G) (K H): rows token 16blk+4lq+r, column dv (the
+        // beta factor of the right-hand side sits in the stored inverses)
         f32x4 R[4][NTW];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
@@ -602,21 +610,21 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         }
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
-            const f32x4 bb = *reinterpret_cast<const f32x4 *>(vb + 16 * blk + 4 * lq);
-            const f32x4 bg = *reinterpret_cast<const f32x4 *>(vbg + 16 * blk + 4 * lq);
+            const f32x4 eg = *reinterpret_cast<const f32x4 *>(veg + 16 * blk + 4 * lq);
             const bf16x8 va = NTW == 2 ? cat(vp[blk][0], vp[blk][NTW - 1]) : ext8(vp[blk][0]);
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
                 // v (row token, k dv) times a selection: (row token 16blk+4lq+r, column dv_of(nt, l16))
                 const f32x4 x = mfma32(va, sel[nt], zero4());
-                R[blk][nt] = x * bb - bg * R[blk][nt];
+                R[blk][nt] = x - eg * R[blk][nt];
             }
         }
 
         load_v(c + 1);   // zero past the end
 
-        // Vnew: block forward substitution X_a = D_a (R_a - sum_{c<a} A_ac X_c)
-        // (sAo holds -A); R becomes Vnew in f32, Xb its bf16 copy.  Right after
+        // Vnew: block forward substitution X_a = D_a diag(b_a) (R~_a - sum_{c<a} A~_ac X_c)
+        // (sAo holds -A~, A = diag(b) A~); Xb is Vnew in bf16 and Vt its rows
+        // scaled by e^{G_L - G} (second scaled inverse, same operand).  Right after
         // block a is solved, the output of token block a is formed and stored:
         // O^T = diag(scale e^G) (H^T Q^T) + Vnew^T P^T (P carries the scale)
         // needs Vnew of blocks <= a only, and its H^T Q^T products do not
@@ -625,7 +633,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         const uint32_t rowb = static_cast<uint32_t>(a.hv) * D * ES;
         const __amdgpu_buffer_rsrc_t ro = chunk_rsrc(
             reinterpret_cast<unsigned char *>(a.o) + (((bos + c * C) * a.hv + h) * D) * ES, L * rowb);
-        bf16x4 Xb[4][NTW];
+        bf16x4 Xb[4][NTW], Vt[4][NTW];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
             const uint16_t *ar = sAo + (16 * blk + l16) * PP;
@@ -640,10 +648,12 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 for (int nt = 0; nt < NTW; ++nt) R[blk][nt] = mfma16z(af, Xb[blk - 1][nt], R[blk][nt]);
             }
             const bf16x4 df = ld4(sDi + (16 * blk + l16) * PDI + 4 * lq);
+            const bf16x4 dd = ld4(sDd + (16 * blk + l16) * PDI + 4 * lq);
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
-                R[blk][nt] = mfma16z(df, cvt4(R[blk][nt]), zero4());
-                Xb[blk][nt] = cvt4(R[blk][nt]);
+                const bf16x4 rb = cvt4(R[blk][nt]);
+                Xb[blk][nt] = cvt4(mfma16z(df, rb, zero4()));
+                Vt[blk][nt] = cvt4(mfma16z(dd, rb, zero4()));
             }
 
             // output of token block blk, stored 4*NTW dv per lane
@@ -691,18 +701,11 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             }
         }
 
-        // H <- e^{G_L} H + K^T diag(e^{G_L - G}) Vnew; the K^T fragments are
+        // H <- e^{G_L} H + K^T Vt, Vt = diag(e^{G_L - G}) Vnew; the K^T fragments are
         // transposing reads of the k rows: lane (l16, lq) of tile kb gets
         // k[32p' + 4lq + r][dk_of(kb, l16)] (and tokens +16 for slots 4-7)
         {
             const float gl = sGL[par];
-            bf16x4 Vt[4][NTW];
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(vdec + 16 * blk + 4 * lq);
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) Vt[blk][nt] = cvt4(R[blk][nt] * d4);
-            }
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 const uint16_t *pkt = sK + (4 * lq + (l16 >> 2)) * PK + 32 * (kb >> 1) + 4 * (kb & 1) + 8 * (l16 & 3);
