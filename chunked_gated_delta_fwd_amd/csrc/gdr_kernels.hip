@@ -96,6 +96,10 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
 __device__ __forceinline__ bf16x4 neg4(bf16x4 x) {   // exact: flips the sign bits
     return __builtin_bit_cast(bf16x4, __builtin_bit_cast(v2u32, x) ^ 0x80008000u);
 }
@@ -214,6 +218,9 @@ __device__ __forceinline__ bf16x8 ext8(bf16x4 a) { return __builtin_shufflevecto
 
 // wait until this wave's LDS accesses are complete (also a compiler barrier)
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// polls of a progress counter before a wave gives up waiting (about 2^18 *
+// 64 cycles); reached only if the other role stopped publishing
+constexpr int kSpinMax = 1 << 18;
 
 template <int D>
 struct FwdLds {
@@ -234,7 +241,8 @@ struct FwdLds {
     static constexpr int oDd = oDi + 2 * 4 * 16 * PDI * 2;
     static constexpr int oS = oDd + 2 * 4 * 16 * PDI * 2;
     // f32 vectors of 64: per preparation wave its own G*log2(e) and beta of
-    // the chunk it prepares; per buffer e^G and scale*e^G; then e^{G_L} per buffer
+    // the chunk it prepares; per buffer e^G and scale*e^G; then e^{G_L} per
+    // buffer and the two progress counters
     static constexpr int bytes = oS + 12 * C * 4 + 16;
 };
 
@@ -300,6 +308,10 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     float *const sGw0 = reinterpret_cast<float *>(smem + Ly::oS);  // [4 prep waves][G*log2e, beta][64]
     float *const sVec0 = sGw0 + 8 * C;                              // [2][2][64]
     float *const sGL = sGw0 + 12 * C;                               // [2]
+    // progress counters: cPrep += 1 per preparation wave per finished step,
+    // cChain += 1 per chain wave per finished chunk
+    uint32_t *const cPrep = reinterpret_cast<uint32_t *>(sGL + 2);
+    uint32_t *const cChain = cPrep + 1;
 
     // per-buffer views
     auto Qb = [&](int b3) { return sQ0 + b3 * C * PK; };   // buffer b3 = chunk % 3
@@ -352,6 +364,24 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     const int lq = lane >> 4;
     const int colw = role * DW;         // the chain wave's 16*NTW state columns
     const int64_t nch = (eos - bos + C - 1) / C;
+
+    // Cross-role hand-off through the LDS counters instead of work-group
+    // barriers: a wave publishes a step after its own LDS accesses are
+    // complete, and waits (bounded, so a wave always finishes) until a
+    // counter reaches a target.
+    auto publish = [&](uint32_t *cnt) {
+        lds_wait();
+        if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    auto wait_for = [&](const uint32_t *cnt, uint32_t target) {
+        for (int it = 0; it < kSpinMax; ++it) {
+            const uint32_t seen = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+            if (seen >= target) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        lds_wait();
+    };
 
     auto chunk_len = [&](int64_t c) -> int {
         const int64_t r = eos - (bos + c * C);
@@ -464,75 +494,74 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 
     // prep: gated K K^T -> A (diagonal blocks transposed, with beta; the
     // others as -A~ = -diag(1/b) A, i.e. without beta) and gated Q K^T -> P
-    // (scale folded in), by row strips: strip i holds
-    // the tiles (i, j <= i) of both products, which share k_j as the A
-    // operand; the B operands (k_i, q_i) stay in registers across the strip.
+    // (scale folded in), by row strips of 16x16 tiles (i, j <= i).  Wave p
+    // takes K K^T strip 3-p and Q K^T strip p: five tiles each, and it owns
+    // diagonal block 3-p of A.  The B operands (k_i, q_i rows) stay in
+    // registers across a strip; each k_j fragment read serves both strips.
     auto prep_kq = [&](int par, int b3) {
         uint16_t *sPp = Pb(par);
         uint16_t *sAo = Aob(par);
         const uint16_t *sQ = Qb(b3);
         const uint16_t *sK = Kb(b3);
         const float *sB = sBw;
-        // strips per prep wave: p0 = K K^T of strip 3, p1 = strip 2, p2 = strip 1,
-        // p3 = Q K^T of strip 3 and strip 0; wave p holds diagonal block 3-p
-        auto strip = [&](int i, bool do_kk, bool do_qk) {
+        auto strips = [&](auto ikc, auto iqc) __attribute__((always_inline)) {
+            constexpr int IK = decltype(ikc)::value, IQ = decltype(iqc)::value;
+            constexpr int JMAX = IK > IQ ? IK : IQ;
             bf16x8 bk[KB / 2], bq[KB / 2];
-            const uint16_t *pki = sK + (16 * i + l16) * PK + 8 * lq;
-            const uint16_t *pqi = sQ + (16 * i + l16) * PK + 8 * lq;
+            const uint16_t *pki = sK + (16 * IK + l16) * PK + 8 * lq;
+            const uint16_t *pqi = sQ + (16 * IQ + l16) * PK + 8 * lq;
 #pragma unroll
             for (int p = 0; p < KB / 2; ++p) {
-                if (do_kk) bk[p] = ld8(pki + 32 * p);
-                if (do_qk) bq[p] = ld8(pqi + 32 * p);
+                bk[p] = ld8(pki + 32 * p);
+                bq[p] = ld8(pqi + 32 * p);
             }
-            const float gi_col = sG2[16 * i + l16];
-            for (int j = 0; j <= i; ++j) {
+            const float gk_col = sG2[16 * IK + l16];
+            const float gq_col = sG2[16 * IQ + l16];
+#pragma unroll
+            for (int j = 0; j <= JMAX; ++j) {
                 f32x4 akk = zero4(), aqk = zero4();
                 const uint16_t *pkj = sK + (16 * j + l16) * PK + 8 * lq;
 #pragma unroll
                 for (int p = 0; p < KB / 2; ++p) {
-                    const bf16x8 af = (j == i && do_kk) ? bk[p] : ld8(pkj + 32 * p);
-                    if (do_kk) akk = mfma32(af, bk[p], akk);
-                    if (do_qk) aqk = mfma32(af, bq[p], aqk);
+                    const bf16x8 af = j == IK ? bk[p] : ld8(pkj + 32 * p);
+                    if (j <= IK) akk = mfma32(af, bk[p], akk);
+                    if (j <= IQ) aqk = mfma32(af, bq[p], aqk);
                 }
                 // tile element (row j' = 16j+4lq+r, column i' = 16i+l16) = k_j' . k_i' (resp. . q_i')
-                const int ic = 16 * i + l16;
                 const f32x4 gj = *reinterpret_cast<const f32x4 *>(sG2 + 16 * j + 4 * lq);
-                if (do_qk) {
+                if (j <= IQ) {
+                    const int ic = 16 * IQ + l16;
                     f32x4 out;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const bool keep = ic >= 16 * j + 4 * lq + r;
-                        out[r] = keep ? a.scale * fast_exp2(gi_col - gj[r]) * aqk[r] : 0.f;
+                        out[r] = keep ? a.scale * fast_exp2(gq_col - gj[r]) * aqk[r] : 0.f;
                     }
                     st4(sPp + ic * PP + pc(16 * j + 4 * lq), cvt4(out));
                 }
-                if (do_kk) {
-                    if (j < i) {
-                        f32x4 out;
+                if (j < IK) {
+                    const int ic = 16 * IK + l16;
+                    f32x4 out;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) out[r] = -fast_exp2(gi_col - gj[r]) * akk[r];
-                        st4(sAo + ic * PP + pc(16 * j + 4 * lq), cvt4(out));
-                    } else {
-                        // diagonal, symmetric: read it as (row i' = 16i+4lq+r, column j' = 16i+l16)
-                        const f32x4 bi = *reinterpret_cast<const f32x4 *>(sB + 16 * i + 4 * lq);
-                        f32x4 out;
+                    for (int r = 0; r < 4; ++r) out[r] = -fast_exp2(gk_col - gj[r]) * akk[r];
+                    st4(sAo + ic * PP + pc(16 * j + 4 * lq), cvt4(out));
+                } else if (j == IK) {
+                    // diagonal, symmetric: read it as (row i' = 16i+4lq+r, column j' = 16i+l16)
+                    const f32x4 bi = *reinterpret_cast<const f32x4 *>(sB + 16 * IK + 4 * lq);
+                    f32x4 out;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const bool keep = 4 * lq + r > l16;
-                            out[r] = keep ? bi[r] * fast_exp2(gj[r] - gi_col) * akk[r] : 0.f;
-                        }
-                        st4(sAT + (16 * i + l16) * PAT + 4 * lq, cvt4(out));
+                    for (int r = 0; r < 4; ++r) {
+                        const bool keep = 4 * lq + r > l16;
+                        out[r] = keep ? bi[r] * fast_exp2(gj[r] - gk_col) * akk[r] : 0.f;
                     }
+                    st4(sAT + (16 * IK + l16) * PAT + 4 * lq, cvt4(out));
                 }
             }
         };
-        if (role == 0) strip(3, true, false);
-        else if (role == 1) strip(2, true, true);
-        else if (role == 2) strip(1, true, true);
-        else {
-            strip(3, false, true);
-            strip(0, true, true);
-        }
+        if (role == 0) strips(IntC<3>{}, IntC<0>{});
+        else if (role == 1) strips(IntC<2>{}, IntC<1>{});
+        else if (role == 2) strips(IntC<1>{}, IntC<2>{});
+        else strips(IntC<0>{}, IntC<3>{});
     };
 
     // prep: inverse of diagonal block b = 3 - role of I + A (the block this
@@ -580,7 +609,8 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             for (int nt = 0; nt < NTW; ++nt) hb[kb][nt] = cvt4(hs[kb][nt]);
     };
 
-    // chain: one chunk.  t0, L: its first token and length.
+    // chain: one chunk.  K H needs only k of the chunk (stored a step
+    // earlier); everything after it waits for the chunk's preparation.
     auto chain_chunk = [&](int par, int b3, int64_t c) {
         const uint16_t *sK = Kb(b3);
         const uint16_t *sQ = Qb(b3);
@@ -608,6 +638,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 for (int nt = 0; nt < NTW; ++nt) R[blk][nt] = mfma32(af, cat(hb[2 * p][nt], hb[2 * p + 1][nt]), R[blk][nt]);
             }
         }
+        wait_for(cPrep, static_cast<uint32_t>(4 * (c + 2)));   // preparation of chunk c published
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
             const f32x4 eg = *reinterpret_cast<const f32x4 *>(veg + 16 * blk + 4 * lq);
@@ -720,13 +751,22 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 }
             }
         }
+        publish(cChain);   // done with chunk c: its q/k buffer and its prepared buffers are free
     };
 
-    // The two roles run separate loops with the same barrier sequence: two
-    // barriers for the prologue, then one per chunk.  (s_barrier counts
-    // arriving waves; the roles are uniform per wave.)  q and k of chunk c sit
-    // in buffer c % 3: the chain reads chunk c, the preparation waves read
-    // chunk c+1 and store chunk c+2, loaded at the start of the same step.
+    // The roles hand chunks over through the two counters (no work-group
+    // barrier after the start).  Preparation step n (n >= 1) prepares chunk
+    // n into buffer n % 2 and stores q, k of chunk n+1 into buffer (n+1) % 3;
+    // it starts once the chain has finished chunk n-2 (the previous user of
+    // those buffers) and every preparation wave has finished step n-1 (which
+    // stored the q, k rows it reads).  The prologue stores q, k of chunks 0
+    // and 1 (cPrep = 4) and prepares chunk 0 (cPrep = 8), so chunk c is
+    // prepared once cPrep >= 4 (c + 2).
+    if (tid == 0) {
+        *cPrep = 0u;
+        *cChain = 0u;
+    }
+    __syncthreads();
     if (chain) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -736,12 +776,10 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 for (int r = 0; r < 4; ++r)
                     hs[kb][nt][r] = a.h0 ? a.h0[sbase + dk_of(kb, 4 * lq + r) * D + dv_of(nt, l16)] : 0.f;
         load_v(0);
-        __syncthreads();
-        __syncthreads();
+        wait_for(cPrep, 4u);   // q, k of chunk 0 stored
         int b3 = 0;
         for (int64_t c = 0; c < nch; ++c) {
             chain_chunk(static_cast<int>(c & 1), b3, c);
-            __syncthreads();
             b3 = b3 == 2 ? 0 : b3 + 1;
         }
         if (a.ht) {
@@ -754,8 +792,6 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                         a.ht[sbase + dk_of(kb, 4 * lq + r) * D + dv_of(nt, l16)] = hs[kb][nt][r];
         }
     } else {
-        // prologue: q, k of chunks 0 and 1 into buffers 0 and 1, gates of
-        // chunk 0, then chunk 0 prepared
         load_qk(0);
         store_qk(0);
         load_qk(1);   // zero when there is no chunk 1
@@ -763,23 +799,26 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         load_gates(0);
         gates(0);
         load_gates(1);
-        __syncthreads();
+        publish(cPrep);
+        wait_for(cPrep, 4u);
         prep_kq(0, 0);
         block_inv(0);
-        __syncthreads();
-        // chunk c+1 while the chain works on chunk c; past the last chunk the
-        // preparation runs on zero rows and its results are never read
-        int b3 = 0;
-        for (int64_t c = 0; c < nch; ++c) {
-            const int npar = static_cast<int>((c + 1) & 1);
-            const int b3n = b3 == 2 ? 0 : b3 + 1, b3nn = b3n == 2 ? 0 : b3n + 1;
-            load_qk(c + 2);
-            gates(npar);
-            load_gates(c + 2);
-            prep_kq(npar, b3n);
-            block_inv(npar);
-            store_qk(b3nn);
-            __syncthreads();
+        publish(cPrep);
+        // past the last chunk the preparation runs on zero rows and its
+        // results are never read
+        int b3 = 1;   // buffer of chunk n
+        for (int64_t n = 1; n <= nch; ++n) {
+            const int par = static_cast<int>(n & 1);
+            const int b3n = b3 == 2 ? 0 : b3 + 1;
+            wait_for(cChain, static_cast<uint32_t>(4 * (n - 1)));
+            wait_for(cPrep, static_cast<uint32_t>(4 * (n + 1)));
+            load_qk(n + 1);
+            gates(par);
+            load_gates(n + 1);
+            prep_kq(par, b3);
+            block_inv(par);
+            store_qk(b3n);
+            publish(cPrep);
             b3 = b3n;
         }
     }
