@@ -368,17 +368,23 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     // Cross-role hand-off through the LDS counters instead of work-group
     // barriers: a wave publishes a step after its own LDS accesses are
     // complete, and waits (bounded, so a wave always finishes) until a
-    // counter reaches a target.
+    // counter reaches a target.  The counters only grow, so a value read
+    // early (issued ahead of other work to hide the LDS latency) that already
+    // reaches the target ends the wait without another read.
     auto publish = [&](uint32_t *cnt) {
         lds_wait();
         if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
-    auto wait_for = [&](const uint32_t *cnt, uint32_t target) {
-        for (int it = 0; it < kSpinMax; ++it) {
-            const uint32_t seen = __builtin_amdgcn_readfirstlane(
-                __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-            if (seen >= target) break;
-            __builtin_amdgcn_s_sleep(1);
+    auto peek = [&](const uint32_t *cnt) {
+        return __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    auto wait_for = [&](const uint32_t *cnt, uint32_t target, uint32_t early) {
+        if (__builtin_amdgcn_readfirstlane(early) < target) {
+#pragma unroll 1
+            for (int it = 0; it < kSpinMax; ++it) {
+                __builtin_amdgcn_s_sleep(1);
+                if (__builtin_amdgcn_readfirstlane(peek(cnt)) >= target) break;
+            }
         }
         lds_wait();
     };
@@ -612,6 +618,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     // chain: one chunk.  K H needs only k of the chunk (stored a step
     // earlier); everything after it waits for the chunk's preparation.
     auto chain_chunk = [&](int par, int b3, int64_t c) {
+        const uint32_t early = peek(cPrep);
         const uint16_t *sK = Kb(b3);
         const uint16_t *sQ = Qb(b3);
         const uint16_t *sAo = Aob(par);
@@ -638,7 +645,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 for (int nt = 0; nt < NTW; ++nt) R[blk][nt] = mfma32(af, cat(hb[2 * p][nt], hb[2 * p + 1][nt]), R[blk][nt]);
             }
         }
-        wait_for(cPrep, static_cast<uint32_t>(4 * (c + 2)));   // preparation of chunk c published
+        wait_for(cPrep, static_cast<uint32_t>(4 * (c + 2)), early);   // preparation of chunk c published
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
             const f32x4 eg = *reinterpret_cast<const f32x4 *>(veg + 16 * blk + 4 * lq);
@@ -776,7 +783,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 for (int r = 0; r < 4; ++r)
                     hs[kb][nt][r] = a.h0 ? a.h0[sbase + dk_of(kb, 4 * lq + r) * D + dv_of(nt, l16)] : 0.f;
         load_v(0);
-        wait_for(cPrep, 4u);   // q, k of chunk 0 stored
+        wait_for(cPrep, 4u, peek(cPrep));   // q, k of chunk 0 stored
         int b3 = 0;
         for (int64_t c = 0; c < nch; ++c) {
             chain_chunk(static_cast<int>(c & 1), b3, c);
@@ -800,7 +807,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         gates(0);
         load_gates(1);
         publish(cPrep);
-        wait_for(cPrep, 4u);
+        wait_for(cPrep, 4u, peek(cPrep));
         prep_kq(0, 0);
         block_inv(0);
         publish(cPrep);
@@ -810,9 +817,10 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         for (int64_t n = 1; n <= nch; ++n) {
             const int par = static_cast<int>(n & 1);
             const int b3n = b3 == 2 ? 0 : b3 + 1;
-            wait_for(cChain, static_cast<uint32_t>(4 * (n - 1)));
-            wait_for(cPrep, static_cast<uint32_t>(4 * (n + 1)));
-            load_qk(n + 1);
+            const uint32_t early_c = peek(cChain), early_p = peek(cPrep);
+            load_qk(n + 1);   // registers only
+            wait_for(cChain, static_cast<uint32_t>(4 * (n - 1)), early_c);
+            wait_for(cPrep, static_cast<uint32_t>(4 * (n + 1)), early_p);
             gates(par);
             load_gates(n + 1);
             prep_kq(par, b3);
