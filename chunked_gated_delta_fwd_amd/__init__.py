@@ -25,8 +25,8 @@ STATUS = {0: "GDR_OK", -1: "GDR_EINVAL", -2: "GDR_ESHAPE", -3: "GDR_EDTYPE", -4:
           -5: "GDR_EALIAS", -6: "GDR_EDEVICE", -7: "GDR_ELAUNCH", -8: "GDR_ENOMEM"}
 
 # every symbol include/gdr.h declares
-EXPORTS = ("gdr_chunk_fwd", "gdr_plan", "gdr_prepare_chunks", "gdr_chunk_local_cumsum",
-           "gdr_last_error", "gdr_version", "gdr_selftest_mfma")
+EXPORTS = ("gdr_chunk_fwd", "gdr_plan", "gdr_prepare_chunks", "gdr_dispatch_order",
+           "gdr_chunk_local_cumsum", "gdr_last_error", "gdr_version", "gdr_selftest_mfma")
 
 
 class GdrError(RuntimeError):
@@ -69,6 +69,8 @@ def library(path: Optional[str] = None):
     lib.gdr_plan.restype = ctypes.c_int
     lib.gdr_prepare_chunks.argtypes = [TP] * 4 + [ctypes.c_void_p]
     lib.gdr_prepare_chunks.restype = ctypes.c_int
+    lib.gdr_dispatch_order.argtypes = [TP, ctypes.c_int32, TP, ctypes.c_void_p]
+    lib.gdr_dispatch_order.restype = ctypes.c_int
     lib.gdr_chunk_local_cumsum.argtypes = [TP] * 3 + [ctypes.c_void_p]
     lib.gdr_chunk_local_cumsum.restype = ctypes.c_int
     lib.gdr_last_error.argtypes = []
@@ -185,6 +187,19 @@ def prepare_chunks(cu_seqlens, nt_max: Optional[int] = None, with_map: bool = Tr
     ds = [_desc(x) for x in (cu_seqlens, offs, cmap, order)]
     _check(lib, lib.gdr_prepare_chunks(*[_ref(x) for x in ds], ctypes.c_void_p(_stream_handle(cu_seqlens))))
     return offs, cmap, order
+
+
+def dispatch_order(cu_seqlens, groups: int):
+    """The order [N] in which the forward pass starts the sequences, for a
+    schedule of ``groups`` machines (see ``gdr_dispatch_order``)."""
+    import torch
+    lib = library()
+    N = cu_seqlens.shape[0] - 1
+    order = torch.empty(max(N, 0), dtype=torch.int32, device=cu_seqlens.device)
+    ds = [_desc(x) for x in (cu_seqlens, order)]
+    _check(lib, lib.gdr_dispatch_order(_ref(ds[0]), ctypes.c_int32(groups), _ref(ds[1]),
+                                       ctypes.c_void_p(_stream_handle(cu_seqlens))))
+    return order
 
 
 def chunk_local_cumsum(g, cu_seqlens=None, out=None):

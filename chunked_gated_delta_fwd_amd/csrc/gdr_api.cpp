@@ -248,6 +248,31 @@ hipError_t workspace_pool(hipMemPool_t *out) {
     return hipSuccess;
 }
 
+// Machines of the dispatch-order model for a forward launch: work-groups
+// resident at once divided by the v-heads of a sequence (each XCD gets Hv/8
+// heads of every sequence, so Hv must split over the 8 XCDs), or 0 when the
+// packed order does not apply.  Occupancy is queried once per device and
+// kernel variant.
+int order_groups(const gdr::FwdArgs &a) {
+    static std::mutex mu;
+    static int cache[64][2][2][2];   // slots + 1; 0 unknown
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int &entry = cache[dev][a.d == 64 ? 0 : 1][a.in_bf16 ? 1 : 0][a.gate_bf16 ? 1 : 0];
+    int slots = 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (entry == 0) {
+            int s = 0;
+            entry = gdr::fwd_slots(a.d, a.in_bf16, a.gate_bf16, &s) == hipSuccess ? s + 1 : 1;
+        }
+        slots = entry - 1;
+    }
+    if (a.hv % 8 != 0 || slots <= 0 || slots % a.hv != 0) return 0;
+    const int groups = slots / a.hv;
+    return (groups >= 2 && groups <= 16 && a.n_seq > groups && a.n_seq <= 64) ? groups : 0;
+}
+
 int launch_error(hipError_t e, const char *what) {
     return fail(GDR_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
 }
@@ -302,7 +327,9 @@ int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
         if (e != hipSuccess) return fail(GDR_ENOMEM, "workspace of %lld bytes: %s",
                                          (long long)p.workspace_bytes, hipGetErrorString(e));
         int32_t *order = static_cast<int32_t *>(ws);
-        e = gdr::launch_prepare(a.cu, p.n_seq, nullptr, nullptr, 0, order, stream);
+        const int groups = order_groups(a);
+        e = groups ? gdr::launch_order(a.cu, p.n_seq, groups, order, stream)
+                   : gdr::launch_prepare(a.cu, p.n_seq, nullptr, nullptr, 0, order, stream);
         if (e != hipSuccess) {
             (void)hipFreeAsync(ws, stream);
             return launch_error(e, "chunk preparation kernel");
@@ -315,6 +342,25 @@ int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
         if (e == hipSuccess && fe != hipSuccess) return launch_error(fe, "workspace release");
     }
     if (e != hipSuccess) return launch_error(e, "forward kernel");
+    return ok();
+}
+
+int gdr_dispatch_order(const gdr_tensor *cu_seqlens, int32_t groups, const gdr_tensor *order,
+                       hipStream_t stream) {
+    int64_t ncu, nord;
+    int rc;
+    if ((rc = check_tensor(cu_seqlens, "cu_seqlens", 1, &ncu, 4))) return rc;
+    if ((rc = check_tensor(order, "order", 1, &nord, 4))) return rc;
+    if (cu_seqlens->dtype != GDR_I32 || order->dtype != GDR_I32) return fail(GDR_EDTYPE, "cu_seqlens and order must be i32");
+    const int64_t N = ncu - 1;
+    if (N < 1 || N > 64) return fail(GDR_ESHAPE, "dispatch order needs 1 <= N <= 64 sequences, got %lld", (long long)N);
+    if (nord != N) return fail(GDR_ESHAPE, "order must have N = %lld entries", (long long)N);
+    if (groups < 1 || groups > 16) return fail(GDR_EINVAL, "groups must be in [1, 16], got %d", groups);
+    if (overlap(span_of(cu_seqlens, ncu), span_of(order, nord))) return fail(GDR_EALIAS, "order overlaps cu_seqlens");
+    if ((rc = check_device())) return rc;
+    const hipError_t e = gdr::launch_order(static_cast<const int32_t *>(cu_seqlens->data), N, groups,
+                                           static_cast<int32_t *>(order->data), stream);
+    if (e != hipSuccess) return launch_error(e, "dispatch order kernel");
     return ok();
 }
 

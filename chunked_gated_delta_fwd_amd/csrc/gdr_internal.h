@@ -36,6 +36,13 @@ hipError_t launch_prepare(const int32_t *cu, int64_t n_seq, int32_t *chunk_offse
                           int32_t *chunk_map, int64_t nt_max, int32_t *order,
                           hipStream_t stream);
 
+// Dispatch order for few sequences (1 <= n_seq <= 64) on `groups` (<= 16)
+// machines of CUs; see the kernel for the model.
+hipError_t launch_order(const int32_t *cu, int64_t n_seq, int32_t groups, int32_t *order,
+                        hipStream_t stream);
+// Work-groups of the fused forward kernel resident on the device at once.
+hipError_t fwd_slots(int d, int in_bf16, int gate_bf16, int *slots);
+
 // chunk_map != NULL: varlen (grid nt_max); else n_rows fixed rows of seq_len tokens.
 hipError_t launch_cumsum(const void *g, int gate_bf16, const int32_t *cu,
                          const int32_t *chunk_map, int64_t nt_max, int64_t n_rows,

@@ -900,6 +900,140 @@ __global__ void __launch_bounds__(kPrepThreads) gdr_prepare_kernel(
 }
 
 // --------------------------------------------------------------------------
+// Dispatch order of the forward work-groups when there are few sequences
+// (one wave).  Model: `groups` identical machines, each a set of CUs that
+// runs all v-heads of one sequence at a time; sequence n keeps one busy for
+// w_n = ceil(L_n / 64) + 1 units; the hardware starts work-groups in grid
+// order, each on the machine that frees first (list scheduling).  Longest
+// first is the baseline.  Each lane tries one capacity with first-fit
+// decreasing bin packing; the smallest capacity that fits gives an
+// assignment, which is turned into a dispatch order by replaying the list
+// schedule: the machine that frees first takes the next sequence of its own
+// bin (the largest one left if its bin is used up).  That order is kept only
+// if its replayed makespan beats longest first.  Length-0 sequences go last.
+// --------------------------------------------------------------------------
+constexpr int kOrderMax = 64;    // sequences
+constexpr int kGroupsMax = 16;   // machines (one 16-lane row)
+
+// Minimum over each 16-lane row, ending in the row's last lane: four DPP
+// row shifts (lanes shifted in from outside the row keep `~0u`).
+__device__ __forceinline__ uint32_t row_min(uint32_t x) {
+    x = min(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, x, 0x111, 0xF, 0xF, false)));
+    x = min(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, x, 0x112, 0xF, 0xF, false)));
+    x = min(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, x, 0x114, 0xF, 0xF, false)));
+    x = min(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, x, 0x118, 0xF, 0xF, false)));
+    return x;
+}
+
+// Machine b < m lives in lane b: `fin` its finishing time (lanes >= m hold
+// kIdle).  first_free: the machine that frees first, ties to the lowest index.
+constexpr uint32_t kIdle = 0x0FFFFFFFu;
+__device__ __forceinline__ int first_free(uint32_t fin, int lane) {
+    const uint32_t key = (fin << 4) | static_cast<uint32_t>(lane & 15);
+    return static_cast<int>(__builtin_amdgcn_readlane(row_min(key), 15) & 15u);
+}
+__device__ __forceinline__ uint32_t makespan_of(uint32_t fin, int lane, int m) {
+    // maximum over lanes < m as the minimum of the complements
+    const uint32_t c = (lane & 15) < m && lane < 16 ? ~fin : ~0u;
+    return ~static_cast<uint32_t>(__builtin_amdgcn_readlane(row_min(c), 15));
+}
+
+__global__ void __launch_bounds__(64) gdr_order_kernel(const int32_t *cu, int32_t n_seq, int32_t groups,
+                                                       int32_t *order) {
+    __shared__ int32_t s_w[kOrderMax], s_idx[kOrderMax], s_bin[kOrderMax];
+    const int lane = threadIdx.x;
+    const int n = n_seq;
+    const int m = groups;
+    int32_t w = 0;
+    if (lane < n) {
+        const int32_t len = cu[lane + 1] - cu[lane];
+        w = len > 0 ? (len + C - 1) / C + 1 : 0;
+    }
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+        const int32_t wj = static_cast<int32_t>(__builtin_amdgcn_readlane(w, j));
+        rank += (wj > w) || (wj == w && j < lane);
+    }
+    if (lane < n) {
+        s_w[rank] = w;
+        s_idx[rank] = lane;
+    }
+    __syncthreads();
+    // from here lane i holds item i of the longest-first list
+    const int32_t wi = lane < n ? s_w[lane] : 0;
+    const int k = __popcll(__ballot(lane < n && wi > 0));   // non-empty sequences come first
+    auto weight = [&](int i) { return static_cast<uint32_t>(__builtin_amdgcn_readlane(wi, i)); };
+    const uint32_t idle0 = lane < m ? 0u : kIdle;
+
+    // longest first, list-scheduled
+    uint32_t fin = idle0;
+    for (int i = 0; i < k; ++i) {
+        const int b = first_free(fin, lane);
+        if (lane == b) fin += weight(i);
+    }
+    const uint32_t mk_lpt = makespan_of(fin, lane, m);
+
+    uint32_t total = 0;
+    for (int i = 0; i < k; ++i) total += weight(i);
+    uint32_t lo = (total + m - 1) / m;
+    if (k > 0 && weight(0) > lo) lo = weight(0);
+    const uint32_t hi = mk_lpt - 1;   // only a smaller makespan helps
+
+    int src = lane;   // output position `lane` takes item src of the longest-first list
+    if (k > m && hi >= lo) {
+        // first-fit decreasing; each 16-lane row tries one capacity (lane = bin),
+        // four capacities per pass, smallest first, until one fits
+        const uint32_t span = hi - lo + 1;
+        const uint32_t step = (span + 63) / 64;
+        const int row = lane >> 4, bin = lane & 15;
+        uint32_t best = 0;
+        for (uint32_t c0 = 0; c0 * step < span && best == 0; c0 += 4) {
+            const uint32_t cap = lo + (c0 + row) * step;
+            uint32_t load = bin < m ? 0u : kIdle;
+            bool ok = cap <= hi;
+            for (int i = 0; i < k; ++i) {
+                const uint32_t x = weight(i);
+                const uint64_t fits = __ballot(load + x <= cap);
+                const uint32_t mine = static_cast<uint32_t>(fits >> (16 * row)) & 0xFFFFu;
+                ok = ok && mine != 0;
+                if (mine && bin == __ffs(mine) - 1) load += x;
+            }
+            const uint64_t good = __ballot(ok && bin == 0);
+            if (good) best = lo + (c0 + static_cast<uint32_t>(__ffsll(static_cast<long long>(good)) - 1) / 16) * step;
+        }
+        if (best) {
+            // the assignment at that capacity, in row 0: item i -> s_bin[i]
+            uint32_t load = bin < m ? 0u : kIdle;
+            for (int i = 0; i < k; ++i) {
+                const uint32_t x = weight(i);
+                const uint32_t mine = static_cast<uint32_t>(__ballot(load + x <= best)) & 0xFFFFu;
+                const int where = __ffs(mine) - 1;
+                if (lane == where) load += x;
+                if (lane == 0) s_bin[i] = where;
+            }
+            __syncthreads();
+            const int mybin = lane < k ? s_bin[lane] : -1;
+            // replay the list schedule: the machine that frees first takes
+            // the next item of its bin, else the largest item left
+            bool left = lane < k;
+            int out = lane;
+            uint32_t mfin = idle0;
+            for (int e = 0; e < k; ++e) {
+                const int bm = first_free(mfin, lane);
+                const uint64_t own = __ballot(left && mybin == bm);
+                const uint64_t any = __ballot(left);
+                const int pick = __ffsll(static_cast<long long>(own ? own : any)) - 1;
+                if (lane == pick) left = false;
+                if (lane == bm) mfin += weight(pick);
+                if (lane == e) out = pick;
+            }
+            if (makespan_of(mfin, lane, m) < mk_lpt) src = out;
+        }
+    }
+    if (lane < n) order[lane] = s_idx[src];
+}
+
+// --------------------------------------------------------------------------
 // Chunk-local prefix sum of the log-gate, one work-group (4 waves) per chunk
 // --------------------------------------------------------------------------
 template <bool GATE_BF16>
@@ -989,6 +1123,35 @@ hipError_t launch_prepare(const int32_t *cu, int64_t n_seq, int32_t *chunk_offse
     hipLaunchKernelGGL(gdr_prepare_kernel, dim3(1), dim3(kPrepThreads), 0, stream, cu, n_seq,
                        chunk_offsets, chunk_map, nt_max, order);
     return hipGetLastError();
+}
+
+hipError_t launch_order(const int32_t *cu, int64_t n_seq, int32_t groups, int32_t *order, hipStream_t stream) {
+    if (n_seq < 1 || n_seq > kOrderMax || groups < 1 || groups > kGroupsMax) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gdr_order_kernel, dim3(1), dim3(64), 0, stream, cu, static_cast<int32_t>(n_seq), groups, order);
+    return hipGetLastError();
+}
+
+hipError_t fwd_slots(int d, int in_bf16, int gate_bf16, int *slots) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const void *kern;
+    if (d == 64)
+        kern = in_bf16 ? (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, true>)
+                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, false>))
+                       : (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<64, false, true>)
+                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<64, false, false>));
+    else
+        kern = in_bf16 ? (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, true>)
+                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, false>))
+                       : (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<128, false, true>)
+                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<128, false, false>));
+    const int lds = fwd_lds_bytes(d);
+    if ((e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFwdThreads, lds)) != hipSuccess) return e;
+    *slots = cus * per_cu;
+    return hipSuccess;
 }
 
 hipError_t launch_cumsum(const void *g, int gate_bf16, const int32_t *cu, const int32_t *chunk_map,

@@ -161,6 +161,34 @@ int gdr_prepare_chunks(const gdr_tensor *cu_seqlens, const gdr_tensor *chunk_off
                        hipStream_t stream);
 
 /*
+ * gdr_dispatch_order - the order in which gdr_chunk_fwd starts the sequences
+ * of a varlen call when there are few of them, derived on the device from the
+ * content of cu_seqlens on every call (the integration report, item 1).
+ *
+ *   cu_seqlens  [N+1] int32 (device), 1 <= N <= 64
+ *   groups      machines of the schedule model, 1..16
+ *   order       [N] int32 out (device): a permutation of 0..N-1
+ *
+ * Model: `groups` identical machines (each the CUs that run all v-heads of
+ * one sequence at once); sequence n keeps one busy for ceil(L_n / 64) + 1
+ * units; work-groups start in grid order on the machine that frees first.
+ * The result is the longest-first order (ties by index, length-0 sequences
+ * last) unless an order built from a first-fit-decreasing bin packing at
+ * the smallest capacity that fits (capacities tried: up to 64 evenly spaced
+ * values below the longest-first makespan) has a smaller makespan in that
+ * model.  gdr_chunk_fwd uses it with groups = (work-groups resident on the
+ * device) / Hv when Hv is a multiple of 8, that ratio is 2..16 and smaller
+ * than N, and N <= 64; otherwise it starts sequences longest first.
+ * Work-list only: results never depend on it.
+ *
+ * Errors: GDR_ESHAPE (N outside 1..64, order not [N]), GDR_EINVAL (groups),
+ * GDR_EDTYPE, GDR_EALIAS (order overlaps cu_seqlens), GDR_EDEVICE,
+ * GDR_ELAUNCH.  Enqueued on `stream`; no workspace.
+ */
+int gdr_dispatch_order(const gdr_tensor *cu_seqlens, int32_t groups, const gdr_tensor *order,
+                       hipStream_t stream);
+
+/*
  * gdr_chunk_local_cumsum - chunk-local inclusive prefix sum of the log-gate:
  * G[t, h] = sum of g[s, h] for s from the start of t's 64-token chunk to t.
  * Chunks restart at every sequence start.  Computed in fp32.

@@ -168,3 +168,26 @@ def test_chunk_fwd_without_gpu_reports_device(lib):
                              ("q", "k", "v", "g", "beta", "cu_seqlens", "h0", "o", "ht")],
                            ctypes.c_float(1.0), None)
     assert rc == -6, (rc, lib.gdr_last_error())
+
+
+@pytest.mark.parametrize("n_seq,groups,order_len,status,text", [
+    (65, 8, 65, -2, "1 <= N <= 64"),
+    (0, 8, 0, -2, "1 <= N <= 64"),
+    (10, 8, 9, -2, "order must have N"),
+    (10, 0, 10, -1, "groups must be in [1, 16]"),
+    (10, 17, 10, -1, "groups must be in [1, 16]"),
+])
+def test_dispatch_order_rejections(lib, n_seq, groups, order_len, status, text):
+    A = Alloc()
+    cu = A(GDR_I32, [n_seq + 1])
+    order = A(GDR_I32, [order_len])
+    rc = lib.gdr_dispatch_order(cu.ref, ctypes.c_int32(groups), order.ref, None)
+    assert rc == status, (rc, lib.gdr_last_error())
+    assert text in lib.gdr_last_error().decode()
+
+
+def test_dispatch_order_rejects_alias(lib):
+    A = Alloc()
+    cu = A(GDR_I32, [11])
+    order = describe(cu.t.data + 4, GDR_I32, [10])
+    assert lib.gdr_dispatch_order(cu.ref, ctypes.c_int32(4), order.ref, None) == -5
