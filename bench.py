@@ -171,7 +171,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": achieved_tflops / PEAK_BF16_TFLOPS,
             "traffic": traffic,
-            "kernel": "gdr_fwd_kernel<128,bf16,bf16> (+ gdr_prepare_kernel in the same call)",
+            "kernel": "gdr_fwd_kernel<128,bf16,bf16> (+ gdr_order_kernel in the same call)",
             "flops_per_launch": f_chunk,
             "launch_ms": launch_ms,
         },
