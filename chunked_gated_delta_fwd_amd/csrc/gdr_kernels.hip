@@ -155,12 +155,22 @@ __device__ __forceinline__ uint16_t elem8(const uint4 &v, int e) {
     return static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xFFFFu));
 }
 
-__device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+// x plus the value DPP control CTRL moves in (0 where no lane is moved in,
+// or outside the rows ROW_MASK selects)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+// Inclusive prefix sum over the 64 lanes of a wave: scans within each
+// 16-lane row (row shifts by 1, 2, 4, 8), then carries row totals with the
+// row broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3).
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+    x = dpp_add<0x111, 0xF>(x);
+    x = dpp_add<0x112, 0xF>(x);
+    x = dpp_add<0x114, 0xF>(x);
+    x = dpp_add<0x118, 0xF>(x);
+    x = dpp_add<0x142, 0xA>(x);
+    x = dpp_add<0x143, 0xC>(x);
     return x;
 }
 
@@ -485,8 +495,8 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     float *const sG2 = sGw0 + (chain ? 0 : role) * 2 * C;   // this wave's G*log2(e)
     float *const sBw = sG2 + C;                              // and beta
     auto gates = [&](int par) {
-        const float G2 = wave_inclusive_scan(pg, lane) * kLog2e;
-        const float GL2 = __shfl(G2, 63, 64);   // padding has g = 0: equals G at the last token
+        const float G2 = wave_inclusive_scan(pg) * kLog2e;
+        const float GL2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G2), 63));   // padding has g = 0: G at the last token
         sG2[lane] = G2;
         sBw[lane] = pb;
         if (role == 0) {
@@ -1065,7 +1075,7 @@ __global__ void __launch_bounds__(256) gdr_cumsum_kernel(const void *g, const in
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int hh = wave; hh < heads; hh += 4) {
         const float x = lane < L ? load_scalar<GATE_BF16>(g, (t0 + lane) * heads + hh) : 0.f;
-        const float s = wave_inclusive_scan(x, lane);
+        const float s = wave_inclusive_scan(x);
         if (lane < L) G[(t0 + lane) * heads + hh] = s;
     }
 }
