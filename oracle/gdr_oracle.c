@@ -32,10 +32,18 @@
  * report) reads nothing and writes nothing: its rows of ht keep whatever the
  * caller put there.  v-head h reads q/k head h / (Hv / Hk).
  *
+ * Chunk-boundary states (optional).  Chunk c of sequence n holds its tokens
+ * cu[n] + 64c .. min(cu[n] + 64(c+1), cu[n+1]) - 1; its state is H after the
+ * last of them, stored at row off[n] + c, where off[n] = sum over m < n of
+ * ceil(L_m / 64) (the prefix caching of the pages' `state_checkpoints`,
+ * "feat(cake_kda): add paired recurrent training for SM100a and SM103a", the
+ * follow-up's kept prefill surface).  The last chunk's state is ht.
+ *
  * Layouts (all row-major, fp64):
  *   q, k  [T, Hk, dk]      v, o  [T, Hv, dv]      g, beta  [T, Hv]
  *   cu    [n_seq + 1]      h0, ht [n_seq, Hv, dk, dv]   (h0 NULL = zero state,
  *                                                          ht NULL = not written)
+ *   hck   [NT, Hv, dk, dv] with NT = off[n_seq]     (NULL = not written)
  */
 #include <math.h>
 #include <pthread.h>
@@ -47,7 +55,8 @@
 typedef struct {
     const double *q, *k, *v, *g, *beta, *h0;
     const int64_t *cu;
-    double *o, *ht;
+    double *o, *ht, *hck;
+    const int64_t *off;  /* chunk offsets per sequence (hck only) */
     int64_t n_seq, T, Hk, Hv, dk, dv;
     double scale;
     int64_t *items;      /* work items n * Hv + h, longest segment first */
@@ -90,6 +99,11 @@ static void run_item(const job_t *J, int64_t n, int64_t h, double *H, double *p)
         for (int64_t i = 0; i < dk; ++i)
             for (int64_t j = 0; j < dv; ++j) ot[j] += H[i * dv + j] * qt[i];
         for (int64_t j = 0; j < dv; ++j) ot[j] *= J->scale;
+
+        if (J->hck && ((t - bos + 1) % 64 == 0 || t == eos - 1)) {
+            const int64_t c = (t - bos) / 64;
+            memcpy(J->hck + (((J->off[n] + c) * Hv + h) * dk) * dv, H, sizeof(double) * dk * dv);
+        }
     }
     if (J->ht) memcpy(J->ht + ((n * Hv + h) * dk) * dv, H, sizeof(double) * dk * dv);
 }
@@ -137,10 +151,25 @@ int gdr_oracle_threads(int requested, int64_t n_items)
  * (non-positive head sizes, Hv not a multiple of Hk, cu not non-decreasing
  * within [0, T]), -2 when memory or threads cannot be obtained.
  */
+int gdr_oracle_fwd_chunks(const double *q, const double *k, const double *v, const double *g,
+                          const double *beta, const int64_t *cu, int64_t n_seq, int64_t T,
+                          int64_t Hk, int64_t Hv, int64_t dk, int64_t dv, const double *h0,
+                          double *o, double *ht, double *hck, double scale, int n_threads);
+
 int gdr_oracle_fwd(const double *q, const double *k, const double *v, const double *g,
                    const double *beta, const int64_t *cu, int64_t n_seq, int64_t T,
                    int64_t Hk, int64_t Hv, int64_t dk, int64_t dv, const double *h0,
                    double *o, double *ht, double scale, int n_threads)
+{
+    return gdr_oracle_fwd_chunks(q, k, v, g, beta, cu, n_seq, T, Hk, Hv, dk, dv, h0, o, ht,
+                                 NULL, scale, n_threads);
+}
+
+/* The same, also writing the chunk-boundary states into hck (may be NULL). */
+int gdr_oracle_fwd_chunks(const double *q, const double *k, const double *v, const double *g,
+                          const double *beta, const int64_t *cu, int64_t n_seq, int64_t T,
+                          int64_t Hk, int64_t Hv, int64_t dk, int64_t dv, const double *h0,
+                          double *o, double *ht, double *hck, double scale, int n_threads)
 {
     if (n_seq < 0 || T < 0 || Hk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || Hv % Hk != 0)
         return -1;
@@ -151,13 +180,21 @@ int gdr_oracle_fwd(const double *q, const double *k, const double *v, const doub
 
     job_t J;
     J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.h0 = h0;
-    J.cu = cu; J.o = o; J.ht = ht;
+    J.cu = cu; J.o = o; J.ht = ht; J.hck = hck;
+    int64_t *off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_seq + 1));
+    if (!off) return -2;
+    off[0] = 0;
+    for (int64_t n = 0; n < n_seq; ++n) off[n + 1] = off[n] + (cu[n + 1] - cu[n] + 63) / 64;
+    J.off = off;
     J.n_seq = n_seq; J.T = T; J.Hk = Hk; J.Hv = Hv; J.dk = dk; J.dv = dv;
     J.scale = scale;
     J.n_items = n_seq * Hv;
     J.next = 0;
     J.items = (int64_t *)malloc(sizeof(int64_t) * (size_t)J.n_items);
-    if (!J.items) return -2;
+    if (!J.items) {
+        free(off);
+        return -2;
+    }
     for (int64_t i = 0; i < J.n_items; ++i) J.items[i] = i;
     g_sort_job = &J;
     qsort(J.items, (size_t)J.n_items, sizeof(int64_t), by_length_desc);
@@ -184,5 +221,6 @@ int gdr_oracle_fwd(const double *q, const double *k, const double *v, const doub
     }
     pthread_mutex_destroy(&J.lock);
     free(J.items);
+    free(off);
     return rc;
 }

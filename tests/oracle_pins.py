@@ -351,6 +351,30 @@ def pin_split_resume(fwd):
         assert np.array_equal(h2, ht), "split at %d: ht" % m
 
 
+def pin_chunk_states(fwd):
+    """The state after every 64-token chunk of every segment (chunk c of
+    segment n at row sum_{m<n} ceil(L_m / 64) + c) equals, bit for bit, the
+    final state of a run over that segment's prefix through the chunk; the last
+    one is ht; length-0 segments own no rows."""
+    lens = [130, 0, 64, 5, 128, 0, 65]
+    c = small_case(31, lens, Hk=1, Hv=2, dk=4, dv=3)
+    o, ht, hck = _run(fwd, c, scale=0.5, chunk_states=True)
+    assert hck.shape == (3 + 1 + 1 + 2 + 2, 2, 4, 3), hck.shape
+    row = 0
+    for n, L in enumerate(lens):
+        bos = int(c["cu"][n])
+        for ci in range((L + 63) // 64):
+            e = bos + min(64 * (ci + 1), L)
+            pre = {key: c[key][:, bos:e] for key in ("q", "k", "v", "g", "beta")}
+            _, hp = fwd(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], None,
+                        c["h0"][n:n + 1], scale=0.5)
+            assert np.array_equal(hck[row], hp[0]), "segment %d chunk %d" % (n, ci)
+            row += 1
+        if L:
+            assert np.array_equal(hck[row - 1], ht[n]), "segment %d: last chunk vs ht" % n
+    assert row == hck.shape[0]
+
+
 def pin_linearity(fwd):
     """For fixed q, k, g, beta the outputs are jointly linear in (v, h0):
     scaling both by 4 scales o and ht by 4 exactly (a power of two)."""
@@ -432,5 +456,5 @@ def pin_page_magnitudes(fwd, T=512):
 ALL_PINS = [pin_exact_rational, pin_literal_matrix_form, pin_chunked_form,
             pin_identity_when_beta_and_g_zero, pin_pure_decay, pin_single_token,
             pin_orthonormal_overwrite, pin_scalar_iir, pin_segment_independence,
-            pin_ghost_segments, pin_split_resume, pin_linearity, pin_causality,
+            pin_ghost_segments, pin_split_resume, pin_chunk_states, pin_linearity, pin_causality,
             pin_contraction_bound, pin_page_magnitudes]

@@ -31,6 +31,8 @@ MUTANTS = [
      " if (0)"),
     ("decay_after_update", "for (int64_t i = 0; i < dk * dv; ++i) H[i] *= a;\n",
      "H[0] *= 1.0;\n"),
+    ("chunk_state_early", "(t - bos + 1) % 64 == 0", "(t - bos) % 64 == 0"),
+    ("chunk_state_row", "((J->off[n] + c) * Hv + h)", "((J->off[n] + c) * Hv + (Hv - 1 - h))"),
 ]
 
 
