@@ -25,7 +25,7 @@ STATUS = {0: "GDR_OK", -1: "GDR_EINVAL", -2: "GDR_ESHAPE", -3: "GDR_EDTYPE", -4:
           -5: "GDR_EALIAS", -6: "GDR_EDEVICE", -7: "GDR_ELAUNCH", -8: "GDR_ENOMEM"}
 
 # every symbol include/gdr.h declares
-EXPORTS = ("gdr_chunk_fwd", "gdr_plan", "gdr_prepare_chunks", "gdr_dispatch_order",
+EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_checkpoints", "gdr_plan", "gdr_prepare_chunks", "gdr_dispatch_order",
            "gdr_chunk_local_cumsum", "gdr_last_error", "gdr_version", "gdr_selftest_mfma")
 
 
@@ -65,6 +65,8 @@ def library(path: Optional[str] = None):
     TP = ctypes.POINTER(GdrTensor)
     lib.gdr_chunk_fwd.argtypes = [TP] * 9 + [ctypes.c_float, ctypes.c_void_p]
     lib.gdr_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_checkpoints.argtypes = [TP] * 10 + [ctypes.c_float, ctypes.c_void_p]
+    lib.gdr_chunk_fwd_checkpoints.restype = ctypes.c_int
     lib.gdr_plan.argtypes = [TP] * 9 + [ctypes.c_float, ctypes.POINTER(GdrLaunchPlan)]
     lib.gdr_plan.restype = ctypes.c_int
     lib.gdr_prepare_chunks.argtypes = [TP] * 4 + [ctypes.c_void_p]
@@ -159,6 +161,32 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Optional[float]
     _check(lib, lib.gdr_chunk_fwd(*[_ref(x) for x in ds], ctypes.c_float(scale),
                                   ctypes.c_void_p(_stream_handle(q))))
     return o, ht
+
+
+def chunk_fwd_checkpoints(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Optional[float] = None,
+                          o=None, ht=None, h_chunks=None):
+    """``chunk_fwd`` that also returns the state after every 64-token chunk:
+    ``(o, ht, h_chunks)`` with h_chunks fp32 ``[R, Hv, dk, dv]``, R = ceil(T/64) + N
+    with ``cu_seqlens`` (rows past the true chunk count are not written) or
+    B * ceil(T/64); chunk c of sequence n at row sum(ceil(L_m/64), m < n) + c."""
+    import torch
+    lib = library()
+    B, T, Hk, d = q.shape
+    Hv = v.shape[2]
+    N = (cu_seqlens.shape[0] - 1) if cu_seqlens is not None else B
+    if scale is None:
+        scale = float(d) ** -0.5
+    rows = ((T + 63) // 64 + N) if cu_seqlens is not None else B * ((T + 63) // 64)
+    if o is None:
+        o = torch.empty((B, T, Hv, v.shape[3]), dtype=q.dtype, device=q.device)
+    if ht is None:
+        ht = torch.zeros((N, Hv, d, v.shape[3]), dtype=torch.float32, device=q.device)
+    if h_chunks is None:
+        h_chunks = torch.zeros((rows, Hv, d, v.shape[3]), dtype=torch.float32, device=q.device)
+    ds = [_desc(x) for x in (q, k, v, g, beta, cu_seqlens, h0, o, ht, h_chunks)]
+    _check(lib, lib.gdr_chunk_fwd_checkpoints(*[_ref(x) for x in ds], ctypes.c_float(scale),
+                                              ctypes.c_void_p(_stream_handle(q))))
+    return o, ht, h_chunks
 
 
 def plan(q, k, v, g, beta, cu_seqlens=None, h0=None, o=None, ht=None, scale: float = 1.0) -> dict:

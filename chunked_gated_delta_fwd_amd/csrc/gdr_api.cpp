@@ -277,24 +277,34 @@ int launch_error(hipError_t e, const char *what) {
     return fail(GDR_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
 }
 
-}  // namespace
-
-extern "C" {
-
-int gdr_plan(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
-             const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
-             const gdr_tensor *o, const gdr_tensor *ht, float scale, gdr_launch_plan *plan) {
-    if (!plan) return fail(GDR_EINVAL, "plan is NULL");
-    const int rc = plan_fwd(q, k, v, g, beta, cu_seqlens, h0, o, ht, scale, plan);
-    return rc ? rc : ok();
-}
-
-int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
-                  const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
-                  const gdr_tensor *o, const gdr_tensor *ht, float scale, hipStream_t stream) {
+// The forward launch shared by gdr_chunk_fwd and gdr_chunk_fwd_checkpoints
+// (hck: chunk-boundary states, or NULL).
+int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
+            const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
+            const gdr_tensor *o, const gdr_tensor *ht, const gdr_tensor *hck, float scale,
+            hipStream_t stream) {
     gdr_launch_plan p;
     int rc = plan_fwd(q, k, v, g, beta, cu_seqlens, h0, o, ht, scale, &p);
     if (rc) return rc;
+    int64_t rows = 0;
+    if (hck) {
+        int64_t nck;
+        if ((rc = check_tensor(hck, "h_chunks", 4, &nck, 4))) return rc;
+        if (hck->dtype != GDR_F32) return fail(GDR_EDTYPE, "h_chunks: dtype must be f32");
+        const int64_t T = q->shape[1];
+        rows = cu_seqlens ? p.nt_max : q->shape[0] * ((T + gdr::kChunk - 1) / gdr::kChunk);
+        if (!shape_is(hck, {rows, p.hv, p.d, p.d}))
+            return fail(GDR_ESHAPE, "h_chunks: shape %s must be [%lld, Hv, dk, dv] = [%lld, %d, %d, %d]",
+                        shape_str(hck).c_str(), (long long)rows, (long long)rows, p.hv, p.d, p.d);
+        const Span sck = span_of(hck, nck);
+        const gdr_tensor *others[] = {q, k, v, g, beta, cu_seqlens, h0, o, ht};
+        for (const gdr_tensor *t : others) {
+            if (!t) continue;
+            int64_t nt = 1;
+            for (int i = 0; i < t->ndim; ++i) nt *= t->shape[i];
+            if (overlap(sck, span_of(t, nt))) return fail(GDR_EALIAS, "h_chunks overlaps another tensor");
+        }
+    }
     if ((rc = check_device())) return rc;
     if (p.n_seq == 0 || p.total_tokens == 0) return ok();
 
@@ -318,23 +328,30 @@ int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
     a.in_bf16 = p.in_dtype == GDR_BF16;
     a.gate_bf16 = p.gate_dtype == GDR_BF16;
     a.scale = scale;
+    a.hck = hck ? static_cast<float *>(hck->data) : nullptr;
+    a.ck_offs = nullptr;
+    a.ck_rows = rows;
 
     void *ws = nullptr;
     if (cu_seqlens) {
+        // order [N], then (checkpoints only) chunk offsets [N + 1]
+        const size_t bytes = static_cast<size_t>(p.workspace_bytes) + (hck ? 4 * static_cast<size_t>(p.n_seq + 1) : 0);
         hipMemPool_t pool = nullptr;
         hipError_t e = workspace_pool(&pool);
-        if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, static_cast<size_t>(p.workspace_bytes), pool, stream);
-        if (e != hipSuccess) return fail(GDR_ENOMEM, "workspace of %lld bytes: %s",
-                                         (long long)p.workspace_bytes, hipGetErrorString(e));
+        if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, bytes, pool, stream);
+        if (e != hipSuccess) return fail(GDR_ENOMEM, "workspace of %lld bytes: %s", (long long)bytes,
+                                         hipGetErrorString(e));
         int32_t *order = static_cast<int32_t *>(ws);
-        const int groups = order_groups(a);
+        int32_t *offs = hck ? order + p.n_seq : nullptr;
+        const int groups = hck ? 0 : order_groups(a);
         e = groups ? gdr::launch_order(a.cu, p.n_seq, groups, order, stream)
-                   : gdr::launch_prepare(a.cu, p.n_seq, nullptr, nullptr, 0, order, stream);
+                   : gdr::launch_prepare(a.cu, p.n_seq, offs, nullptr, 0, order, stream);
         if (e != hipSuccess) {
             (void)hipFreeAsync(ws, stream);
             return launch_error(e, "chunk preparation kernel");
         }
         a.order = order;
+        a.ck_offs = offs;
     }
     hipError_t e = gdr::launch_fwd(a, stream);
     if (ws) {
@@ -343,6 +360,32 @@ int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
     }
     if (e != hipSuccess) return launch_error(e, "forward kernel");
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_plan(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
+             const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
+             const gdr_tensor *o, const gdr_tensor *ht, float scale, gdr_launch_plan *plan) {
+    if (!plan) return fail(GDR_EINVAL, "plan is NULL");
+    const int rc = plan_fwd(q, k, v, g, beta, cu_seqlens, h0, o, ht, scale, plan);
+    return rc ? rc : ok();
+}
+
+int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
+                  const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
+                  const gdr_tensor *o, const gdr_tensor *ht, float scale, hipStream_t stream) {
+    return run_fwd(q, k, v, g, beta, cu_seqlens, h0, o, ht, nullptr, scale, stream);
+}
+
+int gdr_chunk_fwd_checkpoints(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
+                              const gdr_tensor *g, const gdr_tensor *beta, const gdr_tensor *cu_seqlens,
+                              const gdr_tensor *h0, const gdr_tensor *o, const gdr_tensor *ht,
+                              const gdr_tensor *h_chunks, float scale, hipStream_t stream) {
+    if (!h_chunks) return fail(GDR_EINVAL, "h_chunks: descriptor is NULL");
+    return run_fwd(q, k, v, g, beta, cu_seqlens, h0, o, ht, h_chunks, scale, stream);
 }
 
 int gdr_dispatch_order(const gdr_tensor *cu_seqlens, int32_t groups, const gdr_tensor *order,

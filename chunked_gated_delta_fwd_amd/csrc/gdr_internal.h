@@ -22,6 +22,11 @@ struct FwdArgs {
     int32_t in_bf16;        // q/k/v/o dtype: 1 bf16, 0 f32
     int32_t gate_bf16;      // g/beta dtype
     float scale;
+    // chunk-boundary states (NULL: not written): row ck_offs[n] + c (or
+    // n * ceil(seq_len / 64) + c for fixed-length rows) of [ck_rows, Hv, d, d]
+    float *hck;
+    const int32_t *ck_offs;
+    int64_t ck_rows;
 };
 
 // Dynamic LDS bytes and threads per work-group of the fused forward kernel

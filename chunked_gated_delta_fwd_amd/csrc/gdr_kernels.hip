@@ -292,7 +292,7 @@ __device__ __forceinline__ float buf_load_scalar(__amdgpu_buffer_rsrc_t r, uint3
     else return __builtin_bit_cast(float, buf_load<4>(r, off));
 }
 
-template <int D, bool IN_BF16, bool GATE_BF16>
+template <int D, bool IN_BF16, bool GATE_BF16, bool CKPT>
 __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     using Ly = FwdLds<D>;
     constexpr int PK = Ly::PK, PP = Ly::PP, PAT = Ly::PAT, PDI = Ly::PDI;
@@ -374,6 +374,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     const int lq = lane >> 4;
     const int colw = role * DW;         // the chain wave's 16*NTW state columns
     const int64_t nch = (eos - bos + C - 1) / C;
+    const int64_t ck_base = !CKPT ? 0 : a.ck_offs ? static_cast<int64_t>(a.ck_offs[n]) : n * ((a.seq_len + C - 1) / C);
 
     // Cross-role hand-off through the LDS counters instead of work-group
     // barriers: a wave publishes a step after its own LDS accesses are
@@ -768,6 +769,26 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 }
             }
         }
+        if constexpr (CKPT) {
+            // the state after this chunk, plain [dk][dv] fp32 at its chunk row
+            const int64_t row = ck_base + c;
+            if (row < a.ck_rows) {
+                // lane part of the offset in a register, the rest (tile, row
+                // within the tile) as the scalar offset of each store
+                const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(a.hck + (row * a.hv + h) * D * D, D * D * 4);
+                const uint32_t lane_off = (dk_of(0, 4 * lq) * D + dv_of(0, l16)) * 4;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const uint32_t cst = ((dk_of(kb, r) - dk_of(0, 0)) * D + 4 * nt) * 4;
+                            const float val = hs[kb][nt][r];   // (bit-casting the vector element directly stored element 0)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), rd, lane_off, cst, 0);
+                        }
+            }
+        }
         publish(cChain);   // done with chunk c: its q/k buffer and its prepared buffers are free
     };
 
@@ -1103,7 +1124,7 @@ __global__ void __launch_bounds__(64) gdr_selftest_kernel(const uint16_t *a, con
 
 template <int D, bool IN_BF16, bool GATE_BF16>
 hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
-    auto kern = gdr_fwd_kernel<D, IN_BF16, GATE_BF16>;
+    auto kern = a.hck ? gdr_fwd_kernel<D, IN_BF16, GATE_BF16, true> : gdr_fwd_kernel<D, IN_BF16, GATE_BF16, false>;
     const int lds = FwdLds<D>::bytes;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1148,15 +1169,15 @@ hipError_t fwd_slots(int d, int in_bf16, int gate_bf16, int *slots) {
     if (e != hipSuccess) return e;
     const void *kern;
     if (d == 64)
-        kern = in_bf16 ? (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, true>)
-                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, false>))
-                       : (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<64, false, true>)
-                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<64, false, false>));
+        kern = in_bf16 ? (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, true, false>)
+                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, false, false>))
+                       : (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<64, false, true, false>)
+                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<64, false, false, false>));
     else
-        kern = in_bf16 ? (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, true>)
-                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, false>))
-                       : (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<128, false, true>)
-                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<128, false, false>));
+        kern = in_bf16 ? (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, true, false>)
+                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, false, false>))
+                       : (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<128, false, true, false>)
+                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<128, false, false, false>));
     const int lds = fwd_lds_bytes(d);
     if ((e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFwdThreads, lds)) != hipSuccess) return e;

@@ -115,6 +115,35 @@ int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
                   float scale, hipStream_t stream);
 
 /*
+ * gdr_chunk_fwd_checkpoints - gdr_chunk_fwd that also writes the state after
+ * every 64-token chunk of every sequence: the per-chunk state checkpoints that
+ * the pages' prefill surface keeps for prefix caching (`state_checkpoints`,
+ * "feat(cake_kda): add paired recurrent training for SM100a and SM103a", the
+ * follow-up's list of kept kwargs).
+ *
+ *   h_chunks  fp32 [R, Hv, dk, dv] out (device), R = ceil(T/64) + N with
+ *             cu_seqlens, else B * ceil(T/64).  Chunk c of sequence n holds
+ *             its tokens 64c .. min(64(c+1), L_n) - 1; row off_n + c receives
+ *             H (= S^T, [dk][dv]) after the last of them, where off_n = sum
+ *             over m < n of ceil(L_m / 64) (the chunk_offsets of
+ *             gdr_prepare_chunks).  The last chunk of a sequence holds ht.
+ *             Rows past NT = off_N are not written; length-0 sequences own
+ *             no rows.
+ *
+ * Everything else, including o and ht, is exactly gdr_chunk_fwd.  Extra
+ * traffic: 4 * dk * dv bytes per (chunk, v-head) written.  With cu_seqlens the
+ * workspace is 8*N + 4 bytes (order and chunk offsets); sequences start
+ * longest first.  Errors as gdr_chunk_fwd, plus GDR_EINVAL (h_chunks NULL),
+ * GDR_EDTYPE / GDR_ESHAPE for h_chunks, GDR_EALIAS when it overlaps any other
+ * tensor.
+ */
+int gdr_chunk_fwd_checkpoints(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
+                              const gdr_tensor *g, const gdr_tensor *beta,
+                              const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
+                              const gdr_tensor *o, const gdr_tensor *ht,
+                              const gdr_tensor *h_chunks, float scale, hipStream_t stream);
+
+/*
  * Launch plan of a gdr_chunk_fwd call, computed from shapes only (no device
  * access).  gdr_plan validates exactly like gdr_chunk_fwd and fills `plan`;
  * it is what gdr_chunk_fwd launches.

@@ -191,3 +191,33 @@ def test_dispatch_order_rejects_alias(lib):
     cu = A(GDR_I32, [11])
     order = describe(cu.t.data + 4, GDR_I32, [10])
     assert lib.gdr_dispatch_order(cu.ref, ctypes.c_int32(4), order.ref, None) == -5
+
+
+def _ckpt_call(lib, d, hck):
+    args = [d[k] for k in ("q", "k", "v", "g", "beta", "cu_seqlens", "h0", "o", "ht")]
+    refs = [None if x is None else x.ref for x in args] + [None if hck is None else hck.ref]
+    return lib.gdr_chunk_fwd_checkpoints(*refs, ctypes.c_float(0.1), None)
+
+
+@pytest.mark.parametrize("varlen,rows_delta,dtype,status,text", [
+    (True, 1, GDR_F32, -2, "h_chunks: shape"),
+    (True, -1, GDR_F32, -2, "h_chunks: shape"),
+    (False, 1, GDR_F32, -2, "h_chunks: shape"),
+    (True, 0, GDR_BF16, -3, "h_chunks: dtype"),
+])
+def test_checkpoints_rejections(lib, varlen, rows_delta, dtype, status, text):
+    d = fwd_descs(B=1 if varlen else 2, T=200, varlen=varlen)
+    rows = (200 + 63) // 64 + 3 if varlen else 2 * ((200 + 63) // 64)
+    hck = Alloc()(dtype, [rows + rows_delta, 4, 128, 128])
+    assert _ckpt_call(lib, d, hck) == status
+    assert text in lib.gdr_last_error().decode()
+
+
+def test_checkpoints_rejects_null_and_alias(lib):
+    d = fwd_descs(T=200)
+    assert _ckpt_call(lib, d, None) == -1
+    assert "h_chunks" in lib.gdr_last_error().decode()
+    rows = (200 + 63) // 64 + 3
+    hck = describe(d["o"].t.data, GDR_F32, [rows, 4, 128, 128])
+    assert _ckpt_call(lib, d, hck) == -5
+    assert "overlaps" in lib.gdr_last_error().decode()
