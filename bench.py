@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "fwd_packed64k_traffic.txt"))
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     ap.add_argument("--traffic-summary", nargs=4, metavar="DIR", default=None)
+    ap.add_argument("--checkpoints", action="store_true",
+                    help="time gdr_chunk_fwd_checkpoints (state after every chunk written); "
+                         "reported against the HBM roofline")
     return ap.parse_args()
 
 
@@ -119,8 +122,16 @@ def main():
     ht = torch.empty((N, w.hv, w.dk, w.dv), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    def step():
-        gdr.chunk_fwd(q, k, v, g, beta, cu, h0, scale=d["scale"], o=o, ht=ht)
+    nt_chunks = sum((L + CHUNK - 1) // CHUNK for L in d["lengths"])
+    if args.checkpoints:
+        rows = ((T + CHUNK - 1) // CHUNK + N) if cu is not None else B * ((T + CHUNK - 1) // CHUNK)
+        hck = torch.empty((rows, w.hv, w.dk, w.dv), dtype=torch.float32, device=dev)
+
+        def step():
+            gdr.chunk_fwd_checkpoints(q, k, v, g, beta, cu, h0, scale=d["scale"], o=o, ht=ht, h_chunks=hck)
+    else:
+        def step():
+            gdr.chunk_fwd(q, k, v, g, beta, cu, h0, scale=d["scale"], o=o, ht=ht)
 
     # events are created before the warm-up: creating them after it would
     # leave the GPU idle long enough to restart its clock transient
@@ -180,6 +191,15 @@ def main():
                 "frac": nbytes / (launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
         "cpu_baseline": None,
     }
+    if args.checkpoints:
+        # the same call plus 4*dk*dv bytes written per (chunk, v-head): HBM bound
+        ck_bytes = nt_chunks * w.hv * w.dk * w.dv * 4
+        tot = nbytes + ck_bytes
+        out["config"]["checkpoints"] = True
+        out["roofline"] = {"bound": "hbm", "achieved": tot / (launch_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS,
+                           "unit": "GB/s", "frac": tot / (launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "traffic": None,
+                           "kernel": "gdr_fwd_kernel<128,bf16,bf16,checkpoints> (+ gdr_prepare_kernel)",
+                           "bytes_per_launch": tot, "checkpoint_bytes": ck_bytes, "launch_ms": launch_ms}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, w, args.cpu_heads)
     print(json.dumps(out), flush=True)
