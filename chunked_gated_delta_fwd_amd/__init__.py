@@ -25,7 +25,8 @@ STATUS = {0: "GDR_OK", -1: "GDR_EINVAL", -2: "GDR_ESHAPE", -3: "GDR_EDTYPE", -4:
           -5: "GDR_EALIAS", -6: "GDR_EDEVICE", -7: "GDR_ELAUNCH", -8: "GDR_ENOMEM"}
 
 # every symbol include/gdr.h declares
-EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_checkpoints", "gdr_plan", "gdr_prepare_chunks", "gdr_dispatch_order",
+EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_checkpoints", "gdr_decode_step", "gdr_plan",
+           "gdr_prepare_chunks", "gdr_dispatch_order",
            "gdr_chunk_local_cumsum", "gdr_last_error", "gdr_version", "gdr_selftest_mfma")
 
 
@@ -67,6 +68,8 @@ def library(path: Optional[str] = None):
     lib.gdr_chunk_fwd.restype = ctypes.c_int
     lib.gdr_chunk_fwd_checkpoints.argtypes = [TP] * 10 + [ctypes.c_float, ctypes.c_void_p]
     lib.gdr_chunk_fwd_checkpoints.restype = ctypes.c_int
+    lib.gdr_decode_step.argtypes = [TP] * 7 + [ctypes.c_float, ctypes.c_void_p]
+    lib.gdr_decode_step.restype = ctypes.c_int
     lib.gdr_plan.argtypes = [TP] * 9 + [ctypes.c_float, ctypes.POINTER(GdrLaunchPlan)]
     lib.gdr_plan.restype = ctypes.c_int
     lib.gdr_prepare_chunks.argtypes = [TP] * 4 + [ctypes.c_void_p]
@@ -187,6 +190,24 @@ def chunk_fwd_checkpoints(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Opt
     _check(lib, lib.gdr_chunk_fwd_checkpoints(*[_ref(x) for x in ds], ctypes.c_float(scale),
                                               ctypes.c_void_p(_stream_handle(q))))
     return o, ht, h_chunks
+
+
+def decode_step(q, k, v, g, beta, h, scale: Optional[float] = None, o=None):
+    """One recurrent step per sequence: q, k ``[B, Hk, d]``, v ``[B, Hv, d]``,
+    g, beta ``[B, Hv]``, state h fp32 ``[B, Hv, d, d]`` updated in place.
+    Returns o ``[B, Hv, d]``."""
+    import torch
+    lib = library()
+    B, Hk, d = q.shape
+    Hv = v.shape[1]
+    if scale is None:
+        scale = float(d) ** -0.5
+    if o is None:
+        o = torch.empty((B, Hv, d), dtype=q.dtype, device=q.device)
+    ds = [_desc(x) for x in (q, k, v, g, beta, h, o)]
+    _check(lib, lib.gdr_decode_step(*[_ref(x) for x in ds], ctypes.c_float(scale),
+                                    ctypes.c_void_p(_stream_handle(q))))
+    return o
 
 
 def plan(q, k, v, g, beta, cu_seqlens=None, h0=None, o=None, ht=None, scale: float = 1.0) -> dict:

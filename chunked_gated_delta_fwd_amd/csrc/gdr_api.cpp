@@ -388,6 +388,74 @@ int gdr_chunk_fwd_checkpoints(const gdr_tensor *q, const gdr_tensor *k, const gd
     return run_fwd(q, k, v, g, beta, cu_seqlens, h0, o, ht, h_chunks, scale, stream);
 }
 
+int gdr_decode_step(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
+                    const gdr_tensor *beta, const gdr_tensor *h, const gdr_tensor *o, float scale,
+                    hipStream_t stream) {
+    int64_t nq, nk, nv, ng, nb, nh, no;
+    int rc;
+    if ((rc = check_tensor(q, "q", 3, &nq, 8))) return rc;
+    if ((rc = check_tensor(k, "k", 3, &nk, 8))) return rc;
+    if ((rc = check_tensor(v, "v", 3, &nv, 8))) return rc;
+    if ((rc = check_tensor(g, "g", 2, &ng, 4))) return rc;
+    if ((rc = check_tensor(beta, "beta", 2, &nb, 4))) return rc;
+    if ((rc = check_tensor(h, "h", 4, &nh, 16))) return rc;
+    if ((rc = check_tensor(o, "o", 3, &no, 16))) return rc;
+    if (q->dtype != GDR_BF16 && q->dtype != GDR_F32)
+        return fail(GDR_EDTYPE, "q: dtype must be bf16 or f32, got %s", dtype_name(q->dtype));
+    if (k->dtype != q->dtype || v->dtype != q->dtype || o->dtype != q->dtype)
+        return fail(GDR_EDTYPE, "q, k, v and o must share one dtype (q is %s)", dtype_name(q->dtype));
+    if (g->dtype != GDR_BF16 && g->dtype != GDR_F32)
+        return fail(GDR_EDTYPE, "g: dtype must be bf16 or f32, got %s", dtype_name(g->dtype));
+    if (beta->dtype != g->dtype) return fail(GDR_EDTYPE, "beta must have the dtype of g");
+    if (h->dtype != GDR_F32) return fail(GDR_EDTYPE, "h: dtype must be f32");
+    const int64_t B = q->shape[0], Hk = q->shape[1], d = q->shape[2];
+    const int64_t Hv = v->shape[1];
+    if (!shape_is(k, {B, Hk, d}))
+        return fail(GDR_ESHAPE, "k: shape %s must equal q's %s", shape_str(k).c_str(), shape_str(q).c_str());
+    if (v->shape[0] != B || v->shape[2] != d)
+        return fail(GDR_ESHAPE, "v: shape %s must be [B, Hv, d] with q's B and d", shape_str(v).c_str());
+    if (!shape_is(o, {B, Hv, d}))
+        return fail(GDR_ESHAPE, "o: shape %s must equal v's %s", shape_str(o).c_str(), shape_str(v).c_str());
+    if (!shape_is(g, {B, Hv}) || !shape_is(beta, {B, Hv}))
+        return fail(GDR_ESHAPE, "g and beta must be [B, Hv] = [%lld, %lld]", (long long)B, (long long)Hv);
+    if (!shape_is(h, {B, Hv, d, d}))
+        return fail(GDR_ESHAPE, "h: shape %s must be [B, Hv, d, d] = [%lld, %lld, %lld, %lld]",
+                    shape_str(h).c_str(), (long long)B, (long long)Hv, (long long)d, (long long)d);
+    if (d != 64 && d != 128) return fail(GDR_ESHAPE, "head dim must be 64 or 128, got %lld", (long long)d);
+    if (Hk < 1 || Hv < 1) return fail(GDR_ESHAPE, "head counts must be positive");
+    if (Hv % Hk != 0)
+        return fail(GDR_ESHAPE, "Hv (%lld) must be a multiple of Hk (%lld)", (long long)Hv, (long long)Hk);
+    if (B * Hv > 0x7FFFFFFFLL) return fail(GDR_ESHAPE, "B * Hv exceeds the launch grid limit");
+    if (!std::isfinite(scale)) return fail(GDR_EINVAL, "scale must be finite");
+    const Span so = span_of(o, no), sh = span_of(h, nh);
+    const Span ins[] = {span_of(q, nq), span_of(k, nk), span_of(v, nv), span_of(g, ng), span_of(beta, nb)};
+    for (const Span &x : ins) {
+        if (overlap(so, x)) return fail(GDR_EALIAS, "o overlaps an input");
+        if (overlap(sh, x)) return fail(GDR_EALIAS, "h overlaps an input");
+    }
+    if (overlap(so, sh)) return fail(GDR_EALIAS, "o and h overlap");
+    if ((rc = check_device())) return rc;
+    if (B == 0) return ok();
+    gdr::DecodeArgs a;
+    a.q = q->data;
+    a.k = k->data;
+    a.v = v->data;
+    a.g = g->data;
+    a.beta = beta->data;
+    a.h = static_cast<float *>(h->data);
+    a.o = o->data;
+    a.batch = B;
+    a.hk = static_cast<int32_t>(Hk);
+    a.hv = static_cast<int32_t>(Hv);
+    a.d = static_cast<int32_t>(d);
+    a.in_bf16 = q->dtype == GDR_BF16;
+    a.gate_bf16 = g->dtype == GDR_BF16;
+    a.scale = scale;
+    const hipError_t e = gdr::launch_decode(a, stream);
+    if (e != hipSuccess) return launch_error(e, "decode kernel");
+    return ok();
+}
+
 int gdr_dispatch_order(const gdr_tensor *cu_seqlens, int32_t groups, const gdr_tensor *order,
                        hipStream_t stream) {
     int64_t ncu, nord;

@@ -29,6 +29,18 @@ struct FwdArgs {
     int64_t ck_rows;
 };
 
+// One recurrent step per (sequence, v-head), already validated on the host.
+struct DecodeArgs {
+    const void *q, *k, *v, *g, *beta;
+    float *h;               // [B, Hv, d, d] fp32, updated in place
+    void *o;                // [B, Hv, d]
+    int64_t batch;          // B
+    int32_t hk, hv, d;
+    int32_t in_bf16, gate_bf16;
+    float scale;
+};
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
 // Dynamic LDS bytes and threads per work-group of the fused forward kernel
 // (4 state-chain waves + 4 preparation waves).
 int fwd_lds_bytes(int d);

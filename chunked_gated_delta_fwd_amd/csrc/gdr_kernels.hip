@@ -1102,6 +1102,80 @@ __global__ void __launch_bounds__(256) gdr_cumsum_kernel(const void *g, const in
 }
 
 // --------------------------------------------------------------------------
+// One recurrent step (decode): for each (sequence b, v-head h), with the state
+// H = S^T [dk][dv] in fp32,
+//   H <- e^g H,  p = H^T k,  d = beta (v - p),  H <- H + k d^T,  o = scale H^T q
+// (the gated delta rule of one token).  HBM bound: H is read and written once.
+// One work-group of 256 threads per (b, h); thread (rg, cg) owns columns
+// 4cg..4cg+3 of rows RPT*rg .. +RPT-1 in registers (16-byte loads and stores);
+// the column sums over rows go through LDS.
+// --------------------------------------------------------------------------
+template <int D, bool IN_BF16, bool GATE_BF16>
+__global__ void __launch_bounds__(256) gdr_decode_kernel(DecodeArgs a) {
+    constexpr int CG = D / 4;       // column groups of 4
+    constexpr int RG = 256 / CG;    // row groups
+    constexpr int RPT = D / RG;     // rows per thread
+    __shared__ float s_part[RG][D];
+    __shared__ float s_k[D], s_q[D];
+    const int64_t item = blockIdx.x;
+    const int64_t b = item / a.hv;
+    const int h = static_cast<int>(item % a.hv);
+    const int hk = h / (a.hv / a.hk);
+    const int t = threadIdx.x, cg = t % CG, rg = t / CG;
+    const int j0 = 4 * cg, i0 = RPT * rg;
+
+    if (t < D) {
+        s_k[t] = load_scalar<IN_BF16>(a.k, (b * a.hk + hk) * D + t);
+        s_q[t] = load_scalar<IN_BF16>(a.q, (b * a.hk + hk) * D + t);
+    }
+    const float gate = __expf(load_scalar<GATE_BF16>(a.g, b * a.hv + h));
+    const float beta = load_scalar<GATE_BF16>(a.beta, b * a.hv + h);
+    float *hp = a.h + (b * a.hv + h) * D * D;
+    f32x4 H[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) H[i] = *reinterpret_cast<const f32x4 *>(hp + (i0 + i) * D + j0);
+    __syncthreads();
+
+    // p = H^T k (before the decay, which is applied to the sum)
+    f32x4 part = zero4();
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) part = part + H[i] * s_k[i0 + i];
+    *reinterpret_cast<f32x4 *>(&s_part[rg][j0]) = part;
+    __syncthreads();
+    f32x4 p = zero4();
+#pragma unroll
+    for (int r = 0; r < RG; ++r) p = p + *reinterpret_cast<const f32x4 *>(&s_part[r][j0]);
+    f32x4 vj;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vj[c] = load_scalar<IN_BF16>(a.v, (b * a.hv + h) * D + j0 + c);
+    const f32x4 dlt = (vj - p * gate) * beta;
+
+    // H <- e^g H + k d^T, stored; o partial = H^T q
+    f32x4 po = zero4();
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        H[i] = H[i] * gate + dlt * s_k[i0 + i];
+        *reinterpret_cast<f32x4 *>(hp + (i0 + i) * D + j0) = H[i];
+        po = po + H[i] * s_q[i0 + i];
+    }
+    __syncthreads();   // every thread has read s_part
+    *reinterpret_cast<f32x4 *>(&s_part[rg][j0]) = po;
+    __syncthreads();
+    if (rg == 0) {
+        f32x4 o = zero4();
+#pragma unroll
+        for (int r = 0; r < RG; ++r) o = o + *reinterpret_cast<const f32x4 *>(&s_part[r][j0]);
+        o = o * a.scale;
+        const int64_t oo = (b * a.hv + h) * D + j0;
+        if constexpr (IN_BF16) {
+            *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(a.o) + oo) = cvt4(o);
+        } else {
+            *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.o) + oo) = o;
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
 // MFMA lane-layout self test: one wave, both bf16 shapes the kernels use
 // --------------------------------------------------------------------------
 __global__ void __launch_bounds__(64) gdr_selftest_kernel(const uint16_t *a, const uint16_t *b, float *c) {
@@ -1197,6 +1271,24 @@ hipError_t launch_cumsum(const void *g, int gate_bf16, const int32_t *cu, const 
         hipLaunchKernelGGL(gdr_cumsum_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
                            g, cu, chunk_map, n_rows, seq_len, total, heads, G);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(a.batch * a.hv)), block(256);
+    if (a.in_bf16) {
+        if (a.gate_bf16) hipLaunchKernelGGL((gdr_decode_kernel<D, true, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gdr_decode_kernel<D, true, false>), grid, block, 0, s, a);
+    } else {
+        if (a.gate_bf16) hipLaunchKernelGGL((gdr_decode_kernel<D, false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gdr_decode_kernel<D, false, false>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+    if (a.batch == 0 || a.hv == 0) return hipSuccess;
+    return a.d == 64 ? launch_decode_d<64>(a, stream) : launch_decode_d<128>(a, stream);
 }
 
 hipError_t launch_selftest_mfma(const uint16_t *a, const uint16_t *b, float *c, hipStream_t stream) {

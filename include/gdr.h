@@ -144,6 +144,32 @@ int gdr_chunk_fwd_checkpoints(const gdr_tensor *q, const gdr_tensor *k, const gd
                               const gdr_tensor *h_chunks, float scale, hipStream_t stream);
 
 /*
+ * gdr_decode_step - one token of the same recurrence for each of B sequences:
+ * the decode step that follows this forward pass in inference (the pages'
+ * inference surface keeps a decode module beside the prefill, "feat(cake_kda):
+ * add paired recurrent training for SM100a and SM103a", the follow-up's list
+ * of kept modules), consuming the final state of gdr_chunk_fwd.  With the
+ * state H = S^T [dk][dv] of sequence b and v-head h:
+ *     H <- e^g H,  d = beta (v - H^T k),  H <- H + k d^T,  o = scale H^T q.
+ *
+ *   q, k   [B, Hk, d]   bf16 or f32 (one dtype with v and o)
+ *   v      [B, Hv, d]
+ *   g, beta [B, Hv]     bf16 or f32 (g is the log-gate of the token)
+ *   h      [B, Hv, d, d] fp32, read and overwritten with the new state
+ *   o      [B, Hv, d]   out, rounded once to its dtype
+ *   scale  as gdr_chunk_fwd
+ *
+ * d in {64, 128}; Hv % Hk == 0 (v-head h reads q/k head h / (Hv/Hk)).  fp32
+ * arithmetic throughout.  No workspace.  HBM bound: 8 * d * d bytes of state
+ * traffic per (sequence, v-head).  Errors: GDR_ESHAPE, GDR_EDTYPE, GDR_EINVAL
+ * (alignment: q/k/v 8 bytes, h and o 16 bytes; scale), GDR_EALIAS (o or h
+ * overlaps an input or each other), GDR_EDEVICE, GDR_ELAUNCH.
+ */
+int gdr_decode_step(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
+                    const gdr_tensor *g, const gdr_tensor *beta, const gdr_tensor *h,
+                    const gdr_tensor *o, float scale, hipStream_t stream);
+
+/*
  * Launch plan of a gdr_chunk_fwd call, computed from shapes only (no device
  * access).  gdr_plan validates exactly like gdr_chunk_fwd and fills `plan`;
  * it is what gdr_chunk_fwd launches.

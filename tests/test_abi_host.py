@@ -221,3 +221,38 @@ def test_checkpoints_rejects_null_and_alias(lib):
     hck = describe(d["o"].t.data, GDR_F32, [rows, 4, 128, 128])
     assert _ckpt_call(lib, d, hck) == -5
     assert "overlaps" in lib.gdr_last_error().decode()
+
+
+def dec_descs(B=3, Hk=2, Hv=4, d=128, dt=GDR_BF16, gdt=GDR_BF16):
+    A = Alloc()
+    return dict(q=A(dt, [B, Hk, d]), k=A(dt, [B, Hk, d]), v=A(dt, [B, Hv, d]), g=A(gdt, [B, Hv]),
+                beta=A(gdt, [B, Hv]), h=A(GDR_F32, [B, Hv, d, d]), o=A(dt, [B, Hv, d]))
+
+
+def _dec_call(lib, d):
+    refs = [d[key].ref for key in ("q", "k", "v", "g", "beta", "h", "o")]
+    return lib.gdr_decode_step(*refs, ctypes.c_float(0.1), None)
+
+
+@pytest.mark.parametrize("mutate,status,text", [
+    (lambda d, A: d.update(k=A(GDR_BF16, [3, 1, 128])), -2, "k: shape"),
+    (lambda d, A: d.update(v=A(GDR_F32, [3, 4, 128])), -3, "share one dtype"),
+    (lambda d, A: d.update(h=A(GDR_BF16, [3, 4, 128, 128])), -3, "h: dtype"),
+    (lambda d, A: d.update(h=A(GDR_F32, [3, 4, 128, 64])), -2, "h: shape"),
+    (lambda d, A: d.update(g=A(GDR_BF16, [3, 5])), -2, "g and beta"),
+    (lambda d, A: d.update(o=A(GDR_BF16, [3, 4, 64])), -2, "o: shape"),
+    (lambda d, A: d.update(o=describe(d["h"].t.data, GDR_BF16, [3, 4, 128])), -5, "o and h overlap"),
+    (lambda d, A: d.update(h=describe(d["q"].t.data, GDR_F32, [3, 4, 128, 128])), -5, "h overlaps"),
+])
+def test_decode_rejections(lib, mutate, status, text):
+    d = dec_descs()
+    mutate(d, Alloc())
+    assert _dec_call(lib, d) == status
+    assert text in lib.gdr_last_error().decode(), lib.gdr_last_error()
+
+
+def test_decode_rejects_heads_and_dims(lib):
+    assert _dec_call(lib, dec_descs(Hk=3, Hv=4)) == -2
+    assert "multiple of Hk" in lib.gdr_last_error().decode()
+    assert _dec_call(lib, dec_descs(d=96)) == -2
+    assert "64 or 128" in lib.gdr_last_error().decode()
