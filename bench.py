@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "fwd_packed64k_traffic.txt"))
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     ap.add_argument("--traffic-summary", nargs=4, metavar="DIR", default=None)
+    ap.add_argument("--decode", type=int, default=0, metavar="B",
+                    help="time gdr_decode_step for B sequences with the workload's heads "
+                         "(one token each, state in place), against the HBM roofline")
     ap.add_argument("--checkpoints", action="store_true",
                     help="time gdr_chunk_fwd_checkpoints (state after every chunk written); "
                          "reported against the HBM roofline")
@@ -105,6 +108,9 @@ def main():
         copy_probe(args.copy_probe_mib)
         return
     w = gi.WORKLOADS[args.workload]
+    if args.decode:
+        bench_decode(args, w)
+        return
     d = gi.generate(w)
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -202,6 +208,69 @@ def main():
                            "bytes_per_launch": tot, "checkpoint_bytes": ck_bytes, "launch_ms": launch_ms}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, w, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(args, w):
+    """Decode-step throughput: B sequences x Hv heads, one token each, the
+    fp32 state read and written in place (HBM bound)."""
+    import torch
+    import chunked_gated_delta_fwd_amd as gdr
+    B, d = args.decode, w.dk
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cpu").manual_seed(w.seed)
+    rnd = lambda *shape: torch.randn(*shape, generator=gen)
+    q = torch.nn.functional.normalize(rnd(B, w.hk, d), dim=-1).to(dev, dt)
+    k = torch.nn.functional.normalize(rnd(B, w.hk, d), dim=-1).to(dev, dt)
+    v = rnd(B, w.hv, d).to(dev, dt)
+    g = torch.nn.functional.logsigmoid(rnd(B, w.hv)).to(dev, dt)
+    beta = torch.sigmoid(rnd(B, w.hv)).to(dev, dt)
+    h = (0.1 * rnd(B, w.hv, d, d)).to(dev)
+    o = torch.empty((B, w.hv, d), dtype=dt, device=dev)
+    # one decode kernel takes tens of microseconds, less than the host needs
+    # to marshal a call, so the steps are captured in a graph (20 per replay)
+    # and replayed; the step has no allocation and no memset to capture
+    per = 20
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            gdr.decode_step(q, k, v, g, beta, h, o=o)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per):
+            gdr.decode_step(q, k, v, g, beta, h, o=o)
+    reps = max(1, args.steps // per)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for _ in range(max(1, args.warmup // per)):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        graph.replay()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sum(s.elapsed_time(e) for s, e in ev) / len(ev) / per
+    args.steps = reps * per
+    eb = 2 if w.dtype == "bf16" else 4
+    nbytes = B * w.hv * (2 * d * d * 4 + 2 * d * eb + 2 * eb) + B * w.hk * 2 * d * eb
+    out = {"metric": "GDN decode-step tokens/sec on 1 MI355X (one token per sequence)",
+           "value": B / (wall / args.steps), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+           "timing": "graph of %d steps per replay" % per,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+           "data": "synthetic",
+           "config": {"workload": "decode_B%d_Hk%d_Hv%d_d%d" % (B, w.hk, w.hv, d), "batch": B, "hk": w.hk,
+                      "hv": w.hv, "d": d},
+           "roofline": {"bound": "hbm", "achieved": nbytes / (launch_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS,
+                        "unit": "GB/s", "frac": nbytes / (launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "traffic": None,
+                        "kernel": "gdr_decode_kernel", "bytes_per_launch": nbytes, "launch_ms": launch_ms},
+           "cpu_baseline": None}
     print(json.dumps(out), flush=True)
 
 
