@@ -180,3 +180,17 @@ def random_lengths_case(seed: int, n_real: int, lo: int, hi: int, ghost_slots: i
     w = Workload("random", 1, 0, hk, hv, d, d, dtype, seg_range=(lo, hi), n_segments=len(seq),
                  with_h0=with_h0, seed=seed + 1)
     return generate(w, lengths=seq)
+
+
+def generate_grads(case: dict, seed: int) -> dict:
+    """Upstream gradients for a backward pass over ``case`` (a dict from
+    ``generate``): ``do`` ~ N(0, 1) of o's shape, rounded to the case's dtype,
+    and ``dht`` ~ N(0, 1) of the final state's shape, fp32.  Drawn with
+    ``PCG64(seed)`` in the order do -> dht."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    v = case["v"]
+    n_seq = (len(case["cu_seqlens"]) - 1) if case["cu_seqlens"] is not None else v.shape[0]
+    do = _store(rng.standard_normal(v.shape, dtype=np.float32), case["dtype"])
+    dht = rng.standard_normal((n_seq, v.shape[2], case["q"].shape[3], v.shape[3]),
+                              dtype=np.float32).astype(np.float32)
+    return dict(do=do, dht=dht)

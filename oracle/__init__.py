@@ -14,9 +14,15 @@ the recurrence is the gated delta rule of Gated DeltaNet,
 ``o_t = scale * S_t q_t``, with the state kept as ``H = S^T`` in
 ``[N, Hv, dk, dv]`` layout.
 
-Pins: ``tests/test_oracle_pins.py`` checks this function against closed forms,
+``gdr_bwd`` is the reverse-mode derivative of the same recurrence, one token
+at a time in reverse order (also in ``gdr_oracle.c``).
+
+Pins: ``tests/test_oracle_pins.py`` checks ``gdr_fwd`` against closed forms,
 exact rational arithmetic on tiny inputs, an independently derived chunked
-(WY) evaluation, and the packing / ghost / resume invariants.
+(WY) evaluation, and the packing / ghost / resume invariants;
+``tests/test_oracle_bwd_pins.py`` checks ``gdr_bwd`` against automatic
+differentiation of an fp64 recurrence written separately in PyTorch and
+against central finite differences of ``gdr_fwd``.
 """
 from __future__ import annotations
 
@@ -54,6 +60,9 @@ def _bind(path: str):
     lib.gdr_oracle_fwd_chunks.argtypes = [dp, dp, dp, dp, dp, lp, i64, i64, i64, i64, i64, i64,
                                           dp, dp, dp, dp, ctypes.c_double, ctypes.c_int]
     lib.gdr_oracle_fwd_chunks.restype = ctypes.c_int
+    lib.gdr_oracle_bwd.argtypes = [dp, dp, dp, dp, dp, lp, i64, i64, i64, i64, i64, i64,
+                                   dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_double, ctypes.c_int]
+    lib.gdr_oracle_bwd.restype = ctypes.c_int
     lib.gdr_oracle_threads.argtypes = [ctypes.c_int, i64]
     lib.gdr_oracle_threads.restype = ctypes.c_int
     return lib
@@ -138,3 +147,48 @@ def gdr_fwd(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Optional[float] =
     if rc != 0:
         raise ValueError("oracle: gdr_oracle_fwd returned %d" % rc)
     return (o, ht, hck) if chunk_states else (o, ht)
+
+
+def gdr_bwd(q, k, v, g, beta, do, cu_seqlens=None, h0=None, dht=None,
+            scale: Optional[float] = None, dh0_init=None, n_threads: int = 0,
+            _lib_path: Optional[str] = None):
+    """Per-token fp64 backward of the gated delta rule forward (``gdr_fwd``).
+
+    ``do`` ``[B, T, Hv, dv]`` and ``dht`` ``[N, Hv, dk, dv]`` (None = zero) are the
+    upstream gradients of o and ht.  Returns a dict of fp64 arrays: ``dq``,
+    ``dk`` ``[B, T, Hk, dk]`` (summed over the v-heads of each group), ``dv``
+    ``[B, T, Hv, dv]``, ``dg``, ``dbeta`` ``[B, T, Hv]`` and ``dh0``
+    ``[N, Hv, dk, dv]`` (rows of length-0 segments keep ``dh0_init``, default 0).
+    """
+    q, k, v, g, beta, do = (_f64(x) for x in (q, k, v, g, beta, do))
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T) or g.shape != (B, T, Hv) or \
+            beta.shape != g.shape or do.shape != v.shape:
+        raise ValueError("oracle: inconsistent shapes")
+    if cu_seqlens is None:
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        if B != 1:
+            raise ValueError("oracle: cu_seqlens requires B == 1")
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    n_seq = cu.shape[0] - 1
+    if scale is None:
+        scale = dk ** -0.5
+    h0a = None if h0 is None else _f64(h0)
+    dhta = None if dht is None else _f64(dht)
+    for name, x in (("h0", h0a), ("dht", dhta)):
+        if x is not None and x.shape != (n_seq, Hv, dk, dv):
+            raise ValueError("oracle: %s must be [N, Hv, dk, dv]" % name)
+    out = dict(dq=np.zeros((B, T, Hk, dk)), dk=np.zeros((B, T, Hk, dk)),
+               dv=np.zeros((B, T, Hv, dv)), dg=np.zeros((B, T, Hv)), dbeta=np.zeros((B, T, Hv)),
+               dh0=np.zeros((n_seq, Hv, dk, dv)) if dh0_init is None else _f64(dh0_init).copy())
+    lib = _load() if _lib_path is None else _bind(_lib_path)
+    rc = lib.gdr_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                            _ptr(cu, ctypes.c_int64), n_seq, B * T, Hk, Hv, dk, dv, _ptr(h0a),
+                            _ptr(do), _ptr(dhta), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                            _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]), float(scale),
+                            int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle: gdr_oracle_bwd returned %d" % rc)
+    return out

@@ -224,3 +224,275 @@ int gdr_oracle_fwd_chunks(const double *q, const double *k, const double *v, con
     free(off);
     return rc;
 }
+
+/*
+ * Backward pass (reverse-mode derivative of the same per-token recurrence).
+ *
+ * Given upstream gradients do = dL/do [T, Hv, dv] and dht = dL/dht
+ * [n_seq, Hv, dk, dv] (NULL = zero), it returns dL/d of every input: dq, dk
+ * [T, Hk, dk] (summed over the v-heads that share a q/k head), dv [T, Hv, dv],
+ * dg, dbeta [T, Hv] and dh0 [n_seq, Hv, dk, dv].  The pages list this as the
+ * other half of the kernel family (the bit-reproducible backward of "Findings
+ * from integrating FlashQLA's Blackwell GDN kernels into a JAX trainer",
+ * opening summary and items 3-4); they give no formula, so the derivative is
+ * taken of the recurrence above, one token at a time, in reverse order.  For
+ * token t with state H_prev before it (a = exp(g_t), b = beta_t):
+ *
+ *   forward   Hd = a H_prev,  p = Hd^T k,  d = b (v - p),  H = Hd + k d^T,
+ *             o = scale H^T q
+ *   reverse   dq  = scale H do          dH += scale q do^T
+ *             dd  = dH^T k              dk  = dH d
+ *             dv  = b dd                dbeta = dd . (v - p)
+ *             dp  = -b dd               dHd = dH + k dp^T,  dk += Hd dp
+ *             dg  = <dHd, Hd>           dH  = a dHd        (the gradient of H_prev)
+ *
+ * The states H_prev are recomputed from per-chunk copies kept during one
+ * forward sweep (64 tokens at a time), which changes nothing in the values.
+ * Tokens outside every segment get zero gradients; a length-0 segment reads
+ * nothing and writes nothing (its dh0 rows keep the caller's bytes), as in the
+ * forward pass.  dh0 is written whether or not h0 was given (NULL h0 means the
+ * zero state, whose gradient is still defined); dh0 NULL = not written.
+ */
+typedef struct {
+    const double *q, *k, *v, *g, *beta, *h0, *dout, *dht;
+    const int64_t *cu;
+    double *dqv, *dkv;   /* [T, Hv, dk] per v-head, summed over groups afterwards */
+    double *dv, *dg, *dbeta, *dh0;
+    int64_t n_seq, T, Hk, Hv, dk, dv_;
+    double scale;
+    int64_t *items;
+    int64_t n_items;
+    int64_t next;
+    pthread_mutex_t lock;
+} bjob_t;
+
+static void bwd_item(const bjob_t *J, int64_t n, int64_t h, double *ws)
+{
+    const int64_t dk = J->dk, dv = J->dv_, Hk = J->Hk, Hv = J->Hv;
+    const int64_t hk = h / (Hv / Hk);
+    const int64_t bos = J->cu[n], eos = J->cu[n + 1];
+    if (eos <= bos) return;
+    const int64_t L = eos - bos, nc = (L + 63) / 64, S = dk * dv;
+
+    /* ws: chunk-start states [nc][S], per-token states of one chunk [65][S], dH, dHd, vectors */
+    double *Hs = ws;
+    double *Hc = Hs + nc * S;
+    double *dH = Hc + 65 * S;
+    double *dHd = dH + S;
+    double *p = dHd + S, *d = p + dv, *dd = d + dv, *dp = dd + dv;
+
+    /* forward sweep keeping the state at every chunk start */
+    double *H = Hc;
+    if (J->h0) memcpy(H, J->h0 + ((n * Hv + h) * dk) * dv, sizeof(double) * S);
+    else memset(H, 0, sizeof(double) * S);
+    for (int64_t t = bos; t < eos; ++t) {
+        if ((t - bos) % 64 == 0) memcpy(Hs + ((t - bos) / 64) * S, H, sizeof(double) * S);
+        const double *kt = J->k + (t * Hk + hk) * dk;
+        const double *vt = J->v + (t * Hv + h) * dv;
+        const double a = exp(J->g[t * Hv + h]), b = J->beta[t * Hv + h];
+        for (int64_t i = 0; i < S; ++i) H[i] *= a;
+        for (int64_t j = 0; j < dv; ++j) p[j] = 0.0;
+        for (int64_t i = 0; i < dk; ++i)
+            for (int64_t j = 0; j < dv; ++j) p[j] += H[i * dv + j] * kt[i];
+        for (int64_t j = 0; j < dv; ++j) d[j] = b * (vt[j] - p[j]);
+        for (int64_t i = 0; i < dk; ++i)
+            for (int64_t j = 0; j < dv; ++j) H[i * dv + j] += kt[i] * d[j];
+    }
+
+    if (J->dht) memcpy(dH, J->dht + ((n * Hv + h) * dk) * dv, sizeof(double) * S);
+    else memset(dH, 0, sizeof(double) * S);
+
+    for (int64_t c = nc - 1; c >= 0; --c) {
+        const int64_t t0 = bos + 64 * c, t1 = (t0 + 64 < eos) ? t0 + 64 : eos;
+        /* Hc[i] = state before token t0 + i */
+        memcpy(Hc, Hs + c * S, sizeof(double) * S);
+        for (int64_t t = t0; t < t1; ++t) {
+            const double *Hp = Hc + (t - t0) * S;
+            double *Hn = Hc + (t - t0 + 1) * S;
+            const double *kt = J->k + (t * Hk + hk) * dk;
+            const double *vt = J->v + (t * Hv + h) * dv;
+            const double a = exp(J->g[t * Hv + h]), b = J->beta[t * Hv + h];
+            for (int64_t i = 0; i < S; ++i) Hn[i] = a * Hp[i];
+            for (int64_t j = 0; j < dv; ++j) p[j] = 0.0;
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) p[j] += Hn[i * dv + j] * kt[i];
+            for (int64_t j = 0; j < dv; ++j) d[j] = b * (vt[j] - p[j]);
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) Hn[i * dv + j] += kt[i] * d[j];
+        }
+        for (int64_t t = t1 - 1; t >= t0; --t) {
+            const double *Hp = Hc + (t - t0) * S;       /* H_prev */
+            const double *Ht = Hc + (t - t0 + 1) * S;   /* H after token t */
+            const double *kt = J->k + (t * Hk + hk) * dk;
+            const double *qt = J->q + (t * Hk + hk) * dk;
+            const double *vt = J->v + (t * Hv + h) * dv;
+            const double *dot = J->dout + (t * Hv + h) * dv;
+            const double a = exp(J->g[t * Hv + h]), b = J->beta[t * Hv + h];
+            double *dqt = J->dqv + (t * Hv + h) * dk;
+            double *dkt = J->dkv + (t * Hv + h) * dk;
+
+            /* recompute p and d from H_prev */
+            for (int64_t j = 0; j < dv; ++j) p[j] = 0.0;
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) p[j] += a * Hp[i * dv + j] * kt[i];
+            for (int64_t j = 0; j < dv; ++j) d[j] = b * (vt[j] - p[j]);
+
+            /* o = scale H^T q */
+            for (int64_t i = 0; i < dk; ++i) {
+                double s = 0.0;
+                for (int64_t j = 0; j < dv; ++j) s += Ht[i * dv + j] * dot[j];
+                dqt[i] = J->scale * s;
+            }
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) dH[i * dv + j] += J->scale * qt[i] * dot[j];
+
+            /* H = Hd + k d^T */
+            for (int64_t j = 0; j < dv; ++j) dd[j] = 0.0;
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) dd[j] += dH[i * dv + j] * kt[i];
+            for (int64_t i = 0; i < dk; ++i) {
+                double s = 0.0;
+                for (int64_t j = 0; j < dv; ++j) s += dH[i * dv + j] * d[j];
+                dkt[i] = s;
+            }
+
+            /* d = b (v - p) */
+            double db = 0.0;
+            for (int64_t j = 0; j < dv; ++j) {
+                J->dv[(t * Hv + h) * dv + j] = b * dd[j];
+                db += dd[j] * (vt[j] - p[j]);
+                dp[j] = -b * dd[j];
+            }
+            J->dbeta[t * Hv + h] = db;
+
+            /* p = Hd^T k with Hd = a H_prev */
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) dHd[i * dv + j] = dH[i * dv + j] + kt[i] * dp[j];
+            for (int64_t i = 0; i < dk; ++i) {
+                double s = 0.0;
+                for (int64_t j = 0; j < dv; ++j) s += a * Hp[i * dv + j] * dp[j];
+                dkt[i] += s;
+            }
+
+            /* Hd = a H_prev */
+            double dgt = 0.0;
+            for (int64_t i = 0; i < S; ++i) dgt += dHd[i] * a * Hp[i];
+            J->dg[t * Hv + h] = dgt;
+            for (int64_t i = 0; i < S; ++i) dH[i] = a * dHd[i];
+        }
+    }
+    if (J->dh0) memcpy(J->dh0 + ((n * Hv + h) * dk) * dv, dH, sizeof(double) * S);
+}
+
+static void *bwd_worker(void *arg)
+{
+    bjob_t *J = (bjob_t *)arg;
+    int64_t max_nc = 1;
+    for (int64_t n = 0; n < J->n_seq; ++n) {
+        const int64_t nc = (J->cu[n + 1] - J->cu[n] + 63) / 64;
+        if (nc > max_nc) max_nc = nc;
+    }
+    const int64_t S = J->dk * J->dv_;
+    double *ws = (double *)malloc(sizeof(double) * (size_t)((max_nc + 67) * S + 4 * J->dv_));
+    if (!ws) return (void *)1;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int64_t i = J->next++;
+        pthread_mutex_unlock(&J->lock);
+        if (i >= J->n_items) break;
+        const int64_t it = J->items[i];
+        bwd_item(J, it / J->Hv, it % J->Hv, ws);
+    }
+    free(ws);
+    return NULL;
+}
+
+static const bjob_t *g_sort_bjob;
+static int by_length_desc_b(const void *a, const void *b)
+{
+    const bjob_t *J = g_sort_bjob;
+    const int64_t ia = *(const int64_t *)a, ib = *(const int64_t *)b;
+    const int64_t na = ia / J->Hv, nb = ib / J->Hv;
+    const int64_t la = J->cu[na + 1] - J->cu[na], lb = J->cu[nb + 1] - J->cu[nb];
+    if (la != lb) return la > lb ? -1 : 1;
+    return ia < ib ? -1 : (ia > ib);
+}
+
+/*
+ * Returns 0 on success, -1 on a bad argument (as gdr_oracle_fwd), -2 when
+ * memory or threads cannot be obtained.  dq, dk, dv, dg, dbeta are fully
+ * written (zero outside segments); h0, dht and dh0 may be NULL.
+ */
+int gdr_oracle_bwd(const double *q, const double *k, const double *v, const double *g,
+                   const double *beta, const int64_t *cu, int64_t n_seq, int64_t T,
+                   int64_t Hk, int64_t Hv, int64_t dk, int64_t dv, const double *h0,
+                   const double *dout, const double *dht, double *dq, double *dk_out,
+                   double *dv_out, double *dg, double *dbeta, double *dh0, double scale,
+                   int n_threads)
+{
+    if (n_seq < 0 || T < 0 || Hk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || Hv % Hk != 0)
+        return -1;
+    if (n_seq > 0 && cu[0] < 0) return -1;
+    for (int64_t n = 0; n < n_seq; ++n)
+        if (cu[n + 1] < cu[n] || cu[n + 1] > T) return -1;
+
+    memset(dq, 0, sizeof(double) * (size_t)(T * Hk * dk));
+    memset(dk_out, 0, sizeof(double) * (size_t)(T * Hk * dk));
+    memset(dv_out, 0, sizeof(double) * (size_t)(T * Hv * dv));
+    memset(dg, 0, sizeof(double) * (size_t)(T * Hv));
+    memset(dbeta, 0, sizeof(double) * (size_t)(T * Hv));
+    if (n_seq == 0) return 0;
+
+    bjob_t J;
+    J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.h0 = h0; J.dout = dout; J.dht = dht;
+    J.cu = cu; J.dv = dv_out; J.dg = dg; J.dbeta = dbeta; J.dh0 = dh0;
+    J.n_seq = n_seq; J.T = T; J.Hk = Hk; J.Hv = Hv; J.dk = dk; J.dv_ = dv;
+    J.scale = scale;
+    J.dqv = (double *)calloc((size_t)(T * Hv * dk) + 1, sizeof(double));
+    J.dkv = (double *)calloc((size_t)(T * Hv * dk) + 1, sizeof(double));
+    J.n_items = n_seq * Hv;
+    J.next = 0;
+    J.items = (int64_t *)malloc(sizeof(int64_t) * (size_t)J.n_items);
+    if (!J.dqv || !J.dkv || !J.items) {
+        free(J.dqv); free(J.dkv); free(J.items);
+        return -2;
+    }
+    for (int64_t i = 0; i < J.n_items; ++i) J.items[i] = i;
+    g_sort_bjob = &J;
+    qsort(J.items, (size_t)J.n_items, sizeof(int64_t), by_length_desc_b);
+    pthread_mutex_init(&J.lock, NULL);
+
+    const int nt = gdr_oracle_threads(n_threads, J.n_items);
+    int rc = 0;
+    if (nt == 1) {
+        if (bwd_worker(&J)) rc = -2;
+    } else {
+        pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nt);
+        int started = 0;
+        if (!th) rc = -2;
+        for (int i = 0; rc == 0 && i < nt; ++i) {
+            if (pthread_create(&th[i], NULL, bwd_worker, &J) != 0) { rc = -2; break; }
+            ++started;
+        }
+        for (int i = 0; i < started; ++i) {
+            void *ret = NULL;
+            pthread_join(th[i], &ret);
+            if (ret) rc = -2;
+        }
+        free(th);
+    }
+    pthread_mutex_destroy(&J.lock);
+
+    /* q and k are shared by the Hv / Hk v-heads of a group: their gradients add */
+    const int64_t G = Hv / Hk;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < Hv; ++h)
+            for (int64_t i = 0; i < dk; ++i) {
+                dq[(t * Hk + h / G) * dk + i] += J.dqv[(t * Hv + h) * dk + i];
+                dk_out[(t * Hk + h / G) * dk + i] += J.dkv[(t * Hv + h) * dk + i];
+            }
+    free(J.dqv);
+    free(J.dkv);
+    free(J.items);
+    return rc;
+}

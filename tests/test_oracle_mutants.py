@@ -76,3 +76,43 @@ def test_mutant_is_caught(tmp_path, name, old, new):
         except (AssertionError, ValueError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, "mutant %s passed every pin" % name
+
+
+# Mistakes planted in the backward half of the oracle source; the backward
+# pins (against the unmodified, separately pinned forward) must catch each.
+BWD_MUTANTS = [
+    ("bwd_output_no_scale", "dH[i * dv + j] += J->scale * qt[i] * dot[j];",
+     "dH[i * dv + j] += qt[i] * dot[j];"),
+    ("bwd_dbeta_sign", "db += dd[j] * (vt[j] - p[j]);", "db += dd[j] * (vt[j] + p[j]);"),
+    ("bwd_dp_sign", "dp[j] = -b * dd[j];", "dp[j] = b * dd[j];"),
+    ("bwd_dg_no_decay", "dgt += dHd[i] * a * Hp[i];", "dgt += dHd[i] * Hp[i];"),
+    ("bwd_state_no_decay", "for (int64_t i = 0; i < S; ++i) dH[i] = a * dHd[i];",
+     "for (int64_t i = 0; i < S; ++i) dH[i] = dHd[i];"),
+    ("bwd_dk_no_prediction_term", "dkt[i] += s;", "dkt[i] += 0.0 * s;"),
+    ("bwd_dq_previous_state", "s += Ht[i * dv + j] * dot[j];", "s += Hp[i * dv + j] * dot[j];"),
+    ("bwd_gqa_overwrite", "dq[(t * Hk + h / G) * dk + i] += J.dqv", "dq[(t * Hk + h / G) * dk + i] = J.dqv"),
+    ("bwd_no_dht", "if (J->dht) memcpy(dH,", "if (0) memcpy(dH,"),
+    ("bwd_recompute_wrong_chunk", "memcpy(Hc, Hs + c * S, sizeof(double) * S);",
+     "memcpy(Hc, Hs + (c > 0 ? c - 1 : 0) * S, sizeof(double) * S);"),
+    ("bwd_dv_no_beta", "J->dv[(t * Hv + h) * dv + j] = b * dd[j];", "J->dv[(t * Hv + h) * dv + j] = dd[j];"),
+    ("bwd_no_dh0", "if (J->dh0) memcpy(J->dh0", "if (J->dh0 && 0) memcpy(J->dh0"),
+    ("bwd_ghost_writes", "if (eos <= bos) return;\n    const int64_t L = eos - bos",
+     "if (eos < bos) return;\n    const int64_t L = eos - bos"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
+def test_bwd_mutant_is_caught(tmp_path, name, old, new):
+    from oracle_bwd_pins import ALL_BWD_PINS
+    so = _build(tmp_path, name, old, new)
+
+    def bwd(*a, **kw):
+        return oracle.gdr_bwd(*a, _lib_path=so, **kw)
+
+    caught = []
+    for pin in ALL_BWD_PINS:
+        try:
+            pin(bwd, oracle.gdr_fwd)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, "mutant %s passed every backward pin" % name
