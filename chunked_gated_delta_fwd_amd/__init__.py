@@ -25,7 +25,7 @@ STATUS = {0: "GDR_OK", -1: "GDR_EINVAL", -2: "GDR_ESHAPE", -3: "GDR_EDTYPE", -4:
           -5: "GDR_EALIAS", -6: "GDR_EDEVICE", -7: "GDR_ELAUNCH", -8: "GDR_ENOMEM"}
 
 # every symbol include/gdr.h declares
-EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_checkpoints", "gdr_decode_step", "gdr_plan",
+EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_checkpoints", "gdr_chunk_bwd", "gdr_decode_step", "gdr_plan",
            "gdr_prepare_chunks", "gdr_dispatch_order",
            "gdr_chunk_local_cumsum", "gdr_last_error", "gdr_version", "gdr_selftest_mfma")
 
@@ -68,6 +68,8 @@ def library(path: Optional[str] = None):
     lib.gdr_chunk_fwd.restype = ctypes.c_int
     lib.gdr_chunk_fwd_checkpoints.argtypes = [TP] * 10 + [ctypes.c_float, ctypes.c_void_p]
     lib.gdr_chunk_fwd_checkpoints.restype = ctypes.c_int
+    lib.gdr_chunk_bwd.argtypes = [TP] * 15 + [ctypes.c_float, ctypes.c_void_p]
+    lib.gdr_chunk_bwd.restype = ctypes.c_int
     lib.gdr_decode_step.argtypes = [TP] * 7 + [ctypes.c_float, ctypes.c_void_p]
     lib.gdr_decode_step.restype = ctypes.c_int
     lib.gdr_plan.argtypes = [TP] * 9 + [ctypes.c_float, ctypes.POINTER(GdrLaunchPlan)]
@@ -190,6 +192,40 @@ def chunk_fwd_checkpoints(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Opt
     _check(lib, lib.gdr_chunk_fwd_checkpoints(*[_ref(x) for x in ds], ctypes.c_float(scale),
                                               ctypes.c_void_p(_stream_handle(q))))
     return o, ht, h_chunks
+
+
+def chunk_bwd(q, k, v, g, beta, do, cu_seqlens=None, h0=None, dht=None, scale: Optional[float] = None,
+              dq=None, dk=None, dv=None, dg=None, dbeta=None, dh0=None, want_dh0: bool = True):
+    """Backward pass of ``chunk_fwd``: given ``do`` ``[B, T, Hv, dv]`` (dtype of
+    q) and ``dht`` fp32 ``[N, Hv, dk, dv]`` (or None), returns
+    ``(dq, dk, dv, dg, dbeta, dh0)``: dq, dk ``[B, T, Hk, dk]`` and dv in q's
+    dtype, dg and dbeta fp32 ``[B, T, Hv]``, dh0 fp32 ``[N, Hv, dk, dv]`` (None
+    when ``want_dh0`` is False).  Outputs not given are allocated zeroed (rows
+    of tokens outside every segment are not written)."""
+    import torch
+    lib = library()
+    B, T, Hk, d = q.shape
+    Hv = v.shape[2]
+    N = (cu_seqlens.shape[0] - 1) if cu_seqlens is not None else B
+    if scale is None:
+        scale = float(d) ** -0.5
+    dev = q.device
+    if dq is None:
+        dq = torch.zeros_like(q)
+    if dk is None:
+        dk = torch.zeros_like(k)
+    if dv is None:
+        dv = torch.zeros_like(v)
+    if dg is None:
+        dg = torch.zeros((B, T, Hv), dtype=torch.float32, device=dev)
+    if dbeta is None:
+        dbeta = torch.zeros((B, T, Hv), dtype=torch.float32, device=dev)
+    if dh0 is None and want_dh0:
+        dh0 = torch.zeros((N, Hv, d, v.shape[3]), dtype=torch.float32, device=dev)
+    ds = [_desc(x) for x in (q, k, v, g, beta, cu_seqlens, h0, do, dht, dq, dk, dv, dg, dbeta, dh0)]
+    _check(lib, lib.gdr_chunk_bwd(*[_ref(x) for x in ds], ctypes.c_float(scale),
+                                  ctypes.c_void_p(_stream_handle(q))))
+    return dq, dk, dv, dg, dbeta, dh0
 
 
 def decode_step(q, k, v, g, beta, h, scale: Optional[float] = None, o=None):

@@ -109,9 +109,12 @@ std::string shape_str(const gdr_tensor *t) {
 }
 
 // Validates a forward call and fills the plan (shapes only, no device access).
+// The backward pass reuses it for its inputs: there `o` is the incoming
+// gradient do (named `o_name`, an input, so not checked for overlaps).
 int plan_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
              const gdr_tensor *beta, const gdr_tensor *cu, const gdr_tensor *h0, const gdr_tensor *o,
-             const gdr_tensor *ht, float scale, gdr_launch_plan *p) {
+             const gdr_tensor *ht, float scale, gdr_launch_plan *p, const char *o_name = "o") {
+    const bool o_out = std::strcmp(o_name, "o") == 0;
     int64_t nq, nk, nv, ng, nb, no, ncu = 0, nh0 = 0, nht = 0;
     int rc;
     if ((rc = check_tensor(q, "q", 4, &nq, 16))) return rc;
@@ -119,7 +122,7 @@ int plan_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, cons
     if ((rc = check_tensor(v, "v", 4, &nv, 16))) return rc;
     if ((rc = check_tensor(g, "g", 3, &ng, 4))) return rc;
     if ((rc = check_tensor(beta, "beta", 3, &nb, 4))) return rc;
-    if ((rc = check_tensor(o, "o", 4, &no, 16))) return rc;
+    if ((rc = check_tensor(o, o_name, 4, &no, 16))) return rc;
     if (cu && (rc = check_tensor(cu, "cu_seqlens", 1, &ncu, 4))) return rc;
     if (h0 && (rc = check_tensor(h0, "h0", 4, &nh0, 4))) return rc;
     if (ht && (rc = check_tensor(ht, "ht", 4, &nht, 4))) return rc;
@@ -127,7 +130,7 @@ int plan_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, cons
     if (q->dtype != GDR_BF16 && q->dtype != GDR_F32)
         return fail(GDR_EDTYPE, "q: dtype must be bf16 or f32, got %s", dtype_name(q->dtype));
     if (k->dtype != q->dtype || v->dtype != q->dtype || o->dtype != q->dtype)
-        return fail(GDR_EDTYPE, "q, k, v and o must share one dtype (q is %s)", dtype_name(q->dtype));
+        return fail(GDR_EDTYPE, "q, k, v and %s must share one dtype (q is %s)", o_name, dtype_name(q->dtype));
     if (g->dtype != GDR_BF16 && g->dtype != GDR_F32)
         return fail(GDR_EDTYPE, "g: dtype must be bf16 or f32, got %s", dtype_name(g->dtype));
     if (beta->dtype != g->dtype) return fail(GDR_EDTYPE, "beta must have the dtype of g");
@@ -142,7 +145,7 @@ int plan_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, cons
     if (v->shape[0] != B || v->shape[1] != T)
         return fail(GDR_ESHAPE, "v: shape %s must be [B, T, Hv, dv] with q's B, T", shape_str(v).c_str());
     if (!shape_is(o, {B, T, Hv, dv}))
-        return fail(GDR_ESHAPE, "o: shape %s must equal v's %s", shape_str(o).c_str(), shape_str(v).c_str());
+        return fail(GDR_ESHAPE, "%s: shape %s must equal v's %s", o_name, shape_str(o).c_str(), shape_str(v).c_str());
     if (!shape_is(g, {B, T, Hv}) || !shape_is(beta, {B, T, Hv}))
         return fail(GDR_ESHAPE, "g and beta must be [B, T, Hv] = [%lld, %lld, %lld]", (long long)B,
                     (long long)T, (long long)Hv);
@@ -175,7 +178,7 @@ int plan_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, cons
     const Span ins[] = {span_of(q, nq), span_of(k, nk), span_of(v, nv), span_of(g, ng),
                         span_of(beta, nb), span_of(cu, ncu), span_of(h0, nh0)};
     for (const Span &s : ins) {
-        if (overlap(so, s)) return fail(GDR_EALIAS, "o overlaps an input");
+        if (o_out && overlap(so, s)) return fail(GDR_EALIAS, "o overlaps an input");
         if (overlap(sht, s)) return fail(GDR_EALIAS, "ht overlaps an input");
     }
     if (overlap(so, sht)) return fail(GDR_EALIAS, "o and ht overlap");
@@ -362,6 +365,179 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     return ok();
 }
 
+// Workspace of a backward call: chunk indices (varlen only), then per (chunk
+// row, v-head) the forward state, the state gradient, dU, T^T and w^T, each
+// part 256-byte aligned.
+struct BwdWorkspace {
+    size_t ints, hck, dhe, du, tmat, wt, total;
+};
+BwdWorkspace bwd_workspace(int64_t n_seq, int64_t rows, int64_t hv, int64_t d, bool varlen) {
+    auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    const size_t ch = static_cast<size_t>(rows) * static_cast<size_t>(hv);
+    const size_t dd = static_cast<size_t>(d);
+    BwdWorkspace w;
+    size_t o = 0;
+    w.ints = o;
+    o += al(varlen ? 4 * static_cast<size_t>(2 * n_seq + 1 + 2 * rows) : 0);
+    w.hck = o;
+    o += al(ch * dd * dd * 4);
+    w.dhe = o;
+    o += al(ch * dd * dd * 4);
+    w.du = o;
+    o += al(ch * gdr::kChunk * dd * 4);
+    w.tmat = o;
+    o += al(ch * gdr::kChunk * gdr::kChunk * 2);
+    w.wt = o;
+    o += al(ch * dd * gdr::kChunk * 2);
+    w.total = o;
+    return w;
+}
+
+int check_out(const gdr_tensor *t, const char *name, int ndim, int32_t dtype, std::initializer_list<int64_t> shape,
+              int64_t *numel) {
+    int rc = check_tensor(t, name, ndim, numel, 16);
+    if (rc) return rc;
+    if (t->dtype != dtype) return fail(GDR_EDTYPE, "%s: dtype must be %s, got %s", name, dtype_name(dtype), dtype_name(t->dtype));
+    if (!shape_is(t, shape)) return fail(GDR_ESHAPE, "%s: shape %s does not match the inputs", name, shape_str(t).c_str());
+    return GDR_OK;
+}
+
+int run_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
+            const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0, const gdr_tensor *dout,
+            const gdr_tensor *dht, const gdr_tensor *dq, const gdr_tensor *dk, const gdr_tensor *dv,
+            const gdr_tensor *dg, const gdr_tensor *dbeta, const gdr_tensor *dh0, float scale, hipStream_t stream) {
+    gdr_launch_plan p;
+    int rc = plan_fwd(q, k, v, g, beta, cu_seqlens, h0, dout, nullptr, scale, &p, "do");
+    if (rc) return rc;
+    const int64_t B = q->shape[0], T = q->shape[1], N = p.n_seq, Hk = p.hk, Hv = p.hv, d = p.d;
+    int64_t ndht = 0, ndq, ndk, ndv, ndg, ndb, ndh0 = 0;
+    if (dht) {
+        if ((rc = check_tensor(dht, "dht", 4, &ndht, 4))) return rc;
+        if (dht->dtype != GDR_F32) return fail(GDR_EDTYPE, "dht: dtype must be f32");
+        if (!shape_is(dht, {N, Hv, d, d}))
+            return fail(GDR_ESHAPE, "dht: shape %s must be [N, Hv, dk, dv]", shape_str(dht).c_str());
+    }
+    if ((rc = check_out(dq, "dq", 4, q->dtype, {B, T, Hk, d}, &ndq))) return rc;
+    if ((rc = check_out(dk, "dk", 4, q->dtype, {B, T, Hk, d}, &ndk))) return rc;
+    if ((rc = check_out(dv, "dv", 4, q->dtype, {B, T, Hv, d}, &ndv))) return rc;
+    if ((rc = check_out(dg, "dg", 3, GDR_F32, {B, T, Hv}, &ndg))) return rc;
+    if ((rc = check_out(dbeta, "dbeta", 3, GDR_F32, {B, T, Hv}, &ndb))) return rc;
+    if (dh0 && (rc = check_out(dh0, "dh0", 4, GDR_F32, {N, Hv, d, d}, &ndh0))) return rc;
+
+    auto numel = [](const gdr_tensor *t) {
+        int64_t n = 1;
+        for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+        return n;
+    };
+    const gdr_tensor *ins[] = {q, k, v, g, beta, cu_seqlens, h0, dout, dht};
+    const Span outs[] = {span_of(dq, ndq), span_of(dk, ndk), span_of(dv, ndv), span_of(dg, ndg),
+                         span_of(dbeta, ndb), span_of(dh0, ndh0)};
+    for (const gdr_tensor *t : ins) {
+        if (!t) continue;
+        const Span si = span_of(t, numel(t));
+        for (const Span &so : outs)
+            if (overlap(so, si)) return fail(GDR_EALIAS, "a gradient output overlaps an input");
+    }
+    for (int i = 0; i < 6; ++i)
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(outs[i], outs[j])) return fail(GDR_EALIAS, "gradient outputs overlap");
+    if ((rc = check_device())) return rc;
+    if (N == 0 || p.total_tokens == 0) return ok();
+
+    const bool varlen = cu_seqlens != nullptr;
+    const int64_t rows = varlen ? p.nt_max : B * ((T + gdr::kChunk - 1) / gdr::kChunk);
+    const BwdWorkspace wl = bwd_workspace(N, rows, Hv, d, varlen);
+    void *ws = nullptr;
+    {
+        hipMemPool_t pool = nullptr;
+        hipError_t e = workspace_pool(&pool);
+        if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, wl.total, pool, stream);
+        if (e != hipSuccess)
+            return fail(GDR_ENOMEM, "workspace of %lld bytes: %s", (long long)wl.total, hipGetErrorString(e));
+    }
+    unsigned char *base = static_cast<unsigned char *>(ws);
+    int32_t *offs = nullptr, *map = nullptr, *order = nullptr;
+    const int32_t *cu = varlen ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
+    hipError_t e = hipSuccess;
+    if (varlen) {
+        offs = reinterpret_cast<int32_t *>(base + wl.ints);
+        map = offs + N + 1;
+        order = map + 2 * rows;
+        e = gdr::launch_prepare(cu, N, offs, map, rows, order, stream);
+    }
+    float *hck = reinterpret_cast<float *>(base + wl.hck);
+    if (e == hipSuccess) {
+        // forward recompute: the state after every chunk (no o, no ht)
+        gdr::FwdArgs fa;
+        std::memset(&fa, 0, sizeof(fa));
+        fa.q = q->data;
+        fa.k = k->data;
+        fa.v = v->data;
+        fa.g = g->data;
+        fa.beta = beta->data;
+        fa.cu = cu;
+        fa.order = order;
+        fa.h0 = h0 ? static_cast<const float *>(h0->data) : nullptr;
+        fa.o = nullptr;
+        fa.ht = nullptr;
+        fa.n_seq = N;
+        fa.seq_len = varlen ? p.total_tokens : T;
+        fa.total_tokens = p.total_tokens;
+        fa.hk = p.hk;
+        fa.hv = p.hv;
+        fa.d = p.d;
+        fa.in_bf16 = p.in_dtype == GDR_BF16;
+        fa.gate_bf16 = p.gate_dtype == GDR_BF16;
+        fa.scale = scale;
+        fa.hck = hck;
+        fa.ck_offs = offs;
+        fa.ck_rows = rows;
+        e = gdr::launch_fwd(fa, stream);
+    }
+    if (e == hipSuccess) {
+        gdr::BwdArgs ba;
+        std::memset(&ba, 0, sizeof(ba));
+        ba.q = q->data;
+        ba.k = k->data;
+        ba.v = v->data;
+        ba.g = g->data;
+        ba.beta = beta->data;
+        ba.dout = dout->data;
+        ba.cu = cu;
+        ba.map = map;
+        ba.offs = offs;
+        ba.order = order;
+        ba.h0 = h0 ? static_cast<const float *>(h0->data) : nullptr;
+        ba.dht = dht ? static_cast<const float *>(dht->data) : nullptr;
+        ba.hck = hck;
+        ba.tmat = reinterpret_cast<uint16_t *>(base + wl.tmat);
+        ba.wt = reinterpret_cast<uint16_t *>(base + wl.wt);
+        ba.du = reinterpret_cast<float *>(base + wl.du);
+        ba.dhe = reinterpret_cast<float *>(base + wl.dhe);
+        ba.dq = dq->data;
+        ba.dk = dk->data;
+        ba.dv = dv->data;
+        ba.dg = static_cast<float *>(dg->data);
+        ba.dbeta = static_cast<float *>(dbeta->data);
+        ba.dh0 = dh0 ? static_cast<float *>(dh0->data) : nullptr;
+        ba.n_seq = N;
+        ba.seq_len = varlen ? p.total_tokens : T;
+        ba.total_tokens = p.total_tokens;
+        ba.rows = rows;
+        ba.hk = p.hk;
+        ba.hv = p.hv;
+        ba.d = p.d;
+        ba.in_bf16 = p.in_dtype == GDR_BF16;
+        ba.gate_bf16 = p.gate_dtype == GDR_BF16;
+        ba.scale = scale;
+        e = gdr::launch_bwd(ba, stream);
+    }
+    const hipError_t fe = hipFreeAsync(ws, stream);
+    if (e != hipSuccess) return launch_error(e, "backward kernels");
+    if (fe != hipSuccess) return launch_error(fe, "workspace release");
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -386,6 +562,14 @@ int gdr_chunk_fwd_checkpoints(const gdr_tensor *q, const gdr_tensor *k, const gd
                               const gdr_tensor *h_chunks, float scale, hipStream_t stream) {
     if (!h_chunks) return fail(GDR_EINVAL, "h_chunks: descriptor is NULL");
     return run_fwd(q, k, v, g, beta, cu_seqlens, h0, o, ht, h_chunks, scale, stream);
+}
+
+int gdr_chunk_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
+                  const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
+                  const gdr_tensor *dout, const gdr_tensor *dht, const gdr_tensor *dq, const gdr_tensor *dk,
+                  const gdr_tensor *dv, const gdr_tensor *dg, const gdr_tensor *dbeta, const gdr_tensor *dh0,
+                  float scale, hipStream_t stream) {
+    return run_bwd(q, k, v, g, beta, cu_seqlens, h0, dout, dht, dq, dk, dv, dg, dbeta, dh0, scale, stream);
 }
 
 int gdr_decode_step(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,

@@ -1,0 +1,850 @@
+// HIP kernels of the backward pass of the chunked gated delta rule, for
+// gfx950 (CDNA4).  The pages treat the backward as the other half of the
+// FlashQLA kernel family ("Findings from integrating FlashQLA's Blackwell GDN
+// kernels into a JAX trainer": opening summary, items 3-4); they give no
+// formula, so the gradients here are the reverse-mode derivative of the
+// forward recurrence written in chunk form.
+//
+// One chunk of 64 tokens (rows past the sequence end are zero with g = b = 0),
+// state S (= H, dk x dv) at its start, G the chunk-local prefix sum of g,
+// gamma = e^G, lambda = e^{G_L - G}, A~_ij = e^{G_i - G_j} k_i.k_j (j < i),
+// T = (I + diag(b) A~)^-1, M_ij = e^{G_i - G_j} (j <= i).  Forward:
+//
+//   X = K S,  R~ = V - diag(gamma) X,  U = T diag(b) R~
+//   O = scale (diag(gamma) Q S + (M o Q K^T) U)
+//   S' = e^{G_L} S + K^T diag(lambda) U
+//
+// Given dO and dS' (the gradient of the state at the chunk end):
+//
+//   dU  = scale (M o Q K^T)^T dO + diag(lambda) K dS'      (local part dU0 + chain part)
+//   dW  = T^T dU,   dV = diag(b) dW
+//   dS  = e^{G_L} dS' + scale Q^T diag(gamma) dO - w^T dU,  w = T diag(b gamma) K
+//   Zs  = scale M o (dO U^T),   dBn = -(strictly lower M) o (dW U^T),   dB = diag(b) dBn
+//   dQ  = scale diag(gamma) dO S^T + Zs K
+//   dK  = [-diag(b gamma) dW S^T + diag(b) dBn K]              (row uses of k)
+//       + [diag(lambda) U dS'^T + Zs^T Q + dB^T K]              (column uses of k)
+//   db  = rowsum(dW o R~) + rowsum(K o (dBn K))
+//   dG  = rowsum(Q o dQ) + rowsum(K o row part) - rowsum(K o column part),
+//         plus, in the last row, e^{G_L} <dS', S> + sum_j lambda_j k_j . (U dS'^T)_j
+//   dg  = reverse prefix sum of dG within the chunk
+//
+// The gate enters every term as e^{G_i} on a row and e^{-G_j} on a column, so
+// its gradient is q.dq + k.(row part) - k.(column part) (plus the G_L terms).
+// q and k gradients of the v-heads that share a q/k head add up.
+//
+// Kernels (after the forward kernel has written the state after every chunk):
+//   gdr_bwd_prep_kernel   per (chunk, v-head), in parallel: T by block
+//                         substitution, w^T, and the local dU0.
+//   gdr_bwd_chain_kernel  per (sequence, v-head), chunks in reverse order:
+//                         dS' kept in fp32 registers, dU completed in place,
+//                         dS' of every chunk stored for the next kernel.
+//   gdr_bwd_grads_kernel  per (chunk, q/k head), in parallel, looping over the
+//                         v-heads of the group: dq, dk, dv, dg, dbeta.
+#include "gdr_internal.h"
+#include "gdr_device.h"
+
+#include <stdint.h>
+
+namespace gdr {
+namespace {
+
+constexpr int kBwdThreads = 512;     // prep and gradient kernels: 8 waves
+constexpr int kChainThreads = 256;   // reverse chain: 4 waves
+
+// A fragment from [m][k] storage (or a B fragment from [n][k] storage): rows
+// row0 + l16, k = k0 + 16 h + 4 lq + r for the two K16 halves h.
+__device__ __forceinline__ bf16x8 frag_rows(const uint16_t *M, int pitch, int row0, int k0, int l16, int lq) {
+    const uint16_t *p = M + (row0 + l16) * pitch + k0 + 4 * lq;
+    return cat(ld4(p), ld4(p + 16));
+}
+// A fragment from [k][m] storage (or a B fragment from [k][n] storage), by
+// transposing reads: lane i of a 16-lane group receives column col0 + i.
+__device__ __forceinline__ bf16x8 frag_cols(const uint16_t *M, int pitch, int col0, int k0, int l16, int lq) {
+    const uint16_t *p = M + (k0 + 4 * lq + (l16 >> 2)) * pitch + col0 + 4 * (l16 & 3);
+    return cat(ld4_tr(p), ld4_tr(p + 16 * pitch));
+}
+__device__ __forceinline__ float bf16_to_f(uint16_t u) { return __uint_as_float(static_cast<uint32_t>(u) << 16); }
+
+// Sum over each 16-lane row of the wave, left in the row's last lane.
+__device__ __forceinline__ float row_sum16(float x) {
+    x = dpp_add<0x111, 0xF>(x);
+    x = dpp_add<0x112, 0xF>(x);
+    x = dpp_add<0x114, 0xF>(x);
+    x = dpp_add<0x118, 0xF>(x);
+    return x;
+}
+__device__ __forceinline__ float lane63(float x) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_elem(void *p, int64_t i, float v) {
+    if constexpr (BF16) reinterpret_cast<uint16_t *>(p)[i] = bf16_bits(v);
+    else reinterpret_cast<float *>(p)[i] = v;
+}
+
+// Rows t0 .. t0+len-1 of a [tokens, heads, D] tensor (one head) into LDS
+// [64][pitch] bf16; rows from len on are zero.
+template <int D, bool BF16, int NT>
+__device__ __forceinline__ void stage_rows(uint16_t *dst, int pitch, const void *src, int64_t t0, int len,
+                                           int heads, int head, int tid) {
+    constexpr int PR = D / 8;
+    for (int i = tid; i < C * PR; i += NT) {
+        const int row = i / PR, col = 8 * (i % PR);
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (row < len) v = load8<BF16>(src, ((t0 + row) * heads + head) * D + col);
+        *reinterpret_cast<uint4 *>(dst + row * pitch + col) = v;
+    }
+}
+
+// Which sequence and chunk a chunk row belongs to.
+struct ChunkAt {
+    int64_t n, c, t0;
+    int len;
+};
+__device__ __forceinline__ bool chunk_at(const BwdArgs &a, int64_t r, ChunkAt &p) {
+    int64_t bos, eos;
+    if (a.map) {
+        const int32_t n = a.map[2 * r];
+        if (n < 0 || n >= a.n_seq) return false;
+        p.n = n;
+        p.c = a.map[2 * r + 1];
+        bos = a.cu[n];
+        eos = a.cu[n + 1];
+    } else {
+        const int64_t per = (a.seq_len + C - 1) / C;
+        p.n = r / per;
+        p.c = r % per;
+        if (p.n >= a.n_seq) return false;
+        bos = p.n * a.seq_len;
+        eos = bos + a.seq_len;
+    }
+    bos = bos < 0 ? 0 : bos;
+    eos = eos > a.total_tokens ? a.total_tokens : eos;
+    p.t0 = bos + C * p.c;
+    const int64_t len = eos - p.t0 < C ? eos - p.t0 : C;
+    if (len <= 0) return false;
+    p.len = static_cast<int>(len);
+    return true;
+}
+
+// Gate vectors of one chunk, one token per lane of the calling wave: G log2(e)
+// (chunk-local inclusive prefix sum), beta, and e^{G_L} log2(e)'s exponent.
+template <bool GATE_BF16>
+__device__ __forceinline__ void chunk_gates(const BwdArgs &a, int64_t t0, int len, int h, int lane,
+                                            float &G2, float &bv, float &GL2) {
+    float gv = 0.f;
+    bv = 0.f;
+    if (lane < len) {
+        gv = load_scalar<GATE_BF16>(a.g, (t0 + lane) * a.hv + h);
+        bv = load_scalar<GATE_BF16>(a.beta, (t0 + lane) * a.hv + h);
+    }
+    G2 = wave_inclusive_scan(gv * kLog2e);
+    GL2 = lane63(G2);
+}
+
+// --------------------------------------------------------------------------
+// Per (chunk, v-head): T, w^T and the local dU0.
+// --------------------------------------------------------------------------
+template <int D>
+struct PrepLds {
+    static constexpr int PK = D + 16;   // [64][D] bf16 rows
+    static constexpr int PP = C + 8;    // [64][64] bf16
+    static constexpr int PF = 17;       // [16][16] f32 blocks
+    static constexpr int PD = 24;       // [16][16] bf16 blocks
+    static constexpr int oQ = 0;
+    static constexpr int oK = oQ + C * PK * 2;
+    static constexpr int oO = oK + C * PK * 2;
+    static constexpr int oA = oO + C * PK * 2;        // diag(b) A~, strictly lower, [i][j]
+    static constexpr int oPt = oA + C * PP * 2;       // (scale M o Q K^T)^T, [j][i]
+    static constexpr int oTt = oPt + C * PP * 2;      // (T diag(b e^G))^T, [j][i]
+    static constexpr int oAf = oTt + C * PP * 2;      // f32 diagonal blocks of diag(b) A~
+    static constexpr int oDi = oAf + 4 * 16 * PF * 4; // bf16 inverses of the diagonal blocks of I + diag(b) A~
+    static constexpr int oG = oDi + 4 * 16 * PD * 2;  // f32 [64] x3: G log2(e), b, b e^G
+    static constexpr int bytes = oG + 3 * C * 4;
+};
+
+template <int D, bool IN_BF16, bool GATE_BF16>
+__global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
+    using Ly = PrepLds<D>;
+    constexpr int PK = Ly::PK, PP = Ly::PP, PF = Ly::PF, PD = Ly::PD, NTD = D / 16;
+    extern __shared__ __align__(16) unsigned char lds[];
+    uint16_t *sQ = reinterpret_cast<uint16_t *>(lds + Ly::oQ);
+    uint16_t *sK = reinterpret_cast<uint16_t *>(lds + Ly::oK);
+    uint16_t *sO = reinterpret_cast<uint16_t *>(lds + Ly::oO);
+    uint16_t *sA = reinterpret_cast<uint16_t *>(lds + Ly::oA);
+    uint16_t *sPt = reinterpret_cast<uint16_t *>(lds + Ly::oPt);
+    uint16_t *sTt = reinterpret_cast<uint16_t *>(lds + Ly::oTt);
+    float *sAf = reinterpret_cast<float *>(lds + Ly::oAf);
+    uint16_t *sDi = reinterpret_cast<uint16_t *>(lds + Ly::oDi);
+    float *sG2 = reinterpret_cast<float *>(lds + Ly::oG);
+    float *sB = sG2 + C;
+    float *sBG = sB + C;
+
+    ChunkAt p;
+    if (!chunk_at(a, blockIdx.x, p)) return;
+    const int h = blockIdx.y;
+    const int hk = h / (a.hv / a.hk);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lq = lane >> 4;
+    const int64_t rh = static_cast<int64_t>(blockIdx.x) * a.hv + h;
+
+    stage_rows<D, IN_BF16, kBwdThreads>(sQ, PK, a.q, p.t0, p.len, a.hk, hk, tid);
+    stage_rows<D, IN_BF16, kBwdThreads>(sK, PK, a.k, p.t0, p.len, a.hk, hk, tid);
+    stage_rows<D, IN_BF16, kBwdThreads>(sO, PK, a.dout, p.t0, p.len, a.hv, h, tid);
+    for (int i = tid; i < 2 * C * PP / 8; i += kBwdThreads)   // A and P^T (adjacent): blocks above the diagonal stay zero
+        reinterpret_cast<uint4 *>(sA)[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (wave == 0) {
+        float G2, bv, GL2;
+        chunk_gates<GATE_BF16>(a, p.t0, p.len, h, lane, G2, bv, GL2);
+        sG2[lane] = G2;
+        sB[lane] = bv;
+        sBG[lane] = bv * fast_exp2(G2);
+    }
+    __syncthreads();
+
+    // gated K K^T (strictly lower, times b: A) and Q K^T (lower, times scale:
+    // P, stored transposed), the ten lower 16x16 blocks of each
+    for (int t = wave; t < 20; t += 8) {
+        const bool kk = t < 10;
+        const int tt = kk ? t : t - 10;
+        const int bi = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
+        const int bj = tt - bi * (bi + 1) / 2;
+        const uint16_t *Am = kk ? sK : sQ;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += 32)
+            acc = mfma32(frag_rows(Am, PK, 16 * bi, k0, l16, lq), frag_rows(sK, PK, 16 * bj, k0, l16, lq), acc);
+        const int j = 16 * bj + l16;
+        const float gj = sG2[j];
+        f32x4 pv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * bi + 4 * lq + r;
+            const float e = fast_exp2(sG2[i] - gj);   // used only where j <= i (exponent <= 0)
+            if (kk) {
+                const float v = j < i ? sB[i] * e * acc[r] : 0.f;
+                sA[i * PP + j] = bf16_bits(v);
+                if (bi == bj) sAf[(16 * bi + 4 * lq + r) * PF + l16] = v;
+            } else {
+                pv[r] = j <= i ? a.scale * e * acc[r] : 0.f;
+            }
+        }
+        if (!kk) st4(sPt + j * PP + 16 * bi + 4 * lq, cvt4(pv));
+    }
+    __syncthreads();
+
+    // Diagonal blocks: column l16 of (I + A_bb)^-1 by forward substitution in
+    // fp32 (every 16-lane row of the wave computes the same column).
+    f32x4 dcol = zero4();
+    if (wave < 4) {
+        const int b = wave;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float s = i == l16 ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) s -= sAf[(16 * b + i) * PF + m] * x[m];
+            x[i] = s;
+        }
+        if (lq == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sDi[(16 * b + i) * PD + l16] = bf16_bits(x[i]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dcol[r] = lq == 0 ? x[r] : lq == 1 ? x[4 + r] : lq == 2 ? x[8 + r] : x[12 + r];
+    }
+    __syncthreads();
+
+    // Column block j of T: X_j = D_j, X_i = -D_i sum_{m=j}^{i-1} A_im X_m
+    // (C tiles chained through registers).  T^T goes to memory, (T diag(b e^G))^T to LDS.
+    if (wave < 4) {
+        const int j = wave;
+        f32x4 X[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[i] = i == j ? dcol : zero4();
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+            if (i > j) {
+                f32x4 E = zero4();
+#pragma unroll
+                for (int m = 0; m < 3; ++m)
+                    if (m >= j && m < i)
+                        E = mfma16z(ld4(sA + (16 * i + l16) * PP + 16 * m + 4 * lq), cvt4(X[m]), E);
+                X[i] = -mfma16z(ld4(sDi + (16 * i + l16) * PD + 4 * lq), cvt4(E), zero4());
+            }
+        }
+        uint16_t *tg = a.tmat + rh * (C * C);
+        const float bgj = sBG[16 * j + l16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<bf16x4 *>(tg + (16 * j + l16) * C + 16 * i + 4 * lq) = cvt4(X[i]);
+            st4(sTt + (16 * j + l16) * PP + 16 * i + 4 * lq, cvt4(X[i] * bgj));
+        }
+    }
+    __syncthreads();
+
+    // w = T diag(b e^G) K, stored as w^T [D][64]
+    uint16_t *wg = a.wt + rh * (D * C);
+    for (int t = wave; t < 4 * NTD; t += 8) {
+        const int it = t & 3, dt = t >> 2;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32)
+            acc = mfma32(frag_cols(sTt, PP, 16 * it, k0, l16, lq), frag_cols(sK, PK, 16 * dt, k0, l16, lq), acc);
+        *reinterpret_cast<bf16x4 *>(wg + (16 * dt + l16) * C + 16 * it + 4 * lq) = cvt4(acc);
+    }
+    // dU0 = (scale M o Q K^T)^T dO, in 16x16 tiles (token block, dv tile), lane-major
+    float *ug = a.du + rh * (C * D);
+    for (int t = wave; t < 4 * NTD; t += 8) {
+        const int jt = t & 3, nt = t >> 2;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32)
+            if (k0 + 32 > 16 * jt)
+                acc = mfma32(frag_rows(sPt, PP, 16 * jt, k0, l16, lq), frag_cols(sO, PK, 16 * nt, k0, l16, lq), acc);
+        *reinterpret_cast<f32x4 *>(ug + ((jt * NTD + nt) * 64 + lane) * 4) = acc;
+    }
+}
+
+// --------------------------------------------------------------------------
+// Per (sequence, v-head), chunks in reverse order: the gradient of the state.
+// Wave c owns dv columns [c*D/4, (c+1)*D/4) of dS' (fp32 C tiles, rows dk).
+// --------------------------------------------------------------------------
+template <int D>
+struct ChainLds {
+    static constexpr int PK = D + 16;
+    static constexpr int PW = C + 8;
+    static constexpr int oQ = 0;
+    static constexpr int oK = oQ + C * PK * 2;
+    static constexpr int oO = oK + C * PK * 2;
+    static constexpr int oW = oO + C * PK * 2;     // w^T [D][PW]
+    static constexpr int oG = oW + D * PW * 2;     // f32 [64] x2: scale e^G, e^{G_L - G}; then e^{G_L}
+    static constexpr int bytes = oG + 2 * C * 4 + 16;
+};
+
+template <int D, bool IN_BF16, bool GATE_BF16>
+__global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a) {
+    using Ly = ChainLds<D>;
+    constexpr int PK = Ly::PK, PW = Ly::PW;
+    constexpr int MT = D / 16;    // dk tiles
+    constexpr int NTW = D / 64;   // dv tiles per wave
+    extern __shared__ __align__(16) unsigned char lds[];
+    uint16_t *sQ = reinterpret_cast<uint16_t *>(lds + Ly::oQ);
+    uint16_t *sK = reinterpret_cast<uint16_t *>(lds + Ly::oK);
+    uint16_t *sO = reinterpret_cast<uint16_t *>(lds + Ly::oO);
+    uint16_t *sW = reinterpret_cast<uint16_t *>(lds + Ly::oW);
+    float *sGs = reinterpret_cast<float *>(lds + Ly::oG);
+    float *sLam = sGs + C;
+    float *sGL = sLam + C;
+
+    const int64_t rank = blockIdx.x / a.hv;
+    const int h = static_cast<int>(blockIdx.x % a.hv);
+    const int64_t n = a.order ? static_cast<int64_t>(a.order[rank]) : rank;
+    if (n < 0 || n >= a.n_seq) return;
+    int64_t bos, eos;
+    if (a.cu) {
+        bos = a.cu[n];
+        eos = a.cu[n + 1];
+    } else {
+        bos = n * a.seq_len;
+        eos = bos + a.seq_len;
+    }
+    bos = bos < 0 ? 0 : bos;
+    eos = eos > a.total_tokens ? a.total_tokens : eos;
+    if (eos <= bos) return;   // length-0 segment: reads nothing, writes nothing
+    const int hk = h / (a.hv / a.hk);
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int colw = wave * (D / 4);
+    const int64_t nch = (eos - bos + C - 1) / C;
+    const int64_t off = a.offs ? static_cast<int64_t>(a.offs[n]) : n * ((a.seq_len + C - 1) / C);
+
+    f32x4 dH[MT][NTW];
+    {
+        const int lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
+        const float *src = a.dht ? a.dht + (n * a.hv + h) * D * D : nullptr;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dH[mt][nt][r] = src ? src[(16 * mt + 4 * lq + r) * D + colw + 16 * nt + l16] : 0.f;
+    }
+
+    for (int64_t c = nch - 1; c >= 0; --c) {
+        int lane = tid & 63;   // opaque per iteration: keeps per-lane addresses inside the loop
+        asm volatile("" : "+v"(lane));
+        const int l16 = lane & 15, lq = lane >> 4;
+        const int64_t t0 = bos + C * c;
+        const int len = static_cast<int>(eos - t0 < C ? eos - t0 : C);
+        const int64_t rh = (off + c) * a.hv + h;
+        __syncthreads();   // the previous chunk's reads of LDS are done
+        stage_rows<D, IN_BF16, kChainThreads>(sQ, PK, a.q, t0, len, a.hk, hk, tid);
+        stage_rows<D, IN_BF16, kChainThreads>(sK, PK, a.k, t0, len, a.hk, hk, tid);
+        stage_rows<D, IN_BF16, kChainThreads>(sO, PK, a.dout, t0, len, a.hv, h, tid);
+        {
+            const uint16_t *wg = a.wt + rh * (D * C);
+            for (int i = tid; i < D * C / 8; i += kChainThreads) {
+                const int row = i / (C / 8), col = 8 * (i % (C / 8));
+                *reinterpret_cast<uint4 *>(sW + row * PW + col) = *reinterpret_cast<const uint4 *>(wg + row * C + col);
+            }
+        }
+        if (wave == 0) {
+            float G2, bv, GL2;
+            chunk_gates<GATE_BF16>(a, t0, len, h, lane, G2, bv, GL2);
+            sGs[lane] = a.scale * fast_exp2(G2);
+            sLam[lane] = fast_exp2(GL2 - G2);
+            if (lane == 0) sGL[0] = fast_exp2(GL2);
+        }
+        __syncthreads();
+
+        // dS' of this chunk, for the per-chunk gradient kernel
+        {
+            float *dst = a.dhe + rh * D * D;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        dst[(16 * mt + 4 * lq + r) * D + colw + 16 * nt + l16] = dH[mt][nt][r];
+        }
+
+        // X1 = K dS'
+        f32x4 X1[4][NTW];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) X1[mt][nt] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            bf16x8 bh[NTW];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) bh[nt] = cat(cvt4(dH[2 * kk][nt]), cvt4(dH[2 * kk + 1][nt]));
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const bf16x8 af = frag_rows(sK, PK, 16 * mt, 32 * kk, l16, lq);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) X1[mt][nt] = mfma32(af, bh[nt], X1[mt][nt]);
+            }
+        }
+
+        // dU = dU0 + diag(e^{G_L - G}) X1, completed in place
+        float *ug = a.du + rh * (C * D);
+        f32x4 dU[4][NTW];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                f32x4 *up = reinterpret_cast<f32x4 *>(ug + ((mt * MT + colw / 16 + nt) * 64 + lane) * 4);
+                f32x4 u = *up;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) u[r] += sLam[16 * mt + 4 * lq + r] * X1[mt][nt][r];
+                *up = u;
+                dU[mt][nt] = u;
+            }
+
+        // dS <- e^{G_L} dS' + Q^T diag(scale e^G) dO - w^T dU
+        const float gl = sGL[0];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) dH[mt][nt] = dH[mt][nt] * gl;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 bo[NTW], bu[NTW];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                bf16x8 f = frag_cols(sO, PK, colw + 16 * nt, 32 * kk, l16, lq);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const float x = static_cast<float>(f[s]);
+                    f[s] = static_cast<__bf16>(x * sGs[32 * kk + 16 * (s >> 2) + 4 * lq + (s & 3)]);
+                }
+                bo[nt] = f;
+                bu[nt] = cat(cvt4(-dU[2 * kk][nt]), cvt4(-dU[2 * kk + 1][nt]));
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const bf16x8 aq = frag_cols(sQ, PK, 16 * mt, 32 * kk, l16, lq);
+                const bf16x8 aw = frag_rows(sW, PW, 16 * mt, 32 * kk, l16, lq);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    dH[mt][nt] = mfma32(aq, bo[nt], dH[mt][nt]);
+                    dH[mt][nt] = mfma32(aw, bu[nt], dH[mt][nt]);
+                }
+            }
+        }
+    }
+
+    if (a.dh0) {
+        const int lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
+        float *dst = a.dh0 + (n * a.hv + h) * D * D;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dst[(16 * mt + 4 * lq + r) * D + colw + 16 * nt + l16] = dH[mt][nt][r];
+    }
+}
+
+// --------------------------------------------------------------------------
+// Per (chunk, q/k head), looping over the v-heads of the group: all input
+// gradients of the chunk's tokens.
+// --------------------------------------------------------------------------
+template <int D>
+struct GradLds {
+    static constexpr int PK = D + 16;
+    static constexpr int PP = C + 8;
+    static constexpr int oQ = 0;
+    static constexpr int oK = oQ + C * PK * 2;
+    static constexpr int oO = oK + C * PK * 2;
+    static constexpr int oV = oO + C * PK * 2;        // V [64][PK]; later Zs, dBn, dB [64][PP] each
+    static constexpr int oT = oV + C * PK * 2;        // T^T [64][PP]
+    static constexpr int szVT = (C * PK * 2 + C * PP * 2) > 3 * C * PP * 2 ? (C * PK * 2 + C * PP * 2) : 3 * C * PP * 2;
+    static constexpr int oS = oV + szVT;              // S, later dS' [D][PK]
+    static constexpr int oU = oS + D * PK * 2;        // U [64][PK]
+    static constexpr int oW = oU + C * PK * 2;        // dW [64][PK]
+    static constexpr int oG = oW + C * PK * 2;        // f32 [64] x4: G log2(e), b, e^G, e^{G_L - G}
+    static constexpr int oR = oG + 4 * C * 4;         // f32 [8][64] x2: per-wave row sums for dG and db
+    static constexpr int oX = oR + 2 * 8 * C * 4;     // f32 [8] x2: per-wave sums of <dS', S> and the lambda k.(U dS'^T) terms; e^{G_L}
+    static constexpr int bytes = oX + 2 * 8 * 4 + 16;
+};
+
+template <int D, bool IN_BF16, bool GATE_BF16>
+__global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
+    using Ly = GradLds<D>;
+    constexpr int PK = Ly::PK, PP = Ly::PP, NTD = D / 16;
+    extern __shared__ __align__(16) unsigned char lds[];
+    uint16_t *sQ = reinterpret_cast<uint16_t *>(lds + Ly::oQ);
+    uint16_t *sK = reinterpret_cast<uint16_t *>(lds + Ly::oK);
+    uint16_t *sO = reinterpret_cast<uint16_t *>(lds + Ly::oO);
+    uint16_t *sV = reinterpret_cast<uint16_t *>(lds + Ly::oV);
+    uint16_t *sT = reinterpret_cast<uint16_t *>(lds + Ly::oT);
+    uint16_t *sZs = reinterpret_cast<uint16_t *>(lds + Ly::oV);
+    uint16_t *sBn = sZs + C * PP;
+    uint16_t *sBb = sBn + C * PP;
+    uint16_t *sS = reinterpret_cast<uint16_t *>(lds + Ly::oS);
+    uint16_t *sU = reinterpret_cast<uint16_t *>(lds + Ly::oU);
+    uint16_t *sDW = reinterpret_cast<uint16_t *>(lds + Ly::oW);
+    float *sG2 = reinterpret_cast<float *>(lds + Ly::oG);
+    float *sB = sG2 + C;
+    float *sGam = sB + C;
+    float *sLam = sGam + C;
+    float *sRG = reinterpret_cast<float *>(lds + Ly::oR);
+    float *sRB = sRG + 8 * C;
+    float *sXd = reinterpret_cast<float *>(lds + Ly::oX);
+    float *sXl = sXd + 8;
+    float *sGL = sXl + 8;
+
+    ChunkAt p;
+    if (!chunk_at(a, blockIdx.x, p)) return;
+    const int hk = blockIdx.y;
+    const int G = a.hv / a.hk;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const bool colwave = wave < NTD;   // owns column tile `wave` in the column-split phases
+    const int nt = wave;
+
+    stage_rows<D, IN_BF16, kBwdThreads>(sQ, PK, a.q, p.t0, p.len, a.hk, hk, tid);
+    stage_rows<D, IN_BF16, kBwdThreads>(sK, PK, a.k, p.t0, p.len, a.hk, hk, tid);
+
+    f32x4 accQ[4], accK[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) accQ[mt] = accK[mt] = zero4();
+
+    for (int hh = 0; hh < G; ++hh) {
+        // lane indices re-derived opaquely in every iteration, so that the
+        // compiler does not hoist (and spill) per-lane addresses out of the loop
+        int lane = tid & 63;
+        asm volatile("" : "+v"(lane));
+        const int l16 = lane & 15, lq = lane >> 4;
+        const int h = hk * G + hh;
+        const int64_t rh = static_cast<int64_t>(blockIdx.x) * a.hv + h;
+        const float *Sg = p.c > 0 ? a.hck + (rh - a.hv) * D * D
+                                  : (a.h0 ? a.h0 + (p.n * a.hv + h) * D * D : nullptr);
+        __syncthreads();   // the previous v-head's reads of LDS are done
+        stage_rows<D, IN_BF16, kBwdThreads>(sV, PK, a.v, p.t0, p.len, a.hv, h, tid);
+        stage_rows<D, IN_BF16, kBwdThreads>(sO, PK, a.dout, p.t0, p.len, a.hv, h, tid);
+        for (int i = tid; i < D * D / 4; i += kBwdThreads) {
+            const int row = i / (D / 4), col = 4 * (i % (D / 4));
+            const f32x4 v = Sg ? *reinterpret_cast<const f32x4 *>(Sg + row * D + col) : zero4();
+            st4(sS + row * PK + col, cvt4(v));
+        }
+        {
+            const uint16_t *tg = a.tmat + rh * (C * C);
+            for (int i = tid; i < C * C / 8; i += kBwdThreads) {
+                const int row = i / (C / 8), col = 8 * (i % (C / 8));
+                *reinterpret_cast<uint4 *>(sT + row * PP + col) = *reinterpret_cast<const uint4 *>(tg + row * C + col);
+            }
+        }
+        if (wave == 0) {
+            float G2, bv, GL2;
+            chunk_gates<GATE_BF16>(a, p.t0, p.len, h, lane, G2, bv, GL2);
+            sG2[lane] = G2;
+            sB[lane] = bv;
+            sGam[lane] = fast_exp2(G2);
+            sLam[lane] = fast_exp2(GL2 - G2);
+            if (lane == 0) sGL[0] = fast_exp2(GL2);
+        }
+        __syncthreads();
+
+        // X = K S, R~ = V - e^G X, U = T diag(b) R~, dW = T^T dU, dV = b dW (dv tile nt)
+        if (colwave) {
+            f32x4 Rt[4], U[4], dW[4];
+            bf16x4 wb[4], ub[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) Rt[mt] = zero4();
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const bf16x8 bs = frag_cols(sS, PK, 16 * nt, 32 * kk, l16, lq);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) Rt[mt] = mfma32(frag_rows(sK, PK, 16 * mt, 32 * kk, l16, lq), bs, Rt[mt]);
+            }
+            const float *ug = a.du + rh * (C * D);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 w;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * mt + 4 * lq + r;
+                    Rt[mt][r] = bf16_to_f(sV[i * PK + 16 * nt + l16]) - sGam[i] * Rt[mt][r];   // R~ = V - e^G X
+                    w[r] = sB[i] * Rt[mt][r];
+                }
+                wb[mt] = cvt4(w);
+                ub[mt] = cvt4(*reinterpret_cast<const f32x4 *>(ug + ((mt * NTD + nt) * 64 + lane) * 4));
+                U[mt] = dW[mt] = zero4();
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 bw = cat(wb[2 * kk], wb[2 * kk + 1]);
+                const bf16x8 bu = cat(ub[2 * kk], ub[2 * kk + 1]);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    U[mt] = mfma32(frag_cols(sT, PP, 16 * mt, 32 * kk, l16, lq), bw, U[mt]);
+                    dW[mt] = mfma32(frag_rows(sT, PP, 16 * mt, 32 * kk, l16, lq), bu, dW[mt]);
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                float pb[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * mt + 4 * lq + r;
+                    if (i < p.len) store_elem<IN_BF16>(a.dv, ((p.t0 + i) * a.hv + h) * D + 16 * nt + l16, sB[i] * dW[mt][r]);
+                    sU[i * PK + 16 * nt + l16] = bf16_bits(U[mt][r]);
+                    sDW[i * PK + 16 * nt + l16] = bf16_bits(dW[mt][r]);
+                    pb[r] = row_sum16(dW[mt][r] * Rt[mt][r]);
+                }
+                if (l16 == 15) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sRB[wave * C + 16 * mt + 4 * lq + r] = pb[r];
+                }
+            }
+        }
+        __syncthreads();
+
+        // dQ1 = dO S^T, dK1 = dW S^T (dk tile nt)
+        f32x4 dQt[4], dK1[4];   // dQt: scale e^G dO S^T, then + Zs K
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) dQt[mt] = dK1[mt] = zero4();
+        if (colwave) {
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const bf16x8 bs = frag_rows(sS, PK, 16 * nt, 32 * kk, l16, lq);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    dQt[mt] = mfma32(frag_rows(sO, PK, 16 * mt, 32 * kk, l16, lq), bs, dQt[mt]);
+                    dK1[mt] = mfma32(frag_rows(sDW, PK, 16 * mt, 32 * kk, l16, lq), bs, dK1[mt]);
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dQt[mt][r] *= a.scale * sGam[16 * mt + 4 * lq + r];
+        }
+        __syncthreads();   // S, V and T are no longer read
+
+        // dS' into LDS (and the fp32 <dS', S>); Zs, dBn, dB
+        {
+            const float *dg_ = a.dhe + rh * D * D;
+            float part = 0.f;
+            for (int i = tid; i < D * D / 4; i += kBwdThreads) {
+                const int row = i / (D / 4), col = 4 * (i % (D / 4));
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(dg_ + row * D + col);
+                if (Sg) {
+                    const f32x4 s = *reinterpret_cast<const f32x4 *>(Sg + row * D + col);
+                    part += v[0] * s[0] + v[1] * s[1] + v[2] * s[2] + v[3] * s[3];
+                }
+                st4(sS + row * PK + col, cvt4(v));
+            }
+            part = lane63(wave_inclusive_scan(part));
+            if (lane == 0) sXd[wave] = part;
+        }
+        for (int t = wave; t < 16; t += 8) {
+            const int bi = t >> 2, bj = t & 3;
+            f32x4 z0 = zero4(), z1 = zero4();
+            if (bi >= bj) {
+#pragma unroll
+                for (int kk = 0; kk < D / 32; ++kk) {
+                    const bf16x8 bu = frag_rows(sU, PK, 16 * bj, 32 * kk, l16, lq);
+                    z0 = mfma32(frag_rows(sO, PK, 16 * bi, 32 * kk, l16, lq), bu, z0);
+                    z1 = mfma32(frag_rows(sDW, PK, 16 * bi, 32 * kk, l16, lq), bu, z1);
+                }
+            }
+            const int j = 16 * bj + l16;
+            const float gj = sG2[j];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * bi + 4 * lq + r;
+                const float e = fast_exp2(sG2[i] - gj);   // used only where j <= i
+                const float zs = j <= i ? a.scale * e * z0[r] : 0.f;
+                const float bn = j < i ? -e * z1[r] : 0.f;
+                sZs[i * PP + j] = bf16_bits(zs);
+                sBn[i * PP + j] = bf16_bits(bn);
+                sBb[i * PP + j] = bf16_bits(sB[i] * bn);
+            }
+        }
+        __syncthreads();
+
+        // dK5 = U dS'^T, Zs K, dBn K, Zs^T Q, dB^T K (dk tile nt); combine
+        if (colwave) {
+            // Kc: the column uses of k, lambda (U dS'^T) + Zs^T Q + dB^T K
+            f32x4 Kc[4], Yb[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) Kc[mt] = Yb[mt] = zero4();
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const bf16x8 bd = frag_rows(sS, PK, 16 * nt, 32 * kk, l16, lq);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) Kc[mt] = mfma32(frag_rows(sU, PK, 16 * mt, 32 * kk, l16, lq), bd, Kc[mt]);
+            }
+            float lastp = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * mt + 4 * lq + r;
+                    Kc[mt][r] *= sLam[i];
+                    lastp += bf16_to_f(sK[i * PK + 16 * nt + l16]) * Kc[mt][r];
+                }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 bk = frag_cols(sK, PK, 16 * nt, 32 * kk, l16, lq);
+                const bf16x8 bq = frag_cols(sQ, PK, 16 * nt, 32 * kk, l16, lq);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    dQt[mt] = mfma32(frag_rows(sZs, PP, 16 * mt, 32 * kk, l16, lq), bk, dQt[mt]);
+                    Yb[mt] = mfma32(frag_rows(sBn, PP, 16 * mt, 32 * kk, l16, lq), bk, Yb[mt]);
+                    Kc[mt] = mfma32(frag_cols(sZs, PP, 16 * mt, 32 * kk, l16, lq), bq, Kc[mt]);
+                    Kc[mt] = mfma32(frag_cols(sBb, PP, 16 * mt, 32 * kk, l16, lq), bk, Kc[mt]);
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                float pg[4], pb[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * mt + 4 * lq + r;
+                    const int col = 16 * nt + l16;
+                    const float qv = bf16_to_f(sQ[i * PK + col]), kv = bf16_to_f(sK[i * PK + col]);
+                    const float bt = sB[i];
+                    const float dq = dQt[mt][r];
+                    const float dkr = bt * (Yb[mt][r] - sGam[i] * dK1[mt][r]);
+                    const float dkc = Kc[mt][r];
+                    accQ[mt][r] += dq;
+                    accK[mt][r] += dkr + dkc;
+                    pg[r] = row_sum16(qv * dq + kv * (dkr - dkc));
+                    pb[r] = row_sum16(kv * Yb[mt][r]);
+                }
+                if (l16 == 15) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 16 * mt + 4 * lq + r;
+                        sRG[wave * C + i] = pg[r];
+                        sRB[wave * C + i] += pb[r];
+                    }
+                }
+            }
+            lastp = lane63(wave_inclusive_scan(lastp));
+            if (lane == 0) sXl[wave] = lastp;
+        }
+        __syncthreads();
+
+        // dg: reverse prefix sums of dG within the chunk; dbeta
+        if (wave == 0) {
+            float dG = 0.f, db = 0.f;
+            for (int w = 0; w < NTD; ++w) {
+                dG += sRG[w * C + lane];
+                db += sRB[w * C + lane];
+            }
+            if (lane == 63) {
+                float dot = 0.f, kl = 0.f;
+                for (int w = 0; w < 8; ++w) dot += sXd[w];
+                for (int w = 0; w < NTD; ++w) kl += sXl[w];
+                dG += sGL[0] * dot + kl;
+            }
+            const float inc = wave_inclusive_scan(dG);
+            const float dg = lane63(inc) - inc + dG;
+            if (lane < p.len) {
+                a.dg[(p.t0 + lane) * a.hv + h] = dg;
+                a.dbeta[(p.t0 + lane) * a.hv + h] = db;
+            }
+        }
+    }
+
+    // dq, dk summed over the v-heads of this q/k head
+    const int lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
+    if (colwave) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * mt + 4 * lq + r;
+                if (i < p.len) {
+                    const int64_t o = ((p.t0 + i) * a.hk + hk) * D + 16 * nt + l16;
+                    store_elem<IN_BF16>(a.dq, o, accQ[mt][r]);
+                    store_elem<IN_BF16>(a.dk, o, accK[mt][r]);
+                }
+            }
+    }
+}
+
+template <typename K>
+hipError_t launch_with_lds(K kern, dim3 grid, dim3 block, int lds, hipStream_t stream, const BwdArgs &a) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, block, lds, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, bool IN_BF16, bool GATE_BF16>
+hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
+    const unsigned rows = static_cast<unsigned>(a.rows);
+    hipError_t e = launch_with_lds(gdr_bwd_prep_kernel<D, IN_BF16, GATE_BF16>, dim3(rows, a.hv),
+                                   dim3(kBwdThreads), PrepLds<D>::bytes, stream, a);
+    if (e != hipSuccess) return e;
+    e = launch_with_lds(gdr_bwd_chain_kernel<D, IN_BF16, GATE_BF16>,
+                        dim3(static_cast<unsigned>(a.n_seq * a.hv)), dim3(kChainThreads),
+                        ChainLds<D>::bytes, stream, a);
+    if (e != hipSuccess) return e;
+    return launch_with_lds(gdr_bwd_grads_kernel<D, IN_BF16, GATE_BF16>, dim3(rows, a.hk),
+                           dim3(kBwdThreads), GradLds<D>::bytes, stream, a);
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
+    if (a.in_bf16) return a.gate_bf16 ? launch_bwd_t<D, true, true>(a, s) : launch_bwd_t<D, true, false>(a, s);
+    return a.gate_bf16 ? launch_bwd_t<D, false, true>(a, s) : launch_bwd_t<D, false, false>(a, s);
+}
+
+static_assert(GradLds<128>::bytes <= 160 * 1024, "gradient kernel LDS");
+static_assert(PrepLds<128>::bytes <= 160 * 1024, "prep kernel LDS");
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
+    if (a.n_seq == 0 || a.hv == 0 || a.rows == 0) return hipSuccess;
+    return a.d == 64 ? launch_bwd_d<64>(a, stream) : launch_bwd_d<128>(a, stream);
+}
+
+}  // namespace gdr

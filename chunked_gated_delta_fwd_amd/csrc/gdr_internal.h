@@ -13,7 +13,7 @@ struct FwdArgs {
     const int32_t *cu;      // NULL: fixed-length rows
     const int32_t *order;   // NULL: natural order
     const float *h0;        // NULL: zero state
-    void *o;
+    void *o;                // NULL: not written
     float *ht;              // NULL: not written
     int64_t n_seq;          // N
     int64_t seq_len;        // T per row when cu == NULL
@@ -65,6 +65,32 @@ hipError_t launch_cumsum(const void *g, int gate_bf16, const int32_t *cu,
                          const int32_t *chunk_map, int64_t nt_max, int64_t n_rows,
                          int64_t seq_len, int64_t total_tokens, int32_t heads, float *G,
                          hipStream_t stream);
+
+// Everything the backward kernels need, already validated on the host.  The
+// forward recompute (states after every chunk, into hck) is launched first by
+// the caller with the forward kernel.
+struct BwdArgs {
+    const void *q, *k, *v, *g, *beta, *dout;
+    const int32_t *cu;      // NULL: fixed-length rows
+    const int32_t *map;     // chunk row -> (sequence, chunk) pairs; NULL for fixed-length rows
+    const int32_t *offs;    // first chunk row of each sequence; NULL for fixed-length rows
+    const int32_t *order;   // start order of the reverse chain; NULL: natural
+    const float *h0;        // NULL: zero initial state
+    const float *dht;       // NULL: zero gradient of the final state
+    const float *hck;       // forward state after every chunk [rows, Hv, d, d]
+    uint16_t *tmat;         // per chunk: T^T, T = (I + diag(b) A~)^-1, bf16 [rows, Hv, 64, 64]
+    uint16_t *wt;           // per chunk: w^T, w = T diag(b e^G) K, bf16 [rows, Hv, d, 64]
+    float *du;              // per chunk: local dU, then dU, [rows, Hv, 64 * d] in 16x16 tiles, lane-major
+    float *dhe;             // per chunk: gradient of the state at its end [rows, Hv, d, d]
+    void *dq, *dk, *dv;     // dtype of q
+    float *dg, *dbeta;
+    float *dh0;             // NULL: not written
+    int64_t n_seq, seq_len, total_tokens, rows;
+    int32_t hk, hv, d, in_bf16, gate_bf16;
+    float scale;
+};
+// Per-chunk preparation, reverse chain over chunks, per-chunk gradients.
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 
 hipError_t launch_selftest_mfma(const uint16_t *a, const uint16_t *b, float *c,
                                 hipStream_t stream);

@@ -144,6 +144,46 @@ int gdr_chunk_fwd_checkpoints(const gdr_tensor *q, const gdr_tensor *k, const gd
                               const gdr_tensor *h_chunks, float scale, hipStream_t stream);
 
 /*
+ * gdr_chunk_bwd - backward pass of gdr_chunk_fwd: the gradients of the scalar
+ * loss L given dL/do and dL/dht, for every input.  The pages discuss the
+ * backward as the other half of the kernel family ("Findings from integrating
+ * FlashQLA's Blackwell GDN kernels into a JAX trainer", opening summary and
+ * items 3-4) without giving its formula; these are the exact derivatives of
+ * the recurrence above, evaluated in chunks of 64 tokens.
+ *
+ *   q, k, v, g, beta, cu_seqlens, h0   the forward inputs, as in gdr_chunk_fwd
+ *   do          [B, T, Hv, dv]   dL/do, dtype of q
+ *   dht         [N, Hv, dk, dv]  f32 dL/dht, or NULL for zero
+ *   dq, dk      [B, T, Hk, dk]   out, dtype of q (summed over the Hv / Hk
+ *                                v-heads that share each q/k head)
+ *   dv          [B, T, Hv, dv]   out, dtype of q
+ *   dg, dbeta   [B, T, Hv]       out, f32 (dg: gradient of the log-gate)
+ *   dh0         [N, Hv, dk, dv]  out, f32, or NULL (not written); written also
+ *                                when h0 is NULL (the gradient of the zero state)
+ *   scale       the forward's output scale.
+ *
+ * Rows of tokens outside every segment are not written; length-0 segments
+ * read nothing and write nothing (their dh0 rows keep their bytes).  The
+ * gradient outputs must not overlap any input or each other.
+ *
+ * Work: the forward states after every chunk are recomputed (the forward
+ * kernel, without o), then three kernels run: a per-chunk preparation, the
+ * reverse pass over the chunks of each sequence, and the per-chunk gradients.
+ * Numerics: bf16 MFMA operands, fp32 accumulation and fp32 state gradients.
+ *
+ * Workspace: stream-ordered, from the library's pool (see gdr_chunk_fwd), of
+ * R * Hv * (8 d^2 + 384 d + 8192) bytes plus 4 (2N + 1 + 2R) for the
+ * chunk indices, R = ceil(T/64) + N with cu_seqlens else B * ceil(T/64).
+ * About 6.3 GB for 65536 tokens, 32 v-heads, d = 128.  Errors as
+ * gdr_chunk_fwd, with GDR_ENOMEM when the workspace cannot be obtained.
+ */
+int gdr_chunk_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
+                  const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
+                  const gdr_tensor *dout, const gdr_tensor *dht, const gdr_tensor *dq, const gdr_tensor *dk,
+                  const gdr_tensor *dv, const gdr_tensor *dg, const gdr_tensor *dbeta, const gdr_tensor *dh0,
+                  float scale, hipStream_t stream);
+
+/*
  * gdr_decode_step - one token of the same recurrence for each of B sequences:
  * the decode step that follows this forward pass in inference (the pages'
  * inference surface keeps a decode module beside the prefill, "feat(cake_kda):
