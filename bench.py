@@ -58,6 +58,17 @@ def flops_min(dk: int, dv: int, r: int) -> float:
     return kk + qk + tri_apply + inv + state + pv
 
 
+def flops_bwd(dk: int, dv: int) -> int:
+    """Backward flops per (token, v-head), every 64-wide block counted in full:
+    the per-chunk preparation (K K^T, Q K^T, w = T K, dU0 = P^T dO), the reverse
+    chain (K dS', Q^T dO, w^T dU) and the per-chunk gradients (K S, U = T W,
+    T^T dU, dO S^T, dW S^T, U dS'^T, dO U^T, dW U^T and four 64-deep products
+    with K or Q), plus the forward recompute (flops_chunk)."""
+    state = 8 * 2 * dk * dv                  # eight products over a full state, per token
+    intra = 2 * CHUNK * (7 * dk + 5 * dv)    # twelve 64 x 64 x d products, per token
+    return state + intra + flops_chunk(dk, dv)
+
+
 def bytes_alg(T: int, N: int, hk: int, hv: int, dk: int, dv: int, in_bytes: int, gate_bytes: int) -> int:
     """Every input read once and every output written once."""
     per_tok = hk * 2 * dk * in_bytes + hv * (2 * dv * in_bytes + 2 * gate_bytes)
@@ -79,6 +90,9 @@ def parse():
     ap.add_argument("--decode", type=int, default=0, metavar="B",
                     help="time gdr_decode_step for B sequences with the workload's heads "
                          "(one token each, state in place), against the HBM roofline")
+    ap.add_argument("--backward", action="store_true",
+                    help="time gdr_chunk_bwd (forward recompute and all gradients) for the workload, "
+                         "against the MFMA roofline of the backward flops")
     ap.add_argument("--checkpoints", action="store_true",
                     help="time gdr_chunk_fwd_checkpoints (state after every chunk written); "
                          "reported against the HBM roofline")
@@ -129,7 +143,18 @@ def main():
     torch.cuda.synchronize()
 
     nt_chunks = sum((L + CHUNK - 1) // CHUNK for L in d["lengths"])
-    if args.checkpoints:
+    if args.backward:
+        import gdr_inputs
+        gr = gdr_inputs.generate_grads(d, seed=w.seed + 7)
+        do, dht = put(gr["do"], dt), put(gr["dht"], torch.float32)
+        bufs = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                    dg=torch.empty((B, T, w.hv), dtype=torch.float32, device=dev),
+                    dbeta=torch.empty((B, T, w.hv), dtype=torch.float32, device=dev),
+                    dh0=torch.empty((N, w.hv, w.dk, w.dv), dtype=torch.float32, device=dev))
+
+        def step():
+            gdr.chunk_bwd(q, k, v, g, beta, do, cu, h0, dht, scale=d["scale"], **bufs)
+    elif args.checkpoints:
         rows = ((T + CHUNK - 1) // CHUNK + N) if cu is not None else B * ((T + CHUNK - 1) // CHUNK)
         hck = torch.empty((rows, w.hv, w.dk, w.dv), dtype=torch.float32, device=dev)
 
@@ -197,6 +222,17 @@ def main():
                 "frac": nbytes / (launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
         "cpu_baseline": None,
     }
+    if args.backward:
+        fb = flops_bwd(w.dk, w.dv) * tokens * w.hv
+        out["config"]["backward"] = True
+        out["roofline"] = {"bound": "mfma", "achieved": fb / (launch_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": fb / (launch_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                           "traffic": None,
+                           "kernel": "gdr_chunk_bwd: gdr_prepare_kernel, gdr_fwd_kernel<checkpoints>, "
+                                     "gdr_bwd_prep_kernel, gdr_bwd_chain_kernel, gdr_bwd_grads_kernel",
+                           "flops_per_launch": fb, "launch_ms": launch_ms}
+        out.pop("mfma_frac_fmin")
+        out.pop("hbm")
     if args.checkpoints:
         # the same call plus 4*dk*dv bytes written per (chunk, v-head): HBM bound
         ck_bytes = nt_chunks * w.hv * w.dk * w.dv * 4
