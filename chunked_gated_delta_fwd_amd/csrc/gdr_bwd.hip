@@ -97,6 +97,38 @@ __device__ __forceinline__ void stage_rows(uint16_t *dst, int pitch, const void 
     }
 }
 
+// The same rows into registers, 16 bytes of bf16 per piece, through a buffer
+// resource that ends at the last row (rows from len on read as zero).
+template <int D, bool BF16, int NP, int NT>
+__device__ __forceinline__ void fetch_rows(v4u32 (&dst)[NP], const void *src, int64_t t0, int len, int heads,
+                                           int head, int tid) {
+    constexpr int PR = D / 8, ES = BF16 ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t r = chunk_rsrc(
+        reinterpret_cast<const unsigned char *>(src) + ((t0 * heads + head) * D) * ES,
+        static_cast<uint32_t>(len * heads * D * ES));
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        const int i = tid + j * NT, row = i / PR, col = 8 * (i % PR);
+        dst[j] = __builtin_bit_cast(v4u32, buf_load8<BF16>(r, static_cast<uint32_t>((row * heads * D + col) * ES)));
+    }
+}
+
+// NP consecutive 16-byte pieces per thread of a contiguous block, strided by NT threads.
+template <int NP, int NT>
+__device__ __forceinline__ void fetch_block(v4u32 (&dst)[NP], const uint16_t *src, int tid) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) dst[j] = *reinterpret_cast<const v4u32 *>(src + 8 * (tid + j * NT));
+}
+// This wave's dU0 tiles (16x16, lane-major) of dv tiles ct .. ct+NTW-1.
+template <int MT, int NTW>
+__device__ __forceinline__ void fetch_tiles(f32x4 (&dst)[4][NTW], const float *src, int ct, int lane) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+            dst[mt][nt] = *reinterpret_cast<const f32x4 *>(src + ((mt * MT + ct + nt) * 64 + lane) * 4);
+}
+
 // Which sequence and chunk a chunk row belongs to.
 struct ChunkAt {
     int64_t n, c, t0;
@@ -150,24 +182,27 @@ template <int D>
 struct PrepLds {
     static constexpr int PK = D + 16;   // [64][D] bf16 rows
     static constexpr int PP = C + 8;    // [64][64] bf16
-    static constexpr int PF = 17;       // [16][16] f32 blocks
     static constexpr int PD = 24;       // [16][16] bf16 blocks
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + C * PK * 2;
     static constexpr int oO = oK + C * PK * 2;
     static constexpr int oA = oO + C * PK * 2;        // diag(b) A~, strictly lower, [i][j]
     static constexpr int oPt = oA + C * PP * 2;       // (scale M o Q K^T)^T, [j][i]
-    static constexpr int oTt = oPt + C * PP * 2;      // (T diag(b e^G))^T, [j][i]
-    static constexpr int oAf = oTt + C * PP * 2;      // f32 diagonal blocks of diag(b) A~
-    static constexpr int oDi = oAf + 4 * 16 * PF * 4; // bf16 inverses of the diagonal blocks of I + diag(b) A~
-    static constexpr int oG = oDi + 4 * 16 * PD * 2;  // f32 [64] x3: G log2(e), b, b e^G
-    static constexpr int bytes = oG + 3 * C * 4;
+    static constexpr int oG = oPt + C * PP * 2;       // f32 [64] x3: G log2(e), b, b e^G
+    static constexpr int base = oG + 3 * C * 4;
+    // (T diag(b e^G))^T [j][i] and the bf16 inverses of the diagonal blocks of
+    // I + diag(b) A~: in q's rows, dead once Q K^T is formed, when they fit
+    static constexpr int alias = C * PP * 2 + 4 * 16 * PD * 2;
+    static constexpr bool in_q = alias <= C * PK * 2;
+    static constexpr int oTt = in_q ? oQ : base;
+    static constexpr int oDi = oTt + C * PP * 2;
+    static constexpr int bytes = in_q ? base : base + alias;
 };
 
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     using Ly = PrepLds<D>;
-    constexpr int PK = Ly::PK, PP = Ly::PP, PF = Ly::PF, PD = Ly::PD, NTD = D / 16;
+    constexpr int PK = Ly::PK, PP = Ly::PP, PD = Ly::PD, NTD = D / 16;
     extern __shared__ __align__(16) unsigned char lds[];
     uint16_t *sQ = reinterpret_cast<uint16_t *>(lds + Ly::oQ);
     uint16_t *sK = reinterpret_cast<uint16_t *>(lds + Ly::oK);
@@ -175,7 +210,6 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     uint16_t *sA = reinterpret_cast<uint16_t *>(lds + Ly::oA);
     uint16_t *sPt = reinterpret_cast<uint16_t *>(lds + Ly::oPt);
     uint16_t *sTt = reinterpret_cast<uint16_t *>(lds + Ly::oTt);
-    float *sAf = reinterpret_cast<float *>(lds + Ly::oAf);
     uint16_t *sDi = reinterpret_cast<uint16_t *>(lds + Ly::oDi);
     float *sG2 = reinterpret_cast<float *>(lds + Ly::oG);
     float *sB = sG2 + C;
@@ -222,9 +256,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
             const int i = 16 * bi + 4 * lq + r;
             const float e = fast_exp2(sG2[i] - gj);   // used only where j <= i (exponent <= 0)
             if (kk) {
-                const float v = j < i ? sB[i] * e * acc[r] : 0.f;
-                sA[i * PP + j] = bf16_bits(v);
-                if (bi == bj) sAf[(16 * bi + 4 * lq + r) * PF + l16] = v;
+                sA[i * PP + j] = bf16_bits(j < i ? sB[i] * e * acc[r] : 0.f);
             } else {
                 pv[r] = j <= i ? a.scale * e * acc[r] : 0.f;
             }
@@ -234,7 +266,8 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     __syncthreads();
 
     // Diagonal blocks: column l16 of (I + A_bb)^-1 by forward substitution in
-    // fp32 (every 16-lane row of the wave computes the same column).
+    // fp32 on the bf16 block (every 16-lane row of the wave computes the same
+    // column).
     f32x4 dcol = zero4();
     if (wave < 4) {
         const int b = wave;
@@ -243,7 +276,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i) {
             float s = i == l16 ? 1.f : 0.f;
 #pragma unroll
-            for (int m = 0; m < i; ++m) s -= sAf[(16 * b + i) * PF + m] * x[m];
+            for (int m = 0; m < i; ++m) s -= bf16_to_f(sA[(16 * b + i) * PP + 16 * b + m]) * x[m];
             x[i] = s;
         }
         if (lq == 0) {
@@ -294,7 +327,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
         *reinterpret_cast<bf16x4 *>(wg + (16 * dt + l16) * C + 16 * it + 4 * lq) = cvt4(acc);
     }
     // dU0 = (scale M o Q K^T)^T dO, in 16x16 tiles (token block, dv tile), lane-major
-    float *ug = a.du + rh * (C * D);
+    float *ug = a.du0 + rh * (C * D);
     for (int t = wave; t < 4 * NTD; t += 8) {
         const int jt = t & 3, nt = t >> 2;
         f32x4 acc = zero4();
@@ -326,8 +359,11 @@ template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a) {
     using Ly = ChainLds<D>;
     constexpr int PK = Ly::PK, PW = Ly::PW;
-    constexpr int MT = D / 16;    // dk tiles
-    constexpr int NTW = D / 64;   // dv tiles per wave
+    constexpr int MT = D / 16;                        // dk tiles (and dv tiles)
+    constexpr int NTW = D / 64;                       // dv tiles per wave
+    constexpr int PR = D / 8;                         // 16-byte pieces per q / k / dO row
+    constexpr int NQ = C * PR / kChainThreads;        // such pieces per thread
+    constexpr int NW = D * (C / 8) / kChainThreads;   // 16-byte pieces of w^T per thread
     extern __shared__ __align__(16) unsigned char lds[];
     uint16_t *sQ = reinterpret_cast<uint16_t *>(lds + Ly::oQ);
     uint16_t *sK = reinterpret_cast<uint16_t *>(lds + Ly::oK);
@@ -358,6 +394,28 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
     const int64_t nch = (eos - bos + C - 1) / C;
     const int64_t off = a.offs ? static_cast<int64_t>(a.offs[n]) : n * ((a.seq_len + C - 1) / C);
 
+    // Registers of the chunk being fetched while the previous one is processed:
+    // rows of q, k and dO, w^T, this lane's gate (wave 0); then this wave's
+    // dU0 tiles, fetched once the current ones are used.
+    v4u32 pq[NQ], pk[NQ], po[NQ], pw[NW];
+    float pg = 0.f;
+    f32x4 pu[4][NTW];
+#define GDR_FETCH(cc)                                                                                  \
+    {                                                                                                  \
+        const int64_t t0_ = bos + C * (cc);                                                            \
+        const int len_ = static_cast<int>(eos - t0_ < C ? eos - t0_ : C);                              \
+        fetch_rows<D, IN_BF16, NQ, kChainThreads>(pq, a.q, t0_, len_, a.hk, hk, tid);                  \
+        fetch_rows<D, IN_BF16, NQ, kChainThreads>(pk, a.k, t0_, len_, a.hk, hk, tid);                  \
+        fetch_rows<D, IN_BF16, NQ, kChainThreads>(po, a.dout, t0_, len_, a.hv, h, tid);                \
+        fetch_block<NW, kChainThreads>(pw, a.wt + ((off + (cc)) * a.hv + h) * (D * C), tid);           \
+        const int ln_ = tid & 63;                                                                      \
+        if (wave == 0) pg = ln_ < len_ ? load_scalar<GATE_BF16>(a.g, (t0_ + ln_) * a.hv + h) : 0.f;   \
+    }
+#define GDR_FETCH_DU0(cc)                                                                              \
+    {                                                                                                  \
+        fetch_tiles<MT, NTW>(pu, a.du0 + ((off + (cc)) * a.hv + h) * (C * D), colw / 16, tid & 63);   \
+    }
+
     f32x4 dH[MT][NTW];
     {
         const int lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
@@ -370,44 +428,47 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
                 for (int r = 0; r < 4; ++r)
                     dH[mt][nt][r] = src ? src[(16 * mt + 4 * lq + r) * D + colw + 16 * nt + l16] : 0.f;
     }
+    GDR_FETCH(nch - 1)
+    GDR_FETCH_DU0(nch - 1)
 
     for (int64_t c = nch - 1; c >= 0; --c) {
         int lane = tid & 63;   // opaque per iteration: keeps per-lane addresses inside the loop
         asm volatile("" : "+v"(lane));
         const int l16 = lane & 15, lq = lane >> 4;
-        const int64_t t0 = bos + C * c;
-        const int len = static_cast<int>(eos - t0 < C ? eos - t0 : C);
         const int64_t rh = (off + c) * a.hv + h;
         __syncthreads();   // the previous chunk's reads of LDS are done
-        stage_rows<D, IN_BF16, kChainThreads>(sQ, PK, a.q, t0, len, a.hk, hk, tid);
-        stage_rows<D, IN_BF16, kChainThreads>(sK, PK, a.k, t0, len, a.hk, hk, tid);
-        stage_rows<D, IN_BF16, kChainThreads>(sO, PK, a.dout, t0, len, a.hv, h, tid);
-        {
-            const uint16_t *wg = a.wt + rh * (D * C);
-            for (int i = tid; i < D * C / 8; i += kChainThreads) {
-                const int row = i / (C / 8), col = 8 * (i % (C / 8));
-                *reinterpret_cast<uint4 *>(sW + row * PW + col) = *reinterpret_cast<const uint4 *>(wg + row * C + col);
-            }
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const int i = tid + j * kChainThreads, row = i / PR, col = 8 * (i % PR);
+            *reinterpret_cast<v4u32 *>(sQ + row * PK + col) = pq[j];
+            *reinterpret_cast<v4u32 *>(sK + row * PK + col) = pk[j];
+            *reinterpret_cast<v4u32 *>(sO + row * PK + col) = po[j];
+        }
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            const int i = tid + j * kChainThreads, row = i / (C / 8), col = 8 * (i % (C / 8));
+            *reinterpret_cast<v4u32 *>(sW + row * PW + col) = pw[j];
         }
         if (wave == 0) {
-            float G2, bv, GL2;
-            chunk_gates<GATE_BF16>(a, t0, len, h, lane, G2, bv, GL2);
+            const float G2 = wave_inclusive_scan(pg * kLog2e);
+            const float GL2 = lane63(G2);
             sGs[lane] = a.scale * fast_exp2(G2);
             sLam[lane] = fast_exp2(GL2 - G2);
             if (lane == 0) sGL[0] = fast_exp2(GL2);
         }
         __syncthreads();
+        if (c > 0) GDR_FETCH(c - 1)   // in flight during this chunk's products
 
-        // dS' of this chunk, for the per-chunk gradient kernel
+        // dS' of this chunk (bf16), for the per-chunk gradient kernel
         {
-            float *dst = a.dhe + rh * D * D;
+            uint16_t *dst = a.dhe + rh * D * D;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        dst[(16 * mt + 4 * lq + r) * D + colw + 16 * nt + l16] = dH[mt][nt][r];
+                        dst[(16 * mt + 4 * lq + r) * D + colw + 16 * nt + l16] = bf16_bits(dH[mt][nt][r]);
         }
 
         // X1 = K dS'
@@ -429,20 +490,21 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
             }
         }
 
-        // dU = dU0 + diag(e^{G_L - G}) X1, completed in place
-        float *ug = a.du + rh * (C * D);
-        f32x4 dU[4][NTW];
+        // dU = dU0 + diag(e^{G_L - G}) X1, stored in bf16 (the same tiling)
+        uint16_t *ug = a.du + rh * (C * D);
+        bf16x4 dUb[4][NTW];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
-                f32x4 *up = reinterpret_cast<f32x4 *>(ug + ((mt * MT + colw / 16 + nt) * 64 + lane) * 4);
-                f32x4 u = *up;
+                f32x4 u = pu[mt][nt];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) u[r] += sLam[16 * mt + 4 * lq + r] * X1[mt][nt][r];
-                *up = u;
-                dU[mt][nt] = u;
+                dUb[mt][nt] = cvt4(u);
+                *reinterpret_cast<bf16x4 *>(ug + ((mt * MT + colw / 16 + nt) * 64 + lane) * 4) = dUb[mt][nt];
             }
+
+        if (c > 0) GDR_FETCH_DU0(c - 1)
 
         // dS <- e^{G_L} dS' + Q^T diag(scale e^G) dO - w^T dU
         const float gl = sGL[0];
@@ -462,7 +524,7 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
                     f[s] = static_cast<__bf16>(x * sGs[32 * kk + 16 * (s >> 2) + 4 * lq + (s & 3)]);
                 }
                 bo[nt] = f;
-                bu[nt] = cat(cvt4(-dU[2 * kk][nt]), cvt4(-dU[2 * kk + 1][nt]));
+                bu[nt] = cat(neg4(dUb[2 * kk][nt]), neg4(dUb[2 * kk + 1][nt]));
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -488,6 +550,8 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
                 for (int r = 0; r < 4; ++r)
                     dst[(16 * mt + 4 * lq + r) * D + colw + 16 * nt + l16] = dH[mt][nt][r];
     }
+#undef GDR_FETCH
+#undef GDR_FETCH_DU0
 }
 
 // --------------------------------------------------------------------------
@@ -564,6 +628,12 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
         const int64_t rh = static_cast<int64_t>(blockIdx.x) * a.hv + h;
         const float *Sg = p.c > 0 ? a.hck + (rh - a.hv) * D * D
                                   : (a.h0 ? a.h0 + (p.n * a.hv + h) * D * D : nullptr);
+        bf16x4 ub[4];   // this wave's dU tiles (dv tile nt), bf16
+        if (colwave) {
+            const uint16_t *ug = a.du + rh * (C * D);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) ub[mt] = *reinterpret_cast<const bf16x4 *>(ug + ((mt * NTD + nt) * 64 + lane) * 4);
+        }
         __syncthreads();   // the previous v-head's reads of LDS are done
         stage_rows<D, IN_BF16, kBwdThreads>(sV, PK, a.v, p.t0, p.len, a.hv, h, tid);
         stage_rows<D, IN_BF16, kBwdThreads>(sO, PK, a.dout, p.t0, p.len, a.hv, h, tid);
@@ -593,7 +663,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
         // X = K S, R~ = V - e^G X, U = T diag(b) R~, dW = T^T dU, dV = b dW (dv tile nt)
         if (colwave) {
             f32x4 Rt[4], U[4], dW[4];
-            bf16x4 wb[4], ub[4];
+            bf16x4 wb[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) Rt[mt] = zero4();
             for (int kk = 0; kk < D / 32; ++kk) {
@@ -601,7 +671,6 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) Rt[mt] = mfma32(frag_rows(sK, PK, 16 * mt, 32 * kk, l16, lq), bs, Rt[mt]);
             }
-            const float *ug = a.du + rh * (C * D);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 f32x4 w;
@@ -612,7 +681,6 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
                     w[r] = sB[i] * Rt[mt][r];
                 }
                 wb[mt] = cvt4(w);
-                ub[mt] = cvt4(*reinterpret_cast<const f32x4 *>(ug + ((mt * NTD + nt) * 64 + lane) * 4));
                 U[mt] = dW[mt] = zero4();
             }
 #pragma unroll
@@ -645,6 +713,9 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
         __syncthreads();
 
         // dQ1 = dO S^T, dK1 = dW S^T (dk tile nt)
+        constexpr int NDS = D * D / 8 / kBwdThreads;   // 16-byte pieces of dS' per thread
+        v4u32 pds[NDS];
+        fetch_block<NDS, kBwdThreads>(pds, a.dhe + rh * D * D, tid);
         f32x4 dQt[4], dK1[4];   // dQt: scale e^G dO S^T, then + Zs K
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) dQt[mt] = dK1[mt] = zero4();
@@ -664,18 +735,18 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
         }
         __syncthreads();   // S, V and T are no longer read
 
-        // dS' into LDS (and the fp32 <dS', S>); Zs, dBn, dB
+        // dS' into LDS over S, with <dS', S> taken on the way; Zs, dBn, dB
         {
-            const float *dg_ = a.dhe + rh * D * D;
             float part = 0.f;
-            for (int i = tid; i < D * D / 4; i += kBwdThreads) {
-                const int row = i / (D / 4), col = 4 * (i % (D / 4));
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(dg_ + row * D + col);
-                if (Sg) {
-                    const f32x4 s = *reinterpret_cast<const f32x4 *>(Sg + row * D + col);
-                    part += v[0] * s[0] + v[1] * s[1] + v[2] * s[2] + v[3] * s[3];
-                }
-                st4(sS + row * PK + col, cvt4(v));
+#pragma unroll
+            for (int j = 0; j < NDS; ++j) {
+                const int i = tid + j * kBwdThreads, row = i / (D / 8), col = 8 * (i % (D / 8));
+                v4u32 *sp = reinterpret_cast<v4u32 *>(sS + row * PK + col);
+                const bf16x8 sv = __builtin_bit_cast(bf16x8, *sp);
+                const bf16x8 dv = __builtin_bit_cast(bf16x8, pds[j]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) part += static_cast<float>(dv[e]) * static_cast<float>(sv[e]);
+                *sp = pds[j];
             }
             part = lane63(wave_inclusive_scan(part));
             if (lane == 0) sXd[wave] = part;
