@@ -14,6 +14,9 @@ the recurrence is the gated delta rule of Gated DeltaNet,
 ``o_t = scale * S_t q_t``, with the state kept as ``H = S^T`` in
 ``[N, Hv, dk, dv]`` layout.
 
+``gdr_kda_fwd`` is the same recurrence with one log-gate per key channel
+(decay ``diag(exp(g_t))`` on the rows of H), the KDA-style variant.
+
 ``gdr_bwd`` is the reverse-mode derivative of the same recurrence, one token
 at a time in reverse order (also in ``gdr_oracle.c``).
 
@@ -60,6 +63,9 @@ def _bind(path: str):
     lib.gdr_oracle_fwd_chunks.argtypes = [dp, dp, dp, dp, dp, lp, i64, i64, i64, i64, i64, i64,
                                           dp, dp, dp, dp, ctypes.c_double, ctypes.c_int]
     lib.gdr_oracle_fwd_chunks.restype = ctypes.c_int
+    lib.gdr_oracle_kda_fwd.argtypes = [dp, dp, dp, dp, dp, lp, i64, i64, i64, i64, i64, i64,
+                                       dp, dp, dp, ctypes.c_double, ctypes.c_int]
+    lib.gdr_oracle_kda_fwd.restype = ctypes.c_int
     lib.gdr_oracle_bwd.argtypes = [dp, dp, dp, dp, dp, lp, i64, i64, i64, i64, i64, i64,
                                    dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_double, ctypes.c_int]
     lib.gdr_oracle_bwd.restype = ctypes.c_int
@@ -147,6 +153,37 @@ def gdr_fwd(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Optional[float] =
     if rc != 0:
         raise ValueError("oracle: gdr_oracle_fwd returned %d" % rc)
     return (o, ht, hck) if chunk_states else (o, ht)
+
+
+def gdr_kda_fwd(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Optional[float] = None,
+                ht_init=None, n_threads: int = 0, _lib_path: Optional[str] = None):
+    """Per-token fp64 forward with per-channel gates: ``g`` is ``[B, T, Hv, dk]``
+    (natural-log decay of each key channel); everything else as ``gdr_fwd``.
+    Returns ``(o, ht)``."""
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T) or g.shape != (B, T, Hv, dk) or beta.shape != (B, T, Hv):
+        raise ValueError("oracle: expected g [B, T, Hv, dk] and beta [B, T, Hv]")
+    if cu_seqlens is None:
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        if B != 1:
+            raise ValueError("oracle: cu_seqlens requires B == 1")
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    n_seq = cu.shape[0] - 1
+    if scale is None:
+        scale = dk ** -0.5
+    h0a = None if h0 is None else _f64(h0)
+    o = np.zeros((B, T, Hv, dv), dtype=np.float64)
+    ht = np.zeros((n_seq, Hv, dk, dv)) if ht_init is None else _f64(ht_init).copy()
+    lib = _load() if _lib_path is None else _bind(_lib_path)
+    rc = lib.gdr_oracle_kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu, ctypes.c_int64),
+                                n_seq, B * T, Hk, Hv, dk, dv, _ptr(h0a), _ptr(o), _ptr(ht), float(scale),
+                                int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle: gdr_oracle_kda_fwd returned %d" % rc)
+    return o, ht
 
 
 def gdr_bwd(q, k, v, g, beta, do, cu_seqlens=None, h0=None, dht=None,

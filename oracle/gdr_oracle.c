@@ -44,6 +44,7 @@
  *   cu    [n_seq + 1]      h0, ht [n_seq, Hv, dk, dv]   (h0 NULL = zero state,
  *                                                          ht NULL = not written)
  *   hck   [NT, Hv, dk, dv] with NT = off[n_seq]     (NULL = not written)
+ *   gk    [T, Hv, dk] per-channel log-gates (gdr_oracle_kda_fwd only; replaces g)
  */
 #include <math.h>
 #include <pthread.h>
@@ -54,6 +55,7 @@
 
 typedef struct {
     const double *q, *k, *v, *g, *beta, *h0;
+    const double *gk;    /* per-channel log-gates [T, Hv, dk], or NULL (scalar g) */
     const int64_t *cu;
     double *o, *ht, *hck;
     const int64_t *off;  /* chunk offsets per sequence (hck only) */
@@ -80,10 +82,17 @@ static void run_item(const job_t *J, int64_t n, int64_t h, double *H, double *p)
         const double *kt = J->k + (t * Hk + hk) * dk;
         const double *qt = J->q + (t * Hk + hk) * dk;
         const double *vt = J->v + (t * Hv + h) * dv;
-        const double a = exp(J->g[t * Hv + h]);
+        const double a = J->gk ? 1.0 : exp(J->g[t * Hv + h]);
         const double b = J->beta[t * Hv + h];
 
         for (int64_t i = 0; i < dk * dv; ++i) H[i] *= a;
+        if (J->gk) {                              /* per-channel decay of the rows of H */
+            const double *gt = J->gk + (t * Hv + h) * dk;
+            for (int64_t i = 0; i < dk; ++i) {
+                const double ai = exp(gt[i]);
+                for (int64_t j = 0; j < dv; ++j) H[i * dv + j] *= ai;
+            }
+        }
 
         for (int64_t j = 0; j < dv; ++j) p[j] = 0.0;
         for (int64_t i = 0; i < dk; ++i)
@@ -165,11 +174,47 @@ int gdr_oracle_fwd(const double *q, const double *k, const double *v, const doub
                                  NULL, scale, n_threads);
 }
 
+static int run_fwd_job(const double *q, const double *k, const double *v, const double *g,
+                       const double *g_channels, const double *beta, const int64_t *cu, int64_t n_seq,
+                       int64_t T, int64_t Hk, int64_t Hv, int64_t dk, int64_t dv, const double *h0,
+                       double *o, double *ht, double *hck, double scale, int n_threads);
+
 /* The same, also writing the chunk-boundary states into hck (may be NULL). */
 int gdr_oracle_fwd_chunks(const double *q, const double *k, const double *v, const double *g,
                           const double *beta, const int64_t *cu, int64_t n_seq, int64_t T,
                           int64_t Hk, int64_t Hv, int64_t dk, int64_t dv, const double *h0,
                           double *o, double *ht, double *hck, double scale, int n_threads)
+{
+    return run_fwd_job(q, k, v, g, NULL, beta, cu, n_seq, T, Hk, Hv, dk, dv, h0, o, ht, hck, scale,
+                       n_threads);
+}
+
+/*
+ * Per-channel gates (the KDA-style variant of "feat(cake_kda): add paired
+ * recurrent training for SM100a and SM103a", whose raw gate carries one value
+ * per key channel): the scalar decay exp(g_t) becomes diag(exp(g_t)) with
+ * g_t in R^dk, applied to the rows of H (the key side):
+ *
+ *     S_t = S_{t-1} diag(exp(g_t)) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *
+ * g_channels is [T, Hv, dk] (already the log-decay: the pages do not define
+ * the transform that produces it from a raw gate).  Everything else is
+ * gdr_oracle_fwd.
+ */
+int gdr_oracle_kda_fwd(const double *q, const double *k, const double *v, const double *g_channels,
+                       const double *beta, const int64_t *cu, int64_t n_seq, int64_t T, int64_t Hk,
+                       int64_t Hv, int64_t dk, int64_t dv, const double *h0, double *o, double *ht,
+                       double scale, int n_threads)
+{
+    if (!g_channels) return -1;
+    return run_fwd_job(q, k, v, NULL, g_channels, beta, cu, n_seq, T, Hk, Hv, dk, dv, h0, o, ht, NULL,
+                       scale, n_threads);
+}
+
+static int run_fwd_job(const double *q, const double *k, const double *v, const double *g,
+                       const double *g_channels, const double *beta, const int64_t *cu, int64_t n_seq,
+                       int64_t T, int64_t Hk, int64_t Hv, int64_t dk, int64_t dv, const double *h0,
+                       double *o, double *ht, double *hck, double scale, int n_threads)
 {
     if (n_seq < 0 || T < 0 || Hk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || Hv % Hk != 0)
         return -1;
@@ -180,6 +225,7 @@ int gdr_oracle_fwd_chunks(const double *q, const double *k, const double *v, con
 
     job_t J;
     J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.h0 = h0;
+    J.gk = g_channels;
     J.cu = cu; J.o = o; J.ht = ht; J.hck = hck;
     int64_t *off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_seq + 1));
     if (!off) return -2;

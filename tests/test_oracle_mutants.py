@@ -21,8 +21,8 @@ MUTANTS = [
     ("ghost_writes", "if (eos <= bos) return;", "if (eos < bos) return;"),
     ("transposed_update", "H[i * dv + j] += kt[i] * p[j];",
      "H[(i * dv + j) % (dk * dv)] += kt[j % dk] * p[i % dv];"),
-    ("beta_on_decay", "const double a = exp(J->g[t * Hv + h]);",
-     "const double a = exp(J->g[t * Hv + h]) * J->beta[t * Hv + h];"),
+    ("beta_on_decay", "const double a = J->gk ? 1.0 : exp(J->g[t * Hv + h]);",
+     "const double a = J->gk ? 1.0 : exp(J->g[t * Hv + h]) * J->beta[t * Hv + h];"),
     ("output_before_update",  # read the state before the rank-1 write
      "for (int64_t j = 0; j < dv; ++j) p[j] = b * (vt[j] - p[j]);   /* p now holds d */",
      "for (int64_t j = 0; j < dv; ++j) p[j] = b * (vt[j] - p[j]);"
@@ -116,3 +116,31 @@ def test_bwd_mutant_is_caught(tmp_path, name, old, new):
         except (AssertionError, ValueError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, "mutant %s passed every backward pin" % name
+
+
+# Mistakes planted in the per-channel gate path; the KDA pins must catch each.
+KDA_MUTANTS = [
+    ("kda_reversed_channels", "const double ai = exp(gt[i]);", "const double ai = exp(gt[dk - 1 - i]);"),
+    ("kda_one_gate", "const double ai = exp(gt[i]);", "const double ai = exp(gt[0]);"),
+    ("kda_gate_of_qk_head", "const double *gt = J->gk + (t * Hv + h) * dk;",
+     "const double *gt = J->gk + (t * Hv + hk) * dk;"),
+    ("kda_no_channel_decay", "        if (J->gk) {                              /* per-channel decay of the rows of H */",
+     "        if (0) {"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", KDA_MUTANTS, ids=[m[0] for m in KDA_MUTANTS])
+def test_kda_mutant_is_caught(tmp_path, name, old, new):
+    from oracle_kda_pins import ALL_KDA_PINS
+    so = _build(tmp_path, name, old, new)
+
+    def fwd(*a, **kw):
+        return oracle.gdr_kda_fwd(*a, _lib_path=so, **kw)
+
+    caught = []
+    for pin in ALL_KDA_PINS:
+        try:
+            pin(fwd)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, "mutant %s passed every KDA pin" % name
