@@ -69,6 +69,13 @@ def flops_bwd(dk: int, dv: int) -> int:
     return state + intra + flops_chunk(dk, dv)
 
 
+def flops_kda(dk: int, dv: int) -> int:
+    """Per-channel-gate forward flops per (token, v-head), every 64-wide block
+    counted in full: A and P (two 64 x 64 x dk), k~ S and q~ S, U = T W and P U,
+    and k^^T U (three full-state products)."""
+    return 6 * dk * dv + 2 * CHUNK * (2 * dk + 2 * dv)
+
+
 def bytes_alg(T: int, N: int, hk: int, hv: int, dk: int, dv: int, in_bytes: int, gate_bytes: int) -> int:
     """Every input read once and every output written once."""
     per_tok = hk * 2 * dk * in_bytes + hv * (2 * dv * in_bytes + 2 * gate_bytes)
@@ -90,6 +97,9 @@ def parse():
     ap.add_argument("--decode", type=int, default=0, metavar="B",
                     help="time gdr_decode_step for B sequences with the workload's heads "
                          "(one token each, state in place), against the HBM roofline")
+    ap.add_argument("--kda", action="store_true",
+                    help="time gdr_chunk_kda_fwd (one log-gate per key channel, seeded like g) "
+                         "for the workload, against the MFMA roofline of its flops")
     ap.add_argument("--backward", action="store_true",
                     help="time gdr_chunk_bwd (forward recompute and all gradients) for the workload, "
                          "against the MFMA roofline of the backward flops")
@@ -143,7 +153,12 @@ def main():
     torch.cuda.synchronize()
 
     nt_chunks = sum((L + CHUNK - 1) // CHUNK for L in d["lengths"])
-    if args.backward:
+    if args.kda:
+        gk = put(gi.generate_kda_gates(d, seed=w.seed + 3), dt)
+
+        def step():
+            gdr.chunk_kda_fwd(q, k, v, gk, beta, cu, h0, scale=d["scale"], o=o, ht=ht)
+    elif args.backward:
         import gdr_inputs
         gr = gdr_inputs.generate_grads(d, seed=w.seed + 7)
         do, dht = put(gr["do"], dt), put(gr["dht"], torch.float32)
@@ -222,6 +237,17 @@ def main():
                 "frac": nbytes / (launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
         "cpu_baseline": None,
     }
+    if args.kda:
+        fk = flops_kda(w.dk, w.dv) * tokens * w.hv
+        gbytes = tokens * w.hv * w.dk * in_bytes
+        out["config"]["kda"] = True
+        out["roofline"] = {"bound": "mfma", "achieved": fk / (launch_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": fk / (launch_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                           "traffic": None, "kernel": "gdr_kda_fwd_kernel<128,bf16,bf16> (+ gdr_prepare_kernel)",
+                           "flops_per_launch": fk, "launch_ms": launch_ms}
+        out.pop("mfma_frac_fmin")
+        out["hbm"] = {"bytes_alg": nbytes + gbytes, "achieved_GBps": (nbytes + gbytes) / (launch_ms * 1e-3) / 1e9,
+                      "frac": (nbytes + gbytes) / (launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
     if args.backward:
         fb = flops_bwd(w.dk, w.dv) * tokens * w.hv
         out["config"]["backward"] = True

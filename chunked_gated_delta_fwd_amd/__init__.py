@@ -25,7 +25,7 @@ STATUS = {0: "GDR_OK", -1: "GDR_EINVAL", -2: "GDR_ESHAPE", -3: "GDR_EDTYPE", -4:
           -5: "GDR_EALIAS", -6: "GDR_EDEVICE", -7: "GDR_ELAUNCH", -8: "GDR_ENOMEM"}
 
 # every symbol include/gdr.h declares
-EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_checkpoints", "gdr_chunk_bwd", "gdr_decode_step", "gdr_plan",
+EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_checkpoints", "gdr_chunk_bwd", "gdr_chunk_kda_fwd", "gdr_decode_step", "gdr_plan",
            "gdr_prepare_chunks", "gdr_dispatch_order",
            "gdr_chunk_local_cumsum", "gdr_last_error", "gdr_version", "gdr_selftest_mfma")
 
@@ -68,6 +68,8 @@ def library(path: Optional[str] = None):
     lib.gdr_chunk_fwd.restype = ctypes.c_int
     lib.gdr_chunk_fwd_checkpoints.argtypes = [TP] * 10 + [ctypes.c_float, ctypes.c_void_p]
     lib.gdr_chunk_fwd_checkpoints.restype = ctypes.c_int
+    lib.gdr_chunk_kda_fwd.argtypes = [TP] * 9 + [ctypes.c_float, ctypes.c_void_p]
+    lib.gdr_chunk_kda_fwd.restype = ctypes.c_int
     lib.gdr_chunk_bwd.argtypes = [TP] * 15 + [ctypes.c_float, ctypes.c_void_p]
     lib.gdr_chunk_bwd.restype = ctypes.c_int
     lib.gdr_decode_step.argtypes = [TP] * 7 + [ctypes.c_float, ctypes.c_void_p]
@@ -192,6 +194,26 @@ def chunk_fwd_checkpoints(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Opt
     _check(lib, lib.gdr_chunk_fwd_checkpoints(*[_ref(x) for x in ds], ctypes.c_float(scale),
                                               ctypes.c_void_p(_stream_handle(q))))
     return o, ht, h_chunks
+
+
+def chunk_kda_fwd(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Optional[float] = None, o=None, ht=None):
+    """``chunk_fwd`` with per-channel gates: g ``[B, T, Hv, dk]`` (log-decay of
+    each key channel), beta ``[B, T, Hv]``.  Returns ``(o, ht)``."""
+    import torch
+    lib = library()
+    B, T, Hk, d = q.shape
+    Hv = v.shape[2]
+    N = (cu_seqlens.shape[0] - 1) if cu_seqlens is not None else B
+    if scale is None:
+        scale = float(d) ** -0.5
+    if o is None:
+        o = torch.zeros((B, T, Hv, v.shape[3]), dtype=q.dtype, device=q.device)
+    if ht is None:
+        ht = torch.zeros((N, Hv, d, v.shape[3]), dtype=torch.float32, device=q.device)
+    ds = [_desc(x) for x in (q, k, v, g, beta, cu_seqlens, h0, o, ht)]
+    _check(lib, lib.gdr_chunk_kda_fwd(*[_ref(x) for x in ds], ctypes.c_float(scale),
+                                      ctypes.c_void_p(_stream_handle(q))))
+    return o, ht
 
 
 def chunk_bwd(q, k, v, g, beta, do, cu_seqlens=None, h0=None, dht=None, scale: Optional[float] = None,

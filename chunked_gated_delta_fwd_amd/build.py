@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdr.so")
 
-SOURCES = ["gdr_kernels.hip", "gdr_bwd.hip", "gdr_api.cpp"]
+SOURCES = ["gdr_kernels.hip", "gdr_bwd.hip", "gdr_kda.hip", "gdr_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -541,6 +541,67 @@ int run_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     return ok();
 }
 
+// The per-channel-gate forward: g is [B, T, Hv, dk]; everything else is
+// validated as for gdr_chunk_fwd (with beta standing in for the scalar g).
+int run_kda(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
+            const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0, const gdr_tensor *o,
+            const gdr_tensor *ht, float scale, hipStream_t stream) {
+    int64_t ng;
+    int rc;
+    if ((rc = check_tensor(g, "g", 4, &ng, 4))) return rc;
+    gdr_launch_plan p;
+    if ((rc = plan_fwd(q, k, v, beta, beta, cu_seqlens, h0, o, ht, scale, &p))) return rc;
+    if (g->dtype != beta->dtype) return fail(GDR_EDTYPE, "g and beta must share one dtype");
+    const int64_t B = q->shape[0], T = q->shape[1];
+    if (!shape_is(g, {B, T, p.hv, p.d}))
+        return fail(GDR_ESHAPE, "g: shape %s must be [B, T, Hv, dk]", shape_str(g).c_str());
+    int64_t no = 1, nht = 1;
+    for (int i = 0; i < 4; ++i) no *= o->shape[i];
+    if (ht)
+        for (int i = 0; i < 4; ++i) nht *= ht->shape[i];
+    const Span sg = span_of(g, ng);
+    if (overlap(span_of(o, no), sg)) return fail(GDR_EALIAS, "o overlaps an input");
+    if (ht && overlap(span_of(ht, nht), sg)) return fail(GDR_EALIAS, "ht overlaps an input");
+    if ((rc = check_device())) return rc;
+    if (p.n_seq == 0 || p.total_tokens == 0) return ok();
+
+    gdr::FwdArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q->data;
+    a.k = k->data;
+    a.v = v->data;
+    a.g = g->data;
+    a.beta = beta->data;
+    a.cu = cu_seqlens ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
+    a.h0 = h0 ? static_cast<const float *>(h0->data) : nullptr;
+    a.o = o->data;
+    a.ht = ht ? static_cast<float *>(ht->data) : nullptr;
+    a.n_seq = p.n_seq;
+    a.seq_len = cu_seqlens ? p.total_tokens : T;
+    a.total_tokens = p.total_tokens;
+    a.hk = p.hk;
+    a.hv = p.hv;
+    a.d = p.d;
+    a.in_bf16 = p.in_dtype == GDR_BF16;
+    a.gate_bf16 = p.gate_dtype == GDR_BF16;
+    a.scale = scale;
+    void *ws = nullptr;
+    hipError_t e = hipSuccess;
+    if (cu_seqlens) {   // longest sequences first
+        hipMemPool_t pool = nullptr;
+        e = workspace_pool(&pool);
+        if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, static_cast<size_t>(4 * p.n_seq), pool, stream);
+        if (e != hipSuccess) return fail(GDR_ENOMEM, "workspace: %s", hipGetErrorString(e));
+        a.order = static_cast<int32_t *>(ws);
+        e = gdr::launch_prepare(a.cu, p.n_seq, nullptr, nullptr, 0, static_cast<int32_t *>(ws), stream);
+    }
+    if (e == hipSuccess) e = gdr::launch_kda_fwd(a, stream);
+    const hipError_t fe = ws ? hipFreeAsync(ws, stream) : hipSuccess;
+    if (e != hipSuccess) return launch_error(e, "per-channel-gate forward kernel");
+    if (fe != hipSuccess) return launch_error(fe, "workspace release");
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -573,6 +634,12 @@ int gdr_chunk_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
                   const gdr_tensor *dv, const gdr_tensor *dg, const gdr_tensor *dbeta, const gdr_tensor *dh0,
                   float scale, hipStream_t stream) {
     return run_bwd(q, k, v, g, beta, cu_seqlens, h0, dout, dht, dq, dk, dv, dg, dbeta, dh0, scale, stream);
+}
+
+int gdr_chunk_kda_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
+                      const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
+                      const gdr_tensor *o, const gdr_tensor *ht, float scale, hipStream_t stream) {
+    return run_kda(q, k, v, g, beta, cu_seqlens, h0, o, ht, scale, stream);
 }
 
 int gdr_decode_step(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,

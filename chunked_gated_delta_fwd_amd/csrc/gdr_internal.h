@@ -48,6 +48,8 @@ constexpr int kFwdThreads = 512;
 constexpr int kChunk = 64;
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
+// Per-channel gates: the same arguments with g of shape [tokens, Hv, d].
+hipError_t launch_kda_fwd(const FwdArgs &a, hipStream_t stream);
 
 hipError_t launch_prepare(const int32_t *cu, int64_t n_seq, int32_t *chunk_offsets,
                           int32_t *chunk_map, int64_t nt_max, int32_t *order,

@@ -1,0 +1,368 @@
+// HIP kernel of the chunked gated delta rule with per-channel gates (the
+// KDA-style variant of "feat(cake_kda): add paired recurrent training for
+// SM100a and SM103a", whose raw gate carries one value per key channel), for
+// gfx950.  The decay exp(g_t) becomes diag(exp(g_t)), g_t in R^dk, on the key
+// side of the state:  S_t = S_{t-1} diag(e^{g_t}) (I - b_t k_t k_t^T) + b_t v_t k_t^T,
+// o_t = scale S_t q_t.  g is taken as the log-decay itself (the transform that
+// makes it from a raw gate is not defined on the pages).
+//
+// Chunk form.  With G the chunk-local prefix sums of g (per channel, rows past
+// the segment end padded with g = b = 0) and a reference row m = 31 of the
+// chunk, the exponentials are folded into the operands so that every factor
+// stays within e^{+-(half the chunk's decay)}:
+//
+//   q~ = q o e^{G - G_m},  k~ = k o e^{G - G_m},  k^ = k o e^{G_m - G}
+//   A  = tril(diag(b) k~ k^^T, -1),  P = scale tril(q~ k^^T)
+//   S_m = diag(e^{G_m}) H                  (the state decayed to row m)
+//   U  = (I + A)^-1 diag(b) (V - k~ S_m)
+//   O  = scale q~ S_m + P U
+//   H <- diag(e^{G_L}) H + diag(e^{G_L - G_m}) k^^T U
+//
+// A per-channel decay summed over half a chunk must stay above about -85 so
+// that e^{G_m - G} fits in fp32/bf16 (about 2.6 per token and channel).
+//
+// One work-group of 8 waves per (sequence, v-head) walks its chunks in order;
+// wave w owns dv columns [16w, 16w + 16) of the fp32 state (MFMA C tiles, rows
+// dk).  Per chunk: the gate scan (all threads: one channel and a quarter of the
+// tokens each), the gated operands into LDS, S_m into LDS, the ten lower
+// blocks of A and of P, the inverse T = (I + A)^-1 (16x16 diagonal inverses by
+// fp32 substitution, off-diagonal blocks by a chain of MFMA products), then per
+// wave X, U, O and the state update of its columns.
+#include "gdr_internal.h"
+#include "gdr_device.h"
+
+#include <stdint.h>
+
+namespace gdr {
+namespace {
+
+constexpr int kKdaThreads = 512;
+
+__device__ __forceinline__ bf16x8 kfrag_rows(const uint16_t *M, int pitch, int row0, int k0, int l16, int lq) {
+    const uint16_t *p = M + (row0 + l16) * pitch + k0 + 4 * lq;
+    return cat(ld4(p), ld4(p + 16));
+}
+__device__ __forceinline__ bf16x8 kfrag_cols(const uint16_t *M, int pitch, int col0, int k0, int l16, int lq) {
+    const uint16_t *p = M + (k0 + 4 * lq + (l16 >> 2)) * pitch + col0 + 4 * (l16 & 3);
+    return cat(ld4_tr(p), ld4_tr(p + 16 * pitch));
+}
+__device__ __forceinline__ float kbf(uint16_t u) { return __uint_as_float(static_cast<uint32_t>(u) << 16); }
+
+template <int D>
+struct KdaLds {
+    static constexpr int PK = D + 16;
+    static constexpr int PP = C + 8;
+    static constexpr int PD = 24;
+    static constexpr int NG = kKdaThreads / D;   // token groups of the gate scan
+    static constexpr int oQt = 0;                  // q~ [64][PK]
+    static constexpr int oKt = oQt + C * PK * 2;   // k~
+    static constexpr int oKh = oKt + C * PK * 2;   // k^
+    static constexpr int oS = oKh + C * PK * 2;    // S_m bf16 [D][PK]
+    static constexpr int oA = oS + D * PK * 2;     // diag(b) A~ strictly lower [i][j]
+    static constexpr int oP = oA + C * PP * 2;     // scale tril(q~ k^^T) [i][j]
+    static constexpr int oT = oP + C * PP * 2;     // T^T [j][i]
+    static constexpr int oDi = oT + C * PP * 2;    // inverses of the diagonal blocks [4][16][PD]
+    static constexpr int oV = oDi + 4 * 16 * PD * 2;   // f32 [D] x3: e^{G_m}, e^{G_L}, e^{G_L - G_m}; [64] b
+    static constexpr int oTot = oV + (3 * D + C) * 4;  // f32 [NG][D] group totals of the scan
+    static constexpr int bytes = oTot + NG * D * 4;
+};
+
+template <int D, bool IN_BF16, bool GATE_BF16>
+__global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
+    using Ly = KdaLds<D>;
+    constexpr int PK = Ly::PK, PP = Ly::PP, PD = Ly::PD, NG = Ly::NG;
+    constexpr int TPG = C / NG;     // tokens per scan group
+    constexpr int MT = D / 16;      // dk tiles
+    constexpr int NTD = D / 16;     // dv tiles (one per wave while wave < NTD)
+    extern __shared__ __align__(16) unsigned char lds[];
+    uint16_t *sQt = reinterpret_cast<uint16_t *>(lds + Ly::oQt);
+    uint16_t *sKt = reinterpret_cast<uint16_t *>(lds + Ly::oKt);
+    uint16_t *sKh = reinterpret_cast<uint16_t *>(lds + Ly::oKh);
+    uint16_t *sS = reinterpret_cast<uint16_t *>(lds + Ly::oS);
+    uint16_t *sA = reinterpret_cast<uint16_t *>(lds + Ly::oA);
+    uint16_t *sP = reinterpret_cast<uint16_t *>(lds + Ly::oP);
+    uint16_t *sT = reinterpret_cast<uint16_t *>(lds + Ly::oT);
+    uint16_t *sDi = reinterpret_cast<uint16_t *>(lds + Ly::oDi);
+    float *sEm = reinterpret_cast<float *>(lds + Ly::oV);
+    float *sEL = sEm + D;
+    float *sELm = sEL + D;
+    float *sB = sELm + D;
+    float *sTot = reinterpret_cast<float *>(lds + Ly::oTot);
+
+    const int64_t rank = blockIdx.x / a.hv;
+    const int h = static_cast<int>(blockIdx.x % a.hv);
+    const int64_t n = a.order ? static_cast<int64_t>(a.order[rank]) : rank;
+    if (n < 0 || n >= a.n_seq) return;
+    int64_t bos, eos;
+    if (a.cu) {
+        bos = a.cu[n];
+        eos = a.cu[n + 1];
+    } else {
+        bos = n * a.seq_len;
+        eos = bos + a.seq_len;
+    }
+    bos = bos < 0 ? 0 : bos;
+    eos = eos > a.total_tokens ? a.total_tokens : eos;
+    if (eos <= bos) return;   // length-0 segment: reads nothing, writes nothing
+    const int hk = h / (a.hv / a.hk);
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const bool colwave = wave < NTD;
+    const int nt = wave;
+    const int64_t nch = (eos - bos + C - 1) / C;
+
+    // the state: rows dk (tile mt, row 4 lq + r), columns 16 nt + l16
+    f32x4 H[MT];
+    {
+        const int lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                H[mt][r] = (colwave && a.h0) ? a.h0[((n * a.hv + h) * D + 16 * mt + 4 * lq + r) * D + 16 * nt + l16] : 0.f;
+    }
+
+    for (int64_t c = 0; c < nch; ++c) {
+        int lane = tid & 63;   // opaque per iteration: keeps per-lane addresses inside the loop
+        asm volatile("" : "+v"(lane));
+        const int l16 = lane & 15, lq = lane >> 4;
+        const int64_t t0 = bos + C * c;
+        const int len = static_cast<int>(eos - t0 < C ? eos - t0 : C);
+
+        // ---- gates: per-channel prefix sums (log2 units), TPG tokens per thread
+        const int ch = tid % D, grp = tid / D;
+        float G2[TPG];
+        {
+            float run = 0.f;
+#pragma unroll
+            for (int i = 0; i < TPG; ++i) {
+                const int row = grp * TPG + i;
+                const float gv = row < len ? load_scalar<GATE_BF16>(a.g, ((t0 + row) * a.hv + h) * D + ch) : 0.f;
+                run += gv * kLog2e;
+                G2[i] = run;
+            }
+        }
+        __syncthreads();   // the previous chunk's reads of LDS are done
+        sTot[grp * D + ch] = G2[TPG - 1];
+        if (wave == 0) sB[lane] = lane < len ? load_scalar<GATE_BF16>(a.beta, (t0 + lane) * a.hv + h) : 0.f;
+        __syncthreads();
+        {
+            float offs = 0.f, gm = 0.f, gl = 0.f;
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                const float tj = sTot[j * D + ch];
+                offs += j < grp ? tj : 0.f;
+                gm += j < 32 / TPG ? tj : 0.f;
+                gl += tj;
+            }
+            if (grp == 0) {
+                sEm[ch] = fast_exp2(gm);
+                sEL[ch] = fast_exp2(gl);
+                sELm[ch] = fast_exp2(gl - gm);
+            }
+#pragma unroll
+            for (int i = 0; i < TPG; ++i) {
+                const int row = grp * TPG + i;
+                const float x = G2[i] + offs - gm;
+                float qv = 0.f, kv = 0.f;
+                if (row < len) {
+                    qv = load_scalar<IN_BF16>(a.q, ((t0 + row) * a.hk + hk) * D + ch);
+                    kv = load_scalar<IN_BF16>(a.k, ((t0 + row) * a.hk + hk) * D + ch);
+                }
+                const float e = fast_exp2(x), ei = fast_exp2(-x);
+                sQt[row * PK + ch] = bf16_bits(qv * e);
+                sKt[row * PK + ch] = bf16_bits(kv * e);
+                sKh[row * PK + ch] = bf16_bits(kv * ei);
+            }
+        }
+        // zero A and P (blocks above the diagonal stay zero)
+        for (int i = tid; i < 2 * C * PP / 8; i += kKdaThreads)
+            reinterpret_cast<v4u32 *>(sA)[i] = v4u32{0u, 0u, 0u, 0u};
+        __syncthreads();
+
+        // ---- S_m = diag(e^{G_m}) H into LDS (bf16 [dk][dv])
+        if (colwave) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * mt + 4 * lq + r;
+                    sS[row * PK + 16 * nt + l16] = bf16_bits(H[mt][r] * sEm[row]);
+                }
+        }
+        // ---- the ten lower blocks of A = diag(b) k~ k^^T and of P = scale q~ k^^T
+        for (int t = wave; t < 20; t += 8) {
+            const bool ka = t < 10;
+            const int tt = ka ? t : t - 10;
+            const int bi = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
+            const int bj = tt - bi * (bi + 1) / 2;
+            const uint16_t *Am = ka ? sKt : sQt;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < D; k0 += 32)
+                acc = mfma32(kfrag_rows(Am, PK, 16 * bi, k0, l16, lq), kfrag_rows(sKh, PK, 16 * bj, k0, l16, lq), acc);
+            const int j = 16 * bj + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * bi + 4 * lq + r;
+                if (ka) sA[i * PP + j] = bf16_bits(j < i ? sB[i] * acc[r] : 0.f);
+                else sP[i * PP + j] = bf16_bits(j <= i ? a.scale * acc[r] : 0.f);
+            }
+        }
+        __syncthreads();
+
+        // ---- diagonal blocks of (I + A)^-1: column l16 by fp32 forward substitution
+        f32x4 dcol = zero4();
+        if (wave < 4) {
+            const int b = wave;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float s = i == l16 ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < i; ++m) s -= kbf(sA[(16 * b + i) * PP + 16 * b + m]) * x[m];
+                x[i] = s;
+            }
+            if (lq == 0) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sDi[(16 * b + i) * PD + l16] = bf16_bits(x[i]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dcol[r] = lq == 0 ? x[r] : lq == 1 ? x[4 + r] : lq == 2 ? x[8 + r] : x[12 + r];
+        }
+        // ---- meanwhile the other products of the state: X = k~ S_m and q~ S_m (dv tile nt)
+        f32x4 X[4], QS[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) X[mt] = QS[mt] = zero4();
+        if (colwave) {
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const bf16x8 bs = kfrag_cols(sS, PK, 16 * nt, 32 * kk, l16, lq);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    X[mt] = mfma32(kfrag_rows(sKt, PK, 16 * mt, 32 * kk, l16, lq), bs, X[mt]);
+                    QS[mt] = mfma32(kfrag_rows(sQt, PK, 16 * mt, 32 * kk, l16, lq), bs, QS[mt]);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- column block j of T: X_j = D_j, X_i = -D_i sum_{m=j}^{i-1} A_im X_m; T^T to LDS
+        if (wave < 4) {
+            const int j = wave;
+            f32x4 Y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Y[i] = i == j ? dcol : zero4();
+#pragma unroll
+            for (int i = 1; i < 4; ++i) {
+                if (i > j) {
+                    f32x4 E = zero4();
+#pragma unroll
+                    for (int m = 0; m < 3; ++m)
+                        if (m >= j && m < i)
+                            E = mfma16z(ld4(sA + (16 * i + l16) * PP + 16 * m + 4 * lq), cvt4(Y[m]), E);
+                    Y[i] = -mfma16z(ld4(sDi + (16 * i + l16) * PD + 4 * lq), cvt4(E), zero4());
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st4(sT + (16 * j + l16) * PP + 16 * i + 4 * lq, cvt4(Y[i]));
+        }
+        __syncthreads();
+
+        // ---- U = T diag(b) (V - X), O = scale q~ S_m + P U, H update (dv tile nt)
+        if (colwave) {
+            bf16x4 wb[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 w;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * mt + 4 * lq + r;
+                    const float vv = i < len ? load_scalar<IN_BF16>(a.v, ((t0 + i) * a.hv + h) * D + 16 * nt + l16) : 0.f;
+                    w[r] = sB[i] * (vv - X[mt][r]);
+                }
+                wb[mt] = cvt4(w);
+            }
+            f32x4 U[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) U[mt] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 bw = cat(wb[2 * kk], wb[2 * kk + 1]);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) U[mt] = mfma32(kfrag_cols(sT, PP, 16 * mt, 32 * kk, l16, lq), bw, U[mt]);
+            }
+            bf16x4 ub[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                ub[mt] = cvt4(U[mt]);
+                QS[mt] = QS[mt] * a.scale;
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 bu = cat(ub[2 * kk], ub[2 * kk + 1]);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) QS[mt] = mfma32(kfrag_rows(sP, PP, 16 * mt, 32 * kk, l16, lq), bu, QS[mt]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * mt + 4 * lq + r;
+                    if (i < len) {
+                        const int64_t oi = ((t0 + i) * a.hv + h) * D + 16 * nt + l16;
+                        if constexpr (IN_BF16) reinterpret_cast<uint16_t *>(a.o)[oi] = bf16_bits(QS[mt][r]);
+                        else reinterpret_cast<float *>(a.o)[oi] = QS[mt][r];
+                    }
+                }
+            // H <- diag(e^{G_L}) H + diag(e^{G_L - G_m}) k^^T U
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                f32x4 R = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    R = mfma32(kfrag_cols(sKh, PK, 16 * mt, 32 * kk, l16, lq), cat(ub[2 * kk], ub[2 * kk + 1]), R);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * mt + 4 * lq + r;
+                    H[mt][r] = sEL[row] * H[mt][r] + sELm[row] * R[r];
+                }
+            }
+        }
+    }
+
+    if (a.ht && colwave) {
+        const int lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
+        float *dst = a.ht + (n * a.hv + h) * D * D;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(16 * mt + 4 * lq + r) * D + 16 * nt + l16] = H[mt][r];
+    }
+}
+
+template <int D, bool IN_BF16, bool GATE_BF16>
+hipError_t launch_kda_t(const FwdArgs &a, hipStream_t stream) {
+    auto kern = gdr_kda_fwd_kernel<D, IN_BF16, GATE_BF16>;
+    const int lds = KdaLds<D>::bytes;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(a.n_seq * a.hv)), dim3(kKdaThreads), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_kda_d(const FwdArgs &a, hipStream_t s) {
+    if (a.in_bf16) return a.gate_bf16 ? launch_kda_t<D, true, true>(a, s) : launch_kda_t<D, true, false>(a, s);
+    return a.gate_bf16 ? launch_kda_t<D, false, true>(a, s) : launch_kda_t<D, false, false>(a, s);
+}
+
+static_assert(KdaLds<128>::bytes <= 160 * 1024, "KDA kernel LDS");
+
+}  // namespace
+
+hipError_t launch_kda_fwd(const FwdArgs &a, hipStream_t stream) {
+    if (a.n_seq == 0 || a.hv == 0) return hipSuccess;
+    return a.d == 64 ? launch_kda_d<64>(a, stream) : launch_kda_d<128>(a, stream);
+}
+
+}  // namespace gdr

@@ -194,3 +194,13 @@ def generate_grads(case: dict, seed: int) -> dict:
     dht = rng.standard_normal((n_seq, v.shape[2], case["q"].shape[3], v.shape[3]),
                               dtype=np.float32).astype(np.float32)
     return dict(do=do, dht=dht)
+
+
+def generate_kda_gates(case: dict, seed: int, scale: float = 1.0) -> "np.ndarray":
+    """Per-channel log-gates for the per-channel-gate variant of ``case``:
+    ``scale * logsigmoid(N(0, 1))`` of shape ``[B, T, Hv, dk]`` (drawn with
+    ``PCG64(seed)``), rounded to the case's dtype."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    v, q = case["v"], case["q"]
+    x = rng.standard_normal(v.shape[:3] + (q.shape[3],), dtype=np.float32)
+    return _store(scale * _logsigmoid(x), case["dtype"])

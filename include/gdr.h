@@ -184,6 +184,29 @@ int gdr_chunk_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
                   float scale, hipStream_t stream);
 
 /*
+ * gdr_chunk_kda_fwd - gdr_chunk_fwd with one log-gate per key channel: the
+ * KDA-style variant of "feat(cake_kda): add paired recurrent training for
+ * SM100a and SM103a", whose raw gate has one value per key channel.  The
+ * scalar decay exp(g_t) becomes diag(exp(g_t)) on the key side:
+ *
+ *     S_t = S_{t-1} diag(exp(g_t)) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *
+ *   g      [B, T, Hv, dk]   per-channel natural-log decay, bf16 or f32 (the
+ *                           transform from a raw gate, undefined on the pages,
+ *                           is the caller's)
+ *   beta   [B, T, Hv]       same dtype as g
+ *
+ * Everything else (shapes, varlen and ghosts, h0/ht, GQA, errors) is
+ * gdr_chunk_fwd.  Within one 64-token chunk the gates are folded into the
+ * operands around the chunk's row 31, so a channel's log-decay summed over
+ * half a chunk must stay above about -85 (fp32 exponent range); with
+ * cu_seqlens the workspace is 4*N bytes (longest sequences start first).
+ */
+int gdr_chunk_kda_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
+                      const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
+                      const gdr_tensor *o, const gdr_tensor *ht, float scale, hipStream_t stream);
+
+/*
  * gdr_decode_step - one token of the same recurrence for each of B sequences:
  * the decode step that follows this forward pass in inference (the pages'
  * inference surface keeps a decode module beside the prefill, "feat(cake_kda):

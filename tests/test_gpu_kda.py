@@ -1,0 +1,99 @@
+"""Per-channel-gate forward (gdr_chunk_kda_fwd) on the GPU against the fp64
+oracle gdr_kda_fwd, element by element, with the forward's tolerances: the
+seeded workloads with one log-gate per key channel, ragged chunks, ghosts, GQA,
+both head sizes, fp32 gates; the full packed workload on sampled heads."""
+import numpy as np
+import pytest
+
+from gpu_helpers import TOL_HT, TOL_O, dev, np64, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(d, gk, gate_dtype=None):
+    import chunked_gated_delta_fwd_amd as gdr
+    import torch
+    t = to_device(d, gate_dtype)
+    g = dev(gk, gate_dtype or d["dtype"])
+    o, ht = gdr.chunk_kda_fwd(t["q"], t["k"], t["v"], g, t["beta"], t["cu"], t["h0"], scale=d["scale"])
+    torch.cuda.synchronize()
+    return np64(o), np64(ht)
+
+
+def _ref(d, gk, heads=None):
+    import oracle
+    q, k, v, g, beta, h0 = d["q"], d["k"], d["v"], gk, d["beta"], d["h0"]
+    if heads is not None:
+        kh, vh = heads
+        q, k, v, g, beta = q[:, :, kh], k[:, :, kh], v[:, :, vh], g[:, :, vh], beta[:, :, vh]
+        h0 = None if h0 is None else h0[:, vh]
+    return oracle.gdr_kda_fwd(q, k, v, g, beta, d["cu_seqlens"], h0, scale=d["scale"])
+
+
+def _check(o, ht, o_ref, ht_ref, real, what):
+    e_o = float(np.abs(o - o_ref).max())
+    e_h = float(np.abs(ht[real] - ht_ref[real]).max()) if len(real) else 0.0
+    say("%s: max|do| %.3e (max_ref %.3f)  max|dht| %.3e (max_ref %.3f)"
+        % (what, e_o, float(np.abs(o_ref).max()), e_h, float(np.abs(ht_ref).max())))
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(ht)), what + ": non-finite"
+    assert e_o <= TOL_O, "%s: max|do| %.3e > %.1e" % (what, e_o, TOL_O)
+    assert e_h <= TOL_HT, "%s: max|dht| %.3e > %.1e" % (what, e_h, TOL_HT)
+
+
+def _real(d):
+    cu = d["cu_seqlens"]
+    if cu is None:
+        return list(range(len(d["lengths"])))
+    return [i for i in range(len(cu) - 1) if cu[i + 1] > cu[i]]
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32_T128_H2_d64", "fixed_B4_T512_H16_d128", "varlen8_ghost8_H32_d128"])
+def test_kda_workloads(name):
+    import gdr_inputs
+    w = gdr_inputs.WORKLOADS[name]
+    d = gdr_inputs.generate(w)
+    gk = gdr_inputs.generate_kda_gates(d, seed=w.seed + 3)
+    o, ht = _run(d, gk)
+    o_ref, ht_ref = _ref(d, gk)
+    _check(o, ht, o_ref, ht_ref, _real(d), "kda " + name)
+
+
+def test_kda_gqa_ragged_ghosts():
+    import gdr_inputs
+    d = gdr_inputs.random_lengths_case(81, n_real=6, lo=1, hi=300, ghost_slots=4, hk=2, hv=8, d=128)
+    gk = gdr_inputs.generate_kda_gates(d, seed=82)
+    o, ht = _run(d, gk)
+    o_ref, ht_ref = _ref(d, gk)
+    _check(o, ht, o_ref, ht_ref, _real(d), "kda gqa4 ragged ghosts")
+
+
+def test_kda_d64_fp32_gates_slow_decay():
+    import gdr_inputs
+    d = gdr_inputs.random_lengths_case(83, n_real=3, lo=100, hi=400, ghost_slots=1, hk=1, hv=2, d=64)
+    gk = gdr_inputs.generate_kda_gates(d, seed=84, scale=1.0 / 16)
+    o, ht = _run(d, gk, gate_dtype="fp32")
+    o_ref, ht_ref = _ref(d, gk)
+    _check(o, ht, o_ref, ht_ref, _real(d), "kda d64 fp32 gates, slow decay")
+
+
+def test_kda_fast_decay():
+    """Gates twice as steep (mean about -1.6 per token and channel: half a chunk
+    sums to about -51, inside the documented range of about -85)."""
+    import gdr_inputs
+    d = gdr_inputs.random_lengths_case(85, n_real=3, lo=64, hi=200, ghost_slots=0, hk=2, hv=2, d=128)
+    gk = gdr_inputs.generate_kda_gates(d, seed=86, scale=2.0)
+    o, ht = _run(d, gk)
+    o_ref, ht_ref = _ref(d, gk)
+    _check(o, ht, o_ref, ht_ref, _real(d), "kda fast decay")
+
+
+def test_kda_packed64k_sampled_heads():
+    """The benchmark workload with per-channel gates: q/k head 3 and its v-heads 6, 7."""
+    import gdr_inputs
+    w = gdr_inputs.WORKLOADS["packed64k_gqa_Hk16_Hv32_d128"]
+    d = gdr_inputs.generate(w)
+    gk = gdr_inputs.generate_kda_gates(d, seed=w.seed + 3)
+    o, ht = _run(d, gk)
+    heads = ([3], [6, 7])
+    o_ref, ht_ref = _ref(d, gk, heads=heads)
+    _check(o[:, :, heads[1]], ht[:, heads[1]], o_ref, ht_ref, _real(d), "kda packed64k heads 6, 7")
