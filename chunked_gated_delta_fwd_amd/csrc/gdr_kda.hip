@@ -48,6 +48,66 @@ __device__ __forceinline__ bf16x8 kfrag_cols(const uint16_t *M, int pitch, int c
 }
 __device__ __forceinline__ float kbf(uint16_t u) { return __uint_as_float(static_cast<uint32_t>(u) << 16); }
 
+// One element at byte offset off (the whole offset in the range-checked
+// vector offset) of a buffer range, as float (bf16 or f32) or as bf16 bits
+// (f32 rounded); past the range it reads 0.
+template <bool BF16>
+__device__ __forceinline__ float rd_f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (BF16)
+        return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0)) << 16);
+    else return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+template <bool BF16>
+__device__ __forceinline__ uint32_t rd_bits(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (BF16) return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+    else return bf16_bits(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)));
+}
+// Channel ch of g, q and k for the TPG tokens of scan group grp, through
+// ranges that end at the segment's end.
+template <int D, int TPG, bool IN_BF16, bool GATE_BF16>
+__device__ __forceinline__ void kda_fetch_gate(const FwdArgs &a, int64_t t0, int len, int h, int hk, int ch,
+                                               int grp, float (&pg)[TPG], uint32_t (&pqk)[TPG]) {
+    constexpr uint32_t ES = IN_BF16 ? 2 : 4, GS = GATE_BF16 ? 2 : 4;
+    const uint32_t gstride = static_cast<uint32_t>(a.hv) * D * GS, qstride = static_cast<uint32_t>(a.hk) * D * ES;
+    const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(
+        reinterpret_cast<const unsigned char *>(a.g) + ((t0 * a.hv + h) * D) * GS, static_cast<uint32_t>(len) * gstride);
+    const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(
+        reinterpret_cast<const unsigned char *>(a.q) + ((t0 * a.hk + hk) * D) * ES, static_cast<uint32_t>(len) * qstride);
+    const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(
+        reinterpret_cast<const unsigned char *>(a.k) + ((t0 * a.hk + hk) * D) * ES, static_cast<uint32_t>(len) * qstride);
+    int chv = ch;   // opaque: the per-row offsets are formed here, not hoisted by the caller's loop
+    asm volatile("" : "+v"(chv));
+#pragma unroll
+    for (int i = 0; i < TPG; ++i) {
+        const uint32_t row = static_cast<uint32_t>(grp * TPG + i);
+        pg[i] = rd_f<GATE_BF16>(rg, row * gstride + chv * GS);
+        const uint32_t qo = row * qstride + chv * ES;
+        pqk[i] = rd_bits<IN_BF16>(rq, qo) | (rd_bits<IN_BF16>(rk, qo) << 16);
+    }
+}
+// v at rows 16 mt + 4 lq + r, column 16 nt + l16, packed in pairs (zero past len).
+template <int D, bool IN_BF16>
+__device__ __forceinline__ void kda_fetch_v(const FwdArgs &a, int64_t t0, int len, int h, int nt, int lane,
+                                            uint32_t (&pv)[8]) {
+    constexpr uint32_t ES = IN_BF16 ? 2 : 4;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const uint32_t stride = static_cast<uint32_t>(a.hv) * D * ES;
+    const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(
+        reinterpret_cast<const unsigned char *>(a.v) + ((t0 * a.hv + h) * D) * ES, static_cast<uint32_t>(len) * stride);
+    uint32_t voff = 4 * lq * stride + (16 * nt + l16) * ES;
+    asm volatile("" : "+v"(voff));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t pair = 0u;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int mt = (2 * j + e) >> 2, r = (2 * j + e) & 3;
+            pair |= rd_bits<IN_BF16>(rv, voff + static_cast<uint32_t>(16 * mt + r) * stride) << (16 * e);
+        }
+        pv[j] = pair;
+    }
+}
+
 template <int D>
 struct KdaLds {
     static constexpr int PK = D + 16;
@@ -121,6 +181,25 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
                 H[mt][r] = (colwave && a.h0) ? a.h0[((n * a.hv + h) * D + 16 * mt + 4 * lq + r) * D + 16 * nt + l16] : 0.f;
     }
 
+    // Registers of the next chunk, loaded while the current one is processed:
+    // this thread's channel of g, q and k over its TPG tokens (q and k as bf16
+    // bits, packed in pairs), its wave's v values (rows 4 lq + r of the four
+    // token blocks, column 16 nt + l16) and, in wave 0, beta of its token.
+    const int ch = tid % D, grp = tid / D;
+    float pg[TPG];
+    uint32_t pqk[TPG], pv[8];
+    float pb = 0.f;
+#define GDR_KDA_FETCH(cc)                                                                               \
+    {                                                                                                   \
+        const int64_t t0_ = bos + C * (cc);                                                             \
+        const int len_ = static_cast<int>(eos - t0_ < C ? eos - t0_ : C);                               \
+        const int ln_ = tid & 63;                                                                       \
+        kda_fetch_gate<D, TPG, IN_BF16, GATE_BF16>(a, t0_, len_, h, hk, ch, grp, pg, pqk);              \
+        if (colwave) kda_fetch_v<D, IN_BF16>(a, t0_, len_, h, nt, ln_, pv);                             \
+        if (wave == 0) pb = ln_ < len_ ? load_scalar<GATE_BF16>(a.beta, (t0_ + ln_) * a.hv + h) : 0.f; \
+    }
+    GDR_KDA_FETCH(0)
+
     for (int64_t c = 0; c < nch; ++c) {
         int lane = tid & 63;   // opaque per iteration: keeps per-lane addresses inside the loop
         asm volatile("" : "+v"(lane));
@@ -129,21 +208,18 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
         const int len = static_cast<int>(eos - t0 < C ? eos - t0 : C);
 
         // ---- gates: per-channel prefix sums (log2 units), TPG tokens per thread
-        const int ch = tid % D, grp = tid / D;
         float G2[TPG];
         {
             float run = 0.f;
 #pragma unroll
             for (int i = 0; i < TPG; ++i) {
-                const int row = grp * TPG + i;
-                const float gv = row < len ? load_scalar<GATE_BF16>(a.g, ((t0 + row) * a.hv + h) * D + ch) : 0.f;
-                run += gv * kLog2e;
+                run += pg[i] * kLog2e;
                 G2[i] = run;
             }
         }
         __syncthreads();   // the previous chunk's reads of LDS are done
         sTot[grp * D + ch] = G2[TPG - 1];
-        if (wave == 0) sB[lane] = lane < len ? load_scalar<GATE_BF16>(a.beta, (t0 + lane) * a.hv + h) : 0.f;
+        if (wave == 0) sB[lane] = pb;
         __syncthreads();
         {
             float offs = 0.f, gm = 0.f, gl = 0.f;
@@ -163,17 +239,18 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
             for (int i = 0; i < TPG; ++i) {
                 const int row = grp * TPG + i;
                 const float x = G2[i] + offs - gm;
-                float qv = 0.f, kv = 0.f;
-                if (row < len) {
-                    qv = load_scalar<IN_BF16>(a.q, ((t0 + row) * a.hk + hk) * D + ch);
-                    kv = load_scalar<IN_BF16>(a.k, ((t0 + row) * a.hk + hk) * D + ch);
-                }
+                const float qv = kbf(static_cast<uint16_t>(pqk[i] & 0xFFFFu));
+                const float kv = kbf(static_cast<uint16_t>(pqk[i] >> 16));
                 const float e = fast_exp2(x), ei = fast_exp2(-x);
                 sQt[row * PK + ch] = bf16_bits(qv * e);
                 sKt[row * PK + ch] = bf16_bits(kv * e);
                 sKh[row * PK + ch] = bf16_bits(kv * ei);
             }
         }
+        uint32_t cv[8];   // this chunk's v values; the registers above take the next chunk
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cv[j] = pv[j];
+        if (c + 1 < nch) GDR_KDA_FETCH(c + 1)
         // zero A and P (blocks above the diagonal stay zero)
         for (int i = tid; i < 2 * C * PP / 8; i += kKdaThreads)
             reinterpret_cast<v4u32 *>(sA)[i] = v4u32{0u, 0u, 0u, 0u};
@@ -276,7 +353,8 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * mt + 4 * lq + r;
-                    const float vv = i < len ? load_scalar<IN_BF16>(a.v, ((t0 + i) * a.hv + h) * D + 16 * nt + l16) : 0.f;
+                    const uint32_t pair = cv[(4 * mt + r) >> 1];
+                    const float vv = kbf(static_cast<uint16_t>((r & 1) ? (pair >> 16) : (pair & 0xFFFFu)));
                     w[r] = sB[i] * (vv - X[mt][r]);
                 }
                 wb[mt] = cvt4(w);
@@ -337,6 +415,7 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(16 * mt + 4 * lq + r) * D + 16 * nt + l16] = H[mt][r];
     }
+#undef GDR_KDA_FETCH
 }
 
 template <int D, bool IN_BF16, bool GATE_BF16>
