@@ -217,39 +217,100 @@ int check_device() {
     return GDR_OK;
 }
 
-// Library-owned stream-ordered memory pool of a device for the small
-// per-call workspace.  Its release threshold keeps freed blocks reserved, so
-// an allocation never has to map memory again; the default pool hands its
-// memory back at synchronisation points, and re-mapping it now and then
-// stalled a call for tens of milliseconds.  Created on first use, kept until
-// the process ends (it holds at most the largest workspace asked for).
-hipError_t workspace_pool(hipMemPool_t *out) {
-    static std::mutex mu;
-    static hipMemPool_t pools[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
-    if (!pools[dev]) {
-        hipMemPoolProps props;
-        std::memset(&props, 0, sizeof(props));
-        props.allocType = hipMemAllocationTypePinned;
-        props.handleTypes = hipMemHandleTypeNone;
-        props.location.type = hipMemLocationTypeDevice;
-        props.location.id = dev;
-        hipMemPool_t pool = nullptr;
-        if ((e = hipMemPoolCreate(&pool, &props)) != hipSuccess) return e;
-        uint64_t keep = UINT64_MAX;
-        if ((e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) {
-            (void)hipMemPoolDestroy(pool);
-            return e;
-        }
-        pools[dev] = pool;
-    }
-    *out = pools[dev];
-    return hipSuccess;
+// Library-owned device workspaces, reused across calls.  On this runtime
+// freeing a stream-ordered allocation (hipFreeAsync) blocks the calling
+// thread until the stream has caught up, which serialised the host with the
+// GPU at every call.  Instead each device keeps a few buffers that are never
+// freed while in use: a call takes the next slot of a small ring (or the one
+// large slot, for the backward's multi-GB workspace), makes its stream wait on
+// the GPU for the slot's previous user (an event recorded after that user's
+// last kernel, so reuse is ordered across streams without a host wait), and
+// records the event again after its own kernels.  Slots are indexed by a
+// counter, never by stream or tensor identity; a slot only grows (its old
+// buffer is freed once the last user has finished), and the memory is kept
+// until the process ends.
+int launch_error(hipError_t e, const char *what) {
+    return fail(GDR_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
 }
+
+constexpr int kRing = 8;
+struct WsSlot {
+    std::mutex mu;
+    void *ptr = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool used = false;
+};
+struct WsDevice {
+    std::mutex mu;
+    unsigned next = 0;
+    WsSlot ring[kRing];
+    WsSlot big;
+};
+WsDevice g_ws[64];
+
+// Holds one slot from acquire() to release(); the slot's lock is kept in
+// between so that its event is recorded before anyone else can take it.
+class WsLease {
+  public:
+    int acquire(size_t bytes, bool big, hipStream_t stream, void **out) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(GDR_EDEVICE, "no current device");
+        WsDevice &D = g_ws[dev];
+        WsSlot *s;
+        if (big) {
+            s = &D.big;
+        } else {
+            std::lock_guard<std::mutex> g(D.mu);
+            s = &D.ring[D.next++ % kRing];
+        }
+        lock_ = std::unique_lock<std::mutex>(s->mu);
+        if (!s->ev && hipEventCreateWithFlags(&s->ev, hipEventDisableTiming) != hipSuccess) {
+            s->ev = nullptr;
+            return fail(GDR_ENOMEM, "workspace event could not be created");
+        }
+        if (s->cap < bytes) {
+            if (s->ptr) {
+                if (s->used) (void)hipEventSynchronize(s->ev);
+                (void)hipFree(s->ptr);
+                s->ptr = nullptr;
+                s->cap = 0;
+                s->used = false;
+            }
+            const size_t want = ((bytes > 65536 ? bytes : 65536) + 0xFFFFF) & ~static_cast<size_t>(0xFFFFF);
+            const hipError_t e = hipMalloc(&s->ptr, want);
+            if (e != hipSuccess) {
+                s->ptr = nullptr;
+                return fail(GDR_ENOMEM, "workspace of %zu bytes: %s", want, hipGetErrorString(e));
+            }
+            s->cap = want;
+        }
+        if (s->used && hipEventQuery(s->ev) != hipSuccess) {
+            const hipError_t e = hipStreamWaitEvent(stream, s->ev, 0);
+            if (e != hipSuccess) return launch_error(e, "workspace wait");
+        }
+        slot_ = s;
+        stream_ = stream;
+        *out = s->ptr;
+        return GDR_OK;
+    }
+    // After the call's last kernel that touches the workspace (also on error
+    // paths: whatever was enqueued is then ordered before the next user).
+    int release() {
+        if (!slot_) return GDR_OK;
+        const hipError_t e = hipEventRecord(slot_->ev, stream_);
+        if (e == hipSuccess) slot_->used = true;
+        slot_ = nullptr;
+        lock_.unlock();
+        return e == hipSuccess ? GDR_OK : launch_error(e, "workspace release");
+    }
+    ~WsLease() { (void)release(); }
+
+  private:
+    WsSlot *slot_ = nullptr;
+    hipStream_t stream_ = nullptr;
+    std::unique_lock<std::mutex> lock_;
+};
 
 // Machines of the dispatch-order model for a forward launch: work-groups
 // resident at once divided by the v-heads of a sequence (each XCD gets Hv/8
@@ -276,9 +337,6 @@ int order_groups(const gdr::FwdArgs &a) {
     return (groups >= 2 && groups <= 16 && a.n_seq > groups && a.n_seq <= 64) ? groups : 0;
 }
 
-int launch_error(hipError_t e, const char *what) {
-    return fail(GDR_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
-}
 
 // The forward launch shared by gdr_chunk_fwd and gdr_chunk_fwd_checkpoints
 // (hck: chunk-boundary states, or NULL).
@@ -335,34 +393,25 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     a.ck_offs = nullptr;
     a.ck_rows = rows;
 
-    void *ws = nullptr;
+    WsLease lease;
     if (cu_seqlens) {
         // order [N], then (checkpoints only) chunk offsets [N + 1]
         const size_t bytes = static_cast<size_t>(p.workspace_bytes) + (hck ? 4 * static_cast<size_t>(p.n_seq + 1) : 0);
-        hipMemPool_t pool = nullptr;
-        hipError_t e = workspace_pool(&pool);
-        if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, bytes, pool, stream);
-        if (e != hipSuccess) return fail(GDR_ENOMEM, "workspace of %lld bytes: %s", (long long)bytes,
-                                         hipGetErrorString(e));
+        void *ws = nullptr;
+        if ((rc = lease.acquire(bytes, false, stream, &ws))) return rc;
         int32_t *order = static_cast<int32_t *>(ws);
         int32_t *offs = hck ? order + p.n_seq : nullptr;
         const int groups = hck ? 0 : order_groups(a);
-        e = groups ? gdr::launch_order(a.cu, p.n_seq, groups, order, stream)
-                   : gdr::launch_prepare(a.cu, p.n_seq, offs, nullptr, 0, order, stream);
-        if (e != hipSuccess) {
-            (void)hipFreeAsync(ws, stream);
-            return launch_error(e, "chunk preparation kernel");
-        }
+        const hipError_t e = groups ? gdr::launch_order(a.cu, p.n_seq, groups, order, stream)
+                                    : gdr::launch_prepare(a.cu, p.n_seq, offs, nullptr, 0, order, stream);
+        if (e != hipSuccess) return launch_error(e, "chunk preparation kernel");
         a.order = order;
         a.ck_offs = offs;
     }
-    hipError_t e = gdr::launch_fwd(a, stream);
-    if (ws) {
-        const hipError_t fe = hipFreeAsync(ws, stream);
-        if (e == hipSuccess && fe != hipSuccess) return launch_error(fe, "workspace release");
-    }
+    const hipError_t e = gdr::launch_fwd(a, stream);
+    const int rr = lease.release();
     if (e != hipSuccess) return launch_error(e, "forward kernel");
-    return ok();
+    return rr ? rr : ok();
 }
 
 // Workspace of a backward call: chunk indices (varlen only), then per (chunk
@@ -449,14 +498,9 @@ int run_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     const bool varlen = cu_seqlens != nullptr;
     const int64_t rows = varlen ? p.nt_max : B * ((T + gdr::kChunk - 1) / gdr::kChunk);
     const BwdWorkspace wl = bwd_workspace(N, rows, Hv, d, varlen);
+    WsLease lease;
     void *ws = nullptr;
-    {
-        hipMemPool_t pool = nullptr;
-        hipError_t e = workspace_pool(&pool);
-        if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, wl.total, pool, stream);
-        if (e != hipSuccess)
-            return fail(GDR_ENOMEM, "workspace of %lld bytes: %s", (long long)wl.total, hipGetErrorString(e));
-    }
+    if ((rc = lease.acquire(wl.total, true, stream, &ws))) return rc;
     unsigned char *base = static_cast<unsigned char *>(ws);
     int32_t *offs = nullptr, *map = nullptr, *order = nullptr;
     const int32_t *cu = varlen ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
@@ -535,10 +579,9 @@ int run_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
         ba.scale = scale;
         e = gdr::launch_bwd(ba, stream);
     }
-    const hipError_t fe = hipFreeAsync(ws, stream);
+    const int rr = lease.release();
     if (e != hipSuccess) return launch_error(e, "backward kernels");
-    if (fe != hipSuccess) return launch_error(fe, "workspace release");
-    return ok();
+    return rr ? rr : ok();
 }
 
 // The per-channel-gate forward: g is [B, T, Hv, dk]; everything else is
@@ -585,21 +628,18 @@ int run_kda(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     a.in_bf16 = p.in_dtype == GDR_BF16;
     a.gate_bf16 = p.gate_dtype == GDR_BF16;
     a.scale = scale;
-    void *ws = nullptr;
+    WsLease lease;
     hipError_t e = hipSuccess;
     if (cu_seqlens) {   // longest sequences first
-        hipMemPool_t pool = nullptr;
-        e = workspace_pool(&pool);
-        if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, static_cast<size_t>(4 * p.n_seq), pool, stream);
-        if (e != hipSuccess) return fail(GDR_ENOMEM, "workspace: %s", hipGetErrorString(e));
+        void *ws = nullptr;
+        if ((rc = lease.acquire(static_cast<size_t>(4 * p.n_seq), false, stream, &ws))) return rc;
         a.order = static_cast<int32_t *>(ws);
         e = gdr::launch_prepare(a.cu, p.n_seq, nullptr, nullptr, 0, static_cast<int32_t *>(ws), stream);
     }
     if (e == hipSuccess) e = gdr::launch_kda_fwd(a, stream);
-    const hipError_t fe = ws ? hipFreeAsync(ws, stream) : hipSuccess;
+    const int rr = lease.release();
     if (e != hipSuccess) return launch_error(e, "per-channel-gate forward kernel");
-    if (fe != hipSuccess) return launch_error(fe, "workspace release");
-    return ok();
+    return rr ? rr : ok();
 }
 
 }  // namespace
@@ -794,20 +834,18 @@ int gdr_chunk_local_cumsum(const gdr_tensor *g, const gdr_tensor *cu_seqlens, co
     if (nt_max > 0x7FFFFFFFLL) return fail(GDR_ESHAPE, "too many chunks");
     void *ws = nullptr;
     const size_t bytes = static_cast<size_t>(nt_max) * 8;
-    hipMemPool_t pool = nullptr;
-    hipError_t e = workspace_pool(&pool);
-    if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, bytes, pool, stream);
-    if (e != hipSuccess) return fail(GDR_ENOMEM, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
+    WsLease lease;
+    if ((rc = lease.acquire(bytes, false, stream, &ws))) return rc;
+    hipError_t e;
     int32_t *map = static_cast<int32_t *>(ws);
     const int32_t *cu = static_cast<const int32_t *>(cu_seqlens->data);
     e = gdr::launch_prepare(cu, N, nullptr, map, nt_max, nullptr, stream);
     if (e == hipSuccess)
         e = gdr::launch_cumsum(g->data, gate_bf16, cu, map, nt_max, 1, T, T, static_cast<int32_t>(H),
                                static_cast<float *>(G->data), stream);
-    const hipError_t fe = hipFreeAsync(ws, stream);
+    const int rr = lease.release();
     if (e != hipSuccess) return launch_error(e, "chunk preparation / cumsum kernels");
-    if (fe != hipSuccess) return launch_error(fe, "workspace release");
-    return ok();
+    return rr ? rr : ok();
 }
 
 const char *gdr_last_error(void) { return g_last_error.c_str(); }

@@ -51,7 +51,7 @@ typedef enum {
     GDR_ESTRIDE = -4, /* strides are not compact row-major */
     GDR_EALIAS = -5,  /* an output overlaps an input or another output */
     GDR_EDEVICE = -6, /* current device is not gfx950 or cannot be queried */
-    GDR_ELAUNCH = -7, /* a kernel launch or a stream-ordered allocation failed */
+    GDR_ELAUNCH = -7, /* a kernel launch or a stream operation failed */
     GDR_ENOMEM = -8   /* device memory for the call's workspace could not be obtained */
 } gdr_status;
 
@@ -103,11 +103,14 @@ typedef struct {
  * Results do not depend on scheduling: ghost padding and repeated calls are
  * bitwise reproducible.
  *
- * Uses a small stream-ordered device workspace (4*N bytes, allocated and
- * freed on `stream`) when cu_seqlens is given.  It comes from a memory pool
- * the library creates per device on first use and keeps until the process
- * ends, with its release threshold raised so freed blocks stay reserved
- * (the pool holds at most the largest workspace requested).
+ * Uses a small device workspace (4*N bytes) when cu_seqlens is given.  The
+ * library keeps, per device, a ring of 8 reusable workspace buffers (and one
+ * more for the backward pass), each created on first use and kept until the
+ * process ends; it only grows.  A call takes the next buffer of the ring and,
+ * if its previous user may still be running, makes `stream` wait for it on
+ * the GPU (an event recorded after that user's kernels): no host wait, no
+ * allocation or free per call, correct across streams and threads.  The ring
+ * is indexed by a counter, not by stream or tensor identity.
  */
 int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
                   const gdr_tensor *g, const gdr_tensor *beta, const gdr_tensor *cu_seqlens,
@@ -171,7 +174,9 @@ int gdr_chunk_fwd_checkpoints(const gdr_tensor *q, const gdr_tensor *k, const gd
  * reverse pass over the chunks of each sequence, and the per-chunk gradients.
  * Numerics: bf16 MFMA operands, fp32 accumulation and fp32 state gradients.
  *
- * Workspace: stream-ordered, from the library's pool (see gdr_chunk_fwd), of
+ * Workspace: the library's large per-device buffer (reused like the ring of
+ * gdr_chunk_fwd: concurrent backward calls on one device are ordered on the
+ * GPU), of
  * R * Hv * (6 d^2 + 512 d + 8192) bytes plus 4 (2N + 1 + 2R) for the
  * chunk indices, R = ceil(T/64) + N with cu_seqlens else B * ceil(T/64).
  * About 5.7 GB for 65536 tokens, 32 v-heads, d = 128.  Errors as
@@ -315,8 +320,8 @@ int gdr_dispatch_order(const gdr_tensor *cu_seqlens, int32_t groups, const gdr_t
  *   cu_seqlens  [N+1] int32 or NULL (B fixed-length rows)
  *   G           [B, T, H] f32 out (rows outside every segment not written)
  *
- * Uses a stream-ordered workspace for the chunk map (8 * nt_max bytes) from the
- * same per-device pool as gdr_chunk_fwd.
+ * Uses a workspace for the chunk map (8 * nt_max bytes) from the same
+ * per-device ring as gdr_chunk_fwd.
  */
 int gdr_chunk_local_cumsum(const gdr_tensor *g, const gdr_tensor *cu_seqlens,
                            const gdr_tensor *G, hipStream_t stream);
