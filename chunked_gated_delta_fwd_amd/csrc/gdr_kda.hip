@@ -33,6 +33,8 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gdr {
 namespace {
 
@@ -48,25 +50,22 @@ __device__ __forceinline__ bf16x8 kfrag_cols(const uint16_t *M, int pitch, int c
 }
 __device__ __forceinline__ float kbf(uint16_t u) { return __uint_as_float(static_cast<uint32_t>(u) << 16); }
 
-// One element at byte offset off (the whole offset in the range-checked
-// vector offset) of a buffer range, as float (bf16 or f32) or as bf16 bits
-// (f32 rounded); past the range it reads 0.
 template <bool BF16>
-__device__ __forceinline__ float rd_f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    if constexpr (BF16)
-        return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0)) << 16);
+using VRaw = typename std::conditional<BF16, __bf16, float>::type;
+// One element at byte offset off (the whole offset in the range-checked
+// vector offset) of a buffer range, as loaded; past the range it reads 0.
+template <bool BF16>
+__device__ __forceinline__ VRaw<BF16> rd_raw(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (BF16) return __builtin_bit_cast(__bf16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
     else return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
-template <bool BF16>
-__device__ __forceinline__ uint32_t rd_bits(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    if constexpr (BF16) return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
-    else return bf16_bits(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)));
-}
-// Channel ch of g, q and k for the TPG tokens of scan group grp, through
-// ranges that end at the segment's end.
+// Channel ch of g, q and k for the TPG tokens of scan group grp, one element
+// per register as loaded (nothing is computed on them here, so the loads stay
+// in flight), through ranges that end at the segment's end.
 template <int D, int TPG, bool IN_BF16, bool GATE_BF16>
 __device__ __forceinline__ void kda_fetch_gate(const FwdArgs &a, int64_t t0, int len, int h, int hk, int ch,
-                                               int grp, float (&pg)[TPG], uint32_t (&pqk)[TPG]) {
+                                               int grp, VRaw<GATE_BF16> (&pg)[TPG], VRaw<IN_BF16> (&pq)[TPG],
+                                               VRaw<IN_BF16> (&pk)[TPG]) {
     constexpr uint32_t ES = IN_BF16 ? 2 : 4, GS = GATE_BF16 ? 2 : 4;
     const uint32_t gstride = static_cast<uint32_t>(a.hv) * D * GS, qstride = static_cast<uint32_t>(a.hk) * D * ES;
     const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(
@@ -80,15 +79,18 @@ __device__ __forceinline__ void kda_fetch_gate(const FwdArgs &a, int64_t t0, int
 #pragma unroll
     for (int i = 0; i < TPG; ++i) {
         const uint32_t row = static_cast<uint32_t>(grp * TPG + i);
-        pg[i] = rd_f<GATE_BF16>(rg, row * gstride + chv * GS);
-        const uint32_t qo = row * qstride + chv * ES;
-        pqk[i] = rd_bits<IN_BF16>(rq, qo) | (rd_bits<IN_BF16>(rk, qo) << 16);
+        pg[i] = rd_raw<GATE_BF16>(rg, row * gstride + chv * GS);
+        pq[i] = rd_raw<IN_BF16>(rq, row * qstride + chv * ES);
+        pk[i] = rd_raw<IN_BF16>(rk, row * qstride + chv * ES);
     }
 }
-// v at rows 16 mt + 4 lq + r, column 16 nt + l16, packed in pairs (zero past len).
+
+// v at rows 16 mt + 4 lq + r, column 16 nt + l16, one element per register
+// as loaded (bf16, or f32 rounded at use), nothing computed on them here so
+// that the loads stay in flight (zero past len).
 template <int D, bool IN_BF16>
 __device__ __forceinline__ void kda_fetch_v(const FwdArgs &a, int64_t t0, int len, int h, int nt, int lane,
-                                            uint32_t (&pv)[8]) {
+                                            VRaw<IN_BF16> (&pv)[16]) {
     constexpr uint32_t ES = IN_BF16 ? 2 : 4;
     const int l16 = lane & 15, lq = lane >> 4;
     const uint32_t stride = static_cast<uint32_t>(a.hv) * D * ES;
@@ -97,15 +99,21 @@ __device__ __forceinline__ void kda_fetch_v(const FwdArgs &a, int64_t t0, int le
     uint32_t voff = 4 * lq * stride + (16 * nt + l16) * ES;
     asm volatile("" : "+v"(voff));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        uint32_t pair = 0u;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int mt = (2 * j + e) >> 2, r = (2 * j + e) & 3;
-            pair |= rd_bits<IN_BF16>(rv, voff + static_cast<uint32_t>(16 * mt + r) * stride) << (16 * e);
-        }
-        pv[j] = pair;
+    for (int j = 0; j < 16; ++j) {
+        const uint32_t off = voff + static_cast<uint32_t>(16 * (j >> 2) + (j & 3)) * stride;
+        if constexpr (IN_BF16) pv[j] = __builtin_bit_cast(__bf16, __builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, 0));
+        else pv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0));
     }
+}
+// beta of token t0 + lane (zero past len), as loaded
+template <bool GATE_BF16>
+__device__ __forceinline__ VRaw<GATE_BF16> fetch_beta(const FwdArgs &a, int64_t t0, int len, int h, int lane) {
+    constexpr uint32_t GS = GATE_BF16 ? 2 : 4;
+    const uint32_t stride = static_cast<uint32_t>(a.hv) * GS;
+    const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(
+        reinterpret_cast<const unsigned char *>(a.beta) + (t0 * a.hv + h) * GS, static_cast<uint32_t>(len) * stride);
+    if constexpr (GATE_BF16) return __builtin_bit_cast(__bf16, __builtin_amdgcn_raw_buffer_load_b16(rb, lane * stride, 0, 0));
+    else return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lane * stride, 0, 0));
 }
 
 template <int D>
@@ -113,16 +121,16 @@ struct KdaLds {
     static constexpr int PK = D + 16;
     static constexpr int PP = C + 8;
     static constexpr int PD = 24;
-    static constexpr int NG = kKdaThreads / D;   // token groups of the gate scan
     static constexpr int oQt = 0;                  // q~ [64][PK]
     static constexpr int oKt = oQt + C * PK * 2;   // k~
     static constexpr int oKh = oKt + C * PK * 2;   // k^
-    static constexpr int oS = oKh + C * PK * 2;    // S_m bf16 [D][PK]
+    static constexpr int oS = oKh + C * PK * 2;    // S_m^T bf16 [dv][PK]
     static constexpr int oA = oS + D * PK * 2;     // diag(b) A~ strictly lower [i][j]
     static constexpr int oP = oA + C * PP * 2;     // scale tril(q~ k^^T) [i][j]
     static constexpr int oT = oP + C * PP * 2;     // T^T [j][i]
     static constexpr int oDi = oT + C * PP * 2;    // inverses of the diagonal blocks [4][16][PD]
     static constexpr int oV = oDi + 4 * 16 * PD * 2;   // f32 [D] x3: e^{G_m}, e^{G_L}, e^{G_L - G_m}; [64] b
+    static constexpr int NG = kKdaThreads / D;     // token groups of the gate scan
     static constexpr int oTot = oV + (3 * D + C) * 4;  // f32 [NG][D] group totals of the scan
     static constexpr int bytes = oTot + NG * D * 4;
 };
@@ -182,21 +190,25 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
     }
 
     // Registers of the next chunk, loaded while the current one is processed:
-    // this thread's channel of g, q and k over its TPG tokens (q and k as bf16
-    // bits, packed in pairs), its wave's v values (rows 4 lq + r of the four
-    // token blocks, column 16 nt + l16) and, in wave 0, beta of its token.
+    // this thread's channel of g, q and k over its TPG tokens, its wave's v
+    // values (rows 4 lq + r of the four token blocks, column 16 nt + l16) and
+    // beta of its lane's token, each as loaded.
     const int ch = tid % D, grp = tid / D;
-    float pg[TPG];
-    uint32_t pqk[TPG], pv[8];
-    float pb = 0.f;
+    VRaw<GATE_BF16> pg[TPG];
+    VRaw<IN_BF16> pq[TPG], pk[TPG];
+    VRaw<IN_BF16> pv[16];
+    VRaw<GATE_BF16> pb = 0;
+    // Unconditional: past the last chunk the ranges are empty and read zeros
+    // (a branch here would make the compiler wait for the loads at its join).
 #define GDR_KDA_FETCH(cc)                                                                               \
     {                                                                                                   \
         const int64_t t0_ = bos + C * (cc);                                                             \
-        const int len_ = static_cast<int>(eos - t0_ < C ? eos - t0_ : C);                               \
+        const int64_t r_ = eos - t0_;                                                                   \
+        const int len_ = static_cast<int>(r_ <= 0 ? 0 : r_ < C ? r_ : C);                               \
         const int ln_ = tid & 63;                                                                       \
-        kda_fetch_gate<D, TPG, IN_BF16, GATE_BF16>(a, t0_, len_, h, hk, ch, grp, pg, pqk);              \
-        if (colwave) kda_fetch_v<D, IN_BF16>(a, t0_, len_, h, nt, ln_, pv);                             \
-        if (wave == 0) pb = ln_ < len_ ? load_scalar<GATE_BF16>(a.beta, (t0_ + ln_) * a.hv + h) : 0.f; \
+        kda_fetch_gate<D, TPG, IN_BF16, GATE_BF16>(a, t0_, len_, h, hk, ch, grp, pg, pq, pk);          \
+        if (D == 128 || colwave) kda_fetch_v<D, IN_BF16>(a, t0_, len_, h, nt, ln_, pv);                 \
+        pb = fetch_beta<GATE_BF16>(a, t0_, len_, h, ln_);                                               \
     }
     GDR_KDA_FETCH(0)
 
@@ -213,13 +225,13 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
             float run = 0.f;
 #pragma unroll
             for (int i = 0; i < TPG; ++i) {
-                run += pg[i] * kLog2e;
+                run += static_cast<float>(pg[i]) * kLog2e;
                 G2[i] = run;
             }
         }
         __syncthreads();   // the previous chunk's reads of LDS are done
         sTot[grp * D + ch] = G2[TPG - 1];
-        if (wave == 0) sB[lane] = pb;
+        if (wave == 0) sB[lane] = static_cast<float>(pb);
         __syncthreads();
         {
             float offs = 0.f, gm = 0.f, gl = 0.f;
@@ -239,32 +251,32 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
             for (int i = 0; i < TPG; ++i) {
                 const int row = grp * TPG + i;
                 const float x = G2[i] + offs - gm;
-                const float qv = kbf(static_cast<uint16_t>(pqk[i] & 0xFFFFu));
-                const float kv = kbf(static_cast<uint16_t>(pqk[i] >> 16));
+                const float qv = static_cast<float>(static_cast<__bf16>(pq[i]));
+                const float kv = static_cast<float>(static_cast<__bf16>(pk[i]));
                 const float e = fast_exp2(x), ei = fast_exp2(-x);
                 sQt[row * PK + ch] = bf16_bits(qv * e);
                 sKt[row * PK + ch] = bf16_bits(kv * e);
                 sKh[row * PK + ch] = bf16_bits(kv * ei);
             }
         }
-        uint32_t cv[8];   // this chunk's v values; the registers above take the next chunk
+        VRaw<IN_BF16> cv[16];   // this chunk's v values; the registers above take the next chunk
 #pragma unroll
-        for (int j = 0; j < 8; ++j) cv[j] = pv[j];
-        if (c + 1 < nch) GDR_KDA_FETCH(c + 1)
+        for (int j = 0; j < 16; ++j) cv[j] = pv[j];
+        GDR_KDA_FETCH(c + 1)
         // zero A and P (blocks above the diagonal stay zero)
         for (int i = tid; i < 2 * C * PP / 8; i += kKdaThreads)
             reinterpret_cast<v4u32 *>(sA)[i] = v4u32{0u, 0u, 0u, 0u};
         __syncthreads();
 
-        // ---- S_m = diag(e^{G_m}) H into LDS (bf16 [dk][dv])
+        // ---- S_m^T = (diag(e^{G_m}) H)^T into LDS (bf16 [dv][dk]: four dk per 8-byte store)
         if (colwave) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt) {
+                f32x4 sm;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * mt + 4 * lq + r;
-                    sS[row * PK + 16 * nt + l16] = bf16_bits(H[mt][r] * sEm[row]);
-                }
+                for (int r = 0; r < 4; ++r) sm[r] = H[mt][r] * sEm[16 * mt + 4 * lq + r];
+                st4(sS + (16 * nt + l16) * PK + 16 * mt + 4 * lq, cvt4(sm));
+            }
         }
         // ---- the ten lower blocks of A = diag(b) k~ k^^T and of P = scale q~ k^^T
         for (int t = wave; t < 20; t += 8) {
@@ -312,7 +324,7 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
         for (int mt = 0; mt < 4; ++mt) X[mt] = QS[mt] = zero4();
         if (colwave) {
             for (int kk = 0; kk < D / 32; ++kk) {
-                const bf16x8 bs = kfrag_cols(sS, PK, 16 * nt, 32 * kk, l16, lq);
+                const bf16x8 bs = kfrag_rows(sS, PK, 16 * nt, 32 * kk, l16, lq);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     X[mt] = mfma32(kfrag_rows(sKt, PK, 16 * mt, 32 * kk, l16, lq), bs, X[mt]);
@@ -353,8 +365,7 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * mt + 4 * lq + r;
-                    const uint32_t pair = cv[(4 * mt + r) >> 1];
-                    const float vv = kbf(static_cast<uint16_t>((r & 1) ? (pair >> 16) : (pair & 0xFFFFu)));
+                    const float vv = static_cast<float>(static_cast<__bf16>(cv[4 * mt + r]));
                     w[r] = sB[i] * (vv - X[mt][r]);
                 }
                 wb[mt] = cvt4(w);
