@@ -437,7 +437,7 @@ def read_traffic(path: str, workload: str):
 def kernel_source_sha() -> str:
     import hashlib
     h = hashlib.sha256()
-    for name in ("gdr_kernels.hip", "gdr_api.cpp", "gdr_internal.h"):
+    for name in ("gdr_kernels.hip", "gdr_device.h", "gdr_api.cpp", "gdr_internal.h"):
         with open(os.path.join(ROOT, "chunked_gated_delta_fwd_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
