@@ -83,20 +83,6 @@ __device__ __forceinline__ void store_elem(void *p, int64_t i, float v) {
     else reinterpret_cast<float *>(p)[i] = v;
 }
 
-// Rows t0 .. t0+len-1 of a [tokens, heads, D] tensor (one head) into LDS
-// [64][pitch] bf16; rows from len on are zero.
-template <int D, bool BF16, int NT>
-__device__ __forceinline__ void stage_rows(uint16_t *dst, int pitch, const void *src, int64_t t0, int len,
-                                           int heads, int head, int tid) {
-    constexpr int PR = D / 8;
-    for (int i = tid; i < C * PR; i += NT) {
-        const int row = i / PR, col = 8 * (i % PR);
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (row < len) v = load8<BF16>(src, ((t0 + row) * heads + head) * D + col);
-        *reinterpret_cast<uint4 *>(dst + row * pitch + col) = v;
-    }
-}
-
 // The same rows into registers, 16 bytes of bf16 per piece, through a buffer
 // resource that ends at the last row (rows from len on read as zero).
 template <int D, bool BF16, int NP, int NT>
@@ -110,6 +96,38 @@ __device__ __forceinline__ void fetch_rows(v4u32 (&dst)[NP], const void *src, in
     for (int j = 0; j < NP; ++j) {
         const int i = tid + j * NT, row = i / PR, col = 8 * (i % PR);
         dst[j] = __builtin_bit_cast(v4u32, buf_load8<BF16>(r, static_cast<uint32_t>((row * heads * D + col) * ES)));
+    }
+}
+
+// Rows t0 .. t0+len-1 of a [tokens, heads, D] tensor (one head) into LDS
+// [64][pitch] bf16 (rows from len on are zero): every load is issued before
+// the first store.
+template <int D, bool BF16, int NT>
+__device__ __forceinline__ void stage_rows(uint16_t *dst, int pitch, const void *src, int64_t t0, int len,
+                                           int heads, int head, int tid) {
+    constexpr int PR = D / 8, NP = C * PR / NT;
+    v4u32 r[NP];
+    fetch_rows<D, BF16, NP, NT>(r, src, t0, len, heads, head, tid);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        const int i = tid + j * NT;
+        *reinterpret_cast<v4u32 *>(dst + (i / PR) * pitch + 8 * (i % PR)) = r[j];
+    }
+}
+// Two such row blocks (of different tensors), all loads first.
+template <int D, bool BF16, int NT>
+__device__ __forceinline__ void stage_rows2(uint16_t *d0, const void *s0, int heads0, int head0, uint16_t *d1,
+                                            const void *s1, int heads1, int head1, int pitch, int64_t t0, int len,
+                                            int tid) {
+    constexpr int PR = D / 8, NP = C * PR / NT;
+    v4u32 r0[NP], r1[NP];
+    fetch_rows<D, BF16, NP, NT>(r0, s0, t0, len, heads0, head0, tid);
+    fetch_rows<D, BF16, NP, NT>(r1, s1, t0, len, heads1, head1, tid);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        const int i = tid + j * NT, off = (i / PR) * pitch + 8 * (i % PR);
+        *reinterpret_cast<v4u32 *>(d0 + off) = r0[j];
+        *reinterpret_cast<v4u32 *>(d1 + off) = r1[j];
     }
 }
 
@@ -222,8 +240,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lq = lane >> 4;
     const int64_t rh = static_cast<int64_t>(blockIdx.x) * a.hv + h;
 
-    stage_rows<D, IN_BF16, kBwdThreads>(sQ, PK, a.q, p.t0, p.len, a.hk, hk, tid);
-    stage_rows<D, IN_BF16, kBwdThreads>(sK, PK, a.k, p.t0, p.len, a.hk, hk, tid);
+    stage_rows2<D, IN_BF16, kBwdThreads>(sQ, a.q, a.hk, hk, sK, a.k, a.hk, hk, PK, p.t0, p.len, tid);
     stage_rows<D, IN_BF16, kBwdThreads>(sO, PK, a.dout, p.t0, p.len, a.hv, h, tid);
     for (int i = tid; i < 2 * C * PP / 8; i += kBwdThreads)   // A and P^T (adjacent): blocks above the diagonal stay zero
         reinterpret_cast<uint4 *>(sA)[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -611,8 +628,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
     const bool colwave = wave < NTD;   // owns column tile `wave` in the column-split phases
     const int nt = wave;
 
-    stage_rows<D, IN_BF16, kBwdThreads>(sQ, PK, a.q, p.t0, p.len, a.hk, hk, tid);
-    stage_rows<D, IN_BF16, kBwdThreads>(sK, PK, a.k, p.t0, p.len, a.hk, hk, tid);
+    stage_rows2<D, IN_BF16, kBwdThreads>(sQ, a.q, a.hk, hk, sK, a.k, a.hk, hk, PK, p.t0, p.len, tid);
 
     f32x4 accQ[4], accK[4];
 #pragma unroll
@@ -635,18 +651,36 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
             for (int mt = 0; mt < 4; ++mt) ub[mt] = *reinterpret_cast<const bf16x4 *>(ug + ((mt * NTD + nt) * 64 + lane) * 4);
         }
         __syncthreads();   // the previous v-head's reads of LDS are done
-        stage_rows<D, IN_BF16, kBwdThreads>(sV, PK, a.v, p.t0, p.len, a.hv, h, tid);
-        stage_rows<D, IN_BF16, kBwdThreads>(sO, PK, a.dout, p.t0, p.len, a.hv, h, tid);
-        for (int i = tid; i < D * D / 4; i += kBwdThreads) {
-            const int row = i / (D / 4), col = 4 * (i % (D / 4));
-            const f32x4 v = Sg ? *reinterpret_cast<const f32x4 *>(Sg + row * D + col) : zero4();
-            st4(sS + row * PK + col, cvt4(v));
-        }
         {
+            // all of this v-head's staging loads are issued before the first store
+            constexpr int PR = D / 8, NP = C * PR / kBwdThreads, NS = D * D / 4 / kBwdThreads, NT8 = C * C / 8 / kBwdThreads;
+            v4u32 rv[NP], ro[NP], rt[NT8];
+            f32x4 rs[NS];
+            fetch_rows<D, IN_BF16, NP, kBwdThreads>(rv, a.v, p.t0, p.len, a.hv, h, tid);
+            fetch_rows<D, IN_BF16, NP, kBwdThreads>(ro, a.dout, p.t0, p.len, a.hv, h, tid);
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                const int i = tid + j * kBwdThreads;
+                rs[j] = Sg ? *reinterpret_cast<const f32x4 *>(Sg + (i / (D / 4)) * D + 4 * (i % (D / 4))) : zero4();
+            }
             const uint16_t *tg = a.tmat + rh * (C * C);
-            for (int i = tid; i < C * C / 8; i += kBwdThreads) {
-                const int row = i / (C / 8), col = 8 * (i % (C / 8));
-                *reinterpret_cast<uint4 *>(sT + row * PP + col) = *reinterpret_cast<const uint4 *>(tg + row * C + col);
+#pragma unroll
+            for (int j = 0; j < NT8; ++j) rt[j] = *reinterpret_cast<const v4u32 *>(tg + 8 * (tid + j * kBwdThreads));
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                const int i = tid + j * kBwdThreads, off = (i / PR) * PK + 8 * (i % PR);
+                *reinterpret_cast<v4u32 *>(sV + off) = rv[j];
+                *reinterpret_cast<v4u32 *>(sO + off) = ro[j];
+            }
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                const int i = tid + j * kBwdThreads;
+                st4(sS + (i / (D / 4)) * PK + 4 * (i % (D / 4)), cvt4(rs[j]));
+            }
+#pragma unroll
+            for (int j = 0; j < NT8; ++j) {
+                const int i = tid + j * kBwdThreads;
+                *reinterpret_cast<v4u32 *>(sT + (i / (C / 8)) * PP + 8 * (i % (C / 8))) = rt[j];
             }
         }
         if (wave == 0) {
