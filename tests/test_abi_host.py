@@ -256,3 +256,87 @@ def test_decode_rejects_heads_and_dims(lib):
     assert "multiple of Hk" in lib.gdr_last_error().decode()
     assert _dec_call(lib, dec_descs(d=96)) == -2
     assert "64 or 128" in lib.gdr_last_error().decode()
+
+
+# --- backward and per-channel-gate entry points (validation only) ---------------
+
+def bwd_descs(B=1, T=256, Hk=2, Hv=4, d=128, dt=GDR_BF16, N=3, dht=True, dh0=True):
+    A = Alloc()   # one allocator: every descriptor is disjoint from every other
+    return dict(q=A(dt, [B, T, Hk, d]), k=A(dt, [B, T, Hk, d]), v=A(dt, [B, T, Hv, d]),
+                g=A(GDR_BF16, [B, T, Hv]), beta=A(GDR_BF16, [B, T, Hv]), cu_seqlens=A(GDR_I32, [N + 1]),
+                h0=A(GDR_F32, [N, Hv, d, d]), do=A(dt, [B, T, Hv, d]), dht=A(GDR_F32, [N, Hv, d, d]) if dht else None,
+                dq=A(dt, [B, T, Hk, d]), dk=A(dt, [B, T, Hk, d]), dv=A(dt, [B, T, Hv, d]),
+                dg=A(GDR_F32, [B, T, Hv]), dbeta=A(GDR_F32, [B, T, Hv]),
+                dh0=A(GDR_F32, [N, Hv, d, d]) if dh0 else None)
+
+
+BWD_ORDER = ("q", "k", "v", "g", "beta", "cu_seqlens", "h0", "do", "dht", "dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def _bwd_call(lib, d):
+    return lib.gdr_chunk_bwd(*[None if d[n] is None else d[n].ref for n in BWD_ORDER], ctypes.c_float(0.1), None)
+
+
+@pytest.mark.parametrize("mutate,status,text", [
+    (lambda d, A: d.update(do=None), -1, "do: descriptor is NULL"),
+    (lambda d, A: d.update(do=A(GDR_BF16, [1, 256, 4, 64])), -2, "do: shape"),
+    (lambda d, A: d.update(do=A(GDR_F32, [1, 256, 4, 128])), -3, "share one dtype"),
+    (lambda d, A: d.update(dht=A(GDR_BF16, [3, 4, 128, 128])), -3, "dht: dtype"),
+    (lambda d, A: d.update(dht=A(GDR_F32, [2, 4, 128, 128])), -2, "dht: shape"),
+    (lambda d, A: d.update(dq=None), -1, "dq: descriptor is NULL"),
+    (lambda d, A: d.update(dq=A(GDR_F32, [1, 256, 2, 128])), -3, "dq: dtype"),
+    (lambda d, A: d.update(dk=A(GDR_BF16, [1, 256, 4, 128])), -2, "dk: shape"),
+    (lambda d, A: d.update(dv=A(GDR_BF16, [1, 256, 2, 128])), -2, "dv: shape"),
+    (lambda d, A: d.update(dg=A(GDR_BF16, [1, 256, 4])), -3, "dg: dtype"),
+    (lambda d, A: d.update(dbeta=A(GDR_F32, [1, 255, 4])), -2, "dbeta: shape"),
+    (lambda d, A: d.update(dh0=A(GDR_F32, [3, 4, 64, 128])), -2, "dh0: shape"),
+    (lambda d, A: d.update(dq=describe(d["q"].t.data, GDR_BF16, [1, 256, 2, 128])), -5, "overlaps an input"),
+    (lambda d, A: d.update(dv=describe(d["do"].t.data, GDR_BF16, [1, 256, 4, 128])), -5, "overlaps an input"),
+    (lambda d, A: d.update(dk=describe(d["dq"].t.data, GDR_BF16, [1, 256, 2, 128])), -5, "outputs overlap"),
+])
+def test_bwd_rejections(lib, mutate, status, text):
+    d = bwd_descs()
+    mutate(d, Alloc())
+    assert _bwd_call(lib, d) == status, lib.gdr_last_error()
+    assert text in lib.gdr_last_error().decode(), lib.gdr_last_error()
+
+
+def test_bwd_accepts_optional_dht_dh0_then_needs_a_device(lib):
+    """With every descriptor valid (NULL dht and dh0 allowed) the call gets as
+    far as the device check."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except Exception:
+        pass
+    assert _bwd_call(lib, bwd_descs(dht=False, dh0=False)) == -6
+
+
+KDA_ORDER = ("q", "k", "v", "g", "beta", "cu_seqlens", "h0", "o", "ht")
+
+
+def _kda_call(lib, d):
+    return lib.gdr_chunk_kda_fwd(*[None if d[n] is None else d[n].ref for n in KDA_ORDER], ctypes.c_float(0.1), None)
+
+
+def kda_descs(B=1, T=256, Hk=2, Hv=4, d=128, dt=GDR_BF16, N=3):
+    A = Alloc()
+    return dict(q=A(dt, [B, T, Hk, d]), k=A(dt, [B, T, Hk, d]), v=A(dt, [B, T, Hv, d]),
+                g=A(GDR_BF16, [B, T, Hv, d]), beta=A(GDR_BF16, [B, T, Hv]), cu_seqlens=A(GDR_I32, [N + 1]),
+                h0=A(GDR_F32, [N, Hv, d, d]), o=A(dt, [B, T, Hv, d]), ht=A(GDR_F32, [N, Hv, d, d]))
+
+
+@pytest.mark.parametrize("mutate,status,text", [
+    (lambda d, A: d.update(g=A(GDR_BF16, [1, 256, 4])), -2, "g: expected 4 dimensions"),
+    (lambda d, A: d.update(g=A(GDR_BF16, [1, 256, 4, 64])), -2, "g: shape"),
+    (lambda d, A: d.update(g=A(GDR_F32, [1, 256, 4, 128])), -3, "g and beta must share"),
+    (lambda d, A: d.update(beta=A(GDR_BF16, [1, 256, 3])), -2, "g and beta"),
+    (lambda d, A: d.update(o=describe(d["g"].t.data, GDR_BF16, [1, 256, 4, 128])), -5, "o overlaps"),
+    (lambda d, A: d.update(ht=describe(d["g"].t.data, GDR_F32, [3, 4, 128, 128])), -5, "ht overlaps"),
+])
+def test_kda_rejections(lib, mutate, status, text):
+    d = kda_descs()
+    mutate(d, Alloc())
+    assert _kda_call(lib, d) == status, lib.gdr_last_error()
+    assert text in lib.gdr_last_error().decode(), lib.gdr_last_error()
