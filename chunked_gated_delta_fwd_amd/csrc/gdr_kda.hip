@@ -24,10 +24,11 @@
 // One work-group of 8 waves per (sequence, v-head) walks its chunks in order;
 // wave w owns dv columns [16w, 16w + 16) of the fp32 state (MFMA C tiles, rows
 // dk).  Per chunk: the gate scan (all threads: one channel and a quarter of the
-// tokens each), the gated operands into LDS, S_m into LDS, the ten lower
-// blocks of A and of P, the inverse T = (I + A)^-1 (16x16 diagonal inverses by
-// fp32 substitution, off-diagonal blocks by a chain of MFMA products), then per
-// wave X, U, O and the state update of its columns.
+// tokens each) and the gated operands into LDS; the ten lower blocks of A and
+// of P, and beside them each wave's k~ S_m and q~ S_m (S_m taken from the
+// wave's own state registers, whose C-tile layout is the B operand's); the
+// four 16x16 diagonal inverses of I + A by fp32 substitution; then per wave U
+// by block forward substitution over its columns, O and the state update.
 #include "gdr_internal.h"
 #include "gdr_device.h"
 
@@ -124,11 +125,9 @@ struct KdaLds {
     static constexpr int oQt = 0;                  // q~ [64][PK]
     static constexpr int oKt = oQt + C * PK * 2;   // k~
     static constexpr int oKh = oKt + C * PK * 2;   // k^
-    static constexpr int oS = oKh + C * PK * 2;    // S_m^T bf16 [dv][PK]
-    static constexpr int oA = oS + D * PK * 2;     // diag(b) A~ strictly lower [i][j]
+    static constexpr int oA = oKh + C * PK * 2;    // diag(b) A~ strictly lower [i][j]
     static constexpr int oP = oA + C * PP * 2;     // scale tril(q~ k^^T) [i][j]
-    static constexpr int oT = oP + C * PP * 2;     // T^T [j][i]
-    static constexpr int oDi = oT + C * PP * 2;    // inverses of the diagonal blocks [4][16][PD]
+    static constexpr int oDi = oP + C * PP * 2;    // inverses of the diagonal blocks [4][16][PD]
     static constexpr int oV = oDi + 4 * 16 * PD * 2;   // f32 [D] x3: e^{G_m}, e^{G_L}, e^{G_L - G_m}; [64] b
     static constexpr int NG = kKdaThreads / D;     // token groups of the gate scan
     static constexpr int oTot = oV + (3 * D + C) * 4;  // f32 [NG][D] group totals of the scan
@@ -146,10 +145,8 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
     uint16_t *sQt = reinterpret_cast<uint16_t *>(lds + Ly::oQt);
     uint16_t *sKt = reinterpret_cast<uint16_t *>(lds + Ly::oKt);
     uint16_t *sKh = reinterpret_cast<uint16_t *>(lds + Ly::oKh);
-    uint16_t *sS = reinterpret_cast<uint16_t *>(lds + Ly::oS);
     uint16_t *sA = reinterpret_cast<uint16_t *>(lds + Ly::oA);
     uint16_t *sP = reinterpret_cast<uint16_t *>(lds + Ly::oP);
-    uint16_t *sT = reinterpret_cast<uint16_t *>(lds + Ly::oT);
     uint16_t *sDi = reinterpret_cast<uint16_t *>(lds + Ly::oDi);
     float *sEm = reinterpret_cast<float *>(lds + Ly::oV);
     float *sEL = sEm + D;
@@ -268,16 +265,6 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
             reinterpret_cast<v4u32 *>(sA)[i] = v4u32{0u, 0u, 0u, 0u};
         __syncthreads();
 
-        // ---- S_m^T = (diag(e^{G_m}) H)^T into LDS (bf16 [dv][dk]: four dk per 8-byte store)
-        if (colwave) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                f32x4 sm;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sm[r] = H[mt][r] * sEm[16 * mt + 4 * lq + r];
-                st4(sS + (16 * nt + l16) * PK + 16 * mt + 4 * lq, cvt4(sm));
-            }
-        }
         // ---- the ten lower blocks of A = diag(b) k~ k^^T and of P = scale q~ k^^T
         for (int t = wave; t < 20; t += 8) {
             const bool ka = t < 10;
@@ -297,10 +284,31 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
                 else sP[i * PP + j] = bf16_bits(j <= i ? a.scale * acc[r] : 0.f);
             }
         }
+        // ---- meanwhile k~ S_m and q~ S_m for this wave's dv tile, with
+        // S_m = diag(e^{G_m}) H taken from the wave's own state registers
+        f32x4 X[4], QS[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) X[mt] = QS[mt] = zero4();
+        if (colwave) {
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                f32x4 s0, s1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    s0[r] = H[2 * kk][r] * sEm[32 * kk + 4 * lq + r];
+                    s1[r] = H[2 * kk + 1][r] * sEm[32 * kk + 16 + 4 * lq + r];
+                }
+                const bf16x8 bs = cat(cvt4(s0), cvt4(s1));
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    X[mt] = mfma32(kfrag_rows(sKt, PK, 16 * mt, 32 * kk, l16, lq), bs, X[mt]);
+                    QS[mt] = mfma32(kfrag_rows(sQt, PK, 16 * mt, 32 * kk, l16, lq), bs, QS[mt]);
+                }
+            }
+        }
         __syncthreads();
 
         // ---- diagonal blocks of (I + A)^-1: column l16 by fp32 forward substitution
-        f32x4 dcol = zero4();
         if (wave < 4) {
             const int b = wave;
             float x[16];
@@ -315,76 +323,29 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sDi[(16 * b + i) * PD + l16] = bf16_bits(x[i]);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dcol[r] = lq == 0 ? x[r] : lq == 1 ? x[4 + r] : lq == 2 ? x[8 + r] : x[12 + r];
-        }
-        // ---- meanwhile the other products of the state: X = k~ S_m and q~ S_m (dv tile nt)
-        f32x4 X[4], QS[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) X[mt] = QS[mt] = zero4();
-        if (colwave) {
-            for (int kk = 0; kk < D / 32; ++kk) {
-                const bf16x8 bs = kfrag_rows(sS, PK, 16 * nt, 32 * kk, l16, lq);
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    X[mt] = mfma32(kfrag_rows(sKt, PK, 16 * mt, 32 * kk, l16, lq), bs, X[mt]);
-                    QS[mt] = mfma32(kfrag_rows(sQt, PK, 16 * mt, 32 * kk, l16, lq), bs, QS[mt]);
-                }
-            }
         }
         __syncthreads();
 
-        // ---- column block j of T: X_j = D_j, X_i = -D_i sum_{m=j}^{i-1} A_im X_m; T^T to LDS
-        if (wave < 4) {
-            const int j = wave;
-            f32x4 Y[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Y[i] = i == j ? dcol : zero4();
-#pragma unroll
-            for (int i = 1; i < 4; ++i) {
-                if (i > j) {
-                    f32x4 E = zero4();
-#pragma unroll
-                    for (int m = 0; m < 3; ++m)
-                        if (m >= j && m < i)
-                            E = mfma16z(ld4(sA + (16 * i + l16) * PP + 16 * m + 4 * lq), cvt4(Y[m]), E);
-                    Y[i] = -mfma16z(ld4(sDi + (16 * i + l16) * PD + 4 * lq), cvt4(E), zero4());
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st4(sT + (16 * j + l16) * PP + 16 * i + 4 * lq, cvt4(Y[i]));
-        }
-        __syncthreads();
-
-        // ---- U = T diag(b) (V - X), O = scale q~ S_m + P U, H update (dv tile nt)
+        // ---- U = (I + A)^-1 diag(b) (V - X) by block forward substitution,
+        // U_b = D_b (W_b - sum_{c<b} A_bc U_c); O = scale q~ S_m + P U; H update (dv tile nt)
         if (colwave) {
-            bf16x4 wb[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                f32x4 w;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * mt + 4 * lq + r;
-                    const float vv = static_cast<float>(static_cast<__bf16>(cv[4 * mt + r]));
-                    w[r] = sB[i] * (vv - X[mt][r]);
-                }
-                wb[mt] = cvt4(w);
-            }
-            f32x4 U[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) U[mt] = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 bw = cat(wb[2 * kk], wb[2 * kk + 1]);
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) U[mt] = mfma32(kfrag_cols(sT, PP, 16 * mt, 32 * kk, l16, lq), bw, U[mt]);
-            }
             bf16x4 ub[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                ub[mt] = cvt4(U[mt]);
-                QS[mt] = QS[mt] * a.scale;
+            for (int b = 0; b < 4; ++b) {
+                f32x4 e;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * b + 4 * lq + r;
+                    const float vv = static_cast<float>(static_cast<__bf16>(cv[4 * b + r]));
+                    e[r] = sB[i] * (vv - X[b][r]);
+                }
+#pragma unroll
+                for (int cc = 0; cc < 3; ++cc)
+                    if (cc < b) e = mfma16z(ld4(sA + (16 * b + l16) * PP + 16 * cc + 4 * lq), neg4(ub[cc]), e);
+                ub[b] = cvt4(mfma16z(ld4(sDi + (16 * b + l16) * PD + 4 * lq), cvt4(e), zero4()));
             }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) QS[mt] = QS[mt] * a.scale;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const bf16x8 bu = cat(ub[2 * kk], ub[2 * kk + 1]);
