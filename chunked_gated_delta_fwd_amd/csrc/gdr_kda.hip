@@ -25,10 +25,11 @@
 // wave w owns dv columns [16w, 16w + 16) of the fp32 state (MFMA C tiles, rows
 // dk).  Per chunk: the gate scan (all threads: one channel and a quarter of the
 // tokens each) and the gated operands into LDS; the ten lower blocks of A and
-// of P, and beside them each wave's k~ S_m and q~ S_m (S_m taken from the
-// wave's own state registers, whose C-tile layout is the B operand's); the
-// four 16x16 diagonal inverses of I + A by fp32 substitution; then per wave U
-// by block forward substitution over its columns, O and the state update.
+// of P (the four waves that make the diagonal blocks of A also invert them,
+// 16x16 by fp32 substitution), then each wave's k~ S_m and q~ S_m (S_m taken
+// from the wave's own state registers, whose C-tile layout is the B
+// operand's); then per wave U by block forward substitution over its
+// columns, O and the state update.
 #include "gdr_internal.h"
 #include "gdr_device.h"
 
@@ -41,15 +42,19 @@ namespace {
 
 constexpr int kKdaThreads = 512;
 
-__device__ __forceinline__ bf16x8 kfrag_rows(const uint16_t *M, int pitch, int row0, int k0, int l16, int lq) {
-    const uint16_t *p = M + (row0 + l16) * pitch + k0 + 4 * lq;
-    return cat(ld4(p), ld4(p + 16));
+// Column position of key index x within its block of 32 in the q~, k~, k^-copy
+// and P arrays: x = 16 h + 4 j + r is stored at 8 j + 4 h + r, so that one
+// 16-byte read at 8 lq gives lane (l16, lq) the eight key slots of a 16x16x32
+// MFMA operand, keys 4 lq + r and 16 + 4 lq + r, in the order of a C tile's
+// rows (the same order on both operands, so the contraction is unchanged).
+__device__ __forceinline__ int kpos(int x) { return (x & ~31) | ((x & 12) << 1) | ((x >> 2) & 4) | (x & 3); }
+__device__ __forceinline__ bf16x8 kfrag8(const uint16_t *M, int pitch, int row0, int k0, int l16, int lq) {
+    return ld8(M + (row0 + l16) * pitch + k0 + 8 * lq);
 }
 __device__ __forceinline__ bf16x8 kfrag_cols(const uint16_t *M, int pitch, int col0, int k0, int l16, int lq) {
     const uint16_t *p = M + (k0 + 4 * lq + (l16 >> 2)) * pitch + col0 + 4 * (l16 & 3);
     return cat(ld4_tr(p), ld4_tr(p + 16 * pitch));
 }
-__device__ __forceinline__ float kbf(uint16_t u) { return __uint_as_float(static_cast<uint32_t>(u) << 16); }
 
 template <bool BF16>
 using VRaw = typename std::conditional<BF16, __bf16, float>::type;
@@ -119,15 +124,25 @@ __device__ __forceinline__ VRaw<GATE_BF16> fetch_beta(const FwdArgs &a, int64_t 
 
 template <int D>
 struct KdaLds {
-    static constexpr int PK = D + 16;
-    static constexpr int PP = C + 8;
-    static constexpr int PD = 24;
+    // Row pitches (bf16 elements).  q~, k~, the copy of k^ and P are read as
+    // 16-byte row fragments over key-permuted columns (kpos); k^ itself is
+    // read with the transposing loads (4 rows of 32 bytes per 16 lanes) for
+    // the state update; A and the diagonal inverses as 8-byte fragments, at
+    // pitches of 2 mod 32 four-byte banks (16 lanes, one row each, no
+    // conflict).  Measured: the 8-byte reads of q~ and k~ at the old pitch
+    // of 8 mod 32 banks cost twice the time of the whole A/P phase now.
+    static constexpr int PK = D + 16;              // q~, k~ and the k^ copy (key-permuted columns)
+    static constexpr int PH = D + 16;              // k^
+    static constexpr int PP = C + 4;               // A
+    static constexpr int PQ = C + 16;              // P (key-permuted columns)
+    static constexpr int PD = 20;
     static constexpr int oQt = 0;                  // q~ [64][PK]
     static constexpr int oKt = oQt + C * PK * 2;   // k~
-    static constexpr int oKh = oKt + C * PK * 2;   // k^
-    static constexpr int oA = oKh + C * PK * 2;    // diag(b) A~ strictly lower [i][j]
-    static constexpr int oP = oA + C * PP * 2;     // scale tril(q~ k^^T) [i][j]
-    static constexpr int oDi = oP + C * PP * 2;    // inverses of the diagonal blocks [4][16][PD]
+    static constexpr int oKh = oKt + C * PK * 2;   // k^ [64][PH]
+    static constexpr int oKr = oKh + C * PH * 2;   // k^ again [64][PK], for its row-fragment reads
+    static constexpr int oA = oKr + C * PK * 2;    // diag(b) A~ strictly lower [i][j]
+    static constexpr int oP = oA + C * PP * 2;     // scale tril(q~ k^^T) [i][kpos(j)]
+    static constexpr int oDi = oP + C * PQ * 2;    // inverses of the diagonal blocks [4][16][PD]
     static constexpr int oV = oDi + 4 * 16 * PD * 2;   // f32 [D] x3: e^{G_m}, e^{G_L}, e^{G_L - G_m}; [64] b
     static constexpr int NG = kKdaThreads / D;     // token groups of the gate scan
     static constexpr int oTot = oV + (3 * D + C) * 4;  // f32 [NG][D] group totals of the scan
@@ -137,7 +152,7 @@ struct KdaLds {
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
     using Ly = KdaLds<D>;
-    constexpr int PK = Ly::PK, PP = Ly::PP, PD = Ly::PD, NG = Ly::NG;
+    constexpr int PK = Ly::PK, PH = Ly::PH, PP = Ly::PP, PQ = Ly::PQ, PD = Ly::PD, NG = Ly::NG;
     constexpr int TPG = C / NG;     // tokens per scan group
     constexpr int MT = D / 16;      // dk tiles
     constexpr int NTD = D / 16;     // dv tiles (one per wave while wave < NTD)
@@ -145,6 +160,7 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
     uint16_t *sQt = reinterpret_cast<uint16_t *>(lds + Ly::oQt);
     uint16_t *sKt = reinterpret_cast<uint16_t *>(lds + Ly::oKt);
     uint16_t *sKh = reinterpret_cast<uint16_t *>(lds + Ly::oKh);
+    uint16_t *sKr = reinterpret_cast<uint16_t *>(lds + Ly::oKr);
     uint16_t *sA = reinterpret_cast<uint16_t *>(lds + Ly::oA);
     uint16_t *sP = reinterpret_cast<uint16_t *>(lds + Ly::oP);
     uint16_t *sDi = reinterpret_cast<uint16_t *>(lds + Ly::oDi);
@@ -190,24 +206,34 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
     // this thread's channel of g, q and k over its TPG tokens, its wave's v
     // values (rows 4 lq + r of the four token blocks, column 16 nt + l16) and
     // beta of its lane's token, each as loaded.
-    const int ch = tid % D, grp = tid / D;
+    const int ch = tid % D, grp = tid / D, chp = kpos(ch);
     VRaw<GATE_BF16> pg[TPG];
     VRaw<IN_BF16> pq[TPG], pk[TPG];
     VRaw<IN_BF16> pv[16];
     VRaw<GATE_BF16> pb = 0;
     // Unconditional: past the last chunk the ranges are empty and read zeros
     // (a branch here would make the compiler wait for the loads at its join).
-#define GDR_KDA_FETCH(cc)                                                                               \
+    // Two parts issued in different phases, so that no more loads are in
+    // flight per wave than its counter of outstanding loads (63) can track.
+#define GDR_KDA_RANGE(cc)                                                                               \
+    const int64_t t0_ = bos + C * (cc);                                                                 \
+    const int64_t r_ = eos - t0_;                                                                       \
+    const int len_ = static_cast<int>(r_ <= 0 ? 0 : r_ < C ? r_ : C);                                   \
+    const int ln_ = tid & 63;
+#define GDR_KDA_FETCH_G(cc)                                                                             \
     {                                                                                                   \
-        const int64_t t0_ = bos + C * (cc);                                                             \
-        const int64_t r_ = eos - t0_;                                                                   \
-        const int len_ = static_cast<int>(r_ <= 0 ? 0 : r_ < C ? r_ : C);                               \
-        const int ln_ = tid & 63;                                                                       \
+        GDR_KDA_RANGE(cc)                                                                               \
         kda_fetch_gate<D, TPG, IN_BF16, GATE_BF16>(a, t0_, len_, h, hk, ch, grp, pg, pq, pk);          \
+        (void)ln_;                                                                                      \
+    }
+#define GDR_KDA_FETCH_V(cc)                                                                             \
+    {                                                                                                   \
+        GDR_KDA_RANGE(cc)                                                                               \
         if (D == 128 || colwave) kda_fetch_v<D, IN_BF16>(a, t0_, len_, h, nt, ln_, pv);                 \
         pb = fetch_beta<GATE_BF16>(a, t0_, len_, h, ln_);                                               \
     }
-    GDR_KDA_FETCH(0)
+    GDR_KDA_FETCH_G(0)
+    GDR_KDA_FETCH_V(0)
 
     for (int64_t c = 0; c < nch; ++c) {
         int lane = tid & 63;   // opaque per iteration: keeps per-lane addresses inside the loop
@@ -251,40 +277,83 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
                 const float qv = static_cast<float>(static_cast<__bf16>(pq[i]));
                 const float kv = static_cast<float>(static_cast<__bf16>(pk[i]));
                 const float e = fast_exp2(x), ei = fast_exp2(-x);
-                sQt[row * PK + ch] = bf16_bits(qv * e);
-                sKt[row * PK + ch] = bf16_bits(kv * e);
-                sKh[row * PK + ch] = bf16_bits(kv * ei);
+                sQt[row * PK + chp] = bf16_bits(qv * e);
+                sKt[row * PK + chp] = bf16_bits(kv * e);
+                const uint16_t kh_ = bf16_bits(kv * ei);
+                sKh[row * PH + ch] = kh_;
+                sKr[row * PK + chp] = kh_;
             }
         }
         VRaw<IN_BF16> cv[16];   // this chunk's v values; the registers above take the next chunk
 #pragma unroll
         for (int j = 0; j < 16; ++j) cv[j] = pv[j];
-        GDR_KDA_FETCH(c + 1)
+        GDR_KDA_FETCH_G(c + 1)
         // zero A and P (blocks above the diagonal stay zero)
-        for (int i = tid; i < 2 * C * PP / 8; i += kKdaThreads)
+        for (int i = tid; i < C * (PP + PQ) / 8; i += kKdaThreads)
             reinterpret_cast<v4u32 *>(sA)[i] = v4u32{0u, 0u, 0u, 0u};
         __syncthreads();
 
-        // ---- the ten lower blocks of A = diag(b) k~ k^^T and of P = scale q~ k^^T
-        for (int t = wave; t < 20; t += 8) {
-            const bool ka = t < 10;
-            const int tt = ka ? t : t - 10;
-            const int bi = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
-            const int bj = tt - bi * (bi + 1) / 2;
-            const uint16_t *Am = ka ? sKt : sQt;
-            f32x4 acc = zero4();
+        // ---- blocks of A = diag(b) k~ k^^T (strictly lower) and of P = scale q~ k^^T
+        // (lower): waves 0-3 take diagonal block b = wave of A and then its
+        // inverse; waves 4-7 share the six blocks of A below the diagonal and
+        // the ten blocks of P
+        {
+            const bool dw = wave < 4;
+            for (int t = dw ? 0 : wave - 4; t < (dw ? 1 : 16); t += dw ? 1 : 4) {
+                int bi, bj;
+                const bool ka = dw || t < 6;
+                if (dw) {
+                    bi = bj = wave;
+                } else if (t < 6) {
+                    bi = t >= 3 ? 3 : t >= 1 ? 2 : 1;
+                    bj = t - (bi - 1) * bi / 2;
+                } else {
+                    const int tt = t - 6;
+                    bi = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
+                    bj = tt - bi * (bi + 1) / 2;
+                }
+                const uint16_t *Am = ka ? sKt : sQt;
+                f32x4 acc = zero4();
 #pragma unroll
-            for (int k0 = 0; k0 < D; k0 += 32)
-                acc = mfma32(kfrag_rows(Am, PK, 16 * bi, k0, l16, lq), kfrag_rows(sKh, PK, 16 * bj, k0, l16, lq), acc);
-            const int j = 16 * bj + l16;
+                for (int k0 = 0; k0 < D; k0 += 32)
+                    acc = mfma32(kfrag8(Am, PK, 16 * bi, k0, l16, lq), kfrag8(sKr, PK, 16 * bj, k0, l16, lq), acc);
+                const int j = 16 * bj + l16;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * bi + 4 * lq + r;
-                if (ka) sA[i * PP + j] = bf16_bits(j < i ? sB[i] * acc[r] : 0.f);
-                else sP[i * PP + j] = bf16_bits(j <= i ? a.scale * acc[r] : 0.f);
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * bi + 4 * lq + r;
+                    if (ka) sA[i * PP + j] = bf16_bits(j < i ? sB[i] * acc[r] : 0.f);
+                    else sP[i * PQ + kpos(j)] = bf16_bits(j <= i ? a.scale * acc[r] : 0.f);
+                }
+            }
+            if (dw) {
+                // inverse of diagonal block b of I + A, column l16 by fp32 forward
+                // substitution over the bf16 values this wave has just stored
+                lds_wait();
+                const int b = wave;
+                float x[16];
+                x[0] = l16 == 0 ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 1; i < 16; ++i) {
+                    float s = i == l16 ? 1.f : 0.f;
+#pragma unroll
+                    for (int m4 = 0; m4 < i; m4 += 4) {
+                        // entries m4 .. m4 + 3 of row i, one 8-byte read (the same for all lanes)
+                        const v2u32 w = *reinterpret_cast<const v2u32 *>(sA + (16 * b + i) * PP + 16 * b + m4);
+                        const float am[4] = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                                             __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (m4 + u < i) s -= am[u] * x[m4 + u];
+                    }
+                    x[i] = s;
+                }
+                if (lq == 0) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sDi[(16 * b + i) * PD + l16] = bf16_bits(x[i]);
+                }
             }
         }
-        // ---- meanwhile k~ S_m and q~ S_m for this wave's dv tile, with
+        // ---- then k~ S_m and q~ S_m for this wave's dv tile, with
         // S_m = diag(e^{G_m}) H taken from the wave's own state registers
         f32x4 X[4], QS[4];
 #pragma unroll
@@ -301,29 +370,12 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
                 const bf16x8 bs = cat(cvt4(s0), cvt4(s1));
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
-                    X[mt] = mfma32(kfrag_rows(sKt, PK, 16 * mt, 32 * kk, l16, lq), bs, X[mt]);
-                    QS[mt] = mfma32(kfrag_rows(sQt, PK, 16 * mt, 32 * kk, l16, lq), bs, QS[mt]);
+                    X[mt] = mfma32(kfrag8(sKt, PK, 16 * mt, 32 * kk, l16, lq), bs, X[mt]);
+                    QS[mt] = mfma32(kfrag8(sQt, PK, 16 * mt, 32 * kk, l16, lq), bs, QS[mt]);
                 }
             }
         }
-        __syncthreads();
-
-        // ---- diagonal blocks of (I + A)^-1: column l16 by fp32 forward substitution
-        if (wave < 4) {
-            const int b = wave;
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = i == l16 ? 1.f : 0.f;
-#pragma unroll
-                for (int m = 0; m < i; ++m) s -= kbf(sA[(16 * b + i) * PP + 16 * b + m]) * x[m];
-                x[i] = s;
-            }
-            if (lq == 0) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sDi[(16 * b + i) * PD + l16] = bf16_bits(x[i]);
-            }
-        }
+        GDR_KDA_FETCH_V(c + 1)
         __syncthreads();
 
         // ---- U = (I + A)^-1 diag(b) (V - X) by block forward substitution,
@@ -350,7 +402,7 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
             for (int kk = 0; kk < 2; ++kk) {
                 const bf16x8 bu = cat(ub[2 * kk], ub[2 * kk + 1]);
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) QS[mt] = mfma32(kfrag_rows(sP, PP, 16 * mt, 32 * kk, l16, lq), bu, QS[mt]);
+                for (int mt = 0; mt < 4; ++mt) QS[mt] = mfma32(kfrag8(sP, PQ, 16 * mt, 32 * kk, l16, lq), bu, QS[mt]);
             }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
@@ -369,7 +421,7 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
                 f32x4 R = zero4();
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    R = mfma32(kfrag_cols(sKh, PK, 16 * mt, 32 * kk, l16, lq), cat(ub[2 * kk], ub[2 * kk + 1]), R);
+                    R = mfma32(kfrag_cols(sKh, PH, 16 * mt, 32 * kk, l16, lq), cat(ub[2 * kk], ub[2 * kk + 1]), R);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = 16 * mt + 4 * lq + r;
@@ -387,7 +439,9 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(16 * mt + 4 * lq + r) * D + 16 * nt + l16] = H[mt][r];
     }
-#undef GDR_KDA_FETCH
+#undef GDR_KDA_FETCH_G
+#undef GDR_KDA_FETCH_V
+#undef GDR_KDA_RANGE
 }
 
 template <int D, bool IN_BF16, bool GATE_BF16>
