@@ -114,20 +114,40 @@ __device__ __forceinline__ void stage_rows(uint16_t *dst, int pitch, const void 
         *reinterpret_cast<v4u32 *>(dst + (i / PR) * pitch + 8 * (i % PR)) = r[j];
     }
 }
-// Two such row blocks (of different tensors), all loads first.
-template <int D, bool BF16, int NT>
+// 16 bytes to / from LDS at p: one access where p is 16-byte aligned (A16),
+// else two 8-byte ones.
+template <bool A16>
+__device__ __forceinline__ void st16(uint16_t *p, v4u32 v) {
+    if constexpr (A16) {
+        *reinterpret_cast<v4u32 *>(p) = v;
+    } else {
+        reinterpret_cast<v2u32 *>(p)[0] = v2u32{v[0], v[1]};
+        reinterpret_cast<v2u32 *>(p)[1] = v2u32{v[2], v[3]};
+    }
+}
+template <bool A16>
+__device__ __forceinline__ v4u32 ld16(const uint16_t *p) {
+    if constexpr (A16) {
+        return *reinterpret_cast<const v4u32 *>(p);
+    } else {
+        const v2u32 x = reinterpret_cast<const v2u32 *>(p)[0], y = reinterpret_cast<const v2u32 *>(p)[1];
+        return v4u32{x[0], x[1], y[0], y[1]};
+    }
+}
+// Two such row blocks (of different tensors), all loads first; rows of P0
+// and P1 elements.
+template <int D, bool BF16, int NT, int P0, int P1>
 __device__ __forceinline__ void stage_rows2(uint16_t *d0, const void *s0, int heads0, int head0, uint16_t *d1,
-                                            const void *s1, int heads1, int head1, int pitch, int64_t t0, int len,
-                                            int tid) {
+                                            const void *s1, int heads1, int head1, int64_t t0, int len, int tid) {
     constexpr int PR = D / 8, NP = C * PR / NT;
     v4u32 r0[NP], r1[NP];
     fetch_rows<D, BF16, NP, NT>(r0, s0, t0, len, heads0, head0, tid);
     fetch_rows<D, BF16, NP, NT>(r1, s1, t0, len, heads1, head1, tid);
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
-        const int i = tid + j * NT, off = (i / PR) * pitch + 8 * (i % PR);
-        *reinterpret_cast<v4u32 *>(d0 + off) = r0[j];
-        *reinterpret_cast<v4u32 *>(d1 + off) = r1[j];
+        const int i = tid + j * NT, row = i / PR, col = 8 * (i % PR);
+        st16<P0 % 8 == 0>(d0 + row * P0 + col, r0[j]);
+        st16<P1 % 8 == 0>(d1 + row * P1 + col, r1[j]);
     }
 }
 
@@ -198,29 +218,36 @@ __device__ __forceinline__ void chunk_gates(const BwdArgs &a, int64_t t0, int le
 // --------------------------------------------------------------------------
 template <int D>
 struct PrepLds {
-    static constexpr int PK = D + 16;   // [64][D] bf16 rows
-    static constexpr int PP = C + 8;    // [64][64] bf16
-    static constexpr int PD = 24;       // [16][16] bf16 blocks
+    // Row pitches (bf16 elements) by how each array is read, against the 32
+    // four-byte LDS banks: 8-byte row fragments (16 lanes, one row each) are
+    // conflict-free at 2 mod 32 banks, transposing reads (4 rows of 32 bytes
+    // per 16 lanes) at 8 mod 32; k, read both ways, takes 4 mod 32 (2-way).
+    static constexpr int PQ = D + 4;    // q [64][D]: row fragments
+    static constexpr int PK = D + 8;    // k [64][D]: both
+    static constexpr int PO = D + 16;   // dO [64][D]: transposing reads
+    static constexpr int PP = C + 4;    // A, P^T [64][64]: row fragments
+    static constexpr int PT = C + 16;   // (T diag(b e^G))^T [64][64]: transposing reads
+    static constexpr int PD = 20;       // [16][16] bf16 blocks
     static constexpr int oQ = 0;
-    static constexpr int oK = oQ + C * PK * 2;
+    static constexpr int oK = oQ + C * PQ * 2;
     static constexpr int oO = oK + C * PK * 2;
-    static constexpr int oA = oO + C * PK * 2;        // diag(b) A~, strictly lower, [i][j]
+    static constexpr int oA = oO + C * PO * 2;        // diag(b) A~, strictly lower, [i][j]
     static constexpr int oPt = oA + C * PP * 2;       // (scale M o Q K^T)^T, [j][i]
     static constexpr int oG = oPt + C * PP * 2;       // f32 [64] x3: G log2(e), b, b e^G
     static constexpr int base = oG + 3 * C * 4;
     // (T diag(b e^G))^T [j][i] and the bf16 inverses of the diagonal blocks of
     // I + diag(b) A~: in q's rows, dead once Q K^T is formed, when they fit
-    static constexpr int alias = C * PP * 2 + 4 * 16 * PD * 2;
-    static constexpr bool in_q = alias <= C * PK * 2;
+    static constexpr int alias = C * PT * 2 + 4 * 16 * PD * 2;
+    static constexpr bool in_q = alias <= C * PQ * 2;
     static constexpr int oTt = in_q ? oQ : base;
-    static constexpr int oDi = oTt + C * PP * 2;
+    static constexpr int oDi = oTt + C * PT * 2;
     static constexpr int bytes = in_q ? base : base + alias;
 };
 
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     using Ly = PrepLds<D>;
-    constexpr int PK = Ly::PK, PP = Ly::PP, PD = Ly::PD, NTD = D / 16;
+    constexpr int PQ = Ly::PQ, PK = Ly::PK, PO = Ly::PO, PP = Ly::PP, PT = Ly::PT, PD = Ly::PD, NTD = D / 16;
     extern __shared__ __align__(16) unsigned char lds[];
     uint16_t *sQ = reinterpret_cast<uint16_t *>(lds + Ly::oQ);
     uint16_t *sK = reinterpret_cast<uint16_t *>(lds + Ly::oK);
@@ -240,8 +267,8 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lq = lane >> 4;
     const int64_t rh = static_cast<int64_t>(blockIdx.x) * a.hv + h;
 
-    stage_rows2<D, IN_BF16, kBwdThreads>(sQ, a.q, a.hk, hk, sK, a.k, a.hk, hk, PK, p.t0, p.len, tid);
-    stage_rows<D, IN_BF16, kBwdThreads>(sO, PK, a.dout, p.t0, p.len, a.hv, h, tid);
+    stage_rows2<D, IN_BF16, kBwdThreads, PQ, PK>(sQ, a.q, a.hk, hk, sK, a.k, a.hk, hk, p.t0, p.len, tid);
+    stage_rows<D, IN_BF16, kBwdThreads>(sO, PO, a.dout, p.t0, p.len, a.hv, h, tid);
     for (int i = tid; i < 2 * C * PP / 8; i += kBwdThreads)   // A and P^T (adjacent): blocks above the diagonal stay zero
         reinterpret_cast<uint4 *>(sA)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (wave == 0) {
@@ -261,10 +288,11 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
         const int bi = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
         const int bj = tt - bi * (bi + 1) / 2;
         const uint16_t *Am = kk ? sK : sQ;
+        const int pa = kk ? PK : PQ;
         f32x4 acc = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < D; k0 += 32)
-            acc = mfma32(frag_rows(Am, PK, 16 * bi, k0, l16, lq), frag_rows(sK, PK, 16 * bj, k0, l16, lq), acc);
+            acc = mfma32(frag_rows(Am, pa, 16 * bi, k0, l16, lq), frag_rows(sK, PK, 16 * bj, k0, l16, lq), acc);
         const int j = 16 * bj + l16;
         const float gj = sG2[j];
         f32x4 pv;
@@ -328,7 +356,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             *reinterpret_cast<bf16x4 *>(tg + (16 * j + l16) * C + 16 * i + 4 * lq) = cvt4(X[i]);
-            st4(sTt + (16 * j + l16) * PP + 16 * i + 4 * lq, cvt4(X[i] * bgj));
+            st4(sTt + (16 * j + l16) * PT + 16 * i + 4 * lq, cvt4(X[i] * bgj));
         }
     }
     __syncthreads();
@@ -340,7 +368,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < C; k0 += 32)
-            acc = mfma32(frag_cols(sTt, PP, 16 * it, k0, l16, lq), frag_cols(sK, PK, 16 * dt, k0, l16, lq), acc);
+            acc = mfma32(frag_cols(sTt, PT, 16 * it, k0, l16, lq), frag_cols(sK, PK, 16 * dt, k0, l16, lq), acc);
         *reinterpret_cast<bf16x4 *>(wg + (16 * dt + l16) * C + 16 * it + 4 * lq) = cvt4(acc);
     }
     // dU0 = (scale M o Q K^T)^T dO, in 16x16 tiles (token block, dv tile), lane-major
@@ -351,7 +379,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
         for (int k0 = 0; k0 < C; k0 += 32)
             if (k0 + 32 > 16 * jt)
-                acc = mfma32(frag_rows(sPt, PP, 16 * jt, k0, l16, lq), frag_cols(sO, PK, 16 * nt, k0, l16, lq), acc);
+                acc = mfma32(frag_rows(sPt, PP, 16 * jt, k0, l16, lq), frag_cols(sO, PO, 16 * nt, k0, l16, lq), acc);
         *reinterpret_cast<f32x4 *>(ug + ((jt * NTD + nt) * 64 + lane) * 4) = acc;
     }
 }
@@ -362,11 +390,14 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
 // --------------------------------------------------------------------------
 template <int D>
 struct ChainLds {
-    static constexpr int PK = D + 16;
-    static constexpr int PW = C + 8;
+    // q and dO are read with transposing reads (pitch 8 mod 32 four-byte
+    // banks), k and w^T as 8-byte row fragments (2 mod 32): no conflicts
+    static constexpr int PK = D + 16;              // q, dO
+    static constexpr int PR = D + 4;               // k
+    static constexpr int PW = C + 4;
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + C * PK * 2;
-    static constexpr int oO = oK + C * PK * 2;
+    static constexpr int oO = oK + C * PR * 2;
     static constexpr int oW = oO + C * PK * 2;     // w^T [D][PW]
     static constexpr int oG = oW + D * PW * 2;     // f32 [64] x2: scale e^G, e^{G_L - G}; then e^{G_L}
     static constexpr int bytes = oG + 2 * C * 4 + 16;
@@ -375,7 +406,7 @@ struct ChainLds {
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a) {
     using Ly = ChainLds<D>;
-    constexpr int PK = Ly::PK, PW = Ly::PW;
+    constexpr int PK = Ly::PK, PKR = Ly::PR, PW = Ly::PW;
     constexpr int MT = D / 16;                        // dk tiles (and dv tiles)
     constexpr int NTW = D / 64;                       // dv tiles per wave
     constexpr int PR = D / 8;                         // 16-byte pieces per q / k / dO row
@@ -458,13 +489,13 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
         for (int j = 0; j < NQ; ++j) {
             const int i = tid + j * kChainThreads, row = i / PR, col = 8 * (i % PR);
             *reinterpret_cast<v4u32 *>(sQ + row * PK + col) = pq[j];
-            *reinterpret_cast<v4u32 *>(sK + row * PK + col) = pk[j];
+            st16<PKR % 8 == 0>(sK + row * PKR + col, pk[j]);
             *reinterpret_cast<v4u32 *>(sO + row * PK + col) = po[j];
         }
 #pragma unroll
         for (int j = 0; j < NW; ++j) {
             const int i = tid + j * kChainThreads, row = i / (C / 8), col = 8 * (i % (C / 8));
-            *reinterpret_cast<v4u32 *>(sW + row * PW + col) = pw[j];
+            st16<PW % 8 == 0>(sW + row * PW + col, pw[j]);
         }
         if (wave == 0) {
             const float G2 = wave_inclusive_scan(pg * kLog2e);
@@ -501,7 +532,7 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
             for (int nt = 0; nt < NTW; ++nt) bh[nt] = cat(cvt4(dH[2 * kk][nt]), cvt4(dH[2 * kk + 1][nt]));
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8 af = frag_rows(sK, PK, 16 * mt, 32 * kk, l16, lq);
+                const bf16x8 af = frag_rows(sK, PKR, 16 * mt, 32 * kk, l16, lq);
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) X1[mt][nt] = mfma32(af, bh[nt], X1[mt][nt]);
             }
@@ -577,7 +608,9 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
 // --------------------------------------------------------------------------
 template <int D>
 struct GradLds {
-    static constexpr int PK = D + 16;
+    // [64][D] rows at a pitch of 2 mod 32 four-byte banks: their 8-byte
+    // row-fragment reads (16 lanes, one row each) are free of conflicts
+    static constexpr int PK = D + 4;
     static constexpr int PP = C + 8;
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + C * PK * 2;
@@ -628,7 +661,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
     const bool colwave = wave < NTD;   // owns column tile `wave` in the column-split phases
     const int nt = wave;
 
-    stage_rows2<D, IN_BF16, kBwdThreads>(sQ, a.q, a.hk, hk, sK, a.k, a.hk, hk, PK, p.t0, p.len, tid);
+    stage_rows2<D, IN_BF16, kBwdThreads, PK, PK>(sQ, a.q, a.hk, hk, sK, a.k, a.hk, hk, p.t0, p.len, tid);
 
     f32x4 accQ[4], accK[4];
 #pragma unroll
@@ -669,8 +702,8 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < NP; ++j) {
                 const int i = tid + j * kBwdThreads, off = (i / PR) * PK + 8 * (i % PR);
-                *reinterpret_cast<v4u32 *>(sV + off) = rv[j];
-                *reinterpret_cast<v4u32 *>(sO + off) = ro[j];
+                st16<PK % 8 == 0>(sV + off, rv[j]);
+                st16<PK % 8 == 0>(sO + off, ro[j]);
             }
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
@@ -775,12 +808,12 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < NDS; ++j) {
                 const int i = tid + j * kBwdThreads, row = i / (D / 8), col = 8 * (i % (D / 8));
-                v4u32 *sp = reinterpret_cast<v4u32 *>(sS + row * PK + col);
-                const bf16x8 sv = __builtin_bit_cast(bf16x8, *sp);
+                uint16_t *sp = sS + row * PK + col;
+                const bf16x8 sv = __builtin_bit_cast(bf16x8, ld16<PK % 8 == 0>(sp));
                 const bf16x8 dv = __builtin_bit_cast(bf16x8, pds[j]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) part += static_cast<float>(dv[e]) * static_cast<float>(sv[e]);
-                *sp = pds[j];
+                st16<PK % 8 == 0>(sp, pds[j]);
             }
             part = lane63(wave_inclusive_scan(part));
             if (lane == 0) sXd[wave] = part;
