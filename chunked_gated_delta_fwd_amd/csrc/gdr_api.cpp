@@ -312,23 +312,25 @@ class WsLease {
     std::unique_lock<std::mutex> lock_;
 };
 
-// Machines of the dispatch-order model for a forward launch: work-groups
-// resident at once divided by the v-heads of a sequence (each XCD gets Hv/8
-// heads of every sequence, so Hv must split over the 8 XCDs), or 0 when the
-// packed order does not apply.  Occupancy is queried once per device and
-// kernel variant.
-int order_groups(const gdr::FwdArgs &a) {
+// Machines of the dispatch-order model for a forward launch (kda: the
+// per-channel-gate kernel): work-groups resident at once divided by the
+// v-heads of a sequence (each XCD gets Hv/8 heads of every sequence, so Hv
+// must split over the 8 XCDs), or 0 when the packed order does not apply.
+// Occupancy is queried once per device and kernel variant.
+int order_groups(const gdr::FwdArgs &a, bool kda = false) {
     static std::mutex mu;
-    static int cache[64][2][2][2];   // slots + 1; 0 unknown
+    static int cache[64][2][2][2][2];   // slots + 1; 0 unknown
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int &entry = cache[dev][a.d == 64 ? 0 : 1][a.in_bf16 ? 1 : 0][a.gate_bf16 ? 1 : 0];
+    int &entry = cache[dev][kda ? 1 : 0][a.d == 64 ? 0 : 1][a.in_bf16 ? 1 : 0][a.gate_bf16 ? 1 : 0];
     int slots = 0;
     {
         std::lock_guard<std::mutex> lock(mu);
         if (entry == 0) {
             int s = 0;
-            entry = gdr::fwd_slots(a.d, a.in_bf16, a.gate_bf16, &s) == hipSuccess ? s + 1 : 1;
+            const hipError_t e = kda ? gdr::kda_slots(a.d, a.in_bf16, a.gate_bf16, &s)
+                                     : gdr::fwd_slots(a.d, a.in_bf16, a.gate_bf16, &s);
+            entry = e == hipSuccess ? s + 1 : 1;
         }
         slots = entry - 1;
     }
@@ -630,11 +632,14 @@ int run_kda(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     a.scale = scale;
     WsLease lease;
     hipError_t e = hipSuccess;
-    if (cu_seqlens) {   // longest sequences first
+    if (cu_seqlens) {   // the packed dispatch order where it applies, else longest sequences first
         void *ws = nullptr;
         if ((rc = lease.acquire(static_cast<size_t>(4 * p.n_seq), false, stream, &ws))) return rc;
-        a.order = static_cast<int32_t *>(ws);
-        e = gdr::launch_prepare(a.cu, p.n_seq, nullptr, nullptr, 0, static_cast<int32_t *>(ws), stream);
+        int32_t *order = static_cast<int32_t *>(ws);
+        a.order = order;
+        const int groups = order_groups(a, true);
+        e = groups ? gdr::launch_order(a.cu, p.n_seq, groups, order, stream)
+                   : gdr::launch_prepare(a.cu, p.n_seq, nullptr, nullptr, 0, order, stream);
     }
     if (e == hipSuccess) e = gdr::launch_kda_fwd(a, stream);
     const int rr = lease.release();

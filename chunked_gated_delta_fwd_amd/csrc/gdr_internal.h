@@ -61,6 +61,8 @@ hipError_t launch_order(const int32_t *cu, int64_t n_seq, int32_t groups, int32_
                         hipStream_t stream);
 // Work-groups of the fused forward kernel resident on the device at once.
 hipError_t fwd_slots(int d, int in_bf16, int gate_bf16, int *slots);
+// Work-groups of the per-channel-gate forward kernel resident at once.
+hipError_t kda_slots(int d, int in_bf16, int gate_bf16, int *slots);
 
 // chunk_map != NULL: varlen (grid nt_max); else n_rows fixed rows of seq_len tokens.
 hipError_t launch_cumsum(const void *g, int gate_bf16, const int32_t *cu,

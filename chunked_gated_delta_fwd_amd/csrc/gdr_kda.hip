@@ -170,8 +170,21 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
     float *sB = sELm + D;
     float *sTot = reinterpret_cast<float *>(lds + Ly::oTot);
 
-    const int64_t rank = blockIdx.x / a.hv;
-    const int h = static_cast<int>(blockIdx.x % a.hv);
+    // Work-groups are dispatched round-robin over the 8 XCDs (each with its
+    // own L2): blocks b and b + 8 share an XCD, so they are given the v-heads
+    // of one q/k head and the second finds q and k in L2.
+    int64_t item = blockIdx.x;
+    {
+        const int64_t r = a.hv / a.hk;
+        const int64_t span = 8 * r;
+        const int64_t full = (static_cast<int64_t>(gridDim.x) / span) * span;
+        if (r > 1 && item < full) {
+            const int64_t w = item % span;
+            item = (item - w) + (w % 8) * r + w / 8;
+        }
+    }
+    const int64_t rank = item / a.hv;
+    const int h = static_cast<int>(item % a.hv);
     const int64_t n = a.order ? static_cast<int64_t>(a.order[rank]) : rank;
     if (n < 0 || n >= a.n_seq) return;
     int64_t bos, eos;
@@ -463,7 +476,29 @@ hipError_t launch_kda_d(const FwdArgs &a, hipStream_t s) {
 
 static_assert(KdaLds<128>::bytes <= 160 * 1024, "KDA kernel LDS");
 
+template <int D>
+const void *kda_kernel(int in_bf16, int gate_bf16) {
+    if (in_bf16)
+        return gate_bf16 ? reinterpret_cast<const void *>(gdr_kda_fwd_kernel<D, true, true>)
+                         : reinterpret_cast<const void *>(gdr_kda_fwd_kernel<D, true, false>);
+    return gate_bf16 ? reinterpret_cast<const void *>(gdr_kda_fwd_kernel<D, false, true>)
+                     : reinterpret_cast<const void *>(gdr_kda_fwd_kernel<D, false, false>);
+}
+
 }  // namespace
+
+hipError_t kda_slots(int d, int in_bf16, int gate_bf16, int *slots) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const void *kern = d == 64 ? kda_kernel<64>(in_bf16, gate_bf16) : kda_kernel<128>(in_bf16, gate_bf16);
+    const int lds = d == 64 ? KdaLds<64>::bytes : KdaLds<128>::bytes;
+    if ((e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kKdaThreads, lds)) != hipSuccess) return e;
+    *slots = cus * per_cu;
+    return hipSuccess;
+}
 
 hipError_t launch_kda_fwd(const FwdArgs &a, hipStream_t stream) {
     if (a.n_seq == 0 || a.hv == 0) return hipSuccess;
