@@ -372,6 +372,7 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     if (p.n_seq == 0 || p.total_tokens == 0) return ok();
 
     gdr::FwdArgs a;
+    std::memset(&a, 0, sizeof(a));
     a.q = q->data;
     a.k = k->data;
     a.v = v->data;
@@ -431,7 +432,7 @@ BwdWorkspace bwd_workspace(int64_t n_seq, int64_t rows, int64_t hv, int64_t d, b
     w.ints = o;
     o += al(varlen ? 4 * static_cast<size_t>(2 * n_seq + 1 + 2 * rows) : 0);
     w.hck = o;
-    o += al(ch * dd * dd * 4);
+    o += al(ch * dd * dd * 2);
     w.dhe = o;
     o += al(ch * dd * dd * 2);
     w.du0 = o;
@@ -513,7 +514,7 @@ int run_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
         order = map + 2 * rows;
         e = gdr::launch_prepare(cu, N, offs, map, rows, order, stream);
     }
-    float *hck = reinterpret_cast<float *>(base + wl.hck);
+    uint16_t *hck = reinterpret_cast<uint16_t *>(base + wl.hck);
     if (e == hipSuccess) {
         // forward recompute: the state after every chunk (no o, no ht)
         gdr::FwdArgs fa;
@@ -537,7 +538,7 @@ int run_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
         fa.in_bf16 = p.in_dtype == GDR_BF16;
         fa.gate_bf16 = p.gate_dtype == GDR_BF16;
         fa.scale = scale;
-        fa.hck = hck;
+        fa.hck16 = hck;
         fa.ck_offs = offs;
         fa.ck_rows = rows;
         e = gdr::launch_fwd(fa, stream);

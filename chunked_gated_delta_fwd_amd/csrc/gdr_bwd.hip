@@ -675,8 +675,9 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
         const int l16 = lane & 15, lq = lane >> 4;
         const int h = hk * G + hh;
         const int64_t rh = static_cast<int64_t>(blockIdx.x) * a.hv + h;
-        const float *Sg = p.c > 0 ? a.hck + (rh - a.hv) * D * D
-                                  : (a.h0 ? a.h0 + (p.n * a.hv + h) * D * D : nullptr);
+        // the state at the chunk start: bf16 after the previous chunk, else h0 (fp32) or zero
+        const uint16_t *Sb = p.c > 0 ? a.hck + (rh - a.hv) * D * D : nullptr;
+        const float *Sg = p.c == 0 && a.h0 ? a.h0 + (p.n * a.hv + h) * D * D : nullptr;
         bf16x4 ub[4];   // this wave's dU tiles (dv tile nt), bf16
         if (colwave) {
             const uint16_t *ug = a.du + rh * (C * D);
@@ -686,15 +687,24 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
         __syncthreads();   // the previous v-head's reads of LDS are done
         {
             // all of this v-head's staging loads are issued before the first store
-            constexpr int PR = D / 8, NP = C * PR / kBwdThreads, NS = D * D / 4 / kBwdThreads, NT8 = C * C / 8 / kBwdThreads;
-            v4u32 rv[NP], ro[NP], rt[NT8];
-            f32x4 rs[NS];
+            constexpr int PR = D / 8, NP = C * PR / kBwdThreads, NT8 = C * C / 8 / kBwdThreads;
+            constexpr int NS8 = D * D / 8 / kBwdThreads;   // 16-byte pieces (8 bf16) of the state per thread
+            v4u32 rv[NP], ro[NP], rt[NT8], rs8[NS8];
             fetch_rows<D, IN_BF16, NP, kBwdThreads>(rv, a.v, p.t0, p.len, a.hv, h, tid);
             fetch_rows<D, IN_BF16, NP, kBwdThreads>(ro, a.dout, p.t0, p.len, a.hv, h, tid);
+            if (Sb) {
 #pragma unroll
-            for (int j = 0; j < NS; ++j) {
-                const int i = tid + j * kBwdThreads;
-                rs[j] = Sg ? *reinterpret_cast<const f32x4 *>(Sg + (i / (D / 4)) * D + 4 * (i % (D / 4))) : zero4();
+                for (int j = 0; j < NS8; ++j) rs8[j] = *reinterpret_cast<const v4u32 *>(Sb + 8 * (tid + j * kBwdThreads));
+            } else {
+                // a sequence's first chunk: h0 rounded to bf16 here (the only
+                // chunk whose staging waits for its state loads)
+#pragma unroll
+                for (int j = 0; j < NS8; ++j) {
+                    const float *src = Sg ? Sg + 8 * (tid + j * kBwdThreads) : nullptr;
+                    const f32x4 x0 = src ? *reinterpret_cast<const f32x4 *>(src) : zero4();
+                    const f32x4 x1 = src ? *reinterpret_cast<const f32x4 *>(src + 4) : zero4();
+                    rs8[j] = __builtin_bit_cast(v4u32, cat(cvt4(x0), cvt4(x1)));
+                }
             }
             const uint16_t *tg = a.tmat + rh * (C * C);
 #pragma unroll
@@ -706,9 +716,9 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
                 st16<PK % 8 == 0>(sO + off, ro[j]);
             }
 #pragma unroll
-            for (int j = 0; j < NS; ++j) {
+            for (int j = 0; j < NS8; ++j) {
                 const int i = tid + j * kBwdThreads;
-                st4(sS + (i / (D / 4)) * PK + 4 * (i % (D / 4)), cvt4(rs[j]));
+                st16<PK % 8 == 0>(sS + (i / (D / 8)) * PK + 8 * (i % (D / 8)), rs8[j]);
             }
 #pragma unroll
             for (int j = 0; j < NT8; ++j) {

@@ -23,8 +23,11 @@ struct FwdArgs {
     int32_t gate_bf16;      // g/beta dtype
     float scale;
     // chunk-boundary states (NULL: not written): row ck_offs[n] + c (or
-    // n * ceil(seq_len / 64) + c for fixed-length rows) of [ck_rows, Hv, d, d]
+    // n * ceil(seq_len / 64) + c for fixed-length rows) of [ck_rows, Hv, d, d],
+    // fp32 into hck or, when hck16 is set instead, bf16 (rounded to nearest
+    // even) into hck16
     float *hck;
+    uint16_t *hck16;
     const int32_t *ck_offs;
     int64_t ck_rows;
 };
@@ -81,7 +84,7 @@ struct BwdArgs {
     const int32_t *order;   // start order of the reverse chain; NULL: natural
     const float *h0;        // NULL: zero initial state
     const float *dht;       // NULL: zero gradient of the final state
-    const float *hck;       // forward state after every chunk [rows, Hv, d, d]
+    const uint16_t *hck;    // forward state after every chunk [rows, Hv, d, d], bf16
     uint16_t *tmat;         // per chunk: T^T, T = (I + diag(b) A~)^-1, bf16 [rows, Hv, 64, 64]
     uint16_t *wt;           // per chunk: w^T, w = T diag(b e^G) K, bf16 [rows, Hv, d, 64]
     float *du0;             // per chunk: local part of dU, f32 [rows, Hv, 64 * d] in 16x16 tiles, lane-major

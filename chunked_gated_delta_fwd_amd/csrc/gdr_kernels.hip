@@ -114,7 +114,8 @@ struct FwdLds {
 };
 
 
-template <int D, bool IN_BF16, bool GATE_BF16, bool CKPT>
+// CK: chunk-boundary states not written (0), written fp32 (1) or bf16 (2).
+template <int D, bool IN_BF16, bool GATE_BF16, int CK>
 __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     using Ly = FwdLds<D>;
     constexpr int PK = Ly::PK, PP = Ly::PP, PAT = Ly::PAT, PDI = Ly::PDI;
@@ -196,7 +197,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     const int lq = lane >> 4;
     const int colw = role * DW;         // the chain wave's 16*NTW state columns
     const int64_t nch = (eos - bos + C - 1) / C;
-    const int64_t ck_base = !CKPT ? 0 : a.ck_offs ? static_cast<int64_t>(a.ck_offs[n]) : n * ((a.seq_len + C - 1) / C);
+    const int64_t ck_base = CK == 0 ? 0 : a.ck_offs ? static_cast<int64_t>(a.ck_offs[n]) : n * ((a.seq_len + C - 1) / C);
 
     // Cross-role hand-off through the LDS counters instead of work-group
     // barriers: a wave publishes a step after its own LDS accesses are
@@ -591,23 +592,29 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 }
             }
         }
-        if constexpr (CKPT) {
+        if constexpr (CK != 0) {
             // the state after this chunk, plain [dk][dv] fp32 at its chunk row
             const int64_t row = ck_base + c;
             if (row < a.ck_rows) {
                 // lane part of the offset in a register, the rest (tile, row
                 // within the tile) as the scalar offset of each store
-                const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(a.hck + (row * a.hv + h) * D * D, D * D * 4);
-                const uint32_t lane_off = (dk_of(0, 4 * lq) * D + dv_of(0, l16)) * 4;
+                constexpr uint32_t EB = CK == 2 ? 2 : 4;   // bytes per element
+                const __amdgpu_buffer_rsrc_t rd = CK == 2
+                    ? chunk_rsrc(a.hck16 + (row * a.hv + h) * D * D, D * D * EB)
+                    : chunk_rsrc(a.hck + (row * a.hv + h) * D * D, D * D * EB);
+                const uint32_t lane_off = (dk_of(0, 4 * lq) * D + dv_of(0, l16)) * EB;
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const uint32_t cst = ((dk_of(kb, r) - dk_of(0, 0)) * D + 4 * nt) * 4;
+                            const uint32_t cst = ((dk_of(kb, r) - dk_of(0, 0)) * D + 4 * nt) * EB;
                             const float val = hs[kb][nt][r];   // (bit-casting the vector element directly stored element 0)
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), rd, lane_off, cst, 0);
+                            if constexpr (CK == 2)
+                                __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(val), rd, lane_off, cst, 0);
+                            else
+                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), rd, lane_off, cst, 0);
                         }
             }
         }
@@ -1020,7 +1027,9 @@ __global__ void __launch_bounds__(64) gdr_selftest_kernel(const uint16_t *a, con
 
 template <int D, bool IN_BF16, bool GATE_BF16>
 hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
-    auto kern = a.hck ? gdr_fwd_kernel<D, IN_BF16, GATE_BF16, true> : gdr_fwd_kernel<D, IN_BF16, GATE_BF16, false>;
+    auto kern = a.hck16 ? gdr_fwd_kernel<D, IN_BF16, GATE_BF16, 2>
+              : a.hck   ? gdr_fwd_kernel<D, IN_BF16, GATE_BF16, 1>
+                        : gdr_fwd_kernel<D, IN_BF16, GATE_BF16, 0>;
     const int lds = FwdLds<D>::bytes;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1065,15 +1074,15 @@ hipError_t fwd_slots(int d, int in_bf16, int gate_bf16, int *slots) {
     if (e != hipSuccess) return e;
     const void *kern;
     if (d == 64)
-        kern = in_bf16 ? (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, true, false>)
-                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, false, false>))
-                       : (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<64, false, true, false>)
-                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<64, false, false, false>));
+        kern = in_bf16 ? (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, true, 0>)
+                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, false, 0>))
+                       : (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<64, false, true, 0>)
+                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<64, false, false, 0>));
     else
-        kern = in_bf16 ? (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, true, false>)
-                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, false, false>))
-                       : (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<128, false, true, false>)
-                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<128, false, false, false>));
+        kern = in_bf16 ? (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, true, 0>)
+                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, false, 0>))
+                       : (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<128, false, true, 0>)
+                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<128, false, false, 0>));
     const int lds = fwd_lds_bytes(d);
     if ((e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFwdThreads, lds)) != hipSuccess) return e;
