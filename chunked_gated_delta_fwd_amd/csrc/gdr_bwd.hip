@@ -261,11 +261,14 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     float *sBG = sB + C;
 
     ChunkAt p;
-    if (!chunk_at(a, blockIdx.x, p)) return;
-    const int h = blockIdx.y;
+    // one work item per (chunk row, v-head); v-heads of a q/k head share an L2
+    const int64_t item = gqa_xcd_item(blockIdx.x, gridDim.x, a.hv, a.hk);
+    const int64_t crow = item / a.hv;
+    if (!chunk_at(a, crow, p)) return;
+    const int h = static_cast<int>(item % a.hv);
     const int hk = h / (a.hv / a.hk);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lq = lane >> 4;
-    const int64_t rh = static_cast<int64_t>(blockIdx.x) * a.hv + h;
+    const int64_t rh = crow * a.hv + h;
 
     stage_rows2<D, IN_BF16, kBwdThreads, PQ, PK>(sQ, a.q, a.hk, hk, sK, a.k, a.hk, hk, p.t0, p.len, tid);
     stage_rows<D, IN_BF16, kBwdThreads>(sO, PO, a.dout, p.t0, p.len, a.hv, h, tid);
@@ -421,8 +424,9 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
     float *sLam = sGs + C;
     float *sGL = sLam + C;
 
-    const int64_t rank = blockIdx.x / a.hv;
-    const int h = static_cast<int>(blockIdx.x % a.hv);
+    const int64_t item = gqa_xcd_item(blockIdx.x, gridDim.x, a.hv, a.hk);   // v-heads of a q/k head share an L2
+    const int64_t rank = item / a.hv;
+    const int h = static_cast<int>(item % a.hv);
     const int64_t n = a.order ? static_cast<int64_t>(a.order[rank]) : rank;
     if (n < 0 || n >= a.n_seq) return;
     int64_t bos, eos;
@@ -968,7 +972,7 @@ hipError_t launch_with_lds(K kern, dim3 grid, dim3 block, int lds, hipStream_t s
 template <int D, bool IN_BF16, bool GATE_BF16>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     const unsigned rows = static_cast<unsigned>(a.rows);
-    hipError_t e = launch_with_lds(gdr_bwd_prep_kernel<D, IN_BF16, GATE_BF16>, dim3(rows, a.hv),
+    hipError_t e = launch_with_lds(gdr_bwd_prep_kernel<D, IN_BF16, GATE_BF16>, dim3(static_cast<unsigned>(rows * a.hv)),
                                    dim3(kBwdThreads), PrepLds<D>::bytes, stream, a);
     if (e != hipSuccess) return e;
     e = launch_with_lds(gdr_bwd_chain_kernel<D, IN_BF16, GATE_BF16>,

@@ -167,6 +167,22 @@ __device__ __forceinline__ bf16x8 ext8(bf16x4 a) { return __builtin_shufflevecto
 // wait until this wave's LDS accesses are complete (also a compiler barrier)
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Work-groups are dispatched round-robin over the 8 XCDs (each with its own
+// L2), so blocks b and b + 8 run on one XCD at about the same time.  Over a
+// grid of (item / hv, v-head item % hv) work items this renumbering gives
+// such blocks the r = hv / hk v-heads that share a q/k head, so the second
+// finds q and k in L2 (spans of 8 r items; a partial last span is left as is).
+__device__ __forceinline__ int64_t gqa_xcd_item(int64_t item, int64_t grid, int hv, int hk) {
+    const int64_t r = hv / hk;
+    const int64_t span = 8 * r;
+    const int64_t full = (grid / span) * span;
+    if (r > 1 && item < full) {
+        const int64_t w = item % span;
+        item = (item - w) + (w % 8) * r + w / 8;
+    }
+    return item;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0

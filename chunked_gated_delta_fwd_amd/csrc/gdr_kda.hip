@@ -170,19 +170,7 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
     float *sB = sELm + D;
     float *sTot = reinterpret_cast<float *>(lds + Ly::oTot);
 
-    // Work-groups are dispatched round-robin over the 8 XCDs (each with its
-    // own L2): blocks b and b + 8 share an XCD, so they are given the v-heads
-    // of one q/k head and the second finds q and k in L2.
-    int64_t item = blockIdx.x;
-    {
-        const int64_t r = a.hv / a.hk;
-        const int64_t span = 8 * r;
-        const int64_t full = (static_cast<int64_t>(gridDim.x) / span) * span;
-        if (r > 1 && item < full) {
-            const int64_t w = item % span;
-            item = (item - w) + (w % 8) * r + w / 8;
-        }
-    }
+    const int64_t item = gqa_xcd_item(blockIdx.x, gridDim.x, a.hv, a.hk);   // v-heads of a q/k head share an L2
     const int64_t rank = item / a.hv;
     const int h = static_cast<int>(item % a.hv);
     const int64_t n = a.order ? static_cast<int64_t>(a.order[rank]) : rank;

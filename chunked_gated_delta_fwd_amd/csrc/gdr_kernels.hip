@@ -161,16 +161,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     // own L2), so block b and b+8 start together on one XCD: blocks are
     // renumbered so those get the r = Hv/Hk v-heads that share a q/k head,
     // and the second reads q and k from L2.
-    int64_t item = blockIdx.x;
-    {
-        const int64_t r = a.hv / a.hk;
-        const int64_t span = 8 * r;
-        const int64_t full = (static_cast<int64_t>(gridDim.x) / span) * span;
-        if (r > 1 && item < full) {
-            const int64_t w = item % span;
-            item = (item - w) + (w % 8) * r + w / 8;
-        }
-    }
+    const int64_t item = gqa_xcd_item(blockIdx.x, gridDim.x, a.hv, a.hk);
     const int64_t rank = item / a.hv;
     const int h = static_cast<int>(item % a.hv);
     const int64_t n = a.order ? static_cast<int64_t>(a.order[rank]) : rank;
