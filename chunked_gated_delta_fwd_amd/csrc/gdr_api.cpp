@@ -436,7 +436,7 @@ BwdWorkspace bwd_workspace(int64_t n_seq, int64_t rows, int64_t hv, int64_t d, b
     w.dhe = o;
     o += al(ch * dd * dd * 2);
     w.du0 = o;
-    o += al(ch * gdr::kChunk * dd * 4);
+    o += al(ch * gdr::kChunk * dd * 2);
     w.du = o;
     o += al(ch * gdr::kChunk * dd * 2);
     w.tmat = o;
@@ -561,7 +561,7 @@ int run_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
         ba.hck = hck;
         ba.tmat = reinterpret_cast<uint16_t *>(base + wl.tmat);
         ba.wt = reinterpret_cast<uint16_t *>(base + wl.wt);
-        ba.du0 = reinterpret_cast<float *>(base + wl.du0);
+        ba.du0 = reinterpret_cast<uint16_t *>(base + wl.du0);
         ba.du = reinterpret_cast<uint16_t *>(base + wl.du);
         ba.dhe = reinterpret_cast<uint16_t *>(base + wl.dhe);
         ba.dq = dq->data;

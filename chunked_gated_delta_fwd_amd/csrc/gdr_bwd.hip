@@ -157,14 +157,14 @@ __device__ __forceinline__ void fetch_block(v4u32 (&dst)[NP], const uint16_t *sr
 #pragma unroll
     for (int j = 0; j < NP; ++j) dst[j] = *reinterpret_cast<const v4u32 *>(src + 8 * (tid + j * NT));
 }
-// This wave's dU0 tiles (16x16, lane-major) of dv tiles ct .. ct+NTW-1.
+// This wave's dU0 tiles (16x16 bf16, lane-major) of dv tiles ct .. ct+NTW-1.
 template <int MT, int NTW>
-__device__ __forceinline__ void fetch_tiles(f32x4 (&dst)[4][NTW], const float *src, int ct, int lane) {
+__device__ __forceinline__ void fetch_tiles(bf16x4 (&dst)[4][NTW], const uint16_t *src, int ct, int lane) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
-            dst[mt][nt] = *reinterpret_cast<const f32x4 *>(src + ((mt * MT + ct + nt) * 64 + lane) * 4);
+            dst[mt][nt] = *reinterpret_cast<const bf16x4 *>(src + ((mt * MT + ct + nt) * 64 + lane) * 4);
 }
 
 // Which sequence and chunk a chunk row belongs to.
@@ -374,8 +374,8 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
             acc = mfma32(frag_cols(sTt, PT, 16 * it, k0, l16, lq), frag_cols(sK, PK, 16 * dt, k0, l16, lq), acc);
         *reinterpret_cast<bf16x4 *>(wg + (16 * dt + l16) * C + 16 * it + 4 * lq) = cvt4(acc);
     }
-    // dU0 = (scale M o Q K^T)^T dO, in 16x16 tiles (token block, dv tile), lane-major
-    float *ug = a.du0 + rh * (C * D);
+    // dU0 = (scale M o Q K^T)^T dO, in 16x16 tiles (token block, dv tile), lane-major, bf16
+    uint16_t *ug = a.du0 + rh * (C * D);
     for (int t = wave; t < 4 * NTD; t += 8) {
         const int jt = t & 3, nt = t >> 2;
         f32x4 acc = zero4();
@@ -383,7 +383,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
         for (int k0 = 0; k0 < C; k0 += 32)
             if (k0 + 32 > 16 * jt)
                 acc = mfma32(frag_rows(sPt, PP, 16 * jt, k0, l16, lq), frag_cols(sO, PO, 16 * nt, k0, l16, lq), acc);
-        *reinterpret_cast<f32x4 *>(ug + ((jt * NTD + nt) * 64 + lane) * 4) = acc;
+        *reinterpret_cast<bf16x4 *>(ug + ((jt * NTD + nt) * 64 + lane) * 4) = cvt4(acc);
     }
 }
 
@@ -451,7 +451,7 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
     // dU0 tiles, fetched once the current ones are used.
     v4u32 pq[NQ], pk[NQ], po[NQ], pw[NW];
     float pg = 0.f;
-    f32x4 pu[4][NTW];
+    bf16x4 pu[4][NTW];
 #define GDR_FETCH(cc)                                                                                  \
     {                                                                                                  \
         const int64_t t0_ = bos + C * (cc);                                                            \
@@ -549,7 +549,7 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
-                f32x4 u = pu[mt][nt];
+                f32x4 u = up4(pu[mt][nt]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) u[r] += sLam[16 * mt + 4 * lq + r] * X1[mt][nt][r];
                 dUb[mt][nt] = cvt4(u);

@@ -100,6 +100,20 @@ def test_bwd_fp32_inputs_d128():
     _compare(_gpu(d), _oracle(d), "fp32 inputs d128")
 
 
+@pytest.mark.parametrize("g_mode", ["logsigmoid/16", "zero"])
+def test_bwd_slow_and_no_decay(g_mode):
+    """Gates that decay slowly or not at all, so the state gradient carries
+    across many chunks (with logsigmoid(N(0, 1)) gates a chunk decays by about
+    e^-50 and the chunk-to-chunk recursion barely reaches the other chunks'
+    gradients): segments of up to 700 tokens, GQA, ghosts."""
+    import gdr_inputs
+    w = gdr_inputs.Workload("slow", 1, 0, 2, 4, 128, 128, "bf16", seg_range=(100, 700), n_segments=5,
+                            seed=71)
+    d = gdr_inputs.generate(w, g_mode=g_mode)
+    d.update(gdr_inputs.generate_grads(d, seed=72))
+    _compare(_gpu(d), _oracle(d), "decay %s" % g_mode)
+
+
 def test_bwd_long_sampled_heads():
     """T = 20468 (last chunk 52 tokens), 16 heads: all gradients of heads 0 and 9."""
     d = _case("long_T20468_H16_d128")
