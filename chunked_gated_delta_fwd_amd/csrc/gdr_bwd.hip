@@ -511,16 +511,15 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
         __syncthreads();
         if (c > 0) GDR_FETCH(c - 1)   // in flight during this chunk's products
 
-        // dS' of this chunk (bf16), for the per-chunk gradient kernel
+        // dS' of this chunk (bf16 in tile order: a lane's four values of tile
+        // (mt, nt) as one 8-byte piece), for the per-chunk gradient kernel
         {
-            uint16_t *dst = a.dhe + rh * D * D;
+            uint16_t *dst = a.dhe + rh * D * D + (wave * MT * NTW * 64 + lane) * 4;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        dst[(16 * mt + 4 * lq + r) * D + colw + 16 * nt + l16] = bf16_bits(dH[mt][nt][r]);
+                    *reinterpret_cast<bf16x4 *>(dst + (mt * NTW + nt) * 64 * 4) = cvt4(dH[mt][nt]);
         }
 
         // X1 = K dS'
@@ -610,11 +609,36 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
 // Per (chunk, q/k head), looping over the v-heads of the group: all input
 // gradients of the chunk's tokens.
 // --------------------------------------------------------------------------
+// (dv, first dk) of 8-byte piece P (four dk rows of one dv column) of a bf16
+// state in the forward kernel's tile order (4 chain waves of d/4 columns,
+// tiles (kb, nt), kb < d/16, nt < d/64)
+template <int D>
+__device__ __forceinline__ void fwd_piece(int P, int &dv, int &dk0) {
+    constexpr int NTW = D / 64, KB = D / 16;
+    const int ln = P & 63, t = P >> 6, nt = t % NTW, kb = (t / NTW) % KB, w = t / (NTW * KB);
+    dk0 = 32 * (kb >> 1) + 8 * (ln >> 4) + 4 * (kb & 1);
+    dv = w * (D / 4) + 4 * NTW * ((ln & 15) >> 2) + 4 * nt + (ln & 3);
+}
+// The same for the chain kernel's tile order (tiles (mt, nt), mt < d/16, nt < d/64)
+template <int D>
+__device__ __forceinline__ void chain_piece(int P, int &dv, int &dk0) {
+    constexpr int NTW = D / 64, MT = D / 16;
+    const int ln = P & 63, t = P >> 6, nt = t % NTW, mt = (t / NTW) % MT, w = t / (NTW * MT);
+    dk0 = 16 * mt + 4 * (ln >> 4);
+    dv = w * (D / 4) + 16 * nt + (ln & 15);
+}
+// bf16 element e (0..3) of four packed in two words, as bits / as float
+__device__ __forceinline__ uint32_t bf16_of(v2u32 x, int e) { return (e & 1) ? x[e >> 1] >> 16 : x[e >> 1] & 0xFFFFu; }
+
 template <int D>
 struct GradLds {
     // [64][D] rows at a pitch of 2 mod 32 four-byte banks: their 8-byte
     // row-fragment reads (16 lanes, one row each) are free of conflicts
     static constexpr int PK = D + 4;
+    // S^T / dS'^T: 6 mod 32 banks, so that the row fragments and the pieces of
+    // 16 consecutive rows are conflict-free and the transposing reads and the
+    // forward-order pieces at most 2-way
+    static constexpr int PS = D + 12;
     static constexpr int PP = C + 8;
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + C * PK * 2;
@@ -622,8 +646,8 @@ struct GradLds {
     static constexpr int oV = oO + C * PK * 2;        // V [64][PK]; later Zs, dBn, dB [64][PP] each
     static constexpr int oT = oV + C * PK * 2;        // T^T [64][PP]
     static constexpr int szVT = (C * PK * 2 + C * PP * 2) > 3 * C * PP * 2 ? (C * PK * 2 + C * PP * 2) : 3 * C * PP * 2;
-    static constexpr int oS = oV + szVT;              // S, later dS' [D][PK]
-    static constexpr int oU = oS + D * PK * 2;        // U [64][PK]
+    static constexpr int oS = oV + szVT;              // S^T, later dS'^T: [dv][PS] (rows dv, columns dk)
+    static constexpr int oU = oS + D * PS * 2;        // U [64][PK]
     static constexpr int oW = oU + C * PK * 2;        // dW [64][PK]
     static constexpr int oG = oW + C * PK * 2;        // f32 [64] x4: G log2(e), b, e^G, e^{G_L - G}
     static constexpr int oR = oG + 4 * C * 4;         // f32 [8][64] x2: per-wave row sums for dG and db
@@ -634,7 +658,7 @@ struct GradLds {
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
     using Ly = GradLds<D>;
-    constexpr int PK = Ly::PK, PP = Ly::PP, NTD = D / 16;
+    constexpr int PK = Ly::PK, PS = Ly::PS, PP = Ly::PP, NTD = D / 16;
     extern __shared__ __align__(16) unsigned char lds[];
     uint16_t *sQ = reinterpret_cast<uint16_t *>(lds + Ly::oQ);
     uint16_t *sK = reinterpret_cast<uint16_t *>(lds + Ly::oK);
@@ -692,22 +716,21 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
         {
             // all of this v-head's staging loads are issued before the first store
             constexpr int PR = D / 8, NP = C * PR / kBwdThreads, NT8 = C * C / 8 / kBwdThreads;
-            constexpr int NS8 = D * D / 8 / kBwdThreads;   // 16-byte pieces (8 bf16) of the state per thread
-            v4u32 rv[NP], ro[NP], rt[NT8], rs8[NS8];
+            constexpr int NS4 = D * D / 4 / kBwdThreads;   // 8-byte pieces (4 bf16) of the state per thread
+            v4u32 rv[NP], ro[NP], rt[NT8];
+            v2u32 rs4[NS4];
             fetch_rows<D, IN_BF16, NP, kBwdThreads>(rv, a.v, p.t0, p.len, a.hv, h, tid);
             fetch_rows<D, IN_BF16, NP, kBwdThreads>(ro, a.dout, p.t0, p.len, a.hv, h, tid);
             if (Sb) {
 #pragma unroll
-                for (int j = 0; j < NS8; ++j) rs8[j] = *reinterpret_cast<const v4u32 *>(Sb + 8 * (tid + j * kBwdThreads));
+                for (int j = 0; j < NS4; ++j) rs4[j] = *reinterpret_cast<const v2u32 *>(Sb + 4 * (tid + j * kBwdThreads));
             } else {
-                // a sequence's first chunk: h0 rounded to bf16 here (the only
-                // chunk whose staging waits for its state loads)
+                // a sequence's first chunk: h0 ([dk][dv] fp32) rounded to bf16
+                // here (the only chunk whose staging waits for its state loads)
 #pragma unroll
-                for (int j = 0; j < NS8; ++j) {
-                    const float *src = Sg ? Sg + 8 * (tid + j * kBwdThreads) : nullptr;
-                    const f32x4 x0 = src ? *reinterpret_cast<const f32x4 *>(src) : zero4();
-                    const f32x4 x1 = src ? *reinterpret_cast<const f32x4 *>(src + 4) : zero4();
-                    rs8[j] = __builtin_bit_cast(v4u32, cat(cvt4(x0), cvt4(x1)));
+                for (int j = 0; j < NS4; ++j) {
+                    const float *src = Sg ? Sg + 4 * (tid + j * kBwdThreads) : nullptr;
+                    rs4[j] = __builtin_bit_cast(v2u32, cvt4(src ? *reinterpret_cast<const f32x4 *>(src) : zero4()));
                 }
             }
             const uint16_t *tg = a.tmat + rh * (C * C);
@@ -719,10 +742,24 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
                 st16<PK % 8 == 0>(sV + off, rv[j]);
                 st16<PK % 8 == 0>(sO + off, ro[j]);
             }
+            // S^T [dv][dk] in LDS: the bf16 state piece by piece (four dk of
+            // one dv: one 8-byte store), h0 element by element.  Elements are
+            // taken with integer shifts (extracting __bf16 vector elements for
+            // 2-byte stores has been compiled to stores of one register for all)
+            if (Sb) {
 #pragma unroll
-            for (int j = 0; j < NS8; ++j) {
-                const int i = tid + j * kBwdThreads;
-                st16<PK % 8 == 0>(sS + (i / (D / 8)) * PK + 8 * (i % (D / 8)), rs8[j]);
+                for (int j = 0; j < NS4; ++j) {
+                    int dvp, dk0;
+                    fwd_piece<D>(tid + j * kBwdThreads, dvp, dk0);
+                    *reinterpret_cast<v2u32 *>(sS + dvp * PS + dk0) = rs4[j];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NS4; ++j) {
+                    const int i = 4 * (tid + j * kBwdThreads), dk = i / D, dv0 = i % D;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sS[(dv0 + e) * PS + dk] = static_cast<uint16_t>(bf16_of(rs4[j], e));
+                }
             }
 #pragma unroll
             for (int j = 0; j < NT8; ++j) {
@@ -748,7 +785,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) Rt[mt] = zero4();
             for (int kk = 0; kk < D / 32; ++kk) {
-                const bf16x8 bs = frag_cols(sS, PK, 16 * nt, 32 * kk, l16, lq);
+                const bf16x8 bs = frag_rows(sS, PS, 16 * nt, 32 * kk, l16, lq);   // S^T rows: B = S [dk][dv]
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) Rt[mt] = mfma32(frag_rows(sK, PK, 16 * mt, 32 * kk, l16, lq), bs, Rt[mt]);
             }
@@ -794,15 +831,16 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
         __syncthreads();
 
         // dQ1 = dO S^T, dK1 = dW S^T (dk tile nt)
-        constexpr int NDS = D * D / 8 / kBwdThreads;   // 16-byte pieces of dS' per thread
-        v4u32 pds[NDS];
-        fetch_block<NDS, kBwdThreads>(pds, a.dhe + rh * D * D, tid);
+        constexpr int NDS = D * D / 4 / kBwdThreads;   // 8-byte pieces of dS' per thread
+        v2u32 pds[NDS];
+#pragma unroll
+        for (int j = 0; j < NDS; ++j) pds[j] = *reinterpret_cast<const v2u32 *>(a.dhe + rh * D * D + 4 * (tid + j * kBwdThreads));
         f32x4 dQt[4], dK1[4];   // dQt: scale e^G dO S^T, then + Zs K
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) dQt[mt] = dK1[mt] = zero4();
         if (colwave) {
             for (int kk = 0; kk < D / 32; ++kk) {
-                const bf16x8 bs = frag_rows(sS, PK, 16 * nt, 32 * kk, l16, lq);
+                const bf16x8 bs = frag_cols(sS, PS, 16 * nt, 32 * kk, l16, lq);   // B = S^T
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     dQt[mt] = mfma32(frag_rows(sO, PK, 16 * mt, 32 * kk, l16, lq), bs, dQt[mt]);
@@ -821,13 +859,14 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
             float part = 0.f;
 #pragma unroll
             for (int j = 0; j < NDS; ++j) {
-                const int i = tid + j * kBwdThreads, row = i / (D / 8), col = 8 * (i % (D / 8));
-                uint16_t *sp = sS + row * PK + col;
-                const bf16x8 sv = __builtin_bit_cast(bf16x8, ld16<PK % 8 == 0>(sp));
-                const bf16x8 dv = __builtin_bit_cast(bf16x8, pds[j]);
+                int dvp, dk0;
+                chain_piece<D>(tid + j * kBwdThreads, dvp, dk0);
+                v2u32 *sp = reinterpret_cast<v2u32 *>(sS + dvp * PS + dk0);
+                const v2u32 sv = *sp;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) part += static_cast<float>(dv[e]) * static_cast<float>(sv[e]);
-                st16<PK % 8 == 0>(sp, pds[j]);
+                for (int e = 0; e < 4; ++e)
+                    part += __uint_as_float(bf16_of(pds[j], e) << 16) * __uint_as_float(bf16_of(sv, e) << 16);
+                *sp = pds[j];
             }
             part = lane63(wave_inclusive_scan(part));
             if (lane == 0) sXd[wave] = part;
@@ -865,7 +904,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) Kc[mt] = Yb[mt] = zero4();
             for (int kk = 0; kk < D / 32; ++kk) {
-                const bf16x8 bd = frag_rows(sS, PK, 16 * nt, 32 * kk, l16, lq);
+                const bf16x8 bd = frag_cols(sS, PS, 16 * nt, 32 * kk, l16, lq);   // B = dS'^T
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) Kc[mt] = mfma32(frag_rows(sU, PK, 16 * mt, 32 * kk, l16, lq), bd, Kc[mt]);
             }

@@ -24,8 +24,11 @@ struct FwdArgs {
     float scale;
     // chunk-boundary states (NULL: not written): row ck_offs[n] + c (or
     // n * ceil(seq_len / 64) + c for fixed-length rows) of [ck_rows, Hv, d, d],
-    // fp32 into hck or, when hck16 is set instead, bf16 (rounded to nearest
-    // even) into hck16
+    // fp32 [dk][dv] into hck or, when hck16 is set instead, bf16 (rounded to
+    // nearest even) into hck16 in the forward kernel's tile order: 8-byte
+    // piece ((w * d/16 + kb) * (d/64) + nt) * 64 + lane holds rows
+    // 32 (kb/2) + 8 (lane/16) + 4 (kb%2) + 0..3 of column
+    // w d/4 + (d/16) (lane%16 / 4) + 4 nt + lane%4 (w = chain wave 0..3)
     float *hck;
     uint16_t *hck16;
     const int32_t *ck_offs;
@@ -84,12 +87,15 @@ struct BwdArgs {
     const int32_t *order;   // start order of the reverse chain; NULL: natural
     const float *h0;        // NULL: zero initial state
     const float *dht;       // NULL: zero gradient of the final state
-    const uint16_t *hck;    // forward state after every chunk [rows, Hv, d, d], bf16
+    const uint16_t *hck;    // forward state after every chunk [rows, Hv, d*d], bf16 in the forward's tile order (FwdArgs::hck16)
     uint16_t *tmat;         // per chunk: T^T, T = (I + diag(b) A~)^-1, bf16 [rows, Hv, 64, 64]
     uint16_t *wt;           // per chunk: w^T, w = T diag(b e^G) K, bf16 [rows, Hv, d, 64]
     uint16_t *du0;          // per chunk: local part of dU, bf16 [rows, Hv, 64 * d] in 16x16 tiles, lane-major
     uint16_t *du;           // per chunk: dU, bf16, same tiling
-    uint16_t *dhe;          // per chunk: gradient of the state at its end, bf16 [rows, Hv, d, d]
+    // per chunk: gradient of the state at its end, bf16 [rows, Hv, d*d] in the
+    // chain kernel's tile order: 8-byte piece ((w * d/16 + mt) * (d/64) + nt) * 64
+    // + lane holds rows 16 mt + 4 (lane/16) + 0..3 of column w d/4 + 16 nt + lane%16
+    uint16_t *dhe;
     void *dq, *dk, *dv;     // dtype of q
     float *dg, *dbeta;
     float *dh0;             // NULL: not written

@@ -589,24 +589,31 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             if (row < a.ck_rows) {
                 // lane part of the offset in a register, the rest (tile, row
                 // within the tile) as the scalar offset of each store
-                constexpr uint32_t EB = CK == 2 ? 2 : 4;   // bytes per element
-                const __amdgpu_buffer_rsrc_t rd = CK == 2
-                    ? chunk_rsrc(a.hck16 + (row * a.hv + h) * D * D, D * D * EB)
-                    : chunk_rsrc(a.hck + (row * a.hv + h) * D * D, D * D * EB);
-                const uint32_t lane_off = (dk_of(0, 4 * lq) * D + dv_of(0, l16)) * EB;
+                if constexpr (CK == 2) {
+                    // bf16 in tile order: a lane's four values of tile (kb, nt)
+                    // as one 8-byte piece, 512 contiguous bytes per store
+                    const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(a.hck16 + (row * a.hv + h) * D * D, D * D * 2);
+                    const uint32_t lane_off = (role * KB * NTW * 64 + lane) * 8;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+                    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt)
+                        for (int nt = 0; nt < NTW; ++nt)
+                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, cvt4(hs[kb][nt])), rd,
+                                                                  lane_off, (kb * NTW + nt) * 64 * 8, 0);
+                } else {
+                    const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(a.hck + (row * a.hv + h) * D * D, D * D * 4);
+                    const uint32_t lane_off = (dk_of(0, 4 * lq) * D + dv_of(0, l16)) * 4;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const uint32_t cst = ((dk_of(kb, r) - dk_of(0, 0)) * D + 4 * nt) * EB;
-                            const float val = hs[kb][nt][r];   // (bit-casting the vector element directly stored element 0)
-                            if constexpr (CK == 2)
-                                __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(val), rd, lane_off, cst, 0);
-                            else
+                    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const uint32_t cst = ((dk_of(kb, r) - dk_of(0, 0)) * D + 4 * nt) * 4;
+                                const float val = hs[kb][nt][r];   // (bit-casting the vector element directly stored element 0)
                                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), rd, lane_off, cst, 0);
-                        }
+                            }
+                }
             }
         }
         publish(cChain);   // done with chunk c: its q/k buffer and its prepared buffers are free
