@@ -635,6 +635,9 @@ struct GradLds {
     // [64][D] rows at a pitch of 2 mod 32 four-byte banks: their 8-byte
     // row-fragment reads (16 lanes, one row each) are free of conflicts
     static constexpr int PK = D + 4;
+    // dO, U, dW: key-permuted columns (kpos), read as 16-byte fragments
+    // (16-byte aligned rows)
+    static constexpr int PKP = D + 16;
     // S^T / dS'^T: 6 mod 32 banks, so that the row fragments and the pieces of
     // 16 consecutive rows are conflict-free and the transposing reads and the
     // forward-order pieces at most 2-way
@@ -642,14 +645,14 @@ struct GradLds {
     static constexpr int PP = C + 8;
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + C * PK * 2;
-    static constexpr int oO = oK + C * PK * 2;
-    static constexpr int oV = oO + C * PK * 2;        // V [64][PK]; later Zs, dBn, dB [64][PP] each
+    static constexpr int oO = oK + C * PK * 2;        // dO [64][PKP]
+    static constexpr int oV = oO + C * PKP * 2;       // V [64][PK]; later Zs, dBn, dB [64][PP] each
     static constexpr int oT = oV + C * PK * 2;        // T^T [64][PP]
     static constexpr int szVT = (C * PK * 2 + C * PP * 2) > 3 * C * PP * 2 ? (C * PK * 2 + C * PP * 2) : 3 * C * PP * 2;
     static constexpr int oS = oV + szVT;              // S^T, later dS'^T: [dv][PS] (rows dv, columns dk)
-    static constexpr int oU = oS + D * PS * 2;        // U [64][PK]
-    static constexpr int oW = oU + C * PK * 2;        // dW [64][PK]
-    static constexpr int oG = oW + C * PK * 2;        // f32 [64] x4: G log2(e), b, e^G, e^{G_L - G}
+    static constexpr int oU = oS + D * PS * 2;        // U [64][PKP]
+    static constexpr int oW = oU + C * PKP * 2;       // dW [64][PKP]
+    static constexpr int oG = oW + C * PKP * 2;        // f32 [64] x4: G log2(e), b, e^G, e^{G_L - G}
     static constexpr int oR = oG + 4 * C * 4;         // f32 [8][64] x2: per-wave row sums for dG and db
     static constexpr int oX = oR + 2 * 8 * C * 4;     // f32 [8] x2: per-wave sums of <dS', S> and the lambda k.(U dS'^T) terms; e^{G_L}
     static constexpr int bytes = oX + 2 * 8 * 4 + 16;
@@ -658,7 +661,7 @@ struct GradLds {
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
     using Ly = GradLds<D>;
-    constexpr int PK = Ly::PK, PS = Ly::PS, PP = Ly::PP, NTD = D / 16;
+    constexpr int PK = Ly::PK, PKP = Ly::PKP, PS = Ly::PS, PP = Ly::PP, NTD = D / 16;
     extern __shared__ __align__(16) unsigned char lds[];
     uint16_t *sQ = reinterpret_cast<uint16_t *>(lds + Ly::oQ);
     uint16_t *sK = reinterpret_cast<uint16_t *>(lds + Ly::oK);
@@ -740,7 +743,10 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
             for (int j = 0; j < NP; ++j) {
                 const int i = tid + j * kBwdThreads, off = (i / PR) * PK + 8 * (i % PR);
                 st16<PK % 8 == 0>(sV + off, rv[j]);
-                st16<PK % 8 == 0>(sO + off, ro[j]);
+                // dO with key-permuted columns: the piece's two halves of four
+                const int orow = i / PR, oc = 8 * (i % PR);
+                *reinterpret_cast<v2u32 *>(sO + orow * PKP + kpos(oc)) = v2u32{ro[j][0], ro[j][1]};
+                *reinterpret_cast<v2u32 *>(sO + orow * PKP + kpos(oc + 4)) = v2u32{ro[j][2], ro[j][3]};
             }
             // S^T [dv][dk] in LDS: the bf16 state piece by piece (four dk of
             // one dv: one 8-byte store), h0 element by element.  Elements are
@@ -818,8 +824,8 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * mt + 4 * lq + r;
                     if (i < p.len) store_elem<IN_BF16>(a.dv, ((p.t0 + i) * a.hv + h) * D + 16 * nt + l16, sB[i] * dW[mt][r]);
-                    sU[i * PK + 16 * nt + l16] = bf16_bits(U[mt][r]);
-                    sDW[i * PK + 16 * nt + l16] = bf16_bits(dW[mt][r]);
+                    sU[i * PKP + kpos(16 * nt + l16)] = bf16_bits(U[mt][r]);
+                    sDW[i * PKP + kpos(16 * nt + l16)] = bf16_bits(dW[mt][r]);
                     pb[r] = row_sum16(dW[mt][r] * Rt[mt][r]);
                 }
                 if (l16 == 15) {
@@ -843,8 +849,8 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
                 const bf16x8 bs = frag_cols(sS, PS, 16 * nt, 32 * kk, l16, lq);   // B = S^T
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
-                    dQt[mt] = mfma32(frag_rows(sO, PK, 16 * mt, 32 * kk, l16, lq), bs, dQt[mt]);
-                    dK1[mt] = mfma32(frag_rows(sDW, PK, 16 * mt, 32 * kk, l16, lq), bs, dK1[mt]);
+                    dQt[mt] = mfma32(kfrag8(sO, PKP, 16 * mt, 32 * kk, l16, lq), bs, dQt[mt]);
+                    dK1[mt] = mfma32(kfrag8(sDW, PKP, 16 * mt, 32 * kk, l16, lq), bs, dK1[mt]);
                 }
             }
 #pragma unroll
@@ -877,9 +883,9 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
             if (bi >= bj) {
 #pragma unroll
                 for (int kk = 0; kk < D / 32; ++kk) {
-                    const bf16x8 bu = frag_rows(sU, PK, 16 * bj, 32 * kk, l16, lq);
-                    z0 = mfma32(frag_rows(sO, PK, 16 * bi, 32 * kk, l16, lq), bu, z0);
-                    z1 = mfma32(frag_rows(sDW, PK, 16 * bi, 32 * kk, l16, lq), bu, z1);
+                    const bf16x8 bu = kfrag8(sU, PKP, 16 * bj, 32 * kk, l16, lq);
+                    z0 = mfma32(kfrag8(sO, PKP, 16 * bi, 32 * kk, l16, lq), bu, z0);
+                    z1 = mfma32(kfrag8(sDW, PKP, 16 * bi, 32 * kk, l16, lq), bu, z1);
                 }
             }
             const int j = 16 * bj + l16;
@@ -906,7 +912,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
             for (int kk = 0; kk < D / 32; ++kk) {
                 const bf16x8 bd = frag_cols(sS, PS, 16 * nt, 32 * kk, l16, lq);   // B = dS'^T
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) Kc[mt] = mfma32(frag_rows(sU, PK, 16 * mt, 32 * kk, l16, lq), bd, Kc[mt]);
+                for (int mt = 0; mt < 4; ++mt) Kc[mt] = mfma32(kfrag8(sU, PKP, 16 * mt, 32 * kk, l16, lq), bd, Kc[mt]);
             }
             float lastp = 0.f;
 #pragma unroll

@@ -219,5 +219,14 @@ __device__ __forceinline__ float buf_load_scalar(__amdgpu_buffer_rsrc_t r, uint3
     else return __builtin_bit_cast(float, buf_load<4>(r, off));
 }
 
+// Column position of key index x within its block of 32 in a key-permuted LDS
+// array: x = 16 h + 4 j + r is stored at 8 j + 4 h + r, so that one
+// 16-byte read at 8 lq gives lane (l16, lq) the eight key slots of a 16x16x32
+// MFMA operand, keys 4 lq + r and 16 + 4 lq + r, in the order of a C tile's
+// rows (the same order on both operands, so the contraction is unchanged).
+__device__ __forceinline__ int kpos(int x) { return (x & ~31) | ((x & 12) << 1) | ((x >> 2) & 4) | (x & 3); }
+__device__ __forceinline__ bf16x8 kfrag8(const uint16_t *M, int pitch, int row0, int k0, int l16, int lq) {
+    return ld8(M + (row0 + l16) * pitch + k0 + 8 * lq);
+}
 }  // namespace
 }  // namespace gdr

@@ -42,15 +42,6 @@ namespace {
 
 constexpr int kKdaThreads = 512;
 
-// Column position of key index x within its block of 32 in the q~, k~, k^-copy
-// and P arrays: x = 16 h + 4 j + r is stored at 8 j + 4 h + r, so that one
-// 16-byte read at 8 lq gives lane (l16, lq) the eight key slots of a 16x16x32
-// MFMA operand, keys 4 lq + r and 16 + 4 lq + r, in the order of a C tile's
-// rows (the same order on both operands, so the contraction is unchanged).
-__device__ __forceinline__ int kpos(int x) { return (x & ~31) | ((x & 12) << 1) | ((x >> 2) & 4) | (x & 3); }
-__device__ __forceinline__ bf16x8 kfrag8(const uint16_t *M, int pitch, int row0, int k0, int l16, int lq) {
-    return ld8(M + (row0 + l16) * pitch + k0 + 8 * lq);
-}
 __device__ __forceinline__ bf16x8 kfrag_cols(const uint16_t *M, int pitch, int col0, int k0, int l16, int lq) {
     const uint16_t *p = M + (k0 + 4 * lq + (l16 >> 2)) * pitch + col0 + 4 * (l16 & 3);
     return cat(ld4_tr(p), ld4_tr(p + 16 * pitch));
