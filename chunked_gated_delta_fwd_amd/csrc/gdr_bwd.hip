@@ -394,10 +394,11 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
 template <int D>
 struct ChainLds {
     // q and dO are read with transposing reads (pitch 8 mod 32 four-byte
-    // banks), k and w^T as 8-byte row fragments (2 mod 32): no conflicts
+    // banks); k and w^T, A operands against register B operands in C-tile
+    // key order, with key-permuted columns (kpos) as 16-byte fragments
     static constexpr int PK = D + 16;              // q, dO
-    static constexpr int PR = D + 4;               // k
-    static constexpr int PW = C + 4;
+    static constexpr int PR = D + 16;              // k
+    static constexpr int PW = C + 16;
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + C * PK * 2;
     static constexpr int oO = oK + C * PR * 2;
@@ -493,13 +494,15 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
         for (int j = 0; j < NQ; ++j) {
             const int i = tid + j * kChainThreads, row = i / PR, col = 8 * (i % PR);
             *reinterpret_cast<v4u32 *>(sQ + row * PK + col) = pq[j];
-            st16<PKR % 8 == 0>(sK + row * PKR + col, pk[j]);
+            *reinterpret_cast<v2u32 *>(sK + row * PKR + kpos(col)) = v2u32{pk[j][0], pk[j][1]};
+            *reinterpret_cast<v2u32 *>(sK + row * PKR + kpos(col + 4)) = v2u32{pk[j][2], pk[j][3]};
             *reinterpret_cast<v4u32 *>(sO + row * PK + col) = po[j];
         }
 #pragma unroll
         for (int j = 0; j < NW; ++j) {
             const int i = tid + j * kChainThreads, row = i / (C / 8), col = 8 * (i % (C / 8));
-            st16<PW % 8 == 0>(sW + row * PW + col, pw[j]);
+            *reinterpret_cast<v2u32 *>(sW + row * PW + kpos(col)) = v2u32{pw[j][0], pw[j][1]};
+            *reinterpret_cast<v2u32 *>(sW + row * PW + kpos(col + 4)) = v2u32{pw[j][2], pw[j][3]};
         }
         if (wave == 0) {
             const float G2 = wave_inclusive_scan(pg * kLog2e);
@@ -535,7 +538,7 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
             for (int nt = 0; nt < NTW; ++nt) bh[nt] = cat(cvt4(dH[2 * kk][nt]), cvt4(dH[2 * kk + 1][nt]));
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8 af = frag_rows(sK, PKR, 16 * mt, 32 * kk, l16, lq);
+                const bf16x8 af = kfrag8(sK, PKR, 16 * mt, 32 * kk, l16, lq);
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) X1[mt][nt] = mfma32(af, bh[nt], X1[mt][nt]);
             }
@@ -580,7 +583,7 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const bf16x8 aq = frag_cols(sQ, PK, 16 * mt, 32 * kk, l16, lq);
-                const bf16x8 aw = frag_rows(sW, PW, 16 * mt, 32 * kk, l16, lq);
+                const bf16x8 aw = kfrag8(sW, PW, 16 * mt, 32 * kk, l16, lq);
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     dH[mt][nt] = mfma32(aq, bo[nt], dH[mt][nt]);
