@@ -345,7 +345,7 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
                 }
             }
         }
-        // ---- then k~ S_m and q~ S_m for this wave's dv tile, with
+        // ---- then k~ S_m and (q~ S_m)^T for this wave's dv tile, with
         // S_m = diag(e^{G_m}) H taken from the wave's own state registers
         f32x4 X[4], QS[4];
 #pragma unroll
@@ -363,7 +363,7 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     X[mt] = mfma32(kfrag8(sKt, PK, 16 * mt, 32 * kk, l16, lq), bs, X[mt]);
-                    QS[mt] = mfma32(kfrag8(sQt, PK, 16 * mt, 32 * kk, l16, lq), bs, QS[mt]);
+                    QS[mt] = mfma32(bs, kfrag8(sQt, PK, 16 * mt, 32 * kk, l16, lq), QS[mt]);   // (q~ S_m)^T
                 }
             }
         }
@@ -371,7 +371,9 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
         __syncthreads();
 
         // ---- U = (I + A)^-1 diag(b) (V - X) by block forward substitution,
-        // U_b = D_b (W_b - sum_{c<b} A_bc U_c); O = scale q~ S_m + P U; H update (dv tile nt)
+        // U_b = D_b (W_b - sum_{c<b} A_bc U_c); O^T = scale (q~ S_m)^T + (P U)^T, with
+        // the register tiles of S_m and U as A operands (so a lane holds four dv of
+        // one token: one 8-byte store); H update (dv tile nt)
         if (colwave) {
             bf16x4 ub[4];
 #pragma unroll
@@ -394,19 +396,18 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
             for (int kk = 0; kk < 2; ++kk) {
                 const bf16x8 bu = cat(ub[2 * kk], ub[2 * kk + 1]);
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) QS[mt] = mfma32(kfrag8(sP, PQ, 16 * mt, 32 * kk, l16, lq), bu, QS[mt]);
+                for (int mt = 0; mt < 4; ++mt) QS[mt] = mfma32(bu, kfrag8(sP, PQ, 16 * mt, 32 * kk, l16, lq), QS[mt]);   // (P U)^T
             }
+            // O^T tiles: lane (l16, lq) holds token 16 mt + l16, dv 16 nt + 4 lq .. + 3
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * mt + 4 * lq + r;
-                    if (i < len) {
-                        const int64_t oi = ((t0 + i) * a.hv + h) * D + 16 * nt + l16;
-                        if constexpr (IN_BF16) reinterpret_cast<uint16_t *>(a.o)[oi] = bf16_bits(QS[mt][r]);
-                        else reinterpret_cast<float *>(a.o)[oi] = QS[mt][r];
-                    }
+            for (int mt = 0; mt < 4; ++mt) {
+                const int i = 16 * mt + l16;
+                if (i < len) {
+                    const int64_t oi = ((t0 + i) * a.hv + h) * D + 16 * nt + 4 * lq;
+                    if constexpr (IN_BF16) *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(a.o) + oi) = cvt4(QS[mt]);
+                    else *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.o) + oi) = QS[mt];
                 }
+            }
             // H <- diag(e^{G_L}) H + diag(e^{G_L - G_m}) k^^T U
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
