@@ -286,24 +286,13 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
         __syncthreads();
 
         // ---- blocks of A = diag(b) k~ k^^T (strictly lower) and of P = scale q~ k^^T
-        // (lower): waves 0-3 take diagonal block b = wave of A and then its
-        // inverse; waves 4-7 share the six blocks of A below the diagonal and
-        // the ten blocks of P
+        // (lower): waves 0-3 take diagonal block b = wave of A, its inverse, then
+        // block wave of P; waves 4-7 share the six blocks of A below the diagonal
+        // and the other six blocks of P (three each)
         {
             const bool dw = wave < 4;
-            for (int t = dw ? 0 : wave - 4; t < (dw ? 1 : 16); t += dw ? 1 : 4) {
-                int bi, bj;
-                const bool ka = dw || t < 6;
-                if (dw) {
-                    bi = bj = wave;
-                } else if (t < 6) {
-                    bi = t >= 3 ? 3 : t >= 1 ? 2 : 1;
-                    bj = t - (bi - 1) * bi / 2;
-                } else {
-                    const int tt = t - 6;
-                    bi = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
-                    bj = tt - bi * (bi + 1) / 2;
-                }
+            // tile t: A blocks 0..5 below the diagonal, then P blocks (t - 2) for t = 6..11
+            auto tile = [&](bool ka, int bi, int bj) __attribute__((always_inline)) {
                 const uint16_t *Am = ka ? sKt : sQt;
                 f32x4 acc = zero4();
 #pragma unroll
@@ -316,8 +305,13 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
                     if (ka) sA[i * PP + j] = bf16_bits(j < i ? sB[i] * acc[r] : 0.f);
                     else sP[i * PQ + kpos(j)] = bf16_bits(j <= i ? a.scale * acc[r] : 0.f);
                 }
-            }
+            };
+            auto ptile = [&](int tt) __attribute__((always_inline)) {
+                const int bi = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
+                tile(false, bi, tt - bi * (bi + 1) / 2);
+            };
             if (dw) {
+                tile(true, wave, wave);
                 // inverse of diagonal block b of I + A, column l16 by fp32 forward
                 // substitution over the bf16 values this wave has just stored
                 lds_wait();
@@ -342,6 +336,16 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
                 if (lq == 0) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) sDi[(16 * b + i) * PD + l16] = bf16_bits(x[i]);
+                }
+                ptile(wave);
+            } else {
+                for (int t = wave - 4; t < 12; t += 4) {
+                    if (t < 6) {
+                        const int bi = t >= 3 ? 3 : t >= 1 ? 2 : 1;
+                        tile(true, bi, t - (bi - 1) * bi / 2);
+                    } else {
+                        ptile(t - 2);
+                    }
                 }
             }
         }
