@@ -226,6 +226,9 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
     }
     GDR_KDA_FETCH_G(0)
     GDR_KDA_FETCH_V(0)
+    // P's blocks above the diagonal are read (by P U) but never written: zero
+    // them once (all of P).  A's are neither read nor written.
+    for (int i = tid; i < C * PQ / 8; i += kKdaThreads) reinterpret_cast<v4u32 *>(sP)[i] = v4u32{0u, 0u, 0u, 0u};
 
     for (int64_t c = 0; c < nch; ++c) {
         int lane = tid & 63;   // opaque per iteration: keeps per-lane addresses inside the loop
@@ -280,9 +283,6 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) cv[j] = pv[j];
         GDR_KDA_FETCH_G(c + 1)
-        // zero A and P (blocks above the diagonal stay zero)
-        for (int i = tid; i < C * (PP + PQ) / 8; i += kKdaThreads)
-            reinterpret_cast<v4u32 *>(sA)[i] = v4u32{0u, 0u, 0u, 0u};
         __syncthreads();
 
         // ---- blocks of A = diag(b) k~ k^^T (strictly lower) and of P = scale q~ k^^T
