@@ -23,8 +23,8 @@
 //
 // One work-group of 8 waves per (sequence, v-head) walks its chunks in order;
 // wave w owns dv columns [16w, 16w + 16) of the fp32 state (MFMA C tiles, rows
-// dk).  Per chunk: the gate scan (all threads: one channel and a quarter of the
-// tokens each) and the gated operands into LDS; the ten lower blocks of A and
+// dk).  Per chunk: the gate scan (all threads: two adjacent channels and an
+// eighth of the tokens each) and the gated operands into LDS; the ten lower blocks of A and
 // of P (the four waves that make the diagonal blocks of A also invert them,
 // 16x16 by fp32 substitution), then each wave's k~ S_m and q~ S_m (S_m taken
 // from the wave's own state registers, whose C-tile layout is the B
@@ -56,13 +56,27 @@ __device__ __forceinline__ VRaw<BF16> rd_raw(__amdgpu_buffer_rsrc_t r, uint32_t 
     if constexpr (BF16) return __builtin_bit_cast(__bf16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
     else return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
-// Channel ch of g, q and k for the TPG tokens of scan group grp, one element
-// per register as loaded (nothing is computed on them here, so the loads stay
+// Two adjacent channels of one token, as loaded: bf16 pairs in one 32-bit
+// word, f32 pairs in two.
+template <bool BF16>
+using PRaw = typename std::conditional<BF16, uint32_t, v2u32>::type;
+template <bool BF16>
+__device__ __forceinline__ PRaw<BF16> rd_pair(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (BF16) return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    else return __builtin_bit_cast(v2u32, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+template <bool BF16>
+__device__ __forceinline__ float pair_val(PRaw<BF16> x, int e) {
+    if constexpr (BF16) return __uint_as_float(e ? (x & 0xffff0000u) : (x << 16));
+    else return __uint_as_float(x[e]);
+}
+// Channels 2 cp, 2 cp + 1 of g, q and k for the TPG tokens of scan group grp,
+// each pair as loaded (nothing is computed on them here, so the loads stay
 // in flight), through ranges that end at the segment's end.
 template <int D, int TPG, bool IN_BF16, bool GATE_BF16>
-__device__ __forceinline__ void kda_fetch_gate(const FwdArgs &a, int64_t t0, int len, int h, int hk, int ch,
-                                               int grp, VRaw<GATE_BF16> (&pg)[TPG], VRaw<IN_BF16> (&pq)[TPG],
-                                               VRaw<IN_BF16> (&pk)[TPG]) {
+__device__ __forceinline__ void kda_fetch_gate(const FwdArgs &a, int64_t t0, int len, int h, int hk, int cp,
+                                               int grp, PRaw<GATE_BF16> (&pg)[TPG], PRaw<IN_BF16> (&pq)[TPG],
+                                               PRaw<IN_BF16> (&pk)[TPG]) {
     constexpr uint32_t ES = IN_BF16 ? 2 : 4, GS = GATE_BF16 ? 2 : 4;
     const uint32_t gstride = static_cast<uint32_t>(a.hv) * D * GS, qstride = static_cast<uint32_t>(a.hk) * D * ES;
     const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(
@@ -71,14 +85,14 @@ __device__ __forceinline__ void kda_fetch_gate(const FwdArgs &a, int64_t t0, int
         reinterpret_cast<const unsigned char *>(a.q) + ((t0 * a.hk + hk) * D) * ES, static_cast<uint32_t>(len) * qstride);
     const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(
         reinterpret_cast<const unsigned char *>(a.k) + ((t0 * a.hk + hk) * D) * ES, static_cast<uint32_t>(len) * qstride);
-    int chv = ch;   // opaque: the per-row offsets are formed here, not hoisted by the caller's loop
-    asm volatile("" : "+v"(chv));
+    int ch0 = 2 * cp;   // opaque: the per-row offsets are formed here, not hoisted by the caller's loop
+    asm volatile("" : "+v"(ch0));
 #pragma unroll
     for (int i = 0; i < TPG; ++i) {
         const uint32_t row = static_cast<uint32_t>(grp * TPG + i);
-        pg[i] = rd_raw<GATE_BF16>(rg, row * gstride + chv * GS);
-        pq[i] = rd_raw<IN_BF16>(rq, row * qstride + chv * ES);
-        pk[i] = rd_raw<IN_BF16>(rk, row * qstride + chv * ES);
+        pg[i] = rd_pair<GATE_BF16>(rg, row * gstride + ch0 * GS);
+        pq[i] = rd_pair<IN_BF16>(rq, row * qstride + ch0 * ES);
+        pk[i] = rd_pair<IN_BF16>(rk, row * qstride + ch0 * ES);
     }
 }
 
@@ -135,7 +149,7 @@ struct KdaLds {
     static constexpr int oP = oA + C * PP * 2;     // scale tril(q~ k^^T) [i][kpos(j)]
     static constexpr int oDi = oP + C * PQ * 2;    // inverses of the diagonal blocks [4][16][PD]
     static constexpr int oV = oDi + 4 * 16 * PD * 2;   // f32 [D] x3: e^{G_m}, e^{G_L}, e^{G_L - G_m}; [64] b
-    static constexpr int NG = kKdaThreads / D;     // token groups of the gate scan
+    static constexpr int NG = 2 * kKdaThreads / D; // token groups of the gate scan (a thread: 2 channels)
     static constexpr int oTot = oV + (3 * D + C) * 4;  // f32 [NG][D] group totals of the scan
     static constexpr int bytes = oTot + NG * D * 4;
 };
@@ -198,9 +212,9 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
     // this thread's channel of g, q and k over its TPG tokens, its wave's v
     // values (rows 4 lq + r of the four token blocks, column 16 nt + l16) and
     // beta of its lane's token, each as loaded.
-    const int ch = tid % D, grp = tid / D, chp = kpos(ch);
-    VRaw<GATE_BF16> pg[TPG];
-    VRaw<IN_BF16> pq[TPG], pk[TPG];
+    const int cp = tid % (D / 2), grp = tid / (D / 2), ch = 2 * cp, chp = kpos(ch);   // channels ch, ch + 1
+    PRaw<GATE_BF16> pg[TPG];
+    PRaw<IN_BF16> pq[TPG], pk[TPG];
     VRaw<IN_BF16> pv[16];
     VRaw<GATE_BF16> pb = 0;
     // Unconditional: past the last chunk the ranges are empty and read zeros
@@ -215,7 +229,7 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
 #define GDR_KDA_FETCH_G(cc)                                                                             \
     {                                                                                                   \
         GDR_KDA_RANGE(cc)                                                                               \
-        kda_fetch_gate<D, TPG, IN_BF16, GATE_BF16>(a, t0_, len_, h, hk, ch, grp, pg, pq, pk);          \
+        kda_fetch_gate<D, TPG, IN_BF16, GATE_BF16>(a, t0_, len_, h, hk, cp, grp, pg, pq, pk);          \
         (void)ln_;                                                                                      \
     }
 #define GDR_KDA_FETCH_V(cc)                                                                             \
@@ -237,46 +251,61 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
         const int64_t t0 = bos + C * c;
         const int len = static_cast<int>(eos - t0 < C ? eos - t0 : C);
 
-        // ---- gates: per-channel prefix sums (log2 units), TPG tokens per thread
-        float G2[TPG];
-        {
+        // ---- gates: per-channel prefix sums (log2 units), two channels over TPG
+        // tokens per thread
+        float G2[2][TPG];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
             float run = 0.f;
 #pragma unroll
             for (int i = 0; i < TPG; ++i) {
-                run += static_cast<float>(pg[i]) * kLog2e;
-                G2[i] = run;
+                run += pair_val<GATE_BF16>(pg[i], e) * kLog2e;
+                G2[e][i] = run;
             }
         }
         __syncthreads();   // the previous chunk's reads of LDS are done
-        sTot[grp * D + ch] = G2[TPG - 1];
+        *reinterpret_cast<float2 *>(sTot + grp * D + ch) = float2{G2[0][TPG - 1], G2[1][TPG - 1]};
         if (wave == 0) sB[lane] = static_cast<float>(pb);
         __syncthreads();
         {
-            float offs = 0.f, gm = 0.f, gl = 0.f;
+            float offs[2] = {0.f, 0.f}, gm[2] = {0.f, 0.f}, gl[2] = {0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
-                const float tj = sTot[j * D + ch];
-                offs += j < grp ? tj : 0.f;
-                gm += j < 32 / TPG ? tj : 0.f;
-                gl += tj;
+                const float2 tj = *reinterpret_cast<const float2 *>(sTot + j * D + ch);
+                offs[0] += j < grp ? tj.x : 0.f;
+                offs[1] += j < grp ? tj.y : 0.f;
+                gm[0] += j < 32 / TPG ? tj.x : 0.f;
+                gm[1] += j < 32 / TPG ? tj.y : 0.f;
+                gl[0] += tj.x;
+                gl[1] += tj.y;
             }
             if (grp == 0) {
-                sEm[ch] = fast_exp2(gm);
-                sEL[ch] = fast_exp2(gl);
-                sELm[ch] = fast_exp2(gl - gm);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    sEm[ch + e] = fast_exp2(gm[e]);
+                    sEL[ch + e] = fast_exp2(gl[e]);
+                    sELm[ch + e] = fast_exp2(gl[e] - gm[e]);
+                }
             }
 #pragma unroll
             for (int i = 0; i < TPG; ++i) {
                 const int row = grp * TPG + i;
-                const float x = G2[i] + offs - gm;
-                const float qv = static_cast<float>(static_cast<__bf16>(pq[i]));
-                const float kv = static_cast<float>(static_cast<__bf16>(pk[i]));
-                const float e = fast_exp2(x), ei = fast_exp2(-x);
-                sQt[row * PK + chp] = bf16_bits(qv * e);
-                sKt[row * PK + chp] = bf16_bits(kv * e);
-                const uint16_t kh_ = bf16_bits(kv * ei);
-                sKh[row * PH + ch] = kh_;
-                sKr[row * PK + chp] = kh_;
+                uint32_t wq = 0, wk = 0, wh = 0;   // the two channels' bf16 values, packed
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float x = G2[e][i] + offs[e] - gm[e];
+                    const float qv = static_cast<float>(static_cast<__bf16>(pair_val<IN_BF16>(pq[i], e)));
+                    const float kv = static_cast<float>(static_cast<__bf16>(pair_val<IN_BF16>(pk[i], e)));
+                    const float ex = fast_exp2(x), ei = fast_exp2(-x);
+                    wq |= static_cast<uint32_t>(bf16_bits(qv * ex)) << (16 * e);
+                    wk |= static_cast<uint32_t>(bf16_bits(kv * ex)) << (16 * e);
+                    wh |= static_cast<uint32_t>(bf16_bits(kv * ei)) << (16 * e);
+                }
+                // channels ch, ch + 1 stay adjacent under kpos (ch is even)
+                *reinterpret_cast<uint32_t *>(sQt + row * PK + chp) = wq;
+                *reinterpret_cast<uint32_t *>(sKt + row * PK + chp) = wk;
+                *reinterpret_cast<uint32_t *>(sKh + row * PH + ch) = wh;
+                *reinterpret_cast<uint32_t *>(sKr + row * PK + chp) = wh;
             }
         }
         VRaw<IN_BF16> cv[16];   // this chunk's v values; the registers above take the next chunk
