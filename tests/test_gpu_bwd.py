@@ -92,6 +92,15 @@ def test_bwd_gqa_d64_fp32_gates_no_state():
              "gqa4 d64 fp32 gates, no h0, no dht")
 
 
+def test_bwd_gqa_d64_with_state():
+    """d = 64 with h0 (the first chunk of each segment stages h0, the others the
+    recomputed chunk states) and dht, GQA, ragged segments and ghosts."""
+    import gdr_inputs
+    d = gdr_inputs.random_lengths_case(43, n_real=4, lo=30, hi=260, ghost_slots=2, hk=2, hv=4, d=64)
+    d.update(gdr_inputs.generate_grads(d, seed=44))
+    _compare(_gpu(d), _oracle(d), "gqa d64 with h0 and dht")
+
+
 def test_bwd_fp32_inputs_d128():
     import gdr_inputs
     d = gdr_inputs.random_lengths_case(51, n_real=3, lo=60, hi=200, ghost_slots=1, hk=2, hv=2, d=128,
