@@ -143,14 +143,14 @@ struct KdaLds {
     static constexpr int PD = 20;
     static constexpr int oQt = 0;                  // q~ [64][PK]
     static constexpr int oKt = oQt + C * PK * 2;   // k~
-    static constexpr int oKh = oKt + C * PK * 2;   // k^ [64][PH]
+    static constexpr int oKh = oKt + C * PK * 2;   // k o e^{G_L - G} [64][PH] (the state update's)
     static constexpr int oKr = oKh + C * PH * 2;   // k^ again [64][PK], for its row-fragment reads
     static constexpr int oA = oKr + C * PK * 2;    // diag(b) A~ strictly lower [i][j]
     static constexpr int oP = oA + C * PP * 2;     // scale tril(q~ k^^T) [i][kpos(j)]
     static constexpr int oDi = oP + C * PQ * 2;    // inverses of the diagonal blocks [4][16][PD]
-    static constexpr int oV = oDi + 4 * 16 * PD * 2;   // f32 [D] x3: e^{G_m}, e^{G_L}, e^{G_L - G_m}; [64] b
+    static constexpr int oV = oDi + 4 * 16 * PD * 2;   // f32 [D] x2: e^{G_m}, e^{G_L}; [64] b
     static constexpr int NG = 2 * kKdaThreads / D; // token groups of the gate scan (a thread: 2 channels)
-    static constexpr int oTot = oV + (3 * D + C) * 4;  // f32 [NG][D] group totals of the scan
+    static constexpr int oTot = oV + (2 * D + C) * 4;  // f32 [NG][D] group totals of the scan
     static constexpr int bytes = oTot + NG * D * 4;
 };
 
@@ -171,8 +171,7 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
     uint16_t *sDi = reinterpret_cast<uint16_t *>(lds + Ly::oDi);
     float *sEm = reinterpret_cast<float *>(lds + Ly::oV);
     float *sEL = sEm + D;
-    float *sELm = sEL + D;
-    float *sB = sELm + D;
+    float *sB = sEL + D;
     float *sTot = reinterpret_cast<float *>(lds + Ly::oTot);
 
     const int64_t item = gqa_xcd_item(blockIdx.x, gridDim.x, a.hv, a.hk);   // v-heads of a q/k head share an L2
@@ -284,13 +283,14 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
                 for (int e = 0; e < 2; ++e) {
                     sEm[ch + e] = fast_exp2(gm[e]);
                     sEL[ch + e] = fast_exp2(gl[e]);
-                    sELm[ch + e] = fast_exp2(gl[e] - gm[e]);
                 }
             }
+            // the state update's copy of k carries e^{G_L - G} = e^{G_m - G} e^{G_L - G_m} (<= 1)
+            const float elm[2] = {fast_exp2(gl[0] - gm[0]), fast_exp2(gl[1] - gm[1])};
 #pragma unroll
             for (int i = 0; i < TPG; ++i) {
                 const int row = grp * TPG + i;
-                uint32_t wq = 0, wk = 0, wh = 0;   // the two channels' bf16 values, packed
+                uint32_t wq = 0, wk = 0, wh = 0, wl = 0;   // the two channels' bf16 values, packed
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const float x = G2[e][i] + offs[e] - gm[e];
@@ -300,11 +300,12 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
                     wq |= static_cast<uint32_t>(bf16_bits(qv * ex)) << (16 * e);
                     wk |= static_cast<uint32_t>(bf16_bits(kv * ex)) << (16 * e);
                     wh |= static_cast<uint32_t>(bf16_bits(kv * ei)) << (16 * e);
+                    wl |= static_cast<uint32_t>(bf16_bits(kv * ei * elm[e])) << (16 * e);
                 }
                 // channels ch, ch + 1 stay adjacent under kpos (ch is even)
                 *reinterpret_cast<uint32_t *>(sQt + row * PK + chp) = wq;
                 *reinterpret_cast<uint32_t *>(sKt + row * PK + chp) = wk;
-                *reinterpret_cast<uint32_t *>(sKh + row * PH + ch) = wh;
+                *reinterpret_cast<uint32_t *>(sKh + row * PH + ch) = wl;
                 *reinterpret_cast<uint32_t *>(sKr + row * PK + chp) = wh;
             }
         }
@@ -441,7 +442,7 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
                     else *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.o) + oi) = QS[mt];
                 }
             }
-            // H <- diag(e^{G_L}) H + diag(e^{G_L - G_m}) k^^T U
+            // H <- diag(e^{G_L}) H + (k o e^{G_L - G})^T U
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 f32x4 R = zero4();
@@ -451,7 +452,7 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = 16 * mt + 4 * lq + r;
-                    H[mt][r] = sEL[row] * H[mt][r] + sELm[row] * R[r];
+                    H[mt][r] = sEL[row] * H[mt][r] + R[r];
                 }
             }
         }
