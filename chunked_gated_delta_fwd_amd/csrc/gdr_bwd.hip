@@ -701,6 +701,29 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) accQ[mt] = accK[mt] = zero4();
 
+    // dg: reverse prefix sums of dG within the chunk; dbeta (wave 0, for v-head
+    // hv_, from the row sums the previous v-head's phases left in LDS).  Run
+    // at the next v-head's staging, while its loads are in flight.
+#define GDR_GRAD_DG(hv_, ln_)                                                                  \
+    {                                                                                        \
+        float dG = 0.f, db = 0.f;                                                            \
+        for (int w = 0; w < NTD; ++w) {                                                      \
+            dG += sRG[w * C + (ln_)];                                                        \
+            db += sRB[w * C + (ln_)];                                                        \
+        }                                                                                    \
+        if ((ln_) == 63) {                                                                   \
+            float dot = 0.f, kl = 0.f;                                                       \
+            for (int w = 0; w < 8; ++w) dot += sXd[w];                                       \
+            for (int w = 0; w < NTD; ++w) kl += sXl[w];                                      \
+            dG += sGL[0] * dot + kl;                                                         \
+        }                                                                                    \
+        const float inc = wave_inclusive_scan(dG);                                           \
+        const float dgv = lane63(inc) - inc + dG;                                            \
+        if ((ln_) < p.len) {                                                                 \
+            a.dg[(p.t0 + (ln_)) * a.hv + (hv_)] = dgv;                                       \
+            a.dbeta[(p.t0 + (ln_)) * a.hv + (hv_)] = db;                                     \
+        }                                                                                    \
+    }
     for (int hh = 0; hh < G; ++hh) {
         // lane indices re-derived opaquely in every iteration, so that the
         // compiler does not hoist (and spill) per-lane addresses out of the loop
@@ -742,6 +765,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
             const uint16_t *tg = a.tmat + rh * (C * C);
 #pragma unroll
             for (int j = 0; j < NT8; ++j) rt[j] = *reinterpret_cast<const v4u32 *>(tg + 8 * (tid + j * kBwdThreads));
+            if (wave == 0 && hh > 0) GDR_GRAD_DG(h - 1, lane)   // the previous v-head's, while the loads fly
 #pragma unroll
             for (int j = 0; j < NP; ++j) {
                 const int i = tid + j * kBwdThreads, off = (i / PR) * PK + 8 * (i % PR);
@@ -967,29 +991,11 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
             lastp = lane63(wave_inclusive_scan(lastp));
             if (lane == 0) sXl[wave] = lastp;
         }
-        __syncthreads();
-
-        // dg: reverse prefix sums of dG within the chunk; dbeta
-        if (wave == 0) {
-            float dG = 0.f, db = 0.f;
-            for (int w = 0; w < NTD; ++w) {
-                dG += sRG[w * C + lane];
-                db += sRB[w * C + lane];
-            }
-            if (lane == 63) {
-                float dot = 0.f, kl = 0.f;
-                for (int w = 0; w < 8; ++w) dot += sXd[w];
-                for (int w = 0; w < NTD; ++w) kl += sXl[w];
-                dG += sGL[0] * dot + kl;
-            }
-            const float inc = wave_inclusive_scan(dG);
-            const float dg = lane63(inc) - inc + dG;
-            if (lane < p.len) {
-                a.dg[(p.t0 + lane) * a.hv + h] = dg;
-                a.dbeta[(p.t0 + lane) * a.hv + h] = db;
-            }
-        }
     }
+    // the last v-head's dg and dbeta
+    __syncthreads();
+    if (wave == 0) GDR_GRAD_DG(hk * G + G - 1, tid & 63)
+#undef GDR_GRAD_DG
 
     // dq, dk summed over the v-heads of this q/k head
     const int lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
