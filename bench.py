@@ -6,10 +6,13 @@ U{256..8192}, 16 q/k heads shared by 32 v-heads, head dim 128, bf16 inputs,
 fp32 state, per-segment initial state.  Inputs are resident in HBM before the
 timed region.  Prints ONE JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--settle-calls S] [--workload NAME] [--no-cpu-baseline]
 
-The defaults (100 warm-up calls, 200 timed) let the clock settle: the first
-few milliseconds of back-to-back calls run through a clock transient.
+Before the warm-up steps, --settle-calls (default 200) untimed steps run back
+to back: after idle the GPU's clock first drops and needs about 100 calls of
+sustained work to settle (see profiles/fwd_packed64k_clock_transient.md), and
+the timed steps are meant to show the steady state.  The count is reported in
+the JSON line as settle_calls.
 
 Two helper modes feed the HBM traffic figure of the roofline object:
   python bench.py --copy-probe-mib M     a plain device copy of M MiB (one
@@ -88,6 +91,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="packed64k_gqa_Hk16_Hv32_d128")
+    ap.add_argument("--settle-calls", type=int, default=200,
+                    help="back-to-back steps run before the warm-up steps, untimed, so that the GPU's "
+                         "clock has left the transient that follows a burst of work after idle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="v-heads of every segment the CPU baseline runs (a bounded sample)")
@@ -179,11 +185,18 @@ def main():
         def step():
             gdr.chunk_fwd(q, k, v, g, beta, cu, h0, scale=d["scale"], o=o, ht=ht)
 
-    # events are created before the warm-up: creating them after it would
-    # leave the GPU idle long enough to restart its clock transient
+    # Events are created before the warm-up: creating them after it would
+    # leave the GPU idle long enough to restart its clock transient.  That
+    # transient: after idle the first two or three calls run at full clock,
+    # then the clock drops by up to a third and takes about 100 calls to settle
+    # (per-call times and kernel durations in profiles/); so the warm-up steps
+    # are preceded by settle_calls back-to-back steps, and the timed steps
+    # measure the steady state a continuously running caller sees.
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    for _ in range(args.settle_calls):
+        step()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -221,6 +234,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": tokens, "segments": N, "hk": w.hk, "hv": w.hv,
                    "dk": w.dk, "dv": w.dv, "chunk": CHUNK, "seed": w.seed},
+        "settle_calls": args.settle_calls,
         "roofline": {
             "bound": "mfma",
             "achieved": achieved_tflops,

@@ -27,7 +27,12 @@ STATUS = {0: "GDR_OK", -1: "GDR_EINVAL", -2: "GDR_ESHAPE", -3: "GDR_EDTYPE", -4:
 # every symbol include/gdr.h declares
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_checkpoints", "gdr_chunk_bwd", "gdr_chunk_kda_fwd", "gdr_decode_step", "gdr_plan",
            "gdr_prepare_chunks", "gdr_dispatch_order",
-           "gdr_chunk_local_cumsum", "gdr_last_error", "gdr_version", "gdr_selftest_mfma")
+           "gdr_chunk_local_cumsum", "gdr_last_error", "gdr_version", "gdr_selftest_mfma",
+           "gdr_debug_set", "gdr_device_status", "gdr_free_workspaces")
+
+# gdr_debug_set options and device status bits (include/gdr.h)
+GDR_DEBUG_CHECK_CU, GDR_DEBUG_FAIL_LAUNCHES, GDR_DEBUG_SPIN_LIMIT = 1, 2, 3
+GDR_DEVSTAT_WAIT_TIMEOUT = 1
 
 
 class GdrError(RuntimeError):
@@ -88,6 +93,12 @@ def library(path: Optional[str] = None):
     lib.gdr_version.restype = ctypes.c_int
     lib.gdr_selftest_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.gdr_selftest_mfma.restype = ctypes.c_int
+    lib.gdr_debug_set.argtypes = [ctypes.c_int, ctypes.c_int64]
+    lib.gdr_debug_set.restype = ctypes.c_int
+    lib.gdr_device_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
+    lib.gdr_device_status.restype = ctypes.c_int
+    lib.gdr_free_workspaces.argtypes = []
+    lib.gdr_free_workspaces.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -328,6 +339,27 @@ def selftest_mfma(a_bits, b_bits):
     _check(lib, lib.gdr_selftest_mfma(ctypes.c_void_p(a_bits.data_ptr()), ctypes.c_void_p(b_bits.data_ptr()),
                                       ctypes.c_void_p(c.data_ptr()), ctypes.c_void_p(_stream_handle(a_bits))))
     return c
+
+
+def debug_set(option: int, value: int) -> None:
+    """Process-wide debug / test option (``GDR_DEBUG_*``), see include/gdr.h."""
+    lib = library()
+    _check(lib, lib.gdr_debug_set(int(option), int(value)))
+
+
+def device_status(clear: bool = False) -> int:
+    """Sticky status bits the kernels set on the current device
+    (``GDR_DEVSTAT_*``); synchronises the device."""
+    lib = library()
+    bits = ctypes.c_uint32(0)
+    _check(lib, lib.gdr_device_status(ctypes.byref(bits), 1 if clear else 0))
+    return int(bits.value)
+
+
+def free_workspaces() -> None:
+    """Release the current device's library workspaces."""
+    lib = library()
+    _check(lib, lib.gdr_free_workspaces())
 
 
 def version() -> int:

@@ -10,8 +10,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstdint>
 #include <cstring>
@@ -220,34 +222,74 @@ int check_device() {
 // Library-owned device workspaces, reused across calls.  On this runtime
 // freeing a stream-ordered allocation (hipFreeAsync) blocks the calling
 // thread until the stream has caught up, which serialised the host with the
-// GPU at every call.  Instead each device keeps a few buffers that are never
-// freed while in use: a call takes the next slot of a small ring (or the one
-// large slot, for the backward's multi-GB workspace), makes its stream wait on
-// the GPU for the slot's previous user (an event recorded after that user's
-// last kernel, so reuse is ordered across streams without a host wait), and
-// records the event again after its own kernels.  Slots are indexed by a
-// counter, never by stream or tensor identity; a slot only grows (its old
-// buffer is freed once the last user has finished), and the memory is kept
-// until the process ends.
+// GPU at every call.  Instead each device keeps a ring of buffers that are
+// never freed while in use: a call takes the next slot of the ring (or the
+// one large slot, for the backward's multi-GB workspace), makes its stream
+// wait on the GPU for the slot's previous user (an event recorded after that
+// user's last kernel, so reuse is ordered across streams without a host
+// wait), and records the event again after its own kernels.  Slots are
+// indexed by a counter, never by stream or tensor identity.
+//
+// The whole ring is created by the first call on a device: one allocation
+// holding all slots (at least kRingSlot bytes each) and all events, so later
+// calls allocate nothing.  A request larger than a slot regrows the whole ring
+// once (every slot's previous user is waited for first).  Everything is kept
+// until gdr_free_workspaces or the end of the process.
 int launch_error(hipError_t e, const char *what) {
     return fail(GDR_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
 }
 
 constexpr int kRing = 8;
+constexpr size_t kRingSlot = 1u << 20;
+constexpr int kMaxDevices = 64;
 struct WsSlot {
     std::mutex mu;
-    void *ptr = nullptr;
-    size_t cap = 0;
     hipEvent_t ev = nullptr;
     bool used = false;
 };
 struct WsDevice {
+    // mu guards next, block and cap; a regrow also holds every slot's lock,
+    // so a thread holding one slot's lock reads block and cap unchanged.
     std::mutex mu;
     unsigned next = 0;
+    unsigned char *block = nullptr;   // kRing slots of cap bytes
+    size_t cap = 0;
     WsSlot ring[kRing];
     WsSlot big;
+    void *big_ptr = nullptr;
+    size_t big_cap = 0;
 };
-WsDevice g_ws[64];
+WsDevice g_ws[kMaxDevices];
+
+size_t round_mib(size_t x) { return (x + 0xFFFFF) & ~static_cast<size_t>(0xFFFFF); }
+
+// (Re)creates the ring of device D with slots of at least `bytes`; the caller
+// holds D.mu and no slot lock.
+int ring_grow(WsDevice &D, size_t bytes) {
+    std::unique_lock<std::mutex> locks[kRing];
+    for (int i = 0; i < kRing; ++i) locks[i] = std::unique_lock<std::mutex>(D.ring[i].mu);
+    for (WsSlot &s : D.ring)
+        if (s.used) {
+            (void)hipEventSynchronize(s.ev);
+            s.used = false;
+        }
+    if (D.block) (void)hipFree(D.block);
+    D.block = nullptr;
+    D.cap = 0;
+    const size_t cap = round_mib(bytes > kRingSlot ? bytes : kRingSlot);
+    void *p = nullptr;
+    const hipError_t e = hipMalloc(&p, cap * kRing);
+    if (e != hipSuccess) return fail(GDR_ENOMEM, "workspace ring of %zu bytes: %s", cap * kRing, hipGetErrorString(e));
+    for (WsSlot &s : D.ring)
+        if (!s.ev && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess) {
+            s.ev = nullptr;
+            (void)hipFree(p);
+            return fail(GDR_ENOMEM, "workspace event could not be created");
+        }
+    D.block = static_cast<unsigned char *>(p);
+    D.cap = cap;
+    return GDR_OK;
+}
 
 // Holds one slot from acquire() to release(); the slot's lock is kept in
 // between so that its event is recorded before anyone else can take it.
@@ -255,35 +297,48 @@ class WsLease {
   public:
     int acquire(size_t bytes, bool big, hipStream_t stream, void **out) {
         int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(GDR_EDEVICE, "no current device");
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+            return fail(GDR_EDEVICE, "no current device");
         WsDevice &D = g_ws[dev];
         WsSlot *s;
+        void *ptr;
         if (big) {
             s = &D.big;
+            lock_ = std::unique_lock<std::mutex>(s->mu);
+            if (!s->ev && hipEventCreateWithFlags(&s->ev, hipEventDisableTiming) != hipSuccess) {
+                s->ev = nullptr;
+                return fail(GDR_ENOMEM, "workspace event could not be created");
+            }
+            if (D.big_cap < bytes) {
+                if (D.big_ptr) {
+                    if (s->used) (void)hipEventSynchronize(s->ev);
+                    (void)hipFree(D.big_ptr);
+                    D.big_ptr = nullptr;
+                    D.big_cap = 0;
+                    s->used = false;
+                }
+                const size_t want = round_mib(bytes > 65536 ? bytes : 65536);
+                const hipError_t e = hipMalloc(&D.big_ptr, want);
+                if (e != hipSuccess) {
+                    D.big_ptr = nullptr;
+                    return fail(GDR_ENOMEM, "workspace of %zu bytes: %s", want, hipGetErrorString(e));
+                }
+                D.big_cap = want;
+            }
+            ptr = D.big_ptr;
         } else {
-            std::lock_guard<std::mutex> g(D.mu);
-            s = &D.ring[D.next++ % kRing];
-        }
-        lock_ = std::unique_lock<std::mutex>(s->mu);
-        if (!s->ev && hipEventCreateWithFlags(&s->ev, hipEventDisableTiming) != hipSuccess) {
-            s->ev = nullptr;
-            return fail(GDR_ENOMEM, "workspace event could not be created");
-        }
-        if (s->cap < bytes) {
-            if (s->ptr) {
-                if (s->used) (void)hipEventSynchronize(s->ev);
-                (void)hipFree(s->ptr);
-                s->ptr = nullptr;
-                s->cap = 0;
-                s->used = false;
+            unsigned idx;
+            {
+                std::lock_guard<std::mutex> g(D.mu);
+                if (!D.block || D.cap < bytes) {
+                    const int rc = ring_grow(D, bytes);
+                    if (rc) return rc;
+                }
+                idx = D.next++ % kRing;
             }
-            const size_t want = ((bytes > 65536 ? bytes : 65536) + 0xFFFFF) & ~static_cast<size_t>(0xFFFFF);
-            const hipError_t e = hipMalloc(&s->ptr, want);
-            if (e != hipSuccess) {
-                s->ptr = nullptr;
-                return fail(GDR_ENOMEM, "workspace of %zu bytes: %s", want, hipGetErrorString(e));
-            }
-            s->cap = want;
+            s = &D.ring[idx];
+            lock_ = std::unique_lock<std::mutex>(s->mu);
+            ptr = D.block + static_cast<size_t>(idx) * D.cap;
         }
         if (s->used && hipEventQuery(s->ev) != hipSuccess) {
             const hipError_t e = hipStreamWaitEvent(stream, s->ev, 0);
@@ -291,7 +346,7 @@ class WsLease {
         }
         slot_ = s;
         stream_ = stream;
-        *out = s->ptr;
+        *out = ptr;
         return GDR_OK;
     }
     // After the call's last kernel that touches the workspace (also on error
@@ -311,6 +366,55 @@ class WsLease {
     hipStream_t stream_ = nullptr;
     std::unique_lock<std::mutex> lock_;
 };
+
+// Debug and test options (gdr_debug_set).  The cu_seqlens content check can
+// also be switched on for the whole process with GDR_DEBUG_CHECK_CU=1.
+std::atomic<int> g_check_cu{[] {
+    const char *e = std::getenv("GDR_DEBUG_CHECK_CU");
+    return (e && *e && std::strcmp(e, "0") != 0) ? 1 : 0;
+}()};
+std::atomic<int64_t> g_fail_launches{0};
+std::atomic<int32_t> g_spin_max{gdr::kSpinDefault};
+
+// True when the test hook says this launch is to fail (consumes one).
+bool forced_failure() {
+    int64_t n = g_fail_launches.load(std::memory_order_relaxed);
+    while (n > 0)
+        if (g_fail_launches.compare_exchange_weak(n, n - 1, std::memory_order_relaxed)) return true;
+    return false;
+}
+hipError_t launch_or_fail(hipError_t (*launch)(const gdr::FwdArgs &, hipStream_t), const gdr::FwdArgs &a,
+                          hipStream_t stream) {
+    return forced_failure() ? hipErrorLaunchFailure : launch(a, stream);
+}
+
+// Fills the device status pointer and spin limit every forward-kernel launch needs.
+int fwd_defaults(gdr::FwdArgs &a) {
+    const hipError_t e = gdr::device_status_word(&a.status);
+    if (e != hipSuccess) return fail(GDR_EDEVICE, "device status word: %s", hipGetErrorString(e));
+    a.spin_max = g_spin_max.load(std::memory_order_relaxed);
+    return GDR_OK;
+}
+
+// With the cu_seqlens check on: checks the content on the device, waits for
+// the stream and reports the first violated precondition (GDR_EINVAL).
+// `result` is 16 bytes of device workspace owned by the call.
+int check_cu_content(const int32_t *cu, int64_t n_seq, int64_t total, int32_t *result, hipStream_t stream) {
+    if (!g_check_cu.load(std::memory_order_relaxed)) return GDR_OK;
+    hipError_t e = gdr::launch_check_cu(cu, n_seq, total, result, stream);
+    if (e != hipSuccess) return launch_error(e, "cu_seqlens check kernel");
+    int32_t r[4];
+    if ((e = hipMemcpyAsync(r, result, sizeof(r), hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+        (e = hipStreamSynchronize(stream)) != hipSuccess)
+        return launch_error(e, "cu_seqlens check");
+    switch (r[0]) {
+    case 0: return GDR_OK;
+    case 1: return fail(GDR_EINVAL, "cu_seqlens: cu[0] must be 0, got %d", r[2]);
+    case 2: return fail(GDR_EINVAL, "cu_seqlens: offsets must not decrease (cu[%d] = %d > cu[%d] = %d)", r[1], r[2],
+                        r[1] + 1, r[3]);
+    default: return fail(GDR_EINVAL, "cu_seqlens: cu[N] = cu[%d] = %d must equal the %d tokens", r[1], r[2], r[3]);
+    }
+}
 
 // Machines of the dispatch-order model for a forward launch (kda: the
 // per-channel-gate kernel): work-groups resident at once divided by the
@@ -369,10 +473,15 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
         }
     }
     if ((rc = check_device())) return rc;
+    // workspace: order [N], (checkpoints) chunk offsets [N + 1], the 16-byte check result
+    const size_t ws_bytes = cu_seqlens ? static_cast<size_t>(p.workspace_bytes) +
+                                             (hck ? 4 * static_cast<size_t>(p.n_seq + 1) : 0) + 16
+                                       : 0;
     if (p.n_seq == 0 || p.total_tokens == 0) return ok();
 
     gdr::FwdArgs a;
     std::memset(&a, 0, sizeof(a));
+    if ((rc = fwd_defaults(a))) return rc;
     a.q = q->data;
     a.k = k->data;
     a.v = v->data;
@@ -398,12 +507,12 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
 
     WsLease lease;
     if (cu_seqlens) {
-        // order [N], then (checkpoints only) chunk offsets [N + 1]
-        const size_t bytes = static_cast<size_t>(p.workspace_bytes) + (hck ? 4 * static_cast<size_t>(p.n_seq + 1) : 0);
         void *ws = nullptr;
-        if ((rc = lease.acquire(bytes, false, stream, &ws))) return rc;
+        if ((rc = lease.acquire(ws_bytes, false, stream, &ws))) return rc;
         int32_t *order = static_cast<int32_t *>(ws);
         int32_t *offs = hck ? order + p.n_seq : nullptr;
+        int32_t *check = reinterpret_cast<int32_t *>(static_cast<unsigned char *>(ws) + ws_bytes - 16);
+        if ((rc = check_cu_content(a.cu, p.n_seq, p.total_tokens, check, stream))) return rc;
         const int groups = hck ? 0 : order_groups(a);
         const hipError_t e = groups ? gdr::launch_order(a.cu, p.n_seq, groups, order, stream)
                                     : gdr::launch_prepare(a.cu, p.n_seq, offs, nullptr, 0, order, stream);
@@ -411,7 +520,7 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
         a.order = order;
         a.ck_offs = offs;
     }
-    const hipError_t e = gdr::launch_fwd(a, stream);
+    const hipError_t e = launch_or_fail(gdr::launch_fwd, a, stream);
     const int rr = lease.release();
     if (e != hipSuccess) return launch_error(e, "forward kernel");
     return rr ? rr : ok();
@@ -430,7 +539,7 @@ BwdWorkspace bwd_workspace(int64_t n_seq, int64_t rows, int64_t hv, int64_t d, b
     BwdWorkspace w;
     size_t o = 0;
     w.ints = o;
-    o += al(varlen ? 4 * static_cast<size_t>(2 * n_seq + 1 + 2 * rows) : 0);
+    o += al(varlen ? 4 * static_cast<size_t>(2 * n_seq + 1 + 2 * rows + 4) : 0);
     w.hck = o;
     o += al(ch * dd * dd * 2);
     w.dhe = o;
@@ -501,6 +610,9 @@ int run_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     const bool varlen = cu_seqlens != nullptr;
     const int64_t rows = varlen ? p.nt_max : B * ((T + gdr::kChunk - 1) / gdr::kChunk);
     const BwdWorkspace wl = bwd_workspace(N, rows, Hv, d, varlen);
+    gdr::FwdArgs fa;
+    std::memset(&fa, 0, sizeof(fa));
+    if ((rc = fwd_defaults(fa))) return rc;
     WsLease lease;
     void *ws = nullptr;
     if ((rc = lease.acquire(wl.total, true, stream, &ws))) return rc;
@@ -512,13 +624,12 @@ int run_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
         offs = reinterpret_cast<int32_t *>(base + wl.ints);
         map = offs + N + 1;
         order = map + 2 * rows;
+        if ((rc = check_cu_content(cu, N, p.total_tokens, order + N, stream))) return rc;
         e = gdr::launch_prepare(cu, N, offs, map, rows, order, stream);
     }
     uint16_t *hck = reinterpret_cast<uint16_t *>(base + wl.hck);
     if (e == hipSuccess) {
         // forward recompute: the state after every chunk (no o, no ht)
-        gdr::FwdArgs fa;
-        std::memset(&fa, 0, sizeof(fa));
         fa.q = q->data;
         fa.k = k->data;
         fa.v = v->data;
@@ -580,7 +691,7 @@ int run_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
         ba.in_bf16 = p.in_dtype == GDR_BF16;
         ba.gate_bf16 = p.gate_dtype == GDR_BF16;
         ba.scale = scale;
-        e = gdr::launch_bwd(ba, stream);
+        e = forced_failure() ? hipErrorLaunchFailure : gdr::launch_bwd(ba, stream);
     }
     const int rr = lease.release();
     if (e != hipSuccess) return launch_error(e, "backward kernels");
@@ -631,18 +742,20 @@ int run_kda(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     a.in_bf16 = p.in_dtype == GDR_BF16;
     a.gate_bf16 = p.gate_dtype == GDR_BF16;
     a.scale = scale;
+    if ((rc = fwd_defaults(a))) return rc;
     WsLease lease;
     hipError_t e = hipSuccess;
     if (cu_seqlens) {   // the packed dispatch order where it applies, else longest sequences first
         void *ws = nullptr;
-        if ((rc = lease.acquire(static_cast<size_t>(4 * p.n_seq), false, stream, &ws))) return rc;
+        if ((rc = lease.acquire(static_cast<size_t>(4 * p.n_seq + 16), false, stream, &ws))) return rc;
         int32_t *order = static_cast<int32_t *>(ws);
+        if ((rc = check_cu_content(a.cu, p.n_seq, p.total_tokens, order + p.n_seq, stream))) return rc;
         a.order = order;
         const int groups = order_groups(a, true);
         e = groups ? gdr::launch_order(a.cu, p.n_seq, groups, order, stream)
                    : gdr::launch_prepare(a.cu, p.n_seq, nullptr, nullptr, 0, order, stream);
     }
-    if (e == hipSuccess) e = gdr::launch_kda_fwd(a, stream);
+    if (e == hipSuccess) e = launch_or_fail(gdr::launch_kda_fwd, a, stream);
     const int rr = lease.release();
     if (e != hipSuccess) return launch_error(e, "per-channel-gate forward kernel");
     return rr ? rr : ok();
@@ -751,7 +864,7 @@ int gdr_decode_step(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *
     a.in_bf16 = q->dtype == GDR_BF16;
     a.gate_bf16 = g->dtype == GDR_BF16;
     a.scale = scale;
-    const hipError_t e = gdr::launch_decode(a, stream);
+    const hipError_t e = forced_failure() ? hipErrorLaunchFailure : gdr::launch_decode(a, stream);
     if (e != hipSuccess) return launch_error(e, "decode kernel");
     return ok();
 }
@@ -829,8 +942,10 @@ int gdr_chunk_local_cumsum(const gdr_tensor *g, const gdr_tensor *cu_seqlens, co
     if (B * T == 0 || H == 0) return ok();
     const int gate_bf16 = g->dtype == GDR_BF16;
     if (!cu_seqlens) {
-        const hipError_t e = gdr::launch_cumsum(g->data, gate_bf16, nullptr, nullptr, 0, B, T, B * T,
-                                                static_cast<int32_t>(H), static_cast<float *>(G->data), stream);
+        const hipError_t e = forced_failure() ? hipErrorLaunchFailure
+                                              : gdr::launch_cumsum(g->data, gate_bf16, nullptr, nullptr, 0, B, T, B * T,
+                                                                   static_cast<int32_t>(H),
+                                                                   static_cast<float *>(G->data), stream);
         if (e != hipSuccess) return launch_error(e, "cumsum kernel");
         return ok();
     }
@@ -839,24 +954,92 @@ int gdr_chunk_local_cumsum(const gdr_tensor *g, const gdr_tensor *cu_seqlens, co
     const int64_t nt_max = (T + gdr::kChunk - 1) / gdr::kChunk + N;
     if (nt_max > 0x7FFFFFFFLL) return fail(GDR_ESHAPE, "too many chunks");
     void *ws = nullptr;
-    const size_t bytes = static_cast<size_t>(nt_max) * 8;
+    const size_t bytes = static_cast<size_t>(nt_max) * 8 + 16;
     WsLease lease;
     if ((rc = lease.acquire(bytes, false, stream, &ws))) return rc;
     hipError_t e;
     int32_t *map = static_cast<int32_t *>(ws);
     const int32_t *cu = static_cast<const int32_t *>(cu_seqlens->data);
+    if ((rc = check_cu_content(cu, N, T, map + 2 * nt_max, stream))) return rc;
     e = gdr::launch_prepare(cu, N, nullptr, map, nt_max, nullptr, stream);
     if (e == hipSuccess)
-        e = gdr::launch_cumsum(g->data, gate_bf16, cu, map, nt_max, 1, T, T, static_cast<int32_t>(H),
-                               static_cast<float *>(G->data), stream);
+        e = forced_failure() ? hipErrorLaunchFailure
+                             : gdr::launch_cumsum(g->data, gate_bf16, cu, map, nt_max, 1, T, T, static_cast<int32_t>(H),
+                                                  static_cast<float *>(G->data), stream);
     const int rr = lease.release();
     if (e != hipSuccess) return launch_error(e, "chunk preparation / cumsum kernels");
     return rr ? rr : ok();
 }
 
+int gdr_debug_set(int option, int64_t value) {
+    switch (option) {
+    case GDR_DEBUG_CHECK_CU:
+        g_check_cu.store(value != 0 ? 1 : 0);
+        return ok();
+    case GDR_DEBUG_FAIL_LAUNCHES:
+        if (value < 0) return fail(GDR_EINVAL, "GDR_DEBUG_FAIL_LAUNCHES: count must be >= 0, got %lld", (long long)value);
+        g_fail_launches.store(value);
+        return ok();
+    case GDR_DEBUG_SPIN_LIMIT:
+        if (value > 0x7FFFFFFF) return fail(GDR_EINVAL, "GDR_DEBUG_SPIN_LIMIT: at most 2^31 - 1 polls");
+        g_spin_max.store(value < 0 ? gdr::kSpinDefault : static_cast<int32_t>(value));
+        return ok();
+    default:
+        return fail(GDR_EINVAL, "gdr_debug_set: unknown option %d", option);
+    }
+}
+
+int gdr_device_status(uint32_t *bits, int clear) {
+    if (!bits) return fail(GDR_EINVAL, "gdr_device_status: bits is NULL");
+    int rc;
+    if ((rc = check_device())) return rc;
+    uint32_t *st = nullptr;
+    hipError_t e = gdr::device_status_word(&st);
+    if (e != hipSuccess) return fail(GDR_EDEVICE, "device status word: %s", hipGetErrorString(e));
+    if ((e = hipDeviceSynchronize()) != hipSuccess) return launch_error(e, "gdr_device_status: synchronise");
+    if ((e = hipMemcpy(bits, st, sizeof(uint32_t), hipMemcpyDeviceToHost)) != hipSuccess)
+        return launch_error(e, "gdr_device_status: read");
+    if (clear) {
+        const uint32_t zero = 0;
+        if ((e = hipMemcpy(st, &zero, sizeof(zero), hipMemcpyHostToDevice)) != hipSuccess)
+            return launch_error(e, "gdr_device_status: clear");
+    }
+    return ok();
+}
+
+int gdr_free_workspaces(void) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return fail(GDR_EDEVICE, "no current device");
+    WsDevice &D = g_ws[dev];
+    std::lock_guard<std::mutex> g(D.mu);
+    std::unique_lock<std::mutex> locks[kRing];
+    for (int i = 0; i < kRing; ++i) locks[i] = std::unique_lock<std::mutex>(D.ring[i].mu);
+    std::lock_guard<std::mutex> gb(D.big.mu);
+    for (WsSlot *s : {&D.ring[0], &D.ring[1], &D.ring[2], &D.ring[3], &D.ring[4], &D.ring[5], &D.ring[6],
+                      &D.ring[7], &D.big}) {
+        if (s->used) (void)hipEventSynchronize(s->ev);
+        s->used = false;
+        if (s->ev) (void)hipEventDestroy(s->ev);
+        s->ev = nullptr;
+    }
+    static_assert(kRing == 8, "the list above names every ring slot");
+    hipError_t e = hipSuccess;
+    if (D.block) e = hipFree(D.block);
+    if (D.big_ptr) {
+        const hipError_t e2 = hipFree(D.big_ptr);
+        if (e == hipSuccess) e = e2;
+    }
+    D.block = nullptr;
+    D.cap = 0;
+    D.big_ptr = nullptr;
+    D.big_cap = 0;
+    if (e != hipSuccess) return launch_error(e, "gdr_free_workspaces");
+    return ok();
+}
+
 const char *gdr_last_error(void) { return g_last_error.c_str(); }
 
-int gdr_version(void) { return 10000; }
+int gdr_version(void) { return 10100; }
 
 int gdr_selftest_mfma(const uint16_t *a, const uint16_t *b, float *c, hipStream_t stream) {
     if (!a || !b || !c) return fail(GDR_EINVAL, "selftest: NULL pointer");

@@ -33,7 +33,26 @@ struct FwdArgs {
     uint16_t *hck16;
     const int32_t *ck_offs;
     int64_t ck_rows;
+    // device status word (sticky error bits, see kDevStat*) and the number of
+    // polls after which a hand-off wait between the kernel's two wave roles
+    // gives up (it then sets kDevStatWaitTimeout and poisons ht with NaN)
+    uint32_t *status;
+    int32_t spin_max;
 };
+
+// Bits of the per-device status word the kernels set (sticky until cleared).
+constexpr uint32_t kDevStatWaitTimeout = 1u;   // a hand-off wait gave up: outputs of that call are wrong
+constexpr int32_t kSpinDefault = 1 << 18;      // polls (each s_sleep 1, about 64 cycles) before giving up
+
+// The per-device status word lives in a static device array; its address
+// comes from hipGetSymbolAddress for the current device, once per device.
+hipError_t device_status_word(uint32_t **status);
+
+// Device-side check of the cu_seqlens preconditions (cu[0] == 0, non-decreasing,
+// cu[N] == total): writes result[0..3] = {kind, index, value, value}, kind 0
+// when the content is valid (1: cu[0] != 0, 2: cu[i+1] < cu[i], 3: cu[N] != total).
+hipError_t launch_check_cu(const int32_t *cu, int64_t n_seq, int64_t total, int32_t *result,
+                           hipStream_t stream);
 
 // One recurrent step per (sequence, v-head), already validated on the host.
 struct DecodeArgs {

@@ -43,6 +43,16 @@
 
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
+// Library-owned device memory that needs no allocation: each GPU the library
+// runs on holds its own copy until the process ends.  Host code never passes
+// the name to a kernel; it uses the address hipGetSymbolAddress returns for
+// the current device (gdr::device_status_word).
+//   gdr_dev_status  sticky status bits set by the kernels (kDevStat*)
+static __device__ __align__(256) uint32_t gdr_dev_status[64];
+
 namespace gdr {
 namespace {
 
@@ -85,10 +95,6 @@ namespace {
 // --------------------------------------------------------------------------
 __device__ __forceinline__ int pc(int x) { return (x & ~31) | ((x & 12) << 1) | ((x >> 2) & 4) | (x & 3); }
 
-// polls of a progress counter before a wave gives up waiting (about 2^18 *
-// 64 cycles); reached only if the other role stopped publishing
-constexpr int kSpinMax = 1 << 18;
-
 template <int D>
 struct FwdLds {
     // [64][D] bf16 rows: q and k, three buffers each (chunks c, c+1, c+2).
@@ -109,8 +115,8 @@ struct FwdLds {
     static constexpr int oS = oDd + 2 * 4 * 16 * PDI * 2;
     // f32 vectors of 64: per preparation wave its own G*log2(e) and beta of
     // the chunk it prepares; per buffer e^G and scale*e^G; then e^{G_L} per
-    // buffer and the two progress counters
-    static constexpr int bytes = oS + 12 * C * 4 + 16;
+    // buffer, the two progress counters and the give-up flag
+    static constexpr int bytes = oS + 12 * C * 4 + 32;
 };
 
 
@@ -145,6 +151,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     // cChain += 1 per chain wave per finished chunk
     uint32_t *const cPrep = reinterpret_cast<uint32_t *>(sGL + 2);
     uint32_t *const cChain = cPrep + 1;
+    uint32_t *const cGaveUp = cPrep + 2;   // nonzero once any wave stopped waiting
 
     // per-buffer views
     auto Qb = [&](int b3) { return sQ0 + b3 * C * PK; };   // buffer b3 = chunk % 3
@@ -203,12 +210,23 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     auto peek = [&](const uint32_t *cnt) {
         return __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
+    // A wait that runs out of polls does not hang the work-group: it records
+    // the failure in the device status word (read by gdr_device_status) and in
+    // the work-group's flag, which makes the chain waves write NaN to ht.
     auto wait_for = [&](const uint32_t *cnt, uint32_t target, uint32_t early) {
         if (__builtin_amdgcn_readfirstlane(early) < target) {
+            bool reached = false;
 #pragma unroll 1
-            for (int it = 0; it < kSpinMax; ++it) {
+            for (int it = 0; it < a.spin_max; ++it) {
                 __builtin_amdgcn_s_sleep(1);
-                if (__builtin_amdgcn_readfirstlane(peek(cnt)) >= target) break;
+                if (__builtin_amdgcn_readfirstlane(peek(cnt)) >= target) {
+                    reached = true;
+                    break;
+                }
+            }
+            if (!reached && lane == 0) {
+                __hip_atomic_fetch_or(cGaveUp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_or(a.status, kDevStatWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         lds_wait();
@@ -630,6 +648,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     if (tid == 0) {
         *cPrep = 0u;
         *cChain = 0u;
+        *cGaveUp = 0u;
     }
     __syncthreads();
     if (chain) {
@@ -648,13 +667,16 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             b3 = b3 == 2 ? 0 : b3 + 1;
         }
         if (a.ht) {
+            // a give-up anywhere in the work-group makes this state unusable: say so loudly
+            const bool bad = __builtin_amdgcn_readfirstlane(peek(cGaveUp)) != 0u;
+            const float poison = __builtin_nanf("");
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        a.ht[sbase + dk_of(kb, 4 * lq + r) * D + dv_of(nt, l16)] = hs[kb][nt][r];
+                        a.ht[sbase + dk_of(kb, 4 * lq + r) * D + dv_of(nt, l16)] = bad ? poison : hs[kb][nt][r];
         }
     } else {
         load_qk(0);
@@ -1003,6 +1025,52 @@ __global__ void __launch_bounds__(256) gdr_decode_kernel(DecodeArgs a) {
 }
 
 // --------------------------------------------------------------------------
+// Opt-in check of the cu_seqlens preconditions (one work-group): cu[0] == 0,
+// cu[i] <= cu[i+1], cu[N] == total.  result = {kind, index, value, value}
+// with kind 0 for valid content, 1 for cu[0] != 0, 2 for the first i with
+// cu[i+1] < cu[i], 3 for cu[N] != total.  Reads cu[0..N] only.
+// --------------------------------------------------------------------------
+constexpr int kCheckThreads = 256;
+
+__global__ void __launch_bounds__(kCheckThreads) gdr_check_cu_kernel(const int32_t *cu, int64_t n_seq,
+                                                                       int64_t total, int32_t *result) {
+    __shared__ int64_t s_first[kCheckThreads];
+    const int tid = threadIdx.x;
+    int64_t first = INT64_MAX;
+    for (int64_t i = tid; i < n_seq; i += kCheckThreads) {
+        if (cu[i + 1] < cu[i]) {
+            first = i;   // the smallest such i of this thread's stride
+            break;
+        }
+    }
+    s_first[tid] = first;
+    __syncthreads();
+    for (int w = kCheckThreads / 2; w > 0; w >>= 1) {
+        if (tid < w && s_first[tid + w] < s_first[tid]) s_first[tid] = s_first[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const int64_t f = s_first[0];
+        int32_t r[4] = {0, 0, 0, 0};
+        if (cu[0] != 0) {
+            r[0] = 1;
+            r[2] = cu[0];
+        } else if (f != INT64_MAX) {
+            r[0] = 2;
+            r[1] = static_cast<int32_t>(f);
+            r[2] = cu[f];
+            r[3] = cu[f + 1];
+        } else if (static_cast<int64_t>(cu[n_seq]) != total) {
+            r[0] = 3;
+            r[1] = static_cast<int32_t>(n_seq);
+            r[2] = cu[n_seq];
+            r[3] = static_cast<int32_t>(total);
+        }
+        for (int i = 0; i < 4; ++i) result[i] = r[i];
+    }
+}
+
+// --------------------------------------------------------------------------
 // MFMA lane-layout self test: one wave, both bf16 shapes the kernels use
 // --------------------------------------------------------------------------
 __global__ void __launch_bounds__(64) gdr_selftest_kernel(const uint16_t *a, const uint16_t *b, float *c) {
@@ -1123,6 +1191,35 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_selftest_mfma(const uint16_t *a, const uint16_t *b, float *c, hipStream_t stream) {
     hipLaunchKernelGGL(gdr_selftest_kernel, dim3(1), dim3(64), 0, stream, a, b, c);
     return hipGetLastError();
+}
+
+hipError_t launch_check_cu(const int32_t *cu, int64_t n_seq, int64_t total, int32_t *result, hipStream_t stream) {
+    hipLaunchKernelGGL(gdr_check_cu_kernel, dim3(1), dim3(kCheckThreads), 0, stream, cu, n_seq, total, result);
+    return hipGetLastError();
+}
+
+// Address of the status word for the current device, looked up once per
+// device with that device current and kept for the process.
+hipError_t device_status_word(uint32_t **status) {
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static std::atomic<void *> st_ptr[kMaxDev];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    void *st = st_ptr[dev].load(std::memory_order_acquire);
+    if (!st) {
+        std::lock_guard<std::mutex> lock(mu);
+        st = st_ptr[dev].load(std::memory_order_relaxed);
+        if (!st) {
+            if ((e = hipGetSymbolAddress(&st, HIP_SYMBOL(gdr_dev_status))) != hipSuccess) return e;
+            if (!st) return hipErrorInvalidSymbol;
+            st_ptr[dev].store(st, std::memory_order_release);
+        }
+    }
+    *status = static_cast<uint32_t *>(st);
+    return hipSuccess;
 }
 
 }  // namespace gdr

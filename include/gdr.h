@@ -103,14 +103,23 @@ typedef struct {
  * Results do not depend on scheduling: ghost padding and repeated calls are
  * bitwise reproducible.
  *
- * Uses a small device workspace (4*N bytes) when cu_seqlens is given.  The
- * library keeps, per device, a ring of 8 reusable workspace buffers (and one
- * more for the backward pass), each created on first use and kept until the
- * process ends; it only grows.  A call takes the next buffer of the ring and,
- * if its previous user may still be running, makes `stream` wait for it on
- * the GPU (an event recorded after that user's kernels): no host wait, no
- * allocation or free per call, correct across streams and threads.  The ring
- * is indexed by a counter, not by stream or tensor identity.
+ * Uses a small device workspace (4*N + 16 bytes) when cu_seqlens is given.
+ * The library keeps, per device, a ring of 8 reusable workspace buffers, all
+ * created by the first call on the device in one allocation (1 MiB each at
+ * least) and kept until gdr_free_workspaces or the end of the process; a
+ * later request larger than a buffer regrows the whole ring once.  A call
+ * takes the next buffer of the ring and, if its previous user may still be
+ * running, makes `stream` wait for it on the GPU (an event recorded after
+ * that user's kernels): no host wait, no allocation or free per call once
+ * the ring exists, correct across streams and threads.  The ring is indexed
+ * by a counter, not by stream or tensor identity (the review of
+ * "feat(cake_kda): add paired recurrent training for SM100a and SM103a" asks
+ * for bounded workspace caches that are not keyed by stream handles).
+ *
+ * Failure reporting inside the kernel: the kernel's two wave roles hand
+ * chunks to each other through bounded waits.  A wait that gives up (never
+ * expected; see gdr_debug_set) sets GDR_DEVSTAT_WAIT_TIMEOUT in the device
+ * status word (gdr_device_status) and writes NaN to the affected rows of ht.
  */
 int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
                   const gdr_tensor *g, const gdr_tensor *beta, const gdr_tensor *cu_seqlens,
@@ -135,7 +144,7 @@ int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
  *
  * Everything else, including o and ht, is exactly gdr_chunk_fwd.  Extra
  * traffic: 4 * dk * dv bytes per (chunk, v-head) written.  With cu_seqlens the
- * workspace is 8*N + 4 bytes (order and chunk offsets); sequences start
+ * workspace is 8*N + 20 bytes (order and chunk offsets); sequences start
  * longest first.  Errors as gdr_chunk_fwd, plus GDR_EINVAL (h_chunks NULL),
  * GDR_EDTYPE / GDR_ESHAPE for h_chunks, GDR_EALIAS when it overlaps any other
  * tensor.
@@ -239,8 +248,21 @@ int gdr_decode_step(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *
 
 /*
  * Launch plan of a gdr_chunk_fwd call, computed from shapes only (no device
- * access).  gdr_plan validates exactly like gdr_chunk_fwd and fills `plan`;
- * it is what gdr_chunk_fwd launches.
+ * access, no allocation).  gdr_plan validates exactly like gdr_chunk_fwd and
+ * fills `plan`; it is what gdr_chunk_fwd launches.  It exists so that the
+ * validation of every extent can be tested without a GPU: the review of
+ * "feat(cake_kda): add paired recurrent training for SM100a and SM103a" asks
+ * that every tensor's element count be checked before launch (an undersized
+ * tensor must give an error, not out-of-bounds accesses) and tests its
+ * bindings against a recording stand-in for the device module.
+ *
+ *   q .. ht, scale  as gdr_chunk_fwd (data pointers are only compared for
+ *                   overlaps, never dereferenced)
+ *   plan            out, host memory owned by the caller
+ *
+ * Returns the status gdr_chunk_fwd would return for these descriptors before
+ * touching the device (GDR_OK, GDR_EINVAL, GDR_ESHAPE, GDR_EDTYPE,
+ * GDR_ESTRIDE, GDR_EALIAS); GDR_EINVAL when plan is NULL.
  */
 typedef struct {
     int64_t n_seq;          /* N */
@@ -326,8 +348,64 @@ int gdr_dispatch_order(const gdr_tensor *cu_seqlens, int32_t groups, const gdr_t
 int gdr_chunk_local_cumsum(const gdr_tensor *g, const gdr_tensor *cu_seqlens,
                            const gdr_tensor *G, hipStream_t stream);
 
-/* Text of the last non-OK status returned on the calling thread ("" if none). */
+/*
+ * Text of the last non-OK status returned on the calling thread ("" after an
+ * OK status).  Every check of every entry point has its own message naming
+ * the argument and the values involved (the review of "feat(cake_kda): add
+ * paired recurrent training for SM100a and SM103a" asks for a message on
+ * every check).  The pointer is owned by the library and stays valid until
+ * the calling thread's next call into it.
+ */
 const char *gdr_last_error(void);
+
+/* Options of gdr_debug_set. */
+typedef enum {
+    /* value != 0: before every call that takes cu_seqlens, check its content
+     * on the device (cu[0] == 0, non-decreasing, cu[N] == T), wait for the
+     * stream and return GDR_EINVAL with the first violation (the planned
+     * debug check for the content preconditions, which a call cannot check on
+     * the host without a device read).  Also on with GDR_DEBUG_CHECK_CU=1 in
+     * the environment. */
+    GDR_DEBUG_CHECK_CU = 1,
+    /* value = n >= 0: the next n kernel launches of the library's entry
+     * points fail as if the launch had failed (GDR_ELAUNCH; nothing of the
+     * failed kernel runs, outputs stay untouched).  Test hook. */
+    GDR_DEBUG_FAIL_LAUNCHES = 2,
+    /* value = polls before a hand-off wait inside the forward kernel gives up
+     * (each poll sleeps about 64 cycles); value < 0 restores the default
+     * 2^18.  A small value makes the waits give up early, which exercises
+     * GDR_DEVSTAT_WAIT_TIMEOUT without hanging anything.  Test hook. */
+    GDR_DEBUG_SPIN_LIMIT = 3
+} gdr_debug_option;
+
+/*
+ * gdr_debug_set - process-wide debug and test options (see gdr_debug_option).
+ * Returns GDR_OK, or GDR_EINVAL for an unknown option or a value out of range.
+ * No device access.
+ */
+int gdr_debug_set(int option, int64_t value);
+
+/* Bits of the device status word. */
+#define GDR_DEVSTAT_WAIT_TIMEOUT 1u /* a forward kernel's hand-off wait gave up: its outputs are wrong */
+
+/*
+ * gdr_device_status - the status word of the current device: bits the
+ * kernels set when something went wrong inside them (GDR_DEVSTAT_*), sticky
+ * across calls.  Synchronises the current device first.  clear != 0 resets
+ * the word to zero after reading it.  bits: host memory, written on GDR_OK.
+ * Errors: GDR_EINVAL (bits NULL), GDR_EDEVICE, GDR_ELAUNCH (the
+ * synchronisation or copy failed).
+ */
+int gdr_device_status(uint32_t *bits, int clear);
+
+/*
+ * gdr_free_workspaces - release the current device's workspace ring and the
+ * backward pass's large buffer (waiting for their last users first).  The
+ * next call that needs a workspace creates them again.  Must not run while
+ * another thread is inside a call on the same device.  Returns GDR_OK,
+ * GDR_EDEVICE or GDR_ELAUNCH.
+ */
+int gdr_free_workspaces(void);
 
 /* ABI version: major * 10000 + minor * 100 + patch. */
 int gdr_version(void);

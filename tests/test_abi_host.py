@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == set(gdr.EXPORTS), declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.gdr_version() == 10000
+    assert lib.gdr_version() == 10100
 
 
 def test_exports_match_nm():
@@ -340,3 +340,45 @@ def test_kda_rejections(lib, mutate, status, text):
     mutate(d, Alloc())
     assert _kda_call(lib, d) == status, lib.gdr_last_error()
     assert text in lib.gdr_last_error().decode(), lib.gdr_last_error()
+
+
+# --- debug and test options (no device needed) ----------------------------------
+
+def test_debug_set_options(lib):
+    """Known options accept their values; unknown options and out-of-range
+    values are rejected with a message; nothing touches a device."""
+    assert lib.gdr_debug_set(gdr.GDR_DEBUG_CHECK_CU, 1) == 0
+    assert lib.gdr_debug_set(gdr.GDR_DEBUG_CHECK_CU, 0) == 0
+    assert lib.gdr_debug_set(gdr.GDR_DEBUG_SPIN_LIMIT, 5) == 0
+    assert lib.gdr_debug_set(gdr.GDR_DEBUG_SPIN_LIMIT, -1) == 0      # default again
+    assert lib.gdr_debug_set(gdr.GDR_DEBUG_SPIN_LIMIT, 1 << 31) == -1
+    assert b"2^31" in lib.gdr_last_error()
+    assert lib.gdr_debug_set(gdr.GDR_DEBUG_FAIL_LAUNCHES, -3) == -1
+    assert b"GDR_DEBUG_FAIL_LAUNCHES" in lib.gdr_last_error()
+    assert lib.gdr_debug_set(99, 1) == -1
+    assert b"unknown option 99" in lib.gdr_last_error()
+    assert lib.gdr_debug_set(gdr.GDR_DEBUG_FAIL_LAUNCHES, 0) == 0
+    assert lib.gdr_last_error() == b""
+
+
+def test_validation_precedes_forced_launch_failure(lib):
+    """With launch failures armed, a call whose descriptors are invalid still
+    reports the validation error (nothing is enqueued, so nothing can fail)."""
+    ds = fwd_descs()
+    ds["k"] = describe(ds["k"].t.data, GDR_BF16, [1, 256, 2, 64])
+    try:
+        assert lib.gdr_debug_set(gdr.GDR_DEBUG_FAIL_LAUNCHES, 5) == 0
+        with pytest.raises(gdr.GdrError) as e:
+            gdr.plan(**ds)
+        assert e.value.status == -2 and "k: shape" in e.value.message
+        refs = [None if ds[n] is None else ds[n].ref
+                for n in ("q", "k", "v", "g", "beta", "cu_seqlens", "h0", "o", "ht")]
+        assert lib.gdr_chunk_fwd(*refs, ctypes.c_float(0.1), None) == -2
+        assert b"k: shape" in lib.gdr_last_error()
+    finally:
+        lib.gdr_debug_set(gdr.GDR_DEBUG_FAIL_LAUNCHES, 0)
+
+
+def test_device_status_argument_check(lib):
+    assert lib.gdr_device_status(None, 0) == -1
+    assert b"bits is NULL" in lib.gdr_last_error()

@@ -199,10 +199,11 @@ def test_ghost_segments_bit_identical():
     assert torch.all(hti[ghosts] == -7.25)
 
 
-def test_packed64k_sampled_against_oracle():
-    """The benchmark workload at full size: every output checked for
-    finiteness and determinism; the oracle recomputes sampled (segment, v-head)
-    pairs one by one (longest and shortest segments, first and last heads)."""
+def test_packed64k_full_against_oracle():
+    """The benchmark workload at full size, in the launch configuration the
+    benchmark times (varlen, packed dispatch order): every element of o and of
+    every ht row against one oracle call over all 15 segments x 32 v-heads;
+    a repeated call is bit-identical."""
     import torch
     w = gi.WORKLOADS["packed64k_gqa_Hk16_Hv32_d128"]
     say("packed64k: generating inputs")
@@ -212,23 +213,33 @@ def test_packed64k_sampled_against_oracle():
     o, ht = run_gpu(t, d["scale"])
     o2, ht2 = run_gpu(t, d["scale"])
     assert torch.equal(o, o2) and torch.equal(ht, ht2), "repeated calls differ"
-    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(ht).all())
-    cu = d["cu_seqlens"].astype(np.int64)
-    lens = np.diff(cu)
-    picks = [(int(np.argmax(lens)), 0), (int(np.argmax(lens)), 31), (int(np.argmin(lens)), 1),
-             (int(np.argmin(lens)), 30), (len(lens) - 1, 17), (0, 16)]
-    import oracle
-    for n, h in picks:
-        s, e = int(cu[n]), int(cu[n + 1])
-        hk = h // 2
-        say("packed64k: oracle on segment %d (len %d), v-head %d" % (n, e - s, h))
-        o_ref, ht_ref = oracle.gdr_fwd(d["q"][:, s:e, hk:hk + 1], d["k"][:, s:e, hk:hk + 1],
-                                       d["v"][:, s:e, h:h + 1], d["g"][:, s:e, h:h + 1],
-                                       d["beta"][:, s:e, h:h + 1], None, d["h0"][n:n + 1, h:h + 1],
-                                       scale=d["scale"])
-        og = np64(o[:, s:e, h:h + 1])
-        hg = np64(ht[n:n + 1, h:h + 1])
-        compare(og, hg, o_ref, ht_ref, "packed64k n=%d h=%d" % (n, h))
+    say("packed64k: oracle over every segment and v-head")
+    o_ref, ht_ref = run_oracle(d)
+    compare(o, ht, o_ref, ht_ref, "packed64k full")
+
+
+STRESS = [("fixed_B4_T512_H16_d128", "zero"), ("fixed_B4_T512_H16_d128", "logsigmoid/16"),
+          ("long_T20468_H16_d128", "zero"), ("long_T20468_H16_d128", "logsigmoid/16")]
+
+
+@pytest.mark.parametrize("name,g_mode", STRESS)
+def test_stress_slow_and_no_decay(name, g_mode):
+    """Not graded workloads: the shapes of the fixed-length and the long
+    single-sequence workloads with slowly decaying (g = logsigmoid/16) or no
+    decay (g = 0).  The state then carries information across many chunks (320
+    of them at T = 20468), which tests the inter-chunk hand-off and its
+    precision; these gates also reach the output and state magnitudes of the
+    maintainer's tables (max_ref of o about 0.25-0.31, of the state about
+    2.7-3.0).  Every element of o and ht against the oracle."""
+    w = gi.WORKLOADS[name]
+    d = gi.generate(w, g_mode=g_mode)
+    t = to_device(d)
+    say("stress: %s with g = %s" % (name, g_mode))
+    o, ht = run_gpu(t, d["scale"])
+    o_ref, ht_ref = run_oracle(d)
+    do, dh = compare(o, ht, o_ref, ht_ref, "%s g=%s" % (name, g_mode))
+    say("  max|do| / max_ref(o) = %.2e, max|dht| / max_ref(ht) = %.2e"
+        % (do / max(1e-30, float(np.abs(o_ref).max())), dh / max(1e-30, float(np.abs(ht_ref).max()))))
 
 
 def test_fixed_equals_packed_bitwise():
@@ -357,18 +368,6 @@ def test_empty_calls():
     o, ht = gdr.chunk_fwd(q, q, v, g, g, cu, None, ht=ht)
     torch.cuda.synchronize()
     assert o.shape == (1, 0, 2, 128) and torch.all(ht == 1.5)
-
-
-def test_stress_no_decay():
-    """Not a graded workload: g = 0 keeps the whole history in the state, the
-    real test of the inter-chunk carry and its precision."""
-    w = gi.WORKLOADS["fixed_B4_T512_H16_d128"]
-    d = gi.generate(w, g_mode="zero")
-    t = to_device(d)
-    say("stress: g = 0")
-    o, ht = run_gpu(t, d["scale"])
-    o_ref, ht_ref = run_oracle(d)
-    compare(o, ht, o_ref, ht_ref, "no decay", tol_o=TOL_O, tol_ht=TOL_HT)
 
 
 def test_repeat_determinism():
