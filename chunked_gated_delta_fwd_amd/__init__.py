@@ -28,7 +28,7 @@ STATUS = {0: "GDR_OK", -1: "GDR_EINVAL", -2: "GDR_ESHAPE", -3: "GDR_EDTYPE", -4:
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_checkpoints", "gdr_chunk_bwd", "gdr_chunk_kda_fwd", "gdr_decode_step", "gdr_plan",
            "gdr_prepare_chunks", "gdr_dispatch_order",
            "gdr_chunk_local_cumsum", "gdr_last_error", "gdr_version", "gdr_selftest_mfma",
-           "gdr_debug_set", "gdr_device_status", "gdr_free_workspaces")
+           "gdr_debug_set", "gdr_device_status", "gdr_free_workspaces", "gdr_chunk_fwd_noalloc")
 
 # gdr_debug_set options and device status bits (include/gdr.h)
 GDR_DEBUG_CHECK_CU, GDR_DEBUG_FAIL_LAUNCHES, GDR_DEBUG_SPIN_LIMIT = 1, 2, 3
@@ -71,6 +71,8 @@ def library(path: Optional[str] = None):
     TP = ctypes.POINTER(GdrTensor)
     lib.gdr_chunk_fwd.argtypes = [TP] * 9 + [ctypes.c_float, ctypes.c_void_p]
     lib.gdr_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_noalloc.argtypes = [TP] * 9 + [ctypes.c_float, ctypes.c_void_p]
+    lib.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.gdr_chunk_fwd_checkpoints.argtypes = [TP] * 10 + [ctypes.c_float, ctypes.c_void_p]
     lib.gdr_chunk_fwd_checkpoints.restype = ctypes.c_int
     lib.gdr_chunk_kda_fwd.argtypes = [TP] * 9 + [ctypes.c_float, ctypes.c_void_p]
@@ -178,6 +180,28 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Optional[float]
     ds = [_desc(x) for x in (q, k, v, g, beta, cu_seqlens, h0, o, ht)]
     _check(lib, lib.gdr_chunk_fwd(*[_ref(x) for x in ds], ctypes.c_float(scale),
                                   ctypes.c_void_p(_stream_handle(q))))
+    return o, ht
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Optional[float] = None, o=None, ht=None):
+    """``chunk_fwd`` through the entry point that allocates no device memory
+    (its workspace is a static device array shared by every call on the GPU).
+    ``o`` and ``ht`` are allocated here when not given; pass them preallocated
+    when this runs where allocation is not allowed."""
+    import torch
+    lib = library()
+    B, T, Hk, d = q.shape
+    Hv = v.shape[2]
+    N = (cu_seqlens.shape[0] - 1) if cu_seqlens is not None else B
+    if scale is None:
+        scale = float(d) ** -0.5
+    if o is None:
+        o = torch.empty((B, T, Hv, v.shape[3]), dtype=q.dtype, device=q.device)
+    if ht is None:
+        ht = torch.zeros((N, Hv, d, v.shape[3]), dtype=torch.float32, device=q.device)
+    ds = [_desc(x) for x in (q, k, v, g, beta, cu_seqlens, h0, o, ht)]
+    _check(lib, lib.gdr_chunk_fwd_noalloc(*[_ref(x) for x in ds], ctypes.c_float(scale),
+                                          ctypes.c_void_p(_stream_handle(q))))
     return o, ht
 
 

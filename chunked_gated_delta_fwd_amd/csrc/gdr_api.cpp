@@ -390,7 +390,7 @@ hipError_t launch_or_fail(hipError_t (*launch)(const gdr::FwdArgs &, hipStream_t
 
 // Fills the device status pointer and spin limit every forward-kernel launch needs.
 int fwd_defaults(gdr::FwdArgs &a) {
-    const hipError_t e = gdr::device_status_word(&a.status);
+    const hipError_t e = gdr::device_buffers(&a.status, nullptr);
     if (e != hipSuccess) return fail(GDR_EDEVICE, "device status word: %s", hipGetErrorString(e));
     a.spin_max = g_spin_max.load(std::memory_order_relaxed);
     return GDR_OK;
@@ -449,7 +449,7 @@ int order_groups(const gdr::FwdArgs &a, bool kda = false) {
 int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
             const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
             const gdr_tensor *o, const gdr_tensor *ht, const gdr_tensor *hck, float scale,
-            hipStream_t stream) {
+            hipStream_t stream, bool noalloc = false) {
     gdr_launch_plan p;
     int rc = plan_fwd(q, k, v, g, beta, cu_seqlens, h0, o, ht, scale, &p);
     if (rc) return rc;
@@ -473,10 +473,16 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
         }
     }
     if ((rc = check_device())) return rc;
-    // workspace: order [N], (checkpoints) chunk offsets [N + 1], the 16-byte check result
+    // the no-allocation variant keeps its workspace in the static scratch:
+    // order [N], (checkpoints) chunk offsets [N + 1], the 16-byte check result
     const size_t ws_bytes = cu_seqlens ? static_cast<size_t>(p.workspace_bytes) +
                                              (hck ? 4 * static_cast<size_t>(p.n_seq + 1) : 0) + 16
                                        : 0;
+    if (noalloc && ws_bytes > gdr::kScratchBytes)
+        return fail(GDR_ESHAPE,
+                    "no-allocation entry point: %lld sequences need %zu bytes of workspace, more than its %zu-byte "
+                    "scratch (at most %zu sequences); use gdr_chunk_fwd",
+                    (long long)p.n_seq, ws_bytes, gdr::kScratchBytes, (gdr::kScratchBytes - 16) / 4);
     if (p.n_seq == 0 || p.total_tokens == 0) return ok();
 
     gdr::FwdArgs a;
@@ -508,7 +514,13 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     WsLease lease;
     if (cu_seqlens) {
         void *ws = nullptr;
-        if ((rc = lease.acquire(ws_bytes, false, stream, &ws))) return rc;
+        if (noalloc) {
+            const hipError_t e = gdr::device_buffers(nullptr, &ws);
+            if (e != hipSuccess) return fail(GDR_EDEVICE, "scratch of the no-allocation entry point: %s",
+                                             hipGetErrorString(e));
+        } else if ((rc = lease.acquire(ws_bytes, false, stream, &ws))) {
+            return rc;
+        }
         int32_t *order = static_cast<int32_t *>(ws);
         int32_t *offs = hck ? order + p.n_seq : nullptr;
         int32_t *check = reinterpret_cast<int32_t *>(static_cast<unsigned char *>(ws) + ws_bytes - 16);
@@ -971,6 +983,12 @@ int gdr_chunk_local_cumsum(const gdr_tensor *g, const gdr_tensor *cu_seqlens, co
     return rr ? rr : ok();
 }
 
+int gdr_chunk_fwd_noalloc(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
+                          const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
+                          const gdr_tensor *o, const gdr_tensor *ht, float scale, hipStream_t stream) {
+    return run_fwd(q, k, v, g, beta, cu_seqlens, h0, o, ht, nullptr, scale, stream, true);
+}
+
 int gdr_debug_set(int option, int64_t value) {
     switch (option) {
     case GDR_DEBUG_CHECK_CU:
@@ -994,7 +1012,7 @@ int gdr_device_status(uint32_t *bits, int clear) {
     int rc;
     if ((rc = check_device())) return rc;
     uint32_t *st = nullptr;
-    hipError_t e = gdr::device_status_word(&st);
+    hipError_t e = gdr::device_buffers(&st, nullptr);
     if (e != hipSuccess) return fail(GDR_EDEVICE, "device status word: %s", hipGetErrorString(e));
     if ((e = hipDeviceSynchronize()) != hipSuccess) return launch_error(e, "gdr_device_status: synchronise");
     if ((e = hipMemcpy(bits, st, sizeof(uint32_t), hipMemcpyDeviceToHost)) != hipSuccess)

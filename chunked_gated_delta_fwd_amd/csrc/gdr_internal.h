@@ -44,9 +44,11 @@ struct FwdArgs {
 constexpr uint32_t kDevStatWaitTimeout = 1u;   // a hand-off wait gave up: outputs of that call are wrong
 constexpr int32_t kSpinDefault = 1 << 18;      // polls (each s_sleep 1, about 64 cycles) before giving up
 
-// The per-device status word lives in a static device array; its address
-// comes from hipGetSymbolAddress for the current device, once per device.
-hipError_t device_status_word(uint32_t **status);
+// Per-device memory the library keeps in static device arrays: the status
+// word and the scratch of the no-allocation entry point.  Addresses come from
+// hipGetSymbolAddress for the current device, once per device.
+constexpr size_t kScratchBytes = 64 * 1024;
+hipError_t device_buffers(uint32_t **status, void **scratch);
 
 // Device-side check of the cu_seqlens preconditions (cu[0] == 0, non-decreasing,
 // cu[N] == total): writes result[0..3] = {kind, index, value, value}, kind 0

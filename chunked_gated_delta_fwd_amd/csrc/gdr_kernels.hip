@@ -48,10 +48,12 @@
 
 // Library-owned device memory that needs no allocation: each GPU the library
 // runs on holds its own copy until the process ends.  Host code never passes
-// the name to a kernel; it uses the address hipGetSymbolAddress returns for
-// the current device (gdr::device_status_word).
+// these names to a kernel; it uses the addresses hipGetSymbolAddress returns
+// for the current device (gdr::device_buffers).
 //   gdr_dev_status  sticky status bits set by the kernels (kDevStat*)
+//   scratch         workspace of the no-allocation forward entry point
 static __device__ __align__(256) uint32_t gdr_dev_status[64];
+static __device__ __align__(256) unsigned char scratch[gdr::kScratchBytes];
 
 namespace gdr {
 namespace {
@@ -1198,27 +1200,32 @@ hipError_t launch_check_cu(const int32_t *cu, int64_t n_seq, int64_t total, int3
     return hipGetLastError();
 }
 
-// Address of the status word for the current device, looked up once per
-// device with that device current and kept for the process.
-hipError_t device_status_word(uint32_t **status) {
+// Addresses of the static device arrays for the current device, looked up
+// once per device with that device current and kept for the process.
+hipError_t device_buffers(uint32_t **status, void **scr) {
     constexpr int kMaxDev = 64;
     static std::mutex mu;
-    static std::atomic<void *> st_ptr[kMaxDev];
+    static std::atomic<void *> st_ptr[kMaxDev], sc_ptr[kMaxDev];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
     void *st = st_ptr[dev].load(std::memory_order_acquire);
-    if (!st) {
+    void *sc = sc_ptr[dev].load(std::memory_order_acquire);
+    if (!st || !sc) {
         std::lock_guard<std::mutex> lock(mu);
         st = st_ptr[dev].load(std::memory_order_relaxed);
-        if (!st) {
+        sc = sc_ptr[dev].load(std::memory_order_relaxed);
+        if (!st || !sc) {
             if ((e = hipGetSymbolAddress(&st, HIP_SYMBOL(gdr_dev_status))) != hipSuccess) return e;
-            if (!st) return hipErrorInvalidSymbol;
+            if ((e = hipGetSymbolAddress(&sc, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+            if (!st || !sc) return hipErrorInvalidSymbol;
             st_ptr[dev].store(st, std::memory_order_release);
+            sc_ptr[dev].store(sc, std::memory_order_release);
         }
     }
-    *status = static_cast<uint32_t *>(st);
+    if (status) *status = static_cast<uint32_t *>(st);
+    if (scr) *scr = sc;
     return hipSuccess;
 }
 

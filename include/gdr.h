@@ -127,6 +127,24 @@ int gdr_chunk_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
                   float scale, hipStream_t stream);
 
 /*
+ * gdr_chunk_fwd_noalloc - gdr_chunk_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation.  Same arguments, results and errors as
+ * gdr_chunk_fwd, bit for bit; it never calls hipMalloc, hipFree or any
+ * allocating routine.  Its workspace (the dispatch order, 4*N + 16 bytes with
+ * cu_seqlens) is a static 64 KiB device array that each GPU holds until the
+ * process ends, so with cu_seqlens N is limited to 16380 sequences (larger N:
+ * GDR_ESHAPE, use gdr_chunk_fwd).  Every call on one GPU shares that array
+ * and overwrites it before reading it; calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race on it
+ * and must not be issued.  Calls without cu_seqlens use no workspace.
+ */
+int gdr_chunk_fwd_noalloc(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
+                          const gdr_tensor *g, const gdr_tensor *beta, const gdr_tensor *cu_seqlens,
+                          const gdr_tensor *h0, const gdr_tensor *o, const gdr_tensor *ht,
+                          float scale, hipStream_t stream);
+
+/*
  * gdr_chunk_fwd_checkpoints - gdr_chunk_fwd that also writes the state after
  * every 64-token chunk of every sequence: the per-chunk state checkpoints that
  * the pages' prefill surface keeps for prefix caching (`state_checkpoints`,
