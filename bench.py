@@ -195,6 +195,11 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    # torch creates an event's HIP object at its first record: record each
+    # once now, so that no event is created inside the timed region
+    for s_, e_ in ev:
+        s_.record(stream)
+        e_.record(stream)
     for _ in range(args.settle_calls):
         step()
     for _ in range(args.warmup):
