@@ -198,9 +198,10 @@ int plan_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, cons
     p->has_h0 = h0 ? 1 : 0;
     p->has_ht = ht ? 1 : 0;
     p->grid_fwd = N * Hv;
-    p->block_fwd = gdr::kFwdThreads;
-    p->lds_fwd = gdr::fwd_lds_bytes(static_cast<int>(dk));
-    p->workspace_bytes = cu ? 4 * N : 0;
+    const bool f32 = q->dtype == GDR_F32;   // f32 inputs: the token-serial fp32 kernel
+    p->block_fwd = f32 ? gdr::kFwdF32Threads : gdr::kFwdThreads;
+    p->lds_fwd = f32 ? gdr::fwd_f32_lds_bytes(static_cast<int>(dk)) : gdr::fwd_lds_bytes(static_cast<int>(dk));
+    p->workspace_bytes = cu ? 4 * N + 16 : 0;
     return GDR_OK;
 }
 
@@ -422,6 +423,7 @@ int check_cu_content(const int32_t *cu, int64_t n_seq, int64_t total, int32_t *r
 // must split over the 8 XCDs), or 0 when the packed order does not apply.
 // Occupancy is queried once per device and kernel variant.
 int order_groups(const gdr::FwdArgs &a, bool kda = false) {
+    if (!a.in_bf16) return 0;   // f32 inputs run the token-serial kernel: longest first is enough
     static std::mutex mu;
     static int cache[64][2][2][2][2];   // slots + 1; 0 unknown
     int dev = 0;

@@ -72,11 +72,17 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 // (4 state-chain waves + 4 preparation waves).
 int fwd_lds_bytes(int d);
 constexpr int kFwdThreads = 512;
+// Threads and static LDS bytes of the token-serial fp32 kernel (f32 inputs).
+constexpr int kFwdF32Threads = 256;
+int fwd_f32_lds_bytes(int d);
 constexpr int kChunk = 64;
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 // Per-channel gates: the same arguments with g of shape [tokens, Hv, d].
 hipError_t launch_kda_fwd(const FwdArgs &a, hipStream_t stream);
+// f32 q/k/v/o: the token-serial fp32 kernel (launch_fwd and launch_kda_fwd
+// route f32 inputs here; hck16 must be NULL).  per_channel: g is [tokens, Hv, d].
+hipError_t launch_fwd_f32(const FwdArgs &a, bool per_channel, hipStream_t stream);
 
 hipError_t launch_prepare(const int32_t *cu, int64_t n_seq, int32_t *chunk_offsets,
                           int32_t *chunk_map, int64_t nt_max, int32_t *order,

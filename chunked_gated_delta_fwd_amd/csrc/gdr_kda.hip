@@ -516,6 +516,7 @@ hipError_t kda_slots(int d, int in_bf16, int gate_bf16, int *slots) {
 
 hipError_t launch_kda_fwd(const FwdArgs &a, hipStream_t stream) {
     if (a.n_seq == 0 || a.hv == 0) return hipSuccess;
+    if (!a.in_bf16) return launch_fwd_f32(a, true, stream);   // f32 inputs: fp32 arithmetic
     return a.d == 64 ? launch_kda_d<64>(a, stream) : launch_kda_d<128>(a, stream);
 }
 

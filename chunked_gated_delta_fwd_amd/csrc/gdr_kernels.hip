@@ -715,6 +715,145 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 }
 
 // --------------------------------------------------------------------------
+// f32 inputs: the recurrence in fp32 arithmetic, one token at a time.  With
+// q, k, v and o in f32 the caller asks for f32 precision, which bf16 MFMA
+// operands would not give; speed is secondary for this path.  One
+// work-group of 256 threads per (sequence, v-head); thread (rg, cg) holds
+// rows RPT*rg .. +RPT-1, columns 4cg .. 4cg+3 of the fp32 state H = S^T
+// in registers.  Per token t, with the decay a = e^{g_t} (one per row when
+// PER_CHANNEL: g_t then has one log-decay per key channel):
+//   H <- diag(a) H;  d = b_t (v_t - H^T k_t);  H <- H + k_t d^T;  o_t = scale H^T q_t
+// The two column sums over rows go through LDS (two buffers, so a token
+// takes three barriers); the next token's q, k, v, g and beta are loaded
+// while the current one is processed.  CK = 1 also stores H after the last
+// token of every 64-token chunk (and of the sequence), as the fused kernel's
+// checkpoint mode does.  No exponent folding: any g <= 0 is in range.
+// --------------------------------------------------------------------------
+template <int D>
+struct F32Shape {
+    static constexpr int CG = D / 4;                    // column groups of 4
+    static constexpr int RG = kFwdF32Threads / CG;      // row groups
+    static constexpr int RPT = D / RG;                  // rows per thread
+    static constexpr int lds_bytes = 4 * (2 * RG * D + 3 * D + 1);   // scalar gates
+};
+
+template <int D, bool GATE_BF16, bool PER_CHANNEL, int CK>
+__global__ void __launch_bounds__(kFwdF32Threads) gdr_fwd_f32_kernel(FwdArgs a) {
+    constexpr int CG = F32Shape<D>::CG, RG = F32Shape<D>::RG, RPT = F32Shape<D>::RPT;
+    __shared__ float s_part[2][RG][D];
+    __shared__ float s_k[D], s_q[D], s_v[D], s_a[PER_CHANNEL ? D : 1];
+
+    const int64_t item = blockIdx.x;
+    const int64_t rank = item / a.hv;
+    const int h = static_cast<int>(item % a.hv);
+    const int64_t n = a.order ? static_cast<int64_t>(a.order[rank]) : rank;
+    if (n < 0 || n >= a.n_seq) return;
+    int64_t bos, eos;
+    if (a.cu) {
+        bos = a.cu[n];
+        eos = a.cu[n + 1];
+    } else {
+        bos = n * a.seq_len;
+        eos = bos + a.seq_len;
+    }
+    bos = bos < 0 ? 0 : bos;
+    eos = eos > a.total_tokens ? a.total_tokens : eos;
+    if (eos <= bos) return;   // length-0 segment: reads nothing, writes nothing
+    const int hk = h / (a.hv / a.hk);
+    const int t = threadIdx.x, cg = t % CG, rg = t / CG;
+    const int j0 = 4 * cg, i0 = RPT * rg;
+    const float *qf = static_cast<const float *>(a.q);
+    const float *kf = static_cast<const float *>(a.k);
+    const float *vf = static_cast<const float *>(a.v);
+    float *of = static_cast<float *>(a.o);
+    const int64_t sbase = (n * a.hv + h) * static_cast<int64_t>(D) * D;
+    const int64_t ck_base = CK == 0 ? 0 : a.ck_offs ? static_cast<int64_t>(a.ck_offs[n]) : n * ((a.seq_len + C - 1) / C);
+
+    // h0, ht and the checkpoints need only 4-byte alignment: element accesses
+    auto ld4 = [](const float *p) { return f32x4{p[0], p[1], p[2], p[3]}; };
+    auto st4 = [](float *p, f32x4 x) {
+        p[0] = x[0];
+        p[1] = x[1];
+        p[2] = x[2];
+        p[3] = x[3];
+    };
+    f32x4 H[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) H[i] = a.h0 ? ld4(a.h0 + sbase + (i0 + i) * D + j0) : zero4();
+
+    // token `tok`'s inputs in registers: x = (k, q, v, per-channel log-decay)
+    // element t of the row for t < D; lg, lb the scalar gate and beta
+    float xk = 0.f, xq = 0.f, xv = 0.f, xg = 0.f, lg = 0.f, lb = 0.f;
+    auto fetch = [&](int64_t tok) {
+        if (t < D) {
+            xk = kf[(tok * a.hk + hk) * D + t];
+            xq = qf[(tok * a.hk + hk) * D + t];
+            xv = vf[(tok * a.hv + h) * D + t];
+            if constexpr (PER_CHANNEL) xg = load_scalar<GATE_BF16>(a.g, (tok * a.hv + h) * D + t);
+        }
+        if constexpr (!PER_CHANNEL) lg = load_scalar<GATE_BF16>(a.g, tok * a.hv + h);
+        lb = load_scalar<GATE_BF16>(a.beta, tok * a.hv + h);
+    };
+    fetch(bos);
+    for (int64_t tok = bos; tok < eos; ++tok) {
+        if (t < D) {
+            s_k[t] = xk;
+            s_q[t] = xq;
+            s_v[t] = xv;
+            if constexpr (PER_CHANNEL) s_a[t] = __expf(xg);
+        }
+        const float gate = PER_CHANNEL ? 1.f : __expf(lg);
+        const float beta = lb;
+        __syncthreads();   // (A) the token's inputs are in LDS
+        if (tok + 1 < eos) fetch(tok + 1);
+        // decay, then the prediction H^T k from the decayed state
+        f32x4 part = zero4();
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            H[i] = H[i] * (PER_CHANNEL ? s_a[i0 + i] : gate);
+            part = part + H[i] * s_k[i0 + i];
+        }
+        *reinterpret_cast<f32x4 *>(&s_part[0][rg][j0]) = part;
+        __syncthreads();   // (B)
+        f32x4 p = zero4();
+#pragma unroll
+        for (int r = 0; r < RG; ++r) p = p + *reinterpret_cast<const f32x4 *>(&s_part[0][r][j0]);
+        const f32x4 dlt = (*reinterpret_cast<const f32x4 *>(&s_v[j0]) - p) * beta;
+        f32x4 po = zero4();
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            H[i] = H[i] + dlt * s_k[i0 + i];
+            po = po + H[i] * s_q[i0 + i];
+        }
+        *reinterpret_cast<f32x4 *>(&s_part[1][rg][j0]) = po;
+        // (C): buffer 1 is complete, and every thread is done with buffer 0
+        // and with s_k, s_q, s_v, s_a, which the next token overwrites
+        __syncthreads();
+        if (rg == 0 && of) {
+            f32x4 o = zero4();
+#pragma unroll
+            for (int r = 0; r < RG; ++r) o = o + *reinterpret_cast<const f32x4 *>(&s_part[1][r][j0]);
+            *reinterpret_cast<f32x4 *>(of + (tok * a.hv + h) * D + j0) = o * a.scale;
+        }
+        if constexpr (CK == 1) {
+            const int64_t pos = tok - bos;
+            if (pos % C == C - 1 || tok == eos - 1) {
+                const int64_t row = ck_base + pos / C;
+                if (row < a.ck_rows) {
+                    float *dst = a.hck + (row * a.hv + h) * static_cast<int64_t>(D) * D;
+#pragma unroll
+                    for (int i = 0; i < RPT; ++i) st4(dst + (i0 + i) * D + j0, H[i]);
+                }
+            }
+        }
+    }
+    if (a.ht) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) st4(a.ht + sbase + (i0 + i) * D + j0, H[i]);
+    }
+}
+
+// --------------------------------------------------------------------------
 // Chunk indices from cu_seqlens (one work-group of 1024 threads)
 // --------------------------------------------------------------------------
 constexpr int kPrepThreads = 1024;
@@ -1107,19 +1246,42 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int D, bool GATE_BF16, bool PER_CHANNEL>
+hipError_t launch_fwd_f32_t(const FwdArgs &a, hipStream_t stream) {
+    auto kern = a.hck ? gdr_fwd_f32_kernel<D, GATE_BF16, PER_CHANNEL, 1>
+                      : gdr_fwd_f32_kernel<D, GATE_BF16, PER_CHANNEL, 0>;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(a.n_seq * a.hv)), dim3(kFwdF32Threads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, bool PER_CHANNEL>
+hipError_t launch_fwd_f32_d(const FwdArgs &a, hipStream_t s) {
+    return a.gate_bf16 ? launch_fwd_f32_t<D, true, PER_CHANNEL>(a, s) : launch_fwd_f32_t<D, false, PER_CHANNEL>(a, s);
+}
+
 template <int D>
 hipError_t launch_fwd_d(const FwdArgs &a, hipStream_t s) {
     if (a.in_bf16) return a.gate_bf16 ? launch_fwd_t<D, true, true>(a, s) : launch_fwd_t<D, true, false>(a, s);
+    // f32 inputs: fp32 arithmetic; the backward pass's bf16 state recompute (hck16) keeps the fused kernel
+    if (!a.hck16) return launch_fwd_f32_d<D, false>(a, s);
     return a.gate_bf16 ? launch_fwd_t<D, false, true>(a, s) : launch_fwd_t<D, false, false>(a, s);
 }
 
 }  // namespace
 
 int fwd_lds_bytes(int d) { return d == 64 ? FwdLds<64>::bytes : FwdLds<128>::bytes; }
+int fwd_f32_lds_bytes(int d) { return d == 64 ? F32Shape<64>::lds_bytes : F32Shape<128>::lds_bytes; }
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream) {
     if (a.n_seq == 0 || a.hv == 0) return hipSuccess;
     return a.d == 64 ? launch_fwd_d<64>(a, stream) : launch_fwd_d<128>(a, stream);
+}
+
+hipError_t launch_fwd_f32(const FwdArgs &a, bool per_channel, hipStream_t stream) {
+    if (a.n_seq == 0 || a.hv == 0) return hipSuccess;
+    if (a.in_bf16 || a.hck16) return hipErrorInvalidValue;
+    if (per_channel) return a.d == 64 ? launch_fwd_f32_d<64, true>(a, stream) : launch_fwd_f32_d<128, true>(a, stream);
+    return a.d == 64 ? launch_fwd_f32_d<64, false>(a, stream) : launch_fwd_f32_d<128, false>(a, stream);
 }
 
 hipError_t launch_prepare(const int32_t *cu, int64_t n_seq, int32_t *chunk_offsets, int32_t *chunk_map,

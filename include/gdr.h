@@ -98,10 +98,17 @@ typedef struct {
  * q/k head h / (Hv / Hk); all tensors compact row-major.  o and ht must not
  * overlap any input or each other.  The current device must be gfx950.
  *
- * Numerics: bf16 MFMA operands (f32 inputs are rounded to bf16 when staged),
- * fp32 accumulation, fp32 state; o is rounded once to its dtype (nearest-even).
- * Results do not depend on scheduling: ghost padding and repeated calls are
- * bitwise reproducible.
+ * Numerics: bf16 inputs run the chunked kernel (512 threads per (sequence,
+ * v-head)) with bf16 MFMA operands, fp32 accumulation and an fp32 state; o is
+ * rounded once to bf16 (nearest-even).  f32 inputs ask for f32 precision and
+ * run a token-serial kernel (256 threads per (sequence, v-head)) in fp32
+ * arithmetic throughout: H <- e^g H, d = beta (v - H^T k), H <- H + k d^T,
+ * o = scale H^T q for each token in turn, with no bf16 rounding anywhere
+ * (error against an fp64 evaluation at fp32 rounding level, about 1e-7
+ * relative to the state).  It is latency-bound, one token after another, and
+ * meant for checking and for f32 callers, not for throughput.  Results do not
+ * depend on scheduling: ghost padding and repeated calls are bitwise
+ * reproducible.
  *
  * Uses a small device workspace (4*N + 16 bytes) when cu_seqlens is given.
  * The library keeps, per device, a ring of 8 reusable workspace buffers, all
@@ -160,8 +167,9 @@ int gdr_chunk_fwd_noalloc(const gdr_tensor *q, const gdr_tensor *k, const gdr_te
  *             Rows past NT = off_N are not written; length-0 sequences own
  *             no rows.
  *
- * Everything else, including o and ht, is exactly gdr_chunk_fwd.  Extra
- * traffic: 4 * dk * dv bytes per (chunk, v-head) written.  With cu_seqlens the
+ * Everything else, including o and ht, is exactly gdr_chunk_fwd (f32 inputs:
+ * the fp32 kernel, which stores the same rows).  Extra traffic: 4 * dk * dv
+ * bytes per (chunk, v-head) written.  With cu_seqlens the
  * workspace is 8*N + 20 bytes (order and chunk offsets); sequences start
  * longest first.  Errors as gdr_chunk_fwd, plus GDR_EINVAL (h_chunks NULL),
  * GDR_EDTYPE / GDR_ESHAPE for h_chunks, GDR_EALIAS when it overlaps any other
@@ -229,10 +237,12 @@ int gdr_chunk_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
  *   beta   [B, T, Hv]       same dtype as g
  *
  * Everything else (shapes, varlen and ghosts, h0/ht, GQA, errors) is
- * gdr_chunk_fwd.  Within one 64-token chunk the gates are folded into the
- * operands around the chunk's row 31, so a channel's log-decay summed over
- * half a chunk must stay above about -85 (fp32 exponent range); with
- * cu_seqlens the workspace is 4*N bytes (longest sequences start first).
+ * gdr_chunk_fwd.  bf16 inputs: within one 64-token chunk the gates are
+ * folded into the operands around the chunk's row 31, so a channel's
+ * log-decay summed over half a chunk must stay above about -85 (fp32 exponent
+ * range).  f32 inputs run the token-serial fp32 kernel of gdr_chunk_fwd with
+ * diag(exp(g_t)) in place of exp(g_t): any gate is in range.  With cu_seqlens
+ * the workspace is 4*N + 16 bytes (longest sequences start first).
  */
 int gdr_chunk_kda_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
                       const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
@@ -291,10 +301,10 @@ typedef struct {
     int32_t gate_dtype;     /* gdr_dtype of g/beta */
     int32_t varlen;         /* 1 when cu_seqlens is given */
     int32_t has_h0, has_ht;
-    int64_t grid_fwd;       /* work-groups of the fused kernel: N * Hv */
-    int32_t block_fwd;      /* threads per work-group */
+    int64_t grid_fwd;       /* work-groups of the forward kernel: N * Hv */
+    int32_t block_fwd;      /* threads per work-group: 512 (bf16 inputs), 256 (f32) */
     int32_t lds_fwd;        /* bytes of LDS per work-group */
-    int64_t workspace_bytes;/* device workspace per call */
+    int64_t workspace_bytes;/* device workspace per call: 4*N + 16 with cu_seqlens */
 } gdr_launch_plan;
 
 int gdr_plan(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,

@@ -6,8 +6,17 @@ import sys
 
 import numpy as np
 
-TOL_O = 2e-3    # max |o_gpu - o_oracle|, absolute
+TOL_O = 2e-3    # max |o_gpu - o_oracle|, absolute (bf16 inputs: bf16 MFMA operands)
 TOL_HT = 2e-2   # max |ht_gpu - ht_oracle|, absolute
+# f32 inputs run in fp32 arithmetic throughout: the worst case measured, 20468
+# tokens with no decay, stays within 1.3e-7 (o) and 1.5e-6 (state) of the oracle
+TOL_O_F32 = 2e-6
+TOL_HT_F32 = 2e-5
+
+
+def tols(dtype: str):
+    """(tolerance of o, tolerance of ht) for inputs of `dtype`."""
+    return (TOL_O_F32, TOL_HT_F32) if dtype == "fp32" else (TOL_O, TOL_HT)
 
 
 def say(*a):

@@ -77,13 +77,17 @@ def test_plan_varlen(lib):
     assert p["nt_max"] == (1000 + 63) // 64 + 5
     assert p["grid_fwd"] == 5 * 4 and p["block_fwd"] == 512
     assert 0 < p["lds_fwd"] <= 160 * 1024
-    assert p["workspace_bytes"] == 4 * 5 and p["varlen"] == 1
+    assert p["workspace_bytes"] == 4 * 5 + 16 and p["varlen"] == 1
 
 
 def test_plan_fixed_and_d64(lib):
     p = gdr.plan(**fwd_descs(B=4, T=512, Hk=16, Hv=16, d=64, dt=GDR_F32, gdt=GDR_F32, varlen=False))
     assert p["n_seq"] == 4 and p["workspace_bytes"] == 0 and p["varlen"] == 0 and p["d"] == 64
     assert p["lds_fwd"] < gdr.plan(**fwd_descs())["lds_fwd"]
+    # f32 inputs run the token-serial fp32 kernel: 256 threads, static LDS
+    assert p["block_fwd"] == 256 and p["lds_fwd"] == 4 * (2 * 16 * 64 + 3 * 64 + 1)
+    p = gdr.plan(**fwd_descs(dt=GDR_F32, gdt=GDR_BF16))
+    assert p["block_fwd"] == 256 and p["lds_fwd"] == 4 * (2 * 8 * 128 + 3 * 128 + 1)
 
 
 def test_null_strides_equal_compact_strides(lib):

@@ -1,11 +1,12 @@
 """Per-channel-gate forward (gdr_chunk_kda_fwd) on the GPU against the fp64
 oracle gdr_kda_fwd, element by element, with the forward's tolerances: the
 seeded workloads with one log-gate per key channel, ragged chunks, ghosts, GQA,
-both head sizes, fp32 gates; the full packed workload on sampled heads."""
+both head sizes, fp32 gates; the full packed workload on sampled heads.  f32
+inputs run in fp32 arithmetic and meet the f32 tolerances, at any gate."""
 import numpy as np
 import pytest
 
-from gpu_helpers import TOL_HT, TOL_O, dev, np64, say, to_device
+from gpu_helpers import dev, np64, say, to_device, tols
 
 pytestmark = pytest.mark.gpu
 
@@ -30,14 +31,15 @@ def _ref(d, gk, heads=None):
     return oracle.gdr_kda_fwd(q, k, v, g, beta, d["cu_seqlens"], h0, scale=d["scale"])
 
 
-def _check(o, ht, o_ref, ht_ref, real, what):
+def _check(o, ht, o_ref, ht_ref, real, what, dtype="bf16"):
+    tol_o, tol_ht = tols(dtype)
     e_o = float(np.abs(o - o_ref).max())
     e_h = float(np.abs(ht[real] - ht_ref[real]).max()) if len(real) else 0.0
     say("%s: max|do| %.3e (max_ref %.3f)  max|dht| %.3e (max_ref %.3f)"
         % (what, e_o, float(np.abs(o_ref).max()), e_h, float(np.abs(ht_ref).max())))
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(ht)), what + ": non-finite"
-    assert e_o <= TOL_O, "%s: max|do| %.3e > %.1e" % (what, e_o, TOL_O)
-    assert e_h <= TOL_HT, "%s: max|dht| %.3e > %.1e" % (what, e_h, TOL_HT)
+    assert e_o <= tol_o, "%s: max|do| %.3e > %.1e" % (what, e_o, tol_o)
+    assert e_h <= tol_ht, "%s: max|dht| %.3e > %.1e" % (what, e_h, tol_ht)
 
 
 def _real(d):
@@ -55,7 +57,7 @@ def test_kda_workloads(name):
     gk = gdr_inputs.generate_kda_gates(d, seed=w.seed + 3)
     o, ht = _run(d, gk)
     o_ref, ht_ref = _ref(d, gk)
-    _check(o, ht, o_ref, ht_ref, _real(d), "kda " + name)
+    _check(o, ht, o_ref, ht_ref, _real(d), "kda " + name, w.dtype)
 
 
 def test_kda_gqa_ragged_ghosts():
@@ -85,6 +87,21 @@ def test_kda_fast_decay():
     o, ht = _run(d, gk)
     o_ref, ht_ref = _ref(d, gk)
     _check(o, ht, o_ref, ht_ref, _real(d), "kda fast decay")
+
+
+@pytest.mark.parametrize("gval", [-5.0, -60.0])
+def test_kda_f32_inputs_steep_gates(gval):
+    """f32 inputs with every per-channel log-decay at gval per token (half a
+    chunk sums to -160 or -1920, far outside the bf16 kernel's range): the fp32
+    kernel applies each token's decay directly, so any gate is in range."""
+    import gdr_inputs
+    d = gdr_inputs.random_lengths_case(87, n_real=3, lo=1, hi=200, ghost_slots=1, hk=1, hv=2, d=128,
+                                       dtype="fp32")
+    gk = np.full(d["v"].shape[:3] + (d["q"].shape[3],), gval, dtype=np.float32)
+    say("kda f32 inputs, g = %g per token and channel" % gval)
+    o, ht = _run(d, gk)
+    o_ref, ht_ref = _ref(d, gk)
+    _check(o, ht, o_ref, ht_ref, _real(d), "kda f32 g=%g" % gval, "fp32")
 
 
 def test_kda_packed64k_sampled_heads():
