@@ -63,6 +63,9 @@ def _bind(path: str):
     lib.gdr_oracle_fwd_chunks.argtypes = [dp, dp, dp, dp, dp, lp, i64, i64, i64, i64, i64, i64,
                                           dp, dp, dp, dp, ctypes.c_double, ctypes.c_int]
     lib.gdr_oracle_fwd_chunks.restype = ctypes.c_int
+    lib.gdr_oracle_fwd_checkpoints.argtypes = [dp, dp, dp, dp, dp, lp, i64, i64, i64, i64, i64, i64,
+                                               dp, dp, dp, dp, i64, ctypes.c_double, ctypes.c_int]
+    lib.gdr_oracle_fwd_checkpoints.restype = ctypes.c_int
     lib.gdr_oracle_kda_fwd.argtypes = [dp, dp, dp, dp, dp, lp, i64, i64, i64, i64, i64, i64,
                                        dp, dp, dp, ctypes.c_double, ctypes.c_int]
     lib.gdr_oracle_kda_fwd.restype = ctypes.c_int
@@ -100,7 +103,7 @@ def threads_used(n_threads: int, n_items: int) -> int:
 
 def gdr_fwd(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Optional[float] = None,
             ht_init=None, n_threads: int = 0, _lib_path: Optional[str] = None,
-            chunk_states: bool = False):
+            chunk_states: bool = False, checkpoint_every: int = 64):
     """Per-token fp64 forward of the gated delta rule.
 
     Shapes: q, k ``[B, T, Hk, dk]``; v ``[B, T, Hv, dv]``; g, beta ``[B, T, Hv]``;
@@ -114,6 +117,9 @@ def gdr_fwd(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Optional[float] =
     ``chunk_states=True`` also returns the state after every 64-token chunk of
     every segment, ``[NT, Hv, dk, dv]`` with chunk c of segment n at row
     ``sum(ceil(L_m / 64) for m < n) + c`` (the last chunk may be partial).
+    ``checkpoint_every`` (with ``chunk_states``) replaces 64 by that many
+    tokens: row ``sum(ceil(L_m / n) for m < n) + j`` holds the state after
+    ``min((j + 1) * checkpoint_every, L_n)`` tokens of segment n.
     """
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
     if q.ndim != 4 or k.shape != q.shape or v.ndim != 4 or g.ndim != 3 or beta.shape != g.shape:
@@ -143,13 +149,22 @@ def gdr_fwd(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Optional[float] =
             raise ValueError("oracle: ht_init must be [N, Hv, dk, dv]")
     lib = _load() if _lib_path is None else _bind(_lib_path)
     hck = None
+    every = int(checkpoint_every)
+    if every < 1:
+        raise ValueError("oracle: checkpoint_every must be >= 1")
     if chunk_states:
         lens = np.maximum(np.diff(cu), 0)
-        hck = np.zeros((int(((lens + 63) // 64).sum()), Hv, dk, dv), dtype=np.float64)
-    rc = lib.gdr_oracle_fwd_chunks(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                   _ptr(cu, ctypes.c_int64), n_seq, B * T, Hk, Hv, dk, dv,
-                                   _ptr(h0a), _ptr(o), _ptr(ht), _ptr(hck), float(scale),
-                                   int(n_threads))
+        hck = np.zeros((int(((lens + every - 1) // every).sum()), Hv, dk, dv), dtype=np.float64)
+    if every == 64:
+        rc = lib.gdr_oracle_fwd_chunks(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(cu, ctypes.c_int64), n_seq, B * T, Hk, Hv, dk, dv,
+                                       _ptr(h0a), _ptr(o), _ptr(ht), _ptr(hck), float(scale),
+                                       int(n_threads))
+    else:
+        rc = lib.gdr_oracle_fwd_checkpoints(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                            _ptr(cu, ctypes.c_int64), n_seq, B * T, Hk, Hv, dk, dv,
+                                            _ptr(h0a), _ptr(o), _ptr(ht), _ptr(hck), every,
+                                            float(scale), int(n_threads))
     if rc != 0:
         raise ValueError("oracle: gdr_oracle_fwd returned %d" % rc)
     return (o, ht, hck) if chunk_states else (o, ht)

@@ -38,6 +38,10 @@
  * ceil(L_m / 64) (the prefix caching of the pages' `state_checkpoints`,
  * "feat(cake_kda): add paired recurrent training for SM100a and SM103a", the
  * follow-up's kept prefill surface).  The last chunk's state is ht.
+ * gdr_oracle_fwd_checkpoints does the same for pieces of `every` tokens in
+ * place of 64 (that surface also keeps a `checkpoint_every_n_tokens`
+ * argument, with checkpoint granularity 16): row off[n] + j holds H after
+ * min((j+1) every, L_n) tokens, off[n] = sum over m < n of ceil(L_m / every).
  *
  * Layouts (all row-major, fp64):
  *   q, k  [T, Hk, dk]      v, o  [T, Hv, dv]      g, beta  [T, Hv]
@@ -58,7 +62,8 @@ typedef struct {
     const double *gk;    /* per-channel log-gates [T, Hv, dk], or NULL (scalar g) */
     const int64_t *cu;
     double *o, *ht, *hck;
-    const int64_t *off;  /* chunk offsets per sequence (hck only) */
+    const int64_t *off;  /* checkpoint row offsets per sequence (hck only) */
+    int64_t every;       /* tokens per checkpoint piece (hck only) */
     int64_t n_seq, T, Hk, Hv, dk, dv;
     double scale;
     int64_t *items;      /* work items n * Hv + h, longest segment first */
@@ -109,8 +114,8 @@ static void run_item(const job_t *J, int64_t n, int64_t h, double *H, double *p)
             for (int64_t j = 0; j < dv; ++j) ot[j] += H[i * dv + j] * qt[i];
         for (int64_t j = 0; j < dv; ++j) ot[j] *= J->scale;
 
-        if (J->hck && ((t - bos + 1) % 64 == 0 || t == eos - 1)) {
-            const int64_t c = (t - bos) / 64;
+        if (J->hck && ((t - bos + 1) % J->every == 0 || t == eos - 1)) {
+            const int64_t c = (t - bos) / J->every;
             memcpy(J->hck + (((J->off[n] + c) * Hv + h) * dk) * dv, H, sizeof(double) * dk * dv);
         }
     }
@@ -177,7 +182,7 @@ int gdr_oracle_fwd(const double *q, const double *k, const double *v, const doub
 static int run_fwd_job(const double *q, const double *k, const double *v, const double *g,
                        const double *g_channels, const double *beta, const int64_t *cu, int64_t n_seq,
                        int64_t T, int64_t Hk, int64_t Hv, int64_t dk, int64_t dv, const double *h0,
-                       double *o, double *ht, double *hck, double scale, int n_threads);
+                       double *o, double *ht, double *hck, int64_t every, double scale, int n_threads);
 
 /* The same, also writing the chunk-boundary states into hck (may be NULL). */
 int gdr_oracle_fwd_chunks(const double *q, const double *k, const double *v, const double *g,
@@ -185,8 +190,20 @@ int gdr_oracle_fwd_chunks(const double *q, const double *k, const double *v, con
                           int64_t Hk, int64_t Hv, int64_t dk, int64_t dv, const double *h0,
                           double *o, double *ht, double *hck, double scale, int n_threads)
 {
-    return run_fwd_job(q, k, v, g, NULL, beta, cu, n_seq, T, Hk, Hv, dk, dv, h0, o, ht, hck, scale,
-                       n_threads);
+    return run_fwd_job(q, k, v, g, NULL, beta, cu, n_seq, T, Hk, Hv, dk, dv, h0, o, ht, hck, 64,
+                       scale, n_threads);
+}
+
+/* The same with checkpoints every `every` tokens (every >= 1) in place of 64. */
+int gdr_oracle_fwd_checkpoints(const double *q, const double *k, const double *v, const double *g,
+                               const double *beta, const int64_t *cu, int64_t n_seq, int64_t T,
+                               int64_t Hk, int64_t Hv, int64_t dk, int64_t dv, const double *h0,
+                               double *o, double *ht, double *hck, int64_t every, double scale,
+                               int n_threads)
+{
+    if (every < 1) return -1;
+    return run_fwd_job(q, k, v, g, NULL, beta, cu, n_seq, T, Hk, Hv, dk, dv, h0, o, ht, hck, every,
+                       scale, n_threads);
 }
 
 /*
@@ -208,13 +225,13 @@ int gdr_oracle_kda_fwd(const double *q, const double *k, const double *v, const 
 {
     if (!g_channels) return -1;
     return run_fwd_job(q, k, v, NULL, g_channels, beta, cu, n_seq, T, Hk, Hv, dk, dv, h0, o, ht, NULL,
-                       scale, n_threads);
+                       64, scale, n_threads);
 }
 
 static int run_fwd_job(const double *q, const double *k, const double *v, const double *g,
                        const double *g_channels, const double *beta, const int64_t *cu, int64_t n_seq,
                        int64_t T, int64_t Hk, int64_t Hv, int64_t dk, int64_t dv, const double *h0,
-                       double *o, double *ht, double *hck, double scale, int n_threads)
+                       double *o, double *ht, double *hck, int64_t every, double scale, int n_threads)
 {
     if (n_seq < 0 || T < 0 || Hk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || Hv % Hk != 0)
         return -1;
@@ -230,8 +247,9 @@ static int run_fwd_job(const double *q, const double *k, const double *v, const 
     int64_t *off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_seq + 1));
     if (!off) return -2;
     off[0] = 0;
-    for (int64_t n = 0; n < n_seq; ++n) off[n + 1] = off[n] + (cu[n + 1] - cu[n] + 63) / 64;
+    for (int64_t n = 0; n < n_seq; ++n) off[n + 1] = off[n] + (cu[n + 1] - cu[n] + every - 1) / every;
     J.off = off;
+    J.every = every;
     J.n_seq = n_seq; J.T = T; J.Hk = Hk; J.Hv = Hv; J.dk = dk; J.dv = dv;
     J.scale = scale;
     J.n_items = n_seq * Hv;

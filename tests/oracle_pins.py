@@ -375,6 +375,38 @@ def pin_chunk_states(fwd):
     assert row == hck.shape[0]
 
 
+def pin_checkpoints_every_n(fwd):
+    """Checkpoints every n tokens: row sum_{m<s} ceil(L_m / n) + j of segment s
+    equals, bit for bit, the final state of a run over the first
+    min((j+1) n, L_s) tokens of s; the last row of a segment is ht; n = 64
+    gives the 64-token chunk states exactly; o and ht do not depend on n."""
+    lens = [130, 0, 64, 5, 128, 0, 65]
+    c = small_case(32, lens, Hk=1, Hv=2, dk=4, dv=3)
+    o, ht, h64 = _run(fwd, c, scale=0.5, chunk_states=True)
+    for every in (1, 16, 48, 64, 200):
+        on, htn, hn = _run(fwd, c, scale=0.5, chunk_states=True, checkpoint_every=every)
+        assert np.array_equal(on, o) and np.array_equal(htn, ht), "n=%d: o/ht changed" % every
+        assert hn.shape[0] == sum((L + every - 1) // every for L in lens), (every, hn.shape)
+        if every == 64:
+            assert np.array_equal(hn, h64), "n=64 must equal the chunk states"
+        row = 0
+        for s, L in enumerate(lens):
+            bos = int(c["cu"][s])
+            for j in range((L + every - 1) // every):
+                e = bos + min(every * (j + 1), L)
+                if every == 1 and j % 7 != 3 and j != L - 1:
+                    row += 1   # every token: check a sample of rows and the last
+                    continue
+                pre = {key: c[key][:, bos:e] for key in ("q", "k", "v", "g", "beta")}
+                _, hp = fwd(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], None,
+                            c["h0"][s:s + 1], scale=0.5)
+                assert np.array_equal(hn[row], hp[0]), "n=%d segment %d row %d" % (every, s, j)
+                row += 1
+            if L:
+                assert np.array_equal(hn[row - 1], ht[s]), "n=%d segment %d: last row vs ht" % (every, s)
+        assert row == hn.shape[0]
+
+
 def pin_linearity(fwd):
     """For fixed q, k, g, beta the outputs are jointly linear in (v, h0):
     scaling both by 4 scales o and ht by 4 exactly (a power of two)."""
@@ -456,5 +488,6 @@ def pin_page_magnitudes(fwd, T=512):
 ALL_PINS = [pin_exact_rational, pin_literal_matrix_form, pin_chunked_form,
             pin_identity_when_beta_and_g_zero, pin_pure_decay, pin_single_token,
             pin_orthonormal_overwrite, pin_scalar_iir, pin_segment_independence,
-            pin_ghost_segments, pin_split_resume, pin_chunk_states, pin_linearity, pin_causality,
+            pin_ghost_segments, pin_split_resume, pin_chunk_states, pin_checkpoints_every_n,
+            pin_linearity, pin_causality,
             pin_contraction_bound, pin_page_magnitudes]

@@ -31,7 +31,9 @@ MUTANTS = [
      " if (0)"),
     ("decay_after_update", "for (int64_t i = 0; i < dk * dv; ++i) H[i] *= a;\n",
      "H[0] *= 1.0;\n"),
-    ("chunk_state_early", "(t - bos + 1) % 64 == 0", "(t - bos) % 64 == 0"),
+    ("chunk_state_early", "(t - bos + 1) % J->every == 0", "(t - bos) % J->every == 0"),
+    ("checkpoint_piece_64", "const int64_t c = (t - bos) / J->every;", "const int64_t c = (t - bos) / 64;"),
+    ("checkpoint_offsets_64", "(cu[n + 1] - cu[n] + every - 1) / every", "(cu[n + 1] - cu[n] + 63) / 64"),
     ("chunk_state_row", "((J->off[n] + c) * Hv + h)", "((J->off[n] + c) * Hv + (Hv - 1 - h))"),
 ]
 
