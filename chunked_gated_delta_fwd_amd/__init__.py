@@ -28,7 +28,8 @@ STATUS = {0: "GDR_OK", -1: "GDR_EINVAL", -2: "GDR_ESHAPE", -3: "GDR_EDTYPE", -4:
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_checkpoints", "gdr_chunk_bwd", "gdr_chunk_kda_fwd", "gdr_decode_step", "gdr_plan",
            "gdr_prepare_chunks", "gdr_dispatch_order",
            "gdr_chunk_local_cumsum", "gdr_last_error", "gdr_version", "gdr_selftest_mfma",
-           "gdr_debug_set", "gdr_device_status", "gdr_free_workspaces", "gdr_chunk_fwd_noalloc")
+           "gdr_debug_set", "gdr_device_status", "gdr_free_workspaces", "gdr_chunk_fwd_noalloc",
+           "gdr_chunk_fwd_checkpoints_n")
 
 # gdr_debug_set options and device status bits (include/gdr.h)
 GDR_DEBUG_CHECK_CU, GDR_DEBUG_FAIL_LAUNCHES, GDR_DEBUG_SPIN_LIMIT = 1, 2, 3
@@ -75,6 +76,8 @@ def library(path: Optional[str] = None):
     lib.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.gdr_chunk_fwd_checkpoints.argtypes = [TP] * 10 + [ctypes.c_float, ctypes.c_void_p]
     lib.gdr_chunk_fwd_checkpoints.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_checkpoints_n.argtypes = [TP] * 10 + [ctypes.c_int64, ctypes.c_float, ctypes.c_void_p]
+    lib.gdr_chunk_fwd_checkpoints_n.restype = ctypes.c_int
     lib.gdr_chunk_kda_fwd.argtypes = [TP] * 9 + [ctypes.c_float, ctypes.c_void_p]
     lib.gdr_chunk_kda_fwd.restype = ctypes.c_int
     lib.gdr_chunk_bwd.argtypes = [TP] * 15 + [ctypes.c_float, ctypes.c_void_p]
@@ -206,11 +209,13 @@ def chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Optiona
 
 
 def chunk_fwd_checkpoints(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Optional[float] = None,
-                          o=None, ht=None, h_chunks=None):
+                          o=None, ht=None, h_chunks=None, every_n: int = 64):
     """``chunk_fwd`` that also returns the state after every 64-token chunk:
     ``(o, ht, h_chunks)`` with h_chunks fp32 ``[R, Hv, dk, dv]``, R = ceil(T/64) + N
     with ``cu_seqlens`` (rows past the true chunk count are not written) or
-    B * ceil(T/64); chunk c of sequence n at row sum(ceil(L_m/64), m < n) + c."""
+    B * ceil(T/64); chunk c of sequence n at row sum(ceil(L_m/64), m < n) + c.
+    ``every_n`` (a multiple of 16) replaces 64 by that many tokens
+    (gdr_chunk_fwd_checkpoints_n; 64 calls gdr_chunk_fwd_checkpoints)."""
     import torch
     lib = library()
     B, T, Hk, d = q.shape
@@ -218,7 +223,8 @@ def chunk_fwd_checkpoints(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Opt
     N = (cu_seqlens.shape[0] - 1) if cu_seqlens is not None else B
     if scale is None:
         scale = float(d) ** -0.5
-    rows = ((T + 63) // 64 + N) if cu_seqlens is not None else B * ((T + 63) // 64)
+    n = int(every_n)
+    rows = ((T + n - 1) // n + N) if cu_seqlens is not None else B * ((T + n - 1) // n)
     if o is None:
         o = torch.empty((B, T, Hv, v.shape[3]), dtype=q.dtype, device=q.device)
     if ht is None:
@@ -226,8 +232,12 @@ def chunk_fwd_checkpoints(q, k, v, g, beta, cu_seqlens=None, h0=None, scale: Opt
     if h_chunks is None:
         h_chunks = torch.zeros((rows, Hv, d, v.shape[3]), dtype=torch.float32, device=q.device)
     ds = [_desc(x) for x in (q, k, v, g, beta, cu_seqlens, h0, o, ht, h_chunks)]
-    _check(lib, lib.gdr_chunk_fwd_checkpoints(*[_ref(x) for x in ds], ctypes.c_float(scale),
-                                              ctypes.c_void_p(_stream_handle(q))))
+    if n == 64:
+        _check(lib, lib.gdr_chunk_fwd_checkpoints(*[_ref(x) for x in ds], ctypes.c_float(scale),
+                                                  ctypes.c_void_p(_stream_handle(q))))
+    else:
+        _check(lib, lib.gdr_chunk_fwd_checkpoints_n(*[_ref(x) for x in ds], ctypes.c_int64(n),
+                                                    ctypes.c_float(scale), ctypes.c_void_p(_stream_handle(q))))
     return o, ht, h_chunks
 
 

@@ -446,25 +446,27 @@ int order_groups(const gdr::FwdArgs &a, bool kda = false) {
 }
 
 
-// The forward launch shared by gdr_chunk_fwd and gdr_chunk_fwd_checkpoints
-// (hck: chunk-boundary states, or NULL).
+// The forward launch shared by gdr_chunk_fwd, gdr_chunk_fwd_checkpoints(_n)
+// and gdr_chunk_fwd_noalloc (hck: checkpoint states every `every` tokens, or NULL).
 int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
             const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
             const gdr_tensor *o, const gdr_tensor *ht, const gdr_tensor *hck, float scale,
-            hipStream_t stream, bool noalloc = false) {
+            hipStream_t stream, bool noalloc = false, int64_t every = gdr::kChunk) {
     gdr_launch_plan p;
     int rc = plan_fwd(q, k, v, g, beta, cu_seqlens, h0, o, ht, scale, &p);
     if (rc) return rc;
     int64_t rows = 0;
     if (hck) {
+        if (every < 16 || every % 16 != 0 || every > (int64_t{1} << 30))
+            return fail(GDR_EINVAL, "every_n: %lld must be a positive multiple of 16 (at most 2^30)", (long long)every);
         int64_t nck;
         if ((rc = check_tensor(hck, "h_chunks", 4, &nck, 4))) return rc;
         if (hck->dtype != GDR_F32) return fail(GDR_EDTYPE, "h_chunks: dtype must be f32");
         const int64_t T = q->shape[1];
-        rows = cu_seqlens ? p.nt_max : q->shape[0] * ((T + gdr::kChunk - 1) / gdr::kChunk);
+        rows = cu_seqlens ? (p.total_tokens + every - 1) / every + p.n_seq : q->shape[0] * ((T + every - 1) / every);
         if (!shape_is(hck, {rows, p.hv, p.d, p.d}))
-            return fail(GDR_ESHAPE, "h_chunks: shape %s must be [%lld, Hv, dk, dv] = [%lld, %d, %d, %d]",
-                        shape_str(hck).c_str(), (long long)rows, (long long)rows, p.hv, p.d, p.d);
+            return fail(GDR_ESHAPE, "h_chunks: shape %s must be [%lld, Hv, dk, dv] = [%lld, %d, %d, %d] for pieces of %lld tokens",
+                        shape_str(hck).c_str(), (long long)rows, (long long)rows, p.hv, p.d, p.d, (long long)every);
         const Span sck = span_of(hck, nck);
         const gdr_tensor *others[] = {q, k, v, g, beta, cu_seqlens, h0, o, ht};
         for (const gdr_tensor *t : others) {
@@ -477,7 +479,7 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     if ((rc = check_device())) return rc;
     // the no-allocation variant keeps its workspace in the static scratch:
     // order [N], (checkpoints) chunk offsets [N + 1], the 16-byte check result
-    const size_t ws_bytes = cu_seqlens ? static_cast<size_t>(p.workspace_bytes) +
+    const size_t ws_bytes = cu_seqlens ? 4 * static_cast<size_t>(p.n_seq) +
                                              (hck ? 4 * static_cast<size_t>(p.n_seq + 1) : 0) + 16
                                        : 0;
     if (noalloc && ws_bytes > gdr::kScratchBytes)
@@ -512,6 +514,7 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     a.hck = hck ? static_cast<float *>(hck->data) : nullptr;
     a.ck_offs = nullptr;
     a.ck_rows = rows;
+    a.ck_every = static_cast<int32_t>(every);
 
     WsLease lease;
     if (cu_seqlens) {
@@ -529,7 +532,8 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
         if ((rc = check_cu_content(a.cu, p.n_seq, p.total_tokens, check, stream))) return rc;
         const int groups = hck ? 0 : order_groups(a);
         const hipError_t e = groups ? gdr::launch_order(a.cu, p.n_seq, groups, order, stream)
-                                    : gdr::launch_prepare(a.cu, p.n_seq, offs, nullptr, 0, order, stream);
+                                    : gdr::launch_prepare(a.cu, p.n_seq, offs, nullptr, 0, order, stream,
+                                                          static_cast<int32_t>(every));
         if (e != hipSuccess) return launch_error(e, "chunk preparation kernel");
         a.order = order;
         a.ck_offs = offs;
@@ -801,6 +805,14 @@ int gdr_chunk_fwd_checkpoints(const gdr_tensor *q, const gdr_tensor *k, const gd
     return run_fwd(q, k, v, g, beta, cu_seqlens, h0, o, ht, h_chunks, scale, stream);
 }
 
+int gdr_chunk_fwd_checkpoints_n(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
+                                const gdr_tensor *g, const gdr_tensor *beta, const gdr_tensor *cu_seqlens,
+                                const gdr_tensor *h0, const gdr_tensor *o, const gdr_tensor *ht,
+                                const gdr_tensor *h_ckpt, int64_t every_n, float scale, hipStream_t stream) {
+    if (!h_ckpt) return fail(GDR_EINVAL, "h_ckpt: descriptor is NULL");
+    return run_fwd(q, k, v, g, beta, cu_seqlens, h0, o, ht, h_ckpt, scale, stream, false, every_n);
+}
+
 int gdr_chunk_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
                   const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
                   const gdr_tensor *dout, const gdr_tensor *dht, const gdr_tensor *dq, const gdr_tensor *dk,
@@ -1059,7 +1071,7 @@ int gdr_free_workspaces(void) {
 
 const char *gdr_last_error(void) { return g_last_error.c_str(); }
 
-int gdr_version(void) { return 10100; }
+int gdr_version(void) { return 10200; }
 
 int gdr_selftest_mfma(const uint16_t *a, const uint16_t *b, float *c, hipStream_t stream) {
     if (!a || !b || !c) return fail(GDR_EINVAL, "selftest: NULL pointer");

@@ -33,6 +33,11 @@ struct FwdArgs {
     uint16_t *hck16;
     const int32_t *ck_offs;
     int64_t ck_rows;
+    // fp32 checkpoints (hck) every ck_every tokens (a multiple of 16; 64 gives
+    // the chunk-boundary states above): row ck_offs[n] + j (ck_offs then holds
+    // prefix sums of ceil(L / ck_every); fixed-length rows: n * ceil(seq_len /
+    // ck_every) + j) receives the state after min((j+1) ck_every, L) tokens
+    int32_t ck_every;
     // device status word (sticky error bits, see kDevStat*) and the number of
     // polls after which a hand-off wait between the kernel's two wave roles
     // gives up (it then sets kDevStatWaitTimeout and poisons ht with NaN)
@@ -84,9 +89,11 @@ hipError_t launch_kda_fwd(const FwdArgs &a, hipStream_t stream);
 // route f32 inputs here; hck16 must be NULL).  per_channel: g is [tokens, Hv, d].
 hipError_t launch_fwd_f32(const FwdArgs &a, bool per_channel, hipStream_t stream);
 
+// chunk_offsets: prefix sums of ceil(L / unit) (unit = kChunk for chunk
+// indices; the chunk map requires unit = kChunk).
 hipError_t launch_prepare(const int32_t *cu, int64_t n_seq, int32_t *chunk_offsets,
                           int32_t *chunk_map, int64_t nt_max, int32_t *order,
-                          hipStream_t stream);
+                          hipStream_t stream, int32_t unit = kChunk);
 
 // Dispatch order for few sequences (1 <= n_seq <= 64) on `groups` (<= 16)
 // machines of CUs; see the kernel for the model.

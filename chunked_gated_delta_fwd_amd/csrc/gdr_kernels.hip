@@ -117,8 +117,10 @@ struct FwdLds {
     static constexpr int oS = oDd + 2 * 4 * 16 * PDI * 2;
     // f32 vectors of 64: per preparation wave its own G*log2(e) and beta of
     // the chunk it prepares; per buffer e^G and scale*e^G; then e^{G_L} per
-    // buffer, the two progress counters and the give-up flag
-    static constexpr int bytes = oS + 12 * C * 4 + 32;
+    // buffer, the two progress counters and the give-up flag; then per buffer
+    // G*log2(e) for the chain (checkpoints inside a chunk only)
+    static constexpr int oG2 = oS + 12 * C * 4 + 32;
+    static constexpr int bytes = oG2 + 2 * C * 4;
 };
 
 
@@ -164,6 +166,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     auto Ddb = [&](int par) { return sDd0 + par * 4 * 16 * PDI; };   // diag(e^{G_L - G_a}) D_a diag(b_a)
     auto vEG = [&](int par) { return sVec0 + par * 2 * C; };         // e^G
     auto vGam = [&](int par) { return sVec0 + par * 2 * C + C; };    // scale e^G
+    auto vG2 = [&](int par) { return reinterpret_cast<float *>(smem + Ly::oG2) + par * C; };   // G*log2(e)
 
     // ---- work item: (sequence n, v-head h), longest sequences first.
     // Work-groups are dispatched round-robin over the 8 XCDs (each with its
@@ -197,7 +200,11 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     const int lq = lane >> 4;
     const int colw = role * DW;         // the chain wave's 16*NTW state columns
     const int64_t nch = (eos - bos + C - 1) / C;
-    const int64_t ck_base = CK == 0 ? 0 : a.ck_offs ? static_cast<int64_t>(a.ck_offs[n]) : n * ((a.seq_len + C - 1) / C);
+    // checkpoint rows: every ck_unit tokens (CK = 1), at chunk ends (CK = 2)
+    const int64_t ck_unit = CK == 1 && a.ck_every > 0 ? static_cast<int64_t>(a.ck_every) : C;
+    const int64_t ck_base = CK == 0 ? 0
+                          : a.ck_offs ? static_cast<int64_t>(a.ck_offs[n])
+                                      : n * ((a.seq_len + ck_unit - 1) / ck_unit);
 
     // Cross-role hand-off through the LDS counters instead of work-group
     // barriers: a wave publishes a step after its own LDS accesses are
@@ -339,6 +346,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             vEG(par)[lane] = gam;
             vGam(par)[lane] = gam * a.scale;
             if (lane == 0) sGL[par] = fast_exp2(GL2);
+            if constexpr (CK == 1) vG2(par)[lane] = G2;
         }
         lds_wait();   // this wave's copies are written before its strips read them
     };
@@ -584,16 +592,68 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             }
         }
 
-        // H <- e^{G_L} H + K^T Vt, Vt = diag(e^{G_L - G}) Vnew; the K^T fragments are
-        // transposing reads of the k rows: lane (l16, lq) of tile kb gets
-        // k[32p' + 4lq + r][dk_of(kb, l16)] (and tokens +16 for slots 4-7)
+        // lane part of the offset of a checkpoint store (plain [dk][dv] fp32);
+        // tile (kb, nt) element r adds ck_cst(kb, nt, r) as the scalar offset
+        const uint32_t ck_lane_off = (dk_of(0, 4 * lq) * D + dv_of(0, l16)) * 4;
+        auto ck_cst = [&](int kb, int nt, int r) { return static_cast<uint32_t>(((dk_of(kb, r) - dk_of(0, 0)) * D + 4 * nt) * 4); };
+        // the K^T fragments of the state update: transposing reads of the k
+        // rows, lane (l16, lq) of tile kb gets k[32p' + 4lq + r][dk_of(kb, l16)]
+        // (and tokens +16 for slots 4-7)
+        auto kt_frag = [&](int kb, int pair) {
+            const uint16_t *pkt = sK + (4 * lq + (l16 >> 2)) * PK + 32 * (kb >> 1) + 4 * (kb & 1) + 8 * (l16 & 3) + 32 * pair * PK;
+            return cat(ld4_tr(pkt), ld4_tr(pkt + 16 * PK));
+        };
+        if constexpr (CK == 1) {
+            // checkpoints inside the chunk, after P = 16 jb of its tokens, from
+            // the state at its start (hs, not yet updated):
+            //   H_P = e^{G_P} H + K_{<P}^T diag(e^{G_P - G}) Vnew_{<P}
+            // (G at the chunk's token P-1; every factor is at most 1)
+            const int64_t len_seq = eos - bos;
+            const float *vg2 = vG2(par);
+#pragma unroll 1
+            for (int jb = 1; jb < 4; ++jb) {
+                const int64_t P = c * C + 16 * jb;
+                if (P >= len_seq || P % ck_unit != 0) continue;
+                const int64_t row = ck_base + P / ck_unit - 1;
+                if (row >= a.ck_rows) continue;
+                const float gp = vg2[16 * jb - 1];
+                bf16x4 Vm[3][NTW];
+#pragma unroll
+                for (int blk = 0; blk < 3; ++blk) {
+                    const f32x4 gt = *reinterpret_cast<const f32x4 *>(vg2 + 16 * blk + 4 * lq);
+                    f32x4 f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) f[r] = blk < jb ? fast_exp2(gp - gt[r]) : 0.f;
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) Vm[blk][nt] = cvt4(up4(Xb[blk][nt]) * f);
+                }
+                const float eg = fast_exp2(gp);
+                const bf16x4 z4 = cvt4(zero4());
+                const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(a.hck + (row * a.hv + h) * D * D, D * D * 4);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const bf16x8 a01 = kt_frag(kb, 0);
+                    const bf16x8 a23 = kt_frag(kb, 1);
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) {
+                        f32x4 s = hs[kb][nt] * eg;
+                        s = mfma32(a01, cat(Vm[0][nt], Vm[1][nt]), s);
+                        s = mfma32(a23, cat(Vm[2][nt], z4), s);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s[r]), rd, ck_lane_off, ck_cst(kb, nt, r), 0);
+                    }
+                }
+            }
+        }
+
+        // H <- e^{G_L} H + K^T Vt, Vt = diag(e^{G_L - G}) Vnew
         {
             const float gl = sGL[par];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const uint16_t *pkt = sK + (4 * lq + (l16 >> 2)) * PK + 32 * (kb >> 1) + 4 * (kb & 1) + 8 * (l16 & 3);
-                const bf16x8 a01 = cat(ld4_tr(pkt), ld4_tr(pkt + 16 * PK));
-                const bf16x8 a23 = cat(ld4_tr(pkt + 32 * PK), ld4_tr(pkt + 48 * PK));
+                const bf16x8 a01 = kt_frag(kb, 0);
+                const bf16x8 a23 = kt_frag(kb, 1);
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     f32x4 s = hs[kb][nt] * gl;
@@ -604,9 +664,16 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             }
         }
         if constexpr (CK != 0) {
-            // the state after this chunk, plain [dk][dv] fp32 at its chunk row
-            const int64_t row = ck_base + c;
-            if (row < a.ck_rows) {
+            // the state after this chunk: at its chunk row (CK = 2), or (CK = 1)
+            // at the row of the sequence's last checkpoint when the chunk ends
+            // the sequence, else when the chunk end is a multiple of ck_unit
+            int64_t row = ck_base + c;
+            if constexpr (CK == 1) {
+                const int64_t len_seq = eos - bos, p_end = (c + 1) * C;
+                row = p_end >= len_seq ? ck_base + (len_seq + ck_unit - 1) / ck_unit - 1
+                    : p_end % ck_unit == 0 ? ck_base + p_end / ck_unit - 1 : -1;
+            }
+            if (row >= 0 && row < a.ck_rows) {
                 // lane part of the offset in a register, the rest (tile, row
                 // within the tile) as the scalar offset of each store
                 if constexpr (CK == 2) {
@@ -622,16 +689,14 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                                                                   lane_off, (kb * NTW + nt) * 64 * 8, 0);
                 } else {
                     const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(a.hck + (row * a.hv + h) * D * D, D * D * 4);
-                    const uint32_t lane_off = (dk_of(0, 4 * lq) * D + dv_of(0, l16)) * 4;
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                         for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
-                                const uint32_t cst = ((dk_of(kb, r) - dk_of(0, 0)) * D + 4 * nt) * 4;
                                 const float val = hs[kb][nt][r];   // (bit-casting the vector element directly stored element 0)
-                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), rd, lane_off, cst, 0);
+                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), rd, ck_lane_off, ck_cst(kb, nt, r), 0);
                             }
                 }
             }
@@ -725,9 +790,9 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 //   H <- diag(a) H;  d = b_t (v_t - H^T k_t);  H <- H + k_t d^T;  o_t = scale H^T q_t
 // The two column sums over rows go through LDS (two buffers, so a token
 // takes three barriers); the next token's q, k, v, g and beta are loaded
-// while the current one is processed.  CK = 1 also stores H after the last
-// token of every 64-token chunk (and of the sequence), as the fused kernel's
-// checkpoint mode does.  No exponent folding: any g <= 0 is in range.
+// while the current one is processed.  CK = 1 also stores H after every
+// ck_every tokens and after the sequence's last token, as the fused
+// kernel's checkpoint mode does.  No exponent folding: any g <= 0 is in range.
 // --------------------------------------------------------------------------
 template <int D>
 struct F32Shape {
@@ -767,7 +832,10 @@ __global__ void __launch_bounds__(kFwdF32Threads) gdr_fwd_f32_kernel(FwdArgs a) 
     const float *vf = static_cast<const float *>(a.v);
     float *of = static_cast<float *>(a.o);
     const int64_t sbase = (n * a.hv + h) * static_cast<int64_t>(D) * D;
-    const int64_t ck_base = CK == 0 ? 0 : a.ck_offs ? static_cast<int64_t>(a.ck_offs[n]) : n * ((a.seq_len + C - 1) / C);
+    const int64_t ck_unit = a.ck_every > 0 ? static_cast<int64_t>(a.ck_every) : C;   // checkpoint every ck_unit tokens
+    const int64_t ck_base = CK == 0 ? 0
+                          : a.ck_offs ? static_cast<int64_t>(a.ck_offs[n])
+                                      : n * ((a.seq_len + ck_unit - 1) / ck_unit);
 
     // h0, ht and the checkpoints need only 4-byte alignment: element accesses
     auto ld4 = [](const float *p) { return f32x4{p[0], p[1], p[2], p[3]}; };
@@ -836,10 +904,13 @@ __global__ void __launch_bounds__(kFwdF32Threads) gdr_fwd_f32_kernel(FwdArgs a) 
             *reinterpret_cast<f32x4 *>(of + (tok * a.hv + h) * D + j0) = o * a.scale;
         }
         if constexpr (CK == 1) {
-            const int64_t pos = tok - bos;
-            if (pos % C == C - 1 || tok == eos - 1) {
-                const int64_t row = ck_base + pos / C;
-                if (row < a.ck_rows) {
+            // after P tokens: the last row when the sequence ends, else a row
+            // when P is a multiple of ck_unit
+            const int64_t P = tok - bos + 1, len_seq = eos - bos;
+            const int64_t row = P == len_seq ? ck_base + (len_seq + ck_unit - 1) / ck_unit - 1
+                              : P % ck_unit == 0 ? ck_base + P / ck_unit - 1 : -1;
+            {
+                if (row >= 0 && row < a.ck_rows) {
                     float *dst = a.hck + (row * a.hv + h) * static_cast<int64_t>(D) * D;
 #pragma unroll
                     for (int i = 0; i < RPT; ++i) st4(dst + (i0 + i) * D + j0, H[i]);
@@ -860,7 +931,7 @@ constexpr int kPrepThreads = 1024;
 constexpr int kSortMax = 8192;
 
 __global__ void __launch_bounds__(kPrepThreads) gdr_prepare_kernel(
-    const int32_t *cu, int64_t n_seq, int32_t *offs, int32_t *map, int64_t nt_max, int32_t *order) {
+    const int32_t *cu, int64_t n_seq, int32_t *offs, int32_t *map, int64_t nt_max, int32_t *order, int32_t unit) {
     __shared__ int32_t s_scan[kPrepThreads];
     __shared__ int32_t s_len[kSortMax];
     const int tid = threadIdx.x;
@@ -872,7 +943,7 @@ __global__ void __launch_bounds__(kPrepThreads) gdr_prepare_kernel(
             len = cu[n + 1] - cu[n];
             len = len < 0 ? 0 : len;
         }
-        const int32_t nc = (len + C - 1) / C;
+        const int32_t nc = (len + unit - 1) / unit;   // pieces of `unit` tokens (chunks: unit = C)
         s_scan[tid] = nc;
         __syncthreads();
         for (int off = 1; off < kPrepThreads; off <<= 1) {
@@ -1234,9 +1305,14 @@ __global__ void __launch_bounds__(64) gdr_selftest_kernel(const uint16_t *a, con
 
 template <int D, bool IN_BF16, bool GATE_BF16>
 hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
-    auto kern = a.hck16 ? gdr_fwd_kernel<D, IN_BF16, GATE_BF16, 2>
-              : a.hck   ? gdr_fwd_kernel<D, IN_BF16, GATE_BF16, 1>
-                        : gdr_fwd_kernel<D, IN_BF16, GATE_BF16, 0>;
+    // f32 inputs reach the fused kernel only for the backward's bf16 state
+    // recompute (hck16); their other calls run the fp32 kernel
+    void (*kern)(FwdArgs) = gdr_fwd_kernel<D, IN_BF16, GATE_BF16, 2>;
+    if constexpr (IN_BF16) {
+        if (!a.hck16) kern = a.hck ? gdr_fwd_kernel<D, true, GATE_BF16, 1> : gdr_fwd_kernel<D, true, GATE_BF16, 0>;
+    } else if (!a.hck16) {
+        return hipErrorInvalidValue;
+    }
     const int lds = FwdLds<D>::bytes;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1285,9 +1361,10 @@ hipError_t launch_fwd_f32(const FwdArgs &a, bool per_channel, hipStream_t stream
 }
 
 hipError_t launch_prepare(const int32_t *cu, int64_t n_seq, int32_t *chunk_offsets, int32_t *chunk_map,
-                          int64_t nt_max, int32_t *order, hipStream_t stream) {
+                          int64_t nt_max, int32_t *order, hipStream_t stream, int32_t unit) {
+    if (unit < 1 || (chunk_map && unit != C)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(gdr_prepare_kernel, dim3(1), dim3(kPrepThreads), 0, stream, cu, n_seq,
-                       chunk_offsets, chunk_map, nt_max, order);
+                       chunk_offsets, chunk_map, nt_max, order, unit);
     return hipGetLastError();
 }
 
@@ -1302,17 +1379,15 @@ hipError_t fwd_slots(int d, int in_bf16, int gate_bf16, int *slots) {
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
+    // only bf16 inputs run the fused kernel without checkpoints (f32 inputs run the fp32 kernel)
+    if (!in_bf16) return hipErrorInvalidValue;
     const void *kern;
     if (d == 64)
-        kern = in_bf16 ? (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, true, 0>)
-                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, false, 0>))
-                       : (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<64, false, true, 0>)
-                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<64, false, false, 0>));
+        kern = gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, true, 0>)
+                         : reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, false, 0>);
     else
-        kern = in_bf16 ? (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, true, 0>)
-                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, false, 0>))
-                       : (gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<128, false, true, 0>)
-                                    : reinterpret_cast<const void *>(gdr_fwd_kernel<128, false, false, 0>));
+        kern = gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, true, 0>)
+                         : reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, false, 0>);
     const int lds = fwd_lds_bytes(d);
     if ((e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFwdThreads, lds)) != hipSuccess) return e;

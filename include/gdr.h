@@ -182,6 +182,38 @@ int gdr_chunk_fwd_checkpoints(const gdr_tensor *q, const gdr_tensor *k, const gd
                               const gdr_tensor *h_chunks, float scale, hipStream_t stream);
 
 /*
+ * gdr_chunk_fwd_checkpoints_n - gdr_chunk_fwd_checkpoints with a checkpoint
+ * every `every_n` tokens in place of every 64.  The same kept prefill surface
+ * ("feat(cake_kda): add paired recurrent training for SM100a and SM103a", the
+ * follow-up's list of kept kwargs) has a `checkpoint_every_n_tokens` argument
+ * beside `state_checkpoints`, and keeps checkpoint granularity 16.
+ *
+ *   every_n   a multiple of 16, 16 <= every_n <= 2^30
+ *   h_ckpt    fp32 [R, Hv, dk, dv] out (device), R = ceil(T/every_n) + N with
+ *             cu_seqlens, else B * ceil(T/every_n).  Sequence n owns
+ *             ceil(L_n / every_n) rows starting at off_n = sum over m < n of
+ *             ceil(L_m / every_n); row off_n + j receives H (= S^T, [dk][dv])
+ *             after min((j+1) every_n, L_n) tokens, so the last row of a
+ *             sequence is its ht.  Rows past off_N are not written; length-0
+ *             sequences own no rows.
+ *
+ * every_n = 64 gives gdr_chunk_fwd_checkpoints bit for bit, and o and ht are
+ * gdr_chunk_fwd's for any every_n.  bf16 inputs: a checkpoint inside a
+ * 64-token chunk is formed from the state at the chunk's start and the
+ * chunk's first 16, 32 or 48 tokens (bf16 MFMA operands, fp32 accumulation;
+ * same tolerance as the chunk-end rows).  f32 inputs: the fp32 kernel stores
+ * its state after the token.  Extra traffic: 4 * dk * dv bytes per row
+ * written.  With cu_seqlens the workspace is 8*N + 20 bytes.  Errors: those of
+ * gdr_chunk_fwd_checkpoints (for h_ckpt), plus GDR_EINVAL for every_n.
+ */
+int gdr_chunk_fwd_checkpoints_n(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
+                                const gdr_tensor *g, const gdr_tensor *beta,
+                                const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
+                                const gdr_tensor *o, const gdr_tensor *ht,
+                                const gdr_tensor *h_ckpt, int64_t every_n, float scale,
+                                hipStream_t stream);
+
+/*
  * gdr_chunk_bwd - backward pass of gdr_chunk_fwd: the gradients of the scalar
  * loss L given dL/do and dL/dht, for every input.  The pages discuss the
  * backward as the other half of the kernel family ("Findings from integrating

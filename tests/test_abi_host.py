@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == set(gdr.EXPORTS), declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.gdr_version() == 10100
+    assert lib.gdr_version() == 10200
 
 
 def test_exports_match_nm():
@@ -225,6 +225,37 @@ def test_checkpoints_rejects_null_and_alias(lib):
     hck = describe(d["o"].t.data, GDR_F32, [rows, 4, 128, 128])
     assert _ckpt_call(lib, d, hck) == -5
     assert "overlaps" in lib.gdr_last_error().decode()
+
+
+def _ckpt_n_call(lib, d, hck, n):
+    args = [d[k] for k in ("q", "k", "v", "g", "beta", "cu_seqlens", "h0", "o", "ht")]
+    refs = [None if x is None else x.ref for x in args] + [None if hck is None else hck.ref]
+    return lib.gdr_chunk_fwd_checkpoints_n(*refs, ctypes.c_int64(n), ctypes.c_float(0.1), None)
+
+
+@pytest.mark.parametrize("n", [0, 8, 24, -16, 2 ** 31])
+def test_checkpoints_n_rejects_bad_granularity(lib, n):
+    d = fwd_descs(T=200)
+    hck = Alloc()(GDR_F32, [(200 + 15) // 16 + 3, 4, 128, 128])
+    assert _ckpt_n_call(lib, d, hck, n) == -1
+    assert "every_n" in lib.gdr_last_error().decode()
+
+
+@pytest.mark.parametrize("n,varlen", [(16, True), (48, True), (64, True), (16, False), (80, False), (1024, True)])
+def test_checkpoints_n_rows(lib, n, varlen):
+    """R = ceil(T/n) + N rows with cu_seqlens, B ceil(T/n) without: that
+    shape passes validation (then no device: GDR_EDEVICE), one row more or
+    less is GDR_ESHAPE naming the piece size."""
+    B = 1 if varlen else 2
+    d = fwd_descs(B=B, T=200, varlen=varlen)
+    rows = (200 + n - 1) // n + 3 if varlen else B * ((200 + n - 1) // n)
+    far = Alloc()
+    far.next = 1 << 44   # addresses disjoint from the other tensors
+    assert _ckpt_n_call(lib, d, far(GDR_F32, [rows, 4, 128, 128]), n) == -6
+    for delta in (1, -1):
+        assert _ckpt_n_call(lib, d, far(GDR_F32, [rows + delta, 4, 128, 128]), n) == -2
+        assert "pieces of %d tokens" % n in lib.gdr_last_error().decode()
+    assert _ckpt_n_call(lib, d, None, n) == -1 and "h_ckpt" in lib.gdr_last_error().decode()
 
 
 def dec_descs(B=3, Hk=2, Hv=4, d=128, dt=GDR_BF16, gdt=GDR_BF16):
