@@ -34,6 +34,7 @@ EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_checkpoints", "gdr_chunk_bwd", "gdr_c
 # gdr_debug_set options and device status bits (include/gdr.h)
 GDR_DEBUG_CHECK_CU, GDR_DEBUG_FAIL_LAUNCHES, GDR_DEBUG_SPIN_LIMIT = 1, 2, 3
 GDR_DEVSTAT_WAIT_TIMEOUT = 1
+GDR_DEVSTAT_KDA_RANGE = 2
 
 
 class GdrError(RuntimeError):

@@ -47,6 +47,7 @@ struct FwdArgs {
 
 // Bits of the per-device status word the kernels set (sticky until cleared).
 constexpr uint32_t kDevStatWaitTimeout = 1u;   // a hand-off wait gave up: outputs of that call are wrong
+constexpr uint32_t kDevStatKdaRange = 2u;      // per-channel gates beyond the range of their chunk form
 constexpr int32_t kSpinDefault = 1 << 18;      // polls (each s_sleep 1, about 64 cycles) before giving up
 
 // Per-device memory the library keeps in static device arrays: the status

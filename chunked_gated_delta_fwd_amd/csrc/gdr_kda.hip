@@ -7,27 +7,30 @@
 // makes it from a raw gate is not defined on the pages).
 //
 // Chunk form.  With G the chunk-local prefix sums of g (per channel, rows past
-// the segment end padded with g = b = 0) and a reference row m = 31 of the
-// chunk, the exponentials are folded into the operands so that every factor
-// stays within e^{+-(half the chunk's decay)}:
+// the segment end padded with g = b = 0), the exponentials are folded into the
+// operands with one reference per 16-row block: R_b = G at the row before
+// block b (R_0 = 0), b(i) the block of row i,
 //
-//   q~ = q o e^{G - G_m},  k~ = k o e^{G - G_m},  k^ = k o e^{G_m - G}
-//   A  = tril(diag(b) k~ k^^T, -1),  P = scale tril(q~ k^^T)
-//   S_m = diag(e^{G_m}) H                  (the state decayed to row m)
-//   U  = (I + A)^-1 diag(b) (V - k~ S_m)
-//   O  = scale q~ S_m + P U
-//   H <- diag(e^{G_L}) H + diag(e^{G_L - G_m}) k^^T U
+//   q~_i = q_i o e^{G_i - R_b(i)},  k~_i = k_i o e^{G_i - R_b(i)}       (<= 1)
+//   k^(b)_j = k_j o e^{R_b - G_j}  for j < 16 (b + 1)      (<= 1 for j < 16 b)
+//   A_ij = b_i k~_i . k^(b(i))_j (j < i),  P_ij = scale q~_i . k^(b(i))_j (j <= i)
+//   U  = (I + A)^-1 diag(b) (V - (k o e^G) H)
+//   O  = scale (q o e^G) H + P U
+//   H <- diag(e^{G_L}) H + (k o e^{G_L - G})^T U
 //
-// A per-channel decay summed over half a chunk must stay above about -85 so
-// that e^{G_m - G} fits in fp32/bf16 (about 2.6 per token and channel).
+// Every factor is at most 1 except inside a diagonal block, where it is at
+// most e^{-(the block's decay)}: a channel's log-decay summed over 16 tokens
+// must stay above about -87 (fp32 and bf16 exponent range), i.e. about -5.4
+// per token, which holds the pages' safe-gate lower bound of -5.  A block
+// beyond it sets GDR_DEVSTAT_KDA_RANGE in the device status word.
 //
 // One work-group of 8 waves per (sequence, v-head) walks its chunks in order;
 // wave w owns dv columns [16w, 16w + 16) of the fp32 state (MFMA C tiles, rows
 // dk).  Per chunk: the gate scan (all threads: two adjacent channels and an
 // eighth of the tokens each) and the gated operands into LDS; the ten lower blocks of A and
 // of P (the four waves that make the diagonal blocks of A also invert them,
-// 16x16 by fp32 substitution), then each wave's k~ S_m and q~ S_m (S_m taken
-// from the wave's own state registers, whose C-tile layout is the B
+// 16x16 by fp32 substitution), then each wave's (k o e^G) H and (q o e^G) H
+// (H taken from the wave's own state registers, whose C-tile layout is the B
 // operand's); then per wave U by block forward substitution over its
 // columns, O and the state update.
 #include "gdr_internal.h"
@@ -129,29 +132,34 @@ __device__ __forceinline__ VRaw<GATE_BF16> fetch_beta(const FwdArgs &a, int64_t 
 
 template <int D>
 struct KdaLds {
-    // Row pitches (bf16 elements).  q~, k~, the copy of k^ and P are read as
-    // 16-byte row fragments over key-permuted columns (kpos); k^ itself is
-    // read with the transposing loads (4 rows of 32 bytes per 16 lanes) for
-    // the state update; A and the diagonal inverses as 8-byte fragments, at
+    // Row pitches (bf16 elements).  The operand arrays and P are read as
+    // 16-byte row fragments over key-permuted columns (kpos); k o e^{G_L - G}
+    // with the transposing loads (4 rows of 32 bytes per 16 lanes) for the
+    // state update; A and the diagonal inverses as 8-byte fragments, at
     // pitches of 2 mod 32 four-byte banks (16 lanes, one row each, no
-    // conflict).  Measured: the 8-byte reads of q~ and k~ at the old pitch
-    // of 8 mod 32 banks cost twice the time of the whole A/P phase now.
-    static constexpr int PK = D + 16;              // q~, k~ and the k^ copy (key-permuted columns)
-    static constexpr int PH = D + 16;              // k^
+    // conflict).  Measured: the 8-byte reads of q~ and k~ at a pitch of 8 mod
+    // 32 banks cost twice the time of the whole A/P phase.
+    static constexpr int PK = D + 16;              // operand arrays (key-permuted columns)
+    static constexpr int PH = D + 16;              // k o e^{G_L - G}
     static constexpr int PP = C + 4;               // A
     static constexpr int PQ = C + 16;              // P (key-permuted columns)
     static constexpr int PD = 20;
-    static constexpr int oQt = 0;                  // q~ [64][PK]
+    static constexpr int oQt = 0;                  // q~ [64][PK] (block references)
     static constexpr int oKt = oQt + C * PK * 2;   // k~
-    static constexpr int oKh = oKt + C * PK * 2;   // k o e^{G_L - G} [64][PH] (the state update's)
-    static constexpr int oKr = oKh + C * PH * 2;   // k^ again [64][PK], for its row-fragment reads
-    static constexpr int oA = oKr + C * PK * 2;    // diag(b) A~ strictly lower [i][j]
+    static constexpr int oQs = oKt + C * PK * 2;   // q o e^G [64][PK] (the chunk start as reference)
+    static constexpr int oKs = oQs + C * PK * 2;   // k o e^G
+    static constexpr int oKh = oKs + C * PK * 2;   // k o e^{G_L - G} [64][PH] (the state update's)
+    // column copies k^(b), b = 0..3: rows 0 .. 16 b + 15 of copy b at row 8 b (b + 1)
+    static constexpr int oKc = oKh + C * PH * 2;
+    static constexpr int oA = oKc + 160 * PK * 2;  // diag(b) A~ strictly lower [i][j]; the scan's group totals before
     static constexpr int oP = oA + C * PP * 2;     // scale tril(q~ k^^T) [i][kpos(j)]
     static constexpr int oDi = oP + C * PQ * 2;    // inverses of the diagonal blocks [4][16][PD]
-    static constexpr int oV = oDi + 4 * 16 * PD * 2;   // f32 [D] x2: e^{G_m}, e^{G_L}; [64] b
+    static constexpr int oV = oDi + 4 * 16 * PD * 2;   // f32 [D] e^{G_L}; [64] b
     static constexpr int NG = 2 * kKdaThreads / D; // token groups of the gate scan (a thread: 2 channels)
-    static constexpr int oTot = oV + (2 * D + C) * 4;  // f32 [NG][D] group totals of the scan
-    static constexpr int bytes = oTot + NG * D * 4;
+    static constexpr int oTot = oA;                // f32 [NG][D] group totals of the scan (A's space, free then)
+    static constexpr int bytes = oV + (D + C) * 4;
+    static_assert(NG * D * 4 <= C * PP * 2, "the group totals fit in A's space");
+    static_assert(16 % (C / NG) == 0, "a scan group's tokens lie in one 16-row block");
 };
 
 template <int D, bool IN_BF16, bool GATE_BF16>
@@ -164,15 +172,17 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     uint16_t *sQt = reinterpret_cast<uint16_t *>(lds + Ly::oQt);
     uint16_t *sKt = reinterpret_cast<uint16_t *>(lds + Ly::oKt);
+    uint16_t *sQs = reinterpret_cast<uint16_t *>(lds + Ly::oQs);
+    uint16_t *sKs = reinterpret_cast<uint16_t *>(lds + Ly::oKs);
     uint16_t *sKh = reinterpret_cast<uint16_t *>(lds + Ly::oKh);
-    uint16_t *sKr = reinterpret_cast<uint16_t *>(lds + Ly::oKr);
+    uint16_t *sKc = reinterpret_cast<uint16_t *>(lds + Ly::oKc);
     uint16_t *sA = reinterpret_cast<uint16_t *>(lds + Ly::oA);
     uint16_t *sP = reinterpret_cast<uint16_t *>(lds + Ly::oP);
     uint16_t *sDi = reinterpret_cast<uint16_t *>(lds + Ly::oDi);
-    float *sEm = reinterpret_cast<float *>(lds + Ly::oV);
-    float *sEL = sEm + D;
+    float *sEL = reinterpret_cast<float *>(lds + Ly::oV);
     float *sB = sEL + D;
     float *sTot = reinterpret_cast<float *>(lds + Ly::oTot);
+    auto kcopy = [&](int b) { return sKc + 8 * b * (b + 1) * PK; };   // column copy k^(b)
 
     const int64_t item = gqa_xcd_item(blockIdx.x, gridDim.x, a.hv, a.hk);   // v-heads of a q/k head share an L2
     const int64_t rank = item / a.hv;
@@ -191,7 +201,7 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
     eos = eos > a.total_tokens ? a.total_tokens : eos;
     if (eos <= bos) return;   // length-0 segment: reads nothing, writes nothing
     const int hk = h / (a.hv / a.hk);
-    const int tid = threadIdx.x, wave = tid >> 6;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform branches
     const bool colwave = wave < NTD;
     const int nt = wave;
     const int64_t nch = (eos - bos + C - 1) / C;
@@ -262,52 +272,79 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
                 G2[e][i] = run;
             }
         }
-        __syncthreads();   // the previous chunk's reads of LDS are done
+        __syncthreads();   // the previous chunk's reads of LDS are done (A's space takes the totals)
         *reinterpret_cast<float2 *>(sTot + grp * D + ch) = float2{G2[0][TPG - 1], G2[1][TPG - 1]};
         if (wave == 0) sB[lane] = static_cast<float>(pb);
         __syncthreads();
         {
-            float offs[2] = {0.f, 0.f}, gm[2] = {0.f, 0.f}, gl[2] = {0.f, 0.f};
+            // offsets of this thread's tokens, the block references R_b (G at
+            // the row before block b, R_0 = 0) and G_L, per channel (log2 units)
+            constexpr int NB = C / 16;
+            float offs[2] = {0.f, 0.f}, gl[2] = {0.f, 0.f}, rb[2][NB] = {};
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
                 const float2 tj = *reinterpret_cast<const float2 *>(sTot + j * D + ch);
                 offs[0] += j < grp ? tj.x : 0.f;
                 offs[1] += j < grp ? tj.y : 0.f;
-                gm[0] += j < 32 / TPG ? tj.x : 0.f;
-                gm[1] += j < 32 / TPG ? tj.y : 0.f;
+#pragma unroll
+                for (int b = 1; b < NB; ++b) {
+                    rb[0][b] += j < 16 * b / TPG ? tj.x : 0.f;
+                    rb[1][b] += j < 16 * b / TPG ? tj.y : 0.f;
+                }
                 gl[0] += tj.x;
                 gl[1] += tj.y;
             }
             if (grp == 0) {
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    sEm[ch + e] = fast_exp2(gm[e]);
-                    sEL[ch + e] = fast_exp2(gl[e]);
-                }
+                for (int e = 0; e < 2; ++e) sEL[ch + e] = fast_exp2(gl[e]);
             }
-            // the state update's copy of k carries e^{G_L - G} = e^{G_m - G} e^{G_L - G_m} (<= 1)
-            const float elm[2] = {fast_exp2(gl[0] - gm[0]), fast_exp2(gl[1] - gm[1])};
+            // the 16-row block of this thread's tokens (one per wave)
+            const int blk = __builtin_amdgcn_readfirstlane(grp * TPG / 16);
+            // per channel: R_blk, e^{R_blk} and e^{R_b - R_blk} for the later blocks (all <= 1)
+            float rbb[2], eb[2], ratio[2][NB];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                rbb[e] = rb[e][0];
+#pragma unroll
+                for (int b = 1; b < NB; ++b) rbb[e] = b == blk ? rb[e][b] : rbb[e];
+                eb[e] = fast_exp2(rbb[e]);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) ratio[e][b] = fast_exp2(fminf(rb[e][b] - rbb[e], 0.f));
+            }
+            bool out_of_range = false;
 #pragma unroll
             for (int i = 0; i < TPG; ++i) {
                 const int row = grp * TPG + i;
-                uint32_t wq = 0, wk = 0, wh = 0, wl = 0;   // the two channels' bf16 values, packed
+                float x[2], qv[2], kv[2], er[2], ed[2], eu[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const float x = G2[e][i] + offs[e] - gm[e];
-                    const float qv = static_cast<float>(static_cast<__bf16>(pair_val<IN_BF16>(pq[i], e)));
-                    const float kv = static_cast<float>(static_cast<__bf16>(pair_val<IN_BF16>(pk[i], e)));
-                    const float ex = fast_exp2(x), ei = fast_exp2(-x);
-                    wq |= static_cast<uint32_t>(bf16_bits(qv * ex)) << (16 * e);
-                    wk |= static_cast<uint32_t>(bf16_bits(kv * ex)) << (16 * e);
-                    wh |= static_cast<uint32_t>(bf16_bits(kv * ei)) << (16 * e);
-                    wl |= static_cast<uint32_t>(bf16_bits(kv * ei * elm[e])) << (16 * e);
+                    x[e] = G2[e][i] + offs[e];   // G at this row
+                    qv[e] = static_cast<float>(static_cast<__bf16>(pair_val<IN_BF16>(pq[i], e)));
+                    kv[e] = static_cast<float>(static_cast<__bf16>(pair_val<IN_BF16>(pk[i], e)));
+                    // e^{G - R_blk} (<= 1), e^{R_blk - G} (>= 1, the diagonal block's), e^{G_L - G} (<= 1)
+                    er[e] = fast_exp2(x[e] - rbb[e]);
+                    ed[e] = fast_exp2(rbb[e] - x[e]);
+                    eu[e] = fast_exp2(gl[e] - x[e]);
+                    // the largest factor, e^{R_blk - G} inside the block, must stay finite
+                    out_of_range |= rbb[e] - x[e] > 126.f;
                 }
-                // channels ch, ch + 1 stay adjacent under kpos (ch is even)
-                *reinterpret_cast<uint32_t *>(sQt + row * PK + chp) = wq;
-                *reinterpret_cast<uint32_t *>(sKt + row * PK + chp) = wk;
-                *reinterpret_cast<uint32_t *>(sKh + row * PH + ch) = wl;
-                *reinterpret_cast<uint32_t *>(sKr + row * PK + chp) = wh;
+                // the two channels' bf16 values, packed; channels ch, ch + 1 stay
+                // adjacent under kpos (ch is even).  q~, k~ (block reference),
+                // q, k o e^G (chunk start), k o e^{G_L - G}, the column copies k^(b)
+                auto pk2 = [](float lo, float hi) { return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo, (__bf16)hi}); };
+                *reinterpret_cast<uint32_t *>(sQt + row * PK + chp) = pk2(qv[0] * er[0], qv[1] * er[1]);
+                *reinterpret_cast<uint32_t *>(sKt + row * PK + chp) = pk2(kv[0] * er[0], kv[1] * er[1]);
+                *reinterpret_cast<uint32_t *>(sQs + row * PK + chp) = pk2(qv[0] * er[0] * eb[0], qv[1] * er[1] * eb[1]);
+                *reinterpret_cast<uint32_t *>(sKs + row * PK + chp) = pk2(kv[0] * er[0] * eb[0], kv[1] * er[1] * eb[1]);
+                *reinterpret_cast<uint32_t *>(sKh + row * PH + ch) = pk2(kv[0] * eu[0], kv[1] * eu[1]);
+                const float kd0 = kv[0] * ed[0], kd1 = kv[1] * ed[1];
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    if (b >= blk)   // wave-uniform
+                        *reinterpret_cast<uint32_t *>(kcopy(b) + row * PK + chp) = pk2(kd0 * ratio[0][b], kd1 * ratio[1][b]);
             }
+            if (out_of_range)
+                __hip_atomic_fetch_or(a.status, kDevStatKdaRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         VRaw<IN_BF16> cv[16];   // this chunk's v values; the registers above take the next chunk
 #pragma unroll
@@ -324,10 +361,11 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
             // tile t: A blocks 0..5 below the diagonal, then P blocks (t - 2) for t = 6..11
             auto tile = [&](bool ka, int bi, int bj) __attribute__((always_inline)) {
                 const uint16_t *Am = ka ? sKt : sQt;
+                const uint16_t *Bm = kcopy(bi);   // the column copy of row block bi's reference
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int k0 = 0; k0 < D; k0 += 32)
-                    acc = mfma32(kfrag8(Am, PK, 16 * bi, k0, l16, lq), kfrag8(sKr, PK, 16 * bj, k0, l16, lq), acc);
+                    acc = mfma32(kfrag8(Am, PK, 16 * bi, k0, l16, lq), kfrag8(Bm, PK, 16 * bj, k0, l16, lq), acc);
                 const int j = 16 * bj + l16;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -379,25 +417,19 @@ __global__ void __launch_bounds__(kKdaThreads) gdr_kda_fwd_kernel(FwdArgs a) {
                 }
             }
         }
-        // ---- then k~ S_m and (q~ S_m)^T for this wave's dv tile, with
-        // S_m = diag(e^{G_m}) H taken from the wave's own state registers
+        // ---- then (k o e^G) H and ((q o e^G) H)^T for this wave's dv tile,
+        // H taken from the wave's own state registers
         f32x4 X[4], QS[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) X[mt] = QS[mt] = zero4();
         if (colwave) {
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk) {
-                f32x4 s0, s1;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    s0[r] = H[2 * kk][r] * sEm[32 * kk + 4 * lq + r];
-                    s1[r] = H[2 * kk + 1][r] * sEm[32 * kk + 16 + 4 * lq + r];
-                }
-                const bf16x8 bs = cat(cvt4(s0), cvt4(s1));
+                const bf16x8 bs = cat(cvt4(H[2 * kk]), cvt4(H[2 * kk + 1]));
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
-                    X[mt] = mfma32(kfrag8(sKt, PK, 16 * mt, 32 * kk, l16, lq), bs, X[mt]);
-                    QS[mt] = mfma32(bs, kfrag8(sQt, PK, 16 * mt, 32 * kk, l16, lq), QS[mt]);   // (q~ S_m)^T
+                    X[mt] = mfma32(kfrag8(sKs, PK, 16 * mt, 32 * kk, l16, lq), bs, X[mt]);
+                    QS[mt] = mfma32(bs, kfrag8(sQs, PK, 16 * mt, 32 * kk, l16, lq), QS[mt]);   // ((q o e^G) H)^T
                 }
             }
         }
@@ -484,19 +516,17 @@ hipError_t launch_kda_t(const FwdArgs &a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_kda_d(const FwdArgs &a, hipStream_t s) {
-    if (a.in_bf16) return a.gate_bf16 ? launch_kda_t<D, true, true>(a, s) : launch_kda_t<D, true, false>(a, s);
-    return a.gate_bf16 ? launch_kda_t<D, false, true>(a, s) : launch_kda_t<D, false, false>(a, s);
+    // f32 inputs run the fp32 token-serial kernel (launch_kda_fwd)
+    if (!a.in_bf16) return hipErrorInvalidValue;
+    return a.gate_bf16 ? launch_kda_t<D, true, true>(a, s) : launch_kda_t<D, true, false>(a, s);
 }
 
 static_assert(KdaLds<128>::bytes <= 160 * 1024, "KDA kernel LDS");
 
 template <int D>
-const void *kda_kernel(int in_bf16, int gate_bf16) {
-    if (in_bf16)
-        return gate_bf16 ? reinterpret_cast<const void *>(gdr_kda_fwd_kernel<D, true, true>)
-                         : reinterpret_cast<const void *>(gdr_kda_fwd_kernel<D, true, false>);
-    return gate_bf16 ? reinterpret_cast<const void *>(gdr_kda_fwd_kernel<D, false, true>)
-                     : reinterpret_cast<const void *>(gdr_kda_fwd_kernel<D, false, false>);
+const void *kda_kernel(int gate_bf16) {
+    return gate_bf16 ? reinterpret_cast<const void *>(gdr_kda_fwd_kernel<D, true, true>)
+                     : reinterpret_cast<const void *>(gdr_kda_fwd_kernel<D, true, false>);
 }
 
 }  // namespace
@@ -506,7 +536,8 @@ hipError_t kda_slots(int d, int in_bf16, int gate_bf16, int *slots) {
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const void *kern = d == 64 ? kda_kernel<64>(in_bf16, gate_bf16) : kda_kernel<128>(in_bf16, gate_bf16);
+    if (!in_bf16) return hipErrorInvalidValue;   // f32 inputs run the fp32 kernel
+    const void *kern = d == 64 ? kda_kernel<64>(gate_bf16) : kda_kernel<128>(gate_bf16);
     const int lds = d == 64 ? KdaLds<64>::bytes : KdaLds<128>::bytes;
     if ((e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kKdaThreads, lds)) != hipSuccess) return e;

@@ -270,11 +270,16 @@ int gdr_chunk_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
  *
  * Everything else (shapes, varlen and ghosts, h0/ht, GQA, errors) is
  * gdr_chunk_fwd.  bf16 inputs: within one 64-token chunk the gates are
- * folded into the operands around the chunk's row 31, so a channel's
- * log-decay summed over half a chunk must stay above about -85 (fp32 exponent
- * range).  f32 inputs run the token-serial fp32 kernel of gdr_chunk_fwd with
- * diag(exp(g_t)) in place of exp(g_t): any gate is in range.  With cu_seqlens
- * the workspace is 4*N + 16 bytes (longest sequences start first).
+ * folded into the operands with one reference per block of 16 tokens, so a
+ * channel's log-decay summed over 16 tokens must stay above about -87 (fp32
+ * exponent range), about -5.4 per token: this holds the pages' safe-gate
+ * lower bound of -5 ("feat(cake_kda): add paired recurrent training for
+ * SM100a and SM103a", the maintainer's section).  A call that meets steeper
+ * gates sets GDR_DEVSTAT_KDA_RANGE in the device status word
+ * (gdr_device_status).  f32 inputs run the token-serial fp32 kernel of
+ * gdr_chunk_fwd with diag(exp(g_t)) in place of exp(g_t): any gate is in
+ * range.  With cu_seqlens the workspace is 4*N + 16 bytes (longest sequences
+ * start first).
  */
 int gdr_chunk_kda_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
                       const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
@@ -447,6 +452,8 @@ int gdr_debug_set(int option, int64_t value);
 
 /* Bits of the device status word. */
 #define GDR_DEVSTAT_WAIT_TIMEOUT 1u /* a forward kernel's hand-off wait gave up: its outputs are wrong */
+#define GDR_DEVSTAT_KDA_RANGE 2u    /* gdr_chunk_kda_fwd (bf16 inputs) met a channel whose log-decay over
+                                       one 16-token block is below about -87: its outputs are not finite */
 
 /*
  * gdr_device_status - the status word of the current device: bits the

@@ -93,6 +93,78 @@ def chunked(c, C):
     return o, ht
 
 
+def chunked_blocks(c, C, B=16, stats=None):
+    """Chunk form with one reference per block of B rows (per channel), so that
+    no factor exceeds e^{(decay of one block)}: with R_b = G at the row before
+    block b (R_0 = 0) and b(i) the block of row i,
+      row operands   q~_i = q_i e^{G_i - R_b(i)},  k~_i = k_i e^{G_i - R_b(i)}      (<= 1)
+      column copies  k^(b)_j = k_j e^{R_b - G_j},  j < B (b + 1)                  (<= 1 for j < B b)
+      A_ij = b_i k~_i . k^(b(i))_j (j < i),  P_ij = q~_i . k^(b(i))_j (j <= i)
+      state terms    q_i e^{G_i} H and k_i e^{G_i} H (reference: the chunk start)
+      U = (I + A)^-1 diag(b) (V - (k e^G) H),  O = scale ((q e^G) H + P U)
+      H <- diag(e^{G_L}) H + (k e^{G_L - G})^T U.
+    ``stats`` (a dict) receives the largest exponent any factor takes."""
+    q, k, v, g, beta, cu, h0, sc = (c[n] for n in ("q", "k", "v", "g", "beta", "cu", "h0", "scale"))
+    Hk, Hv, dk, dv = q.shape[2], v.shape[2], q.shape[3], v.shape[3]
+    o = np.zeros(v.shape)
+    ht = np.zeros((len(cu) - 1, Hv, dk, dv))
+    top = -np.inf
+    for n in range(len(cu) - 1):
+        for h in range(Hv):
+            hk = h // (Hv // Hk)
+            H = np.zeros((dk, dv)) if h0 is None else h0[n, h].copy()
+            for a0 in range(cu[n], cu[n + 1], C):
+                L = min(C, cu[n + 1] - a0)
+                Q = np.zeros((C, dk)); K = np.zeros((C, dk)); V = np.zeros((C, dv))
+                gg = np.zeros((C, dk)); bb = np.zeros(C)
+                Q[:L], K[:L], V[:L] = q[0, a0:a0 + L, hk], k[0, a0:a0 + L, hk], v[0, a0:a0 + L, h]
+                gg[:L], bb[:L] = g[0, a0:a0 + L, h], beta[0, a0:a0 + L, h]
+                G = np.cumsum(gg, axis=0)
+                GL = G[-1]
+                blk = np.arange(C) // B
+                R = np.stack([np.zeros(dk) if b == 0 else G[B * b - 1] for b in range(C // B)])
+                Qt, Kt = Q * np.exp(G - R[blk]), K * np.exp(G - R[blk])
+                A = np.zeros((C, C)); P = np.zeros((C, C))
+                for i in range(C):
+                    b = blk[i]
+                    Kc = K[:B * (b + 1)] * np.exp(R[b] - G[:B * (b + 1)])
+                    top = max(top, float((R[b] - G[:B * (b + 1)]).max()), float((G[i] - R[b]).max()))
+                    A[i, :i] = bb[i] * (Kc[:i] @ Kt[i])
+                    P[i, :i + 1] = Kc[:i + 1] @ Qt[i]
+                Qs, Ks = Q * np.exp(G), K * np.exp(G)
+                U = np.linalg.solve(np.eye(C) + A, bb[:, None] * (V - Ks @ H))
+                o[0, a0:a0 + L, h] = (sc * (Qs @ H + P @ U))[:L]
+                H = np.exp(GL)[:, None] * H + (K * np.exp(GL - G)).T @ U
+            if cu[n + 1] > cu[n]:
+                ht[n, h] = H
+    if stats is not None:
+        stats["max_exponent"] = top
+    return o, ht
+
+
+def pin_kda_block_references(fwd, _scalar=None):
+    """Against the chunk form with one reference per 16-row block (the form the
+    GPU kernel evaluates), chunks of 64 and 16 and blocks of 16 and 4; with
+    every gate at -5 per token and channel (the pages' safe-gate lower bound)
+    no factor of that form exceeds e^{80} (inside fp32), while the form with
+    one reference row per 64-token chunk needs e^{160}."""
+    c = _case(76, [150, 1, 64, 65], 280, 1, 2, 8, 8)
+    o, ht = _call(fwd, c)
+    for C, B in ((64, 16), (16, 16), (64, 4)):
+        o2, ht2 = chunked_blocks(c, C, B)
+        _close("blocks(%d, %d) o" % (C, B), o, o2, 1e-10)
+        _close("blocks(%d, %d) ht" % (C, B), ht, ht2, 1e-10)
+    c5 = _case(77, [100, 37], 137, 1, 1, 8, 8)
+    c5["g"][:] = -5.0
+    o, ht = _call(fwd, c5)
+    st = {}
+    o2, ht2 = chunked_blocks(c5, 64, 16, st)
+    _close("g = -5 o", o, o2, 1e-10)
+    _close("g = -5 ht", ht, ht2, 1e-10)
+    assert st["max_exponent"] <= 80.0 + 1e-9, st
+    assert 5.0 * 32 > 88.0   # the reference-row form: e^{G_m - G} over half a chunk
+
+
 def pin_kda_scalar_reduction(fwd, _scalar=None):
     """Gates equal over the channels give the scalar recurrence: against the
     (separately pinned) scalar oracle."""
@@ -153,5 +225,5 @@ def pin_kda_channel_selective(fwd, _scalar=None):
     _close("kept channels", np.delete(ht[0, 0], 2, axis=0), np.delete(H0, 2, axis=0), 0.0)
 
 
-ALL_KDA_PINS = [pin_kda_scalar_reduction, pin_kda_literal, pin_kda_chunked, pin_kda_pure_decay,
-                pin_kda_channel_selective]
+ALL_KDA_PINS = [pin_kda_scalar_reduction, pin_kda_literal, pin_kda_chunked, pin_kda_block_references,
+                pin_kda_pure_decay, pin_kda_channel_selective]

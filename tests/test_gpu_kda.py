@@ -89,6 +89,48 @@ def test_kda_fast_decay():
     _check(o, ht, o_ref, ht_ref, _real(d), "kda fast decay")
 
 
+@pytest.mark.parametrize("mode", ["const-5", "uniform-5..0"])
+def test_kda_bf16_gates_at_safe_lower_bound(mode):
+    """bf16 inputs with every per-channel log-decay at -5 per token (the pages'
+    safe-gate lower bound), or uniform in [-5, 0] per token and channel: the
+    16-row block references keep every factor inside fp32, no range flag is
+    raised, and o and ht match the oracle at the bf16 tolerances."""
+    import chunked_gated_delta_fwd_amd as gdr
+    import gdr_inputs
+    d = gdr_inputs.random_lengths_case(88, n_real=4, lo=1, hi=300, ghost_slots=1, hk=2, hv=4, d=128)
+    shape = d["v"].shape[:3] + (d["q"].shape[3],)
+    if mode == "const-5":
+        gk = np.full(shape, -5.0, dtype=np.float32)
+    else:
+        gk = gdr_inputs.round_to_bf16(
+            -5.0 * np.random.Generator(np.random.PCG64(89)).random(shape).astype(np.float32))
+    say("kda bf16 gates %s" % mode)
+    assert gdr.device_status(clear=True) == 0
+    o, ht = _run(d, gk)
+    assert gdr.device_status() == 0, "range flag raised inside the documented range"
+    o_ref, ht_ref = _ref(d, gk)
+    _check(o, ht, o_ref, ht_ref, _real(d), "kda bf16 g %s" % mode)
+
+
+def test_kda_bf16_gates_beyond_range_are_flagged():
+    """Gates of -6 per token (-96 over a 16-token block, beyond fp32's
+    exponent range) set GDR_DEVSTAT_KDA_RANGE; the next in-range call is clean."""
+    import chunked_gated_delta_fwd_amd as gdr
+    import gdr_inputs
+    d = gdr_inputs.random_lengths_case(90, n_real=2, lo=40, hi=80, ghost_slots=0, hk=1, hv=2, d=64)
+    shape = d["v"].shape[:3] + (d["q"].shape[3],)
+    say("kda bf16 gates -6: range flag")
+    assert gdr.device_status(clear=True) == 0
+    _run(d, np.full(shape, -6.0, dtype=np.float32))
+    bits = gdr.device_status(clear=True)
+    assert bits & gdr.GDR_DEVSTAT_KDA_RANGE, bits
+    gk = np.full(shape, -1.0, dtype=np.float32)
+    o, ht = _run(d, gk)
+    assert gdr.device_status() == 0
+    o_ref, ht_ref = _ref(d, gk)
+    _check(o, ht, o_ref, ht_ref, _real(d), "kda bf16 g -1 after a flagged call")
+
+
 @pytest.mark.parametrize("gval", [-5.0, -60.0])
 def test_kda_f32_inputs_steep_gates(gval):
     """f32 inputs with every per-channel log-decay at gval per token (half a
