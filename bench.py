@@ -192,29 +192,33 @@ def main():
     # (per-call times and kernel durations in profiles/); so the warm-up steps
     # are preceded by settle_calls back-to-back steps, and the timed steps
     # measure the steady state a continuously running caller sees.
+    #
+    # Two events bracket the K timed steps on the launch stream (timing
+    # events between consecutive calls left the GPU idle between them, which
+    # a caller running the steps back to back does not pay).  launch_ms is
+    # the average time per call on the stream: both kernels of the call and
+    # the dispatch gap between calls included.
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    # torch creates an event's HIP object at its first record: record each
+    ev_start = torch.cuda.Event(enable_timing=True)
+    ev_end = torch.cuda.Event(enable_timing=True)
+    # torch creates an event's HIP object at its first record: record both
     # once now, so that no event is created inside the timed region
-    for s_, e_ in ev:
-        s_.record(stream)
-        e_.record(stream)
+    ev_start.record(stream)
+    ev_end.record(stream)
     for _ in range(args.settle_calls):
         step()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s, e in ev:
-        s.record(stream)
+    ev_start.record(stream)
+    for _ in range(args.steps):
         step()
-        e.record(stream)
+    ev_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_call_ms = [s.elapsed_time(e) for s, e in ev]
     ms_per_step = wall * 1e3 / args.steps
-    launch_ms = sum(per_call_ms) / len(per_call_ms)
+    launch_ms = ev_start.elapsed_time(ev_end) / args.steps
 
     tokens = B * T
     in_bytes = 2 if w.dtype == "bf16" else 4
