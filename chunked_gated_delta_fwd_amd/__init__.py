@@ -55,7 +55,7 @@ class GdrLaunchPlan(ctypes.Structure):
                 ("in_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32), ("varlen", ctypes.c_int32),
                 ("has_h0", ctypes.c_int32), ("has_ht", ctypes.c_int32), ("grid_fwd", ctypes.c_int64),
                 ("block_fwd", ctypes.c_int32), ("lds_fwd", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_int64)]
+                ("workspace_bytes", ctypes.c_int64), ("dv", ctypes.c_int32)]
 
 
 _lib = None
@@ -297,17 +297,17 @@ def chunk_bwd(q, k, v, g, beta, do, cu_seqlens=None, h0=None, dht=None, scale: O
 
 
 def decode_step(q, k, v, g, beta, h, scale: Optional[float] = None, o=None):
-    """One recurrent step per sequence: q, k ``[B, Hk, d]``, v ``[B, Hv, d]``,
-    g, beta ``[B, Hv]``, state h fp32 ``[B, Hv, d, d]`` updated in place.
-    Returns o ``[B, Hv, d]``."""
+    """One recurrent step per sequence: q, k ``[B, Hk, dk]``, v ``[B, Hv, dv]``,
+    g, beta ``[B, Hv]``, state h fp32 ``[B, Hv, dk, dv]`` updated in place.
+    Returns o ``[B, Hv, dv]``."""
     import torch
     lib = library()
     B, Hk, d = q.shape
-    Hv = v.shape[1]
+    Hv, dv = v.shape[1], v.shape[2]
     if scale is None:
         scale = float(d) ** -0.5
     if o is None:
-        o = torch.empty((B, Hv, d), dtype=q.dtype, device=q.device)
+        o = torch.empty((B, Hv, dv), dtype=q.dtype, device=q.device)
     ds = [_desc(x) for x in (q, k, v, g, beta, h, o)]
     _check(lib, lib.gdr_decode_step(*[_ref(x) for x in ds], ctypes.c_float(scale),
                                     ctypes.c_void_p(_stream_handle(q))))

@@ -151,8 +151,8 @@ int plan_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, cons
     if (!shape_is(g, {B, T, Hv}) || !shape_is(beta, {B, T, Hv}))
         return fail(GDR_ESHAPE, "g and beta must be [B, T, Hv] = [%lld, %lld, %lld]", (long long)B,
                     (long long)T, (long long)Hv);
-    if (dk != dv) return fail(GDR_ESHAPE, "dk (%lld) must equal dv (%lld)", (long long)dk, (long long)dv);
-    if (dk != 64 && dk != 128) return fail(GDR_ESHAPE, "head dim must be 64 or 128, got %lld", (long long)dk);
+    if (dk != 64 && dk != 128) return fail(GDR_ESHAPE, "dk must be 64 or 128, got %lld", (long long)dk);
+    if (dv != 64 && dv != 128) return fail(GDR_ESHAPE, "dv must be 64 or 128, got %lld", (long long)dv);
     if (Hk < 1 || Hv < 1) return fail(GDR_ESHAPE, "head counts must be positive");
     if (Hv % Hk != 0)
         return fail(GDR_ESHAPE, "Hv (%lld) must be a multiple of Hk (%lld)", (long long)Hv, (long long)Hk);
@@ -192,6 +192,7 @@ int plan_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, cons
     p->hk = static_cast<int32_t>(Hk);
     p->hv = static_cast<int32_t>(Hv);
     p->d = static_cast<int32_t>(dk);
+    p->dv = static_cast<int32_t>(dv);
     p->in_dtype = q->dtype;
     p->gate_dtype = g->dtype;
     p->varlen = cu ? 1 : 0;
@@ -200,7 +201,8 @@ int plan_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, cons
     p->grid_fwd = N * Hv;
     const bool f32 = q->dtype == GDR_F32;   // f32 inputs: the token-serial fp32 kernel
     p->block_fwd = f32 ? gdr::kFwdF32Threads : gdr::kFwdThreads;
-    p->lds_fwd = f32 ? gdr::fwd_f32_lds_bytes(static_cast<int>(dk)) : gdr::fwd_lds_bytes(static_cast<int>(dk));
+    p->lds_fwd = f32 ? gdr::fwd_f32_lds_bytes(static_cast<int>(dk), static_cast<int>(dv))
+                     : gdr::fwd_lds_bytes(static_cast<int>(dk));
     p->workspace_bytes = cu ? 4 * N + 16 : 0;
     return GDR_OK;
 }
@@ -425,17 +427,17 @@ int check_cu_content(const int32_t *cu, int64_t n_seq, int64_t total, int32_t *r
 int order_groups(const gdr::FwdArgs &a, bool kda = false) {
     if (!a.in_bf16) return 0;   // f32 inputs run the token-serial kernel: longest first is enough
     static std::mutex mu;
-    static int cache[64][2][2][2][2];   // slots + 1; 0 unknown
+    static int cache[64][2][2][2][2][2];   // slots + 1; 0 unknown
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int &entry = cache[dev][kda ? 1 : 0][a.d == 64 ? 0 : 1][a.in_bf16 ? 1 : 0][a.gate_bf16 ? 1 : 0];
+    int &entry = cache[dev][kda ? 1 : 0][a.d == 64 ? 0 : 1][a.dv == 64 ? 0 : 1][a.in_bf16 ? 1 : 0][a.gate_bf16 ? 1 : 0];
     int slots = 0;
     {
         std::lock_guard<std::mutex> lock(mu);
         if (entry == 0) {
             int s = 0;
             const hipError_t e = kda ? gdr::kda_slots(a.d, a.in_bf16, a.gate_bf16, &s)
-                                     : gdr::fwd_slots(a.d, a.in_bf16, a.gate_bf16, &s);
+                                     : gdr::fwd_slots(a.d, a.dv, a.in_bf16, a.gate_bf16, &s);
             entry = e == hipSuccess ? s + 1 : 1;
         }
         slots = entry - 1;
@@ -464,9 +466,9 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
         if (hck->dtype != GDR_F32) return fail(GDR_EDTYPE, "h_chunks: dtype must be f32");
         const int64_t T = q->shape[1];
         rows = cu_seqlens ? (p.total_tokens + every - 1) / every + p.n_seq : q->shape[0] * ((T + every - 1) / every);
-        if (!shape_is(hck, {rows, p.hv, p.d, p.d}))
+        if (!shape_is(hck, {rows, p.hv, p.d, p.dv}))
             return fail(GDR_ESHAPE, "h_chunks: shape %s must be [%lld, Hv, dk, dv] = [%lld, %d, %d, %d] for pieces of %lld tokens",
-                        shape_str(hck).c_str(), (long long)rows, (long long)rows, p.hv, p.d, p.d, (long long)every);
+                        shape_str(hck).c_str(), (long long)rows, (long long)rows, p.hv, p.d, p.dv, (long long)every);
         const Span sck = span_of(hck, nck);
         const gdr_tensor *others[] = {q, k, v, g, beta, cu_seqlens, h0, o, ht};
         for (const gdr_tensor *t : others) {
@@ -508,6 +510,7 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     a.hk = p.hk;
     a.hv = p.hv;
     a.d = p.d;
+    a.dv = p.dv;
     a.in_bf16 = p.in_dtype == GDR_BF16;
     a.gate_bf16 = p.gate_dtype == GDR_BF16;
     a.scale = scale;
@@ -590,6 +593,8 @@ int run_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     gdr_launch_plan p;
     int rc = plan_fwd(q, k, v, g, beta, cu_seqlens, h0, dout, nullptr, scale, &p, "do");
     if (rc) return rc;
+    if (p.d != p.dv)
+        return fail(GDR_ESHAPE, "gdr_chunk_bwd needs dk == dv (got dk = %d, dv = %d)", p.d, p.dv);
     const int64_t B = q->shape[0], T = q->shape[1], N = p.n_seq, Hk = p.hk, Hv = p.hv, d = p.d;
     int64_t ndht = 0, ndq, ndk, ndv, ndg, ndb, ndh0 = 0;
     if (dht) {
@@ -664,6 +669,7 @@ int run_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
         fa.hk = p.hk;
         fa.hv = p.hv;
         fa.d = p.d;
+        fa.dv = p.dv;
         fa.in_bf16 = p.in_dtype == GDR_BF16;
         fa.gate_bf16 = p.gate_dtype == GDR_BF16;
         fa.scale = scale;
@@ -726,6 +732,8 @@ int run_kda(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     if ((rc = check_tensor(g, "g", 4, &ng, 4))) return rc;
     gdr_launch_plan p;
     if ((rc = plan_fwd(q, k, v, beta, beta, cu_seqlens, h0, o, ht, scale, &p))) return rc;
+    if (p.d != p.dv)
+        return fail(GDR_ESHAPE, "gdr_chunk_kda_fwd needs dk == dv (got dk = %d, dv = %d)", p.d, p.dv);
     if (g->dtype != beta->dtype) return fail(GDR_EDTYPE, "g and beta must share one dtype");
     const int64_t B = q->shape[0], T = q->shape[1];
     if (!shape_is(g, {B, T, p.hv, p.d}))
@@ -757,6 +765,7 @@ int run_kda(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
     a.hk = p.hk;
     a.hv = p.hv;
     a.d = p.d;
+    a.dv = p.dv;
     a.in_bf16 = p.in_dtype == GDR_BF16;
     a.gate_bf16 = p.gate_dtype == GDR_BF16;
     a.scale = scale;
@@ -848,19 +857,20 @@ int gdr_decode_step(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *
     if (beta->dtype != g->dtype) return fail(GDR_EDTYPE, "beta must have the dtype of g");
     if (h->dtype != GDR_F32) return fail(GDR_EDTYPE, "h: dtype must be f32");
     const int64_t B = q->shape[0], Hk = q->shape[1], d = q->shape[2];
-    const int64_t Hv = v->shape[1];
+    const int64_t Hv = v->shape[1], dv = v->shape[2];
     if (!shape_is(k, {B, Hk, d}))
         return fail(GDR_ESHAPE, "k: shape %s must equal q's %s", shape_str(k).c_str(), shape_str(q).c_str());
-    if (v->shape[0] != B || v->shape[2] != d)
-        return fail(GDR_ESHAPE, "v: shape %s must be [B, Hv, d] with q's B and d", shape_str(v).c_str());
-    if (!shape_is(o, {B, Hv, d}))
+    if (v->shape[0] != B)
+        return fail(GDR_ESHAPE, "v: shape %s must be [B, Hv, dv] with q's B", shape_str(v).c_str());
+    if (!shape_is(o, {B, Hv, dv}))
         return fail(GDR_ESHAPE, "o: shape %s must equal v's %s", shape_str(o).c_str(), shape_str(v).c_str());
     if (!shape_is(g, {B, Hv}) || !shape_is(beta, {B, Hv}))
         return fail(GDR_ESHAPE, "g and beta must be [B, Hv] = [%lld, %lld]", (long long)B, (long long)Hv);
-    if (!shape_is(h, {B, Hv, d, d}))
-        return fail(GDR_ESHAPE, "h: shape %s must be [B, Hv, d, d] = [%lld, %lld, %lld, %lld]",
-                    shape_str(h).c_str(), (long long)B, (long long)Hv, (long long)d, (long long)d);
-    if (d != 64 && d != 128) return fail(GDR_ESHAPE, "head dim must be 64 or 128, got %lld", (long long)d);
+    if (!shape_is(h, {B, Hv, d, dv}))
+        return fail(GDR_ESHAPE, "h: shape %s must be [B, Hv, dk, dv] = [%lld, %lld, %lld, %lld]",
+                    shape_str(h).c_str(), (long long)B, (long long)Hv, (long long)d, (long long)dv);
+    if (d != 64 && d != 128) return fail(GDR_ESHAPE, "dk must be 64 or 128, got %lld", (long long)d);
+    if (dv != 64 && dv != 128) return fail(GDR_ESHAPE, "dv must be 64 or 128, got %lld", (long long)dv);
     if (Hk < 1 || Hv < 1) return fail(GDR_ESHAPE, "head counts must be positive");
     if (Hv % Hk != 0)
         return fail(GDR_ESHAPE, "Hv (%lld) must be a multiple of Hk (%lld)", (long long)Hv, (long long)Hk);
@@ -887,6 +897,7 @@ int gdr_decode_step(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *
     a.hk = static_cast<int32_t>(Hk);
     a.hv = static_cast<int32_t>(Hv);
     a.d = static_cast<int32_t>(d);
+    a.dv = static_cast<int32_t>(dv);
     a.in_bf16 = q->dtype == GDR_BF16;
     a.gate_bf16 = g->dtype == GDR_BF16;
     a.scale = scale;
@@ -1071,7 +1082,7 @@ int gdr_free_workspaces(void) {
 
 const char *gdr_last_error(void) { return g_last_error.c_str(); }
 
-int gdr_version(void) { return 10200; }
+int gdr_version(void) { return 10300; }
 
 int gdr_selftest_mfma(const uint16_t *a, const uint16_t *b, float *c, hipStream_t stream) {
     if (!a || !b || !c) return fail(GDR_EINVAL, "selftest: NULL pointer");

@@ -18,7 +18,8 @@ struct FwdArgs {
     int64_t n_seq;          // N
     int64_t seq_len;        // T per row when cu == NULL
     int64_t total_tokens;   // rows of q/k/v/o (B * T); bounds every token index
-    int32_t hk, hv, d;
+    int32_t hk, hv, d;      // d: key head dim dk
+    int32_t dv;             // value head dim (64 or 128)
     int32_t in_bf16;        // q/k/v/o dtype: 1 bf16, 0 f32
     int32_t gate_bf16;      // g/beta dtype
     float scale;
@@ -68,19 +69,20 @@ struct DecodeArgs {
     float *h;               // [B, Hv, d, d] fp32, updated in place
     void *o;                // [B, Hv, d]
     int64_t batch;          // B
-    int32_t hk, hv, d;
+    int32_t hk, hv, d;      // d: key head dim dk
+    int32_t dv;             // value head dim
     int32_t in_bf16, gate_bf16;
     float scale;
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
-// Dynamic LDS bytes and threads per work-group of the fused forward kernel
-// (4 state-chain waves + 4 preparation waves).
-int fwd_lds_bytes(int d);
+// Dynamic LDS bytes (they depend on dk only) and threads per work-group of
+// the fused forward kernel (4 state-chain waves + 4 preparation waves).
+int fwd_lds_bytes(int dk);
 constexpr int kFwdThreads = 512;
 // Threads and static LDS bytes of the token-serial fp32 kernel (f32 inputs).
 constexpr int kFwdF32Threads = 256;
-int fwd_f32_lds_bytes(int d);
+int fwd_f32_lds_bytes(int dk, int dv);
 constexpr int kChunk = 64;
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
@@ -101,7 +103,7 @@ hipError_t launch_prepare(const int32_t *cu, int64_t n_seq, int32_t *chunk_offse
 hipError_t launch_order(const int32_t *cu, int64_t n_seq, int32_t groups, int32_t *order,
                         hipStream_t stream);
 // Work-groups of the fused forward kernel resident on the device at once.
-hipError_t fwd_slots(int d, int in_bf16, int gate_bf16, int *slots);
+hipError_t fwd_slots(int dk, int dv, int in_bf16, int gate_bf16, int *slots);
 // Work-groups of the per-channel-gate forward kernel resident at once.
 hipError_t kda_slots(int d, int in_bf16, int gate_bf16, int *slots);
 

@@ -97,13 +97,13 @@ namespace {
 // --------------------------------------------------------------------------
 __device__ __forceinline__ int pc(int x) { return (x & ~31) | ((x & 12) << 1) | ((x >> 2) & 4) | (x & 3); }
 
-template <int D>
+template <int DK>
 struct FwdLds {
-    // [64][D] bf16 rows: q and k, three buffers each (chunks c, c+1, c+2).
-    // The pitch (D + 16 elements) keeps both the 16-byte row-fragment reads
+    // [64][DK] bf16 rows: q and k, three buffers each (chunks c, c+1, c+2).
+    // The pitch (DK + 16 elements) keeps both the 16-byte row-fragment reads
     // and the transposing reads of k (4 rows x 32 bytes per 16 lanes) free of
     // bank conflicts.
-    static constexpr int PK = D + 16;
+    static constexpr int PK = DK + 16;
     static constexpr int PP = C + 8;    // [64][64] bf16, keys permuted: P and -A~ off the diagonal, two buffers each
     static constexpr int PAT = 16;      // [4][16][16] bf16: diagonal blocks of A, transposed (preparation only)
     static constexpr int PDI = 16;      // [4][16][16] bf16: scaled inverses of the diagonal blocks, two kinds x two buffers
@@ -125,14 +125,14 @@ struct FwdLds {
 
 
 // CK: chunk-boundary states not written (0), written fp32 (1) or bf16 (2).
-template <int D, bool IN_BF16, bool GATE_BF16, int CK>
+template <int DK, int DV, bool IN_BF16, bool GATE_BF16, int CK>
 __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
-    using Ly = FwdLds<D>;
+    using Ly = FwdLds<DK>;
     constexpr int PK = Ly::PK, PP = Ly::PP, PAT = Ly::PAT, PDI = Ly::PDI;
-    constexpr int DW = D / 4;      // state columns per chain wave
+    constexpr int DW = DV / 4;     // state columns per chain wave
     constexpr int NTW = DW / 16;   // 16-wide tiles of those
-    constexpr int KB = D / 16;     // K16 blocks over the head dim
-    constexpr int FG = D / 8;      // staging: 8-element feature groups per row
+    constexpr int KB = DK / 16;    // K16 blocks over the key head dim
+    constexpr int FG = DK / 8;     // staging: 8-element feature groups per row
     constexpr int TG = 256 / FG;   // staging: token groups over the 4 prep waves
     constexpr int TPT = C / TG;    // staging: tokens per prep thread
     static_assert(KB % 2 == 0 && NTW >= 1 && (TPT == 2 || TPT == 4), "unsupported head dim");
@@ -267,14 +267,14 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     uint4 pq[TPT], pk[TPT];   // q, k rows of the chunk to store next
     float pg = 0.f, pb = 0.f; // gate and beta of the next chunk to prepare (lane = token)
 
-    const int64_t sbase = (n * a.hv + h) * static_cast<int64_t>(D) * D;
+    const int64_t sbase = (n * a.hv + h) * static_cast<int64_t>(DK) * DV;
 
     // chain: v of chunk c as A fragments (rows past the segment end read as zero)
     auto load_v = [&](int64_t c) {
         const int64_t t0 = bos + c * C;
-        const uint32_t rowb = static_cast<uint32_t>(a.hv) * D * ES;
+        const uint32_t rowb = static_cast<uint32_t>(a.hv) * DV * ES;
         const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(
-            reinterpret_cast<const unsigned char *>(a.v) + ((t0 * a.hv + h) * D) * ES, chunk_len(c) * rowb);
+            reinterpret_cast<const unsigned char *>(a.v) + ((t0 * a.hv + h) * DV) * ES, chunk_len(c) * rowb);
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
             const uint32_t off = (16 * blk + l16) * rowb + (colw + 4 * NTW * lq) * ES;
@@ -295,8 +295,8 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         const int64_t t0 = bos + c * C;
         const int L = chunk_len(c);
         const int pt = tid - 256, fg = pt % FG, tg = pt / FG;
-        const uint32_t rowb = static_cast<uint32_t>(a.hk) * D * ES;
-        const int64_t base = (t0 * a.hk + hk) * D * ES;
+        const uint32_t rowb = static_cast<uint32_t>(a.hk) * DK * ES;
+        const int64_t base = (t0 * a.hk + hk) * DK * ES;
         const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(reinterpret_cast<const unsigned char *>(a.q) + base, L * rowb);
         const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(reinterpret_cast<const unsigned char *>(a.k) + base, L * rowb);
 #pragma unroll
@@ -521,9 +521,9 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         // needs Vnew of blocks <= a only, and its H^T Q^T products do not
         // depend on the substitution, so they fill its dependency gaps.
         const int L = chunk_len(c);
-        const uint32_t rowb = static_cast<uint32_t>(a.hv) * D * ES;
+        const uint32_t rowb = static_cast<uint32_t>(a.hv) * DV * ES;
         const __amdgpu_buffer_rsrc_t ro = chunk_rsrc(   // an empty range when o is not wanted
-            reinterpret_cast<unsigned char *>(a.o) + (((bos + c * C) * a.hv + h) * D) * ES, a.o ? L * rowb : 0u);
+            reinterpret_cast<unsigned char *>(a.o) + (((bos + c * C) * a.hv + h) * DV) * ES, a.o ? L * rowb : 0u);
         bf16x4 Xb[4][NTW], Vt[4][NTW];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
@@ -594,8 +594,8 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 
         // lane part of the offset of a checkpoint store (plain [dk][dv] fp32);
         // tile (kb, nt) element r adds ck_cst(kb, nt, r) as the scalar offset
-        const uint32_t ck_lane_off = (dk_of(0, 4 * lq) * D + dv_of(0, l16)) * 4;
-        auto ck_cst = [&](int kb, int nt, int r) { return static_cast<uint32_t>(((dk_of(kb, r) - dk_of(0, 0)) * D + 4 * nt) * 4); };
+        const uint32_t ck_lane_off = (dk_of(0, 4 * lq) * DV + dv_of(0, l16)) * 4;
+        auto ck_cst = [&](int kb, int nt, int r) { return static_cast<uint32_t>(((dk_of(kb, r) - dk_of(0, 0)) * DV + 4 * nt) * 4); };
         // the K^T fragments of the state update: transposing reads of the k
         // rows, lane (l16, lq) of tile kb gets k[32p' + 4lq + r][dk_of(kb, l16)]
         // (and tokens +16 for slots 4-7)
@@ -629,7 +629,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 }
                 const float eg = fast_exp2(gp);
                 const bf16x4 z4 = cvt4(zero4());
-                const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(a.hck + (row * a.hv + h) * D * D, D * D * 4);
+                const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(a.hck + (row * a.hv + h) * DK * DV, DK * DV * 4);
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
                     const bf16x8 a01 = kt_frag(kb, 0);
@@ -679,7 +679,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 if constexpr (CK == 2) {
                     // bf16 in tile order: a lane's four values of tile (kb, nt)
                     // as one 8-byte piece, 512 contiguous bytes per store
-                    const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(a.hck16 + (row * a.hv + h) * D * D, D * D * 2);
+                    const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(a.hck16 + (row * a.hv + h) * DK * DV, DK * DV * 2);
                     const uint32_t lane_off = (role * KB * NTW * 64 + lane) * 8;
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb)
@@ -688,7 +688,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, cvt4(hs[kb][nt])), rd,
                                                                   lane_off, (kb * NTW + nt) * 64 * 8, 0);
                 } else {
-                    const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(a.hck + (row * a.hv + h) * D * D, D * D * 4);
+                    const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(a.hck + (row * a.hv + h) * DK * DV, DK * DV * 4);
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -725,7 +725,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    hs[kb][nt][r] = a.h0 ? a.h0[sbase + dk_of(kb, 4 * lq + r) * D + dv_of(nt, l16)] : 0.f;
+                    hs[kb][nt][r] = a.h0 ? a.h0[sbase + dk_of(kb, 4 * lq + r) * DV + dv_of(nt, l16)] : 0.f;
         load_v(0);
         wait_for(cPrep, 4u, peek(cPrep));   // q, k of chunk 0 stored
         int b3 = 0;
@@ -743,7 +743,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        a.ht[sbase + dk_of(kb, 4 * lq + r) * D + dv_of(nt, l16)] = bad ? poison : hs[kb][nt][r];
+                        a.ht[sbase + dk_of(kb, 4 * lq + r) * DV + dv_of(nt, l16)] = bad ? poison : hs[kb][nt][r];
         }
     } else {
         load_qk(0);
@@ -794,19 +794,19 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 // ck_every tokens and after the sequence's last token, as the fused
 // kernel's checkpoint mode does.  No exponent folding: any g <= 0 is in range.
 // --------------------------------------------------------------------------
-template <int D>
+template <int DK, int DV>
 struct F32Shape {
-    static constexpr int CG = D / 4;                    // column groups of 4
+    static constexpr int CG = DV / 4;                   // column groups of 4
     static constexpr int RG = kFwdF32Threads / CG;      // row groups
-    static constexpr int RPT = D / RG;                  // rows per thread
-    static constexpr int lds_bytes = 4 * (2 * RG * D + 3 * D + 1);   // scalar gates
+    static constexpr int RPT = DK / RG;                 // rows per thread
+    static constexpr int lds_bytes = 4 * (2 * RG * DV + 2 * DK + DV + 1);   // scalar gates
 };
 
-template <int D, bool GATE_BF16, bool PER_CHANNEL, int CK>
+template <int DK, int DV, bool GATE_BF16, bool PER_CHANNEL, int CK>
 __global__ void __launch_bounds__(kFwdF32Threads) gdr_fwd_f32_kernel(FwdArgs a) {
-    constexpr int CG = F32Shape<D>::CG, RG = F32Shape<D>::RG, RPT = F32Shape<D>::RPT;
-    __shared__ float s_part[2][RG][D];
-    __shared__ float s_k[D], s_q[D], s_v[D], s_a[PER_CHANNEL ? D : 1];
+    constexpr int CG = F32Shape<DK, DV>::CG, RG = F32Shape<DK, DV>::RG, RPT = F32Shape<DK, DV>::RPT;
+    __shared__ float s_part[2][RG][DV];
+    __shared__ float s_k[DK], s_q[DK], s_v[DV], s_a[PER_CHANNEL ? DK : 1];
 
     const int64_t item = blockIdx.x;
     const int64_t rank = item / a.hv;
@@ -831,7 +831,7 @@ __global__ void __launch_bounds__(kFwdF32Threads) gdr_fwd_f32_kernel(FwdArgs a) 
     const float *kf = static_cast<const float *>(a.k);
     const float *vf = static_cast<const float *>(a.v);
     float *of = static_cast<float *>(a.o);
-    const int64_t sbase = (n * a.hv + h) * static_cast<int64_t>(D) * D;
+    const int64_t sbase = (n * a.hv + h) * static_cast<int64_t>(DK) * DV;
     const int64_t ck_unit = a.ck_every > 0 ? static_cast<int64_t>(a.ck_every) : C;   // checkpoint every ck_unit tokens
     const int64_t ck_base = CK == 0 ? 0
                           : a.ck_offs ? static_cast<int64_t>(a.ck_offs[n])
@@ -847,29 +847,29 @@ __global__ void __launch_bounds__(kFwdF32Threads) gdr_fwd_f32_kernel(FwdArgs a) 
     };
     f32x4 H[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) H[i] = a.h0 ? ld4(a.h0 + sbase + (i0 + i) * D + j0) : zero4();
+    for (int i = 0; i < RPT; ++i) H[i] = a.h0 ? ld4(a.h0 + sbase + (i0 + i) * DV + j0) : zero4();
 
-    // token `tok`'s inputs in registers: x = (k, q, v, per-channel log-decay)
-    // element t of the row for t < D; lg, lb the scalar gate and beta
+    // token `tok`'s inputs in registers: element t of the rows of k, q and the
+    // per-channel log-decay (t < DK) and of v (t < DV); lg, lb the scalar gate and beta
     float xk = 0.f, xq = 0.f, xv = 0.f, xg = 0.f, lg = 0.f, lb = 0.f;
     auto fetch = [&](int64_t tok) {
-        if (t < D) {
-            xk = kf[(tok * a.hk + hk) * D + t];
-            xq = qf[(tok * a.hk + hk) * D + t];
-            xv = vf[(tok * a.hv + h) * D + t];
-            if constexpr (PER_CHANNEL) xg = load_scalar<GATE_BF16>(a.g, (tok * a.hv + h) * D + t);
+        if (t < DK) {
+            xk = kf[(tok * a.hk + hk) * DK + t];
+            xq = qf[(tok * a.hk + hk) * DK + t];
+            if constexpr (PER_CHANNEL) xg = load_scalar<GATE_BF16>(a.g, (tok * a.hv + h) * DK + t);
         }
+        if (t < DV) xv = vf[(tok * a.hv + h) * DV + t];
         if constexpr (!PER_CHANNEL) lg = load_scalar<GATE_BF16>(a.g, tok * a.hv + h);
         lb = load_scalar<GATE_BF16>(a.beta, tok * a.hv + h);
     };
     fetch(bos);
     for (int64_t tok = bos; tok < eos; ++tok) {
-        if (t < D) {
+        if (t < DK) {
             s_k[t] = xk;
             s_q[t] = xq;
-            s_v[t] = xv;
             if constexpr (PER_CHANNEL) s_a[t] = __expf(xg);
         }
+        if (t < DV) s_v[t] = xv;
         const float gate = PER_CHANNEL ? 1.f : __expf(lg);
         const float beta = lb;
         __syncthreads();   // (A) the token's inputs are in LDS
@@ -901,7 +901,7 @@ __global__ void __launch_bounds__(kFwdF32Threads) gdr_fwd_f32_kernel(FwdArgs a) 
             f32x4 o = zero4();
 #pragma unroll
             for (int r = 0; r < RG; ++r) o = o + *reinterpret_cast<const f32x4 *>(&s_part[1][r][j0]);
-            *reinterpret_cast<f32x4 *>(of + (tok * a.hv + h) * D + j0) = o * a.scale;
+            *reinterpret_cast<f32x4 *>(of + (tok * a.hv + h) * DV + j0) = o * a.scale;
         }
         if constexpr (CK == 1) {
             // after P tokens: the last row when the sequence ends, else a row
@@ -911,16 +911,16 @@ __global__ void __launch_bounds__(kFwdF32Threads) gdr_fwd_f32_kernel(FwdArgs a) 
                               : P % ck_unit == 0 ? ck_base + P / ck_unit - 1 : -1;
             {
                 if (row >= 0 && row < a.ck_rows) {
-                    float *dst = a.hck + (row * a.hv + h) * static_cast<int64_t>(D) * D;
+                    float *dst = a.hck + (row * a.hv + h) * static_cast<int64_t>(DK) * DV;
 #pragma unroll
-                    for (int i = 0; i < RPT; ++i) st4(dst + (i0 + i) * D + j0, H[i]);
+                    for (int i = 0; i < RPT; ++i) st4(dst + (i0 + i) * DV + j0, H[i]);
                 }
             }
         }
     }
     if (a.ht) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) st4(a.ht + sbase + (i0 + i) * D + j0, H[i]);
+        for (int i = 0; i < RPT; ++i) st4(a.ht + sbase + (i0 + i) * DV + j0, H[i]);
     }
 }
 
@@ -1171,13 +1171,13 @@ __global__ void __launch_bounds__(256) gdr_cumsum_kernel(const void *g, const in
 // 4cg..4cg+3 of rows RPT*rg .. +RPT-1 in registers (16-byte loads and stores);
 // the column sums over rows go through LDS.
 // --------------------------------------------------------------------------
-template <int D, bool IN_BF16, bool GATE_BF16>
+template <int DK, int DV, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(256) gdr_decode_kernel(DecodeArgs a) {
-    constexpr int CG = D / 4;       // column groups of 4
+    constexpr int CG = DV / 4;      // column groups of 4
     constexpr int RG = 256 / CG;    // row groups
-    constexpr int RPT = D / RG;     // rows per thread
-    __shared__ float s_part[RG][D];
-    __shared__ float s_k[D], s_q[D];
+    constexpr int RPT = DK / RG;    // rows per thread
+    __shared__ float s_part[RG][DV];
+    __shared__ float s_k[DK], s_q[DK];
     const int64_t item = blockIdx.x;
     const int64_t b = item / a.hv;
     const int h = static_cast<int>(item % a.hv);
@@ -1185,16 +1185,16 @@ __global__ void __launch_bounds__(256) gdr_decode_kernel(DecodeArgs a) {
     const int t = threadIdx.x, cg = t % CG, rg = t / CG;
     const int j0 = 4 * cg, i0 = RPT * rg;
 
-    if (t < D) {
-        s_k[t] = load_scalar<IN_BF16>(a.k, (b * a.hk + hk) * D + t);
-        s_q[t] = load_scalar<IN_BF16>(a.q, (b * a.hk + hk) * D + t);
+    if (t < DK) {
+        s_k[t] = load_scalar<IN_BF16>(a.k, (b * a.hk + hk) * DK + t);
+        s_q[t] = load_scalar<IN_BF16>(a.q, (b * a.hk + hk) * DK + t);
     }
     const float gate = __expf(load_scalar<GATE_BF16>(a.g, b * a.hv + h));
     const float beta = load_scalar<GATE_BF16>(a.beta, b * a.hv + h);
-    float *hp = a.h + (b * a.hv + h) * D * D;
+    float *hp = a.h + (b * a.hv + h) * DK * DV;
     f32x4 H[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) H[i] = *reinterpret_cast<const f32x4 *>(hp + (i0 + i) * D + j0);
+    for (int i = 0; i < RPT; ++i) H[i] = *reinterpret_cast<const f32x4 *>(hp + (i0 + i) * DV + j0);
     __syncthreads();
 
     // p = H^T k (before the decay, which is applied to the sum)
@@ -1208,7 +1208,7 @@ __global__ void __launch_bounds__(256) gdr_decode_kernel(DecodeArgs a) {
     for (int r = 0; r < RG; ++r) p = p + *reinterpret_cast<const f32x4 *>(&s_part[r][j0]);
     f32x4 vj;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) vj[c] = load_scalar<IN_BF16>(a.v, (b * a.hv + h) * D + j0 + c);
+    for (int c = 0; c < 4; ++c) vj[c] = load_scalar<IN_BF16>(a.v, (b * a.hv + h) * DV + j0 + c);
     const f32x4 dlt = (vj - p * gate) * beta;
 
     // H <- e^g H + k d^T, stored; o partial = H^T q
@@ -1216,7 +1216,7 @@ __global__ void __launch_bounds__(256) gdr_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         H[i] = H[i] * gate + dlt * s_k[i0 + i];
-        *reinterpret_cast<f32x4 *>(hp + (i0 + i) * D + j0) = H[i];
+        *reinterpret_cast<f32x4 *>(hp + (i0 + i) * DV + j0) = H[i];
         po = po + H[i] * s_q[i0 + i];
     }
     __syncthreads();   // every thread has read s_part
@@ -1227,7 +1227,7 @@ __global__ void __launch_bounds__(256) gdr_decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < RG; ++r) o = o + *reinterpret_cast<const f32x4 *>(&s_part[r][j0]);
         o = o * a.scale;
-        const int64_t oo = (b * a.hv + h) * D + j0;
+        const int64_t oo = (b * a.hv + h) * DV + j0;
         if constexpr (IN_BF16) {
             *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(a.o) + oo) = cvt4(o);
         } else {
@@ -1303,17 +1303,18 @@ __global__ void __launch_bounds__(64) gdr_selftest_kernel(const uint16_t *a, con
     }
 }
 
-template <int D, bool IN_BF16, bool GATE_BF16>
+template <int DK, int DV, bool IN_BF16, bool GATE_BF16>
 hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     // f32 inputs reach the fused kernel only for the backward's bf16 state
-    // recompute (hck16); their other calls run the fp32 kernel
-    void (*kern)(FwdArgs) = gdr_fwd_kernel<D, IN_BF16, GATE_BF16, 2>;
-    if constexpr (IN_BF16) {
-        if (!a.hck16) kern = a.hck ? gdr_fwd_kernel<D, true, GATE_BF16, 1> : gdr_fwd_kernel<D, true, GATE_BF16, 0>;
-    } else if (!a.hck16) {
-        return hipErrorInvalidValue;
+    // recompute (hck16, dk == dv); their other calls run the fp32 kernel
+    void (*kern)(FwdArgs) = nullptr;
+    if (a.hck16) {
+        if constexpr (DK == DV) kern = gdr_fwd_kernel<DK, DV, IN_BF16, GATE_BF16, 2>;
+    } else if constexpr (IN_BF16) {
+        kern = a.hck ? gdr_fwd_kernel<DK, DV, true, GATE_BF16, 1> : gdr_fwd_kernel<DK, DV, true, GATE_BF16, 0>;
     }
-    const int lds = FwdLds<D>::bytes;
+    if (!kern) return hipErrorInvalidValue;
+    const int lds = FwdLds<DK>::bytes;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
@@ -1322,42 +1323,54 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, bool GATE_BF16, bool PER_CHANNEL>
+template <int DK, int DV, bool GATE_BF16, bool PER_CHANNEL>
 hipError_t launch_fwd_f32_t(const FwdArgs &a, hipStream_t stream) {
-    auto kern = a.hck ? gdr_fwd_f32_kernel<D, GATE_BF16, PER_CHANNEL, 1>
-                      : gdr_fwd_f32_kernel<D, GATE_BF16, PER_CHANNEL, 0>;
+    auto kern = a.hck ? gdr_fwd_f32_kernel<DK, DV, GATE_BF16, PER_CHANNEL, 1>
+                      : gdr_fwd_f32_kernel<DK, DV, GATE_BF16, PER_CHANNEL, 0>;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(a.n_seq * a.hv)), dim3(kFwdF32Threads), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int D, bool PER_CHANNEL>
+template <int DK, int DV, bool PER_CHANNEL>
 hipError_t launch_fwd_f32_d(const FwdArgs &a, hipStream_t s) {
-    return a.gate_bf16 ? launch_fwd_f32_t<D, true, PER_CHANNEL>(a, s) : launch_fwd_f32_t<D, false, PER_CHANNEL>(a, s);
+    return a.gate_bf16 ? launch_fwd_f32_t<DK, DV, true, PER_CHANNEL>(a, s)
+                       : launch_fwd_f32_t<DK, DV, false, PER_CHANNEL>(a, s);
 }
 
-template <int D>
+template <int DK, int DV>
 hipError_t launch_fwd_d(const FwdArgs &a, hipStream_t s) {
-    if (a.in_bf16) return a.gate_bf16 ? launch_fwd_t<D, true, true>(a, s) : launch_fwd_t<D, true, false>(a, s);
+    if (a.in_bf16) return a.gate_bf16 ? launch_fwd_t<DK, DV, true, true>(a, s) : launch_fwd_t<DK, DV, true, false>(a, s);
     // f32 inputs: fp32 arithmetic; the backward pass's bf16 state recompute (hck16) keeps the fused kernel
-    if (!a.hck16) return launch_fwd_f32_d<D, false>(a, s);
-    return a.gate_bf16 ? launch_fwd_t<D, false, true>(a, s) : launch_fwd_t<D, false, false>(a, s);
+    if (!a.hck16) return launch_fwd_f32_d<DK, DV, false>(a, s);
+    return a.gate_bf16 ? launch_fwd_t<DK, DV, false, true>(a, s) : launch_fwd_t<DK, DV, false, false>(a, s);
+}
+
+// Calls f.template operator()<DK, DV>() for the head dims (each 64 or 128).
+template <typename F>
+hipError_t by_dims(int dk, int dv, F &&f) {
+    if (dk == 64) return dv == 64 ? f.template operator()<64, 64>() : f.template operator()<64, 128>();
+    return dv == 64 ? f.template operator()<128, 64>() : f.template operator()<128, 128>();
 }
 
 }  // namespace
 
-int fwd_lds_bytes(int d) { return d == 64 ? FwdLds<64>::bytes : FwdLds<128>::bytes; }
-int fwd_f32_lds_bytes(int d) { return d == 64 ? F32Shape<64>::lds_bytes : F32Shape<128>::lds_bytes; }
+int fwd_lds_bytes(int dk) { return dk == 64 ? FwdLds<64>::bytes : FwdLds<128>::bytes; }
+int fwd_f32_lds_bytes(int dk, int dv) {
+    if (dk == 64) return dv == 64 ? F32Shape<64, 64>::lds_bytes : F32Shape<64, 128>::lds_bytes;
+    return dv == 64 ? F32Shape<128, 64>::lds_bytes : F32Shape<128, 128>::lds_bytes;
+}
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream) {
     if (a.n_seq == 0 || a.hv == 0) return hipSuccess;
-    return a.d == 64 ? launch_fwd_d<64>(a, stream) : launch_fwd_d<128>(a, stream);
+    return by_dims(a.d, a.dv, [&]<int DK, int DV>() { return launch_fwd_d<DK, DV>(a, stream); });
 }
 
 hipError_t launch_fwd_f32(const FwdArgs &a, bool per_channel, hipStream_t stream) {
     if (a.n_seq == 0 || a.hv == 0) return hipSuccess;
     if (a.in_bf16 || a.hck16) return hipErrorInvalidValue;
-    if (per_channel) return a.d == 64 ? launch_fwd_f32_d<64, true>(a, stream) : launch_fwd_f32_d<128, true>(a, stream);
-    return a.d == 64 ? launch_fwd_f32_d<64, false>(a, stream) : launch_fwd_f32_d<128, false>(a, stream);
+    return by_dims(a.d, a.dv, [&]<int DK, int DV>() {
+        return per_channel ? launch_fwd_f32_d<DK, DV, true>(a, stream) : launch_fwd_f32_d<DK, DV, false>(a, stream);
+    });
 }
 
 hipError_t launch_prepare(const int32_t *cu, int64_t n_seq, int32_t *chunk_offsets, int32_t *chunk_map,
@@ -1374,20 +1387,19 @@ hipError_t launch_order(const int32_t *cu, int64_t n_seq, int32_t groups, int32_
     return hipGetLastError();
 }
 
-hipError_t fwd_slots(int d, int in_bf16, int gate_bf16, int *slots) {
+hipError_t fwd_slots(int d, int dv, int in_bf16, int gate_bf16, int *slots) {
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     // only bf16 inputs run the fused kernel without checkpoints (f32 inputs run the fp32 kernel)
     if (!in_bf16) return hipErrorInvalidValue;
-    const void *kern;
-    if (d == 64)
-        kern = gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, true, 0>)
-                         : reinterpret_cast<const void *>(gdr_fwd_kernel<64, true, false, 0>);
-    else
-        kern = gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, true, 0>)
-                         : reinterpret_cast<const void *>(gdr_fwd_kernel<128, true, false, 0>);
+    const void *kern = nullptr;
+    (void)by_dims(d, dv, [&]<int DK, int DV>() {
+        kern = gate_bf16 ? reinterpret_cast<const void *>(gdr_fwd_kernel<DK, DV, true, true, 0>)
+                         : reinterpret_cast<const void *>(gdr_fwd_kernel<DK, DV, true, false, 0>);
+        return hipSuccess;
+    });
     const int lds = fwd_lds_bytes(d);
     if ((e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFwdThreads, lds)) != hipSuccess) return e;
@@ -1409,22 +1421,22 @@ hipError_t launch_cumsum(const void *g, int gate_bf16, const int32_t *cu, const 
     return hipGetLastError();
 }
 
-template <int D>
+template <int DK, int DV>
 hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.batch * a.hv)), block(256);
     if (a.in_bf16) {
-        if (a.gate_bf16) hipLaunchKernelGGL((gdr_decode_kernel<D, true, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gdr_decode_kernel<D, true, false>), grid, block, 0, s, a);
+        if (a.gate_bf16) hipLaunchKernelGGL((gdr_decode_kernel<DK, DV, true, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gdr_decode_kernel<DK, DV, true, false>), grid, block, 0, s, a);
     } else {
-        if (a.gate_bf16) hipLaunchKernelGGL((gdr_decode_kernel<D, false, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gdr_decode_kernel<D, false, false>), grid, block, 0, s, a);
+        if (a.gate_bf16) hipLaunchKernelGGL((gdr_decode_kernel<DK, DV, false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gdr_decode_kernel<DK, DV, false, false>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     if (a.batch == 0 || a.hv == 0) return hipSuccess;
-    return a.d == 64 ? launch_decode_d<64>(a, stream) : launch_decode_d<128>(a, stream);
+    return by_dims(a.d, a.dv, [&]<int DK, int DV>() { return launch_decode_d<DK, DV>(a, stream); });
 }
 
 hipError_t launch_selftest_mfma(const uint16_t *a, const uint16_t *b, float *c, hipStream_t stream) {

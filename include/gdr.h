@@ -94,7 +94,7 @@ typedef struct {
  *   scale       output scale (callers usually pass dk^-0.5).
  *   stream      HIP stream the work is enqueued on.
  *
- * Constraints: dk == dv, dk in {64, 128}; Hv % Hk == 0 and v-head h reads
+ * Constraints: dk and dv each 64 or 128 (independently); Hv % Hk == 0 and v-head h reads
  * q/k head h / (Hv / Hk); all tensors compact row-major.  o and ht must not
  * overlap any input or each other.  The current device must be gfx950.
  *
@@ -247,7 +247,9 @@ int gdr_chunk_fwd_checkpoints_n(const gdr_tensor *q, const gdr_tensor *k, const 
  * R * Hv * (4 d^2 + 384 d + 8192) bytes plus 4 (2N + 1 + 2R) for the
  * chunk indices, R = ceil(T/64) + N with cu_seqlens else B * ceil(T/64).
  * About 4.1 GB for 65536 tokens, 32 v-heads, d = 128.  Errors as
- * gdr_chunk_fwd, with GDR_ENOMEM when the workspace cannot be obtained.
+ * gdr_chunk_fwd, with GDR_ENOMEM when the workspace cannot be obtained, and
+ * GDR_ESHAPE unless dk == dv (the backward kernels are written for square
+ * states).
  */
 int gdr_chunk_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const gdr_tensor *g,
                   const gdr_tensor *beta, const gdr_tensor *cu_seqlens, const gdr_tensor *h0,
@@ -269,7 +271,7 @@ int gdr_chunk_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,
  *   beta   [B, T, Hv]       same dtype as g
  *
  * Everything else (shapes, varlen and ghosts, h0/ht, GQA, errors) is
- * gdr_chunk_fwd.  bf16 inputs: within one 64-token chunk the gates are
+ * gdr_chunk_fwd, except that dk must equal dv (GDR_ESHAPE otherwise).  bf16 inputs: within one 64-token chunk the gates are
  * folded into the operands with one reference per block of 16 tokens, so a
  * channel's log-decay summed over 16 tokens must stay above about -87 (fp32
  * exponent range), about -5.4 per token: this holds the pages' safe-gate
@@ -294,15 +296,15 @@ int gdr_chunk_kda_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor
  * state H = S^T [dk][dv] of sequence b and v-head h:
  *     H <- e^g H,  d = beta (v - H^T k),  H <- H + k d^T,  o = scale H^T q.
  *
- *   q, k   [B, Hk, d]   bf16 or f32 (one dtype with v and o)
- *   v      [B, Hv, d]
+ *   q, k   [B, Hk, dk]  bf16 or f32 (one dtype with v and o)
+ *   v      [B, Hv, dv]
  *   g, beta [B, Hv]     bf16 or f32 (g is the log-gate of the token)
- *   h      [B, Hv, d, d] fp32, read and overwritten with the new state
- *   o      [B, Hv, d]   out, rounded once to its dtype
+ *   h      [B, Hv, dk, dv] fp32, read and overwritten with the new state
+ *   o      [B, Hv, dv]  out, rounded once to its dtype
  *   scale  as gdr_chunk_fwd
  *
- * d in {64, 128}; Hv % Hk == 0 (v-head h reads q/k head h / (Hv/Hk)).  fp32
- * arithmetic throughout.  No workspace.  HBM bound: 8 * d * d bytes of state
+ * dk and dv each 64 or 128; Hv % Hk == 0 (v-head h reads q/k head h / (Hv/Hk)).  fp32
+ * arithmetic throughout.  No workspace.  HBM bound: 8 * dk * dv bytes of state
  * traffic per (sequence, v-head).  Errors: GDR_ESHAPE, GDR_EDTYPE, GDR_EINVAL
  * (alignment: q/k/v 8 bytes, h and o 16 bytes; scale), GDR_EALIAS (o or h
  * overlaps an input or each other), GDR_EDEVICE, GDR_ELAUNCH.
@@ -333,7 +335,7 @@ typedef struct {
     int64_t n_seq;          /* N */
     int64_t total_tokens;   /* B * T */
     int64_t nt_max;         /* upper bound on the number of 64-token chunks: ceil(B*T/64) + N */
-    int32_t hk, hv, d;      /* heads and head dim (dk == dv == d) */
+    int32_t hk, hv, d;      /* heads and the key head dim dk */
     int32_t in_dtype;       /* gdr_dtype of q/k/v/o */
     int32_t gate_dtype;     /* gdr_dtype of g/beta */
     int32_t varlen;         /* 1 when cu_seqlens is given */
@@ -342,6 +344,7 @@ typedef struct {
     int32_t block_fwd;      /* threads per work-group: 512 (bf16 inputs), 256 (f32) */
     int32_t lds_fwd;        /* bytes of LDS per work-group */
     int64_t workspace_bytes;/* device workspace per call: 4*N + 16 with cu_seqlens */
+    int32_t dv;             /* the value head dim */
 } gdr_launch_plan;
 
 int gdr_plan(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v,

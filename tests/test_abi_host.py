@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == set(gdr.EXPORTS), declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.gdr_version() == 10200
+    assert lib.gdr_version() == 10300
 
 
 def test_exports_match_nm():
@@ -417,3 +417,68 @@ def test_validation_precedes_forced_launch_failure(lib):
 def test_device_status_argument_check(lib):
     assert lib.gdr_device_status(None, 0) == -1
     assert b"bits is NULL" in lib.gdr_last_error()
+
+
+# --- independent key and value head dims -----------------------------------------
+
+def _far():
+    A = Alloc()
+    A.next = 1 << 44   # addresses disjoint from the helpers' allocations
+    return A
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128)])
+def test_plan_independent_head_dims(lib, dk, dv):
+    """dk and dv are each 64 or 128: v, o [.., dv], h0 and ht [N, Hv, dk, dv]."""
+    A = _far()
+    d = fwd_descs(d=dk)
+    d.update(v=A(GDR_BF16, [1, 256, 4, dv]), o=A(GDR_BF16, [1, 256, 4, dv]),
+             h0=A(GDR_F32, [3, 4, dk, dv]), ht=A(GDR_F32, [3, 4, dk, dv]))
+    p = gdr.plan(**d)
+    assert p["d"] == dk and p["dv"] == dv and p["block_fwd"] == 512
+    d.update(ht=A(GDR_F32, [3, 4, dv, dk]))
+    with pytest.raises(gdr.GdrError) as e:
+        gdr.plan(**d)
+    assert e.value.status == -2 and "ht: shape" in e.value.message
+    # f32 inputs: the token-serial kernel's static LDS for these dims
+    d = fwd_descs(d=dk, dt=GDR_F32)
+    d.update(v=A(GDR_F32, [1, 256, 4, dv]), o=A(GDR_F32, [1, 256, 4, dv]),
+             h0=A(GDR_F32, [3, 4, dk, dv]), ht=A(GDR_F32, [3, 4, dk, dv]))
+    p = gdr.plan(**d)
+    rg = 256 // (dv // 4)
+    assert p["block_fwd"] == 256 and p["lds_fwd"] == 4 * (2 * rg * dv + 2 * dk + dv + 1)
+    d.update(v=A(GDR_F32, [1, 256, 4, 96]), o=A(GDR_F32, [1, 256, 4, 96]))
+    with pytest.raises(gdr.GdrError) as e:
+        gdr.plan(**d)
+    assert "dv must be 64 or 128" in e.value.message
+
+
+def test_mixed_head_dims_pass_validation_of_fwd_checkpoints_and_decode(lib):
+    A = _far()
+    d = fwd_descs(d=128)
+    d.update(v=A(GDR_BF16, [1, 256, 4, 64]), o=A(GDR_BF16, [1, 256, 4, 64]),
+             h0=A(GDR_F32, [3, 4, 128, 64]), ht=A(GDR_F32, [3, 4, 128, 64]))
+    args = [d[n] for n in ("q", "k", "v", "g", "beta", "cu_seqlens", "h0", "o", "ht")]
+    refs = [None if x is None else x.ref for x in args]
+    assert lib.gdr_chunk_fwd(*refs, ctypes.c_float(0.1), None) == -6   # valid; no device here
+    hck = A(GDR_F32, [(256 + 15) // 16 + 3, 4, 128, 64])
+    assert lib.gdr_chunk_fwd_checkpoints_n(*refs, hck.ref, ctypes.c_int64(16), ctypes.c_float(0.1), None) == -6
+    dd = dec_descs()
+    dd.update(v=A(GDR_BF16, [3, 4, 64]), o=A(GDR_BF16, [3, 4, 64]), h=A(GDR_F32, [3, 4, 128, 64]))
+    assert _dec_call(lib, dd) == -6
+    dd.update(h=A(GDR_F32, [3, 4, 64, 128]))
+    assert _dec_call(lib, dd) == -2 and "h: shape" in lib.gdr_last_error().decode()
+
+
+def test_bwd_and_kda_need_square_states(lib):
+    A = _far()
+    d = bwd_descs()
+    d.update(v=A(GDR_BF16, [1, 256, 4, 64]), do=A(GDR_BF16, [1, 256, 4, 64]),
+             h0=A(GDR_F32, [3, 4, 128, 64]))
+    assert _bwd_call(lib, d) == -2
+    assert "dk == dv" in lib.gdr_last_error().decode()
+    k = kda_descs()
+    k.update(v=A(GDR_BF16, [1, 256, 4, 64]), o=A(GDR_BF16, [1, 256, 4, 64]),
+             h0=A(GDR_F32, [3, 4, 128, 64]), ht=A(GDR_F32, [3, 4, 128, 64]))
+    assert _kda_call(lib, k) == -2
+    assert "dk == dv" in lib.gdr_last_error().decode()

@@ -27,9 +27,9 @@ def _run(t, d, rows, sentinel=7.0):
     import chunked_gated_delta_fwd_amd as gdr
     cu = t["cu"]
     N = (cu.shape[0] - 1) if cu is not None else t["q"].shape[0]
-    hv, dk = t["v"].shape[2], t["q"].shape[3]
-    hck = torch.full((rows, hv, dk, dk), sentinel, dtype=torch.float32, device="cuda")
-    ht = torch.zeros((N, hv, dk, dk), dtype=torch.float32, device="cuda")
+    hv, dk, dv = t["v"].shape[2], t["q"].shape[3], t["v"].shape[3]
+    hck = torch.full((rows, hv, dk, dv), sentinel, dtype=torch.float32, device="cuda")
+    ht = torch.zeros((N, hv, dk, dv), dtype=torch.float32, device="cuda")
     o, ht, hck = gdr.chunk_fwd_checkpoints(t["q"], t["k"], t["v"], t["g"], t["beta"], cu, t["h0"],
                                            scale=d["scale"], ht=ht, h_chunks=hck)
     torch.cuda.synchronize()
@@ -89,9 +89,9 @@ def _run_n(t, d, rows, every, sentinel=7.0):
     import chunked_gated_delta_fwd_amd as gdr
     cu = t["cu"]
     N = (cu.shape[0] - 1) if cu is not None else t["q"].shape[0]
-    hv, dk = t["v"].shape[2], t["q"].shape[3]
-    hck = torch.full((rows, hv, dk, dk), sentinel, dtype=torch.float32, device="cuda")
-    ht = torch.zeros((N, hv, dk, dk), dtype=torch.float32, device="cuda")
+    hv, dk, dv = t["v"].shape[2], t["q"].shape[3], t["v"].shape[3]
+    hck = torch.full((rows, hv, dk, dv), sentinel, dtype=torch.float32, device="cuda")
+    ht = torch.zeros((N, hv, dk, dv), dtype=torch.float32, device="cuda")
     o, ht, hck = gdr.chunk_fwd_checkpoints(t["q"], t["k"], t["v"], t["g"], t["beta"], cu, t["h0"],
                                            scale=d["scale"], ht=ht, h_chunks=hck, every_n=every)
     torch.cuda.synchronize()
@@ -180,3 +180,15 @@ def test_checkpoints_n64_equals_chunk_entry_point():
             assert torch.equal(h16[off16 + j16], h64[off64 + j]), "L=%d chunk %d" % (L, j)
         off16 += n16
         off64 += n64
+
+
+@pytest.mark.parametrize("every,dk,dv,dtype", [(16, 128, 64, "bf16"), (64, 64, 128, "bf16"), (32, 128, 64, "fp32")])
+def test_checkpoints_independent_head_dims(every, dk, dv, dtype):
+    """Checkpoints with dk != dv: rows of [dk][dv] states."""
+    lens = [17, 0, 64, 130, 200]
+    say("checkpoints every %d, dk=%d dv=%d %s" % (every, dk, dv, dtype))
+    w = gi.Workload("ragged", 1, 0, 2, 4, dk, dv, dtype, seg_range=(1, 2), n_segments=len(lens), seed=97)
+    d = gi.generate(w, lengths=lens)
+    t = to_device(d)
+    rows = (sum(lens) + every - 1) // every + len(lens)
+    _check_n(t, d, rows, every, "ckpt/%d dk=%d dv=%d %s" % (every, dk, dv, dtype))

@@ -14,11 +14,12 @@ from gpu_helpers import TOL_HT, TOL_O, dev, np64, say
 pytestmark = pytest.mark.gpu
 
 
-def _case(seed, B, T, hk, hv, d, dtype):
-    w = gi.Workload("decode", B, T, hk, hv, d, d, dtype, seed=seed)
+def _case(seed, B, T, hk, hv, d, dtype, dv=None):
+    dv = dv or d
+    w = gi.Workload("decode", B, T, hk, hv, d, dv, dtype, seed=seed)
     c = gi.generate(w)
     rng = np.random.default_rng(seed)
-    c["h0"] = (0.3 * rng.standard_normal((B, hv, d, d))).astype(np.float32)
+    c["h0"] = (0.3 * rng.standard_normal((B, hv, d, dv))).astype(np.float32)
     return c
 
 
@@ -53,6 +54,18 @@ def test_decode_one_step(B, hk, hv, d, dtype):
     dh = float(np.abs(h - h_ref).max())
     say("decode B=%d Hk=%d Hv=%d d=%d %s: max|do| %.3e max|dh| %.3e" % (B, hk, hv, d, dtype, do, dh))
     assert do <= TOL_O and dh <= TOL_HT
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 64, "bf16"), (64, 128, "fp32")])
+def test_decode_independent_head_dims(dk, dv, dtype):
+    """dk != dv: a chain of 10 steps against the oracle over the same tokens."""
+    c = _case(31, 4, 10, 2, 4, dk, dtype, dv=dv)
+    o, h = _steps(c)
+    o_ref, h_ref = _oracle(c)
+    do = float(np.abs(o - o_ref).max())
+    dh = float(np.abs(h - h_ref).max())
+    say("decode dk=%d dv=%d %s: max|do| %.3e max|dh| %.3e" % (dk, dv, dtype, do, dh))
+    assert o.shape == o_ref.shape and do <= TOL_O and dh <= TOL_HT
 
 
 def test_decode_chain_of_steps():

@@ -341,6 +341,27 @@ def test_ragged_lengths_and_gqa(d_head, dtype, gdtype, hk, hv):
     compare(o, ht, o_ref, ht_ref, "ragged d=%d %s" % (d_head, dtype), *tols(dtype))
 
 
+@pytest.mark.parametrize("dk,dv,dtype,gdtype,hk,hv", [
+    (128, 64, "bf16", "bf16", 2, 4), (64, 128, "bf16", "fp32", 1, 2),
+    (128, 64, "fp32", "fp32", 1, 2), (64, 128, "fp32", "bf16", 2, 2)])
+def test_independent_head_dims(dk, dv, dtype, gdtype, hk, hv):
+    """dk != dv (each 64 or 128): ragged lengths with ghosts, GQA, both input
+    dtypes; every element of o and ht, ghost rows of ht keep their sentinel."""
+    import torch
+    say("head dims dk=%d dv=%d %s gates %s Hk=%d Hv=%d" % (dk, dv, dtype, gdtype, hk, hv))
+    lens = [1, 63, 0, 64, 65, 127, 0, 128, 129, 200]
+    w = gi.Workload("ragged", 1, 0, hk, hv, dk, dv, dtype, seg_range=(1, 2), n_segments=len(lens), seed=79)
+    d = gi.generate(w, lengths=lens)
+    if gdtype == "bf16" and dtype == "fp32":
+        d["g"], d["beta"] = gi.round_to_bf16(d["g"]), gi.round_to_bf16(d["beta"])
+    t = to_device(d, gate_dtype=gdtype)
+    sentinel = np.full((len(lens), hv, dk, dv), 5.0)
+    o, ht = run_gpu(t, d["scale"], ht_init=torch.from_numpy(sentinel.astype(np.float32)).cuda())
+    assert tuple(o.shape) == (1, sum(lens), hv, dv) and tuple(ht.shape) == (len(lens), hv, dk, dv)
+    o_ref, ht_ref = run_oracle(d, ht_init=sentinel)
+    compare(o, ht, o_ref, ht_ref, "dk=%d dv=%d %s" % (dk, dv, dtype), *tols(dtype))
+
+
 def test_rows_outside_segments_untouched_and_canaries():
     """cu[N] < T: rows past the last segment are not written; margins around o
     and ht keep their sentinel (no out-of-bounds store)."""
