@@ -137,6 +137,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
     constexpr int TPT = C / TG;    // staging: tokens per prep thread
     static_assert(KB % 2 == 0 && NTW >= 1 && (TPT == 2 || TPT == 4), "unsupported head dim");
     static_assert(Ly::bytes <= 160 * 1024, "LDS budget");
+    constexpr bool OUT = CK != 2;   // the output o (and with it q, P and scale e^G) is produced
     constexpr uint32_t ES = IN_BF16 ? 2 : 4;      // bytes per q/k/v/o element
     constexpr uint32_t GES = GATE_BF16 ? 2 : 4;   // bytes per g/beta element
 
@@ -302,7 +303,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
             const uint32_t off = (tg * TPT + j) * rowb + 8 * fg * ES;
-            pq[j] = __builtin_bit_cast(uint4, buf_load8<IN_BF16>(rq, off));
+            if constexpr (OUT) pq[j] = __builtin_bit_cast(uint4, buf_load8<IN_BF16>(rq, off));
             pk[j] = __builtin_bit_cast(uint4, buf_load8<IN_BF16>(rk, off));
         }
     };
@@ -314,7 +315,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
             const int t = tg * TPT + j;
-            *reinterpret_cast<uint4 *>(sQ + t * PK + 8 * fg) = pq[j];
+            if constexpr (OUT) *reinterpret_cast<uint4 *>(sQ + t * PK + 8 * fg) = pq[j];
             *reinterpret_cast<uint4 *>(sK + t * PK + 8 * fg) = pk[j];
         }
     };
@@ -363,19 +364,21 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         const uint16_t *sQ = Qb(b3);
         const uint16_t *sK = Kb(b3);
         const float *sB = sBw;
+        // strip IK of K K^T and strip IQ of Q K^T (IQ = -1: none)
         auto strips = [&](auto ikc, auto iqc) __attribute__((always_inline)) {
             constexpr int IK = decltype(ikc)::value, IQ = decltype(iqc)::value;
             constexpr int JMAX = IK > IQ ? IK : IQ;
+            constexpr int IQ0 = IQ < 0 ? 0 : IQ;
             bf16x8 bk[KB / 2], bq[KB / 2];
             const uint16_t *pki = sK + (16 * IK + l16) * PK + 8 * lq;
-            const uint16_t *pqi = sQ + (16 * IQ + l16) * PK + 8 * lq;
+            const uint16_t *pqi = sQ + (16 * IQ0 + l16) * PK + 8 * lq;
 #pragma unroll
             for (int p = 0; p < KB / 2; ++p) {
                 bk[p] = ld8(pki + 32 * p);
-                bq[p] = ld8(pqi + 32 * p);
+                if constexpr (IQ >= 0) bq[p] = ld8(pqi + 32 * p);
             }
             const float gk_col = sG2[16 * IK + l16];
-            const float gq_col = sG2[16 * IQ + l16];
+            const float gq_col = IQ >= 0 ? sG2[16 * IQ0 + l16] : 0.f;
 #pragma unroll
             for (int j = 0; j <= JMAX; ++j) {
                 f32x4 akk = zero4(), aqk = zero4();
@@ -417,10 +420,17 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 }
             }
         };
-        if (role == 0) strips(IntC<3>{}, IntC<0>{});
-        else if (role == 1) strips(IntC<2>{}, IntC<1>{});
-        else if (role == 2) strips(IntC<1>{}, IntC<2>{});
-        else strips(IntC<0>{}, IntC<3>{});
+        if constexpr (OUT) {
+            if (role == 0) strips(IntC<3>{}, IntC<0>{});
+            else if (role == 1) strips(IntC<2>{}, IntC<1>{});
+            else if (role == 2) strips(IntC<1>{}, IntC<2>{});
+            else strips(IntC<0>{}, IntC<3>{});
+        } else {   // states only: no P
+            if (role == 0) strips(IntC<3>{}, IntC<-1>{});
+            else if (role == 1) strips(IntC<2>{}, IntC<-1>{});
+            else if (role == 2) strips(IntC<1>{}, IntC<-1>{});
+            else strips(IntC<0>{}, IntC<-1>{});
+        }
     };
 
     // prep: inverse of diagonal block b = 3 - role of I + A (the block this
@@ -547,7 +557,9 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 Vt[blk][nt] = cvt4(mfma16z(dd, rb, zero4()));
             }
 
-            // output of token block blk, stored 4*NTW dv per lane
+            // output of token block blk, stored 4*NTW dv per lane (the
+            // backward's state recompute, CK = 2, has no output)
+            if constexpr (OUT) {
             f32x4 Ot[NTW];
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) Ot[nt] = zero4();
@@ -589,6 +601,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt)
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, Ot[nt]), ro, off + 16 * nt, 0, 0);
+            }
             }
         }
 
