@@ -418,6 +418,17 @@ def traffic_summary(args):
     w = gi.WORKLOADS[args.workload]
     lines = [
         "# HBM traffic of %s on %s (rocprofv3 --pmc, KiB per dispatch)" % (FWD_KERNEL, w.name),
+        "# made by four counter runs, one counter each, then this summary:",
+        "#   rocprofv3 --pmc FETCH_SIZE -f csv -d FETCH_DIR -o fwd -- "
+        "python3 bench.py --steps 3 --warmup 1 --settle-calls 0 --no-cpu-baseline",
+        "#   rocprofv3 --pmc WRITE_SIZE -f csv -d WRITE_DIR -o fwd -- "
+        "python3 bench.py --steps 3 --warmup 1 --settle-calls 0 --no-cpu-baseline",
+        "#   rocprofv3 --pmc FETCH_SIZE -f csv -d COPY_FETCH_DIR -o copy -- "
+        "python3 bench.py --copy-probe-mib %d" % args.copy_probe_mib,
+        "#   rocprofv3 --pmc WRITE_SIZE -f csv -d COPY_WRITE_DIR -o copy -- "
+        "python3 bench.py --copy-probe-mib %d" % args.copy_probe_mib,
+        "#   python3 bench.py --traffic-summary FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR "
+        "--copy-probe-mib %d" % args.copy_probe_mib,
         "workload: %s" % w.name,
         "kernel_source_sha: %s" % kernel_source_sha(),
         "fwd_dispatches: %d" % len(fetch),
