@@ -548,10 +548,10 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
 }
 
 // Workspace of a backward call: chunk indices (varlen only), then per (chunk
-// row, v-head) the forward state, the state gradient, the local dU0, dU, T^T
-// and w^T, each part 256-byte aligned.
+// row, v-head) the forward state, the state gradient, dU, T^T and w^T, each
+// part 256-byte aligned.
 struct BwdWorkspace {
-    size_t ints, hck, dhe, du0, du, tmat, wt, total;
+    size_t ints, hck, dhe, du, tmat, wt, total;
 };
 BwdWorkspace bwd_workspace(int64_t n_seq, int64_t rows, int64_t hv, int64_t d, bool varlen) {
     auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
@@ -565,8 +565,6 @@ BwdWorkspace bwd_workspace(int64_t n_seq, int64_t rows, int64_t hv, int64_t d, b
     o += al(ch * dd * dd * 2);
     w.dhe = o;
     o += al(ch * dd * dd * 2);
-    w.du0 = o;
-    o += al(ch * gdr::kChunk * dd * 2);
     w.du = o;
     o += al(ch * gdr::kChunk * dd * 2);
     w.tmat = o;
@@ -696,7 +694,6 @@ int run_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
         ba.hck = hck;
         ba.tmat = reinterpret_cast<uint16_t *>(base + wl.tmat);
         ba.wt = reinterpret_cast<uint16_t *>(base + wl.wt);
-        ba.du0 = reinterpret_cast<uint16_t *>(base + wl.du0);
         ba.du = reinterpret_cast<uint16_t *>(base + wl.du);
         ba.dhe = reinterpret_cast<uint16_t *>(base + wl.dhe);
         ba.dq = dq->data;

@@ -34,9 +34,10 @@
 //
 // Kernels (after the forward kernel has written the state after every chunk):
 //   gdr_bwd_prep_kernel   per (chunk, v-head), in parallel: T by block
-//                         substitution, w^T, and the local dU0.
+//                         substitution and w^T.
 //   gdr_bwd_chain_kernel  per (sequence, v-head), chunks in reverse order:
-//                         dS' kept in fp32 registers, dU completed in place,
+//                         dS' kept in fp32 registers, dU = dU0 + its chain
+//                         part (dU0 formed in the chain from q, k, dO),
 //                         dS' of every chunk stored for the next kernel.
 //   gdr_bwd_grads_kernel  per (chunk, q/k head), in parallel, looping over the
 //                         v-heads of the group: dq, dk, dv, dg, dbeta.
@@ -157,16 +158,6 @@ __device__ __forceinline__ void fetch_block(v4u32 (&dst)[NP], const uint16_t *sr
 #pragma unroll
     for (int j = 0; j < NP; ++j) dst[j] = *reinterpret_cast<const v4u32 *>(src + 8 * (tid + j * NT));
 }
-// This wave's dU0 tiles (16x16 bf16, lane-major) of dv tiles ct .. ct+NTW-1.
-template <int MT, int NTW>
-__device__ __forceinline__ void fetch_tiles(bf16x4 (&dst)[4][NTW], const uint16_t *src, int ct, int lane) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
-            dst[mt][nt] = *reinterpret_cast<const bf16x4 *>(src + ((mt * MT + ct + nt) * 64 + lane) * 4);
-}
-
 // Which sequence and chunk a chunk row belongs to.
 struct ChunkAt {
     int64_t n, c, t0;
@@ -214,7 +205,7 @@ __device__ __forceinline__ void chunk_gates(const BwdArgs &a, int64_t t0, int le
 }
 
 // --------------------------------------------------------------------------
-// Per (chunk, v-head): T, w^T and the local dU0.
+// Per (chunk, v-head): T and w^T.
 // --------------------------------------------------------------------------
 template <int D>
 struct PrepLds {
@@ -222,38 +213,25 @@ struct PrepLds {
     // four-byte LDS banks: 8-byte row fragments (16 lanes, one row each) are
     // conflict-free at 2 mod 32 banks, transposing reads (4 rows of 32 bytes
     // per 16 lanes) at 8 mod 32; k, read both ways, takes 4 mod 32 (2-way).
-    static constexpr int PQ = D + 4;    // q [64][D]: row fragments
     static constexpr int PK = D + 8;    // k [64][D]: both
-    static constexpr int PO = D + 16;   // dO [64][D]: transposing reads
-    static constexpr int PP = C + 4;    // A, P^T [64][64]: row fragments
+    static constexpr int PP = C + 4;    // A [64][64]: row fragments
     static constexpr int PT = C + 16;   // (T diag(b e^G))^T [64][64]: transposing reads
     static constexpr int PD = 20;       // [16][16] bf16 blocks
-    static constexpr int oQ = 0;
-    static constexpr int oK = oQ + C * PQ * 2;
-    static constexpr int oO = oK + C * PK * 2;
-    static constexpr int oA = oO + C * PO * 2;        // diag(b) A~, strictly lower, [i][j]
-    static constexpr int oPt = oA + C * PP * 2;       // (scale M o Q K^T)^T, [j][i]
-    static constexpr int oG = oPt + C * PP * 2;       // f32 [64] x3: G log2(e), b, b e^G
-    static constexpr int base = oG + 3 * C * 4;
-    // (T diag(b e^G))^T [j][i] and the bf16 inverses of the diagonal blocks of
-    // I + diag(b) A~: in q's rows, dead once Q K^T is formed, when they fit
-    static constexpr int alias = C * PT * 2 + 4 * 16 * PD * 2;
-    static constexpr bool in_q = alias <= C * PQ * 2;
-    static constexpr int oTt = in_q ? oQ : base;
-    static constexpr int oDi = oTt + C * PT * 2;
-    static constexpr int bytes = in_q ? base : base + alias;
+    static constexpr int oK = 0;
+    static constexpr int oA = oK + C * PK * 2;        // diag(b) A~, strictly lower, [i][j]
+    static constexpr int oG = oA + C * PP * 2;        // f32 [64] x3: G log2(e), b, b e^G
+    static constexpr int oTt = oG + 3 * C * 4;        // (T diag(b e^G))^T [j][i]
+    static constexpr int oDi = oTt + C * PT * 2;      // bf16 inverses of the diagonal blocks of I + diag(b) A~
+    static constexpr int bytes = oDi + 4 * 16 * PD * 2;
 };
 
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     using Ly = PrepLds<D>;
-    constexpr int PQ = Ly::PQ, PK = Ly::PK, PO = Ly::PO, PP = Ly::PP, PT = Ly::PT, PD = Ly::PD, NTD = D / 16;
+    constexpr int PK = Ly::PK, PP = Ly::PP, PT = Ly::PT, PD = Ly::PD, NTD = D / 16;
     extern __shared__ __align__(16) unsigned char lds[];
-    uint16_t *sQ = reinterpret_cast<uint16_t *>(lds + Ly::oQ);
     uint16_t *sK = reinterpret_cast<uint16_t *>(lds + Ly::oK);
-    uint16_t *sO = reinterpret_cast<uint16_t *>(lds + Ly::oO);
     uint16_t *sA = reinterpret_cast<uint16_t *>(lds + Ly::oA);
-    uint16_t *sPt = reinterpret_cast<uint16_t *>(lds + Ly::oPt);
     uint16_t *sTt = reinterpret_cast<uint16_t *>(lds + Ly::oTt);
     uint16_t *sDi = reinterpret_cast<uint16_t *>(lds + Ly::oDi);
     float *sG2 = reinterpret_cast<float *>(lds + Ly::oG);
@@ -270,9 +248,8 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lq = lane >> 4;
     const int64_t rh = crow * a.hv + h;
 
-    stage_rows2<D, IN_BF16, kBwdThreads, PQ, PK>(sQ, a.q, a.hk, hk, sK, a.k, a.hk, hk, p.t0, p.len, tid);
-    stage_rows<D, IN_BF16, kBwdThreads>(sO, PO, a.dout, p.t0, p.len, a.hv, h, tid);
-    for (int i = tid; i < 2 * C * PP / 8; i += kBwdThreads)   // A and P^T (adjacent): blocks above the diagonal stay zero
+    stage_rows<D, IN_BF16, kBwdThreads>(sK, PK, a.k, p.t0, p.len, a.hk, hk, tid);
+    for (int i = tid; i < C * PP / 8; i += kBwdThreads)   // A: blocks above the diagonal stay zero
         reinterpret_cast<uint4 *>(sA)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (wave == 0) {
         float G2, bv, GL2;
@@ -283,33 +260,22 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // gated K K^T (strictly lower, times b: A) and Q K^T (lower, times scale:
-    // P, stored transposed), the ten lower 16x16 blocks of each
-    for (int t = wave; t < 20; t += 8) {
-        const bool kk = t < 10;
-        const int tt = kk ? t : t - 10;
-        const int bi = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
-        const int bj = tt - bi * (bi + 1) / 2;
-        const uint16_t *Am = kk ? sK : sQ;
-        const int pa = kk ? PK : PQ;
+    // gated K K^T, strictly lower and times b (A): its ten lower 16x16 blocks
+    for (int t = wave; t < 10; t += 8) {
+        const int bi = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+        const int bj = t - bi * (bi + 1) / 2;
         f32x4 acc = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < D; k0 += 32)
-            acc = mfma32(frag_rows(Am, pa, 16 * bi, k0, l16, lq), frag_rows(sK, PK, 16 * bj, k0, l16, lq), acc);
+            acc = mfma32(frag_rows(sK, PK, 16 * bi, k0, l16, lq), frag_rows(sK, PK, 16 * bj, k0, l16, lq), acc);
         const int j = 16 * bj + l16;
         const float gj = sG2[j];
-        f32x4 pv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * bi + 4 * lq + r;
-            const float e = fast_exp2(sG2[i] - gj);   // used only where j <= i (exponent <= 0)
-            if (kk) {
-                sA[i * PP + j] = bf16_bits(j < i ? sB[i] * e * acc[r] : 0.f);
-            } else {
-                pv[r] = j <= i ? a.scale * e * acc[r] : 0.f;
-            }
+            const float e = fast_exp2(sG2[i] - gj);   // used only where j < i (exponent <= 0)
+            sA[i * PP + j] = bf16_bits(j < i ? sB[i] * e * acc[r] : 0.f);
         }
-        if (!kk) st4(sPt + j * PP + 16 * bi + 4 * lq, cvt4(pv));
     }
     __syncthreads();
 
@@ -374,17 +340,6 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
             acc = mfma32(frag_cols(sTt, PT, 16 * it, k0, l16, lq), frag_cols(sK, PK, 16 * dt, k0, l16, lq), acc);
         *reinterpret_cast<bf16x4 *>(wg + (16 * dt + l16) * C + 16 * it + 4 * lq) = cvt4(acc);
     }
-    // dU0 = (scale M o Q K^T)^T dO, in 16x16 tiles (token block, dv tile), lane-major, bf16
-    uint16_t *ug = a.du0 + rh * (C * D);
-    for (int t = wave; t < 4 * NTD; t += 8) {
-        const int jt = t & 3, nt = t >> 2;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32)
-            if (k0 + 32 > 16 * jt)
-                acc = mfma32(frag_rows(sPt, PP, 16 * jt, k0, l16, lq), frag_cols(sO, PO, 16 * nt, k0, l16, lq), acc);
-        *reinterpret_cast<bf16x4 *>(ug + ((jt * NTD + nt) * 64 + lane) * 4) = cvt4(acc);
-    }
 }
 
 // --------------------------------------------------------------------------
@@ -393,24 +348,26 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
 // --------------------------------------------------------------------------
 template <int D>
 struct ChainLds {
-    // q and dO are read with transposing reads (pitch 8 mod 32 four-byte
-    // banks); k and w^T, A operands against register B operands in C-tile
-    // key order, with key-permuted columns (kpos) as 16-byte fragments
-    static constexpr int PK = D + 16;              // q, dO
+    // dO is read with transposing reads (pitch 8 mod 32 four-byte banks:
+    // conflict-free); q both ways (4 mod 32: at most 2-way either way); k
+    // and w^T, A operands in C-tile key order, with key-permuted columns
+    // (kpos) as 16-byte fragments
+    static constexpr int PQ = D + 8;               // q
+    static constexpr int PK = D + 16;              // dO
     static constexpr int PR = D + 16;              // k
     static constexpr int PW = C + 16;
     static constexpr int oQ = 0;
-    static constexpr int oK = oQ + C * PK * 2;
+    static constexpr int oK = oQ + C * PQ * 2;
     static constexpr int oO = oK + C * PR * 2;
     static constexpr int oW = oO + C * PK * 2;     // w^T [D][PW]
-    static constexpr int oG = oW + D * PW * 2;     // f32 [64] x2: scale e^G, e^{G_L - G}; then e^{G_L}
-    static constexpr int bytes = oG + 2 * C * 4 + 16;
+    static constexpr int oG = oW + D * PW * 2;     // f32 [64] x3: scale e^G, e^{G_L - G}, G log2(e); then e^{G_L}
+    static constexpr int bytes = oG + 3 * C * 4 + 16;
 };
 
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a) {
     using Ly = ChainLds<D>;
-    constexpr int PK = Ly::PK, PKR = Ly::PR, PW = Ly::PW;
+    constexpr int PQ = Ly::PQ, PK = Ly::PK, PKR = Ly::PR, PW = Ly::PW;
     constexpr int MT = D / 16;                        // dk tiles (and dv tiles)
     constexpr int NTW = D / 64;                       // dv tiles per wave
     constexpr int PR = D / 8;                         // 16-byte pieces per q / k / dO row
@@ -423,7 +380,8 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
     uint16_t *sW = reinterpret_cast<uint16_t *>(lds + Ly::oW);
     float *sGs = reinterpret_cast<float *>(lds + Ly::oG);
     float *sLam = sGs + C;
-    float *sGL = sLam + C;
+    float *sG2 = sLam + C;
+    float *sGL = sG2 + C;
 
     const int64_t item = gqa_xcd_item(blockIdx.x, gridDim.x, a.hv, a.hk);   // v-heads of a q/k head share an L2
     const int64_t rank = item / a.hv;
@@ -448,11 +406,9 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
     const int64_t off = a.offs ? static_cast<int64_t>(a.offs[n]) : n * ((a.seq_len + C - 1) / C);
 
     // Registers of the chunk being fetched while the previous one is processed:
-    // rows of q, k and dO, w^T, this lane's gate (wave 0); then this wave's
-    // dU0 tiles, fetched once the current ones are used.
+    // rows of q, k and dO, w^T, this lane's gate (wave 0).
     v4u32 pq[NQ], pk[NQ], po[NQ], pw[NW];
     float pg = 0.f;
-    bf16x4 pu[4][NTW];
 #define GDR_FETCH(cc)                                                                                  \
     {                                                                                                  \
         const int64_t t0_ = bos + C * (cc);                                                            \
@@ -463,10 +419,6 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
         fetch_block<NW, kChainThreads>(pw, a.wt + ((off + (cc)) * a.hv + h) * (D * C), tid);           \
         const int ln_ = tid & 63;                                                                      \
         if (wave == 0) pg = ln_ < len_ ? load_scalar<GATE_BF16>(a.g, (t0_ + ln_) * a.hv + h) : 0.f;   \
-    }
-#define GDR_FETCH_DU0(cc)                                                                              \
-    {                                                                                                  \
-        fetch_tiles<MT, NTW>(pu, a.du0 + ((off + (cc)) * a.hv + h) * (C * D), colw / 16, tid & 63);   \
     }
 
     f32x4 dH[MT][NTW];
@@ -482,7 +434,6 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
                     dH[mt][nt][r] = src ? src[(16 * mt + 4 * lq + r) * D + colw + 16 * nt + l16] : 0.f;
     }
     GDR_FETCH(nch - 1)
-    GDR_FETCH_DU0(nch - 1)
 
     for (int64_t c = nch - 1; c >= 0; --c) {
         int lane = tid & 63;   // opaque per iteration: keeps per-lane addresses inside the loop
@@ -493,7 +444,7 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             const int i = tid + j * kChainThreads, row = i / PR, col = 8 * (i % PR);
-            *reinterpret_cast<v4u32 *>(sQ + row * PK + col) = pq[j];
+            *reinterpret_cast<v4u32 *>(sQ + row * PQ + col) = pq[j];
             *reinterpret_cast<v2u32 *>(sK + row * PKR + kpos(col)) = v2u32{pk[j][0], pk[j][1]};
             *reinterpret_cast<v2u32 *>(sK + row * PKR + kpos(col + 4)) = v2u32{pk[j][2], pk[j][3]};
             *reinterpret_cast<v4u32 *>(sO + row * PK + col) = po[j];
@@ -509,6 +460,7 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
             const float GL2 = lane63(G2);
             sGs[lane] = a.scale * fast_exp2(G2);
             sLam[lane] = fast_exp2(GL2 - G2);
+            sG2[lane] = G2;
             if (lane == 0) sGL[0] = fast_exp2(GL2);
         }
         __syncthreads();
@@ -523,6 +475,48 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt)
                     *reinterpret_cast<bf16x4 *>(dst + (mt * NTW + nt) * 64 * 4) = cvt4(dH[mt][nt]);
+        }
+
+        // dU0 = (scale M o Q K^T)^T dO, this wave's dv columns.  Tile (ib, jb)
+        // of P = scale M o Q K^T comes out of the MFMA in C layout (rows
+        // 16 ib + 4 lq + r, column 16 jb + l16), which is the A-operand layout
+        // of rows 16 jb + l16 of P^T at keys 16 ib + 4 lq + r: every wave
+        // forms the lower tiles it needs in registers (measured faster than
+        // sharing the ten tiles through LDS, which costs a barrier).
+        f32x4 U0[4][NTW];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) U0[jb][nt] = zero4();
+            const float gj = sG2[16 * jb + l16];
+#pragma unroll
+            for (int kk = jb / 2; kk < 2; ++kk) {
+                bf16x4 half[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int ib = 2 * kk + hh;
+                    if (ib < jb) {
+                        half[hh] = cvt4(zero4());
+                        continue;
+                    }
+                    f32x4 sc = zero4();
+#pragma unroll
+                    for (int k0 = 0; k0 < D; k0 += 32)
+                        sc = mfma32(frag_rows(sQ, PQ, 16 * ib, k0, l16, lq), kfrag8(sK, PKR, 16 * jb, k0, l16, lq), sc);
+                    const f32x4 gi = *reinterpret_cast<const f32x4 *>(sG2 + 16 * ib + 4 * lq);
+                    f32x4 pv;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const bool keep = ib > jb || l16 <= 4 * lq + r;
+                        pv[r] = keep ? a.scale * fast_exp2(gi[r] - gj) * sc[r] : 0.f;
+                    }
+                    half[hh] = cvt4(pv);
+                }
+                const bf16x8 af = cat(half[0], half[1]);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+                    U0[jb][nt] = mfma32(af, frag_cols(sO, PK, colw + 16 * nt, 32 * kk, l16, lq), U0[jb][nt]);
+            }
         }
 
         // X1 = K dS'
@@ -551,14 +545,12 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
-                f32x4 u = up4(pu[mt][nt]);
+                f32x4 u = U0[mt][nt];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) u[r] += sLam[16 * mt + 4 * lq + r] * X1[mt][nt][r];
                 dUb[mt][nt] = cvt4(u);
                 *reinterpret_cast<bf16x4 *>(ug + ((mt * MT + colw / 16 + nt) * 64 + lane) * 4) = dUb[mt][nt];
             }
-
-        if (c > 0) GDR_FETCH_DU0(c - 1)
 
         // dS <- e^{G_L} dS' + Q^T diag(scale e^G) dO - w^T dU
         const float gl = sGL[0];
@@ -582,7 +574,7 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const bf16x8 aq = frag_cols(sQ, PK, 16 * mt, 32 * kk, l16, lq);
+                const bf16x8 aq = frag_cols(sQ, PQ, 16 * mt, 32 * kk, l16, lq);
                 const bf16x8 aw = kfrag8(sW, PW, 16 * mt, 32 * kk, l16, lq);
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
@@ -605,7 +597,6 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
                     dst[(16 * mt + 4 * lq + r) * D + colw + 16 * nt + l16] = dH[mt][nt][r];
     }
 #undef GDR_FETCH
-#undef GDR_FETCH_DU0
 }
 
 // --------------------------------------------------------------------------
