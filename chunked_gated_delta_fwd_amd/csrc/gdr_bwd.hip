@@ -204,6 +204,21 @@ __device__ __forceinline__ void chunk_gates(const BwdArgs &a, int64_t t0, int le
     GL2 = lane63(G2);
 }
 
+// Raw bits of the gate of token t0 + lane, v-head h (zero past len): one
+// buffer load, no branch; gate_value converts them.
+template <bool GATE_BF16>
+__device__ __forceinline__ uint32_t gate_bits(const void *g, int64_t t0, int len, int hv, int h, int lane) {
+    constexpr int ES = GATE_BF16 ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t r = chunk_rsrc(reinterpret_cast<const unsigned char *>(g) + (t0 * hv + h) * ES,
+                                                static_cast<uint32_t>(len * hv * ES));
+    if constexpr (GATE_BF16) return static_cast<uint32_t>(buf_load<2>(r, static_cast<uint32_t>(lane * hv * ES)));
+    else return buf_load<4>(r, static_cast<uint32_t>(lane * hv * ES));
+}
+template <bool GATE_BF16>
+__device__ __forceinline__ float gate_value(uint32_t bits) {
+    return __uint_as_float(GATE_BF16 ? bits << 16 : bits);
+}
+
 // --------------------------------------------------------------------------
 // Per (chunk, v-head): T and w^T.
 // --------------------------------------------------------------------------
@@ -406,19 +421,34 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
     const int64_t off = a.offs ? static_cast<int64_t>(a.offs[n]) : n * ((a.seq_len + C - 1) / C);
 
     // Registers of the chunk being fetched while the previous one is processed:
-    // rows of q, k and dO, w^T, this lane's gate (wave 0).
+    // rows of q, k and dO, w^T, this lane's gate (wave 0; its raw bits, by a
+    // buffer load that reads zero past the segment end, converted at use: a
+    // lane-dependent load or a conversion right after it would make the wave
+    // wait there for every load of the prefetch).
     v4u32 pq[NQ], pk[NQ], po[NQ], pw[NW];
-    float pg = 0.f;
-#define GDR_FETCH(cc)                                                                                  \
+    uint32_t pg = 0u;
+    // One quarter of the next chunk's loads (part 0: q rows, 1: k rows, 2: dO
+    // rows, 3: w^T and the gate).  The chain issues the quarters between the
+    // phases of a chunk's products, so that the wave's vector-memory issue
+    // overlaps its MFMA work instead of stalling ahead of it.
+#define GDR_FETCH_PART(cc, part)                                                                       \
     {                                                                                                  \
         const int64_t t0_ = bos + C * (cc);                                                            \
         const int len_ = static_cast<int>(eos - t0_ < C ? eos - t0_ : C);                              \
-        fetch_rows<D, IN_BF16, NQ, kChainThreads>(pq, a.q, t0_, len_, a.hk, hk, tid);                  \
-        fetch_rows<D, IN_BF16, NQ, kChainThreads>(pk, a.k, t0_, len_, a.hk, hk, tid);                  \
-        fetch_rows<D, IN_BF16, NQ, kChainThreads>(po, a.dout, t0_, len_, a.hv, h, tid);                \
-        fetch_block<NW, kChainThreads>(pw, a.wt + ((off + (cc)) * a.hv + h) * (D * C), tid);           \
-        const int ln_ = tid & 63;                                                                      \
-        if (wave == 0) pg = ln_ < len_ ? load_scalar<GATE_BF16>(a.g, (t0_ + ln_) * a.hv + h) : 0.f;   \
+        if ((part) == 0) fetch_rows<D, IN_BF16, NQ, kChainThreads>(pq, a.q, t0_, len_, a.hk, hk, tid); \
+        if ((part) == 1) fetch_rows<D, IN_BF16, NQ, kChainThreads>(pk, a.k, t0_, len_, a.hk, hk, tid); \
+        if ((part) == 2) fetch_rows<D, IN_BF16, NQ, kChainThreads>(po, a.dout, t0_, len_, a.hv, h, tid); \
+        if ((part) == 3) {                                                                             \
+            fetch_block<NW, kChainThreads>(pw, a.wt + ((off + (cc)) * a.hv + h) * (D * C), tid);       \
+            if (wave == 0) pg = gate_bits<GATE_BF16>(a.g, t0_, len_, a.hv, h, tid & 63);                \
+        }                                                                                              \
+    }
+#define GDR_FETCH(cc)                                                                                  \
+    {                                                                                                  \
+        GDR_FETCH_PART(cc, 0)                                                                          \
+        GDR_FETCH_PART(cc, 1)                                                                          \
+        GDR_FETCH_PART(cc, 2)                                                                          \
+        GDR_FETCH_PART(cc, 3)                                                                          \
     }
 
     f32x4 dH[MT][NTW];
@@ -456,7 +486,7 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
             *reinterpret_cast<v2u32 *>(sW + row * PW + kpos(col + 4)) = v2u32{pw[j][2], pw[j][3]};
         }
         if (wave == 0) {
-            const float G2 = wave_inclusive_scan(pg * kLog2e);
+            const float G2 = wave_inclusive_scan(gate_value<GATE_BF16>(pg) * kLog2e);
             const float GL2 = lane63(G2);
             sGs[lane] = a.scale * fast_exp2(G2);
             sLam[lane] = fast_exp2(GL2 - G2);
@@ -464,18 +494,6 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
             if (lane == 0) sGL[0] = fast_exp2(GL2);
         }
         __syncthreads();
-        if (c > 0) GDR_FETCH(c - 1)   // in flight during this chunk's products
-
-        // dS' of this chunk (bf16 in tile order: a lane's four values of tile
-        // (mt, nt) as one 8-byte piece), for the per-chunk gradient kernel
-        {
-            uint16_t *dst = a.dhe + rh * D * D + (wave * MT * NTW * 64 + lane) * 4;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt)
-                    *reinterpret_cast<bf16x4 *>(dst + (mt * NTW + nt) * 64 * 4) = cvt4(dH[mt][nt]);
-        }
 
         // dU0 = (scale M o Q K^T)^T dO, this wave's dv columns.  Tile (ib, jb)
         // of P = scale M o Q K^T comes out of the MFMA in C layout (rows
@@ -483,53 +501,74 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
         // of rows 16 jb + l16 of P^T at keys 16 ib + 4 lq + r: every wave
         // forms the lower tiles it needs in registers (measured faster than
         // sharing the ten tiles through LDS, which costs a barrier).
+        // Row block ib of Q is read once and meets the k blocks jb <= ib; the
+        // quarters of the next chunk's loads go out between the row blocks.
         f32x4 U0[4][NTW];
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
+        for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) U0[jb][nt] = zero4();
-            const float gj = sG2[16 * jb + l16];
+        float gjv[4];
 #pragma unroll
-            for (int kk = jb / 2; kk < 2; ++kk) {
-                bf16x4 half[2];
+        for (int jb = 0; jb < 4; ++jb) gjv[jb] = sG2[16 * jb + l16];
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int ib = 2 * kk + hh;
-                    if (ib < jb) {
-                        half[hh] = cvt4(zero4());
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x4 half[2][4];   // P tiles (2 kk + hh, jb) in bf16; zero above the diagonal
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int ib = 2 * kk + hh;
+                if (c > 0) GDR_FETCH_PART(c - 1, ib)   // in flight during this chunk's products
+                bf16x8 aq[D / 32];
+#pragma unroll
+                for (int k0 = 0; k0 < D; k0 += 32) aq[k0 / 32] = frag_rows(sQ, PQ, 16 * ib, k0, l16, lq);
+                const f32x4 gi = *reinterpret_cast<const f32x4 *>(sG2 + 16 * ib + 4 * lq);
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                    if (jb > ib) {
+                        half[hh][jb] = cvt4(zero4());
                         continue;
                     }
                     f32x4 sc = zero4();
 #pragma unroll
                     for (int k0 = 0; k0 < D; k0 += 32)
-                        sc = mfma32(frag_rows(sQ, PQ, 16 * ib, k0, l16, lq), kfrag8(sK, PKR, 16 * jb, k0, l16, lq), sc);
-                    const f32x4 gi = *reinterpret_cast<const f32x4 *>(sG2 + 16 * ib + 4 * lq);
+                        sc = mfma32(aq[k0 / 32], kfrag8(sK, PKR, 16 * jb, k0, l16, lq), sc);
                     f32x4 pv;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const bool keep = ib > jb || l16 <= 4 * lq + r;
-                        pv[r] = keep ? a.scale * fast_exp2(gi[r] - gj) * sc[r] : 0.f;
+                        pv[r] = keep ? a.scale * fast_exp2(gi[r] - gjv[jb]) * sc[r] : 0.f;
                     }
-                    half[hh] = cvt4(pv);
+                    half[hh][jb] = cvt4(pv);
                 }
-                const bf16x8 af = cat(half[0], half[1]);
+            }
+#pragma unroll
+            for (int jb = 0; jb <= 2 * kk + 1; ++jb) {
+                const bf16x8 af = cat(half[0][jb], half[1][jb]);
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt)
                     U0[jb][nt] = mfma32(af, frag_cols(sO, PK, colw + 16 * nt, 32 * kk, l16, lq), U0[jb][nt]);
             }
         }
 
-        // X1 = K dS'
+        // X1 = K dS', and dS' of this chunk stored for the per-chunk gradient
+        // kernel from the same bf16 tiles (tile order: a lane's four values of
+        // tile (mt, nt) as one 8-byte piece), the stores between the products
         f32x4 X1[4][NTW];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) X1[mt][nt] = zero4();
+        uint16_t *dst = a.dhe + rh * D * D + (wave * MT * NTW * 64 + lane) * 4;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             bf16x8 bh[NTW];
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) bh[nt] = cat(cvt4(dH[2 * kk][nt]), cvt4(dH[2 * kk + 1][nt]));
+            for (int nt = 0; nt < NTW; ++nt) {
+                const bf16x4 lo = cvt4(dH[2 * kk][nt]), hi = cvt4(dH[2 * kk + 1][nt]);
+                *reinterpret_cast<bf16x4 *>(dst + (2 * kk * NTW + nt) * 64 * 4) = lo;
+                *reinterpret_cast<bf16x4 *>(dst + ((2 * kk + 1) * NTW + nt) * 64 * 4) = hi;
+                bh[nt] = cat(lo, hi);
+            }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 const bf16x8 af = kfrag8(sK, PKR, 16 * mt, 32 * kk, l16, lq);
@@ -597,6 +636,7 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
                     dst[(16 * mt + 4 * lq + r) * D + colw + 16 * nt + l16] = dH[mt][nt][r];
     }
 #undef GDR_FETCH
+#undef GDR_FETCH_PART
 }
 
 // --------------------------------------------------------------------------
