@@ -548,10 +548,10 @@ int run_fwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
 }
 
 // Workspace of a backward call: chunk indices (varlen only), then per (chunk
-// row, v-head) the forward state, the state gradient, dU, T^T and w^T, each
-// part 256-byte aligned.
+// row, v-head) the forward state, the state gradient, dU and T^T, each part
+// 256-byte aligned.
 struct BwdWorkspace {
-    size_t ints, hck, dhe, du, tmat, wt, total;
+    size_t ints, hck, dhe, du, tmat, total;
 };
 BwdWorkspace bwd_workspace(int64_t n_seq, int64_t rows, int64_t hv, int64_t d, bool varlen) {
     auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
@@ -569,8 +569,6 @@ BwdWorkspace bwd_workspace(int64_t n_seq, int64_t rows, int64_t hv, int64_t d, b
     o += al(ch * gdr::kChunk * dd * 2);
     w.tmat = o;
     o += al(ch * gdr::kChunk * gdr::kChunk * 2);
-    w.wt = o;
-    o += al(ch * dd * gdr::kChunk * 2);
     w.total = o;
     return w;
 }
@@ -693,7 +691,6 @@ int run_bwd(const gdr_tensor *q, const gdr_tensor *k, const gdr_tensor *v, const
         ba.dht = dht ? static_cast<const float *>(dht->data) : nullptr;
         ba.hck = hck;
         ba.tmat = reinterpret_cast<uint16_t *>(base + wl.tmat);
-        ba.wt = reinterpret_cast<uint16_t *>(base + wl.wt);
         ba.du = reinterpret_cast<uint16_t *>(base + wl.du);
         ba.dhe = reinterpret_cast<uint16_t *>(base + wl.dhe);
         ba.dq = dq->data;

@@ -34,10 +34,11 @@
 //
 // Kernels (after the forward kernel has written the state after every chunk):
 //   gdr_bwd_prep_kernel   per (chunk, v-head), in parallel: T by block
-//                         substitution and w^T.
+//                         substitution.
 //   gdr_bwd_chain_kernel  per (sequence, v-head), chunks in reverse order:
 //                         dS' kept in fp32 registers, dU = dU0 + its chain
-//                         part (dU0 formed in the chain from q, k, dO),
+//                         part (dU0 and w formed in the chain from q, k, dO
+//                         and T),
 //                         dS' of every chunk stored for the next kernel.
 //   gdr_bwd_grads_kernel  per (chunk, q/k head), in parallel, looping over the
 //                         v-heads of the group: dq, dk, dv, dg, dbeta.
@@ -62,6 +63,12 @@ __device__ __forceinline__ bf16x8 frag_rows(const uint16_t *M, int pitch, int ro
 // transposing reads: lane i of a 16-lane group receives column col0 + i.
 __device__ __forceinline__ bf16x8 frag_cols(const uint16_t *M, int pitch, int col0, int k0, int l16, int lq) {
     const uint16_t *p = M + (k0 + 4 * lq + (l16 >> 2)) * pitch + col0 + 4 * (l16 & 3);
+    return cat(ld4_tr(p), ld4_tr(p + 16 * pitch));
+}
+// The same from storage whose columns are key-permuted (kpos): every 4-column
+// group stays contiguous, so each lane reads the same 8 bytes at their new place.
+__device__ __forceinline__ bf16x8 frag_cols_kp(const uint16_t *M, int pitch, int col0, int k0, int l16, int lq) {
+    const uint16_t *p = M + (k0 + 4 * lq + (l16 >> 2)) * pitch + kpos(col0 + 4 * (l16 & 3));
     return cat(ld4_tr(p), ld4_tr(p + 16 * pitch));
 }
 __device__ __forceinline__ float bf16_to_f(uint16_t u) { return __uint_as_float(static_cast<uint32_t>(u) << 16); }
@@ -220,7 +227,7 @@ __device__ __forceinline__ float gate_value(uint32_t bits) {
 }
 
 // --------------------------------------------------------------------------
-// Per (chunk, v-head): T and w^T.
+// Per (chunk, v-head): T.
 // --------------------------------------------------------------------------
 template <int D>
 struct PrepLds {
@@ -228,30 +235,26 @@ struct PrepLds {
     // four-byte LDS banks: 8-byte row fragments (16 lanes, one row each) are
     // conflict-free at 2 mod 32 banks, transposing reads (4 rows of 32 bytes
     // per 16 lanes) at 8 mod 32; k, read both ways, takes 4 mod 32 (2-way).
-    static constexpr int PK = D + 8;    // k [64][D]: both
+    static constexpr int PK = D + 4;    // k [64][D]: row fragments
     static constexpr int PP = C + 4;    // A [64][64]: row fragments
-    static constexpr int PT = C + 16;   // (T diag(b e^G))^T [64][64]: transposing reads
     static constexpr int PD = 20;       // [16][16] bf16 blocks
     static constexpr int oK = 0;
     static constexpr int oA = oK + C * PK * 2;        // diag(b) A~, strictly lower, [i][j]
-    static constexpr int oG = oA + C * PP * 2;        // f32 [64] x3: G log2(e), b, b e^G
-    static constexpr int oTt = oG + 3 * C * 4;        // (T diag(b e^G))^T [j][i]
-    static constexpr int oDi = oTt + C * PT * 2;      // bf16 inverses of the diagonal blocks of I + diag(b) A~
+    static constexpr int oG = oA + C * PP * 2;        // f32 [64] x2: G log2(e), b
+    static constexpr int oDi = oG + 2 * C * 4;        // bf16 inverses of the diagonal blocks of I + diag(b) A~
     static constexpr int bytes = oDi + 4 * 16 * PD * 2;
 };
 
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     using Ly = PrepLds<D>;
-    constexpr int PK = Ly::PK, PP = Ly::PP, PT = Ly::PT, PD = Ly::PD, NTD = D / 16;
+    constexpr int PK = Ly::PK, PP = Ly::PP, PD = Ly::PD;
     extern __shared__ __align__(16) unsigned char lds[];
     uint16_t *sK = reinterpret_cast<uint16_t *>(lds + Ly::oK);
     uint16_t *sA = reinterpret_cast<uint16_t *>(lds + Ly::oA);
-    uint16_t *sTt = reinterpret_cast<uint16_t *>(lds + Ly::oTt);
     uint16_t *sDi = reinterpret_cast<uint16_t *>(lds + Ly::oDi);
     float *sG2 = reinterpret_cast<float *>(lds + Ly::oG);
     float *sB = sG2 + C;
-    float *sBG = sB + C;
 
     ChunkAt p;
     // one work item per (chunk row, v-head); v-heads of a q/k head share an L2
@@ -263,7 +266,16 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lq = lane >> 4;
     const int64_t rh = crow * a.hv + h;
 
-    stage_rows<D, IN_BF16, kBwdThreads>(sK, PK, a.k, p.t0, p.len, a.hk, hk, tid);
+    {
+        constexpr int PR = D / 8, NP = C * PR / kBwdThreads;
+        v4u32 rk[NP];
+        fetch_rows<D, IN_BF16, NP, kBwdThreads>(rk, a.k, p.t0, p.len, a.hk, hk, tid);
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int i = tid + j * kBwdThreads;
+            st16<PK % 8 == 0>(sK + (i / PR) * PK + 8 * (i % PR), rk[j]);
+        }
+    }
     for (int i = tid; i < C * PP / 8; i += kBwdThreads)   // A: blocks above the diagonal stay zero
         reinterpret_cast<uint4 *>(sA)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (wave == 0) {
@@ -271,7 +283,6 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
         chunk_gates<GATE_BF16>(a, p.t0, p.len, h, lane, G2, bv, GL2);
         sG2[lane] = G2;
         sB[lane] = bv;
-        sBG[lane] = bv * fast_exp2(G2);
     }
     __syncthreads();
 
@@ -318,7 +329,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     __syncthreads();
 
     // Column block j of T: X_j = D_j, X_i = -D_i sum_{m=j}^{i-1} A_im X_m
-    // (C tiles chained through registers).  T^T goes to memory, (T diag(b e^G))^T to LDS.
+    // (C tiles chained through registers).  T^T goes to memory.
     if (wave < 4) {
         const int j = wave;
         f32x4 X[4];
@@ -336,24 +347,9 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
             }
         }
         uint16_t *tg = a.tmat + rh * (C * C);
-        const float bgj = sBG[16 * j + l16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
             *reinterpret_cast<bf16x4 *>(tg + (16 * j + l16) * C + 16 * i + 4 * lq) = cvt4(X[i]);
-            st4(sTt + (16 * j + l16) * PT + 16 * i + 4 * lq, cvt4(X[i] * bgj));
-        }
-    }
-    __syncthreads();
-
-    // w = T diag(b e^G) K, stored as w^T [D][64]
-    uint16_t *wg = a.wt + rh * (D * C);
-    for (int t = wave; t < 4 * NTD; t += 8) {
-        const int it = t & 3, dt = t >> 2;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32)
-            acc = mfma32(frag_cols(sTt, PT, 16 * it, k0, l16, lq), frag_cols(sK, PK, 16 * dt, k0, l16, lq), acc);
-        *reinterpret_cast<bf16x4 *>(wg + (16 * dt + l16) * C + 16 * it + 4 * lq) = cvt4(acc);
     }
 }
 
@@ -363,40 +359,41 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
 // --------------------------------------------------------------------------
 template <int D>
 struct ChainLds {
-    // dO is read with transposing reads (pitch 8 mod 32 four-byte banks:
-    // conflict-free); q both ways (4 mod 32: at most 2-way either way); k
-    // and w^T, A operands in C-tile key order, with key-permuted columns
-    // (kpos) as 16-byte fragments
+    // dO and T^T are read with transposing reads (pitch 8 mod 32 four-byte
+    // banks: conflict-free); q both ways (4 mod 32: at most 2-way either
+    // way); k with key-permuted columns (kpos): 16-byte row fragments in
+    // C-tile key order, and transposing reads (2-way)
     static constexpr int PQ = D + 8;               // q
     static constexpr int PK = D + 16;              // dO
     static constexpr int PR = D + 16;              // k
-    static constexpr int PW = C + 16;
+    static constexpr int PT = C + 16;              // T^T
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + C * PQ * 2;
     static constexpr int oO = oK + C * PR * 2;
-    static constexpr int oW = oO + C * PK * 2;     // w^T [D][PW]
-    static constexpr int oG = oW + D * PW * 2;     // f32 [64] x3: scale e^G, e^{G_L - G}, G log2(e); then e^{G_L}
-    static constexpr int bytes = oG + 3 * C * 4 + 16;
+    static constexpr int oT = oO + C * PK * 2;     // T^T [64][PT]
+    static constexpr int oG = oT + C * PT * 2;     // f32 [64] x4: scale e^G, e^{G_L - G}, G log2(e), b e^G; then e^{G_L}
+    static constexpr int bytes = oG + 4 * C * 4 + 16;
 };
 
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a) {
     using Ly = ChainLds<D>;
-    constexpr int PQ = Ly::PQ, PK = Ly::PK, PKR = Ly::PR, PW = Ly::PW;
+    constexpr int PQ = Ly::PQ, PK = Ly::PK, PKR = Ly::PR, PT = Ly::PT;
     constexpr int MT = D / 16;                        // dk tiles (and dv tiles)
     constexpr int NTW = D / 64;                       // dv tiles per wave
     constexpr int PR = D / 8;                         // 16-byte pieces per q / k / dO row
     constexpr int NQ = C * PR / kChainThreads;        // such pieces per thread
-    constexpr int NW = D * (C / 8) / kChainThreads;   // 16-byte pieces of w^T per thread
+    constexpr int NT8 = C * (C / 8) / kChainThreads;  // 16-byte pieces of T^T per thread
     extern __shared__ __align__(16) unsigned char lds[];
     uint16_t *sQ = reinterpret_cast<uint16_t *>(lds + Ly::oQ);
     uint16_t *sK = reinterpret_cast<uint16_t *>(lds + Ly::oK);
     uint16_t *sO = reinterpret_cast<uint16_t *>(lds + Ly::oO);
-    uint16_t *sW = reinterpret_cast<uint16_t *>(lds + Ly::oW);
+    uint16_t *sT = reinterpret_cast<uint16_t *>(lds + Ly::oT);
     float *sGs = reinterpret_cast<float *>(lds + Ly::oG);
     float *sLam = sGs + C;
     float *sG2 = sLam + C;
-    float *sGL = sG2 + C;
+    float *sBG = sG2 + C;
+    float *sGL = sBG + C;
 
     const int64_t item = gqa_xcd_item(blockIdx.x, gridDim.x, a.hv, a.hk);   // v-heads of a q/k head share an L2
     const int64_t rank = item / a.hv;
@@ -421,14 +418,14 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
     const int64_t off = a.offs ? static_cast<int64_t>(a.offs[n]) : n * ((a.seq_len + C - 1) / C);
 
     // Registers of the chunk being fetched while the previous one is processed:
-    // rows of q, k and dO, w^T, this lane's gate (wave 0; its raw bits, by a
-    // buffer load that reads zero past the segment end, converted at use: a
-    // lane-dependent load or a conversion right after it would make the wave
-    // wait there for every load of the prefetch).
-    v4u32 pq[NQ], pk[NQ], po[NQ], pw[NW];
-    uint32_t pg = 0u;
+    // rows of q, k and dO, T^T, this lane's gate and beta (wave 0; their raw
+    // bits, by buffer loads that read zero past the segment end, converted at
+    // use: a lane-dependent load or a conversion right after it would make
+    // the wave wait there for every load of the prefetch).
+    v4u32 pq[NQ], pk[NQ], po[NQ], pt[NT8];
+    uint32_t pg = 0u, pb = 0u;
     // One quarter of the next chunk's loads (part 0: q rows, 1: k rows, 2: dO
-    // rows, 3: w^T and the gate).  The chain issues the quarters between the
+    // rows, 3: T^T, the gate and beta).  The chain issues the quarters between the
     // phases of a chunk's products, so that the wave's vector-memory issue
     // overlaps its MFMA work instead of stalling ahead of it.
 #define GDR_FETCH_PART(cc, part)                                                                       \
@@ -439,8 +436,11 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
         if ((part) == 1) fetch_rows<D, IN_BF16, NQ, kChainThreads>(pk, a.k, t0_, len_, a.hk, hk, tid); \
         if ((part) == 2) fetch_rows<D, IN_BF16, NQ, kChainThreads>(po, a.dout, t0_, len_, a.hv, h, tid); \
         if ((part) == 3) {                                                                             \
-            fetch_block<NW, kChainThreads>(pw, a.wt + ((off + (cc)) * a.hv + h) * (D * C), tid);       \
-            if (wave == 0) pg = gate_bits<GATE_BF16>(a.g, t0_, len_, a.hv, h, tid & 63);                \
+            fetch_block<NT8, kChainThreads>(pt, a.tmat + ((off + (cc)) * a.hv + h) * (C * C), tid);     \
+            if (wave == 0) {                                                                           \
+                pg = gate_bits<GATE_BF16>(a.g, t0_, len_, a.hv, h, tid & 63);                          \
+                pb = gate_bits<GATE_BF16>(a.beta, t0_, len_, a.hv, h, tid & 63);                       \
+            }                                                                                          \
         }                                                                                              \
     }
 #define GDR_FETCH(cc)                                                                                  \
@@ -480,10 +480,9 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
             *reinterpret_cast<v4u32 *>(sO + row * PK + col) = po[j];
         }
 #pragma unroll
-        for (int j = 0; j < NW; ++j) {
-            const int i = tid + j * kChainThreads, row = i / (C / 8), col = 8 * (i % (C / 8));
-            *reinterpret_cast<v2u32 *>(sW + row * PW + kpos(col)) = v2u32{pw[j][0], pw[j][1]};
-            *reinterpret_cast<v2u32 *>(sW + row * PW + kpos(col + 4)) = v2u32{pw[j][2], pw[j][3]};
+        for (int j = 0; j < NT8; ++j) {
+            const int i = tid + j * kChainThreads;
+            *reinterpret_cast<v4u32 *>(sT + (i / (C / 8)) * PT + 8 * (i % (C / 8))) = pt[j];
         }
         if (wave == 0) {
             const float G2 = wave_inclusive_scan(gate_value<GATE_BF16>(pg) * kLog2e);
@@ -491,6 +490,7 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
             sGs[lane] = a.scale * fast_exp2(G2);
             sLam[lane] = fast_exp2(GL2 - G2);
             sG2[lane] = G2;
+            sBG[lane] = gate_value<GATE_BF16>(pb) * fast_exp2(G2);
             if (lane == 0) sGL[0] = fast_exp2(GL2);
         }
         __syncthreads();
@@ -591,7 +591,13 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
                 *reinterpret_cast<bf16x4 *>(ug + ((mt * MT + colw / 16 + nt) * 64 + lane) * 4) = dUb[mt][nt];
             }
 
-        // dS <- e^{G_L} dS' + Q^T diag(scale e^G) dO - w^T dU
+        // dS <- e^{G_L} dS' + Q^T diag(scale e^G) dO - w^T dU, with
+        // w = T diag(b e^G) K formed here: tile (tb, db) of w comes out of the
+        // MFMA in C layout (rows 16 tb + 4 lq + r, column 16 db + l16), the
+        // A-operand layout of rows 16 db + l16 of w^T at keys 16 tb + 4 lq + r.
+        // Its A operand, rows of T diag(b e^G), is read transposed from T^T
+        // with each key scaled by its b e^G; T is lower triangular, so row
+        // blocks 0-1 need keys 0-31 only.
         const float gl = sGL[0];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -611,10 +617,30 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
                 bo[nt] = f;
                 bu[nt] = cat(neg4(dUb[2 * kk][nt]), neg4(dUb[2 * kk + 1][nt]));
             }
+            bf16x8 at[2][2];   // [tb - 2 kk][key block kk2 <= kk]
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int kk2 = 0; kk2 <= kk; ++kk2) {
+                    bf16x8 f = frag_cols(sT, PT, 16 * (2 * kk + hh), 32 * kk2, l16, lq);
+                    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(sBG + 32 * kk2 + 4 * lq);
+                    const f32x4 b1 = *reinterpret_cast<const f32x4 *>(sBG + 32 * kk2 + 16 + 4 * lq);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        f[e] = static_cast<__bf16>(static_cast<float>(f[e]) * (e < 4 ? b0[e] : b1[e - 4]));
+                    at[hh][kk2] = f;
+                }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const bf16x8 aq = frag_cols(sQ, PQ, 16 * mt, 32 * kk, l16, lq);
-                const bf16x8 aw = kfrag8(sW, PW, 16 * mt, 32 * kk, l16, lq);
+                f32x4 w0 = zero4(), w1 = zero4();
+#pragma unroll
+                for (int kk2 = 0; kk2 <= kk; ++kk2) {
+                    const bf16x8 bk = frag_cols_kp(sK, PKR, 16 * mt, 32 * kk2, l16, lq);
+                    w0 = mfma32(at[0][kk2], bk, w0);
+                    w1 = mfma32(at[1][kk2], bk, w1);
+                }
+                const bf16x8 aw = cat(cvt4(w0), cvt4(w1));
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     dH[mt][nt] = mfma32(aq, bo[nt], dH[mt][nt]);
@@ -1076,6 +1102,7 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
 
 static_assert(GradLds<128>::bytes <= 160 * 1024, "gradient kernel LDS");
 static_assert(PrepLds<128>::bytes <= 160 * 1024, "prep kernel LDS");
+static_assert(ChainLds<128>::bytes <= 160 * 1024, "chain kernel LDS");
 
 }  // namespace
 

@@ -126,7 +126,6 @@ struct BwdArgs {
     const float *dht;       // NULL: zero gradient of the final state
     const uint16_t *hck;    // forward state after every chunk [rows, Hv, d*d], bf16 in the forward's tile order (FwdArgs::hck16)
     uint16_t *tmat;         // per chunk: T^T, T = (I + diag(b) A~)^-1, bf16 [rows, Hv, 64, 64]
-    uint16_t *wt;           // per chunk: w^T, w = T diag(b e^G) K, bf16 [rows, Hv, d, 64]
     uint16_t *du;           // per chunk: dU, bf16 [rows, Hv, 64 * d] in 16x16 tiles, lane-major
     // per chunk: gradient of the state at its end, bf16 [rows, Hv, d*d] in the
     // chain kernel's tile order: 8-byte piece ((w * d/16 + mt) * (d/64) + nt) * 64

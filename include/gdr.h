@@ -244,9 +244,9 @@ int gdr_chunk_fwd_checkpoints_n(const gdr_tensor *q, const gdr_tensor *k, const 
  * Workspace: the library's large per-device buffer (reused like the ring of
  * gdr_chunk_fwd: concurrent backward calls on one device are ordered on the
  * GPU), of
- * R * Hv * (4 d^2 + 256 d + 8192) bytes plus 4 (2N + 1 + 2R) for the
+ * R * Hv * (4 d^2 + 128 d + 8192) bytes plus 4 (2N + 1 + 2R) for the
  * chunk indices, R = ceil(T/64) + N with cu_seqlens else B * ceil(T/64).
- * About 3.5 GB for 65536 tokens, 32 v-heads, d = 128.  Errors as
+ * About 3.0 GB for 65536 tokens, 32 v-heads, d = 128.  Errors as
  * gdr_chunk_fwd, with GDR_ENOMEM when the workspace cannot be obtained, and
  * GDR_ESHAPE unless dk == dv (the backward kernels are written for square
  * states).
