@@ -196,21 +196,6 @@ __device__ __forceinline__ bool chunk_at(const BwdArgs &a, int64_t r, ChunkAt &p
     return true;
 }
 
-// Gate vectors of one chunk, one token per lane of the calling wave: G log2(e)
-// (chunk-local inclusive prefix sum), beta, and e^{G_L} log2(e)'s exponent.
-template <bool GATE_BF16>
-__device__ __forceinline__ void chunk_gates(const BwdArgs &a, int64_t t0, int len, int h, int lane,
-                                            float &G2, float &bv, float &GL2) {
-    float gv = 0.f;
-    bv = 0.f;
-    if (lane < len) {
-        gv = load_scalar<GATE_BF16>(a.g, (t0 + lane) * a.hv + h);
-        bv = load_scalar<GATE_BF16>(a.beta, (t0 + lane) * a.hv + h);
-    }
-    G2 = wave_inclusive_scan(gv * kLog2e);
-    GL2 = lane63(G2);
-}
-
 // Raw bits of the gate of token t0 + lane, v-head h (zero past len): one
 // buffer load, no branch; gate_value converts them.
 template <bool GATE_BF16>
@@ -224,6 +209,17 @@ __device__ __forceinline__ uint32_t gate_bits(const void *g, int64_t t0, int len
 template <bool GATE_BF16>
 __device__ __forceinline__ float gate_value(uint32_t bits) {
     return __uint_as_float(GATE_BF16 ? bits << 16 : bits);
+}
+
+// Gate vectors of one chunk from the raw bits of its gate and beta, one token
+// per lane of the calling wave: G log2(e) (chunk-local inclusive prefix sum),
+// beta, and G_L log2(e).  The bits are loaded ahead (gate_bits) with the other
+// loads of a phase, so that the scan does not wait for a load of its own.
+template <bool GATE_BF16>
+__device__ __forceinline__ void chunk_gates(uint32_t gbits, uint32_t bbits, float &G2, float &bv, float &GL2) {
+    bv = gate_value<GATE_BF16>(bbits);
+    G2 = wave_inclusive_scan(gate_value<GATE_BF16>(gbits) * kLog2e);
+    GL2 = lane63(G2);
 }
 
 // --------------------------------------------------------------------------
@@ -266,6 +262,11 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lq = lane >> 4;
     const int64_t rh = crow * a.hv + h;
 
+    uint32_t gbits = 0u, bbits = 0u;
+    if (wave == 0) {
+        gbits = gate_bits<GATE_BF16>(a.g, p.t0, p.len, a.hv, h, lane);
+        bbits = gate_bits<GATE_BF16>(a.beta, p.t0, p.len, a.hv, h, lane);
+    }
     {
         constexpr int PR = D / 8, NP = C * PR / kBwdThreads;
         v4u32 rk[NP];
@@ -280,7 +281,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
         reinterpret_cast<uint4 *>(sA)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (wave == 0) {
         float G2, bv, GL2;
-        chunk_gates<GATE_BF16>(a, p.t0, p.len, h, lane, G2, bv, GL2);
+        chunk_gates<GATE_BF16>(gbits, bbits, G2, bv, GL2);
         sG2[lane] = G2;
         sB[lane] = bv;
     }
@@ -793,6 +794,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
         const uint16_t *Sb = p.c > 0 ? a.hck + (rh - a.hv) * D * D : nullptr;
         const float *Sg = p.c == 0 && a.h0 ? a.h0 + (p.n * a.hv + h) * D * D : nullptr;
         bf16x4 ub[4];   // this wave's dU tiles (dv tile nt), bf16
+        uint32_t gbits = 0u, bbits = 0u;   // wave 0: raw gate and beta bits of the chunk
         if (colwave) {
             const uint16_t *ug = a.du + rh * (C * D);
 #pragma unroll
@@ -805,6 +807,10 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
             constexpr int NS4 = D * D / 4 / kBwdThreads;   // 8-byte pieces (4 bf16) of the state per thread
             v4u32 rv[NP], ro[NP], rt[NT8];
             v2u32 rs4[NS4];
+            if (wave == 0) {
+                gbits = gate_bits<GATE_BF16>(a.g, p.t0, p.len, a.hv, h, lane);
+                bbits = gate_bits<GATE_BF16>(a.beta, p.t0, p.len, a.hv, h, lane);
+            }
             fetch_rows<D, IN_BF16, NP, kBwdThreads>(rv, a.v, p.t0, p.len, a.hv, h, tid);
             fetch_rows<D, IN_BF16, NP, kBwdThreads>(ro, a.dout, p.t0, p.len, a.hv, h, tid);
             if (Sb) {
@@ -859,7 +865,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
         }
         if (wave == 0) {
             float G2, bv, GL2;
-            chunk_gates<GATE_BF16>(a, p.t0, p.len, h, lane, G2, bv, GL2);
+            chunk_gates<GATE_BF16>(gbits, bbits, G2, bv, GL2);
             sG2[lane] = G2;
             sB[lane] = bv;
             sGam[lane] = fast_exp2(G2);
