@@ -50,8 +50,10 @@
  *   hck   [NT, Hv, dk, dv] with NT = off[n_seq]     (NULL = not written)
  *   gk    [T, Hv, dk] per-channel log-gates (gdr_oracle_kda_fwd only; replaces g)
  */
+#define _GNU_SOURCE   /* sched_getaffinity, CPU_COUNT */
 #include <math.h>
 #include <pthread.h>
+#include <sched.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -151,10 +153,18 @@ static int by_length_desc(const void *a, const void *b)
     return ia < ib ? -1 : (ia > ib);
 }
 
-/* Threads actually used for a call with `requested` threads (<= 0: all cores). */
+/* Threads actually used for a call with `requested` threads (<= 0: the cores
+ * this process may run on, at most OMP_NUM_THREADS when that is set). */
 int gdr_oracle_threads(int requested, int64_t n_items)
 {
-    long n = requested > 0 ? requested : sysconf(_SC_NPROCESSORS_ONLN);
+    long n = requested;
+    if (n <= 0) {
+        cpu_set_t set;
+        n = sched_getaffinity(0, sizeof(set), &set) == 0 ? CPU_COUNT(&set) : sysconf(_SC_NPROCESSORS_ONLN);
+        const char *env = getenv("OMP_NUM_THREADS");
+        const long cap = env ? strtol(env, NULL, 10) : 0;
+        if (cap > 0 && cap < n) n = cap;
+    }
     if (n < 1) n = 1;
     if (n > n_items) n = n_items > 0 ? n_items : 1;
     return (int)n;

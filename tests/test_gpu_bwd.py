@@ -1,7 +1,7 @@
 """Backward pass on the GPU against the fp64 backward oracle, element by
 element: every gradient (dq, dk, dv, dg, dbeta, dh0) on the seeded workloads,
-ragged chunks, ghosts, GQA, both head sizes and both gate dtypes; at the full
-long and packed sizes on a sample of heads the oracle computes one by one.
+ragged chunks, ghosts, GQA, both head sizes and both gate dtypes, and the
+long and benchmark workloads at full size on every head.
 Also: repeated calls and ghost padding are bitwise reproducible."""
 import numpy as np
 import pytest
@@ -123,20 +123,19 @@ def test_bwd_slow_and_no_decay(g_mode):
     _compare(_gpu(d), _oracle(d), "decay %s" % g_mode)
 
 
-def test_bwd_long_sampled_heads():
-    """T = 20468 (last chunk 52 tokens), 16 heads: all gradients of heads 0 and 9."""
+def test_bwd_long_all_heads():
+    """T = 20468 (last chunk 52 tokens), 16 heads: all gradients of every head."""
     d = _case("long_T20468_H16_d128")
     got = _gpu(d)
-    heads = ([0, 9], [0, 9])
-    _compare(got, _oracle(d, heads=heads), "long T20468 heads 0, 9", heads=heads)
+    _compare(got, _oracle(d), "long T20468 all heads")
 
 
-def test_bwd_packed64k_sampled_heads():
-    """The benchmark workload at full size: q/k head 5 and its v-heads 10, 11."""
+def test_bwd_packed64k_all_heads():
+    """The benchmark workload at full size: all six gradients of every head,
+    element by element (the fp64 oracle takes about half a minute on 16 cores)."""
     d = _case("packed64k_gqa_Hk16_Hv32_d128")
     got = _gpu(d)
-    heads = ([5], [10, 11])
-    _compare(got, _oracle(d, heads=heads), "packed64k k-head 5", heads=heads)
+    _compare(got, _oracle(d), "packed64k all heads")
 
 
 def test_bwd_bitwise_repeatable_and_ghost_padding():

@@ -1,7 +1,7 @@
 """Per-channel-gate forward (gdr_chunk_kda_fwd) on the GPU against the fp64
 oracle gdr_kda_fwd, element by element, with the forward's tolerances: the
 seeded workloads with one log-gate per key channel, ragged chunks, ghosts, GQA,
-both head sizes, fp32 gates; the full packed workload on sampled heads.  f32
+both head sizes, fp32 gates; the full packed workload on every head.  f32
 inputs run in fp32 arithmetic and meet the f32 tolerances, at any gate."""
 import numpy as np
 import pytest
@@ -146,13 +146,13 @@ def test_kda_f32_inputs_steep_gates(gval):
     _check(o, ht, o_ref, ht_ref, _real(d), "kda f32 g=%g" % gval, "fp32")
 
 
-def test_kda_packed64k_sampled_heads():
-    """The benchmark workload with per-channel gates: q/k head 3 and its v-heads 6, 7."""
+def test_kda_packed64k_all_heads():
+    """The benchmark workload with per-channel gates, every head element by
+    element (the fp64 oracle takes about ten seconds on 16 cores)."""
     import gdr_inputs
     w = gdr_inputs.WORKLOADS["packed64k_gqa_Hk16_Hv32_d128"]
     d = gdr_inputs.generate(w)
     gk = gdr_inputs.generate_kda_gates(d, seed=w.seed + 3)
     o, ht = _run(d, gk)
-    heads = ([3], [6, 7])
-    o_ref, ht_ref = _ref(d, gk, heads=heads)
-    _check(o[:, :, heads[1]], ht[:, heads[1]], o_ref, ht_ref, _real(d), "kda packed64k heads 6, 7")
+    o_ref, ht_ref = _ref(d, gk)
+    _check(o, ht, o_ref, ht_ref, _real(d), "kda packed64k all heads")
