@@ -631,22 +631,30 @@ __global__ void __launch_bounds__(kChainThreads) gdr_bwd_chain_kernel(BwdArgs a)
                         f[e] = static_cast<__bf16>(static_cast<float>(f[e]) * (e < 4 ? b0[e] : b1[e - 4]));
                     at[hh][kk2] = f;
                 }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const bf16x8 aq = frag_cols(sQ, PQ, 16 * mt, 32 * kk, l16, lq);
-                f32x4 w0 = zero4(), w1 = zero4();
+            // the w tiles of dk block mt + 1 are formed while block mt's
+            // products run, so their results are ready when converted
+            auto wtiles = [&](int mt, f32x4 &w0, f32x4 &w1) __attribute__((always_inline)) {
+                w0 = zero4();
+                w1 = zero4();
 #pragma unroll
                 for (int kk2 = 0; kk2 <= kk; ++kk2) {
                     const bf16x8 bk = frag_cols_kp(sK, PKR, 16 * mt, 32 * kk2, l16, lq);
                     w0 = mfma32(at[0][kk2], bk, w0);
                     w1 = mfma32(at[1][kk2], bk, w1);
                 }
+            };
+            f32x4 wn0, wn1;
+            wtiles(0, wn0, wn1);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const f32x4 w0 = wn0, w1 = wn1;
+                if (mt + 1 < MT) wtiles(mt + 1, wn0, wn1);
+                const bf16x8 aq = frag_cols(sQ, PQ, 16 * mt, 32 * kk, l16, lq);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) dH[mt][nt] = mfma32(aq, bo[nt], dH[mt][nt]);
                 const bf16x8 aw = cat(cvt4(w0), cvt4(w1));
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) {
-                    dH[mt][nt] = mfma32(aq, bo[nt], dH[mt][nt]);
-                    dH[mt][nt] = mfma32(aw, bu[nt], dH[mt][nt]);
-                }
+                for (int nt = 0; nt < NTW; ++nt) dH[mt][nt] = mfma32(aw, bu[nt], dH[mt][nt]);
             }
         }
     }
