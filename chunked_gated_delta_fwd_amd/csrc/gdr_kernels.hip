@@ -471,6 +471,10 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         st4(Ddb(par) + (16 * b + l16) * PDI + 4 * lq, cvt4(d1 * dec));
     };
 
+    // CK = 2: the state in bf16, converted once at the end of a chunk for both
+    // its store and the next chunk's K H (a conversion per store into one
+    // register pair would make each store wait for the previous one to issue)
+    bf16x4 hbn[KB][NTW];
     auto to_bf16_state = [&](bf16x4 (&hb)[KB][NTW]) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -491,7 +495,14 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
         const float *veg = vEG(par), *vgam = vGam(par);
 
         bf16x4 hb[KB][NTW];
-        to_bf16_state(hb);
+        if constexpr (CK == 2) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) hb[kb][nt] = hbn[kb][nt];
+        } else {
+            to_bf16_state(hb);
+        }
 
         // R~ = V - diag(e^G) (K H): rows token 16blk+4lq+r, column dv (the
         // beta factor of the right-hand side sits in the stored inverses)
@@ -676,6 +687,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                 }
             }
         }
+        if constexpr (CK == 2) to_bf16_state(hbn);   // for the store below and the next chunk's K H
         if constexpr (CK != 0) {
             // the state after this chunk: at its chunk row (CK = 2), or (CK = 1)
             // at the row of the sequence's last checkpoint when the chunk ends
@@ -698,7 +710,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
                     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                         for (int nt = 0; nt < NTW; ++nt)
-                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, cvt4(hs[kb][nt])), rd,
+                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, hbn[kb][nt]), rd,
                                                                   lane_off, (kb * NTW + nt) * 64 * 8, 0);
                 } else {
                     const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(a.hck + (row * a.hv + h) * DK * DV, DK * DV * 4);
@@ -739,6 +751,7 @@ __global__ void __launch_bounds__(kFwdThreads) gdr_fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     hs[kb][nt][r] = a.h0 ? a.h0[sbase + dk_of(kb, 4 * lq + r) * DV + dv_of(nt, l16)] : 0.f;
+        if constexpr (CK == 2) to_bf16_state(hbn);
         load_v(0);
         wait_for(cPrep, 4u, peek(cPrep));   // q, k of chunk 0 stored
         int b3 = 0;
