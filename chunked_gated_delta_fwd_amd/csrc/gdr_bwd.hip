@@ -33,8 +33,8 @@
 // q and k gradients of the v-heads that share a q/k head add up.
 //
 // Kernels (after the forward kernel has written the state after every chunk):
-//   gdr_bwd_prep_kernel   per (chunk, v-head), in parallel: T by block
-//                         substitution.
+//   gdr_bwd_prep_kernel   per (chunk, v-head pair of one q/k head, or one
+//                         v-head), in parallel: T by block substitution.
 //   gdr_bwd_chain_kernel  per (sequence, v-head), chunks in reverse order:
 //                         dS' kept in fp32 registers, dU = dU0 + its chain
 //                         part (dU0 and w formed in the chain from q, k, dO
@@ -89,6 +89,12 @@ template <bool BF16>
 __device__ __forceinline__ void store_elem(void *p, int64_t i, float v) {
     if constexpr (BF16) reinterpret_cast<uint16_t *>(p)[i] = bf16_bits(v);
     else reinterpret_cast<float *>(p)[i] = v;
+}
+// four consecutive elements from element i (a multiple of 4)
+template <bool BF16>
+__device__ __forceinline__ void store_four(void *p, int64_t i, f32x4 v) {
+    if constexpr (BF16) *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(p) + i) = cvt4(v);
+    else *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p) + i) = v;
 }
 
 // The same rows into registers, 16 bytes of bf16 per piece, through a buffer
@@ -223,9 +229,11 @@ __device__ __forceinline__ void chunk_gates(uint32_t gbits, uint32_t bbits, floa
 }
 
 // --------------------------------------------------------------------------
-// Per (chunk, v-head): T.
+// Per (chunk, NH v-heads of one q/k head): T.  With NH = 2 the k rows and
+// K K^T are shared by the two v-heads, and all 8 waves work in the
+// substitution phases (four per v-head).
 // --------------------------------------------------------------------------
-template <int D>
+template <int D, int NH>
 struct PrepLds {
     // Row pitches (bf16 elements) by how each array is read, against the 32
     // four-byte LDS banks: 8-byte row fragments (16 lanes, one row each) are
@@ -235,37 +243,39 @@ struct PrepLds {
     static constexpr int PP = C + 4;    // A [64][64]: row fragments
     static constexpr int PD = 20;       // [16][16] bf16 blocks
     static constexpr int oK = 0;
-    static constexpr int oA = oK + C * PK * 2;        // diag(b) A~, strictly lower, [i][j]
-    static constexpr int oG = oA + C * PP * 2;        // f32 [64] x2: G log2(e), b
-    static constexpr int oDi = oG + 2 * C * 4;        // bf16 inverses of the diagonal blocks of I + diag(b) A~
-    static constexpr int bytes = oDi + 4 * 16 * PD * 2;
+    static constexpr int oA = oK + C * PK * 2;         // per v-head: diag(b) A~, strictly lower, [i][j]
+    static constexpr int oG = oA + NH * C * PP * 2;    // per v-head f32 [64] x2: G log2(e), b
+    static constexpr int oDi = oG + NH * 2 * C * 4;    // per v-head: bf16 inverses of the diagonal blocks of I + diag(b) A~
+    static constexpr int bytes = oDi + NH * 4 * 16 * PD * 2;
 };
 
-template <int D, bool IN_BF16, bool GATE_BF16>
+template <int D, bool IN_BF16, bool GATE_BF16, int NH>
 __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
-    using Ly = PrepLds<D>;
+    using Ly = PrepLds<D, NH>;
     constexpr int PK = Ly::PK, PP = Ly::PP, PD = Ly::PD;
     extern __shared__ __align__(16) unsigned char lds[];
     uint16_t *sK = reinterpret_cast<uint16_t *>(lds + Ly::oK);
-    uint16_t *sA = reinterpret_cast<uint16_t *>(lds + Ly::oA);
-    uint16_t *sDi = reinterpret_cast<uint16_t *>(lds + Ly::oDi);
-    float *sG2 = reinterpret_cast<float *>(lds + Ly::oG);
-    float *sB = sG2 + C;
+    // per v-head s of the block: A at sA0 + s C PP, G log2(e) at sG0 + 2 s C
+    // (b C further on), inverses at sDi0 + 64 s PD
+    uint16_t *sA0 = reinterpret_cast<uint16_t *>(lds + Ly::oA);
+    uint16_t *sDi0 = reinterpret_cast<uint16_t *>(lds + Ly::oDi);
+    float *sG0 = reinterpret_cast<float *>(lds + Ly::oG);
 
     ChunkAt p;
-    // one work item per (chunk row, v-head); v-heads of a q/k head share an L2
-    const int64_t item = gqa_xcd_item(blockIdx.x, gridDim.x, a.hv, a.hk);
-    const int64_t crow = item / a.hv;
+    // one work item per (chunk row, group of NH v-heads); groups of one q/k
+    // head share an L2
+    const int ng = a.hv / NH;
+    const int64_t item = gqa_xcd_item(blockIdx.x, gridDim.x, ng, a.hk);
+    const int64_t crow = item / ng;
     if (!chunk_at(a, crow, p)) return;
-    const int h = static_cast<int>(item % a.hv);
-    const int hk = h / (a.hv / a.hk);
+    const int hb = static_cast<int>(item % ng) * NH;   // the block's first v-head
+    const int hk = hb / (a.hv / a.hk);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lq = lane >> 4;
-    const int64_t rh = crow * a.hv + h;
 
     uint32_t gbits = 0u, bbits = 0u;
-    if (wave == 0) {
-        gbits = gate_bits<GATE_BF16>(a.g, p.t0, p.len, a.hv, h, lane);
-        bbits = gate_bits<GATE_BF16>(a.beta, p.t0, p.len, a.hv, h, lane);
+    if (wave < NH) {   // wave s: gate and beta of v-head hb + s
+        gbits = gate_bits<GATE_BF16>(a.g, p.t0, p.len, a.hv, hb + wave, lane);
+        bbits = gate_bits<GATE_BF16>(a.beta, p.t0, p.len, a.hv, hb + wave, lane);
     }
     {
         constexpr int PR = D / 8, NP = C * PR / kBwdThreads;
@@ -277,48 +287,58 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
             st16<PK % 8 == 0>(sK + (i / PR) * PK + 8 * (i % PR), rk[j]);
         }
     }
-    for (int i = tid; i < C * PP / 8; i += kBwdThreads)   // A: blocks above the diagonal stay zero
-        reinterpret_cast<uint4 *>(sA)[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (wave == 0) {
+    for (int i = tid; i < NH * C * PP / 8; i += kBwdThreads)   // A: blocks above the diagonal stay zero
+        reinterpret_cast<uint4 *>(sA0)[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (wave < NH) {
         float G2, bv, GL2;
         chunk_gates<GATE_BF16>(gbits, bbits, G2, bv, GL2);
-        sG2[lane] = G2;
-        sB[lane] = bv;
+        sG0[2 * wave * C + lane] = G2;
+        sG0[(2 * wave + 1) * C + lane] = bv;
     }
     __syncthreads();
 
-    // gated K K^T, strictly lower and times b (A): its ten lower 16x16 blocks
+    // K K^T, strictly lower, gated and times b per v-head (A): its ten lower
+    // 16x16 blocks.  Formed transposed (the row block as the B operand), so
+    // that a lane holds four consecutive columns j of one row i.
     for (int t = wave; t < 10; t += 8) {
         const int bi = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
         const int bj = t - bi * (bi + 1) / 2;
         f32x4 acc = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < D; k0 += 32)
-            acc = mfma32(frag_rows(sK, PK, 16 * bi, k0, l16, lq), frag_rows(sK, PK, 16 * bj, k0, l16, lq), acc);
-        const int j = 16 * bj + l16;
-        const float gj = sG2[j];
+            acc = mfma32(frag_rows(sK, PK, 16 * bj, k0, l16, lq), frag_rows(sK, PK, 16 * bi, k0, l16, lq), acc);
+        const int i = 16 * bi + l16, j0 = 16 * bj + 4 * lq;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * bi + 4 * lq + r;
-            const float e = fast_exp2(sG2[i] - gj);   // used only where j < i (exponent <= 0)
-            sA[i * PP + j] = bf16_bits(j < i ? sB[i] * e * acc[r] : 0.f);
+        for (int s = 0; s < NH; ++s) {
+            const float *sG2 = sG0 + 2 * s * C, *sB = sG2 + C;
+            const float gi = sG2[i], bi_ = sB[i];
+            f32x4 out;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float e = fast_exp2(gi - sG2[j0 + r]);   // used only where j < i (exponent <= 0)
+                out[r] = j0 + r < i ? bi_ * e * acc[r] : 0.f;
+            }
+            st4(sA0 + s * C * PP + i * PP + j0, cvt4(out));
         }
     }
     __syncthreads();
 
     // Diagonal blocks: column l16 of (I + A_bb)^-1 by forward substitution in
     // fp32 on the bf16 block (every 16-lane row of the wave computes the same
-    // column).
+    // column).  Wave 4 s + b: block b of v-head s.
+    const int s = wave >> 2;
+    const uint16_t *sA = sA0 + s * C * PP;
+    uint16_t *sDi = sDi0 + s * 64 * PD;
     f32x4 dcol = zero4();
-    if (wave < 4) {
-        const int b = wave;
+    if (wave < 4 * NH) {
+        const int b = wave & 3;
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float s = i == l16 ? 1.f : 0.f;
+            float sm = i == l16 ? 1.f : 0.f;
 #pragma unroll
-            for (int m = 0; m < i; ++m) s -= bf16_to_f(sA[(16 * b + i) * PP + 16 * b + m]) * x[m];
-            x[i] = s;
+            for (int m = 0; m < i; ++m) sm -= bf16_to_f(sA[(16 * b + i) * PP + 16 * b + m]) * x[m];
+            x[i] = sm;
         }
         if (lq == 0) {
 #pragma unroll
@@ -330,9 +350,10 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
     __syncthreads();
 
     // Column block j of T: X_j = D_j, X_i = -D_i sum_{m=j}^{i-1} A_im X_m
-    // (C tiles chained through registers).  T^T goes to memory.
-    if (wave < 4) {
-        const int j = wave;
+    // (C tiles chained through registers).  T^T goes to memory.  Wave 4 s + j:
+    // column block j of v-head s.
+    if (wave < 4 * NH) {
+        const int j = wave & 3;
         f32x4 X[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) X[i] = i == j ? dcol : zero4();
@@ -347,7 +368,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_prep_kernel(BwdArgs a) {
                 X[i] = -mfma16z(ld4(sDi + (16 * i + l16) * PD + 4 * lq), cvt4(E), zero4());
             }
         }
-        uint16_t *tg = a.tmat + rh * (C * C);
+        uint16_t *tg = a.tmat + (crow * a.hv + hb + s) * (C * C);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             *reinterpret_cast<bf16x4 *>(tg + (16 * j + l16) * C + 16 * i + 4 * lq) = cvt4(X[i]);
@@ -882,9 +903,12 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
         }
         __syncthreads();
 
-        // X = K S, R~ = V - e^G X, U = T diag(b) R~, dW = T^T dU, dV = b dW (dv tile nt)
+        // X = K S, R~ = V - e^G X, U = T diag(b) R~, dW = T^T dU, dV = b dW (dv tile nt).
+        // U and dW are also formed transposed (the same products with the
+        // operands swapped: a lane then holds four consecutive dv columns of
+        // one token), for 8-byte stores of U, dW and dV.
         if (colwave) {
-            f32x4 Rt[4], U[4], dW[4];
+            f32x4 Rt[4], Ut[4], dW[4], dWt[4];
             bf16x4 wb[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) Rt[mt] = zero4();
@@ -903,7 +927,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
                     w[r] = sB[i] * Rt[mt][r];
                 }
                 wb[mt] = cvt4(w);
-                U[mt] = dW[mt] = zero4();
+                Ut[mt] = dW[mt] = dWt[mt] = zero4();
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -911,21 +935,22 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
                 const bf16x8 bu = cat(ub[2 * kk], ub[2 * kk + 1]);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
-                    U[mt] = mfma32(frag_cols(sT, PP, 16 * mt, 32 * kk, l16, lq), bw, U[mt]);
-                    dW[mt] = mfma32(frag_rows(sT, PP, 16 * mt, 32 * kk, l16, lq), bu, dW[mt]);
+                    const bf16x8 tr = frag_rows(sT, PP, 16 * mt, 32 * kk, l16, lq);
+                    Ut[mt] = mfma32(bw, frag_cols(sT, PP, 16 * mt, 32 * kk, l16, lq), Ut[mt]);
+                    dW[mt] = mfma32(tr, bu, dW[mt]);
+                    dWt[mt] = mfma32(bu, tr, dWt[mt]);
                 }
             }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
+                const int i = 16 * mt + l16, c = 16 * nt + 4 * lq;   // transposed tiles: token i, dv c..c+3
+                const float bi = sB[i];
+                if (i < p.len) store_four<IN_BF16>(a.dv, ((p.t0 + i) * a.hv + h) * D + c, f32x4{bi * dWt[mt][0], bi * dWt[mt][1], bi * dWt[mt][2], bi * dWt[mt][3]});
+                st4(sU + i * PKP + kpos(c), cvt4(Ut[mt]));
+                st4(sDW + i * PKP + kpos(c), cvt4(dWt[mt]));
                 float pb[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * mt + 4 * lq + r;
-                    if (i < p.len) store_elem<IN_BF16>(a.dv, ((p.t0 + i) * a.hv + h) * D + 16 * nt + l16, sB[i] * dW[mt][r]);
-                    sU[i * PKP + kpos(16 * nt + l16)] = bf16_bits(U[mt][r]);
-                    sDW[i * PKP + kpos(16 * nt + l16)] = bf16_bits(dW[mt][r]);
-                    pb[r] = row_sum16(dW[mt][r] * Rt[mt][r]);
-                }
+                for (int r = 0; r < 4; ++r) pb[r] = row_sum16(dW[mt][r] * Rt[mt][r]);
                 if (l16 == 15) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) sRB[wave * C + 16 * mt + 4 * lq + r] = pb[r];
@@ -978,26 +1003,30 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
         for (int t = wave; t < 16; t += 8) {
             const int bi = t >> 2, bj = t & 3;
             f32x4 z0 = zero4(), z1 = zero4();
+            // transposed tiles (U rows as the A operand): a lane holds four
+            // consecutive columns j of one row i, for 8-byte stores
             if (bi >= bj) {
 #pragma unroll
                 for (int kk = 0; kk < D / 32; ++kk) {
                     const bf16x8 bu = kfrag8(sU, PKP, 16 * bj, 32 * kk, l16, lq);
-                    z0 = mfma32(kfrag8(sO, PKP, 16 * bi, 32 * kk, l16, lq), bu, z0);
-                    z1 = mfma32(kfrag8(sDW, PKP, 16 * bi, 32 * kk, l16, lq), bu, z1);
+                    z0 = mfma32(bu, kfrag8(sO, PKP, 16 * bi, 32 * kk, l16, lq), z0);
+                    z1 = mfma32(bu, kfrag8(sDW, PKP, 16 * bi, 32 * kk, l16, lq), z1);
                 }
             }
-            const int j = 16 * bj + l16;
-            const float gj = sG2[j];
+            const int i = 16 * bi + l16, j0 = 16 * bj + 4 * lq;
+            const float gi = sG2[i], bti = sB[i];
+            f32x4 zs, bn, bb;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * bi + 4 * lq + r;
-                const float e = fast_exp2(sG2[i] - gj);   // used only where j <= i
-                const float zs = j <= i ? a.scale * e * z0[r] : 0.f;
-                const float bn = j < i ? -e * z1[r] : 0.f;
-                sZs[i * PP + j] = bf16_bits(zs);
-                sBn[i * PP + j] = bf16_bits(bn);
-                sBb[i * PP + j] = bf16_bits(sB[i] * bn);
+                const int j = j0 + r;
+                const float e = fast_exp2(gi - sG2[j]);   // used only where j <= i
+                zs[r] = j <= i ? a.scale * e * z0[r] : 0.f;
+                bn[r] = j < i ? -e * z1[r] : 0.f;
+                bb[r] = bti * bn[r];
             }
+            st4(sZs + i * PP + j0, cvt4(zs));
+            st4(sBn + i * PP + j0, cvt4(bn));
+            st4(sBb + i * PP + j0, cvt4(bb));
         }
         __syncthreads();
 
@@ -1097,8 +1126,14 @@ hipError_t launch_with_lds(K kern, dim3 grid, dim3 block, int lds, hipStream_t s
 template <int D, bool IN_BF16, bool GATE_BF16>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     const unsigned rows = static_cast<unsigned>(a.rows);
-    hipError_t e = launch_with_lds(gdr_bwd_prep_kernel<D, IN_BF16, GATE_BF16>, dim3(static_cast<unsigned>(rows * a.hv)),
-                                   dim3(kBwdThreads), PrepLds<D>::bytes, stream, a);
+    // two v-heads per prep block where they share a q/k head
+    hipError_t e = (a.hv / a.hk) % 2 == 0
+                       ? launch_with_lds(gdr_bwd_prep_kernel<D, IN_BF16, GATE_BF16, 2>,
+                                         dim3(static_cast<unsigned>(rows * (a.hv / 2))), dim3(kBwdThreads),
+                                         PrepLds<D, 2>::bytes, stream, a)
+                       : launch_with_lds(gdr_bwd_prep_kernel<D, IN_BF16, GATE_BF16, 1>,
+                                         dim3(static_cast<unsigned>(rows * a.hv)), dim3(kBwdThreads),
+                                         PrepLds<D, 1>::bytes, stream, a);
     if (e != hipSuccess) return e;
     e = launch_with_lds(gdr_bwd_chain_kernel<D, IN_BF16, GATE_BF16>,
                         dim3(static_cast<unsigned>(a.n_seq * a.hv)), dim3(kChainThreads),
@@ -1115,7 +1150,7 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
 }
 
 static_assert(GradLds<128>::bytes <= 160 * 1024, "gradient kernel LDS");
-static_assert(PrepLds<128>::bytes <= 160 * 1024, "prep kernel LDS");
+static_assert(PrepLds<128, 2>::bytes <= 160 * 1024, "prep kernel LDS");
 static_assert(ChainLds<128>::bytes <= 160 * 1024, "chain kernel LDS");
 
 }  // namespace
