@@ -72,6 +72,11 @@ __device__ __forceinline__ bf16x8 frag_cols_kp(const uint16_t *M, int pitch, int
     return cat(ld4_tr(p), ld4_tr(p + 16 * pitch));
 }
 __device__ __forceinline__ float bf16_to_f(uint16_t u) { return __uint_as_float(static_cast<uint32_t>(u) << 16); }
+// Rows row0 + 4 lq + r (r = 0..3) of column col0 + l16, as floats: a lane's
+// C-tile positions, by one transposing read.
+__device__ __forceinline__ f32x4 col4(const uint16_t *M, int pitch, int row0, int col0, int l16, int lq) {
+    return up4(ld4_tr(M + (row0 + 4 * lq + (l16 >> 2)) * pitch + col0 + 4 * (l16 & 3)));
+}
 
 // Sum over each 16-lane row of the wave, left in the row's last lane.
 __device__ __forceinline__ float row_sum16(float x) {
@@ -829,9 +834,9 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) ub[mt] = *reinterpret_cast<const bf16x4 *>(ug + ((mt * NTD + nt) * 64 + lane) * 4);
         }
-        __syncthreads();   // the previous v-head's reads of LDS are done
         {
-            // all of this v-head's staging loads are issued before the first store
+            // all of this v-head's staging loads are issued before the barrier
+            // (they go to registers), and so before the first store
             constexpr int PR = D / 8, NP = C * PR / kBwdThreads, NT8 = C * C / 8 / kBwdThreads;
             constexpr int NS4 = D * D / 4 / kBwdThreads;   // 8-byte pieces (4 bf16) of the state per thread
             v4u32 rv[NP], ro[NP], rt[NT8];
@@ -857,6 +862,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
             const uint16_t *tg = a.tmat + rh * (C * C);
 #pragma unroll
             for (int j = 0; j < NT8; ++j) rt[j] = *reinterpret_cast<const v4u32 *>(tg + 8 * (tid + j * kBwdThreads));
+            __syncthreads();   // the previous v-head's reads of LDS are done
             if (wave == 0 && hh > 0) GDR_GRAD_DG(h - 1, lane)   // the previous v-head's, while the loads fly
 #pragma unroll
             for (int j = 0; j < NP; ++j) {
@@ -920,10 +926,11 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 f32x4 w;
+                const f32x4 vv = col4(sV, PK, 16 * mt, 16 * nt, l16, lq);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * mt + 4 * lq + r;
-                    Rt[mt][r] = bf16_to_f(sV[i * PK + 16 * nt + l16]) - sGam[i] * Rt[mt][r];   // R~ = V - e^G X
+                    Rt[mt][r] = vv[r] - sGam[i] * Rt[mt][r];   // R~ = V - e^G X
                     w[r] = sB[i] * Rt[mt][r];
                 }
                 wb[mt] = cvt4(w);
@@ -1043,13 +1050,15 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
             }
             float lastp = 0.f;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt) {
+                const f32x4 kv = col4(sK, PK, 16 * mt, 16 * nt, l16, lq);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * mt + 4 * lq + r;
                     Kc[mt][r] *= sLam[i];
-                    lastp += bf16_to_f(sK[i * PK + 16 * nt + l16]) * Kc[mt][r];
+                    lastp += kv[r] * Kc[mt][r];
                 }
+            }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const bf16x8 bk = frag_cols(sK, PK, 16 * nt, 32 * kk, l16, lq);
@@ -1065,11 +1074,11 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 float pg[4], pb[4];
+                const f32x4 q4 = col4(sQ, PK, 16 * mt, 16 * nt, l16, lq), k4 = col4(sK, PK, 16 * mt, 16 * nt, l16, lq);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * mt + 4 * lq + r;
-                    const int col = 16 * nt + l16;
-                    const float qv = bf16_to_f(sQ[i * PK + col]), kv = bf16_to_f(sK[i * PK + col]);
+                    const float qv = q4[r], kv = k4[r];
                     const float bt = sB[i];
                     const float dq = dQt[mt][r];
                     const float dkr = bt * (Yb[mt][r] - sGam[i] * dK1[mt][r]);
