@@ -793,28 +793,28 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) accQ[mt] = accK[mt] = zero4();
 
-    // dg: reverse prefix sums of dG within the chunk; dbeta (wave 0, for v-head
-    // hv_, from the row sums the previous v-head's phases left in LDS).  Run
-    // at the next v-head's staging, while its loads are in flight.
-#define GDR_GRAD_DG(hv_, ln_)                                                                  \
-    {                                                                                        \
-        float dG = 0.f, db = 0.f;                                                            \
-        for (int w = 0; w < NTD; ++w) {                                                      \
-            dG += sRG[w * C + (ln_)];                                                        \
-            db += sRB[w * C + (ln_)];                                                        \
-        }                                                                                    \
+    // dg: reverse prefix sums of dG within the chunk (wave 0); dbeta (wave 2);
+    // for v-head hv_ of parity hp_, from the row sums the previous v-head's
+    // phases left in LDS.  Run at the next v-head's staging, while its loads
+    // are in flight; wave 1 forms that v-head's gate vectors meanwhile (e^{G_L}
+    // is kept per v-head parity for this reason).
+#define GDR_GRAD_DG(hv_, ln_, hp_)                                                             \
+    if (wave == 0) {                                                                         \
+        float dG = 0.f;                                                                      \
+        for (int w = 0; w < NTD; ++w) dG += sRG[w * C + (ln_)];                              \
         if ((ln_) == 63) {                                                                   \
             float dot = 0.f, kl = 0.f;                                                       \
             for (int w = 0; w < 8; ++w) dot += sXd[w];                                       \
             for (int w = 0; w < NTD; ++w) kl += sXl[w];                                      \
-            dG += sGL[0] * dot + kl;                                                         \
+            dG += sGL[(hp_)] * dot + kl;                                                     \
         }                                                                                    \
         const float inc = wave_inclusive_scan(dG);                                           \
         const float dgv = lane63(inc) - inc + dG;                                            \
-        if ((ln_) < p.len) {                                                                 \
-            a.dg[(p.t0 + (ln_)) * a.hv + (hv_)] = dgv;                                       \
-            a.dbeta[(p.t0 + (ln_)) * a.hv + (hv_)] = db;                                     \
-        }                                                                                    \
+        if ((ln_) < p.len) a.dg[(p.t0 + (ln_)) * a.hv + (hv_)] = dgv;                         \
+    } else if (wave == 2) {                                                                  \
+        float db = 0.f;                                                                      \
+        for (int w = 0; w < NTD; ++w) db += sRB[w * C + (ln_)];                              \
+        if ((ln_) < p.len) a.dbeta[(p.t0 + (ln_)) * a.hv + (hv_)] = db;                       \
     }
     for (int hh = 0; hh < G; ++hh) {
         // lane indices re-derived opaquely in every iteration, so that the
@@ -828,7 +828,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
         const uint16_t *Sb = p.c > 0 ? a.hck + (rh - a.hv) * D * D : nullptr;
         const float *Sg = p.c == 0 && a.h0 ? a.h0 + (p.n * a.hv + h) * D * D : nullptr;
         bf16x4 ub[4];   // this wave's dU tiles (dv tile nt), bf16
-        uint32_t gbits = 0u, bbits = 0u;   // wave 0: raw gate and beta bits of the chunk
+        uint32_t gbits = 0u, bbits = 0u;   // wave 1: raw gate and beta bits of the chunk
         if (colwave) {
             const uint16_t *ug = a.du + rh * (C * D);
 #pragma unroll
@@ -841,7 +841,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
             constexpr int NS4 = D * D / 4 / kBwdThreads;   // 8-byte pieces (4 bf16) of the state per thread
             v4u32 rv[NP], ro[NP], rt[NT8];
             v2u32 rs4[NS4];
-            if (wave == 0) {
+            if (wave == 1) {
                 gbits = gate_bits<GATE_BF16>(a.g, p.t0, p.len, a.hv, h, lane);
                 bbits = gate_bits<GATE_BF16>(a.beta, p.t0, p.len, a.hv, h, lane);
             }
@@ -863,7 +863,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < NT8; ++j) rt[j] = *reinterpret_cast<const v4u32 *>(tg + 8 * (tid + j * kBwdThreads));
             __syncthreads();   // the previous v-head's reads of LDS are done
-            if (wave == 0 && hh > 0) GDR_GRAD_DG(h - 1, lane)   // the previous v-head's, while the loads fly
+            if (hh > 0) GDR_GRAD_DG(h - 1, lane, (hh - 1) & 1)   // the previous v-head's, while the loads fly
 #pragma unroll
             for (int j = 0; j < NP; ++j) {
                 const int i = tid + j * kBwdThreads, off = (i / PR) * PK + 8 * (i % PR);
@@ -898,14 +898,14 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
                 *reinterpret_cast<v4u32 *>(sT + (i / (C / 8)) * PP + 8 * (i % (C / 8))) = rt[j];
             }
         }
-        if (wave == 0) {
+        if (wave == 1) {
             float G2, bv, GL2;
             chunk_gates<GATE_BF16>(gbits, bbits, G2, bv, GL2);
             sG2[lane] = G2;
             sB[lane] = bv;
             sGam[lane] = fast_exp2(G2);
             sLam[lane] = fast_exp2(GL2 - G2);
-            if (lane == 0) sGL[0] = fast_exp2(GL2);
+            if (lane == 0) sGL[hh & 1] = fast_exp2(GL2);
         }
         __syncthreads();
 
@@ -1007,8 +1007,13 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
             part = lane63(wave_inclusive_scan(part));
             if (lane == 0) sXd[wave] = part;
         }
+        // tiles (bi, bj) in the order of a list with the ten lower tiles
+        // (bi >= bj) first, so that the two waves of each SIMD share about
+        // the same number of them; the six upper tiles only store zeros
         for (int t = wave; t < 16; t += 8) {
-            const int bi = t >> 2, bj = t & 3;
+            constexpr uint64_t kTiles = 0x2110003333222110ull;   // bi of list entry t in nibble t ...
+            constexpr uint64_t kTilesJ = 0x3323213210210100ull;  // ... and bj
+            const int bi = static_cast<int>((kTiles >> (4 * t)) & 15), bj = static_cast<int>((kTilesJ >> (4 * t)) & 15);
             f32x4 z0 = zero4(), z1 = zero4();
             // transposed tiles (U rows as the A operand): a lane holds four
             // consecutive columns j of one row i, for 8-byte stores
@@ -1103,7 +1108,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
     }
     // the last v-head's dg and dbeta
     __syncthreads();
-    if (wave == 0) GDR_GRAD_DG(hk * G + G - 1, tid & 63)
+    GDR_GRAD_DG(hk * G + G - 1, tid & 63, (G - 1) & 1)
 #undef GDR_GRAD_DG
 
     // dq, dk summed over the v-heads of this q/k head

@@ -101,6 +101,15 @@ def test_bwd_gqa_d64_with_state():
     _compare(_gpu(d), _oracle(d), "gqa d64 with h0 and dht")
 
 
+def test_bwd_gqa_odd_group_d128():
+    """Three v-heads per q/k head: the prep kernel then takes one v-head per
+    work-group (it pairs v-heads only within a q/k head)."""
+    import gdr_inputs
+    d = gdr_inputs.random_lengths_case(61, n_real=3, lo=20, hi=180, ghost_slots=1, hk=2, hv=6, d=128)
+    d.update(gdr_inputs.generate_grads(d, seed=62))
+    _compare(_gpu(d), _oracle(d), "gqa3 d128")
+
+
 def test_bwd_fp32_inputs_d128():
     import gdr_inputs
     d = gdr_inputs.random_lengths_case(51, n_real=3, lo=60, hi=200, ghost_slots=1, hk=2, hv=2, d=128,
