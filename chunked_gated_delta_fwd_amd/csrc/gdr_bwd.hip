@@ -727,23 +727,26 @@ __device__ __forceinline__ uint32_t bf16_of(v2u32 x, int e) { return (e & 1) ? x
 
 template <int D>
 struct GradLds {
-    // [64][D] rows at a pitch of 2 mod 32 four-byte banks: their 8-byte
-    // row-fragment reads (16 lanes, one row each) are free of conflicts
-    static constexpr int PK = D + 4;
+    // Row pitches (bf16 elements), chosen by timing the kernel over a sweep
+    // of them (the results are bit-identical).  q and v, read by transposing
+    // reads only: 16 mod 64
+    static constexpr int PQ = D + 16;
+    // k: 8-byte row fragments (X = K S) and transposing reads
+    static constexpr int PK = D + 12;
     // dO, U, dW: key-permuted columns (kpos), read as 16-byte fragments
     // (16-byte aligned rows)
     static constexpr int PKP = D + 16;
-    // S^T / dS'^T: 6 mod 32 banks, so that the row fragments and the pieces of
-    // 16 consecutive rows are conflict-free and the transposing reads and the
-    // forward-order pieces at most 2-way
+    // S^T / dS'^T: row fragments, transposing reads, pieces of four rows
     static constexpr int PS = D + 12;
-    static constexpr int PP = C + 8;
+    // T^T and the Zs, dBn, dB tiles: 8-byte row fragments, transposing reads
+    // and 8-byte stores (rows only 8-byte aligned)
+    static constexpr int PP = C + 4;
     static constexpr int oQ = 0;
-    static constexpr int oK = oQ + C * PK * 2;
+    static constexpr int oK = oQ + C * PQ * 2;
     static constexpr int oO = oK + C * PK * 2;        // dO [64][PKP]
-    static constexpr int oV = oO + C * PKP * 2;       // V [64][PK]; later Zs, dBn, dB [64][PP] each
-    static constexpr int oT = oV + C * PK * 2;        // T^T [64][PP]
-    static constexpr int szVT = (C * PK * 2 + C * PP * 2) > 3 * C * PP * 2 ? (C * PK * 2 + C * PP * 2) : 3 * C * PP * 2;
+    static constexpr int oV = oO + C * PKP * 2;       // V [64][PQ]; later Zs, dBn, dB [64][PP] each
+    static constexpr int oT = oV + C * PQ * 2;        // T^T [64][PP]
+    static constexpr int szVT = (C * PQ * 2 + C * PP * 2) > 3 * C * PP * 2 ? (C * PQ * 2 + C * PP * 2) : 3 * C * PP * 2;
     static constexpr int oS = oV + szVT;              // S^T, later dS'^T: [dv][PS] (rows dv, columns dk)
     static constexpr int oU = oS + D * PS * 2;        // U [64][PKP]
     static constexpr int oW = oU + C * PKP * 2;       // dW [64][PKP]
@@ -756,7 +759,7 @@ struct GradLds {
 template <int D, bool IN_BF16, bool GATE_BF16>
 __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
     using Ly = GradLds<D>;
-    constexpr int PK = Ly::PK, PKP = Ly::PKP, PS = Ly::PS, PP = Ly::PP, NTD = D / 16;
+    constexpr int PQ = Ly::PQ, PK = Ly::PK, PKP = Ly::PKP, PS = Ly::PS, PP = Ly::PP, NTD = D / 16;
     extern __shared__ __align__(16) unsigned char lds[];
     uint16_t *sQ = reinterpret_cast<uint16_t *>(lds + Ly::oQ);
     uint16_t *sK = reinterpret_cast<uint16_t *>(lds + Ly::oK);
@@ -787,7 +790,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
     const bool colwave = wave < NTD;   // owns column tile `wave` in the column-split phases
     const int nt = wave;
 
-    stage_rows2<D, IN_BF16, kBwdThreads, PK, PK>(sQ, a.q, a.hk, hk, sK, a.k, a.hk, hk, p.t0, p.len, tid);
+    stage_rows2<D, IN_BF16, kBwdThreads, PQ, PK>(sQ, a.q, a.hk, hk, sK, a.k, a.hk, hk, p.t0, p.len, tid);
 
     f32x4 accQ[4], accK[4];
 #pragma unroll
@@ -866,8 +869,8 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
             if (hh > 0) GDR_GRAD_DG(h - 1, lane, (hh - 1) & 1)   // the previous v-head's, while the loads fly
 #pragma unroll
             for (int j = 0; j < NP; ++j) {
-                const int i = tid + j * kBwdThreads, off = (i / PR) * PK + 8 * (i % PR);
-                st16<PK % 8 == 0>(sV + off, rv[j]);
+                const int i = tid + j * kBwdThreads, off = (i / PR) * PQ + 8 * (i % PR);
+                st16<PQ % 8 == 0>(sV + off, rv[j]);
                 // dO with key-permuted columns: the piece's two halves of four
                 const int orow = i / PR, oc = 8 * (i % PR);
                 *reinterpret_cast<v2u32 *>(sO + orow * PKP + kpos(oc)) = v2u32{ro[j][0], ro[j][1]};
@@ -895,7 +898,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < NT8; ++j) {
                 const int i = tid + j * kBwdThreads;
-                *reinterpret_cast<v4u32 *>(sT + (i / (C / 8)) * PP + 8 * (i % (C / 8))) = rt[j];
+                st16<PP % 8 == 0>(sT + (i / (C / 8)) * PP + 8 * (i % (C / 8)), rt[j]);
             }
         }
         if (wave == 1) {
@@ -926,7 +929,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 f32x4 w;
-                const f32x4 vv = col4(sV, PK, 16 * mt, 16 * nt, l16, lq);
+                const f32x4 vv = col4(sV, PQ, 16 * mt, 16 * nt, l16, lq);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * mt + 4 * lq + r;
@@ -1067,7 +1070,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const bf16x8 bk = frag_cols(sK, PK, 16 * nt, 32 * kk, l16, lq);
-                const bf16x8 bq = frag_cols(sQ, PK, 16 * nt, 32 * kk, l16, lq);
+                const bf16x8 bq = frag_cols(sQ, PQ, 16 * nt, 32 * kk, l16, lq);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     dQt[mt] = mfma32(frag_rows(sZs, PP, 16 * mt, 32 * kk, l16, lq), bk, dQt[mt]);
@@ -1079,7 +1082,7 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 float pg[4], pb[4];
-                const f32x4 q4 = col4(sQ, PK, 16 * mt, 16 * nt, l16, lq), k4 = col4(sK, PK, 16 * mt, 16 * nt, l16, lq);
+                const f32x4 q4 = col4(sQ, PQ, 16 * mt, 16 * nt, l16, lq), k4 = col4(sK, PK, 16 * mt, 16 * nt, l16, lq);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * mt + 4 * lq + r;
