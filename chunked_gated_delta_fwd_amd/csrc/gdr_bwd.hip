@@ -797,10 +797,10 @@ __global__ void __launch_bounds__(kBwdThreads) gdr_bwd_grads_kernel(BwdArgs a) {
     for (int mt = 0; mt < 4; ++mt) accQ[mt] = accK[mt] = zero4();
 
     // dg: reverse prefix sums of dG within the chunk (wave 0); dbeta (wave 2);
-    // for v-head hv_ of parity hp_, from the row sums the previous v-head's
-    // phases left in LDS.  Run at the next v-head's staging, while its loads
-    // are in flight; wave 1 forms that v-head's gate vectors meanwhile (e^{G_L}
-    // is kept per v-head parity for this reason).
+    // for v-head hv_ of parity hp_, from the row sums its phases left in LDS.
+    // Run at the next v-head's staging, while that one's loads are in flight;
+    // meanwhile wave 1 forms the next v-head's gate vectors, so e^{G_L} is
+    // kept per v-head parity (the value read here is not overwritten).
 #define GDR_GRAD_DG(hv_, ln_, hp_)                                                             \
     if (wave == 0) {                                                                         \
         float dG = 0.f;                                                                      \
